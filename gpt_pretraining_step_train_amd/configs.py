@@ -1,0 +1,63 @@
+"""The five named model/step configurations (shapes only).
+
+depth sets the rest on the nanochat pages ("one dial"); the shapes here are
+the tiny, laptop-scale, d12, d24 and d26 GPTs with vocab 2^15 = 32768 for the
+depth-dialled ones and 4096 for the two small ones, sequence length 2048 and
+device batch 16 for the depth-dialled ones.
+"""
+from __future__ import annotations
+
+PRECISION = {"fp32": 0, "bf16": 1, "fp8": 2}
+
+CONFIGS = {
+    "tiny": dict(depth=2, d_model=128, n_head=4, head_dim=32, d_ff=512, vocab=4096,
+                 seq_len=128, batch=4, precision="fp32", tokens="uniform"),
+    "laptop": dict(depth=3, d_model=192, n_head=3, head_dim=64, d_ff=768, vocab=4096,
+                   seq_len=256, batch=32, precision="bf16", tokens="zipf"),
+    "d12": dict(depth=12, d_model=768, n_head=6, head_dim=128, d_ff=3072, vocab=32768,
+                seq_len=2048, batch=16, precision="bf16", tokens="zipf"),
+    "d24": dict(depth=24, d_model=1536, n_head=12, head_dim=128, d_ff=6144, vocab=32768,
+                seq_len=2048, batch=16, precision="bf16", tokens="zipf"),
+    "d26": dict(depth=26, d_model=1664, n_head=13, head_dim=128, d_ff=6656, vocab=32768,
+                seq_len=2048, batch=16, precision="fp8", tokens="zipf"),
+}
+
+DEFAULTS = dict(init_std=0.02, rope_base=10000.0, norm_eps=1e-6, muon_momentum=0.95,
+                ns_steps=5)
+
+
+def get(name: str, **over) -> dict:
+    c = dict(DEFAULTS)
+    c.update(CONFIGS[name])
+    c.update(over)
+    c["name"] = name
+    return c
+
+
+def n_params(cfg: dict) -> int:
+    d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
+    return 2 * V * d + L * (4 * d * d + 2 * F * d)
+
+
+def step_flops(cfg: dict) -> dict:
+    """Algorithmic FLOPs of one step: dense GEMMs, exact causal attention, Newton-Schulz.
+
+    fwd+bwd = 6 N (12 L d^2 + d V) when F = 4d (generally 6 N (4 L d^2 + 2 L d F + d V)),
+    plus causal attention 6 L d N (T+1) (fwd 2 d T (T+1) per sequence and layer, bwd 2x).
+    Muon = ns_steps * sum over block matrices of (4 s^2 l + 2 s^3), s = min dim, l = max dim.
+    """
+    d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
+    B, T = cfg["batch"], cfg["seq_len"]
+    N = B * T
+    linear = 6 * N * (4 * L * d * d + 2 * L * d * F)
+    head = 6 * N * d * V
+    attn = 6 * L * d * N * (T + 1)
+    k = cfg.get("ns_steps", 5)
+    mats = [(d, d)] * 4 + [(F, d), (d, F)]
+    muon = 0
+    for (r, c) in mats:
+        s, l = min(r, c), max(r, c)
+        muon += k * (4 * s * s * l + 2 * s ** 3)
+    muon *= L
+    return dict(linear=linear, head=head, attn=attn, muon=muon,
+                total=linear + head + attn + muon)

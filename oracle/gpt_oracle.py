@@ -1,0 +1,298 @@
+"""fp64 CPU oracle of one nanochat-style GPT pretraining step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+run this module; only the tests, the smoke check and the benchmark's CPU
+baseline do.  It shares no code with the HIP library.
+
+What it computes (plain definitions, no blocking or fusion):
+
+* Forward of the pre-norm decoder GPT that the nanochat articles describe
+  ("nanochat Nasil Calisir? / 1. GPT Modeli" on the dev.to page in Turkish and
+  the same section of its Arabic translation): token-embedding lookup with an
+  untied LM head, rotary position embeddings and QK normalisation on queries
+  and keys, causal multi-head attention, a ReLU^2 MLP, bias-free linears
+  (the article's ``Linear`` casts its weight and calls ``F.linear`` with no
+  bias, section "3. Hassasiyet Yonetimi"), a final norm, then the mean
+  softmax cross-entropy over the vocabulary.
+* Its exact gradient, by a hand-written reverse pass.
+* The Muon update of every block matrix: heavy-ball momentum, Frobenius
+  normalisation, then the Newton-Schulz / Polar Express loop exactly in the
+  form the article prints (section "2. Muon Optimize Edici": A = X^T X,
+  B = b A + c A^2, X = a X + X B for each (a, b, c) of the table).
+
+Readings where the pages are silent (all parameter-free norms, eps = 1e-6 inside
+the square root, RoPE base 10000 with half-split pairs, QK-norm as a per-head
+RMSNorm applied after the rotation, MHA with scale 1/sqrt(head_dim), loss =
+mean over all B*T positions, heavy-ball momentum, X0 = B/(|B|_F + 1e-7),
+W <- W - lr X) are listed with the design notes of this repository.
+
+Parity pins: every function here is pinned by a test under tests/ that does not
+re-type its formula (finite differences, closed forms, library routines,
+invariants).  fp8 quantisation is not modelled: the fp8 path is compared with
+this unquantised result.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# configuration / parameter table
+
+
+def unpack(params, cfg):
+    """Split the flat tensor table [E, (Wq,Wk,Wv,Wo,W1,W2)*L, U] into parts."""
+    L = cfg["depth"]
+    assert len(params) == 2 + 6 * L
+    E = params[0]
+    layers = [tuple(params[1 + 6 * l: 7 + 6 * l]) for l in range(L)]
+    U = params[1 + 6 * L]
+    return E, layers, U
+
+
+# ---------------------------------------------------------------------------
+# building blocks
+
+
+def rms_norm(x, eps):
+    """Parameter-free RMSNorm over the last axis: y = x / sqrt(mean(x^2) + eps).
+
+    Returns (y, r) with r = 1/sqrt(mean(x^2) + eps) kept for the backward.
+    """
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * r, r
+
+
+def rms_norm_bwd(dy, y, r):
+    """Gradient of rms_norm: dx = r * (dy - y * mean(dy * y))."""
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def rope_angles(T, hd, base):
+    """angle[t, i] = t * base^(-2i/hd) for i < hd/2 (positions 0..T-1)."""
+    i = np.arange(hd // 2, dtype=np.float64)
+    freq = base ** (-2.0 * i / hd)
+    t = np.arange(T, dtype=np.float64)
+    return t[:, None] * freq[None, :]
+
+
+def rope(x, ang, inverse=False):
+    """Rotate half-split pairs (i, i + hd/2) of x [..., T, H, hd] by angle [T, hd/2].
+
+    forward:  x'_i = x_i cos - x_{i+h} sin ;  x'_{i+h} = x_i sin + x_{i+h} cos.
+    inverse=True rotates by -angle (this is also the backward of the rotation).
+    """
+    h = x.shape[-1] // 2
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    if inverse:
+        s = -s
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def causal_attention(q, k, v):
+    """o[b,i,h] = sum_{j<=i} softmax_j(q_i . k_j / sqrt(hd)) v_j ; q,k,v [B,T,H,hd]."""
+    B, T, H, hd = q.shape
+    S = np.einsum("bihd,bjhd->bhij", q, k) / np.sqrt(hd)
+    mask = np.triu(np.ones((T, T), dtype=bool), 1)
+    S = np.where(mask, -np.inf, S)
+    S = S - S.max(axis=-1, keepdims=True)
+    P = np.exp(S)
+    P /= P.sum(axis=-1, keepdims=True)
+    o = np.einsum("bhij,bjhd->bihd", P, v)
+    return o, P
+
+
+def causal_attention_bwd(do, q, k, v, o, P=None):
+    """Backward of causal_attention.
+
+    dP = dO v^T ; dS = P * (dP - rowsum(dO * O)) ; dq = dS k / sqrt(hd);
+    dk = dS^T q / sqrt(hd) ; dv = P^T dO.
+    """
+    B, T, H, hd = q.shape
+    if P is None:
+        _, P = causal_attention(q, k, v)
+    dv = np.einsum("bhij,bihd->bjhd", P, do)
+    dP = np.einsum("bihd,bjhd->bhij", do, v)
+    D = np.einsum("bihd,bihd->bhi", do, o)[..., None]
+    dS = P * (dP - D)
+    sc = 1.0 / np.sqrt(hd)
+    dq = np.einsum("bhij,bjhd->bihd", dS, k) * sc
+    dk = np.einsum("bhij,bihd->bjhd", dS, q) * sc
+    return dq, dk, dv
+
+
+def logsumexp(z):
+    m = z.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def argmax_lowest(z):
+    """Index of the maximum along the last axis, lowest index among exact ties."""
+    return np.argmax(z, axis=-1).astype(np.int32)  # numpy returns the first maximum
+
+
+# ---------------------------------------------------------------------------
+# forward / backward
+
+
+def forward(params, tokens, cfg, keep=True):
+    """Forward pass.  Returns (logits [B,T,V], cache for backward)."""
+    p = [np.asarray(w, dtype=np.float64) for w in params]
+    E, layers, U = unpack(p, cfg)
+    eps = cfg.get("norm_eps", 1e-6)
+    H, hd = cfg["n_head"], cfg["head_dim"]
+    B, T = tokens.shape
+    d = cfg["d_model"]
+    ang = rope_angles(T, hd, cfg.get("rope_base", 10000.0))
+
+    h = E[tokens]                                         # [B,T,d]
+    cache = {"tokens": tokens, "ang": ang, "layers": [], "p": p}
+    for (Wq, Wk, Wv, Wo, W1, W2) in layers:
+        a, ra = rms_norm(h, eps)
+        q = (a @ Wq.T).reshape(B, T, H, hd)
+        k = (a @ Wk.T).reshape(B, T, H, hd)
+        v = (a @ Wv.T).reshape(B, T, H, hd)
+        qn, rq = rms_norm(rope(q, ang), eps)
+        kn, rk = rms_norm(rope(k, ang), eps)
+        o, _ = causal_attention(qn, kn, v)
+        o2 = o.reshape(B, T, d)
+        h1 = h + o2 @ Wo.T
+        m, rm = rms_norm(h1, eps)
+        u = m @ W1.T
+        g = np.maximum(u, 0.0) ** 2
+        h2 = h1 + g @ W2.T
+        if keep:
+            cache["layers"].append(dict(h=h, a=a, ra=ra, qn=qn, rq=rq, kn=kn, rk=rk,
+                                        v=v, o=o, h1=h1, m=m, rm=rm, u=u, g=g))
+        h = h2
+    r, rf = rms_norm(h, eps)
+    z = r @ U.T
+    cache.update(hL=h, r=r, rf=rf)
+    return z, cache
+
+
+def loss_from_logits(z, targets):
+    """Mean over positions of logsumexp(z) - z[target]."""
+    lse = logsumexp(z)
+    zy = np.take_along_axis(z, targets[..., None].astype(np.int64), axis=-1)[..., 0]
+    return float(np.mean(lse - zy)), lse - zy
+
+
+def backward(z, targets, cache, cfg):
+    """Exact gradient of the mean cross-entropy w.r.t. every tensor of the table."""
+    p = cache["p"]
+    E, layers, U = unpack(p, cfg)
+    H, hd = cfg["n_head"], cfg["head_dim"]
+    B, T, V = z.shape
+    d = cfg["d_model"]
+    N = B * T
+    ang = cache["ang"]
+    tokens = cache["tokens"]
+
+    # softmax cross-entropy: dz = (softmax(z) - onehot(y)) / N
+    zs = z - z.max(axis=-1, keepdims=True)
+    P = np.exp(zs)
+    P /= P.sum(axis=-1, keepdims=True)
+    dz = P
+    np.put_along_axis(dz, targets[..., None].astype(np.int64),
+                      np.take_along_axis(dz, targets[..., None].astype(np.int64), -1) - 1.0, -1)
+    dz /= N
+
+    r = cache["r"]
+    dU = dz.reshape(N, V).T @ r.reshape(N, d)
+    dr = dz @ U
+    dh = rms_norm_bwd(dr, r, cache["rf"])
+
+    grads_layers = []
+    for (Wq, Wk, Wv, Wo, W1, W2), c in zip(reversed(layers), reversed(cache["layers"])):
+        # MLP block: h2 = h1 + g W2^T, g = relu(u)^2, u = m W1^T, m = rms(h1)
+        dW2 = dh.reshape(N, d).T @ c["g"].reshape(N, -1)
+        dg = dh @ W2
+        du = dg * 2.0 * np.maximum(c["u"], 0.0)
+        dW1 = du.reshape(N, -1).T @ c["m"].reshape(N, d)
+        dm = du @ W1
+        dh1 = dh + rms_norm_bwd(dm, c["m"], c["rm"])
+        # attention block: h1 = h + o Wo^T
+        o2 = c["o"].reshape(B, T, d)
+        dWo = dh1.reshape(N, d).T @ o2.reshape(N, d)
+        do = (dh1 @ Wo).reshape(B, T, H, hd)
+        dqn, dkn, dv = causal_attention_bwd(do, c["qn"], c["kn"], c["v"], c["o"])
+        dq = rope(rms_norm_bwd(dqn, c["qn"], c["rq"]), ang, inverse=True).reshape(B, T, d)
+        dk = rope(rms_norm_bwd(dkn, c["kn"], c["rk"]), ang, inverse=True).reshape(B, T, d)
+        dv = dv.reshape(B, T, d)
+        a2 = c["a"].reshape(N, d)
+        dWq = dq.reshape(N, d).T @ a2
+        dWk = dk.reshape(N, d).T @ a2
+        dWv = dv.reshape(N, d).T @ a2
+        da = dq @ Wq + dk @ Wk + dv @ Wv
+        dh = dh1 + rms_norm_bwd(da, c["a"], c["ra"])
+        grads_layers.append((dWq, dWk, dWv, dWo, dW1, dW2))
+    grads_layers.reverse()
+
+    dE = np.zeros_like(E)
+    np.add.at(dE, tokens.reshape(-1), dh.reshape(N, d))
+    grads = [dE]
+    for gl in grads_layers:
+        grads.extend(gl)
+    grads.append(dU)
+    return grads
+
+
+def loss_and_grads(params, tokens, targets, cfg):
+    """(loss, grads in tensor-table order, argmax [B,T], per-position loss [B,T])."""
+    z, cache = forward(params, tokens, cfg)
+    loss, per_pos = loss_from_logits(z, targets)
+    grads = backward(z, targets, cache, cfg)
+    return loss, grads, argmax_lowest(z), per_pos
+
+
+def loss_only(params, tokens, targets, cfg):
+    z, _ = forward(params, tokens, cfg, keep=False)
+    return loss_from_logits(z, targets)[0]
+
+
+# ---------------------------------------------------------------------------
+# Muon
+
+
+def newton_schulz(X, coeffs):
+    """The article's orthogonalisation loop, verbatim in form:
+
+    for (a, b, c): A = X^T X ; B = b A + c A A ; X = a X + X B.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    for (a, b, c) in coeffs:
+        A = X.T @ X
+        Bm = b * A + c * (A @ A)
+        X = a * X + X @ Bm
+    return X
+
+
+def muon_matrix(G, Bm, coeffs, mu=0.95, eps=1e-7):
+    """One Muon direction for one matrix.
+
+    Bm <- mu Bm + G (heavy ball, starts at zero); X0 = Bm / (|Bm|_F + eps);
+    returns (X_ns, Bm_new).
+    """
+    Bm = mu * np.asarray(Bm, dtype=np.float64) + np.asarray(G, dtype=np.float64)
+    X0 = Bm / (np.linalg.norm(Bm) + eps)
+    return newton_schulz(X0, coeffs), Bm
+
+
+def muon_update(params, grads, moms, cfg, lr, coeffs):
+    """Muon step on every block matrix (Wq, Wk, Wv, Wo, W1, W2 of each layer,
+    each separately).  E and U are left untouched (their AdamW group is not part
+    of this step).  Returns (new_params, new_moms, directions) as lists in
+    tensor-table order (None for E and U)."""
+    L = cfg["depth"]
+    mu = cfg.get("muon_momentum", 0.95)
+    newp = [np.asarray(w, dtype=np.float64).copy() for w in params]
+    newm = [None] * len(params)
+    dirs = [None] * len(params)
+    for i in range(1, 1 + 6 * L):
+        X, Bm = muon_matrix(grads[i], moms[i], coeffs, mu)
+        newp[i] = newp[i] - lr * X
+        newm[i] = Bm
+        dirs[i] = X
+    return newp, newm, dirs

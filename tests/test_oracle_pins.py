@@ -1,0 +1,454 @@
+"""Pins of the fp64 oracle against facts it does not itself define.
+
+Each test checks the oracle against finite differences, closed forms,
+library routines (torch CPU fp64, scipy, LAPACK SVD), invariants or brute
+force, chosen so that a dropped term, a wrong sign or index or a transposed
+operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import gpt_oracle as O
+from oracle import polar_express as PE
+from gpt_pretraining_step_train_amd import inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+MICRO = dict(depth=1, d_model=16, n_head=2, head_dim=8, d_ff=64, vocab=64, seq_len=8,
+             batch=2, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
+MICRO2 = dict(MICRO, depth=2)
+TINY = dict(depth=2, d_model=128, n_head=4, head_dim=32, d_ff=512, vocab=4096, seq_len=128,
+            batch=4, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
+
+
+def _params(cfg, seed=0, std=None):
+    c = dict(cfg)
+    if std is not None:
+        c["init_std"] = std
+    return [w.astype(np.float64) for w in inputs.init_weights(c, seed)]
+
+
+def _tokens(cfg, seed=0, dist="uniform"):
+    return inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=dist, seed=seed)
+
+
+# --------------------------------------------------------------------------
+# P1: the whole backward against centred finite differences
+
+
+@pytest.mark.parametrize("cfg", [MICRO, MICRO2])
+def test_fd_gradient_every_element(cfg):
+    params = _params(cfg, seed=1, std=0.5)          # large weights: non-linear regime
+    tok, tgt = _tokens(cfg, seed=2)
+    tok[0, 3] = tok[0, 5] = tok[1, 0]               # repeated ids exercise the scatter-add
+    loss, grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    h = 1e-5
+    for ti, (w, g) in enumerate(zip(params, grads)):
+        fd = np.zeros_like(w)
+        it = np.nditer(w, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = w[idx]
+            w[idx] = old + h
+            lp = O.loss_only(params, tok, tgt, cfg)
+            w[idx] = old - h
+            lm = O.loss_only(params, tok, tgt, cfg)
+            w[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        rel = np.linalg.norm(fd - g) / max(np.linalg.norm(g), 1e-300)
+        assert rel <= 1e-6, (ti, rel)
+
+
+def test_fd_gradient_directions_tiny():
+    cfg = TINY
+    params = _params(cfg, seed=3, std=0.1)
+    tok, tgt = _tokens(cfg, seed=4)
+    loss, grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    rng = np.random.default_rng(5)
+    h = 1e-5
+    for ti in range(len(params)):
+        gn = np.linalg.norm(grads[ti])
+        for j in range(3):
+            # the gradient direction itself, then random directions; the error is
+            # measured against |grad| (the largest directional derivative)
+            v = grads[ti] / gn if j == 0 else rng.standard_normal(params[ti].shape)
+            v = v / np.linalg.norm(v)
+            w0 = params[ti]
+            params[ti] = w0 + h * v
+            lp = O.loss_only(params, tok, tgt, cfg)
+            params[ti] = w0 - h * v
+            lm = O.loss_only(params, tok, tgt, cfg)
+            params[ti] = w0
+            fd = (lp - lm) / (2 * h)
+            an = float(np.sum(grads[ti] * v))
+            assert abs(fd - an) <= 1e-6 * gn, (ti, j, fd, an, gn)
+
+
+# --------------------------------------------------------------------------
+# P2: zero LM head => uniform prediction
+
+
+def test_zero_head_gives_ln_vocab_and_closed_form_grads():
+    gold = json.load(open(os.path.join(GOLD, "vocab_and_uniform_loss.json")))
+    cfg = dict(TINY)
+    params = _params(cfg, seed=7, std=0.05)
+    params[-1][:] = 0.0
+    tok, tgt = _tokens(cfg, seed=8)
+    loss, grads, am, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    assert loss == pytest.approx(gold["small_uniform_loss"], abs=1e-12)
+    assert math.log(cfg["vocab"]) == pytest.approx(gold["small_uniform_loss"], abs=1e-12)
+    for g in grads[:-1]:
+        assert np.all(g == 0.0)
+    assert np.all(am == 0)                  # all logits tie -> lowest index
+    # dU = (1/N) sum_n (1/V - e_{y_n}) r_n^T, r_n = final-norm output
+    z, cache = O.forward(params, tok, cfg)
+    N = tok.size
+    r = cache["r"].reshape(N, -1)
+    want = np.tile(r.sum(0) / cfg["vocab"], (cfg["vocab"], 1))
+    np.subtract.at(want, tgt.reshape(-1), r)
+    want /= N
+    np.testing.assert_allclose(grads[-1], want, rtol=1e-12, atol=1e-15)
+
+
+def test_zero_head_at_32768_vocab():
+    gold = json.load(open(os.path.join(GOLD, "vocab_and_uniform_loss.json")))
+    cfg = dict(MICRO, vocab=gold["vocab"])
+    params = _params(cfg, seed=9)
+    params[-1][:] = 0.0
+    tok, tgt = _tokens(cfg, seed=10, dist="zipf")
+    z, _ = O.forward(params, tok, cfg)
+    assert O.loss_from_logits(z, tgt)[0] == pytest.approx(gold["uniform_loss"], abs=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P3: initial loss near ln V + s^2/2 (logits ~ N(0, 0.02^2 d), unit-RMS final norm)
+
+
+def test_initial_loss_statistics():
+    cfg = TINY
+    params = _params(cfg, seed=0)
+    tok, tgt = _tokens(cfg, seed=0)
+    z, _ = O.forward(params, tok, cfg)
+    loss = O.loss_from_logits(z, tgt)[0]
+    want = math.log(cfg["vocab"]) + 0.5 * 0.02 ** 2 * cfg["d_model"]
+    assert abs(loss - want) < 0.03, (loss, want)
+
+
+# --------------------------------------------------------------------------
+# P4: causality
+
+
+def test_causality_exact():
+    cfg = TINY
+    params = _params(cfg, seed=11, std=0.2)
+    tok, _ = _tokens(cfg, seed=12)
+    z0, _ = O.forward(params, tok, cfg, keep=False)
+    t = 57
+    tok2 = tok.copy()
+    tok2[:, t + 1] = (tok2[:, t + 1] + 17) % cfg["vocab"]
+    z1, _ = O.forward(params, tok2, cfg, keep=False)
+    assert np.array_equal(z0[:, : t + 1], z1[:, : t + 1])
+    assert not np.array_equal(z0[:, t + 1], z1[:, t + 1])
+
+
+# --------------------------------------------------------------------------
+# P5: attention special cases and a library routine
+
+
+def test_attention_special_cases_and_sdpa():
+    rng = np.random.default_rng(0)
+    B, T, H, hd = 2, 9, 3, 8
+    q, k, v = (rng.standard_normal((B, T, H, hd)) for _ in range(3))
+    o, _ = O.causal_attention(q[:, :1], k[:, :1], v[:, :1])
+    np.testing.assert_array_equal(o, v[:, :1])                    # T = 1 -> o = v
+    o, _ = O.causal_attention(np.zeros_like(q), k, v)               # q = 0 -> running mean
+    want = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None, None]
+    np.testing.assert_allclose(o, want, rtol=1e-13, atol=1e-14)
+    o, _ = O.causal_attention(q, k, v)
+    t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True)
+    np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=1e-12, atol=1e-13)
+    # brute force on one (b, h, i)
+    b, h, i = 1, 2, 6
+    s = np.array([np.dot(q[b, i, h], k[b, j, h]) / math.sqrt(hd) for j in range(i + 1)])
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    np.testing.assert_allclose(o[b, i, h], sum(w[j] * v[b, j, h] for j in range(i + 1)),
+                               rtol=1e-12)
+
+
+def test_attention_backward_vs_autograd():
+    rng = np.random.default_rng(1)
+    B, T, H, hd = 2, 7, 2, 4
+    q, k, v, do = (rng.standard_normal((B, T, H, hd)) for _ in range(4))
+    o, _ = O.causal_attention(q, k, v)
+    dq, dk, dv = O.causal_attention_bwd(do, q, k, v, o)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).requires_grad_() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    ref.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
+    for mine, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, t.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P6: RMSNorm, RoPE, QK-norm invariants
+
+
+def test_rmsnorm_library_and_closed_form():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 33)) * 3
+    y, r = O.rms_norm(x, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (33,), eps=1e-6).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-13)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, -1)), np.sqrt(ms / (ms + 1e-6)), rtol=1e-13)
+    # backward against autograd
+    tx = torch.from_numpy(x).requires_grad_()
+    dy = rng.standard_normal(x.shape)
+    torch.nn.functional.rms_norm(tx, (33,), eps=1e-6).backward(torch.from_numpy(dy))
+    np.testing.assert_allclose(O.rms_norm_bwd(dy, y, r), tx.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_rope_pairing_frequencies_and_relative_property():
+    T, hd, base = 11, 8, 10000.0
+    ang = O.rope_angles(T, hd, base)
+    x = np.zeros((1, T, 1, hd))
+    x[..., 0] = 1.0          # unit vector on the first pair (frequency base^0 = 1)
+    y = O.rope(x, ang)
+    t = np.arange(T)
+    np.testing.assert_allclose(y[0, :, 0, 0], np.cos(t), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, hd // 2], np.sin(t), rtol=1e-14, atol=1e-15)
+    x = np.zeros((1, T, 1, hd))
+    x[..., hd // 2 + 1] = 1.0  # second element of pair 1 (frequency base^(-2/hd))
+    y = O.rope(x, ang)
+    f1 = base ** (-2.0 / hd)
+    np.testing.assert_allclose(y[0, :, 0, 1], -np.sin(t * f1), atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, hd // 2 + 1], np.cos(t * f1), atol=1e-15)
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, T, 1, hd))
+    np.testing.assert_array_equal(O.rope(q, ang)[0, 0], q[0, 0])      # position 0: identity
+    np.testing.assert_allclose(O.rope(O.rope(q, ang), ang, inverse=True), q, rtol=1e-13, atol=1e-14)
+    k = rng.standard_normal((1, T, 1, hd))
+    qq = np.repeat(q[:, :1], T, axis=1)
+    kk = np.repeat(k[:, :1], T, axis=1)
+    rq, rk = O.rope(qq, ang), O.rope(kk, ang)
+    dots = np.einsum("btd,bsd->ts", rq[:, :, 0], rk[:, :, 0])
+    for dlt in range(-3, 4):
+        dd = np.diagonal(dots, offset=dlt)
+        np.testing.assert_allclose(dd, dd[0], rtol=1e-12, atol=1e-13)   # depends on m - n only
+    # norm commutes with the rotation
+    a, _ = O.rms_norm(O.rope(q, ang), 1e-6)
+    b = O.rope(O.rms_norm(q, 1e-6)[0], ang)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# P7: cross-entropy against library routines
+
+
+def test_cross_entropy_library():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((3, 5, 97)) * 4
+    y = rng.integers(0, 97, (3, 5))
+    loss, per = O.loss_from_logits(z, y)
+    ref = scipy.special.logsumexp(z, axis=-1) - np.take_along_axis(z, y[..., None], -1)[..., 0]
+    np.testing.assert_allclose(per, ref, rtol=1e-14)
+    tl = torch.nn.functional.cross_entropy(torch.from_numpy(z.reshape(-1, 97)),
+                                           torch.from_numpy(y.reshape(-1)))
+    assert loss == pytest.approx(float(tl), rel=1e-14)
+
+
+def test_argmax_lowest_index():
+    z = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0], [0.0, -1.0, 0.5, 0.5]])
+    assert O.argmax_lowest(z).tolist() == [1, 0, 2]
+
+
+# --------------------------------------------------------------------------
+# P8: Newton-Schulz
+
+
+def _composed(coeffs, s):
+    for abc in coeffs:
+        s = PE.quintic(s, abc)
+    return s
+
+
+def test_polar_express_table_printed_prefix_and_band():
+    gold = json.load(open(os.path.join(GOLD, "ns_printed_coeffs.json")))
+    table, iv = PE.coefficients(gold["ns_steps"])
+    assert [list(t) for t in table[:2]] == gold["printed"]
+    lo, hi = iv[-1]
+    assert 0.85 < lo < 0.9 and 1.1 < hi < 1.15
+    # each derived step is minimax: the error equioscillates (max |1-p| reached >= 4 times)
+    for k in range(2, 5):
+        l0, h0 = iv[k]
+        x = np.geomspace(l0, h0, 20001)
+        e = 1 - PE.quintic(x, table[k])
+        emax = np.abs(e).max()
+        peaks = np.sum((np.abs(e[1:-1]) >= np.abs(e[:-2])) & (np.abs(e[1:-1]) >= np.abs(e[2:]))
+                       & (np.abs(e[1:-1]) > 0.999 * emax)) + (abs(e[0]) > 0.999 * emax) + (abs(e[-1]) > 0.999 * emax)
+        assert peaks >= 4, (k, peaks)
+
+
+def test_newton_schulz_closed_form_band_and_symmetries():
+    table, _ = PE.coefficients()
+    rng = np.random.default_rng(6)
+    G = rng.standard_normal((24, 40))
+    X0 = G / np.linalg.norm(G)
+    X = O.newton_schulz(X0, table)
+    U, S, Vt = np.linalg.svd(X0, full_matrices=False)
+    np.testing.assert_allclose(X, (U * _composed(table, S)) @ Vt, rtol=1e-11, atol=1e-12)
+    sv = np.linalg.svd(X, compute_uv=False)
+    keep = S >= 1e-3
+    assert np.all(sv[keep] > 0.85) and np.all(sv[keep] < 1.15)
+    # scale invariance of the normalised direction, transpose and orthogonal equivariance
+    Xa, _ = O.muon_matrix(3.7 * G, np.zeros_like(G), table, mu=0.95)
+    Xb, _ = O.muon_matrix(G, np.zeros_like(G), table, mu=0.95)
+    np.testing.assert_allclose(Xa, Xb, rtol=0, atol=1e-7)   # up to eps=1e-7 in the normaliser
+    Xt, _ = O.muon_matrix(G.T, np.zeros_like(G.T), table)
+    np.testing.assert_allclose(Xt, Xb.T, rtol=1e-10, atol=1e-11)
+    P, _ = np.linalg.qr(rng.standard_normal((24, 24)))
+    Q, _ = np.linalg.qr(rng.standard_normal((40, 40)))
+    Xpq, _ = O.muon_matrix(P @ G @ Q, np.zeros_like(G), table)
+    np.testing.assert_allclose(Xpq, P @ Xb @ Q, rtol=1e-9, atol=1e-10)
+    # the two Gram orientations agree
+    Y = X0.copy()
+    for (a, b, c) in table:
+        A = Y @ Y.T
+        Y = a * Y + (b * A + c * A @ A) @ Y
+    np.testing.assert_allclose(Y, X, rtol=1e-11, atol=1e-12)
+
+
+def test_newton_schulz_textbook_quintic():
+    # with the fixed quintic (15x - 10x^3 + 3x^5)/8 repeated, NS converges to the polar factor
+    rng = np.random.default_rng(8)
+    G = rng.standard_normal((6, 9)) + 3 * np.eye(6, 9)
+    X0 = G / np.linalg.norm(G, 2)     # spectral normalisation -> sigma in (0, 1]
+    X = O.newton_schulz(X0, [(15 / 8, -10 / 8, 3 / 8)] * 60)
+    U, _, Vt = np.linalg.svd(G, full_matrices=False)
+    np.testing.assert_allclose(X, U @ Vt, atol=1e-10)
+
+
+# --------------------------------------------------------------------------
+# P9: momentum
+
+
+def test_momentum_heavy_ball():
+    table, _ = PE.coefficients()
+    rng = np.random.default_rng(9)
+    G1, G2 = rng.standard_normal((2, 8, 12))
+    _, B1 = O.muon_matrix(G1, np.zeros_like(G1), table, mu=0.95)
+    np.testing.assert_array_equal(B1, G1)
+    X2, B2 = O.muon_matrix(G2, B1, table, mu=0.95)
+    np.testing.assert_allclose(B2, 0.95 * G1 + G2, rtol=1e-15)
+    # EMA form B <- mu B + (1-mu) G gives the same direction (normalisation is scale-free;
+    # eps = 0 removes the only scale-dependent term)
+    Xe, _ = O.muon_matrix(0.05 * G2, 0.05 * B1, table, mu=0.95, eps=0.0)
+    Xh, _ = O.muon_matrix(G2, B1, table, mu=0.95, eps=0.0)
+    np.testing.assert_allclose(Xe, Xh, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(Xh, X2, rtol=0, atol=1e-5)
+
+
+def test_muon_update_touches_only_block_matrices():
+    cfg = MICRO2
+    table, _ = PE.coefficients()
+    params = _params(cfg, seed=3)
+    rng = np.random.default_rng(1)
+    grads = [rng.standard_normal(w.shape) for w in params]
+    moms = [np.zeros_like(w) for w in params]
+    newp, newm, dirs = O.muon_update(params, grads, moms, cfg, 0.02, table)
+    np.testing.assert_array_equal(newp[0], params[0])
+    np.testing.assert_array_equal(newp[-1], params[-1])
+    for i in range(1, len(params) - 1):
+        np.testing.assert_allclose(newp[i], params[i] - 0.02 * dirs[i], rtol=1e-15)
+        np.testing.assert_array_equal(newm[i], grads[i])
+
+
+# --------------------------------------------------------------------------
+# P11: whole-model gradient against torch fp64 autograd; structural special cases
+
+
+def _torch_loss(params, tok, tgt, cfg):
+    """An independent torch formulation using library ops (rms_norm, SDPA, cross_entropy)."""
+    E, U = params[0], params[-1]
+    L, H, hd, d = cfg["depth"], cfg["n_head"], cfg["head_dim"], cfg["d_model"]
+    B, T = tok.shape
+    eps = cfg["norm_eps"]
+    pos = torch.arange(T, dtype=torch.float64)
+    inv = cfg["rope_base"] ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    ang = pos[:, None] * inv[None, :]
+    cos = torch.cat([ang.cos(), ang.cos()], -1)[None, :, None, :]
+    sin = torch.cat([ang.sin(), ang.sin()], -1)[None, :, None, :]
+
+    def rot(x):
+        x1, x2 = x[..., : hd // 2], x[..., hd // 2:]
+        return x * cos + torch.cat([-x2, x1], -1) * sin
+
+    rms = lambda x: torch.nn.functional.rms_norm(x, (x.shape[-1],), eps=eps)
+    x = E[torch.from_numpy(tok).long()]
+    for l in range(L):
+        Wq, Wk, Wv, Wo, W1, W2 = params[1 + 6 * l: 7 + 6 * l]
+        a = rms(x)
+        q = rms(rot((a @ Wq.T).view(B, T, H, hd)))
+        k = rms(rot((a @ Wk.T).view(B, T, H, hd)))
+        v = (a @ Wv.T).view(B, T, H, hd)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), is_causal=True)
+        x = x + o.transpose(1, 2).reshape(B, T, d) @ Wo.T
+        x = x + torch.relu(rms(x) @ W1.T).square() @ W2.T
+    z = rms(x) @ U.T
+    return torch.nn.functional.cross_entropy(z.reshape(B * T, -1),
+                                             torch.from_numpy(tgt).long().reshape(-1))
+
+
+def test_full_gradient_vs_torch_autograd():
+    cfg = TINY
+    params = _params(cfg, seed=21, std=0.1)
+    tok, tgt = _tokens(cfg, seed=22, dist="zipf")
+    loss, grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    tp = [torch.from_numpy(w.copy()).requires_grad_() for w in params]
+    tl = _torch_loss(tp, tok, tgt, cfg)
+    tl.backward()
+    assert loss == pytest.approx(float(tl), rel=1e-12)
+    for g, t in zip(grads, tp):
+        rel = np.linalg.norm(g - t.grad.numpy()) / np.linalg.norm(t.grad.numpy())
+        assert rel < 1e-10
+
+
+def test_identity_blocks_reduce_to_embedding_head():
+    cfg = TINY
+    params = _params(cfg, seed=23, std=0.3)
+    for l in range(cfg["depth"]):
+        params[1 + 6 * l + 3][:] = 0.0     # Wo
+        params[1 + 6 * l + 5][:] = 0.0     # W2
+    tok, tgt = _tokens(cfg, seed=24)
+    z, _ = O.forward(params, tok, cfg)
+    x = params[0][tok]
+    r = x / np.sqrt(np.mean(x * x, -1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(z, r @ params[-1].T, rtol=1e-12, atol=1e-13)
+    per = scipy.special.logsumexp(z, -1) - np.take_along_axis(z, tgt[..., None], -1)[..., 0]
+    assert O.loss_from_logits(z, tgt)[0] == pytest.approx(per.mean(), rel=1e-14)
+
+
+# --------------------------------------------------------------------------
+# P12: batch symmetry
+
+
+def test_batch_row_swap_symmetry():
+    cfg = TINY
+    params = _params(cfg, seed=31, std=0.1)
+    tok, tgt = _tokens(cfg, seed=32)
+    l0, g0, a0, p0 = O.loss_and_grads(params, tok, tgt, cfg)
+    perm = [2, 0, 3, 1]
+    l1, g1, a1, p1 = O.loss_and_grads(params, tok[perm], tgt[perm], cfg)
+    assert l1 == pytest.approx(l0, rel=1e-13)
+    np.testing.assert_array_equal(a1, a0[perm])
+    np.testing.assert_allclose(p1, p0[perm], rtol=1e-13)
+    for x, y in zip(g0, g1):
+        np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-14)
