@@ -1,0 +1,764 @@
+// Bandwidth-bound kernels of the GPT step: embedding gather and deterministic
+// scatter-add, RMSNorm forward/backward, RoPE + QK-norm, fused softmax
+// cross-entropy, and the elementwise pieces of Muon.  One wave per row for the
+// per-row kernels, float4 accesses across the 64 lanes.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+template <typename T>
+__device__ inline void st(T* p, float v);
+template <>
+__device__ inline void st<float>(float* p, float v) { *p = v; }
+template <>
+__device__ inline void st<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
+template <typename T>
+__device__ inline float ld(const T* p);
+template <>
+__device__ inline float ld<float>(const float* p) { return *p; }
+template <>
+__device__ inline float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+
+template <typename T>
+__device__ inline void st4(T* p, float4 v) {
+  st<T>(p, v.x); st<T>(p + 1, v.y); st<T>(p + 2, v.z); st<T>(p + 3, v.w);
+}
+template <>
+__device__ inline void st4<float>(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+template <>
+__device__ inline void st4<bf16_t>(bf16_t* p, float4 v) {
+  uint2 u = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
+constexpr int MAXV4 = 8;           // float4 per lane -> d <= 2048
+
+// ---------------------------------------------------------------------------
+// embedding gather: h[n] = E[tok[n]]
+
+__global__ void __launch_bounds__(256) embed_gather_kernel(const int32_t* __restrict__ tok,
+                                                           const float* __restrict__ E, float* __restrict__ h,
+                                                           int N, int d, int V, int* err) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const int t = tok[row];
+  const bool ok = (t >= 0 && t < V);
+  if (!ok && lane == 0) atomicOr(err, 1);
+  const float4* src = reinterpret_cast<const float4*>(E + (long)(ok ? t : 0) * d);
+  float4* dst = reinterpret_cast<float4*>(h + (long)row * d);
+  for (int i = lane; i < d / 4; i += 64) dst[i] = ok ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm (no gain): y = x / sqrt(mean(x^2) + eps)
+
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                                          float* __restrict__ rstd, int N, int d, float eps) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (long)row * d);
+  const int n4 = d / 4;
+  float4 v[MAXV4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    v[j] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  T* yr = y + (long)row * d;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    if (i < n4) st4<T>(yr + 4 * i, make_float4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r));
+  }
+  if (lane == 0) rstd[row] = r;
+}
+
+// dx = dres + r * (dy - y * mean(dy * y)),  y = x * r
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                          const float* __restrict__ rstd, const float* __restrict__ dres,
+                                                          float* __restrict__ dx, T* __restrict__ dxa, int N, int d) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const long off = (long)row * d;
+  const float4* xr = reinterpret_cast<const float4*>(x + off);
+  const float4* gr = reinterpret_cast<const float4*>(dy + off);
+  const int n4 = d / 4;
+  const float r = rstd[row];
+  float4 yv[MAXV4], gv[MAXV4];
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), g = a;
+    if (i < n4) { a = xr[i]; g = gr[i]; }
+    yv[j] = make_float4(a.x * r, a.y * r, a.z * r, a.w * r);
+    gv[j] = g;
+    dot += g.x * yv[j].x + g.y * yv[j].y + g.z * yv[j].z + g.w * yv[j].w;
+  }
+  dot = wave_sum(dot) / (float)d;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    if (i >= n4) continue;
+    float4 o;
+    o.x = r * (gv[j].x - yv[j].x * dot);
+    o.y = r * (gv[j].y - yv[j].y * dot);
+    o.z = r * (gv[j].z - yv[j].z * dot);
+    o.w = r * (gv[j].w - yv[j].w * dot);
+    if (dres) {
+      const float4 q = reinterpret_cast<const float4*>(dres + off)[i];
+      o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+    }
+    reinterpret_cast<float4*>(dx + off)[i] = o;
+    if (dxa) st4<T>(dxa + off + 4 * i, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE table: cs[t][i] = (cos, sin)(t * base^(-2i/hd)), angles in double precision
+
+__global__ void rope_table_kernel(float* cs, int T, int hd, float base) {
+  const int half = hd / 2;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= T * half) return;
+  const int t = e / half, i = e % half;
+  const double ang = (double)t * pow((double)base, -2.0 * (double)i / (double)hd);
+  cs[2 * e] = (float)cos(ang);
+  cs[2 * e + 1] = (float)sin(ang);
+}
+
+// q and k of every (token, head): rotate half-split pairs, then RMS-normalise the
+// head vector; in place in the qkv buffer [B*T][3*H*hd]
+template <typename T>
+__global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(T* __restrict__ qkv, const float* __restrict__ cs,
+                                                              float* __restrict__ rq, float* __restrict__ rk, int N,
+                                                              int Tlen, int H, int hd, float eps) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, head, q/k)
+  const int lane = threadIdx.x & 63;
+  if (w >= N * H * 2) return;
+  const int which = w & 1, nh = w >> 1, n = nh / H, h = nh % H;
+  const int t = n % Tlen, half = hd / 2;
+  T* p = qkv + (long)n * 3 * H * hd + which * H * hd + h * hd;
+  float y1[2], y2[2];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    y1[j] = y2[j] = 0.f;
+    if (i < half) {
+      const float x1 = ld<T>(p + i), x2 = ld<T>(p + i + half);
+      const float c = cs[2 * (t * half + i)], s = cs[2 * (t * half + i) + 1];
+      y1[j] = x1 * c - x2 * s;
+      y2[j] = x1 * s + x2 * c;
+      ss += y1[j] * y1[j] + y2[j] * y2[j];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    if (i < half) {
+      st<T>(p + i, y1[j] * r);
+      st<T>(p + i + half, y2[j] * r);
+    }
+  }
+  if (lane == 0) (which ? rk : rq)[nh] = r;
+}
+
+// backward: dz = r (dy - y mean(dy y)) in the rotated frame, then rotate by -angle
+template <typename T>
+__global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
+                                                              const float* __restrict__ cs, const float* __restrict__ rq,
+                                                              const float* __restrict__ rk, int N, int Tlen, int H,
+                                                              int hd) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= N * H * 2) return;
+  const int which = w & 1, nh = w >> 1, n = nh / H, h = nh % H;
+  const int t = n % Tlen, half = hd / 2;
+  const long off = (long)n * 3 * H * hd + which * H * hd + h * hd;
+  T* dp = dqkv + off;
+  const T* yp = qkv + off;
+  const float r = (which ? rk : rq)[nh];
+  float g1[2], g2[2], a1[2], a2[2];
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    g1[j] = g2[j] = a1[j] = a2[j] = 0.f;
+    if (i < half) {
+      g1[j] = ld<T>(dp + i); g2[j] = ld<T>(dp + i + half);
+      a1[j] = ld<T>(yp + i); a2[j] = ld<T>(yp + i + half);
+      dot += g1[j] * a1[j] + g2[j] * a2[j];
+    }
+  }
+  dot = wave_sum(dot) / (float)hd;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    if (i < half) {
+      const float z1 = r * (g1[j] - a1[j] * dot), z2 = r * (g2[j] - a2[j] * dot);
+      const float c = cs[2 * (t * half + i)], s = cs[2 * (t * half + i) + 1];
+      st<T>(dp + i, z1 * c + z2 * s);
+      st<T>(dp + i + half, -z1 * s + z2 * c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fused softmax cross-entropy over a vocabulary row held in registers.
+// row_loss[n] = lse - z[y]; dz = (softmax - onehot) * inv_n; argmax (lowest index)
+
+__device__ inline void blk_argmax(float& v, int& idx, float* sv, int* si) {
+  // wave level
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  }
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { sv[w] = v; si[w] = idx; }
+  __syncthreads();
+  v = sv[0]; idx = si[0];
+  for (int k = 1; k < (int)(blockDim.x >> 6); ++k) {
+    if (sv[k] > v || (sv[k] == v && si[k] < idx)) { v = sv[k]; idx = si[k]; }
+  }
+  __syncthreads();
+}
+
+__device__ inline float blk_sum(float v, float* sv) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sv[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int k = 0; k < (int)(blockDim.x >> 6); ++k) s += sv[k];
+  __syncthreads();
+  return s;
+}
+
+template <typename T, int C>  // C float4 per thread, 256 threads -> V = 1024*C
+__global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ tgt,
+                                                 T* __restrict__ dz, float* __restrict__ row_loss,
+                                                 int32_t* __restrict__ amax, int V, float inv_n, int* err) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const long n = blockIdx.x;
+  const float4* zr = reinterpret_cast<const float4*>(z + n * V);
+  float4 v[C];
+  float mx = -INFINITY;
+  int mi = 0x7fffffff;
+  bool bad = false;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int i4 = threadIdx.x + c * 256;
+    v[c] = zr[i4];
+    const float e[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bad |= !isfinite(e[k]);
+      if (e[k] > mx) { mx = e[k]; mi = 4 * i4 + k; }
+    }
+  }
+  blk_argmax(mx, mi, sv, si);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    v[c].x = __expf(v[c].x - mx); v[c].y = __expf(v[c].y - mx);
+    v[c].z = __expf(v[c].z - mx); v[c].w = __expf(v[c].w - mx);
+    s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+  }
+  s = blk_sum(s, sv);
+  const int y = tgt[n];
+  const bool yok = (y >= 0 && y < V);
+  const float inv = 1.f / s;
+  const float sc = inv * inv_n;
+  T* dr = dz + n * V;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int i4 = threadIdx.x + c * 256;
+    float4 p = make_float4(v[c].x * sc, v[c].y * sc, v[c].z * sc, v[c].w * sc);
+    if (yok && (y >> 2) == i4) {
+      const int k = y & 3;
+      if (k == 0) p.x -= inv_n; else if (k == 1) p.y -= inv_n; else if (k == 2) p.z -= inv_n; else p.w -= inv_n;
+    }
+    st4<T>(dr + 4 * i4, p);
+  }
+  if (threadIdx.x == 0) {
+    const float zy = yok ? z[n * V + y] : 0.f;
+    row_loss[n] = (mx + logf(s)) - zy;
+    amax[n] = mi;
+    if (!yok) atomicOr(err, 1);
+  }
+  if (bad) atomicOr(err, 2);
+}
+
+// any V: three passes over the row from memory
+template <typename T>
+__global__ void __launch_bounds__(256) ce_generic_kernel(const float* __restrict__ z, const int32_t* __restrict__ tgt,
+                                                         T* __restrict__ dz, float* __restrict__ row_loss,
+                                                         int32_t* __restrict__ amax, int V, float inv_n, int* err) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const long n = blockIdx.x;
+  const float* zr = z + n * V;
+  float mx = -INFINITY;
+  int mi = 0x7fffffff;
+  bool bad = false;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    const float e = zr[i];
+    bad |= !isfinite(e);
+    if (e > mx) { mx = e; mi = i; }
+  }
+  blk_argmax(mx, mi, sv, si);
+  float s = 0.f;
+  for (int i = threadIdx.x; i < V; i += 256) s += __expf(zr[i] - mx);
+  s = blk_sum(s, sv);
+  const int y = tgt[n];
+  const bool yok = (y >= 0 && y < V);
+  const float inv = 1.f / s;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    float p = __expf(zr[i] - mx) * inv * inv_n;
+    if (i == y) p -= inv_n;
+    st<T>(dz + n * V + i, p);
+  }
+  if (threadIdx.x == 0) {
+    row_loss[n] = (mx + logf(s)) - (yok ? zr[y] : 0.f);
+    amax[n] = mi;
+    if (!yok) atomicOr(err, 1);
+  }
+  if (bad) atomicOr(err, 2);
+}
+
+// deterministic sum of n floats into one double (one block, fixed order)
+__global__ void __launch_bounds__(256) sum_rows_kernel(const float* __restrict__ x, int n, double* out) {
+  __shared__ double sd[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) s += (double)x[i];
+  sd[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sd[threadIdx.x] += sd[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = sd[0];
+}
+
+// ---------------------------------------------------------------------------
+// deterministic embedding backward
+//   1 per-chunk histograms  table[p][v] (chunks of 1024 positions)
+//   2 per token: exclusive prefix over chunks, total count
+//   3 exclusive scan of counts over the vocabulary -> offsets
+//   4 stable fill: sorted[offsets[v] + table[p][v] + rank within chunk] = n
+//   5 segment sums: fixed segments of 64 sorted entries, one partial per run
+//   6 per token: sum its runs' partials in order (zero rows for absent ids)
+
+constexpr int SC_CHUNK = 1024;
+constexpr int SC_SEG = 64;
+
+__global__ void __launch_bounds__(SC_CHUNK) sc_hist_kernel(const int32_t* tok, int N, int V, int* table) {
+  const int n = blockIdx.x * SC_CHUNK + threadIdx.x;
+  if (n < N) {
+    const int t = tok[n];
+    if (t >= 0 && t < V) atomicAdd(&table[(long)blockIdx.x * V + t], 1);
+  }
+}
+
+__global__ void __launch_bounds__(256) sc_colscan_kernel(int* table, int P, int V, int* counts) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= V) return;
+  int run = 0;
+  for (int p = 0; p < P; ++p) {
+    const int c = table[(long)p * V + v];
+    table[(long)p * V + v] = run;
+    run += c;
+  }
+  counts[v] = run;
+}
+
+__global__ void __launch_bounds__(1024) sc_vscan_kernel(const int* counts, int V, int* offsets) {
+  __shared__ int part[1024];
+  const int per = (V + 1023) / 1024;
+  const int b = threadIdx.x * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < V) s += counts[b + i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of 1024 partial sums
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = (int)threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int i = 0; i < per; ++i)
+    if (b + i < V) { offsets[b + i] = run; run += counts[b + i]; }
+  if (threadIdx.x == 1023) offsets[V] = part[1023];
+}
+
+__global__ void __launch_bounds__(SC_CHUNK) sc_fill_kernel(const int32_t* tok, int N, int V, const int* table,
+                                                           const int* offsets, int* sorted) {
+  __shared__ int st_tok[SC_CHUNK];
+  const int base = blockIdx.x * SC_CHUNK;
+  const int n = base + threadIdx.x;
+  const int t = n < N ? tok[n] : -1;
+  st_tok[threadIdx.x] = t;
+  __syncthreads();
+  if (n >= N || t < 0 || t >= V) return;
+  int rank = 0;
+  for (int m = 0; m < (int)threadIdx.x; ++m) rank += (st_tok[m] == t);
+  sorted[offsets[t] + table[(long)blockIdx.x * V + t] + rank] = n;
+}
+
+// segments of SC_SEG sorted entries x column chunks of 256 floats (64 lanes x float4)
+__global__ void __launch_bounds__(64) sc_segsum_kernel(const int32_t* tok, const int* sorted, const int* nsorted_p,
+                                                       const float* dh, int d, float* partial) {
+  const int nsorted = *nsorted_p;  // positions with a valid id (the rest of sorted is unfilled)
+  const int s0 = blockIdx.x * SC_SEG;
+  const int c = blockIdx.y * 256 + threadIdx.x * 4;
+  const bool on = c < d;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int run_start = s0;
+  const int s1 = min(s0 + SC_SEG, nsorted);
+  for (int i = s0; i < s1; ++i) {
+    const int row = sorted[i];
+    if (on) {
+      const float4 x = *reinterpret_cast<const float4*>(dh + (long)row * d + c);
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    const bool last = (i + 1 == s1) || (tok[sorted[i + 1]] != tok[row]);
+    if (last) {
+      if (on) *reinterpret_cast<float4*>(partial + (long)run_start * d + c) = acc;
+      acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      run_start = i + 1;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64) sc_combine_kernel(const int* offsets, const float* partial, int d, float* dE) {
+  const int v = blockIdx.x;
+  const int c = blockIdx.y * 256 + threadIdx.x * 4;
+  if (c >= d) return;
+  const int b = offsets[v], e = offsets[v + 1];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (e > b) {
+    for (int s = b / SC_SEG; s <= (e - 1) / SC_SEG; ++s) {
+      const int start = max(b, s * SC_SEG);
+      const float4 x = *reinterpret_cast<const float4*>(partial + (long)start * d + c);
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+  }
+  *reinterpret_cast<float4*>(dE + (long)v * d + c) = acc;
+}
+
+// ---------------------------------------------------------------------------
+// misc
+
+template <typename T>
+__global__ void cast_kernel(const float* __restrict__ x, T* __restrict__ y, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    st<T>(y + i, x[i]);
+}
+
+__global__ void zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__device__ inline uint64_t splitmix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// counter-based N(0, std^2): SplitMix64 on (seed, stream, index) -> Box-Muller
+__global__ void fill_normal_kernel(float* w, size_t n, uint64_t seed, uint64_t sid, float stddev) {
+  const uint64_t key = splitmix64(seed ^ splitmix64(sid + 0x632BE59BD9B4E019ull));
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const uint64_t r1 = splitmix64(key + 2 * i), r2 = splitmix64(key + 2 * i + 1);
+    const double u1 = ((double)(r1 >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    const double u2 = (double)(r2 >> 11) * (1.0 / 9007199254740992.0);
+    w[i] = (float)(stddev * sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2));
+  }
+}
+
+__global__ void momentum_kernel(float* __restrict__ m, const float* __restrict__ g, float mu, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x, t = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t n4 = n / 4;
+  for (size_t i = t; i < n4; i += stride) {
+    float4 a = reinterpret_cast<float4*>(m)[i];
+    const float4 b = reinterpret_cast<const float4*>(g)[i];
+    a.x = mu * a.x + b.x; a.y = mu * a.y + b.y; a.z = mu * a.z + b.z; a.w = mu * a.w + b.w;
+    reinterpret_cast<float4*>(m)[i] = a;
+  }
+  for (size_t i = n4 * 4 + t; i < n; i += stride) m[i] = mu * m[i] + g[i];
+}
+
+__global__ void __launch_bounds__(256) sumsq_part_kernel(const float* __restrict__ x, const long* offs,
+                                                         const long* sizes, int parts, double* partial) {
+  __shared__ double sd[4];
+  const int mat = blockIdx.y, part = blockIdx.x;
+  const float* p = x + offs[mat];
+  const long n = sizes[mat];
+  const long per = (n + parts - 1) / parts;
+  const long b = part * per, e = min(n, b + per);
+  double s = 0.0;
+  for (long i = b + threadIdx.x; i < e; i += 256) {
+    const double v = p[i];
+    s += v * v;
+  }
+  s = wave_sum_d(s);
+  if ((threadIdx.x & 63) == 0) sd[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[(long)mat * parts + part] = (sd[0] + sd[1]) + (sd[2] + sd[3]);
+}
+
+__global__ void sumsq_final_kernel(const double* partial, int parts, int nmat, double* out) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= nmat) return;
+  double s = 0.0;
+  for (int k = 0; k < parts; ++k) s += partial[(long)m * parts + k];
+  out[m] = s;
+}
+
+// X = src / (sqrt(sumsq) + eps), written transposed ([cols][rows]) when asked; 32x32 LDS tiles
+template <typename T>
+__global__ void __launch_bounds__(256) ns_normalize_kernel(const float* __restrict__ src, const double* sumsq, int mat,
+                                                           float eps, int rows, int cols, int transpose,
+                                                           float* __restrict__ xf, T* __restrict__ xa) {
+  __shared__ float tile[32][33];
+  const float scale = (float)(1.0 / (sqrt(sumsq[mat]) + (double)eps));
+  const int tr = blockIdx.y * 32, tc = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  if (!transpose) {
+    for (int i = ty; i < 32; i += 8) {
+      const int r = tr + i, c = tc + tx;
+      if (r < rows && c < cols) {
+        const float v = src[(long)r * cols + c] * scale;
+        xf[(long)r * cols + c] = v;
+        st<T>(xa + (long)r * cols + c, v);
+      }
+    }
+    return;
+  }
+  for (int i = ty; i < 32; i += 8) {
+    const int r = tr + i, c = tc + tx;
+    tile[i][tx] = (r < rows && c < cols) ? src[(long)r * cols + c] * scale : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = tc + i, r = tr + tx;  // output row c, column r of the [cols][rows] matrix
+    if (r < rows && c < cols) {
+      const float v = tile[tx][i];
+      xf[(long)c * rows + r] = v;
+      st<T>(xa + (long)c * rows + r, v);
+    }
+  }
+}
+
+// W -= lr * X (X stored [cols][rows] when transposed); refresh the act copy of W
+template <typename T>
+__global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, T* __restrict__ wa,
+                                                         const float* __restrict__ x, float lr, int rows, int cols,
+                                                         int transposed) {
+  __shared__ float tile[32][33];
+  const int tr = blockIdx.y * 32, tc = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  if (transposed) {
+    for (int i = ty; i < 32; i += 8) {  // read X^T tile rows (columns of W)
+      const int c = tc + i, r = tr + tx;
+      tile[i][tx] = (r < rows && c < cols) ? x[(long)c * rows + r] : 0.f;
+    }
+    __syncthreads();
+  }
+  for (int i = ty; i < 32; i += 8) {
+    const int r = tr + i, c = tc + tx;
+    if (r < rows && c < cols) {
+      const float xv = transposed ? tile[tx][i] : x[(long)r * cols + c];
+      const float nw = w[(long)r * cols + c] - lr * xv;
+      w[(long)r * cols + c] = nw;
+      if (wa) st<T>(wa + (long)r * cols + c, nw);
+    }
+  }
+}
+
+inline int grid_for(size_t n, int block = 256, int cap = 65536) {
+  size_t g = (n + block - 1) / block;
+  if (g > (size_t)cap) g = cap;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+void launch_embed_gather(const int32_t* tok, const float* E, float* h, int N, int d, int V, int* err,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(embed_gather_kernel, dim3((N + 3) / 4), dim3(256), 0, st, tok, E, h, N, d, V, err);
+}
+
+void launch_rmsnorm_fwd(const float* x, void* y, int yt, float* rstd, int N, int d, float eps, hipStream_t st) {
+  dim3 g((N + 3) / 4), b(256);
+  if (yt == ACT_BF16)
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, g, b, 0, st, x, (bf16_t*)y, rstd, N, d, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, b, 0, st, x, (float*)y, rstd, N, d, eps);
+}
+
+void launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
+                        void* dxa, int at, int N, int d, float eps, hipStream_t st) {
+  (void)eps;
+  dim3 g((N + 3) / 4), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, g, b, 0, st, dy, x, rstd, dres, dx, (bf16_t*)dxa, N, d);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, b, 0, st, dy, x, rstd, dres, dx, (float*)dxa, N, d);
+}
+
+void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st) {
+  const int n = T * (hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, cs, T, hd, base);
+}
+
+void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float* rk, int B, int T, int H, int hd,
+                            float eps, hipStream_t st) {
+  const int N = B * T;
+  dim3 g((N * H * 2 + 3) / 4), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)qkv, cs, rq, rk, N, T, H, hd, eps);
+  else
+    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<float>, g, b, 0, st, (float*)qkv, cs, rq, rk, N, T, H, hd, eps);
+}
+
+void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs, const float* rq, const float* rk,
+                            int B, int T, int H, int hd, hipStream_t st) {
+  const int N = B * T;
+  dim3 g((N * H * 2 + 3) / 4), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(rope_qknorm_bwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N,
+                       T, H, hd);
+  else
+    hipLaunchKernelGGL(rope_qknorm_bwd_kernel<float>, g, b, 0, st, (float*)dqkv, (const float*)qkv, cs, rq, rk, N, T,
+                       H, hd);
+}
+
+template <typename T>
+static void ce_dispatch(const float* z, const int32_t* tgt, T* dz, float* rl, int32_t* am, int N, int V, float inv_n,
+                        int* err, hipStream_t st) {
+  dim3 g(N), b(256);
+  switch (V % 1024 == 0 ? V / 1024 : -1) {
+    case 1: hipLaunchKernelGGL((ce_kernel<T, 1>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    case 2: hipLaunchKernelGGL((ce_kernel<T, 2>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    case 4: hipLaunchKernelGGL((ce_kernel<T, 4>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    case 8: hipLaunchKernelGGL((ce_kernel<T, 8>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    case 16: hipLaunchKernelGGL((ce_kernel<T, 16>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    case 32: hipLaunchKernelGGL((ce_kernel<T, 32>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    default: hipLaunchKernelGGL(ce_generic_kernel<T>, g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+  }
+}
+
+void launch_cross_entropy(const float* z, const int32_t* tgt, void* dz, int at, float* rl, int32_t* am, int N, int V,
+                          float inv_n, int* err, hipStream_t st) {
+  if (N <= 0) return;
+  if (at == ACT_BF16)
+    ce_dispatch<bf16_t>(z, tgt, (bf16_t*)dz, rl, am, N, V, inv_n, err, st);
+  else
+    ce_dispatch<float>(z, tgt, (float*)dz, rl, am, N, V, inv_n, err, st);
+}
+
+void launch_sum_rows(const float* x, int n, double* out, hipStream_t st) {
+  hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, st, x, n, out);
+}
+
+static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t embed_ws_bytes(int N, int V, int d) {
+  const size_t P = (N + SC_CHUNK - 1) / SC_CHUNK;
+  return al256(P * (size_t)V * 4) + al256((size_t)V * 4) + al256(((size_t)V + 1) * 4) + al256((size_t)N * 4) +
+         al256((size_t)N * d * 4);
+}
+
+void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws,
+                          int32_t* sorted_out, hipStream_t st) {
+  const int P = (N + SC_CHUNK - 1) / SC_CHUNK;
+  char* w = (char*)ws;
+  int* table = (int*)w; w += al256((size_t)P * V * 4);
+  int* counts = (int*)w; w += al256((size_t)V * 4);
+  int* offsets = (int*)w; w += al256(((size_t)V + 1) * 4);
+  int* sorted = (int*)w; w += al256((size_t)N * 4);
+  float* partial = (float*)w;
+  if (sorted_out) sorted = sorted_out;
+  launch_zero(table, (size_t)P * V * 4, st);
+  if (N > 0) hipLaunchKernelGGL(sc_hist_kernel, dim3(P), dim3(SC_CHUNK), 0, st, tok, N, V, table);
+  hipLaunchKernelGGL(sc_colscan_kernel, dim3((V + 255) / 256), dim3(256), 0, st, table, P, V, counts);
+  hipLaunchKernelGGL(sc_vscan_kernel, dim3(1), dim3(1024), 0, st, counts, V, offsets);
+  if (N > 0) {
+    hipLaunchKernelGGL(sc_fill_kernel, dim3(P), dim3(SC_CHUNK), 0, st, tok, N, V, table, offsets, sorted);
+    // every valid position has a slot; out-of-range ids were rejected by the gather
+    hipLaunchKernelGGL(sc_segsum_kernel, dim3((N + SC_SEG - 1) / SC_SEG, (d + 255) / 256), dim3(64), 0, st, tok,
+                       sorted, offsets + V, dh, d, partial);
+  }
+  hipLaunchKernelGGL(sc_combine_kernel, dim3(V, (d + 255) / 256), dim3(64), 0, st, offsets, partial, d, dE);
+}
+
+void launch_cast_f32_to_act(const float* x, void* y, int at, size_t n, hipStream_t st) {
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, st, x, (bf16_t*)y, n);
+  else
+    hipLaunchKernelGGL(cast_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, x, (float*)y, n);
+}
+
+void launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;  // callers pass multiples of 4 bytes
+  if (n) hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n)), dim3(256), 0, st, (uint32_t*)p, n);
+}
+
+void launch_fill_normal(float* w, size_t n, uint64_t seed, uint64_t sid, float stddev, hipStream_t st) {
+  hipLaunchKernelGGL(fill_normal_kernel, dim3(grid_for(n)), dim3(256), 0, st, w, n, seed, sid, stddev);
+}
+
+void launch_momentum(float* m, const float* g, float mu, size_t n, hipStream_t st) {
+  hipLaunchKernelGGL(momentum_kernel, dim3(grid_for(n / 4 + 1)), dim3(256), 0, st, m, g, mu, n);
+}
+
+void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, int nmat, double* partial, int parts,
+                         double* out, hipStream_t st) {
+  hipLaunchKernelGGL(sumsq_part_kernel, dim3(parts, nmat), dim3(256), 0, st, x, offs, sizes, parts, partial);
+  hipLaunchKernelGGL(sumsq_final_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, partial, parts, nmat, out);
+}
+
+void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols, bool tr,
+                         float* xf, void* xa, int at, hipStream_t st) {
+  dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(ns_normalize_kernel<bf16_t>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
+                       (bf16_t*)xa);
+  else
+    hipLaunchKernelGGL(ns_normalize_kernel<float>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
+                       (float*)xa);
+}
+
+void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int rows, int cols, bool tr,
+                       hipStream_t st) {
+  dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(muon_apply_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, rows, cols, (int)tr);
+  else
+    hipLaunchKernelGGL(muon_apply_kernel<float>, g, b, 0, st, w, (float*)wa, x, lr, rows, cols, (int)tr);
+}

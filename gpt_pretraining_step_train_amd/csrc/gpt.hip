@@ -1,0 +1,861 @@
+// C ABI of the GPT training step: configuration, arena carving, the forward /
+// backward launch sequence of gpt_step, Muon, and the kernel-level entry points.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "common.h"
+#include "kernels.h"
+
+// Polar Express table: the first two (a, b, c) are the ones the nanochat article
+// prints (section "2. Muon Optimize Edici"); the last three are this library's
+// reading of the elided rows: each is the odd quintic minimising max|1 - p(x)| on
+// the interval the singular values occupy after the previous steps, starting from
+// [1e-3, 1] (images [0.033,1.966] -> [0.131,1.869] -> [0.432,1.568] -> [0.871,1.129]).
+static const float kNsCoeffs[5][3] = {
+    {8.156f, -22.483f, 15.879f},
+    {4.043f, -2.809f, 0.500f},
+    {3.982259f, -2.970419f, 0.565428f},
+    {3.335152f, -2.500954f, 0.511463f},
+    {2.315355f, -1.682066f, 0.420231f},
+};
+
+namespace {
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  size_t total = 0;
+  size_t add(size_t bytes) {
+    const size_t o = total;
+    total += al256(bytes);
+    return o;
+  }
+};
+
+// element offsets of the six block matrices inside one layer's slice
+struct LayerOffs {
+  size_t q, k, v, o, w1, w2, stride;
+};
+inline LayerOffs layer_offs(const gpt_cfg& c) {
+  const size_t d = c.d_model, F = c.d_ff;
+  LayerOffs L;
+  L.q = 0; L.k = d * d; L.v = 2 * d * d; L.o = 3 * d * d; L.w1 = 4 * d * d; L.w2 = 4 * d * d + F * d;
+  L.stride = 4 * d * d + 2 * d * F;
+  return L;
+}
+
+struct Offsets {
+  size_t params, grads, mom, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
+      dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, Af,
+      Aa, Ba, ss_part, ss, mat_off, mat_size, rope, loss, err;
+  size_t splitws_bytes;
+};
+
+constexpr int kSumsqParts = 64;
+
+int act_of(const gpt_cfg& c) { return c.precision == GPT_FP32 ? ACT_F32 : ACT_BF16; }
+
+size_t wgrad_ws_bytes(const gpt_cfg& c) {
+  const int N = c.batch * c.seq_len, d = c.d_model, F = c.d_ff, V = c.vocab;
+  const int shapes[5][2] = {{d, F}, {F, d}, {d, d}, {3 * d, d}, {V, d}};
+  size_t best = 0;
+  for (auto& s : shapes) {
+    GemmArgs p;
+    p.M = s[0]; p.N = s[1]; p.K = N; p.dtype = act_of(c); p.a_kmaj = false; p.b_kmaj = false;
+    const int sp = gemm_auto_splits(p);
+    if (sp > 1) best = std::max(best, (size_t)sp * s[0] * s[1] * 4);
+  }
+  return best;
+}
+
+Offsets plan(const gpt_cfg& c, size_t* total) {
+  Plan P;
+  Offsets O;
+  const size_t N = (size_t)c.batch * c.seq_len, d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth;
+  const size_t H = c.n_head, T = c.seq_len, B = c.batch;
+  const size_t es = act_of(c) == ACT_BF16 ? 2 : 4;
+  const size_t nE = V * d, nU = V * d, nBlk = L * layer_offs(c).stride;
+  const size_t s = std::min(d, F), l = std::max(d, F);
+  O.params = P.add((nE + nBlk + nU) * 4);
+  O.grads = P.add((nE + nBlk + nU) * 4);
+  O.mom = P.add(nBlk * 4);
+  O.wact = es == 2 ? P.add(nBlk * es) : 0;
+  O.uact = es == 2 ? P.add(nU * es) : 0;
+  O.hs = P.add((2 * L + 1) * N * d * 4);
+  O.a = P.add(L * N * d * es);
+  O.rstd_a = P.add(L * N * 4);
+  O.qkv = P.add(L * N * 3 * d * es);
+  O.rq = P.add(L * N * H * 4);
+  O.rk = P.add(L * N * H * 4);
+  O.o = P.add(L * N * d * es);
+  O.lse = P.add(L * B * H * T * 4);
+  O.m = P.add(L * N * d * es);
+  O.rstd_m = P.add(L * N * 4);
+  O.u = P.add(L * N * F * es);
+  O.g = P.add(L * N * F * es);
+  O.r = P.add(N * d * es);
+  O.rstd_f = P.add(N * 4);
+  O.logits = P.add(N * V * 4);
+  O.dlogits = P.add(N * V * es);
+  O.row_loss = P.add(N * 4);
+  O.argmax = P.add(N * 4);
+  O.dh0 = P.add(N * d * 4);
+  O.dh1 = P.add(N * d * 4);
+  O.dh_act = P.add(N * d * es);
+  O.dtmp = P.add(N * d * 4);
+  O.dbig = P.add(N * F * es);
+  O.dqkv = P.add(N * 3 * d * es);
+  O.do_act = P.add(N * d * es);
+  O.Dbuf = P.add(B * H * T * 4);
+  O.splitws_bytes = wgrad_ws_bytes(c);
+  O.splitws = P.add(std::max<size_t>(O.splitws_bytes, 256));
+  O.embws = P.add(embed_ws_bytes((int)N, (int)V, (int)d));
+  O.xf = P.add(nBlk * 4);
+  O.xa0 = P.add(nBlk * es);
+  O.xa1 = P.add(nBlk * es);
+  O.Af = P.add(std::max(4 * L * d * d, 2 * L * s * s) * 4);
+  O.Aa = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
+  O.Ba = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
+  (void)l;
+  O.ss_part = P.add(6 * L * kSumsqParts * 8);
+  O.ss = P.add(6 * L * 8);
+  O.mat_off = P.add(6 * L * 8);
+  O.mat_size = P.add(6 * L * 8);
+  O.rope = P.add(T * (c.head_dim / 2) * 2 * 4);
+  O.loss = P.add(8);
+  O.err = P.add(16);
+  *total = P.total;
+  return O;
+}
+
+}  // namespace
+
+struct gpt_model {
+  gpt_cfg cfg;
+  Offsets off;
+  char* base = nullptr;
+  size_t bytes = 0;
+  int at = ACT_BF16;
+  size_t es = 2;
+  int N = 0;
+  size_t nE = 0, nBlk = 0, nU = 0;
+  LayerOffs lo;
+  int last_status = GPT_OK;
+  bool stepped = false;
+  // matrix table for Muon, in layer order (q, k, v, o, w1, w2)
+  std::vector<long> moff, msize;
+  // profiling
+  std::string prof_name;
+  std::vector<hipEvent_t> ev;
+  std::vector<double> evflops;
+  size_t ev_used = 0;
+
+  template <typename T>
+  T* at_off(size_t o) { return reinterpret_cast<T*>(base + o); }
+  float* params() { return at_off<float>(off.params); }
+  float* grads() { return at_off<float>(off.grads); }
+  float* blk(float* region) { return region + nE; }
+  char* act(size_t o, size_t elems) { return base + o + elems * es; }
+  // act-typed copies of the block matrices and of U (the fp32 masters in fp32 mode)
+  void* wact(size_t elem) {
+    return at == ACT_BF16 ? (void*)(base + off.wact + elem * 2) : (void*)(blk(params()) + elem);
+  }
+  void* uact() { return at == ACT_BF16 ? (void*)(base + off.uact) : (void*)(params() + nE + nBlk); }
+};
+
+namespace {
+
+int run_gemm(gpt_model* M, GemmArgs p, hipStream_t st, bool allow_split) {
+  p.dtype = M->at;
+  if (allow_split) {
+    p.splits = gemm_auto_splits(p);
+    p.ws = M->at_off<float>(M->off.splitws);
+    p.ws_bytes = M->off.splitws_bytes;
+    if ((size_t)p.splits * p.batch * p.M * p.N * 4 > p.ws_bytes) p.splits = 1;
+  } else {
+    p.splits = 1;
+  }
+  const bool prof = !M->prof_name.empty() && M->prof_name == gemm_kernel_name(p);
+  if (prof) {
+    if (M->ev_used + 2 > M->ev.size()) {
+      for (int i = 0; i < 64; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return GPT_ERR_HIP;
+        M->ev.push_back(e);
+      }
+      M->evflops.resize(M->ev.size() / 2 + 1);
+    }
+    (void)hipEventRecord(M->ev[M->ev_used], st);
+  }
+  const int rc = launch_gemm(p, st);
+  if (prof) {
+    (void)hipEventRecord(M->ev[M->ev_used + 1], st);
+    M->evflops[M->ev_used / 2] = 2.0 * p.M * p.N * (double)p.K * p.batch;
+    M->ev_used += 2;
+  }
+  return rc ? GPT_ERR_SHAPE : GPT_OK;
+}
+
+bool same_shape(const gpt_cfg& a, const gpt_cfg& b) {
+  return a.depth == b.depth && a.d_model == b.d_model && a.n_head == b.n_head && a.head_dim == b.head_dim &&
+         a.d_ff == b.d_ff && a.vocab == b.vocab && a.seq_len == b.seq_len && a.batch == b.batch &&
+         a.precision == b.precision;
+}
+
+// element offset of tensor id inside the parameter/gradient vector, and its shape
+bool tensor_loc(const gpt_cfg& c, int id, size_t* off, int* rows, int* cols) {
+  const size_t d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth;
+  const LayerOffs lo = layer_offs(c);
+  if (id == 0) { *off = 0; *rows = (int)V; *cols = (int)d; return true; }
+  if (id == (int)(1 + 6 * L)) { *off = V * d + L * lo.stride; *rows = (int)V; *cols = (int)d; return true; }
+  if (id < 1 || id > (int)(6 * L)) return false;
+  const int l = (id - 1) / 6, j = (id - 1) % 6;
+  const size_t b = V * d + l * lo.stride;
+  const size_t o6[6] = {lo.q, lo.k, lo.v, lo.o, lo.w1, lo.w2};
+  *off = b + o6[j];
+  *rows = j == 4 ? (int)F : (int)d;
+  *cols = j == 5 ? (int)F : (int)d;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
+  if (!out || depth < 1 || depth > 64) return GPT_ERR_ARG;
+  memset(out, 0, sizeof(*out));
+  int d = 64 * depth;
+  d = (d + 127) / 128 * 128;
+  out->depth = depth;
+  out->d_model = d;
+  out->head_dim = 128;
+  out->n_head = d / 128;
+  out->d_ff = 4 * d;
+  out->vocab = 32768;
+  out->seq_len = 2048;
+  out->batch = 16;
+  out->precision = GPT_BF16;
+  out->init_std = 0.02f;
+  out->rope_base = 10000.f;
+  out->norm_eps = 1e-6f;
+  out->muon_momentum = 0.95f;
+  out->ns_steps = 5;
+  memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
+  const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
+  out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
+  return GPT_OK;
+}
+
+int gpt_cfg_validate(const gpt_cfg* c) {
+  if (!c) return GPT_ERR_ARG;
+  if (c->depth < 1 || c->d_model < 8 || c->n_head < 1 || c->d_ff < 8 || c->vocab < 8 || c->seq_len < 1 ||
+      c->batch < 1)
+    return GPT_ERR_SHAPE;
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return GPT_ERR_UNSUPPORTED;
+  if (c->n_head * c->head_dim != c->d_model) return GPT_ERR_SHAPE;
+  if (c->d_model % 8 || c->d_ff % 8 || c->vocab % 8) return GPT_ERR_SHAPE;
+  if (c->d_model > 2048) return GPT_ERR_UNSUPPORTED;
+  if (((long)c->batch * c->seq_len) % 8) return GPT_ERR_SHAPE;
+  if ((long)c->batch * c->seq_len > (1L << 30) / 4) return GPT_ERR_UNSUPPORTED;
+  if (c->precision != GPT_FP32 && c->precision != GPT_BF16) return GPT_ERR_UNSUPPORTED;
+  if (c->ns_steps < 0 || c->ns_steps > 5) return GPT_ERR_ARG;
+  if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
+  return GPT_OK;
+}
+
+size_t gpt_state_bytes(const gpt_cfg* c) {
+  if (gpt_cfg_validate(c) != GPT_OK) return 0;
+  size_t total = 0;
+  plan(*c, &total);
+  return total;
+}
+
+int gpt_tensor_count(const gpt_cfg* c) { return c ? 2 + 6 * c->depth : 0; }
+
+int gpt_tensor_shape(const gpt_cfg* c, int32_t id, int32_t* rows, int32_t* cols) {
+  if (!c || !rows || !cols) return GPT_ERR_ARG;
+  size_t off;
+  int r, k;
+  if (!tensor_loc(*c, id, &off, &r, &k)) return GPT_ERR_ARG;
+  *rows = r;
+  *cols = k;
+  return GPT_OK;
+}
+
+const char* gpt_status_str(int s) {
+  switch (s) {
+    case GPT_OK: return "ok";
+    case GPT_ERR_ARG: return "invalid argument";
+    case GPT_ERR_SHAPE: return "shape mismatch";
+    case GPT_ERR_TOKEN_RANGE: return "token id out of range";
+    case GPT_ERR_NONFINITE: return "non-finite logits";
+    case GPT_ERR_HIP: return "HIP runtime error";
+    case GPT_ERR_UNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+  }
+}
+
+int gpt_last_status(const gpt_model* m) { return m ? m->last_status : GPT_ERR_ARG; }
+
+static void refresh_act(gpt_model* M, hipStream_t st) {
+  if (M->at != ACT_BF16) return;
+  launch_cast_f32_to_act(M->blk(M->params()), M->wact(0), M->at, M->nBlk, st);
+  launch_cast_f32_to_act(M->params() + M->nE + M->nBlk, M->uact(), M->at, M->nU, st);
+}
+
+int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes, void* stream, gpt_model** out) {
+  if (!out) return GPT_ERR_ARG;
+  *out = nullptr;
+  int rc = gpt_cfg_validate(cfg);
+  if (rc) return rc;
+  if (!arena || ((uintptr_t)arena & 255)) return GPT_ERR_ARG;
+  size_t need = 0;
+  Offsets O = plan(*cfg, &need);
+  if (arena_bytes < need) return GPT_ERR_ARG;
+  gpt_model* M = new (std::nothrow) gpt_model();
+  if (!M) return GPT_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  M->cfg = *cfg;
+  M->off = O;
+  M->base = (char*)arena;
+  M->bytes = arena_bytes;
+  M->at = act_of(*cfg);
+  M->es = M->at == ACT_BF16 ? 2 : 4;
+  M->N = cfg->batch * cfg->seq_len;
+  M->lo = layer_offs(*cfg);
+  M->nE = (size_t)cfg->vocab * cfg->d_model;
+  M->nU = M->nE;
+  M->nBlk = (size_t)cfg->depth * M->lo.stride;
+  const int L = cfg->depth, d = cfg->d_model, F = cfg->d_ff;
+  for (int l = 0; l < L; ++l) {
+    const size_t b = (size_t)l * M->lo.stride;
+    const size_t o6[6] = {M->lo.q, M->lo.k, M->lo.v, M->lo.o, M->lo.w1, M->lo.w2};
+    for (int j = 0; j < 6; ++j) {
+      M->moff.push_back((long)(b + o6[j]));
+      M->msize.push_back(j < 4 ? (long)d * d : (long)d * F);
+    }
+  }
+  // weights: one counter-based stream per tensor id
+  const int nt = 2 + 6 * L;
+  for (int id = 0; id < nt; ++id) {
+    size_t off;
+    int r, c;
+    tensor_loc(*cfg, id, &off, &r, &c);
+    const int j = (id >= 1 && id <= 6 * L) ? (id - 1) % 6 : -1;
+    const float sd = cfg->init_std * ((j == 3 || j == 5) ? 1.f / sqrtf(2.f * L) : 1.f);
+    launch_fill_normal(M->params() + off, (size_t)r * c, seed, (uint64_t)id, sd, st);
+  }
+  launch_zero(M->at_off<float>(O.mom), M->nBlk * 4, st);
+  launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU) * 4, st);
+  refresh_act(M, st);
+  launch_rope_table(M->at_off<float>(O.rope), cfg->seq_len, cfg->head_dim, cfg->rope_base, st);
+  if (hipMemcpyAsync(M->at_off<long>(O.mat_off), M->moff.data(), M->moff.size() * 8, hipMemcpyHostToDevice, st) !=
+          hipSuccess ||
+      hipMemcpyAsync(M->at_off<long>(O.mat_size), M->msize.data(), M->msize.size() * 8, hipMemcpyHostToDevice,
+                     st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    delete M;
+    return GPT_ERR_HIP;
+  }
+  if (hipGetLastError() != hipSuccess) {
+    delete M;
+    return GPT_ERR_HIP;
+  }
+  *out = M;
+  return GPT_OK;
+}
+
+void gpt_free(gpt_model* M) {
+  if (!M) return;
+  for (auto e : M->ev) (void)hipEventDestroy(e);
+  delete M;
+}
+
+static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, hipStream_t st) {
+  const gpt_cfg& c = M->cfg;
+  const int N = M->N, d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth, H = c.n_head, hd = c.head_dim;
+  const int B = c.batch, T = c.seq_len;
+  const int at = M->at;
+  const size_t es = M->es;
+  const Offsets& O = M->off;
+  float* hs = M->at_off<float>(O.hs);
+  float* grads = M->grads();
+  float* gblk = M->blk(grads);
+  int* err = M->at_off<int>(O.err);
+  const float eps = c.norm_eps;
+  auto actp = [&](size_t o, size_t elems) -> void* { return M->base + o + elems * es; };
+  auto hsl = [&](int i) { return hs + (size_t)i * N * d; };
+  int rc;
+
+  launch_zero(err, 16, st);
+  launch_embed_gather(tok, M->params(), hsl(0), N, d, V, err, st);
+  for (int l = 0; l < L; ++l) {
+    const size_t wl = (size_t)l * M->lo.stride;
+    void* a = actp(O.a, (size_t)l * N * d);
+    void* qkv = actp(O.qkv, (size_t)l * N * 3 * d);
+    void* o = actp(O.o, (size_t)l * N * d);
+    void* m = actp(O.m, (size_t)l * N * d);
+    void* u = actp(O.u, (size_t)l * N * F);
+    void* g = actp(O.g, (size_t)l * N * F);
+    float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
+    float* rk = M->at_off<float>(O.rk) + (size_t)l * N * H;
+    float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
+    launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
+    {
+      GemmArgs p;
+      p.M = N; p.N = 3 * d; p.K = d;
+      p.A = a; p.lda = d; p.B = M->wact(wl + M->lo.q); p.ldb = d;
+      p.outA = qkv; p.ldoa = 3 * d;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, eps, st);
+    launch_attn_fwd(qkv, o, lse, at, B, T, H, hd, st);
+    {
+      GemmArgs p;
+      p.M = N; p.N = d; p.K = d;
+      p.A = o; p.lda = d; p.B = M->wact(wl + M->lo.o); p.ldb = d;
+      p.Cin = hsl(2 * l); p.ldcin = d; p.beta = 1.f;
+      p.outF = hsl(2 * l + 1); p.ldo = d;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    launch_rmsnorm_fwd(hsl(2 * l + 1), m, at, M->at_off<float>(O.rstd_m) + (size_t)l * N, N, d, eps, st);
+    {
+      GemmArgs p;
+      p.M = N; p.N = F; p.K = d;
+      p.A = m; p.lda = d; p.B = M->wact(wl + M->lo.w1); p.ldb = d;
+      p.epi = EPI_RELU2; p.outA = u; p.out2 = g; p.ldoa = F;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    {
+      GemmArgs p;
+      p.M = N; p.N = d; p.K = F;
+      p.A = g; p.lda = F; p.B = M->wact(wl + M->lo.w2); p.ldb = F;
+      p.Cin = hsl(2 * l + 1); p.ldcin = d; p.beta = 1.f;
+      p.outF = hsl(2 * l + 2); p.ldo = d;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+  }
+  void* r = M->base + O.r;
+  launch_rmsnorm_fwd(hsl(2 * L), r, at, M->at_off<float>(O.rstd_f), N, d, eps, st);
+  float* logits = M->at_off<float>(O.logits);
+  void* dlogits = M->base + O.dlogits;
+  {
+    GemmArgs p;
+    p.M = N; p.N = V; p.K = d;
+    p.A = r; p.lda = d; p.B = M->uact(); p.ldb = d;
+    p.outF = logits; p.ldo = V;
+    if ((rc = run_gemm(M, p, st, false))) return rc;
+  }
+  launch_cross_entropy(logits, tgt, dlogits, at, M->at_off<float>(O.row_loss), M->at_off<int32_t>(O.argmax), N, V,
+                       1.f / (float)N, err, st);
+  launch_sum_rows(M->at_off<float>(O.row_loss), N, M->at_off<double>(O.loss), st);
+
+  // ---------------- backward
+  float* dtmp = M->at_off<float>(O.dtmp);
+  float* dh[2] = {M->at_off<float>(O.dh0), M->at_off<float>(O.dh1)};
+  void* dh_act = M->base + O.dh_act;
+  void* dbig = M->base + O.dbig;
+  void* dqkv = M->base + O.dqkv;
+  void* do_act = M->base + O.do_act;
+  {
+    GemmArgs p;  // dr = dz U
+    p.M = N; p.N = d; p.K = V;
+    p.A = dlogits; p.lda = V; p.B = M->uact(); p.ldb = d; p.b_kmaj = false;
+    p.outF = dtmp; p.ldo = d;
+    if ((rc = run_gemm(M, p, st, false))) return rc;
+  }
+  {
+    GemmArgs p;  // dU = dz^T r
+    p.M = V; p.N = d; p.K = N;
+    p.A = dlogits; p.lda = V; p.a_kmaj = false; p.B = r; p.ldb = d; p.b_kmaj = false;
+    p.outF = grads + M->nE + M->nBlk; p.ldo = d;
+    if ((rc = run_gemm(M, p, st, true))) return rc;
+  }
+  launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps, st);
+  int cur = 0;
+  for (int l = L - 1; l >= 0; --l) {
+    const size_t wl = (size_t)l * M->lo.stride;
+    void* a = actp(O.a, (size_t)l * N * d);
+    void* qkv = actp(O.qkv, (size_t)l * N * 3 * d);
+    void* o = actp(O.o, (size_t)l * N * d);
+    void* m = actp(O.m, (size_t)l * N * d);
+    void* u = actp(O.u, (size_t)l * N * F);
+    void* g = actp(O.g, (size_t)l * N * F);
+    float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
+    float* rk = M->at_off<float>(O.rk) + (size_t)l * N * H;
+    float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
+    {
+      GemmArgs p;  // dW2 = dY^T g
+      p.M = d; p.N = F; p.K = N;
+      p.A = dh_act; p.lda = d; p.a_kmaj = false; p.B = g; p.ldb = F; p.b_kmaj = false;
+      p.outF = gblk + wl + M->lo.w2; p.ldo = F;
+      if ((rc = run_gemm(M, p, st, true))) return rc;
+    }
+    {
+      GemmArgs p;  // du = (dY W2) * 2 relu(u)
+      p.M = N; p.N = F; p.K = d;
+      p.A = dh_act; p.lda = d; p.B = M->wact(wl + M->lo.w2); p.ldb = F; p.b_kmaj = false;
+      p.epi = EPI_DRELU2; p.aux = u; p.outA = dbig; p.ldoa = F;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    {
+      GemmArgs p;  // dW1 = du^T m
+      p.M = F; p.N = d; p.K = N;
+      p.A = dbig; p.lda = F; p.a_kmaj = false; p.B = m; p.ldb = d; p.b_kmaj = false;
+      p.outF = gblk + wl + M->lo.w1; p.ldo = d;
+      if ((rc = run_gemm(M, p, st, true))) return rc;
+    }
+    {
+      GemmArgs p;  // dm = du W1
+      p.M = N; p.N = d; p.K = F;
+      p.A = dbig; p.lda = F; p.B = M->wact(wl + M->lo.w1); p.ldb = d; p.b_kmaj = false;
+      p.outF = dtmp; p.ldo = d;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur], dh[cur ^ 1],
+                       dh_act, at, N, d, eps, st);
+    cur ^= 1;
+    {
+      GemmArgs p;  // dWo = dY^T o
+      p.M = d; p.N = d; p.K = N;
+      p.A = dh_act; p.lda = d; p.a_kmaj = false; p.B = o; p.ldb = d; p.b_kmaj = false;
+      p.outF = gblk + wl + M->lo.o; p.ldo = d;
+      if ((rc = run_gemm(M, p, st, true))) return rc;
+    }
+    {
+      GemmArgs p;  // do = dY Wo
+      p.M = N; p.N = d; p.K = d;
+      p.A = dh_act; p.lda = d; p.B = M->wact(wl + M->lo.o); p.ldb = d; p.b_kmaj = false;
+      p.outA = do_act; p.ldoa = d;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, hd, st);
+    launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, st);
+    {
+      GemmArgs p;  // dWqkv = dqkv^T a
+      p.M = 3 * d; p.N = d; p.K = N;
+      p.A = dqkv; p.lda = 3 * d; p.a_kmaj = false; p.B = a; p.ldb = d; p.b_kmaj = false;
+      p.outF = gblk + wl + M->lo.q; p.ldo = d;
+      if ((rc = run_gemm(M, p, st, true))) return rc;
+    }
+    {
+      GemmArgs p;  // da = dqkv Wqkv
+      p.M = N; p.N = d; p.K = 3 * d;
+      p.A = dqkv; p.lda = 3 * d; p.B = M->wact(wl + M->lo.q); p.ldb = d; p.b_kmaj = false;
+      p.outF = dtmp; p.ldo = d;
+      if ((rc = run_gemm(M, p, st, false))) return rc;
+    }
+    launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur], dh[cur ^ 1], dh_act,
+                       at, N, d, eps, st);
+    cur ^= 1;
+  }
+  launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st);
+  return GPT_OK;
+}
+
+float gpt_step(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg, void* stream) {
+  if (!M) return NAN;
+  if (!tok || !tgt) { M->last_status = GPT_ERR_ARG; return NAN; }
+  if (cfg && !same_shape(*cfg, M->cfg)) { M->last_status = GPT_ERR_SHAPE; return NAN; }
+  hipStream_t st = (hipStream_t)stream;
+  int rc = forward_backward(M, tok, tgt, st);
+  if (rc) { M->last_status = rc; return NAN; }
+  struct { double loss; int err[4]; } h;
+  if (hipGetLastError() != hipSuccess ||
+      hipMemcpyAsync(&h.loss, M->base + M->off.loss, 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(h.err, M->base + M->off.err, 16, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    M->last_status = GPT_ERR_HIP;
+    return NAN;
+  }
+  M->stepped = true;
+  if (h.err[0] & 1) { M->last_status = GPT_ERR_TOKEN_RANGE; return NAN; }
+  if (h.err[0] & 2) { M->last_status = GPT_ERR_NONFINITE; return NAN; }
+  M->last_status = GPT_OK;
+  return (float)(h.loss / (double)M->N);
+}
+
+int muon_update(gpt_model* M, float lr, void* stream) {
+  if (!M) return GPT_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const gpt_cfg& c = M->cfg;
+  const Offsets& O = M->off;
+  const int L = c.depth, d = c.d_model, F = c.d_ff;
+  const int s = std::min(d, F), lw = std::max(d, F);
+  float* mom = M->at_off<float>(O.mom);
+  float* xf = M->at_off<float>(O.xf);
+  char* xa[2] = {M->base + O.xa0, M->base + O.xa1};
+  const size_t es = M->es;
+  launch_momentum(mom, M->blk(M->grads()), c.muon_momentum, M->nBlk, st);
+  launch_matrix_sumsq(mom, M->at_off<long>(O.mat_off), M->at_off<long>(O.mat_size), 6 * L,
+                      M->at_off<double>(O.ss_part), kSumsqParts, M->at_off<double>(O.ss), st);
+  // X0 into the NS workspace: squares first (q, k, v, o of each layer), then the
+  // d x F pairs, every matrix in its wide orientation
+  auto xdst = [&](int l, int j) -> size_t {
+    if (j < 4) return (size_t)(4 * l + j) * d * d;
+    return (size_t)4 * L * d * d + (size_t)(2 * l + (j - 4)) * s * lw;
+  };
+  auto transposed = [&](int j) { return (j == 4 && F > d) || (j == 5 && d > F); };
+  for (int l = 0; l < L; ++l)
+    for (int j = 0; j < 6; ++j) {
+      const int rows = j == 4 ? F : d, cols = j == 5 ? F : d;
+      const size_t dst = xdst(l, j);
+      launch_ns_normalize(mom + M->moff[6 * l + j], M->at_off<double>(O.ss), 6 * l + j, 1e-7f, rows, cols,
+                          transposed(j), xf + dst, xa[0] + dst * es, M->at, st);
+    }
+  struct Batch { int s, l, nb; size_t off; };
+  const Batch batches[2] = {{d, d, 4 * L, 0}, {s, lw, 2 * L, (size_t)4 * L * d * d}};
+  float* Af = M->at_off<float>(O.Af);
+  void* Aa = M->base + O.Aa;
+  void* Ba = M->base + O.Ba;
+  int rc;
+  for (const Batch& bt : batches) {
+    int cur = 0;
+    const long ss = (long)bt.s * bt.s, sl = (long)bt.s * bt.l;
+    for (int it = 0; it < c.ns_steps; ++it) {
+      const float a = c.ns_coeffs[it][0], b = c.ns_coeffs[it][1], cc = c.ns_coeffs[it][2];
+      {
+        GemmArgs p;  // A = X X^T
+        p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
+        p.A = xa[cur] + bt.off * es; p.lda = bt.l; p.strideA = sl;
+        p.B = xa[cur] + bt.off * es; p.ldb = bt.l; p.strideB = sl;
+        p.outF = Af; p.ldo = bt.s; p.strideO = ss;
+        p.outA = Aa; p.ldoa = bt.s; p.strideOA = ss;
+        if ((rc = run_gemm(M, p, st, false))) return rc;
+      }
+      {
+        GemmArgs p;  // Bm = b A + c A A   (A symmetric)
+        p.M = bt.s; p.N = bt.s; p.K = bt.s; p.batch = bt.nb;
+        p.A = Aa; p.lda = bt.s; p.strideA = ss;
+        p.B = Aa; p.ldb = bt.s; p.strideB = ss;
+        p.alpha = cc; p.beta = b; p.Cin = Af; p.ldcin = bt.s; p.strideCin = ss;
+        p.outA = Ba; p.ldoa = bt.s; p.strideOA = ss;
+        if ((rc = run_gemm(M, p, st, false))) return rc;
+      }
+      {
+        GemmArgs p;  // X <- a X + Bm X
+        p.M = bt.s; p.N = bt.l; p.K = bt.s; p.batch = bt.nb;
+        p.A = Ba; p.lda = bt.s; p.strideA = ss;
+        p.B = xa[cur] + bt.off * es; p.ldb = bt.l; p.strideB = sl; p.b_kmaj = false;
+        p.beta = a; p.Cin = xf + bt.off; p.ldcin = bt.l; p.strideCin = sl;
+        p.outF = xf + bt.off; p.ldo = bt.l; p.strideO = sl;
+        p.outA = xa[cur ^ 1] + bt.off * es; p.ldoa = bt.l; p.strideOA = sl;
+        if ((rc = run_gemm(M, p, st, false))) return rc;
+      }
+      cur ^= 1;
+    }
+  }
+  float* wblk = M->blk(M->params());
+  for (int l = 0; l < L; ++l)
+    for (int j = 0; j < 6; ++j) {
+      const int rows = j == 4 ? F : d, cols = j == 5 ? F : d;
+      const size_t mo = M->moff[6 * l + j];
+      launch_muon_apply(wblk + mo, M->at == ACT_BF16 ? M->wact(mo) : nullptr, M->at, xf + xdst(l, j), lr, rows, cols,
+                        transposed(j), st);
+    }
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+static int copy_tensor(gpt_model* M, int id, float* region, bool to_host, float* h, size_t n, hipStream_t st,
+                       bool blocks_only) {
+  size_t off;
+  int r, c;
+  if (!M || !h || !tensor_loc(M->cfg, id, &off, &r, &c)) return GPT_ERR_ARG;
+  if (n != (size_t)r * c) return GPT_ERR_ARG;
+  if (blocks_only) {
+    if (id == 0 || id == 1 + 6 * M->cfg.depth) return GPT_ERR_ARG;
+    off -= M->nE;
+  }
+  float* p = region + off;
+  if (hipStreamSynchronize(st) != hipSuccess) return GPT_ERR_HIP;
+  if (hipMemcpy(to_host ? (void*)h : (void*)p, to_host ? (const void*)p : (const void*)h, n * 4,
+                to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice) != hipSuccess)
+    return GPT_ERR_HIP;
+  return GPT_OK;
+}
+
+int gpt_grads(gpt_model* M, int32_t id, float* h, size_t n, void* s) {
+  return M ? copy_tensor(M, id, M->grads(), true, h, n, (hipStream_t)s, false) : GPT_ERR_ARG;
+}
+int gpt_get_params(gpt_model* M, int32_t id, float* h, size_t n, void* s) {
+  return M ? copy_tensor(M, id, M->params(), true, h, n, (hipStream_t)s, false) : GPT_ERR_ARG;
+}
+int gpt_set_grads(gpt_model* M, int32_t id, const float* h, size_t n, void* s) {
+  return M ? copy_tensor(M, id, M->grads(), false, const_cast<float*>(h), n, (hipStream_t)s, false) : GPT_ERR_ARG;
+}
+int gpt_get_momentum(gpt_model* M, int32_t id, float* h, size_t n, void* s) {
+  return M ? copy_tensor(M, id, M->at_off<float>(M->off.mom), true, h, n, (hipStream_t)s, true) : GPT_ERR_ARG;
+}
+int gpt_set_momentum(gpt_model* M, int32_t id, const float* h, size_t n, void* s) {
+  return M ? copy_tensor(M, id, M->at_off<float>(M->off.mom), false, const_cast<float*>(h), n, (hipStream_t)s, true)
+           : GPT_ERR_ARG;
+}
+int gpt_set_params(gpt_model* M, int32_t id, const float* h, size_t n, void* s) {
+  if (!M) return GPT_ERR_ARG;
+  hipStream_t st = (hipStream_t)s;
+  int rc = copy_tensor(M, id, M->params(), false, const_cast<float*>(h), n, st, false);
+  if (rc) return rc;
+  if (M->at == ACT_BF16) {
+    size_t off;
+    int r, c;
+    tensor_loc(M->cfg, id, &off, &r, &c);
+    if (id == 1 + 6 * M->cfg.depth)
+      launch_cast_f32_to_act(M->params() + off, M->uact(), M->at, n, st);
+    else if (id != 0)
+      launch_cast_f32_to_act(M->params() + off, M->wact(off - M->nE), M->at, n, st);
+  }
+  return hipStreamSynchronize(st) == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gpt_argmax(gpt_model* M, int32_t* d_out, void* s) {
+  if (!M || !d_out || !M->stepped) return GPT_ERR_ARG;
+  return hipMemcpyAsync(d_out, M->base + M->off.argmax, (size_t)M->N * 4, hipMemcpyDeviceToDevice,
+                        (hipStream_t)s) == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gpt_row_loss(gpt_model* M, float* d_out, void* s) {
+  if (!M || !d_out || !M->stepped) return GPT_ERR_ARG;
+  return hipMemcpyAsync(d_out, M->base + M->off.row_loss, (size_t)M->N * 4, hipMemcpyDeviceToDevice,
+                        (hipStream_t)s) == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gpt_prof_enable(gpt_model* M, const char* name) {
+  if (!M) return GPT_ERR_ARG;
+  M->prof_name = name ? name : "";
+  M->ev_used = 0;
+  return GPT_OK;
+}
+
+int gpt_prof_read(gpt_model* M, int64_t* launches, double* ms, double* flops) {
+  if (!M || !launches || !ms || !flops) return GPT_ERR_ARG;
+  double t = 0, f = 0;
+  for (size_t i = 0; i + 1 < M->ev_used; i += 2) {
+    if (hipEventSynchronize(M->ev[i + 1]) != hipSuccess) return GPT_ERR_HIP;
+    float e = 0;
+    if (hipEventElapsedTime(&e, M->ev[i], M->ev[i + 1]) != hipSuccess) return GPT_ERR_HIP;
+    t += e;
+    f += M->evflops[i / 2];
+  }
+  *launches = (int64_t)(M->ev_used / 2);
+  *ms = t;
+  *flops = f;
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel-level entry points
+
+static int act_type(int dtype) { return dtype == GPT_FP32 ? ACT_F32 : dtype == GPT_BF16 ? ACT_BF16 : -1; }
+
+int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* A, long lda, long sA,
+              const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits, void* ws,
+              size_t ws_bytes, void* stream) {
+  const int at = act_type(dtype);
+  if (at < 0) return GPT_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || batch < 0 || !C) return GPT_ERR_ARG;
+  GemmArgs p;
+  p.M = M; p.N = N; p.K = K; p.batch = batch;
+  p.A = A; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
+  p.B = B; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
+  p.dtype = at; p.outF = C; p.ldo = ldc; p.strideO = sC;
+  p.tile = tile; p.splits = splits < 1 ? 1 : splits; p.ws = (float*)ws; p.ws_bytes = ws_bytes;
+  const int rc = launch_gemm(p, (hipStream_t)stream);
+  if (rc == 1) return GPT_ERR_ARG;
+  if (rc == 2) return GPT_ERR_SHAPE;
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+const char* gpt_gemm_kernel_name(int dtype, int M, int N, int K, int batch) {
+  GemmArgs p;
+  p.M = M; p.N = N; p.K = K; p.batch = batch; p.dtype = act_type(dtype) < 0 ? ACT_BF16 : act_type(dtype);
+  return gemm_kernel_name(p);
+}
+
+static int attn_ok(int dtype, int hd) {
+  if (act_type(dtype) < 0) return GPT_ERR_UNSUPPORTED;
+  if (hd != 32 && hd != 64 && hd != 128) return GPT_ERR_UNSUPPORTED;
+  return GPT_OK;
+}
+
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, void* stream) {
+  int rc = attn_ok(dtype, hd);
+  if (rc) return rc;
+  if (B < 0 || T < 0 || H < 0 || !qkv || !o || !lse) return GPT_ERR_ARG;
+  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, hd, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv,
+                  int B, int T, int H, int hd, void* stream) {
+  int rc = attn_ok(dtype, hd);
+  if (rc) return rc;
+  if (B < 0 || T < 0 || H < 0 || !qkv || !o || !dO || !lse || !D || !dqkv) return GPT_ERR_ARG;
+  launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, hd, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int N, int d, float eps, void* stream) {
+  if (act_type(dtype) < 0) return GPT_ERR_UNSUPPORTED;
+  if (N < 0 || d < 4 || d % 4 || d > 2048 || !x || !y || !rstd) return GPT_ERR_ARG;
+  launch_rmsnorm_fwd(x, y, act_type(dtype), rstd, N, d, eps, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_rmsnorm_bwd(int dtype, const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
+                     void* dxa, int N, int d, void* stream) {
+  if (act_type(dtype) < 0) return GPT_ERR_UNSUPPORTED;
+  if (N < 0 || d < 4 || d % 4 || d > 2048 || !dy || !x || !rstd || !dx) return GPT_ERR_ARG;
+  launch_rmsnorm_bwd(dy, x, rstd, dres, dx, dxa, act_type(dtype), N, d, 0.f, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_rope_qknorm_fwd(int dtype, void* qkv, float* cs, float* rq, float* rk, int B, int T, int H, int hd,
+                         float base, float eps, void* stream) {
+  int rc = attn_ok(dtype, hd);
+  if (rc) return rc;
+  if (!qkv || !cs || !rq || !rk || B < 0 || T < 0 || H < 0) return GPT_ERR_ARG;
+  launch_rope_table(cs, T, hd, base, (hipStream_t)stream);
+  launch_rope_qknorm_fwd(qkv, act_type(dtype), cs, rq, rk, B, T, H, hd, eps, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, float* cs, const float* rq, const float* rk, int B,
+                         int T, int H, int hd, float base, void* stream) {
+  int rc = attn_ok(dtype, hd);
+  if (rc) return rc;
+  if (!dqkv || !qkv || !cs || !rq || !rk || B < 0 || T < 0 || H < 0) return GPT_ERR_ARG;
+  launch_rope_table(cs, T, hd, base, (hipStream_t)stream);
+  launch_rope_qknorm_bwd(dqkv, qkv, act_type(dtype), cs, rq, rk, B, T, H, hd, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz, float* rl, int32_t* am, int N, int V,
+                       float inv_n, int32_t* err, void* stream) {
+  if (act_type(dtype) < 0) return GPT_ERR_UNSUPPORTED;
+  if (N < 0 || V < 1 || !z || !tgt || !dz || !rl || !am || !err) return GPT_ERR_ARG;
+  launch_cross_entropy(z, tgt, dz, act_type(dtype), rl, am, N, V, inv_n, err, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_embed_gather(const int32_t* tok, const float* E, float* h, int N, int d, int V, int32_t* err, void* stream) {
+  if (N < 0 || d < 4 || d % 4 || V < 1 || !tok || !E || !h || !err) return GPT_ERR_ARG;
+  launch_embed_gather(tok, E, h, N, d, V, err, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+size_t gptk_embed_ws_bytes(int N, int V, int d) { return embed_ws_bytes(N, V, d); }
+
+int gptk_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws, int32_t* sorted,
+                       void* stream) {
+  if (N < 0 || d < 4 || d % 4 || V < 1 || !tok || !dh || !dE || !ws) return GPT_ERR_ARG;
+  launch_embed_scatter(tok, dh, dE, N, V, d, ws, sorted, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal launcher interface of the HIP kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+
+enum GemmEpi {
+  EPI_LINEAR = 0,  // v = alpha*acc + beta*Cin -> outF (fp32) and/or outA (act type)
+  EPI_RELU2 = 1,   // u = alpha*acc -> outA ; g = max(u,0)^2 -> out2
+  EPI_DRELU2 = 2,  // v = alpha*acc * 2*max(aux,0) -> outA
+};
+
+// C[M,N] = sum_k A(m,k) B(n,k), batched over `batch` with element strides.
+//   a_kmaj: A(m,k) = A[m*lda + k]  else A(m,k) = A[k*lda + m]
+//   b_kmaj: B(n,k) = B[n*ldb + k]  else B(n,k) = B[k*ldb + n]
+struct GemmArgs {
+  int M = 0, N = 0, K = 0, batch = 1;
+  const void* A = nullptr; long lda = 0, strideA = 0;
+  const void* B = nullptr; long ldb = 0, strideB = 0;
+  bool a_kmaj = true, b_kmaj = true;
+  int dtype = ACT_BF16;           // operand type (and outA type)
+  int epi = EPI_LINEAR;
+  float alpha = 1.f, beta = 0.f;
+  const float* Cin = nullptr; long ldcin = 0, strideCin = 0;
+  float* outF = nullptr; long ldo = 0, strideO = 0;
+  void* outA = nullptr; long ldoa = 0, strideOA = 0;
+  void* out2 = nullptr;           // EPI_RELU2 second output (same ld/stride as outA)
+  const void* aux = nullptr;      // EPI_DRELU2 input (same ld/stride as outA)
+  int splits = 1;                 // split-K factor; >1 needs ws
+  float* ws = nullptr; size_t ws_bytes = 0;
+  int tile = 0;                   // 0 = auto, 1 = 256x256, 2 = 128x128
+};
+
+// returns 0 on success, else an error code (argument/shape problems)
+int launch_gemm(const GemmArgs& p, hipStream_t st);
+// split-K factor the launcher would use for these arguments (for workspace sizing)
+int gemm_auto_splits(const GemmArgs& p);
+const char* gemm_kernel_name(const GemmArgs& p);
+
+// ---------------------------------------------------------------------------
+// elementwise / reduction kernels
+void launch_embed_gather(const int32_t* tok, const float* E, float* h, int N, int d, int V,
+                         int* err_flag, hipStream_t st);
+void launch_rmsnorm_fwd(const float* x, void* y, int ytype, float* rstd, int N, int d, float eps,
+                        hipStream_t st);
+void launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres,
+                        float* dx, void* dx_act, int act_type, int N, int d, float eps, hipStream_t st);
+void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st);
+void launch_rope_qknorm_fwd(void* qkv, int act_type, const float* cs, float* rstd_q, float* rstd_k,
+                            int B, int T, int H, int hd, float eps, hipStream_t st);
+void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int act_type, const float* cs,
+                            const float* rstd_q, const float* rstd_k, int B, int T, int H, int hd,
+                            hipStream_t st);
+void launch_cross_entropy(const float* logits, const int32_t* targets, void* dlogits, int act_type,
+                          float* row_loss, int32_t* argmax, int N, int V, float inv_n, int* err_flag,
+                          hipStream_t st);
+void launch_sum_rows(const float* x, int n, double* out, hipStream_t st);
+// deterministic embedding backward: dE[v] = sum over positions n with tok[n]==v of dh[n], summed in
+// increasing n.  ws must hold embed_ws_bytes(N, V, d).
+size_t embed_ws_bytes(int N, int V, int d);
+void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d,
+                          void* ws, int32_t* sorted_out, hipStream_t st);
+void launch_cast_f32_to_act(const float* x, void* y, int act_type, size_t n, hipStream_t st);
+void launch_fill_normal(float* w, size_t n, uint64_t seed, uint64_t stream_id, float stddev,
+                        hipStream_t st);
+void launch_zero(void* p, size_t bytes, hipStream_t st);
+
+// Muon pieces
+void launch_momentum(float* mom, const float* g, float mu, size_t n, hipStream_t st);
+// per-matrix sum of squares of mom; matrix i occupies [offs[i], offs[i]+sizes[i])
+void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, int nmat, double* partial,
+                         int parts, double* out, hipStream_t st);
+// X = src / (norm + eps) written (optionally transposed) into fp32 and act copies
+void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols,
+                         bool transpose, float* xf, void* xa, int act_type, hipStream_t st);
+void launch_muon_apply(float* w, void* w_act, int act_type, const float* x, float lr, int rows,
+                       int cols, bool transposed, hipStream_t st);
+
+// attention
+void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int hd,
+                     hipStream_t st);
+void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,
+                     void* dqkv, int act_type, int B, int T, int H, int hd, hipStream_t st);

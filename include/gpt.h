@@ -1,0 +1,199 @@
+/* gpt.h -- C ABI of a single-GPU GPT pretraining step on MI355X (gfx950).
+ *
+ * One training step on one GPU's micro-batch of the nanochat-style GPT that the
+ * dev.to article "ChatGPT'nizi 50 Dolara Nasil Egitirsiniz?" (and its Arabic
+ * translation) describes in "nanochat Nasil Calisir? / 1. GPT Modeli":
+ * token-embedding lookup (untied from the LM head), pre-norm decoder blocks with
+ * RoPE and QK-normalised causal multi-head attention and a ReLU^2 MLP, a final
+ * norm, the LM head and the softmax cross-entropy over the 32,768-token
+ * vocabulary; forward and backward; then the Muon update of section
+ * "2. Muon Optimize Edici" (momentum, then Newton-Schulz orthogonalisation of
+ * every 2-D block matrix with the Polar Express coefficient table).
+ *
+ * Conventions
+ *  - Every pointer named d_* is device memory; h_* is host memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *    work is stream-ordered; only gpt_step, gpt_grads, gpt_get_* synchronise.
+ *  - Matrices are row-major [rows][cols] float32 in the [out][in] convention of
+ *    the article's Linear layer (F.linear with no bias).
+ *  - Tensor ids (gpt_tensor_shape): 0 = E [V][d]; for layer l, ids 1+6l .. 6+6l
+ *    are Wq [d][d], Wk [d][d], Wv [d][d], Wo [d][d], W1 [F][d], W2 [d][F];
+ *    id 1+6L = U [V][d] (LM head).  Count = 2 + 6L.
+ *  - Ownership: the caller owns the arena, the token buffers and the stream and
+ *    keeps them alive until the stream's work completes.  The library never
+ *    allocates device memory; gpt_free releases host bookkeeping only.
+ *  - Errors: functions return a gpt_status; gpt_step returns NaN on error and
+ *    records the status (gpt_last_status).  No C++ exception crosses the ABI.
+ *  - A model is used by one host thread at a time.
+ */
+#ifndef GPT_H
+#define GPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT_OK = 0,
+  GPT_ERR_ARG = 1,          /* bad argument, arena too small, id out of range */
+  GPT_ERR_SHAPE = 2,        /* cfg inconsistent, or differs from the model's */
+  GPT_ERR_TOKEN_RANGE = 3,  /* a token or target id outside [0, vocab) */
+  GPT_ERR_NONFINITE = 4,    /* a non-finite logit */
+  GPT_ERR_HIP = 5,          /* a HIP runtime call failed */
+  GPT_ERR_UNSUPPORTED = 6   /* a precision/shape this build does not support */
+} gpt_status;
+
+typedef enum { GPT_FP32 = 0, GPT_BF16 = 1, GPT_FP8 = 2 } gpt_precision;
+
+/* Model + step configuration.  depth is the one dial of the article's
+ * "Felsefe" section: gpt_cfg_from_depth derives the rest. */
+typedef struct gpt_cfg {
+  int32_t depth;      /* L: decoder blocks */
+  int32_t d_model;    /* d: residual width (multiple of 8) */
+  int32_t n_head;     /* H: attention heads (n_head * head_dim == d_model) */
+  int32_t head_dim;   /* hd: 32, 64 or 128 */
+  int32_t d_ff;       /* F: MLP hidden width */
+  int32_t vocab;      /* V */
+  int32_t seq_len;    /* T */
+  int32_t batch;      /* B: sequences in the micro-batch */
+  int32_t precision;  /* gpt_precision: FP32 = all fp32; BF16 = fp32 master weights and
+                         residual stream, bf16 GEMM/attention operands, fp32 accumulate */
+  float init_std;     /* 0.02; Wo and W2 use init_std / sqrt(2 depth) */
+  float rope_base;    /* 10000 */
+  float norm_eps;     /* 1e-6, inside the square root of every RMSNorm */
+  float muon_momentum;/* 0.95 */
+  int32_t ns_steps;   /* Newton-Schulz iterations, 0..5 */
+  float ns_coeffs[5][3]; /* (a, b, c) per iteration */
+  int64_t num_steps;  /* informational: steps at a tokens:params ratio of 8 with 2^20-token batches */
+} gpt_cfg;
+
+typedef struct gpt_model gpt_model; /* opaque */
+
+/* Fill *out from depth: d = 64*depth (rounded up to a multiple of 128), hd = 128,
+ * H = d/128, F = 4d, V = 32768, T = 2048, B = 16, bf16, the default Newton-Schulz
+ * table.  Returns GPT_ERR_ARG for depth < 1 or out == NULL. */
+int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out);
+
+/* CPU-only consistency check of a configuration. */
+int gpt_cfg_validate(const gpt_cfg* cfg);
+
+/* Bytes of device memory the model needs (parameters, gradients, momentum,
+ * saved activations and workspaces); 0 when cfg is invalid. */
+size_t gpt_state_bytes(const gpt_cfg* cfg);
+
+/* Carve the caller's arena (>= gpt_state_bytes, 256-byte aligned), draw the
+ * initial weights on the device from a counter-based generator keyed by seed
+ * (N(0, init_std^2), output projections scaled), zero the momentum. */
+int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* d_arena, size_t arena_bytes, void* stream,
+             gpt_model** out);
+
+/* One forward + backward pass over the micro-batch d_tokens/d_targets (int32,
+ * row-major [batch][seq_len]).  Overwrites every gradient.  Returns the mean
+ * cross-entropy over the batch*seq_len positions, or NaN on error.  cfg must
+ * match the model's configuration. */
+float gpt_step(gpt_model* m, const int32_t* d_tokens, const int32_t* d_targets, const gpt_cfg* cfg, void* stream);
+
+/* Copy the fp32 gradient of tensor `tensor_id` (n elements) to host memory. */
+int gpt_grads(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* stream);
+
+/* Muon on every block matrix (Wq, Wk, Wv, Wo, W1, W2 of every layer, each
+ * separately): B <- mu B + G; X = B / (|B|_F + 1e-7); ns_steps iterations of
+ * A = X X^T, X <- a X + (b A + c A^2) X on the wide orientation; W <- W - lr X.
+ * E and U are not touched.  Stream-ordered, no synchronisation. */
+int muon_update(gpt_model* m, float lr, void* stream);
+
+/* Device copy of the argmax over the vocabulary of every position's logits of the
+ * last gpt_step (lowest index among equal maxima), int32 [batch*seq_len]. */
+int gpt_argmax(gpt_model* m, int32_t* d_out, void* stream);
+
+/* Device copy of the per-position cross-entropy of the last gpt_step, fp32. */
+int gpt_row_loss(gpt_model* m, float* d_out, void* stream);
+
+/* Host copies in and out of parameters, gradients and Muon momentum (fp32).
+ * Setting a parameter refreshes its low-precision copy. */
+int gpt_get_params(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* stream);
+int gpt_set_params(gpt_model* m, int32_t tensor_id, const float* h_in, size_t n, void* stream);
+int gpt_set_grads(gpt_model* m, int32_t tensor_id, const float* h_in, size_t n, void* stream);
+int gpt_get_momentum(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* stream);
+int gpt_set_momentum(gpt_model* m, int32_t tensor_id, const float* h_in, size_t n, void* stream);
+
+int gpt_tensor_count(const gpt_cfg* cfg);
+int gpt_tensor_shape(const gpt_cfg* cfg, int32_t tensor_id, int32_t* rows, int32_t* cols);
+
+int gpt_last_status(const gpt_model* m);
+const char* gpt_status_str(int status);
+void gpt_free(gpt_model* m);
+
+/* Optional per-launch timing of one GEMM kernel class inside gpt_step and
+ * muon_update: events are recorded around each launch whose kernel name
+ * (gpt_gemm_kernel_name) equals `name`; NULL disables.  gpt_prof_read returns
+ * the launch count, the summed milliseconds and the summed algorithmic FLOPs. */
+int gpt_prof_enable(gpt_model* m, const char* name);
+int gpt_prof_read(gpt_model* m, int64_t* launches, double* ms, double* flops);
+
+/* ------------------------------------------------------------------------
+ * Kernel-level entry points for stage-isolated checks.  All pointers are
+ * device pointers owned by the caller; `dtype` is GPT_FP32 or GPT_BF16 and
+ * gives the element type of the activation-typed buffers (act); every call is
+ * stream-ordered and returns a gpt_status.
+ */
+
+/* C[b][m][n] (fp32) = sum_k A(m,k) B(n,k) for b < batch, where A(m,k) =
+ * A[m*lda+k] if a_kmaj else A[k*lda+m], and likewise B.  Element strides
+ * between batches sA, sB, sC.  tile: 0 auto, 1 = 256x256, 2 = 128x128 (bf16).
+ * splits > 1 splits K and needs ws of splits*batch*M*N*4 bytes. */
+int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* A, long lda,
+              long sA, const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* name of the kernel gptk_gemm / gpt_step would launch for these sizes */
+const char* gpt_gemm_kernel_name(int dtype, int M, int N, int K, int batch);
+
+/* causal attention over qkv act [B*T][3*H*hd] -> o act [B*T][H*hd], lse fp32
+ * [B][H][T] (natural log of the sum of exp of q.k/sqrt(hd)). hd in {32,64,128}. */
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, void* stream);
+/* backward: dqkv act [B*T][3*H*hd] from qkv, o, dO act [B*T][H*hd] and lse;
+ * D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */
+int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D,
+                  void* dqkv, int B, int T, int H, int hd, void* stream);
+
+/* y act = x / sqrt(mean(x^2) + eps) per row of x fp32 [N][d]; rstd fp32 [N] */
+int gptk_rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int N, int d, float eps, void* stream);
+/* dx fp32 (and act copy if dx_act) = dres + rstd*(dy - y*mean(dy*y)), y = x*rstd;
+ * dres may be NULL */
+int gptk_rmsnorm_bwd(int dtype, const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
+                     void* dx_act, int N, int d, void* stream);
+
+/* in place on the q and k parts of qkv act [B*T][3*H*hd]: rotate half-split pairs
+ * by t*base^(-2i/hd) then RMS-normalise each head vector; rstd_q, rstd_k fp32
+ * [B*T][H].  cs is fp32 scratch of T*hd floats (the rotation table). */
+int gptk_rope_qknorm_fwd(int dtype, void* qkv, float* cs, float* rstd_q, float* rstd_k, int B, int T, int H, int hd,
+                         float base, float eps, void* stream);
+/* in place on the q and k parts of dqkv: gradient through the norm and rotation */
+int gptk_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, float* cs, const float* rstd_q,
+                         const float* rstd_k, int B, int T, int H, int hd, float base, void* stream);
+
+/* fused softmax cross-entropy over logits fp32 [N][V]: row_loss fp32 [N],
+ * dlogits act [N][V] = (softmax - onehot(target)) * inv_n, argmax int32 [N]
+ * (lowest index among equal maxima); err int32 [1] gets bit 1 for a target out
+ * of range and bit 2 for a non-finite logit. */
+int gptk_cross_entropy(int dtype, const float* logits, const int32_t* targets, void* dlogits, float* row_loss,
+                       int32_t* argmax, int N, int V, float inv_n, int32_t* err, void* stream);
+
+/* h fp32 [N][d] = E fp32 [V][d] rows of tokens; err bit 1 on an id outside [0,V) */
+int gptk_embed_gather(const int32_t* tokens, const float* E, float* h, int N, int d, int V, int32_t* err,
+                      void* stream);
+/* dE fp32 [V][d] = sum over positions n with tokens[n]==v of dh[n] (in increasing
+ * n, deterministic); sorted int32 [N] receives the stable order of positions by
+ * token; ws must hold gptk_embed_ws_bytes(N, V, d) bytes. */
+size_t gptk_embed_ws_bytes(int N, int V, int d);
+int gptk_embed_scatter(const int32_t* tokens, const float* dh, float* dE, int N, int V, int d, void* ws,
+                       int32_t* sorted, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_H */

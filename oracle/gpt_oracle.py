@@ -93,13 +93,14 @@ def rope(x, ang, inverse=False):
 def causal_attention(q, k, v):
     """o[b,i,h] = sum_{j<=i} softmax_j(q_i . k_j / sqrt(hd)) v_j ; q,k,v [B,T,H,hd]."""
     B, T, H, hd = q.shape
-    S = np.einsum("bihd,bjhd->bhij", q, k) / np.sqrt(hd)
+    qh, kh, vh = (x.transpose(0, 2, 1, 3) for x in (q, k, v))      # [B,H,T,hd]
+    S = (qh @ kh.transpose(0, 1, 3, 2)) / np.sqrt(hd)             # [B,H,T,T]
     mask = np.triu(np.ones((T, T), dtype=bool), 1)
     S = np.where(mask, -np.inf, S)
     S = S - S.max(axis=-1, keepdims=True)
     P = np.exp(S)
     P /= P.sum(axis=-1, keepdims=True)
-    o = np.einsum("bhij,bjhd->bihd", P, v)
+    o = (P @ vh).transpose(0, 2, 1, 3)
     return o, P
 
 
@@ -112,14 +113,15 @@ def causal_attention_bwd(do, q, k, v, o, P=None):
     B, T, H, hd = q.shape
     if P is None:
         _, P = causal_attention(q, k, v)
-    dv = np.einsum("bhij,bihd->bjhd", P, do)
-    dP = np.einsum("bihd,bjhd->bhij", do, v)
-    D = np.einsum("bihd,bihd->bhi", do, o)[..., None]
+    qh, kh, vh, doh, oh = (x.transpose(0, 2, 1, 3) for x in (q, k, v, do, o))
+    dv = P.transpose(0, 1, 3, 2) @ doh
+    dP = doh @ vh.transpose(0, 1, 3, 2)
+    D = np.sum(doh * oh, axis=-1, keepdims=True)
     dS = P * (dP - D)
     sc = 1.0 / np.sqrt(hd)
-    dq = np.einsum("bhij,bjhd->bihd", dS, k) * sc
-    dk = np.einsum("bhij,bihd->bjhd", dS, q) * sc
-    return dq, dk, dv
+    dq = (dS @ kh) * sc
+    dk = (dS.transpose(0, 1, 3, 2) @ qh) * sc
+    return tuple(x.transpose(0, 2, 1, 3) for x in (dq, dk, dv))
 
 
 def logsumexp(z):
@@ -179,6 +181,16 @@ def loss_from_logits(z, targets):
     return float(np.mean(lse - zy)), lse - zy
 
 
+def cross_entropy_grad(z, targets):
+    """d(mean cross-entropy)/dz = (softmax(z) - onehot(y)) / (number of positions)."""
+    n = targets.size
+    P = np.exp(z - z.max(axis=-1, keepdims=True))
+    P /= P.sum(axis=-1, keepdims=True)
+    idx = targets[..., None].astype(np.int64)
+    np.put_along_axis(P, idx, np.take_along_axis(P, idx, -1) - 1.0, -1)
+    return P / n
+
+
 def backward(z, targets, cache, cfg):
     """Exact gradient of the mean cross-entropy w.r.t. every tensor of the table."""
     p = cache["p"]
@@ -190,14 +202,7 @@ def backward(z, targets, cache, cfg):
     ang = cache["ang"]
     tokens = cache["tokens"]
 
-    # softmax cross-entropy: dz = (softmax(z) - onehot(y)) / N
-    zs = z - z.max(axis=-1, keepdims=True)
-    P = np.exp(zs)
-    P /= P.sum(axis=-1, keepdims=True)
-    dz = P
-    np.put_along_axis(dz, targets[..., None].astype(np.int64),
-                      np.take_along_axis(dz, targets[..., None].astype(np.int64), -1) - 1.0, -1)
-    dz /= N
+    dz = cross_entropy_grad(z, targets)
 
     r = cache["r"]
     dU = dz.reshape(N, V).T @ r.reshape(N, d)

@@ -1,0 +1,30 @@
+"""Helpers shared by the GPU tests: bf16 rounding on the host, error metrics."""
+import numpy as np
+import torch
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest even) and back, on the CPU."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).bfloat16().float().numpy()
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    """numpy float array -> device tensor of the activation type ('bf16' or 'fp32')."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.bfloat16()
+    return t.cuda()
+
+
+def from_dev(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def say(*a):
+    print(*a, flush=True)

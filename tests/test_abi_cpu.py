@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU calls): the library loads, exports every
+declared symbol, and its configuration / sizing / validation logic is right."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gpt_pretraining_step_train_amd import binding, configs, inputs
+from oracle import polar_express
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "gpt.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"\b((?:gpt|gptk|muon)_\w+)\s*\(", hdr))
+    assert len(names) >= 30
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_cfg_from_depth(lib):
+    want = {12: (768, 6, 3072), 24: (1536, 12, 6144), 26: (1664, 13, 6656)}
+    for depth, (d, h, f) in want.items():
+        c = binding.GptCfg()
+        assert lib.gpt_cfg_from_depth(depth, ctypes.byref(c)) == 0
+        assert (c.d_model, c.n_head, c.head_dim, c.d_ff) == (d, h, 128, f)
+        assert (c.vocab, c.seq_len, c.batch) == (32768, 2048, 16)
+        assert lib.gpt_cfg_validate(ctypes.byref(c)) == 0
+        n = configs.n_params(dict(depth=depth, d_model=d, d_ff=f, vocab=32768))
+        assert c.num_steps == round(8 * n / 2 ** 20)
+    c = binding.GptCfg()
+    assert lib.gpt_cfg_from_depth(0, ctypes.byref(c)) == 1
+    c = binding.GptCfg()
+    lib.gpt_cfg_from_depth(13, ctypes.byref(c))
+    assert c.d_model % 128 == 0 and c.n_head * c.head_dim == c.d_model
+
+
+def test_param_counts_match_survey_shapes():
+    assert configs.n_params(configs.get("tiny")) == 1441792
+    assert configs.n_params(configs.get("laptop")) == 2899968
+    assert configs.n_params(configs.get("d12")) == 135266304
+    assert configs.n_params(configs.get("d24")) == 780140544
+    assert configs.n_params(configs.get("d26")) == 972947456
+
+
+def test_default_ns_table(lib):
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "ns_printed_coeffs.json")))
+    c = binding.GptCfg()
+    lib.gpt_cfg_from_depth(24, ctypes.byref(c))
+    tab = c.coeffs()
+    assert c.ns_steps == gold["ns_steps"]
+    np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
+    derived, _ = polar_express.coefficients()
+    np.testing.assert_allclose(tab[2:], derived[2:], rtol=0, atol=2e-5)
+
+
+def test_validation_errors(lib):
+    base = binding.make_cfg(configs.get("laptop"))
+    assert lib.gpt_cfg_validate(ctypes.byref(base)) == 0
+    for field, val, code in [("head_dim", 48, 6), ("n_head", 5, 2), ("d_model", 2056, 2), ("precision", 7, 6),
+                             ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2)]:
+        c = binding.make_cfg(configs.get("laptop"))
+        setattr(c, field, val)
+        assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, field
+        assert lib.gpt_state_bytes(ctypes.byref(c)) == 0
+    assert lib.gpt_cfg_validate(None) == 1
+    assert lib.gpt_status_str(3).decode() == "token id out of range"
+
+
+def test_state_bytes_and_tensor_table(lib):
+    for name in ("tiny", "laptop", "d12", "d24"):
+        cfg = configs.get(name)
+        c = binding.make_cfg(cfg)
+        nb = lib.gpt_state_bytes(ctypes.byref(c))
+        n = configs.n_params(cfg)
+        assert nb > 3 * 4 * n                     # params + grads + momentum at least
+        assert nb < 288 * 2 ** 30                # fits one MI355X
+        assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"]
+        shapes = inputs.tensor_shapes(cfg)
+        for i, (nm, shp) in enumerate(shapes):
+            r, k = ctypes.c_int32(), ctypes.c_int32()
+            assert lib.gpt_tensor_shape(ctypes.byref(c), i, ctypes.byref(r), ctypes.byref(k)) == 0
+            assert (r.value, k.value) == shp, nm
+        r, k = ctypes.c_int32(), ctypes.c_int32()
+        assert lib.gpt_tensor_shape(ctypes.byref(c), len(shapes), ctypes.byref(r), ctypes.byref(k)) == 1
+    d24 = binding.make_cfg(configs.get("d24"))
+    assert lib.gpt_state_bytes(ctypes.byref(d24)) < 100 * 2 ** 30
+
+
+def test_kernel_names(lib):
+    assert binding.gemm_kernel_name(1, 32768, 6144, 1536) == "gemm_bf16_kernel<256,256>"
+    assert binding.gemm_kernel_name(1, 512, 384, 128) == "gemm_bf16_kernel<128,128>"
+    assert binding.gemm_kernel_name(0, 512, 384, 128) == "gemm_f32_kernel"
+
+
+def test_configs_flops_formula():
+    f = configs.step_flops(configs.get("d24"))
+    assert abs(f["total"] - 1.844e14) / 1.844e14 < 3e-3
+    assert abs(f["muon"] - 300 * 24 * 1536 ** 3) < 1

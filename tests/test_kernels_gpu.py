@@ -1,0 +1,314 @@
+"""Stage-isolated parity of each HIP kernel against the fp64 oracle pieces.
+
+Inputs are seeded and rounded to the kernel's operand type on the host, so the
+oracle sees exactly the values the kernel reads; the remaining differences are
+accumulation order/precision and the kernel's own roundings.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpt_pretraining_step_train_amd import binding as B
+from oracle import gpt_oracle as O
+from tests.gpu_util import bf16_round, from_dev, rel_l2, say, to_dev
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": B.GPT_BF16, "fp32": B.GPT_FP32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    torch.cuda.set_device(0)
+
+
+def _round(x, dtype):
+    return bf16_round(x) if dtype == "bf16" else x.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+GEMM_CASES = [
+    # dtype, a_kmaj, b_kmaj, M, N, K, batch, tile, splits
+    ("bf16", 1, 1, 300, 200, 136, 1, 0, 1),
+    ("bf16", 1, 1, 520, 264, 200, 1, 1, 1),
+    ("bf16", 1, 0, 296, 264, 136, 1, 2, 1),
+    ("bf16", 1, 0, 512, 520, 256, 1, 1, 1),
+    ("bf16", 0, 0, 296, 200, 264, 1, 2, 1),
+    ("bf16", 0, 0, 264, 528, 520, 1, 1, 1),
+    ("bf16", 0, 1, 136, 300, 72, 1, 2, 1),
+    ("bf16", 1, 1, 256, 384, 128, 3, 2, 1),
+    ("bf16", 0, 0, 136, 200, 1032, 1, 2, 3),
+    ("fp32", 1, 1, 100, 70, 33, 1, 0, 1),
+    ("fp32", 1, 0, 96, 72, 40, 2, 0, 1),
+    ("fp32", 0, 0, 72, 96, 200, 1, 0, 2),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES)
+def test_gemm_layouts_tails_batch_split(case):
+    dtype, ak, bk, M, N, K, batch, tile, splits = case
+    say("gemm", case)
+    rng = np.random.default_rng(M * 7 + N)
+    a_shape = (batch, M, K) if ak else (batch, K, M)
+    b_shape = (batch, N, K) if bk else (batch, K, N)
+    A = _round(rng.standard_normal(a_shape), dtype)
+    Bm = _round(rng.standard_normal(b_shape), dtype)
+    Am = A if ak else A.transpose(0, 2, 1)
+    Bn = Bm if bk else Bm.transpose(0, 2, 1)
+    ref = np.einsum("zmk,znk->zmn", Am.astype(np.float64), Bn.astype(np.float64))
+    dA, dB = to_dev(A, dtype), to_dev(Bm, dtype)
+    C = torch.full((batch, M, N), float("nan"), device="cuda")
+    ws = torch.empty(splits * batch * M * N, device="cuda") if splits > 1 else None
+    B.gemm(DT[dtype], ak, bk, M, N, K, dA, K if ak else M, dB, K if bk else N, C, N, batch=batch,
+           sA=A[0].size, sB=Bm[0].size, sC=M * N, tile=tile, splits=splits, ws=ws)
+    torch.cuda.synchronize()
+    got = from_dev(C)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert np.isfinite(got).all()
+    assert err < (1e-5 if dtype == "bf16" else 1e-5), err
+
+
+def test_gemm_full_size_sampled():
+    """d24 MLP up-projection shape [32768 x 6144 x 1536] in the launch configuration of
+    the step; 4096 sampled outputs recomputed one by one in fp64."""
+    M, N, K = 32768, 6144, 1536
+    g = torch.Generator(device="cuda").manual_seed(0)
+    A = torch.randn(M, K, device="cuda", generator=g).bfloat16()
+    Bw = torch.randn(N, K, device="cuda", generator=g).bfloat16()
+    C = torch.empty(M, N, device="cuda")
+    B.gemm(B.GPT_BF16, 1, 1, M, N, K, A, K, Bw, K, C, N)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, M, 4096)
+    cols = rng.integers(0, N, 4096)
+    rows[:2], cols[:2] = [0, M - 1], [0, N - 1]
+    a = A[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    b = Bw[torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64)
+    ref = np.sum(a * b, axis=1)
+    got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    assert np.abs(got - ref).max() < 1e-4 * np.sqrt(K) * 4
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _qkv(Bn, T, H, hd, seed, dtype):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Bn, T, H, hd))
+    k = rng.standard_normal((Bn, T, H, hd))
+    v = rng.standard_normal((Bn, T, H, hd))
+    q, _ = O.rms_norm(q, 1e-6)          # unit-RMS heads, as after QK-norm
+    k, _ = O.rms_norm(k, 1e-6)
+    qkv = np.concatenate([q.reshape(Bn, T, -1), k.reshape(Bn, T, -1), v.reshape(Bn, T, -1)], -1)
+    qkv = _round(qkv, dtype)
+    d = H * hd
+    q = qkv[..., :d].reshape(Bn, T, H, hd).astype(np.float64)
+    k = qkv[..., d:2 * d].reshape(Bn, T, H, hd).astype(np.float64)
+    v = qkv[..., 2 * d:].reshape(Bn, T, H, hd).astype(np.float64)
+    return qkv, q, k, v
+
+
+ATTN_CASES = [("bf16", 2, 300, 3, 128), ("bf16", 1, 256, 2, 64), ("bf16", 2, 130, 2, 32),
+              ("bf16", 1, 1, 1, 128), ("fp32", 2, 128, 4, 32), ("fp32", 1, 77, 2, 64)]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_fwd_bwd(case):
+    dtype, Bn, T, H, hd = case
+    say("attention", case)
+    qkv, q, k, v = _qkv(Bn, T, H, hd, 11, dtype)
+    o_ref, _ = O.causal_attention(q, k, v)
+    qh = q.transpose(0, 2, 1, 3)
+    S = qh @ k.transpose(0, 2, 3, 1) / np.sqrt(hd)
+    S = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, S)
+    lse_ref = O.logsumexp(S)                               # [B,H,T]
+    d = H * hd
+    dq = to_dev(qkv, dtype)
+    o = torch.zeros(Bn * T, d, device="cuda", dtype=dq.dtype)
+    lse = torch.zeros(Bn * H * T, device="cuda")
+    B.attn_fwd(DT[dtype], dq, o, lse, Bn, T, H, hd)
+    torch.cuda.synchronize()
+    o_got = from_dev(o).reshape(Bn, T, H, hd)
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    assert rel_l2(o_got, o_ref) < tol
+    assert np.abs(from_dev(lse).reshape(Bn, H, T) - lse_ref).max() < (2e-3 if dtype == "bf16" else 1e-5)
+    # backward, from the kernel's own forward output (as in the step)
+    rng = np.random.default_rng(12)
+    dO = _round(rng.standard_normal((Bn, T, H, hd)), dtype)
+    o_in = o_got
+    dq_ref, dk_ref, dv_ref = O.causal_attention_bwd(dO.astype(np.float64), q, k, v, o_in)
+    ddo = to_dev(dO.reshape(Bn * T, d), dtype)
+    D = torch.zeros(Bn * H * T, device="cuda")
+    dqkv = torch.full((Bn * T, 3 * d), float("nan"), device="cuda", dtype=dq.dtype)
+    B.attn_bwd(DT[dtype], dq, o, ddo, lse, D, dqkv, Bn, T, H, hd)
+    torch.cuda.synchronize()
+    g = from_dev(dqkv).reshape(Bn, T, 3, H, hd)
+    gtol = 2e-2 if dtype == "bf16" else 1e-4
+    for i, ref in enumerate((dq_ref, dk_ref, dv_ref)):
+        e = rel_l2(g[:, :, i], ref)
+        assert e < gtol, (i, e)
+
+
+def test_attention_full_size_sampled_heads():
+    """d24 shape (B=16, T=2048, 12 heads of 128) in the step's launch configuration;
+    the oracle recomputes two (sequence, head) pairs."""
+    Bn, T, H, hd = 16, 2048, 12, 128
+    g = torch.Generator(device="cuda").manual_seed(3)
+    qkv = torch.randn(Bn * T, 3 * H * hd, device="cuda", generator=g)
+    qkv = qkv.bfloat16()
+    o = torch.empty(Bn * T, H * hd, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(Bn * H * T, device="cuda")
+    B.attn_fwd(B.GPT_BF16, qkv, o, lse, Bn, T, H, hd)
+    torch.cuda.synchronize()
+    x = qkv.float().cpu().numpy().astype(np.float64).reshape(Bn, T, 3, H, hd)
+    og = o.float().cpu().numpy().reshape(Bn, T, H, hd)
+    for (b, h) in [(0, 0), (Bn - 1, H - 1)]:
+        q, k, v = (x[b:b + 1, :, i, h:h + 1] for i in range(3))
+        ref, _ = O.causal_attention(q, k, v)
+        assert rel_l2(og[b:b + 1, :, h:h + 1], ref) < 1e-2
+
+
+# ----------------------------------------------------------------------------- norms
+
+
+@pytest.mark.parametrize("dtype,N,d", [("bf16", 37, 1536), ("bf16", 64, 192), ("fp32", 29, 128),
+                                       ("bf16", 5, 1664), ("fp32", 3, 2048)])
+def test_rmsnorm_fwd_bwd(dtype, N, d):
+    rng = np.random.default_rng(d + N)
+    x = (rng.standard_normal((N, d)) * 2.5).astype(np.float32)
+    dy = rng.standard_normal((N, d)).astype(np.float32)
+    dres = rng.standard_normal((N, d)).astype(np.float32)
+    y_ref, r_ref = O.rms_norm(x.astype(np.float64), 1e-6)
+    dx_ref = O.rms_norm_bwd(dy.astype(np.float64), y_ref, r_ref) + dres
+    tx, tdy, tres = (torch.from_numpy(a).cuda() for a in (x, dy, dres))
+    y = torch.empty(N, d, device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    rstd = torch.empty(N, device="cuda")
+    B.rmsnorm_fwd(DT[dtype], tx, y, rstd, N, d, 1e-6)
+    dx = torch.empty(N, d, device="cuda")
+    dxa = torch.empty_like(y)
+    B.rmsnorm_bwd(DT[dtype], tdy, tx, rstd, tres, dx, dxa, N, d)
+    torch.cuda.synchronize()
+    assert rel_l2(from_dev(y), y_ref) < (4e-3 if dtype == "bf16" else 1e-6)
+    assert np.abs(rstd.cpu().numpy() - r_ref[:, 0]).max() / r_ref.max() < 1e-6
+    assert rel_l2(dx.cpu().numpy(), dx_ref) < 1e-5
+    assert rel_l2(from_dev(dxa), dx_ref) < (4e-3 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("dtype,Bn,T,H,hd", [("bf16", 2, 100, 3, 128), ("bf16", 1, 64, 2, 64),
+                                             ("fp32", 2, 40, 4, 32), ("bf16", 1, 2048, 1, 128)])
+def test_rope_qknorm_fwd_bwd(dtype, Bn, T, H, hd):
+    rng = np.random.default_rng(T)
+    d = H * hd
+    qkv = _round(rng.standard_normal((Bn, T, 3 * d)) * 0.7, dtype)
+    dqkv = _round(rng.standard_normal((Bn, T, 3 * d)), dtype)
+    ang = O.rope_angles(T, hd, 10000.0)
+    x = qkv.astype(np.float64)
+    outs, grads = [], []
+    for i in range(2):  # q, k
+        part = x[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd)
+        y, r = O.rms_norm(O.rope(part, ang), 1e-6)
+        outs.append((y, r))
+    tq = to_dev(qkv.reshape(Bn * T, 3 * d), dtype)
+    cs = torch.empty(T * hd, device="cuda")
+    rq = torch.empty(Bn * T * H, device="cuda")
+    rk = torch.empty(Bn * T * H, device="cuda")
+    B.rope_qknorm_fwd(DT[dtype], tq, cs, rq, rk, Bn, T, H, hd, 10000.0, 1e-6)
+    torch.cuda.synchronize()
+    got = from_dev(tq).reshape(Bn, T, 3 * d)
+    tol = 5e-3 if dtype == "bf16" else 2e-6
+    for i, (y, r) in enumerate(outs):
+        assert rel_l2(got[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd), y) < tol
+    np.testing.assert_array_equal(got[..., 2 * d:], qkv[..., 2 * d:].astype(np.float64))   # v untouched
+    assert np.abs(rq.cpu().numpy().reshape(Bn, T, H) - outs[0][1][..., 0]).max() / outs[0][1].max() < 1e-5
+    # backward uses the kernel's normalised q, k as y (what the step saves)
+    ddq = to_dev(dqkv.reshape(Bn * T, 3 * d), dtype)
+    B.rope_qknorm_bwd(DT[dtype], ddq, tq, cs, rq, rk, Bn, T, H, hd, 10000.0)
+    torch.cuda.synchronize()
+    gg = from_dev(ddq).reshape(Bn, T, 3 * d)
+    for i, (y, r) in enumerate(outs):
+        dy = dqkv[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd).astype(np.float64)
+        ref = O.rope(O.rms_norm_bwd(dy, y, r), ang, inverse=True)
+        assert rel_l2(gg[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd), ref) < (1e-2 if dtype == "bf16" else 1e-5)
+    np.testing.assert_array_equal(gg[..., 2 * d:], dqkv[..., 2 * d:].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- cross-entropy
+
+
+@pytest.mark.parametrize("dtype,N,V", [("bf16", 40, 4096), ("fp32", 33, 4096), ("bf16", 9, 32768),
+                                       ("fp32", 7, 1000)])
+def test_cross_entropy_and_argmax(dtype, N, V):
+    rng = np.random.default_rng(V + N)
+    z = (rng.standard_normal((N, V)) * 3).astype(np.float32)
+    z[0, :] = 1.25                       # all tied -> index 0
+    z[1, [7, 300, 901]] = 50.0           # tie among three -> 7
+    z[2, V - 1] = 60.0                   # max at the last index
+    y = rng.integers(0, V, N).astype(np.int32)
+    y[3] = V - 1
+    per_ref = O.loss_from_logits(z.astype(np.float64), y)[1]
+    dz_ref = O.cross_entropy_grad(z.astype(np.float64), y)
+    am_ref = O.argmax_lowest(z)
+    tz, ty = torch.from_numpy(z).cuda(), torch.from_numpy(y).cuda()
+    dz = torch.empty(N, V, device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    rl = torch.empty(N, device="cuda")
+    am = torch.empty(N, device="cuda", dtype=torch.int32)
+    err = torch.zeros(4, device="cuda", dtype=torch.int32)
+    B.cross_entropy(DT[dtype], tz, ty, dz, rl, am, N, V, 1.0 / N, err)
+    torch.cuda.synchronize()
+    assert err.cpu().numpy()[0] == 0
+    np.testing.assert_array_equal(am.cpu().numpy(), am_ref)
+    assert np.abs(rl.cpu().numpy() - per_ref).max() < 1e-5 * np.abs(per_ref).max()
+    assert rel_l2(from_dev(dz), dz_ref) < (4e-3 if dtype == "bf16" else 1e-6)
+    # error flags: a target out of range, a non-finite logit
+    y2 = y.copy(); y2[4] = V
+    z2 = z.copy(); z2[5, 3] = np.inf
+    B.cross_entropy(DT[dtype], torch.from_numpy(z2).cuda(), torch.from_numpy(y2).cuda(), dz, rl, am, N, V,
+                    1.0 / N, err)
+    torch.cuda.synchronize()
+    assert err.cpu().numpy()[0] == 3
+
+
+# ----------------------------------------------------------------------------- embedding
+
+
+@pytest.mark.parametrize("N,V,d,dist", [(512, 4096, 128, "uniform"), (8192, 4096, 192, "zipf"),
+                                        (2056, 32768, 1664, "zipf"), (32768, 32768, 1536, "zipf")])
+def test_embedding_gather_scatter(N, V, d, dist):
+    from gpt_pretraining_step_train_amd import inputs
+    say("embedding", N, V, d, dist)
+    tok, _ = inputs.token_batch(1, N, V, dist=dist, seed=5)
+    tok = tok.reshape(-1)
+    rng = np.random.default_rng(6)
+    E = rng.standard_normal((V, d)).astype(np.float32)
+    dh = rng.standard_normal((N, d)).astype(np.float32)
+    tt = torch.from_numpy(tok).cuda()
+    tE = torch.from_numpy(E).cuda()
+    h = torch.empty(N, d, device="cuda")
+    err = torch.zeros(4, device="cuda", dtype=torch.int32)
+    B.embed_gather(tt, tE, h, N, d, V, err)
+    ws = torch.empty(B.embed_ws_bytes(N, V, d), device="cuda", dtype=torch.uint8)
+    dE = torch.full((V, d), float("nan"), device="cuda")
+    srt = torch.empty(N, device="cuda", dtype=torch.int32)
+    B.embed_scatter(tt, torch.from_numpy(dh).cuda(), dE, N, V, d, ws, srt)
+    torch.cuda.synchronize()
+    assert err.cpu().numpy()[0] == 0
+    np.testing.assert_array_equal(h.cpu().numpy(), E[tok])                       # bit-exact copy
+    np.testing.assert_array_equal(srt.cpu().numpy(), np.argsort(tok, kind="stable"))
+    ref = np.zeros((V, d))
+    np.add.at(ref, tok, dh.astype(np.float64))
+    got = dE.cpu().numpy()
+    absent = np.bincount(tok, minlength=V) == 0
+    assert np.all(got[absent] == 0.0)
+    assert np.abs(got - ref).max() < 1e-4 * max(1.0, np.sqrt(np.bincount(tok).max()))
+    # determinism
+    dE2 = torch.empty_like(dE)
+    B.embed_scatter(tt, torch.from_numpy(dh).cuda(), dE2, N, V, d, ws, srt)
+    torch.cuda.synchronize()
+    assert torch.equal(dE, dE2)
+    bad = tok.copy(); bad[7] = V
+    B.embed_gather(torch.from_numpy(bad).cuda(), tE, h, N, d, V, err)
+    torch.cuda.synchronize()
+    assert err.cpu().numpy()[0] == 1

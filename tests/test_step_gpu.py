@@ -1,0 +1,176 @@
+"""Whole-step parity of the HIP path (gpt_step + muon_update through the C ABI)
+against the fp64 oracle on identical host-generated weights and tokens.
+
+Bars: loss relative error <= 1e-3 and per-tensor gradient / update relative L2
+<= 2e-2 (bf16 and fp32); integer work bit-exact.  The tiny config runs in fp32
+and is also held to the tighter bounds fp32 arithmetic gives.  The d12 config
+runs at batch 1 (full width, depth, vocabulary and sequence length).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpt_pretraining_step_train_amd import binding, configs, inputs
+from oracle import gpt_oracle as O
+from oracle import polar_express as PE
+from tests.gpu_util import rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+LR = 0.02
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+    torch.cuda.set_device(0)
+
+
+def _setup(name, seed=0, **over):
+    cfg = configs.get(name, **over)
+    model = binding.Model(cfg, seed=seed)
+    params = inputs.init_weights(cfg, seed)
+    model.set_all_params(params)
+    tok, tgt = inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=seed)
+    return cfg, model, params, tok, tgt
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1})]
+
+
+@pytest.mark.parametrize("name,over", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_step_and_muon_parity(name, over):
+    say("step parity", name, over)
+    cfg, model, params, tok, tgt = _setup(name, **over)
+    loss = model.step(_dev(tok), _dev(tgt))
+    torch.cuda.synchronize()
+    ref_loss, ref_grads, ref_am, ref_rows = O.loss_and_grads(params, tok, tgt, cfg)
+    fp32 = cfg["precision"] == "fp32"
+    lrel = abs(loss - ref_loss) / abs(ref_loss)
+    say(f"  loss {loss:.7f} oracle {ref_loss:.7f} rel {lrel:.2e}")
+    assert lrel <= (1e-5 if fp32 else 1e-3)
+    rows = model.row_loss().cpu().numpy().reshape(tok.shape)
+    assert rel_l2(rows, ref_rows) < (1e-5 if fp32 else 2e-3)
+    am = model.argmax().cpu().numpy().reshape(tok.shape)
+    assert np.mean(am == ref_am) > (0.999 if fp32 else 0.95)
+    worst = 0.0
+    grads = []
+    for i, ref in enumerate(ref_grads):
+        g = model.grads(i)
+        grads.append(g)
+        e = rel_l2(g, ref)
+        worst = max(worst, e)
+        assert e <= (1e-4 if fp32 else 2e-2), (i, e)
+    say(f"  worst grad rel L2 {worst:.2e}")
+    # Muon fed the GPU's own gradients (and zero momentum) on both sides
+    table, _ = PE.coefficients()
+    L = cfg["depth"]
+    ids = list(range(1, 1 + 6 * L))
+    if len(ids) > 12:
+        ids = ids[:6] + ids[-6:]
+    before = {i: model.get_params(i) for i in ids}
+    model.muon_update(LR)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i in ids:
+        X, Bm = O.muon_matrix(grads[i], np.zeros_like(grads[i]), table, mu=cfg["muon_momentum"])
+        upd = model.get_params(i).astype(np.float64) - before[i]
+        e = rel_l2(upd, -LR * X)
+        worst = max(worst, e)
+        assert e <= (1e-4 if fp32 else 2e-2), (i, e)
+        np.testing.assert_array_equal(model.get_momentum(i), grads[i])
+    say(f"  worst Muon update rel L2 {worst:.2e}")
+    # E and U untouched
+    np.testing.assert_array_equal(model.get_params(0), params[0])
+    np.testing.assert_array_equal(model.get_params(1 + 6 * L), params[-1])
+
+
+def test_second_muon_step_uses_momentum():
+    cfg, model, params, tok, tgt = _setup("laptop", batch=4)
+    table, _ = PE.coefficients()
+    rng = np.random.default_rng(3)
+    i = 5  # layer 0 W1 [F, d]
+    shp = model.shape(i)
+    G1, G2 = rng.standard_normal(shp).astype(np.float32), rng.standard_normal(shp).astype(np.float32)
+    model.set_grads(i, G1)
+    model.muon_update(LR)
+    w1 = model.get_params(i)
+    model.set_grads(i, G2)
+    model.muon_update(LR)
+    w2 = model.get_params(i)
+    X2, B2 = O.muon_matrix(G2, G1.astype(np.float64), table, mu=cfg["muon_momentum"])
+    np.testing.assert_allclose(model.get_momentum(i), B2, rtol=1e-6, atol=1e-6)
+    assert rel_l2(w2.astype(np.float64) - w1, -LR * X2) < 2e-2
+
+
+def test_step_is_deterministic_and_causal():
+    cfg, model, params, tok, tgt = _setup("laptop", batch=8)
+    l1 = model.step(_dev(tok), _dev(tgt))
+    g1 = [model.grads(i) for i in (0, 3, len(params) - 1)]
+    r1 = model.row_loss().cpu().numpy().reshape(tok.shape)
+    l2 = model.step(_dev(tok), _dev(tgt))
+    g2 = [model.grads(i) for i in (0, 3, len(params) - 1)]
+    assert l1 == l2
+    for a, b in zip(g1, g2):
+        np.testing.assert_array_equal(a, b)
+    t = 100
+    tok2 = tok.copy()
+    tok2[:, t + 1] = (tok2[:, t + 1] + 7) % cfg["vocab"]
+    model.step(_dev(tok2), _dev(tgt))
+    r2 = model.row_loss().cpu().numpy().reshape(tok.shape)
+    np.testing.assert_array_equal(r1[:, : t + 1], r2[:, : t + 1])
+    assert not np.array_equal(r1[:, t + 1], r2[:, t + 1])
+
+
+def test_error_paths():
+    cfg, model, params, tok, tgt = _setup("tiny")
+    bad = tok.copy()
+    bad[1, 5] = cfg["vocab"]
+    with pytest.raises(binding.GptError, match="token id out of range"):
+        model.step(_dev(bad), _dev(tgt))
+    badt = tgt.copy()
+    badt[0, 0] = -1
+    with pytest.raises(binding.GptError, match="token id out of range"):
+        model.step(_dev(tok), _dev(badt))
+    w = params[-1].copy()
+    w[3, 3] = np.nan
+    model.set_params(len(params) - 1, w)
+    with pytest.raises(binding.GptError, match="non-finite"):
+        model.step(_dev(tok), _dev(tgt))
+    other = binding.make_cfg(configs.get("tiny", batch=2))
+    loss = binding.lib().gpt_step(model._h, binding._ptr(_dev(tok)), binding._ptr(_dev(tgt)),
+                                  binding.ctypes.byref(other), binding._stream())
+    assert np.isnan(loss) and binding.lib().gpt_last_status(model._h) == 2
+
+
+def test_zero_head_gives_uniform_loss():
+    cfg, model, params, tok, tgt = _setup("laptop", batch=4)
+    model.set_params(len(params) - 1, np.zeros_like(params[-1]))
+    loss = model.step(_dev(tok), _dev(tgt))
+    assert abs(loss - np.log(cfg["vocab"])) < 1e-6
+    assert np.all(model.argmax().cpu().numpy() == 0)
+    assert np.all(model.grads(3) == 0)
+
+
+def test_device_init_statistics():
+    """gpt_init's counter-based N(0, std^2) weights (no host upload)."""
+    cfg = configs.get("laptop", batch=2)
+    model = binding.Model(cfg, seed=7)
+    E = model.get_params(0)
+    Wo = model.get_params(4)
+    L = cfg["depth"]
+    assert abs(E.std() - 0.02) < 0.02 * 0.01
+    assert abs(Wo.std() - 0.02 / np.sqrt(2 * L)) < 0.02 / np.sqrt(2 * L) * 0.02
+    assert abs(E.mean()) < 1e-4
+    model2 = binding.Model(cfg, seed=7)
+    np.testing.assert_array_equal(model2.get_params(0), E)
+    tok, tgt = inputs.token_batch(2, cfg["seq_len"], cfg["vocab"], seed=1)
+    loss = model.step(_dev(tok), _dev(tgt))
+    want = np.log(cfg["vocab"]) + 0.5 * 0.02 ** 2 * cfg["d_model"]
+    assert abs(loss - want) < 0.05
