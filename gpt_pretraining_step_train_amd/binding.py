@@ -63,7 +63,7 @@ _SIGS = {
     "gpt_prof_read": (_I, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)]),
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
-    "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I]),
+    "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gptk_rmsnorm_fwd": (_I, [_I, _P, _P, _P, _I, _I, _F, _P]),
@@ -240,8 +240,8 @@ def gemm(dtype, a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, 
                           _ptr(C), ldc, sC, tile, splits, ws_p, ws_b, _stream()), "gptk_gemm")
 
 
-def gemm_kernel_name(dtype, M, N, K, batch=1) -> str:
-    return lib().gpt_gemm_kernel_name(dtype, M, N, K, batch).decode()
+def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
+    return lib().gpt_gemm_kernel_name(dtype, a_kmaj, b_kmaj, M, N, K, batch).decode()
 
 
 def attn_fwd(dtype, qkv, o, lse, B, T, H, hd):

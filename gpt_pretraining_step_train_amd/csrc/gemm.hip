@@ -169,21 +169,31 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
       la.load(A, p.lda, m0, p.M, kbeg + (it + 1) * BK, kend, tid);
       lb.load(B, p.ldb, n0, p.N, kbeg + (it + 1) * BK, kend, tid);
     }
-    const bf16_t* as = As[cur];
-    const bf16_t* bs = Bs[cur];
+    const bf16_t* as = As[cur] + (wm * TM + lr) * LDSS + lk;
+    const bf16_t* bs = Bs[cur] + (wn * TN + lr) * LDSS + lk;
+    // fragments double-buffered across the 16-wide k steps so LDS reads overlap MFMAs
+    bf16x8_t af[2][FM], bfv[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LDSS);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfv[0][j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * LDSS);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[FM], bfv[FN];
+      const int c = kk & 1;
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LDSS + (kk + 1) * 16);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfv[c ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * LDSS + (kk + 1) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the next step's LDS reads ahead of these MFMAs
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm * TM + i * 32 + lr) * LDSS + kk * 16 + lk);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfv[j] = *reinterpret_cast<const bf16x8_t*>(bs + (wn * TN + j * 32 + lr) * LDSS + kk * 16 + lk);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[i], bfv[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bfv[c][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 < nk) {
       la.store(As[cur ^ 1], tid);
@@ -192,22 +202,56 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // epilogue
+  // epilogue through LDS, one 32-row block of every wave at a time: the accumulator
+  // fragments go to LDS with constant register indices, then each wave reads its
+  // 32 x TN block back row by row (two adjacent columns per lane) for coalesced stores
+  constexpr int CS = TN + 4;  // fp32 row stride of the staging block
+  static_assert(WM * WN * 32 * CS * 4 <= 2 * BM * LDSS * 2, "staging block must fit in As");
+  static_assert(TN == 64 || TN % 128 == 0, "epilogue column mapping");
+  float* stage = reinterpret_cast<float*>(&As[0][0]) + wave * 32 * CS;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TM + i * 32 + acc_row(lane, r);
-        const int col = n0 + wn * TN + j * 32 + lr;
-        if (row < p.M && col < p.N) {
-          if (p.splits > 1)
-            p.ws[((long)blockIdx.y * p.M + row) * p.N + col] = acc[i][j][r];
-          else
-            epilogue_elem<bf16_t>(p, bz, row, col, acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r];
+    __syncthreads();
+    const int row0 = m0 + wm * TM + i * 32;
+    for (int rr = 0; rr < 32; ++rr) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+#pragma unroll
+      for (int cc = 0; cc < TN / 128; ++cc) {
+        const int lc = cc * 128 + lane * 2;
+        const int col = n0 + wn * TN + lc;
+        const float v0 = stage[rr * CS + lc], v1 = stage[rr * CS + lc + 1];
+        if (p.splits > 1) {
+          float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
+          if (col < p.N) w[0] = v0;
+          if (col + 1 < p.N) w[1] = v1;
+        } else {
+          if (col < p.N) epilogue_elem<bf16_t>(p, bz, row, col, v0);
+          if (col + 1 < p.N) epilogue_elem<bf16_t>(p, bz, row, col + 1, v1);
         }
       }
+      if (TN % 128) {  // TN = 64: lanes 0..31 cover the row
+        const int lc = lane * 2;
+        const int col = n0 + wn * TN + lc;
+        if (lc < TN) {
+          const float v0 = stage[rr * CS + lc], v1 = stage[rr * CS + lc + 1];
+          if (p.splits > 1) {
+            float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
+            if (col < p.N) w[0] = v0;
+            if (col + 1 < p.N) w[1] = v1;
+          } else {
+            if (col < p.N) epilogue_elem<bf16_t>(p, bz, row, col, v0);
+            if (col + 1 < p.N) epilogue_elem<bf16_t>(p, bz, row, col + 1, v1);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -343,9 +387,18 @@ int gemm_auto_splits(const GemmArgs& p) {
   return s;
 }
 
+// one name per kernel instantiation: tile and operand layouts (N = reduction index
+// contiguous, T = transposed on load), as "gemm_bf16_kernel<256,256,NT>"
 const char* gemm_kernel_name(const GemmArgs& p) {
-  if (p.dtype == ACT_F32) return "gemm_f32_kernel";
-  return pick_tile(p) == 1 ? "gemm_bf16_kernel<256,256>" : "gemm_bf16_kernel<128,128>";
+  static const char* names[3][4] = {
+      {"gemm_f32_kernel<NT>", "gemm_f32_kernel<NN>", "gemm_f32_kernel<TN>", "gemm_f32_kernel<TT>"},
+      {"gemm_bf16_kernel<256,256,NT>", "gemm_bf16_kernel<256,256,NN>", "gemm_bf16_kernel<256,256,TN>",
+       "gemm_bf16_kernel<256,256,TT>"},
+      {"gemm_bf16_kernel<128,128,NT>", "gemm_bf16_kernel<128,128,NN>", "gemm_bf16_kernel<128,128,TN>",
+       "gemm_bf16_kernel<128,128,TT>"}};
+  const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
+  const int t = p.dtype == ACT_F32 ? 0 : pick_tile(p);
+  return names[t][lay];
 }
 
 int launch_gemm(const GemmArgs& p0, hipStream_t st) {

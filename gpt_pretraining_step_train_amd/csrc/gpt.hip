@@ -771,9 +771,10 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
-const char* gpt_gemm_kernel_name(int dtype, int M, int N, int K, int batch) {
+const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch) {
   GemmArgs p;
   p.M = M; p.N = N; p.K = K; p.batch = batch; p.dtype = act_type(dtype) < 0 ? ACT_BF16 : act_type(dtype);
+  p.a_kmaj = a_kmaj != 0; p.b_kmaj = b_kmaj != 0;
   return gemm_kernel_name(p);
 }
 

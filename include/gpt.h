@@ -149,8 +149,10 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
               long sA, const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits,
               void* ws, size_t ws_bytes, void* stream);
 
-/* name of the kernel gptk_gemm / gpt_step would launch for these sizes */
-const char* gpt_gemm_kernel_name(int dtype, int M, int N, int K, int batch);
+/* name of the GEMM kernel instantiation gptk_gemm / gpt_step launch for these
+ * layouts and sizes, e.g. "gemm_bf16_kernel<256,256,NT>" (NT: both operands have
+ * the reduction index contiguous; NN: B transposed on load; TN: both) */
+const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch);
 
 /* causal attention over qkv act [B*T][3*H*hd] -> o act [B*T][H*hd], lse fp32
  * [B][H][T] (natural log of the sum of exp of q.k/sqrt(hd)). hd in {32,64,128}. */

@@ -147,8 +147,10 @@ def test_attention_fwd_bwd(case):
     torch.cuda.synchronize()
     g = from_dev(dqkv).reshape(Bn, T, 3, H, hd)
     gtol = 2e-2 if dtype == "bf16" else 1e-4
+    # relative to the largest of the three references: at T = 1 dq and dk are exactly 0
+    scale = max(np.linalg.norm(r) for r in (dq_ref, dk_ref, dv_ref))
     for i, ref in enumerate((dq_ref, dk_ref, dv_ref)):
-        e = rel_l2(g[:, :, i], ref)
+        e = np.linalg.norm(g[:, :, i] - ref) / max(np.linalg.norm(ref), 1e-3 * scale)
         assert e < gtol, (i, e)
 
 
