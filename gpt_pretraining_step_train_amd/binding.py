@@ -26,6 +26,7 @@ class GptCfg(ctypes.Structure):
         ("init_std", ctypes.c_float), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("muon_momentum", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("ns_coeffs", (ctypes.c_float * 3) * 5), ("num_steps", ctypes.c_int64),
+        ("ns_split_steps", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
     def coeffs(self):
@@ -63,6 +64,7 @@ _SIGS = {
     "gpt_prof_read": (_I, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)]),
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
+    "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -116,6 +118,8 @@ def make_cfg(c: dict) -> GptCfg:
             setattr(cfg, k, float(c[k]))
     if "ns_steps" in c:
         cfg.ns_steps = int(c["ns_steps"])
+    if "ns_split_steps" in c:
+        cfg.ns_split_steps = int(c["ns_split_steps"])
     if "ns_coeffs" in c:
         for i, abc in enumerate(c["ns_coeffs"]):
             for j in range(3):
@@ -238,6 +242,11 @@ def gemm(dtype, a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, 
     ws_b = ws.numel() * ws.element_size() if ws is not None else 0
     check(lib().gptk_gemm(dtype, int(a_kmaj), int(b_kmaj), M, N, K, batch, _ptr(A), lda, sA, _ptr(B), ldb, sB,
                           _ptr(C), ldc, sC, tile, splits, ws_p, ws_b, _stream()), "gptk_gemm")
+
+
+def gemm_split(a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, sB=0, sC=0):
+    check(lib().gptk_gemm_split(int(a_kmaj), int(b_kmaj), M, N, K, batch, _ptr(A), lda, sA, _ptr(B), ldb, sB,
+                                _ptr(C), ldc, sC, _stream()), "gptk_gemm_split")
 
 
 def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:

@@ -51,8 +51,8 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 
 struct Offsets {
   size_t params, grads, mom, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
-      dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, Af,
-      Aa, Ba, ss_part, ss, mat_off, mat_size, rope, loss, err;
+      dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xf2, xa0, xa1,
+      Af, Aa, Ba, Bf, ss_part, ss, mat_off, mat_size, rope, loss, err;
   size_t splitws_bytes;
 };
 
@@ -116,11 +116,13 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.splitws = P.add(std::max<size_t>(O.splitws_bytes, 256));
   O.embws = P.add(embed_ws_bytes((int)N, (int)V, (int)d));
   O.xf = P.add(nBlk * 4);
+  O.xf2 = P.add(nBlk * 4);
   O.xa0 = P.add(nBlk * es);
   O.xa1 = P.add(nBlk * es);
   O.Af = P.add(std::max(4 * L * d * d, 2 * L * s * s) * 4);
   O.Aa = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
   O.Ba = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
+  O.Bf = P.add(std::max(4 * L * d * d, 2 * L * s * s) * 4);
   (void)l;
   O.ss_part = P.add(6 * L * kSumsqParts * 8);
   O.ss = P.add(6 * L * 8);
@@ -246,6 +248,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->norm_eps = 1e-6f;
   out->muon_momentum = 0.95f;
   out->ns_steps = 5;
+  out->ns_split_steps = 3;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
   out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
@@ -264,7 +267,7 @@ int gpt_cfg_validate(const gpt_cfg* c) {
   if (((long)c->batch * c->seq_len) % 8) return GPT_ERR_SHAPE;
   if ((long)c->batch * c->seq_len > (1L << 30) / 4) return GPT_ERR_UNSUPPORTED;
   if (c->precision != GPT_FP32 && c->precision != GPT_BF16) return GPT_ERR_UNSUPPORTED;
-  if (c->ns_steps < 0 || c->ns_steps > 5) return GPT_ERR_ARG;
+  if (c->ns_steps < 0 || c->ns_steps > 5 || c->ns_split_steps < 0) return GPT_ERR_ARG;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
 }
@@ -612,45 +615,59 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   struct Batch { int s, l, nb; size_t off; };
   const Batch batches[2] = {{d, d, 4 * L, 0}, {s, lw, 2 * L, (size_t)4 * L * d * d}};
   float* Af = M->at_off<float>(O.Af);
+  float* Bf = M->at_off<float>(O.Bf);
   void* Aa = M->base + O.Aa;
   void* Ba = M->base + O.Ba;
+  float* xfb[2] = {xf, M->at_off<float>(O.xf2)};
+  // the leading iterations run on fp32 operands split into bf16 hi + lo (three MFMA
+  // products each): rounding errors of the early iterations are amplified by the later
+  // ones along small singular directions, those of the last iterations are not
+  const int nsplit = M->at == ACT_BF16 ? std::min(c.ns_split_steps, c.ns_steps) : 0;
   int rc;
   for (const Batch& bt : batches) {
     int cur = 0;
     const long ss = (long)bt.s * bt.s, sl = (long)bt.s * bt.l;
     for (int it = 0; it < c.ns_steps; ++it) {
       const float a = c.ns_coeffs[it][0], b = c.ns_coeffs[it][1], cc = c.ns_coeffs[it][2];
+      const bool sp = it < nsplit;
+      const bool next_bf = it + 1 < c.ns_steps && it + 1 >= nsplit;
+      const void* xop = sp ? (const void*)(xfb[cur] + bt.off) : (const void*)(xa[cur] + bt.off * es);
       {
         GemmArgs p;  // A = X X^T
+        p.split = sp;
         p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
-        p.A = xa[cur] + bt.off * es; p.lda = bt.l; p.strideA = sl;
-        p.B = xa[cur] + bt.off * es; p.ldb = bt.l; p.strideB = sl;
+        p.A = xop; p.lda = bt.l; p.strideA = sl;
+        p.B = xop; p.ldb = bt.l; p.strideB = sl;
         p.outF = Af; p.ldo = bt.s; p.strideO = ss;
-        p.outA = Aa; p.ldoa = bt.s; p.strideOA = ss;
+        if (!sp) { p.outA = Aa; p.ldoa = bt.s; p.strideOA = ss; }
         if ((rc = run_gemm(M, p, st, false))) return rc;
       }
       {
         GemmArgs p;  // Bm = b A + c A A   (A symmetric)
+        p.split = sp;
         p.M = bt.s; p.N = bt.s; p.K = bt.s; p.batch = bt.nb;
-        p.A = Aa; p.lda = bt.s; p.strideA = ss;
-        p.B = Aa; p.ldb = bt.s; p.strideB = ss;
+        p.A = sp ? (const void*)Af : Aa; p.lda = bt.s; p.strideA = ss;
+        p.B = sp ? (const void*)Af : Aa; p.ldb = bt.s; p.strideB = ss;
         p.alpha = cc; p.beta = b; p.Cin = Af; p.ldcin = bt.s; p.strideCin = ss;
-        p.outA = Ba; p.ldoa = bt.s; p.strideOA = ss;
+        if (sp) { p.outF = Bf; p.ldo = bt.s; p.strideO = ss; }
+        else { p.outA = Ba; p.ldoa = bt.s; p.strideOA = ss; }
         if ((rc = run_gemm(M, p, st, false))) return rc;
       }
       {
-        GemmArgs p;  // X <- a X + Bm X
+        GemmArgs p;  // X' = a X + Bm X
+        p.split = sp;
         p.M = bt.s; p.N = bt.l; p.K = bt.s; p.batch = bt.nb;
-        p.A = Ba; p.lda = bt.s; p.strideA = ss;
-        p.B = xa[cur] + bt.off * es; p.ldb = bt.l; p.strideB = sl; p.b_kmaj = false;
-        p.beta = a; p.Cin = xf + bt.off; p.ldcin = bt.l; p.strideCin = sl;
-        p.outF = xf + bt.off; p.ldo = bt.l; p.strideO = sl;
-        p.outA = xa[cur ^ 1] + bt.off * es; p.ldoa = bt.l; p.strideOA = sl;
+        p.A = sp ? (const void*)Bf : Ba; p.lda = bt.s; p.strideA = ss;
+        p.B = xop; p.ldb = bt.l; p.strideB = sl; p.b_kmaj = false;
+        p.beta = a; p.Cin = xfb[cur] + bt.off; p.ldcin = bt.l; p.strideCin = sl;
+        p.outF = xfb[cur ^ 1] + bt.off; p.ldo = bt.l; p.strideO = sl;
+        if (next_bf) { p.outA = xa[cur ^ 1] + bt.off * es; p.ldoa = bt.l; p.strideOA = sl; }
         if ((rc = run_gemm(M, p, st, false))) return rc;
       }
       cur ^= 1;
     }
   }
+  xf = xfb[c.ns_steps & 1];
   float* wblk = M->blk(M->params());
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
@@ -768,6 +785,19 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc == 1) return GPT_ERR_ARG;
   if (rc == 2) return GPT_ERR_SHAPE;
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const float* A, long lda, long sA,
+                    const float* B, long ldb, long sB, float* C, long ldc, long sC, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || batch < 0 || !C || !A || !B) return GPT_ERR_ARG;
+  GemmArgs p;
+  p.M = M; p.N = N; p.K = K; p.batch = batch; p.split = true; p.dtype = ACT_BF16;
+  p.A = A; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
+  p.B = B; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
+  p.outF = C; p.ldo = ldc; p.strideO = sC;
+  const int rc = launch_gemm(p, (hipStream_t)stream);
+  if (rc) return rc == 1 ? GPT_ERR_ARG : GPT_ERR_SHAPE;
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 

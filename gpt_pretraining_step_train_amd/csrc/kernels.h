@@ -30,6 +30,10 @@ struct GemmArgs {
   int splits = 1;                 // split-K factor; >1 needs ws
   float* ws = nullptr; size_t ws_bytes = 0;
   int tile = 0;                   // 0 = auto, 1 = 256x256, 2 = 128x128
+  // split: A and B are fp32; each is split on load into bf16 hi + bf16 lo (the
+  // rounding residual) and the product is accumulated as hi*hi + hi*lo + lo*hi
+  // (bf16 MFMA, ~16 significant bits per operand)
+  bool split = false;
 };
 
 // returns 0 on success, else an error code (argument/shape problems)

@@ -68,6 +68,9 @@ typedef struct gpt_cfg {
   int32_t ns_steps;   /* Newton-Schulz iterations, 0..5 */
   float ns_coeffs[5][3]; /* (a, b, c) per iteration */
   int64_t num_steps;  /* informational: steps at a tokens:params ratio of 8 with 2^20-token batches */
+  int32_t ns_split_steps; /* bf16 precision: the first ns_split_steps iterations multiply fp32
+                             operands split into bf16 hi + lo parts (3 MFMA products); default 3 */
+  int32_t reserved;
 } gpt_cfg;
 
 typedef struct gpt_model gpt_model; /* opaque */
@@ -148,6 +151,13 @@ int gpt_prof_read(gpt_model* m, int64_t* launches, double* ms, double* flops);
 int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* A, long lda,
               long sA, const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits,
               void* ws, size_t ws_bytes, void* stream);
+
+/* as gptk_gemm with fp32 operands A and B, each split on load into a bf16 high
+ * part and a bf16 residual; C = Ah*Bh + Ah*Bl + Al*Bh on bf16 MFMA with fp32
+ * accumulation (the product Muon's Newton-Schulz uses in its early iterations).
+ * Row counts of transposed operands and K must be multiples of 8. */
+int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const float* A, long lda, long sA,
+                    const float* B, long ldb, long sB, float* C, long ldc, long sC, void* stream);
 
 /* name of the GEMM kernel instantiation gptk_gemm / gpt_step launch for these
  * layouts and sizes, e.g. "gemm_bf16_kernel<256,256,NT>" (NT: both operands have

@@ -62,7 +62,8 @@ def test_default_ns_table(lib):
     c = binding.GptCfg()
     lib.gpt_cfg_from_depth(24, ctypes.byref(c))
     tab = c.coeffs()
-    assert c.ns_steps == gold["ns_steps"]
+    assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 3
+    assert ctypes.sizeof(binding.GptCfg) == 136
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
     derived, _ = polar_express.coefficients()
     np.testing.assert_allclose(tab[2:], derived[2:], rtol=0, atol=2e-5)

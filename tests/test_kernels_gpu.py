@@ -71,6 +71,27 @@ def test_gemm_layouts_tails_batch_split(case):
     assert err < (1e-5 if dtype == "bf16" else 1e-5), err
 
 
+SPLIT_CASES = [(1, 1, 300, 200, 136, 1), (1, 0, 296, 264, 264, 2), (0, 0, 136, 200, 1032, 1), (0, 1, 128, 72, 72, 1)]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_gemm_split_precision(case):
+    """fp32 operands split into bf16 hi + lo: ~16-bit operands, far tighter than bf16."""
+    ak, bk, M, N, K, batch = case
+    rng = np.random.default_rng(K + M)
+    A = rng.standard_normal((batch, M, K) if ak else (batch, K, M)).astype(np.float32)
+    Bm = rng.standard_normal((batch, N, K) if bk else (batch, K, N)).astype(np.float32)
+    Am = A if ak else A.transpose(0, 2, 1)
+    Bn = Bm if bk else Bm.transpose(0, 2, 1)
+    ref = np.einsum("zmk,znk->zmn", Am.astype(np.float64), Bn.astype(np.float64))
+    C = torch.full((batch, M, N), float("nan"), device="cuda")
+    B.gemm_split(ak, bk, M, N, K, torch.from_numpy(A).cuda(), K if ak else M, torch.from_numpy(Bm).cuda(),
+                 K if bk else N, C, N, batch=batch, sA=A[0].size, sB=Bm[0].size, sC=M * N)
+    torch.cuda.synchronize()
+    got = from_dev(C)
+    assert np.abs(got - ref).max() / np.abs(ref).max() < 5e-5
+
+
 def test_gemm_full_size_sampled():
     """d24 MLP up-projection shape [32768 x 6144 x 1536] in the launch configuration of
     the step; 4096 sampled outputs recomputed one by one in fp64."""
