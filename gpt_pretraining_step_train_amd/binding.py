@@ -64,7 +64,7 @@ _SIGS = {
     "gpt_prof_read": (_I, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)]),
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
-    "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _P]),
+    "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _L, _L, _P, _L, _L, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -244,9 +244,9 @@ def gemm(dtype, a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, 
                           _ptr(C), ldc, sC, tile, splits, ws_p, ws_b, _stream()), "gptk_gemm")
 
 
-def gemm_split(a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, sB=0, sC=0):
-    check(lib().gptk_gemm_split(int(a_kmaj), int(b_kmaj), M, N, K, batch, _ptr(A), lda, sA, _ptr(B), ldb, sB,
-                                _ptr(C), ldc, sC, _stream()), "gptk_gemm_split")
+def gemm_split(a_kmaj, b_kmaj, M, N, K, Ah, Al, lda, Bh, Bl, ldb, C, ldc, batch=1, sA=0, sB=0, sC=0):
+    check(lib().gptk_gemm_split(int(a_kmaj), int(b_kmaj), M, N, K, batch, _ptr(Ah), _ptr(Al), lda, sA, _ptr(Bh),
+                                _ptr(Bl), ldb, sB, _ptr(C), ldc, sC, _stream()), "gptk_gemm_split")
 
 
 def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:

@@ -540,9 +540,16 @@ __global__ void sumsq_final_kernel(const double* partial, int parts, int nmat, d
 
 // X = src / (sqrt(sumsq) + eps), written transposed ([cols][rows]) when asked; 32x32 LDS tiles
 template <typename T>
+__device__ inline void st_hilo(T* hi, T* lo, long o, float v) {
+  st<T>(hi + o, v);
+  if (lo) st<T>(lo + o, v - ld<T>(hi + o));
+}
+
+template <typename T>
 __global__ void __launch_bounds__(256) ns_normalize_kernel(const float* __restrict__ src, const double* sumsq, int mat,
                                                            float eps, int rows, int cols, int transpose,
-                                                           float* __restrict__ xf, T* __restrict__ xa) {
+                                                           float* __restrict__ xf, T* __restrict__ xa,
+                                                           T* __restrict__ xlo) {
   __shared__ float tile[32][33];
   const float scale = (float)(1.0 / (sqrt(sumsq[mat]) + (double)eps));
   const int tr = blockIdx.y * 32, tc = blockIdx.x * 32;
@@ -553,7 +560,7 @@ __global__ void __launch_bounds__(256) ns_normalize_kernel(const float* __restri
       if (r < rows && c < cols) {
         const float v = src[(long)r * cols + c] * scale;
         xf[(long)r * cols + c] = v;
-        st<T>(xa + (long)r * cols + c, v);
+        st_hilo<T>(xa, xlo, (long)r * cols + c, v);
       }
     }
     return;
@@ -568,7 +575,7 @@ __global__ void __launch_bounds__(256) ns_normalize_kernel(const float* __restri
     if (r < rows && c < cols) {
       const float v = tile[tx][i];
       xf[(long)c * rows + r] = v;
-      st<T>(xa + (long)c * rows + r, v);
+      st_hilo<T>(xa, xlo, (long)c * rows + r, v);
     }
   }
 }
@@ -744,14 +751,14 @@ void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, in
 }
 
 void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols, bool tr,
-                         float* xf, void* xa, int at, hipStream_t st) {
+                         float* xf, void* xa, void* xlo, int at, hipStream_t st) {
   dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(ns_normalize_kernel<bf16_t>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
-                       (bf16_t*)xa);
+                       (bf16_t*)xa, (bf16_t*)xlo);
   else
     hipLaunchKernelGGL(ns_normalize_kernel<float>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
-                       (float*)xa);
+                       (float*)xa, (float*)nullptr);
 }
 
 void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int rows, int cols, bool tr,

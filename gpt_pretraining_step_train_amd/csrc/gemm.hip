@@ -107,7 +107,11 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
   if (p.epi == EPI_LINEAR) {
     if (p.Cin) v += p.beta * p.Cin[bz * p.strideCin + (long)row * p.ldcin + col];
     if (p.outF) p.outF[bz * p.strideO + (long)row * p.ldo + col] = v;
-    if (p.outA) store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + bz * p.strideOA + (long)row * p.ldoa + col, v);
+    if (p.outA) {
+      const long o = bz * p.strideOA + (long)row * p.ldoa + col;
+      store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
+      if (p.outA_lo) store_act<OutT>(reinterpret_cast<OutT*>(p.outA_lo) + o, v - load_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o));
+    }
   } else if (p.epi == EPI_RELU2) {
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
@@ -138,10 +142,18 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
   const int kper = ((p.K + p.splits - 1) / p.splits + BK - 1) / BK * BK;
   const int kbeg = sk * kper;
   const int kend = min(p.K, kbeg + kper);
-  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int nks = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;  // k tiles per segment
+  const int nseg = p.split ? 3 : 1;                                 // hi*hi, hi*lo, lo*hi
+  const int nk = nks * nseg;
 
-  const bf16_t* A = reinterpret_cast<const bf16_t*>(p.A) + bz * p.strideA;
-  const bf16_t* B = reinterpret_cast<const bf16_t*>(p.B) + bz * p.strideB;
+  const bf16_t* Ah = reinterpret_cast<const bf16_t*>(p.A) + bz * p.strideA;
+  const bf16_t* Bh = reinterpret_cast<const bf16_t*>(p.B) + bz * p.strideB;
+  const bf16_t* Al = p.split ? reinterpret_cast<const bf16_t*>(p.A_lo) + bz * p.strideA : Ah;
+  const bf16_t* Bl = p.split ? reinterpret_cast<const bf16_t*>(p.B_lo) + bz * p.strideB : Bh;
+  // k tile t: segment t / nks selects the operand planes, (t % nks) the k offset
+  auto seg_a = [&](int t) { return t / nks == 2 ? Al : Ah; };
+  auto seg_b = [&](int t) { return t / nks == 1 ? Bl : Bh; };
+  auto seg_k = [&](int t) { return kbeg + (t % nks) * BK; };
 
   TileLoader<BM, AK, NT> la;
   TileLoader<BN, BKM, NT> lb;
@@ -155,8 +167,8 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
-    lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
+    la.load(seg_a(0), p.lda, m0, p.M, seg_k(0), kend, tid);
+    lb.load(seg_b(0), p.ldb, n0, p.N, seg_k(0), kend, tid);
     la.store(As[0], tid);
     lb.store(Bs[0], tid);
   }
@@ -166,8 +178,8 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
   for (int it = 0; it < nk; ++it) {
     const int cur = it & 1;
     if (it + 1 < nk) {
-      la.load(A, p.lda, m0, p.M, kbeg + (it + 1) * BK, kend, tid);
-      lb.load(B, p.ldb, n0, p.N, kbeg + (it + 1) * BK, kend, tid);
+      la.load(seg_a(it + 1), p.lda, m0, p.M, seg_k(it + 1), kend, tid);
+      lb.load(seg_b(it + 1), p.ldb, n0, p.N, seg_k(it + 1), kend, tid);
     }
     const bf16_t* as = As[cur] + (wm * TM + lr) * LDSS + lk;
     const bf16_t* bs = Bs[cur] + (wn * TN + lr) * LDSS + lk;
@@ -249,196 +261,6 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
           }
         }
       }
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// split-precision GEMM: fp32 operands, each split on load into bf16 hi and lo
-// (lo = bf16 of the residual x - hi), accumulated as hi*hi + hi*lo + lo*hi.
-// 128x128 tile, 4 waves of 64x64; LDS holds hi and lo tiles of both operands.
-
-__device__ inline void split8(const float (&x)[8], uint4& hi, uint4& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const bf16_t h0 = f2bf(x[2 * t]), h1 = f2bf(x[2 * t + 1]);
-    const bf16_t l0 = f2bf(x[2 * t] - bf2f(h0)), l1 = f2bf(x[2 * t + 1] - bf2f(h1));
-    h[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[t] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-template <int R, bool KMAJ, int NT>
-struct SplitLoader {
-  // unit: 8 consecutive k of one row (K-major) or an 8x8 (k, row) block (transposed)
-  static constexpr int NUNIT = KMAJ ? R * (BK / 8) : (R / 8) * (BK / 8);
-  static constexpr int UPT = (NUNIT + NT - 1) / NT;
-  static constexpr int NREG = KMAJ ? UPT * 2 : UPT * 16;
-  float4 regs[NREG];
-
-  __device__ inline void load(const float* __restrict__ base, long ld, int row0, int rows, int k0, int kend, int tid) {
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * NT;
-      if (KMAJ) {
-        const int r = u >> 3, kc = u & 7;
-        const int grow = row0 + r, gk = k0 + kc * 8;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (u < NUNIT && grow < rows && gk < kend) {
-          const float4* q = reinterpret_cast<const float4*>(base + (long)grow * ld + gk);
-          a = q[0];
-          b = q[1];
-        }
-        regs[2 * i] = a;
-        regs[2 * i + 1] = b;
-      } else {
-        const int kb = u & 7, rb = u >> 3;
-        const int grow = row0 + rb * 8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int gk = k0 + kb * 8 + j;
-          float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-          if (u < NUNIT && grow < rows && gk < kend) {
-            const float4* q = reinterpret_cast<const float4*>(base + (long)gk * ld + grow);
-            a = q[0];
-            b = q[1];
-          }
-          regs[i * 16 + 2 * j] = a;
-          regs[i * 16 + 2 * j + 1] = b;
-        }
-      }
-    }
-  }
-
-  __device__ inline void store(bf16_t* hi_t, bf16_t* lo_t, int tid) {
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * NT;
-      if (u >= NUNIT) continue;
-      if (KMAJ) {
-        const int r = u >> 3, kc = u & 7;
-        const float x[8] = {regs[2 * i].x, regs[2 * i].y, regs[2 * i].z, regs[2 * i].w,
-                            regs[2 * i + 1].x, regs[2 * i + 1].y, regs[2 * i + 1].z, regs[2 * i + 1].w};
-        uint4 h, l;
-        split8(x, h, l);
-        *reinterpret_cast<uint4*>(hi_t + r * LDSS + kc * 8) = h;
-        *reinterpret_cast<uint4*>(lo_t + r * LDSS + kc * 8) = l;
-      } else {
-        const int kb = u & 7, rb = u >> 3;
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {  // output row rb*8+rr: element rr of each k row j
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float4 v = regs[i * 16 + 2 * j + (rr >> 2)];
-            const int e = rr & 3;
-            x[j] = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
-          }
-          uint4 h, l;
-          split8(x, h, l);
-          *reinterpret_cast<uint4*>(hi_t + (rb * 8 + rr) * LDSS + kb * 8) = h;
-          *reinterpret_cast<uint4*>(lo_t + (rb * 8 + rr) * LDSS + kb * 8) = l;
-        }
-      }
-    }
-  }
-};
-
-template <bool AK, bool BKM>
-__global__ void __launch_bounds__(256) gemm_split_kernel(GemmArgs p) {
-  constexpr int BM = 128, BN = 128, WN = 2, NT = 256;
-  constexpr int TM = 64, TN = 64, FM = 2, FN = 2;
-  __shared__ __attribute__((aligned(16))) bf16_t Ah[2][BM * LDSS];
-  __shared__ __attribute__((aligned(16))) bf16_t Al[2][BM * LDSS];
-  __shared__ __attribute__((aligned(16))) bf16_t Bh[2][BN * LDSS];
-  __shared__ __attribute__((aligned(16))) bf16_t Bl[2][BN * LDSS];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int tilesM = (p.M + BM - 1) / BM, tilesN = (p.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
-  const int bz = blockIdx.y;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kend = p.K;
-  const int nk = (p.K + BK - 1) / BK;
-  const float* A = reinterpret_cast<const float*>(p.A) + bz * p.strideA;
-  const float* B = reinterpret_cast<const float*>(p.B) + bz * p.strideB;
-  SplitLoader<BM, AK, NT> la;
-  SplitLoader<BN, BKM, NT> lb;
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, 0, kend, tid);
-    lb.load(B, p.ldb, n0, p.N, 0, kend, tid);
-    la.store(Ah[0], Al[0], tid);
-    lb.store(Bh[0], Bl[0], tid);
-  }
-  __syncthreads();
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) {
-      la.load(A, p.lda, m0, p.M, (it + 1) * BK, kend, tid);
-      lb.load(B, p.ldb, n0, p.N, (it + 1) * BK, kend, tid);
-    }
-    const int ao = (wm * TM + lr) * LDSS + lk, bo = (wn * TN + lr) * LDSS + lk;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t ah[FM], al[FM], bh[FN], bl[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        ah[i] = *reinterpret_cast<const bf16x8_t*>(Ah[cur] + ao + i * 32 * LDSS + kk * 16);
-        al[i] = *reinterpret_cast<const bf16x8_t*>(Al[cur] + ao + i * 32 * LDSS + kk * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        bh[j] = *reinterpret_cast<const bf16x8_t*>(Bh[cur] + bo + j * 32 * LDSS + kk * 16);
-        bl[j] = *reinterpret_cast<const bf16x8_t*>(Bl[cur] + bo + j * 32 * LDSS + kk * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = mfma32x32x16_bf16(al[i], bh[j], acc[i][j]);
-          acc[i][j] = mfma32x32x16_bf16(ah[i], bl[j], acc[i][j]);
-          acc[i][j] = mfma32x32x16_bf16(ah[i], bh[j], acc[i][j]);
-        }
-    }
-    if (it + 1 < nk) {
-      la.store(Ah[cur ^ 1], Al[cur ^ 1], tid);
-      lb.store(Bh[cur ^ 1], Bl[cur ^ 1], tid);
-    }
-    __syncthreads();
-  }
-  // epilogue through LDS (as in the bf16 kernel; TN = 64: lanes 0..31 cover a row)
-  constexpr int CS = TN + 4;
-  float* stage = reinterpret_cast<float*>(&Ah[0][0]) + wave * 32 * CS;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r];
-    __syncthreads();
-    const int row0 = m0 + wm * TM + i * 32;
-    const int lc = lane * 2;
-    for (int rr = 0; rr < 32 && lc < TN; ++rr) {
-      const int row = row0 + rr;
-      if (row >= p.M) break;
-      const int col = n0 + wn * TN + lc;
-      const float v0 = stage[rr * CS + lc], v1 = stage[rr * CS + lc + 1];
-      if (col < p.N) epilogue_elem<bf16_t>(p, bz, row, col, v0);
-      if (col + 1 < p.N) epilogue_elem<bf16_t>(p, bz, row, col + 1, v1);
     }
     __syncthreads();
   }
@@ -586,10 +408,7 @@ const char* gemm_kernel_name(const GemmArgs& p) {
        "gemm_bf16_kernel<256,256,TT>"},
       {"gemm_bf16_kernel<128,128,NT>", "gemm_bf16_kernel<128,128,NN>", "gemm_bf16_kernel<128,128,TN>",
        "gemm_bf16_kernel<128,128,TT>"}};
-  static const char* split_names[4] = {"gemm_split_kernel<NT>", "gemm_split_kernel<NN>", "gemm_split_kernel<TN>",
-                                       "gemm_split_kernel<TT>"};
   const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
-  if (p.split && p.dtype == ACT_BF16) return split_names[lay];
   const int t = p.dtype == ACT_F32 ? 0 : pick_tile(p);
   return names[t][lay];
 }
@@ -603,23 +422,7 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if (p.epi != EPI_LINEAR || !p.ws) return 1;
     if ((size_t)p.splits * p.batch * p.M * p.N * sizeof(float) > p.ws_bytes) return 1;
   }
-  if (p.split && p.dtype == ACT_BF16) {
-    if (p.K % 8 || p.splits != 1 || p.epi != EPI_LINEAR) return 2;
-    if (!p.a_kmaj && (p.M % 8 || p.lda % 4)) return 2;
-    if (!p.b_kmaj && (p.N % 8 || p.ldb % 4)) return 2;
-    if ((p.a_kmaj && p.lda % 4) || (p.b_kmaj && p.ldb % 4)) return 2;
-    const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-    dim3 grid(tiles, p.batch), block(256);
-    if (p.a_kmaj && p.b_kmaj)
-      hipLaunchKernelGGL((gemm_split_kernel<true, true>), grid, block, 0, st, p);
-    else if (p.a_kmaj && !p.b_kmaj)
-      hipLaunchKernelGGL((gemm_split_kernel<true, false>), grid, block, 0, st, p);
-    else if (!p.a_kmaj && !p.b_kmaj)
-      hipLaunchKernelGGL((gemm_split_kernel<false, false>), grid, block, 0, st, p);
-    else
-      hipLaunchKernelGGL((gemm_split_kernel<false, true>), grid, block, 0, st, p);
-    return 0;
-  }
+  if (p.split && (p.dtype != ACT_BF16 || p.splits != 1 || !p.A_lo || !p.B_lo)) return 1;
   if (p.dtype == ACT_BF16) {
     // 16-byte vector loads: k (K-major operands) or rows (transposed operands) in multiples of 8
     if (p.K % 8) return 2;

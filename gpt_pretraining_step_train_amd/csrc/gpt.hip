@@ -51,8 +51,8 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 
 struct Offsets {
   size_t params, grads, mom, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
-      dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xf2, xa0, xa1,
-      Af, Aa, Ba, Bf, ss_part, ss, mat_off, mat_size, rope, loss, err;
+      dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
+      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err;
   size_t splitws_bytes;
 };
 
@@ -116,13 +116,15 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.splitws = P.add(std::max<size_t>(O.splitws_bytes, 256));
   O.embws = P.add(embed_ws_bytes((int)N, (int)V, (int)d));
   O.xf = P.add(nBlk * 4);
-  O.xf2 = P.add(nBlk * 4);
   O.xa0 = P.add(nBlk * es);
   O.xa1 = P.add(nBlk * es);
+  O.xl0 = P.add(nBlk * es);
+  O.xl1 = P.add(nBlk * es);
   O.Af = P.add(std::max(4 * L * d * d, 2 * L * s * s) * 4);
   O.Aa = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
   O.Ba = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
-  O.Bf = P.add(std::max(4 * L * d * d, 2 * L * s * s) * 4);
+  O.Al = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
+  O.Bl = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
   (void)l;
   O.ss_part = P.add(6 * L * kSumsqParts * 8);
   O.ss = P.add(6 * L * 8);
@@ -594,6 +596,11 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   float* mom = M->at_off<float>(O.mom);
   float* xf = M->at_off<float>(O.xf);
   char* xa[2] = {M->base + O.xa0, M->base + O.xa1};
+  char* xl[2] = {M->base + O.xl0, M->base + O.xl1};
+  // the leading iterations multiply with operands carried as bf16 hi + lo planes
+  // (three MFMA products each): rounding errors of the early iterations are amplified
+  // by the later ones along small singular directions, those of the last are not
+  const int nsplit = M->at == ACT_BF16 ? std::min(c.ns_split_steps, c.ns_steps) : 0;
   const size_t es = M->es;
   launch_momentum(mom, M->blk(M->grads()), c.muon_momentum, M->nBlk, st);
   launch_matrix_sumsq(mom, M->at_off<long>(O.mat_off), M->at_off<long>(O.mat_size), 6 * L,
@@ -610,64 +617,63 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       const int rows = j == 4 ? F : d, cols = j == 5 ? F : d;
       const size_t dst = xdst(l, j);
       launch_ns_normalize(mom + M->moff[6 * l + j], M->at_off<double>(O.ss), 6 * l + j, 1e-7f, rows, cols,
-                          transposed(j), xf + dst, xa[0] + dst * es, M->at, st);
+                          transposed(j), xf + dst, xa[0] + dst * es, nsplit > 0 ? xl[0] + dst * es : nullptr, M->at,
+                          st);
     }
   struct Batch { int s, l, nb; size_t off; };
   const Batch batches[2] = {{d, d, 4 * L, 0}, {s, lw, 2 * L, (size_t)4 * L * d * d}};
   float* Af = M->at_off<float>(O.Af);
-  float* Bf = M->at_off<float>(O.Bf);
   void* Aa = M->base + O.Aa;
   void* Ba = M->base + O.Ba;
-  float* xfb[2] = {xf, M->at_off<float>(O.xf2)};
-  // the leading iterations run on fp32 operands split into bf16 hi + lo (three MFMA
-  // products each): rounding errors of the early iterations are amplified by the later
-  // ones along small singular directions, those of the last iterations are not
-  const int nsplit = M->at == ACT_BF16 ? std::min(c.ns_split_steps, c.ns_steps) : 0;
+  void* Alo = M->base + O.Al;
+  void* Blo = M->base + O.Bl;
   int rc;
   for (const Batch& bt : batches) {
     int cur = 0;
     const long ss = (long)bt.s * bt.s, sl = (long)bt.s * bt.l;
     for (int it = 0; it < c.ns_steps; ++it) {
       const float a = c.ns_coeffs[it][0], b = c.ns_coeffs[it][1], cc = c.ns_coeffs[it][2];
-      const bool sp = it < nsplit;
-      const bool next_bf = it + 1 < c.ns_steps && it + 1 >= nsplit;
-      const void* xop = sp ? (const void*)(xfb[cur] + bt.off) : (const void*)(xa[cur] + bt.off * es);
+      const bool sp = it < nsplit;                      // this iteration multiplies hi/lo planes
+      const bool next_sp = it + 1 < nsplit;             // the next one needs X's lo plane
+      const void* xh = xa[cur] + bt.off * es;
+      const void* xlo = xl[cur] + bt.off * es;
       {
         GemmArgs p;  // A = X X^T
-        p.split = sp;
+        p.split = sp; p.A_lo = xlo; p.B_lo = xlo;
         p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
-        p.A = xop; p.lda = bt.l; p.strideA = sl;
-        p.B = xop; p.ldb = bt.l; p.strideB = sl;
+        p.A = xh; p.lda = bt.l; p.strideA = sl;
+        p.B = xh; p.ldb = bt.l; p.strideB = sl;
         p.outF = Af; p.ldo = bt.s; p.strideO = ss;
-        if (!sp) { p.outA = Aa; p.ldoa = bt.s; p.strideOA = ss; }
+        p.outA = Aa; p.ldoa = bt.s; p.strideOA = ss;
+        if (sp) p.outA_lo = Alo;
         if ((rc = run_gemm(M, p, st, false))) return rc;
       }
       {
         GemmArgs p;  // Bm = b A + c A A   (A symmetric)
-        p.split = sp;
+        p.split = sp; p.A_lo = Alo; p.B_lo = Alo;
         p.M = bt.s; p.N = bt.s; p.K = bt.s; p.batch = bt.nb;
-        p.A = sp ? (const void*)Af : Aa; p.lda = bt.s; p.strideA = ss;
-        p.B = sp ? (const void*)Af : Aa; p.ldb = bt.s; p.strideB = ss;
+        p.A = Aa; p.lda = bt.s; p.strideA = ss;
+        p.B = Aa; p.ldb = bt.s; p.strideB = ss;
         p.alpha = cc; p.beta = b; p.Cin = Af; p.ldcin = bt.s; p.strideCin = ss;
-        if (sp) { p.outF = Bf; p.ldo = bt.s; p.strideO = ss; }
-        else { p.outA = Ba; p.ldoa = bt.s; p.strideOA = ss; }
+        p.outA = Ba; p.ldoa = bt.s; p.strideOA = ss;
+        if (sp) p.outA_lo = Blo;
         if ((rc = run_gemm(M, p, st, false))) return rc;
       }
       {
-        GemmArgs p;  // X' = a X + Bm X
-        p.split = sp;
+        GemmArgs p;  // X <- a X + Bm X   (fp32 X read and written by the same thread)
+        p.split = sp; p.A_lo = Blo; p.B_lo = xlo;
         p.M = bt.s; p.N = bt.l; p.K = bt.s; p.batch = bt.nb;
-        p.A = sp ? (const void*)Bf : Ba; p.lda = bt.s; p.strideA = ss;
-        p.B = xop; p.ldb = bt.l; p.strideB = sl; p.b_kmaj = false;
-        p.beta = a; p.Cin = xfb[cur] + bt.off; p.ldcin = bt.l; p.strideCin = sl;
-        p.outF = xfb[cur ^ 1] + bt.off; p.ldo = bt.l; p.strideO = sl;
-        if (next_bf) { p.outA = xa[cur ^ 1] + bt.off * es; p.ldoa = bt.l; p.strideOA = sl; }
+        p.A = Ba; p.lda = bt.s; p.strideA = ss;
+        p.B = xh; p.ldb = bt.l; p.strideB = sl; p.b_kmaj = false;
+        p.beta = a; p.Cin = xf + bt.off; p.ldcin = bt.l; p.strideCin = sl;
+        p.outF = xf + bt.off; p.ldo = bt.l; p.strideO = sl;
+        p.outA = xa[cur ^ 1] + bt.off * es; p.ldoa = bt.l; p.strideOA = sl;
+        if (next_sp) p.outA_lo = xl[cur ^ 1] + bt.off * es;
         if ((rc = run_gemm(M, p, st, false))) return rc;
       }
       cur ^= 1;
     }
   }
-  xf = xfb[c.ns_steps & 1];
   float* wblk = M->blk(M->params());
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
@@ -788,13 +794,14 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
-int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const float* A, long lda, long sA,
-                    const float* B, long ldb, long sB, float* C, long ldc, long sC, void* stream) {
-  if (M < 0 || N < 0 || K < 0 || batch < 0 || !C || !A || !B) return GPT_ERR_ARG;
+int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* Ah, const void* Al, long lda,
+                    long sA, const void* Bh, const void* Bl, long ldb, long sB, float* C, long ldc, long sC,
+                    void* stream) {
+  if (M < 0 || N < 0 || K < 0 || batch < 0 || !C || !Ah || !Al || !Bh || !Bl) return GPT_ERR_ARG;
   GemmArgs p;
   p.M = M; p.N = N; p.K = K; p.batch = batch; p.split = true; p.dtype = ACT_BF16;
-  p.A = A; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
-  p.B = B; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
+  p.A = Ah; p.A_lo = Al; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
+  p.B = Bh; p.B_lo = Bl; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
   p.outF = C; p.ldo = ldc; p.strideO = sC;
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc) return rc == 1 ? GPT_ERR_ARG : GPT_ERR_SHAPE;

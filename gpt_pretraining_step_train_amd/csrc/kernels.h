@@ -30,10 +30,13 @@ struct GemmArgs {
   int splits = 1;                 // split-K factor; >1 needs ws
   float* ws = nullptr; size_t ws_bytes = 0;
   int tile = 0;                   // 0 = auto, 1 = 256x256, 2 = 128x128
-  // split: A and B are fp32; each is split on load into bf16 hi + bf16 lo (the
-  // rounding residual) and the product is accumulated as hi*hi + hi*lo + lo*hi
-  // (bf16 MFMA, ~16 significant bits per operand)
+  // split: A and B come as two bf16 planes each, hi (A, B) and lo (A_lo, B_lo = the
+  // rounding residual of fp32 values); the product runs as three K segments
+  // hi*hi + hi*lo + lo*hi on bf16 MFMA (~16 significant bits per operand)
   bool split = false;
+  const void* A_lo = nullptr;
+  const void* B_lo = nullptr;
+  void* outA_lo = nullptr;        // optional lo plane of outA (v - bf16(v)), same ld/stride
 };
 
 // returns 0 on success, else an error code (argument/shape problems)
@@ -77,7 +80,7 @@ void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, in
                          int parts, double* out, hipStream_t st);
 // X = src / (norm + eps) written (optionally transposed) into fp32 and act copies
 void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols,
-                         bool transpose, float* xf, void* xa, int act_type, hipStream_t st);
+                         bool transpose, float* xf, void* xa, void* xa_lo, int act_type, hipStream_t st);
 void launch_muon_apply(float* w, void* w_act, int act_type, const float* x, float lr, int rows,
                        int cols, bool transposed, hipStream_t st);
 

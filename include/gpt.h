@@ -152,12 +152,13 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
               long sA, const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits,
               void* ws, size_t ws_bytes, void* stream);
 
-/* as gptk_gemm with fp32 operands A and B, each split on load into a bf16 high
- * part and a bf16 residual; C = Ah*Bh + Ah*Bl + Al*Bh on bf16 MFMA with fp32
- * accumulation (the product Muon's Newton-Schulz uses in its early iterations).
- * Row counts of transposed operands and K must be multiples of 8. */
-int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const float* A, long lda, long sA,
-                    const float* B, long ldb, long sB, float* C, long ldc, long sC, void* stream);
+/* as gptk_gemm (bf16) with each operand given as two bf16 planes, a high part
+ * (Ah, Bh) and the residual of an fp32 value (Al, Bl), same layout and strides:
+ * C = Ah*Bh + Ah*Bl + Al*Bh on bf16 MFMA with fp32 accumulation -- the product
+ * Muon's Newton-Schulz uses in its leading iterations. */
+int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* Ah, const void* Al, long lda,
+                    long sA, const void* Bh, const void* Bl, long ldb, long sB, float* C, long ldc, long sC,
+                    void* stream);
 
 /* name of the GEMM kernel instantiation gptk_gemm / gpt_step launch for these
  * layouts and sizes, e.g. "gemm_bf16_kernel<256,256,NT>" (NT: both operands have

@@ -76,7 +76,7 @@ SPLIT_CASES = [(1, 1, 300, 200, 136, 1), (1, 0, 296, 264, 264, 2), (0, 0, 136, 2
 
 @pytest.mark.parametrize("case", SPLIT_CASES)
 def test_gemm_split_precision(case):
-    """fp32 operands split into bf16 hi + lo: ~16-bit operands, far tighter than bf16."""
+    """fp32 operands carried as bf16 hi + lo planes: ~16-bit operands, far tighter than bf16."""
     ak, bk, M, N, K, batch = case
     rng = np.random.default_rng(K + M)
     A = rng.standard_normal((batch, M, K) if ak else (batch, K, M)).astype(np.float32)
@@ -84,9 +84,17 @@ def test_gemm_split_precision(case):
     Am = A if ak else A.transpose(0, 2, 1)
     Bn = Bm if bk else Bm.transpose(0, 2, 1)
     ref = np.einsum("zmk,znk->zmn", Am.astype(np.float64), Bn.astype(np.float64))
+
+    def planes(x):
+        hi = torch.from_numpy(x).bfloat16()
+        lo = (torch.from_numpy(x) - hi.float()).bfloat16()
+        return hi.cuda(), lo.cuda()
+
+    Ah, Al = planes(A)
+    Bh, Bl = planes(Bm)
     C = torch.full((batch, M, N), float("nan"), device="cuda")
-    B.gemm_split(ak, bk, M, N, K, torch.from_numpy(A).cuda(), K if ak else M, torch.from_numpy(Bm).cuda(),
-                 K if bk else N, C, N, batch=batch, sA=A[0].size, sB=Bm[0].size, sC=M * N)
+    B.gemm_split(ak, bk, M, N, K, Ah, Al, K if ak else M, Bh, Bl, K if bk else N, C, N, batch=batch,
+                 sA=A[0].size, sB=Bm[0].size, sC=M * N)
     torch.cuda.synchronize()
     got = from_dev(C)
     assert np.abs(got - ref).max() / np.abs(ref).max() < 5e-5
