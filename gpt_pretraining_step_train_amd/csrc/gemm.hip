@@ -17,6 +17,21 @@ namespace {
 constexpr int BK = 64;        // bf16 elements of k per LDS stage
 constexpr int LDSS = BK + 8;  // LDS row stride in elements (16-byte pad)
 
+// Buffer resource over one operand matrix: raw buffer loads return zeros for
+// byte offsets at or past `bytes`, which covers the row tail; the k tail and the
+// column tail of transposed operands are mapped to an out-of-range offset.
+constexpr uint32_t OOB = 0xFFFFFFF0u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int R, bool KMAJ, int NT>
 struct TileLoader {
   static constexpr int NUNIT = KMAJ ? R * (BK / 8) : (R / 8) * (BK / 8);
@@ -25,26 +40,23 @@ struct TileLoader {
   uint4 regs[NREG];
 
   // element (row, k) lives at base[row*ld + k] (KMAJ) or base[k*ld + row]
-  __device__ inline void load(const bf16_t* __restrict__ base, long ld, int row0, int rows, int k0, int kend,
-                              int tid) {
+  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, long ld, int row0, int rows, int k0, int kend, int tid) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
       if (KMAJ) {
         const int r = u >> 3, kc = u & 7;
-        const int grow = row0 + r, gk = k0 + kc * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (u < NUNIT && grow < rows && gk < kend) v = *reinterpret_cast<const uint4*>(base + (long)grow * ld + gk);
-        regs[i] = v;
+        const int gk = k0 + kc * 8;
+        const bool ok = u < NUNIT && gk < kend && row0 + r < rows;
+        regs[i] = buf_load16(rs, ok ? (uint32_t)(((long)(row0 + r) * ld + gk) * 2) : OOB);
       } else {
         const int kb = u & 7, rb = u >> 3;
         const int grow = row0 + rb * 8;
+        const bool okr = u < NUNIT && grow < rows;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int gk = k0 + kb * 8 + j;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (u < NUNIT && grow < rows && gk < kend) v = *reinterpret_cast<const uint4*>(base + (long)gk * ld + grow);
-          regs[i * 8 + j] = v;
+          regs[i * 8 + j] = buf_load16(rs, (okr && gk < kend) ? (uint32_t)(((long)gk * ld + grow) * 2) : OOB);
         }
       }
     }
@@ -54,7 +66,7 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
-      if (u >= NUNIT) continue;
+      if (NUNIT % NT != 0 && u >= NUNIT) continue;
       if (KMAJ) {
         const int r = u >> 3, kc = u & 7;
         *reinterpret_cast<uint4*>(lds + r * LDSS + kc * 8) = regs[i];
@@ -124,12 +136,57 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
   }
 }
 
+// four consecutive columns (col % 4 == 0, col + 3 < N, every leading dimension a
+// multiple of 4): one vector load/store per operand instead of four scalar ones
+__device__ inline void st4_act(bf16_t* q, const float (&v)[4]) {
+  *reinterpret_cast<uint2*>(q) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+}
+__device__ inline void ld4_act(const bf16_t* q, float (&v)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(q);
+  v[0] = bf2f((bf16_t)(u.x & 0xffff)); v[1] = bf2f((bf16_t)(u.x >> 16));
+  v[2] = bf2f((bf16_t)(u.y & 0xffff)); v[3] = bf2f((bf16_t)(u.y >> 16));
+}
+
+__device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col, float4 a) {
+  float v[4] = {p.alpha * a.x, p.alpha * a.y, p.alpha * a.z, p.alpha * a.w};
+  if (p.epi == EPI_LINEAR) {
+    if (p.Cin) {
+      const float4 c = *reinterpret_cast<const float4*>(p.Cin + bz * p.strideCin + (long)row * p.ldcin + col);
+      v[0] += p.beta * c.x; v[1] += p.beta * c.y; v[2] += p.beta * c.z; v[3] += p.beta * c.w;
+    }
+    if (p.outF)
+      *reinterpret_cast<float4*>(p.outF + bz * p.strideO + (long)row * p.ldo + col) = make_float4(v[0], v[1], v[2], v[3]);
+    if (p.outA) {
+      const long o = bz * p.strideOA + (long)row * p.ldoa + col;
+      bf16_t* q = reinterpret_cast<bf16_t*>(p.outA) + o;
+      st4_act(q, v);
+      if (p.outA_lo) {
+        float h[4], l[4];
+        ld4_act(q, h);
+        for (int t = 0; t < 4; ++t) l[t] = v[t] - h[t];
+        st4_act(reinterpret_cast<bf16_t*>(p.outA_lo) + o, l);
+      }
+    }
+  } else if (p.epi == EPI_RELU2) {
+    const long o = bz * p.strideOA + (long)row * p.ldoa + col;
+    float g[4];
+    for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
+    st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
+    st4_act(reinterpret_cast<bf16_t*>(p.out2) + o, g);
+  } else {  // EPI_DRELU2
+    const long o = bz * p.strideOA + (long)row * p.ldoa + col;
+    float u[4];
+    ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + o, u);
+    for (int t = 0; t < 4; ++t) v[t] *= 2.f * fmaxf(u[t], 0.f);
+    st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
 __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDSS];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDSS];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * LDSS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -150,13 +207,17 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
   const bf16_t* Bh = reinterpret_cast<const bf16_t*>(p.B) + bz * p.strideB;
   const bf16_t* Al = p.split ? reinterpret_cast<const bf16_t*>(p.A_lo) + bz * p.strideA : Ah;
   const bf16_t* Bl = p.split ? reinterpret_cast<const bf16_t*>(p.B_lo) + bz * p.strideB : Bh;
-  // k tile t: segment t / nks selects the operand planes, (t % nks) the k offset
-  auto seg_a = [&](int t) { return t / nks == 2 ? Al : Ah; };
-  auto seg_b = [&](int t) { return t / nks == 1 ? Bl : Bh; };
-  auto seg_k = [&](int t) { return kbeg + (t % nks) * BK; };
+  // operand extents in bytes (the launcher guarantees they fit 32-bit offsets)
+  const uint32_t abytes = (uint32_t)((long)(AK ? p.M : p.K) * p.lda * 2);
+  const uint32_t bbytes = (uint32_t)((long)(BKM ? p.N : p.K) * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t rAh = make_rsrc(Ah, abytes), rAl = make_rsrc(Al, abytes);
+  const __amdgpu_buffer_rsrc_t rBh = make_rsrc(Bh, bbytes), rBl = make_rsrc(Bl, bbytes);
+  // k tile t: segment t / nks selects the operand planes (hi*hi, hi*lo, lo*hi), t % nks the offset
 
-  TileLoader<BM, AK, NT> la;
-  TileLoader<BN, BKM, NT> lb;
+  // two register stages: the global loads of tile t+2 are issued while tile t is
+  // multiplied, so each load has two k-tiles of MFMA work to arrive
+  TileLoader<BM, AK, NT> la0, la1;
+  TileLoader<BN, BKM, NT> lb0, lb1;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -166,61 +227,81 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (nk > 0) {
-    la.load(seg_a(0), p.lda, m0, p.M, seg_k(0), kend, tid);
-    lb.load(seg_b(0), p.ldb, n0, p.N, seg_k(0), kend, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+
+#define GEMM_LOAD(LA, LB, T)                                                              \
+  do {                                                                                    \
+    const int t_ = (T), sg_ = t_ < nk ? t_ / nks : 0;                                     \
+    const int k_ = t_ < nk ? kbeg + (t_ % nks) * BK : kend; /* padding tile: all zeros */ \
+    LA.load(sg_ == 2 ? rAl : rAh, p.lda, m0, p.M, k_, kend, tid);                         \
+    LB.load(sg_ == 1 ? rBl : rBh, p.ldb, n0, p.N, k_, kend, tid);                         \
+  } while (0)
+
+#define GEMM_COMPUTE(BUF)                                                                 \
+  do {                                                                                    \
+    const bf16_t* as_ = smem + (BUF) * (BM * LDSS) + (wm * TM + lr) * LDSS + lk;          \
+    const bf16_t* bs_ = smem + 2 * BM * LDSS + (BUF) * (BN * LDSS) + (wn * TN + lr) * LDSS + lk; \
+    bf16x8_t af_[2][FM], bf_[2][FN];                                                      \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                         \
+      af_[0][i] = *reinterpret_cast<const bf16x8_t*>(as_ + i * 32 * LDSS);                \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                         \
+      bf_[0][j] = *reinterpret_cast<const bf16x8_t*>(bs_ + j * 32 * LDSS);                \
+    _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                               \
+      const int c_ = kk & 1;                                                              \
+      if (kk + 1 < BK / 16) {                                                             \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                     \
+          af_[c_ ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(as_ + i * 32 * LDSS + (kk + 1) * 16); \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
+          bf_[c_ ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(bs_ + j * 32 * LDSS + (kk + 1) * 16); \
+      }                                                                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                       \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
+          acc[i][j] = mfma32x32x16_bf16(af_[c_][i], bf_[c_][j], acc[i][j]);              \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+  } while (0)
+
+  // an odd tile count is padded with one all-zero tile so the loop runs in pairs
+  const int nk2 = (nk + 1) & ~1;
+  if (nk2 > 0) {
+    GEMM_LOAD(la0, lb0, 0);
+    la0.store(smem, tid);
+    lb0.store(smem + 2 * BM * LDSS, tid);
+    GEMM_LOAD(la1, lb1, 1);
   }
   __syncthreads();
-
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) {
-      la.load(seg_a(it + 1), p.lda, m0, p.M, seg_k(it + 1), kend, tid);
-      lb.load(seg_b(it + 1), p.ldb, n0, p.N, seg_k(it + 1), kend, tid);
-    }
-    const bf16_t* as = As[cur] + (wm * TM + lr) * LDSS + lk;
-    const bf16_t* bs = Bs[cur] + (wn * TN + lr) * LDSS + lk;
-    // fragments double-buffered across the 16-wide k steps so LDS reads overlap MFMAs
-    bf16x8_t af[2][FM], bfv[2][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) af[0][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LDSS);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bfv[0][j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * LDSS);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk & 1;
-      if (kk + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LDSS + (kk + 1) * 16);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfv[c ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(bs + j * 32 * LDSS + (kk + 1) * 16);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the next step's LDS reads ahead of these MFMAs
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bfv[c][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (it + 1 < nk) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+  // tile t sits in LDS buffer t&1 and register stage t&1; unrolled by two so the
+  // stage registers are addressed statically
+  for (int it = 0; it < nk2; it += 2) {
+    if (it + 2 < nk2) GEMM_LOAD(la0, lb0, it + 2);
+    GEMM_COMPUTE(0);
+    la1.store(smem + BM * LDSS, tid);
+    lb1.store(smem + 2 * BM * LDSS + BN * LDSS, tid);
+    __syncthreads();
+    if (it + 3 < nk2) GEMM_LOAD(la1, lb1, it + 3);
+    GEMM_COMPUTE(1);
+    if (it + 2 < nk2) {
+      la0.store(smem, tid);
+      lb0.store(smem + 2 * BM * LDSS, tid);
     }
     __syncthreads();
   }
+#undef GEMM_LOAD
+#undef GEMM_COMPUTE
 
   // epilogue through LDS, one 32-row block of every wave at a time: the accumulator
   // fragments go to LDS with constant register indices, then each wave reads its
-  // 32 x TN block back row by row (two adjacent columns per lane) for coalesced stores
+  // 32 x TN block back by rows, four adjacent columns per lane, for vector stores
   constexpr int CS = TN + 4;  // fp32 row stride of the staging block
-  static_assert(WM * WN * 32 * CS * 4 <= 2 * BM * LDSS * 2, "staging block must fit in As");
-  static_assert(TN == 64 || TN % 128 == 0, "epilogue column mapping");
-  float* stage = reinterpret_cast<float*>(&As[0][0]) + wave * 32 * CS;
+  static_assert(WM * WN * 32 * CS * 4 <= 2 * (BM + BN) * LDSS * 2, "staging block must fit in LDS");
+  static_assert(TN % 4 == 0 && 64 % (TN / 4) == 0, "epilogue lane mapping");
+  constexpr int LPR = TN / 4;        // lanes per row
+  constexpr int RPI = 64 / LPR;      // rows per wave instruction
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * CS;
+  const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
+                   (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
+  const int lc = (lane % LPR) * 4, lrow = lane / LPR;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -229,37 +310,26 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r];
     __syncthreads();
     const int row0 = m0 + wm * TM + i * 32;
-    for (int rr = 0; rr < 32; ++rr) {
+    const int col = n0 + wn * TN + lc;
+    for (int rr = lrow; rr < 32; rr += RPI) {
       const int row = row0 + rr;
       if (row >= p.M) break;
-#pragma unroll
-      for (int cc = 0; cc < TN / 128; ++cc) {
-        const int lc = cc * 128 + lane * 2;
-        const int col = n0 + wn * TN + lc;
-        const float v0 = stage[rr * CS + lc], v1 = stage[rr * CS + lc + 1];
-        if (p.splits > 1) {
-          float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
-          if (col < p.N) w[0] = v0;
-          if (col + 1 < p.N) w[1] = v1;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+      if (p.splits > 1) {
+        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
+        if (vec && col + 3 < p.N) {
+          *reinterpret_cast<float4*>(w) = a;
         } else {
-          if (col < p.N) epilogue_elem<bf16_t>(p, bz, row, col, v0);
-          if (col + 1 < p.N) epilogue_elem<bf16_t>(p, bz, row, col + 1, v1);
+          const float e[4] = {a.x, a.y, a.z, a.w};
+          for (int t = 0; t < 4; ++t)
+            if (col + t < p.N) w[t] = e[t];
         }
-      }
-      if (TN % 128) {  // TN = 64: lanes 0..31 cover the row
-        const int lc = lane * 2;
-        const int col = n0 + wn * TN + lc;
-        if (lc < TN) {
-          const float v0 = stage[rr * CS + lc], v1 = stage[rr * CS + lc + 1];
-          if (p.splits > 1) {
-            float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
-            if (col < p.N) w[0] = v0;
-            if (col + 1 < p.N) w[1] = v1;
-          } else {
-            if (col < p.N) epilogue_elem<bf16_t>(p, bz, row, col, v0);
-            if (col + 1 < p.N) epilogue_elem<bf16_t>(p, bz, row, col + 1, v1);
-          }
-        }
+      } else if (vec && col + 3 < p.N) {
+        epilogue_vec4(p, bz, row, col, a);
+      } else {
+        const float e[4] = {a.x, a.y, a.z, a.w};
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);
       }
     }
     __syncthreads();
@@ -373,7 +443,7 @@ void launch_f32(const GemmArgs& p, hipStream_t st) {
 }
 
 int pick_tile(const GemmArgs& p) {
-  if (p.tile) return p.tile;
+  if (p.tile) return p.tile > 4 ? 1 : p.tile;
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
   return big >= 128 ? 1 : 2;
 }
@@ -385,7 +455,7 @@ int gemm_auto_splits(const GemmArgs& p) {
   int tm, tn;
   if (p.dtype == ACT_F32) {
     tm = 64; tn = 64;
-  } else if (pick_tile(p) == 1) {
+  } else if (pick_tile(p) != 2) {
     tm = 256; tn = 256;
   } else {
     tm = 128; tn = 128;
@@ -409,7 +479,7 @@ const char* gemm_kernel_name(const GemmArgs& p) {
       {"gemm_bf16_kernel<128,128,NT>", "gemm_bf16_kernel<128,128,NN>", "gemm_bf16_kernel<128,128,TN>",
        "gemm_bf16_kernel<128,128,TT>"}};
   const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
-  const int t = p.dtype == ACT_F32 ? 0 : pick_tile(p);
+  const int t = p.dtype == ACT_F32 ? 0 : (pick_tile(p) == 2 ? 2 : 1);
   return names[t][lay];
 }
 
@@ -424,15 +494,20 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
   }
   if (p.split && (p.dtype != ACT_BF16 || p.splits != 1 || !p.A_lo || !p.B_lo)) return 1;
   if (p.dtype == ACT_BF16) {
+    // buffer loads address each operand matrix with 32-bit byte offsets
+    const long abytes = (long)(p.a_kmaj ? p.M : p.K) * p.lda * 2, bbytes = (long)(p.b_kmaj ? p.N : p.K) * p.ldb * 2;
+    if (abytes >= (long)0xFFFFFFF0u || bbytes >= (long)0xFFFFFFF0u) return 2;
     // 16-byte vector loads: k (K-major operands) or rows (transposed operands) in multiples of 8
     if (p.K % 8) return 2;
     if (!p.a_kmaj && (p.M % 8 || p.lda % 8)) return 2;
     if (!p.b_kmaj && (p.N % 8 || p.ldb % 8)) return 2;
     if ((p.a_kmaj && p.lda % 8) || (p.b_kmaj && p.ldb % 8)) return 2;
-    if (pick_tile(p) == 1)
-      launch_bf16<256, 256, 2, 2>(p, st);
-    else
-      launch_bf16<128, 128, 2, 2>(p, st);
+    switch (pick_tile(p)) {
+      case 1: launch_bf16<256, 256, 2, 2>(p, st); break;
+      case 3: launch_bf16<256, 256, 2, 4>(p, st); break;
+      case 4: launch_bf16<256, 256, 4, 2>(p, st); break;
+      default: launch_bf16<128, 128, 2, 2>(p, st); break;
+    }
   } else {
     launch_f32(p, st);
   }
