@@ -182,7 +182,7 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool SPLIT>
 __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -200,13 +200,13 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
   const int kbeg = sk * kper;
   const int kend = min(p.K, kbeg + kper);
   const int nks = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;  // k tiles per segment
-  const int nseg = p.split ? 3 : 1;                                 // hi*hi, hi*lo, lo*hi
+  const int nseg = SPLIT ? 3 : 1;                                   // hi*hi, hi*lo, lo*hi
   const int nk = nks * nseg;
 
   const bf16_t* Ah = reinterpret_cast<const bf16_t*>(p.A) + bz * p.strideA;
   const bf16_t* Bh = reinterpret_cast<const bf16_t*>(p.B) + bz * p.strideB;
-  const bf16_t* Al = p.split ? reinterpret_cast<const bf16_t*>(p.A_lo) + bz * p.strideA : Ah;
-  const bf16_t* Bl = p.split ? reinterpret_cast<const bf16_t*>(p.B_lo) + bz * p.strideB : Bh;
+  const bf16_t* Al = SPLIT ? reinterpret_cast<const bf16_t*>(p.A_lo) + bz * p.strideA : Ah;
+  const bf16_t* Bl = SPLIT ? reinterpret_cast<const bf16_t*>(p.B_lo) + bz * p.strideB : Bh;
   // operand extents in bytes (the launcher guarantees they fit 32-bit offsets)
   const uint32_t abytes = (uint32_t)((long)(AK ? p.M : p.K) * p.lda * 2);
   const uint32_t bbytes = (uint32_t)((long)(BKM ? p.N : p.K) * p.ldb * 2);
@@ -415,18 +415,26 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-void launch_bf16(const GemmArgs& p, hipStream_t st) {
+template <int BM, int BN, int WM, int WN, bool SPLIT>
+void launch_bf16_s(const GemmArgs& p, hipStream_t st) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   dim3 grid(tiles, p.batch * p.splits), block(WM * WN * 64);
   if (p.a_kmaj && p.b_kmaj)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true, true>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true, true, SPLIT>), grid, block, 0, st, p);
   else if (p.a_kmaj && !p.b_kmaj)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true, false>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true, false, SPLIT>), grid, block, 0, st, p);
   else if (!p.a_kmaj && !p.b_kmaj)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false, false>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false, false, SPLIT>), grid, block, 0, st, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false, true>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false, true, SPLIT>), grid, block, 0, st, p);
+}
+
+template <int BM, int BN, int WM, int WN>
+void launch_bf16(const GemmArgs& p, hipStream_t st) {
+  if (p.split)
+    launch_bf16_s<BM, BN, WM, WN, true>(p, st);
+  else
+    launch_bf16_s<BM, BN, WM, WN, false>(p, st);
 }
 
 void launch_f32(const GemmArgs& p, hipStream_t st) {
@@ -443,7 +451,7 @@ void launch_f32(const GemmArgs& p, hipStream_t st) {
 }
 
 int pick_tile(const GemmArgs& p) {
-  if (p.tile) return p.tile > 4 ? 1 : p.tile;
+  if (p.tile) return p.tile == 2 ? 2 : 1;
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
   return big >= 128 ? 1 : 2;
 }
@@ -478,8 +486,15 @@ const char* gemm_kernel_name(const GemmArgs& p) {
        "gemm_bf16_kernel<256,256,TT>"},
       {"gemm_bf16_kernel<128,128,NT>", "gemm_bf16_kernel<128,128,NN>", "gemm_bf16_kernel<128,128,TN>",
        "gemm_bf16_kernel<128,128,TT>"}};
+  static const char* split_names[3][4] = {
+      {"", "", "", ""},
+      {"gemm_bf16x3_kernel<256,256,NT>", "gemm_bf16x3_kernel<256,256,NN>", "gemm_bf16x3_kernel<256,256,TN>",
+       "gemm_bf16x3_kernel<256,256,TT>"},
+      {"gemm_bf16x3_kernel<128,128,NT>", "gemm_bf16x3_kernel<128,128,NN>", "gemm_bf16x3_kernel<128,128,TN>",
+       "gemm_bf16x3_kernel<128,128,TT>"}};
   const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
   const int t = p.dtype == ACT_F32 ? 0 : (pick_tile(p) == 2 ? 2 : 1);
+  if (p.split && t) return split_names[t][lay];
   return names[t][lay];
 }
 
@@ -502,12 +517,10 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if (!p.a_kmaj && (p.M % 8 || p.lda % 8)) return 2;
     if (!p.b_kmaj && (p.N % 8 || p.ldb % 8)) return 2;
     if ((p.a_kmaj && p.lda % 8) || (p.b_kmaj && p.ldb % 8)) return 2;
-    switch (pick_tile(p)) {
-      case 1: launch_bf16<256, 256, 2, 2>(p, st); break;
-      case 3: launch_bf16<256, 256, 2, 4>(p, st); break;
-      case 4: launch_bf16<256, 256, 4, 2>(p, st); break;
-      default: launch_bf16<128, 128, 2, 2>(p, st); break;
-    }
+    if (pick_tile(p) == 2)
+      launch_bf16<128, 128, 2, 2>(p, st);
+    else
+      launch_bf16<256, 256, 2, 2>(p, st);
   } else {
     launch_f32(p, st);
   }
