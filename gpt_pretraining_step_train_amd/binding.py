@@ -26,7 +26,7 @@ class GptCfg(ctypes.Structure):
         ("init_std", ctypes.c_float), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("muon_momentum", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("ns_coeffs", (ctypes.c_float * 3) * 5), ("num_steps", ctypes.c_int64),
-        ("ns_split_steps", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("ns_split_steps", ctypes.c_int32), ("fp8_gemms", ctypes.c_int32),
     ]
 
     def coeffs(self):
@@ -65,6 +65,8 @@ _SIGS = {
                            ctypes.POINTER(ctypes.c_double)]),
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
     "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _L, _L, _P, _L, _L, _P]),
+    "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
+    "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -120,6 +122,8 @@ def make_cfg(c: dict) -> GptCfg:
         cfg.ns_steps = int(c["ns_steps"])
     if "ns_split_steps" in c:
         cfg.ns_split_steps = int(c["ns_split_steps"])
+    if "fp8_gemms" in c:
+        cfg.fp8_gemms = int(c["fp8_gemms"])
     if "ns_coeffs" in c:
         for i, abc in enumerate(c["ns_coeffs"]):
             for j in range(3):
@@ -247,6 +251,17 @@ def gemm(dtype, a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, 
 def gemm_split(a_kmaj, b_kmaj, M, N, K, Ah, Al, lda, Bh, Bl, ldb, C, ldc, batch=1, sA=0, sB=0, sC=0):
     check(lib().gptk_gemm_split(int(a_kmaj), int(b_kmaj), M, N, K, batch, _ptr(Ah), _ptr(Al), lda, sA, _ptr(Bh),
                                 _ptr(Bl), ldb, sB, _ptr(C), ldc, sC, _stream()), "gptk_gemm_split")
+
+
+def quant_e4m3(dtype, x, rows, cols, ld, amax_slot, q, qt, inv_scale):
+    nul = ctypes.c_void_p()
+    check(lib().gptk_quant_e4m3(dtype, _ptr(x), rows, cols, ld, _ptr(amax_slot), _ptr(q) if q is not None else nul,
+                                _ptr(qt) if qt is not None else nul, _ptr(inv_scale), _stream()), "gptk_quant_e4m3")
+
+
+def gemm_fp8(M, N, K, A, lda, B, ldb, dq_a, dq_b, C, ldc):
+    check(lib().gptk_gemm_fp8(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(dq_a), _ptr(dq_b), _ptr(C), ldc, _stream()),
+          "gptk_gemm_fp8")
 
 
 def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:

@@ -606,6 +606,72 @@ __global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 e4m3fn (OCP): 1 sign, 4 exponent (bias 7), 3 mantissa bits; max 448, no
+// infinities, 0x7F / 0xFF are NaN.  Round to nearest even, saturate to +-448.
+
+__device__ inline uint8_t f32_to_e4m3(float x) {
+  const uint8_t sign = (uint8_t)((__float_as_uint(x) >> 24) & 0x80);
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7F;
+  if (a >= 448.f) return sign | 0x7E;
+  if (a < 0.015625f) return sign | (uint8_t)rintf(a * 512.f);  // subnormals, step 2^-9 (8 -> min normal)
+  int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;      // 2^e <= a < 2^(e+1), e in [-6, 8]
+  int mant = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
+  if (mant == 8) { mant = 0; ++e; }
+  int code = ((e + 7) << 3) | mant;
+  if (code > 0x7E) code = 0x7E;
+  return sign | (uint8_t)code;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) amax_kernel(const T* __restrict__ x, long rows, long cols, long ldx,
+                                                   unsigned* amax_bits) {
+  __shared__ float sm[4];
+  float m = 0.f;
+  const long n = rows * cols;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const long r = i / cols, c = i - r * cols;
+    m = fmaxf(m, fabsf(ld<T>(x + r * ldx + c)));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    atomicMax(amax_bits, __float_as_uint(m));
+  }
+}
+
+// 64x64 tiles through LDS so both the row-major and the transposed copies are coalesced
+template <typename T>
+__global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x, int rows, int cols, long ldx,
+                                                         const unsigned* amax_bits, uint8_t* __restrict__ q,
+                                                         long ldq, uint8_t* __restrict__ qt, long ldqt,
+                                                         float* inv_scale) {
+  __shared__ uint8_t tile[64][65];
+  const float amax = __uint_as_float(*amax_bits);
+  const float s = amax > 0.f ? 448.f / amax : 1.f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    uint8_t b = 0;
+    if (r < rows && c < cols) {
+      b = f32_to_e4m3(ld<T>(x + (long)r * ldx + c) * s);
+      if (q) q[(long)r * ldq + c] = b;
+    }
+    tile[i][tx] = b;
+  }
+  if (!qt) return;
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) qt[(long)c * ldqt + r] = tile[tx][i];
+  }
+}
+
 inline int grid_for(size_t n, int block = 256, int cap = 65536) {
   size_t g = (n + block - 1) / block;
   if (g > (size_t)cap) g = cap;
@@ -768,4 +834,26 @@ void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int
     hipLaunchKernelGGL(muon_apply_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, rows, cols, (int)tr);
   else
     hipLaunchKernelGGL(muon_apply_kernel<float>, g, b, 0, st, w, (float*)wa, x, lr, rows, cols, (int)tr);
+}
+
+void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st) {
+  const long n = rows * cols;
+  const int g = (int)std::min<long>((n + 255) / 256, 2048);
+  if (n <= 0) return;
+  if (it == ACT_BF16)
+    hipLaunchKernelGGL(amax_kernel<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits);
+  else
+    hipLaunchKernelGGL(amax_kernel<float>, dim3(g), dim3(256), 0, st, (const float*)x, rows, cols, ld, amax_bits);
+}
+
+void launch_quant_e4m3(const void* x, int it, int rows, int cols, long ld, const unsigned* amax_bits, uint8_t* q,
+                       long ldq, uint8_t* qt, long ldqt, float* inv_scale, hipStream_t st) {
+  dim3 g((cols + 63) / 64, (rows + 63) / 64), b(256);
+  if (rows <= 0 || cols <= 0) return;
+  if (it == ACT_BF16)
+    hipLaunchKernelGGL(quant_e4m3_kernel<bf16_t>, g, b, 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits, q, ldq,
+                       qt, ldqt, inv_scale);
+  else
+    hipLaunchKernelGGL(quant_e4m3_kernel<float>, g, b, 0, st, (const float*)x, rows, cols, ld, amax_bits, q, ldq, qt,
+                       ldqt, inv_scale);
 }

@@ -14,6 +14,7 @@
 
 namespace {
 
+typedef unsigned int u32x8_t __attribute__((ext_vector_type(8)));
 constexpr int BK = 64;        // bf16 elements of k per LDS stage
 constexpr int LDSS = BK + 8;  // LDS row stride in elements (16-byte pad)
 
@@ -337,6 +338,160 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// fp8 (e4m3) GEMM, both operands with the reduction index contiguous (the
+// quantisation pass writes transposed copies where a product needs them).
+// 256x256 tile, k-tiles of 128 bytes (same LDS footprint as the bf16 kernel),
+// v_mfma_f32_32x32x64_f8f6f4: lane half h of a 64-wide k step holds its 32 k bytes
+// contiguously, for A (row lane%32) and B (column lane%32) alike.
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int R, int NT>
+struct ByteTileLoader {
+  static constexpr int NUNIT = R * 8;  // 16-byte chunks of 128-byte rows
+  static constexpr int UPT = (NUNIT + NT - 1) / NT;
+  uint4 regs[UPT];
+  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, long ld, int row0, int rows, int k0, int kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      const int r = u >> 3, kc = u & 7;
+      const int gk = k0 + kc * 16;
+      const bool ok = u < NUNIT && gk < kend && row0 + r < rows;
+      regs[i] = buf_load16(rs, ok ? (uint32_t)((long)(row0 + r) * ld + gk) : OOB);
+    }
+  }
+  __device__ inline void store(uint8_t* lds, int tid) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      if (NUNIT % NT != 0 && u >= NUNIT) continue;
+      *reinterpret_cast<uint4*>(lds + (u >> 3) * (LDSS * 2) + (u & 7) * 16) = regs[i];
+    }
+  }
+};
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(WM* WN * 64) gemm_fp8_kernel(GemmArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int BKB = 128;           // k bytes per tile
+  constexpr int RS = LDSS * 2;       // LDS row stride in bytes (16-byte pad)
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * LDSS];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tilesM = (p.M + BM - 1) / BM, tilesN = (p.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
+  const int bz = blockIdx.y / p.splits, sk = blockIdx.y % p.splits;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kper = ((p.K + p.splits - 1) / p.splits + BKB - 1) / BKB * BKB;
+  const int kbeg = sk * kper;
+  const int kend = min(p.K, kbeg + kper);
+  const int nk = kend > kbeg ? (kend - kbeg + BKB - 1) / BKB : 0;
+  const uint8_t* A = reinterpret_cast<const uint8_t*>(p.A) + bz * p.strideA;
+  const uint8_t* B = reinterpret_cast<const uint8_t*>(p.B) + bz * p.strideB;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)((long)p.M * p.lda));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, (uint32_t)((long)p.N * p.ldb));
+  const float dq = p.dq_a[0] * p.dq_b[0];
+
+  ByteTileLoader<BM, NT> la0, la1;
+  ByteTileLoader<BN, NT> lb0, lb1;
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int lr = lane & 31, lh = (lane >> 5) * 32;
+
+#define FP8_LOAD(LA, LB, T)                                                     \
+  do {                                                                          \
+    const int k_ = (T) < nk ? kbeg + (T) * BKB : kend;                          \
+    LA.load(rA, p.lda, m0, p.M, k_, kend, tid);                                 \
+    LB.load(rB, p.ldb, n0, p.N, k_, kend, tid);                                 \
+  } while (0)
+#define FP8_FRAG(PTR) __builtin_bit_cast(i32x8_t, *reinterpret_cast<const u32x8_t*>(PTR))
+#define FP8_COMPUTE(BUF)                                                                     \
+  do {                                                                                       \
+    const uint8_t* as_ = lds + (BUF) * (BM * RS) + (wm * TM + lr) * RS + lh;                 \
+    const uint8_t* bs_ = lds + 2 * BM * RS + (BUF) * (BN * RS) + (wn * TN + lr) * RS + lh;    \
+    _Pragma("unroll") for (int kk = 0; kk < BKB / 64; ++kk) {                                \
+      i32x8_t af_[FM], bf_[FN];                                                              \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) af_[i] = FP8_FRAG(as_ + i * 32 * RS + kk * 64); \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) bf_[j] = FP8_FRAG(bs_ + j * 32 * RS + kk * 64); \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                         \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af_[i], bf_[j], acc[i][j], 0, 0, 0, 0, 0, 0); \
+    }                                                                                        \
+  } while (0)
+
+  const int nk2 = (nk + 1) & ~1;
+  if (nk2 > 0) {
+    FP8_LOAD(la0, lb0, 0);
+    la0.store(lds, tid);
+    lb0.store(lds + 2 * BM * RS, tid);
+    FP8_LOAD(la1, lb1, 1);
+  }
+  __syncthreads();
+  for (int it = 0; it < nk2; it += 2) {
+    if (it + 2 < nk2) FP8_LOAD(la0, lb0, it + 2);
+    FP8_COMPUTE(0);
+    la1.store(lds + BM * RS, tid);
+    lb1.store(lds + 2 * BM * RS + BN * RS, tid);
+    __syncthreads();
+    if (it + 3 < nk2) FP8_LOAD(la1, lb1, it + 3);
+    FP8_COMPUTE(1);
+    if (it + 2 < nk2) {
+      la0.store(lds, tid);
+      lb0.store(lds + 2 * BM * RS, tid);
+    }
+    __syncthreads();
+  }
+#undef FP8_LOAD
+#undef FP8_FRAG
+#undef FP8_COMPUTE
+
+  constexpr int CS = TN + 4;
+  constexpr int LPR = TN / 4, RPI = 64 / LPR;
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * CS;
+  const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
+                   (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
+  const int lc = (lane % LPR) * 4, lrow = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r] * dq;
+    __syncthreads();
+    const int row0 = m0 + wm * TM + i * 32;
+    const int col = n0 + wn * TN + lc;
+    for (int rr = lrow; rr < 32; rr += RPI) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+      if (p.splits > 1) {
+        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
+        const float e[4] = {a.x, a.y, a.z, a.w};
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) w[t] = e[t];
+      } else if (vec && col + 3 < p.N) {
+        epilogue_vec4(p, bz, row, col, a);
+      } else {
+        const float e[4] = {a.x, a.y, a.z, a.w};
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 SIMT GEMM: 64x64 tile, 256 threads, 4x4 outputs per thread
 
 template <bool AK, bool BKM>
@@ -463,7 +618,7 @@ int gemm_auto_splits(const GemmArgs& p) {
   int tm, tn;
   if (p.dtype == ACT_F32) {
     tm = 64; tn = 64;
-  } else if (pick_tile(p) != 2) {
+  } else if (p.fp8 || pick_tile(p) != 2) {
     tm = 256; tn = 256;
   } else {
     tm = 128; tn = 128;
@@ -492,6 +647,7 @@ const char* gemm_kernel_name(const GemmArgs& p) {
        "gemm_bf16x3_kernel<256,256,TT>"},
       {"gemm_bf16x3_kernel<128,128,NT>", "gemm_bf16x3_kernel<128,128,NN>", "gemm_bf16x3_kernel<128,128,TN>",
        "gemm_bf16x3_kernel<128,128,TT>"}};
+  if (p.fp8) return "gemm_fp8_kernel<256,256,NT>";
   const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
   const int t = p.dtype == ACT_F32 ? 0 : (pick_tile(p) == 2 ? 2 : 1);
   if (p.split && t) return split_names[t][lay];
@@ -508,6 +664,13 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if ((size_t)p.splits * p.batch * p.M * p.N * sizeof(float) > p.ws_bytes) return 1;
   }
   if (p.split && (p.dtype != ACT_BF16 || p.splits != 1 || !p.A_lo || !p.B_lo)) return 1;
+  if (p.fp8) {
+    if (!p.a_kmaj || !p.b_kmaj || p.split || !p.dq_a || !p.dq_b) return 1;
+    if (p.K % 16 || p.lda % 16 || p.ldb % 16) return 2;
+    if ((long)p.M * p.lda >= (long)0xFFFFFFF0u || (long)p.N * p.ldb >= (long)0xFFFFFFF0u) return 2;
+    const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    hipLaunchKernelGGL((gemm_fp8_kernel<256, 256, 2, 2>), dim3(tiles, p.batch * p.splits), dim3(256), 0, st, p);
+  } else
   if (p.dtype == ACT_BF16) {
     // buffer loads address each operand matrix with 32-bit byte offsets
     const long abytes = (long)(p.a_kmaj ? p.M : p.K) * p.lda * 2, bbytes = (long)(p.b_kmaj ? p.N : p.K) * p.ldb * 2;

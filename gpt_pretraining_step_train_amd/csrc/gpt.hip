@@ -52,11 +52,15 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 struct Offsets {
   size_t params, grads, mom, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
-      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err;
+      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
+      amax, qinv;
   size_t splitws_bytes;
 };
 
 constexpr int kSumsqParts = 64;
+// quantisation events of one fp8 step: weights (4 per layer + head), forward inputs
+// (4 per layer + head), backward output gradients and inputs (8 per layer + 2)
+inline size_t kQuantSlots(const gpt_cfg& c) { return 16 * (size_t)c.depth + 8; }
 
 int act_of(const gpt_cfg& c) { return c.precision == GPT_FP32 ? ACT_F32 : ACT_BF16; }
 
@@ -130,6 +134,19 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.ss = P.add(6 * L * 8);
   O.mat_off = P.add(6 * L * 8);
   O.mat_size = P.add(6 * L * 8);
+  if (c.precision == GPT_FP8) {
+    const size_t wide = std::max(std::max(3 * d, F), V);
+    O.wq8 = P.add(nBlk + nU);
+    O.wtq8 = P.add(nBlk + nU);
+    O.wscale = P.add((4 * L + 1) * 4);
+    O.q8a = P.add(N * wide);
+    O.q8b = P.add(N * wide);
+    O.q8c = P.add(N * std::max(d, F));
+    O.amax = P.add(kQuantSlots(c) * 4);
+    O.qinv = P.add(kQuantSlots(c) * 4);
+  } else {
+    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.amax = O.qinv = 0;
+  }
   O.rope = P.add(T * (c.head_dim / 2) * 2 * 4);
   O.loss = P.add(8);
   O.err = P.add(16);
@@ -151,6 +168,9 @@ struct gpt_model {
   LayerOffs lo;
   int last_status = GPT_OK;
   bool stepped = false;
+  bool fp8 = false;
+  bool wq_dirty = true;  // fp8 weight copies must be refreshed before the next step
+  int qslot = 0;         // next quantisation slot of the current step
   // matrix table for Muon, in layer order (q, k, v, o, w1, w2)
   std::vector<long> moff, msize;
   // profiling
@@ -251,6 +271,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->muon_momentum = 0.95f;
   out->ns_steps = 5;
   out->ns_split_steps = 3;
+  out->fp8_gemms = GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
   out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
@@ -268,8 +289,12 @@ int gpt_cfg_validate(const gpt_cfg* c) {
   if (c->d_model > 2048) return GPT_ERR_UNSUPPORTED;
   if (((long)c->batch * c->seq_len) % 8) return GPT_ERR_SHAPE;
   if ((long)c->batch * c->seq_len > (1L << 30) / 4) return GPT_ERR_UNSUPPORTED;
-  if (c->precision != GPT_FP32 && c->precision != GPT_BF16) return GPT_ERR_UNSUPPORTED;
+  if (c->precision != GPT_FP32 && c->precision != GPT_BF16 && c->precision != GPT_FP8) return GPT_ERR_UNSUPPORTED;
+  if (c->precision == GPT_FP8 && (c->d_model % 16 || c->d_ff % 16 || c->vocab % 16 ||
+                                  ((long)c->batch * c->seq_len) % 16))
+    return GPT_ERR_SHAPE;
   if (c->ns_steps < 0 || c->ns_steps > 5 || c->ns_split_steps < 0) return GPT_ERR_ARG;
+  if (c->fp8_gemms & ~(GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD)) return GPT_ERR_ARG;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
 }
@@ -332,6 +357,7 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   M->bytes = arena_bytes;
   M->at = act_of(*cfg);
   M->es = M->at == ACT_BF16 ? 2 : 4;
+  M->fp8 = cfg->precision == GPT_FP8;
   M->N = cfg->batch * cfg->seq_len;
   M->lo = layer_offs(*cfg);
   M->nE = (size_t)cfg->vocab * cfg->d_model;
@@ -382,6 +408,108 @@ void gpt_free(gpt_model* M) {
   delete M;
 }
 
+// Linear weights as GEMM operands: index w = 4l + {0: Wqkv [3d][d], 1: Wo, 2: W1, 3: W2}, w = 4L: U.
+struct WInfo {
+  size_t off;  // element offset inside the (blocks | U) part of the tensor table
+  int rows, cols;
+};
+static WInfo winfo(const gpt_model* M, int w) {
+  const gpt_cfg& c = M->cfg;
+  if (w == 4 * c.depth) return {M->nBlk, c.vocab, c.d_model};
+  const int l = w / 4, j = w % 4, d = c.d_model, F = c.d_ff;
+  const size_t b = (size_t)l * M->lo.stride;
+  switch (j) {
+    case 0: return {b + M->lo.q, 3 * d, d};
+    case 1: return {b + M->lo.o, d, d};
+    case 2: return {b + M->lo.w1, F, d};
+    default: return {b + M->lo.w2, d, F};
+  }
+}
+
+// e4m3 copies (row-major and transposed) of every Linear weight with its own
+// per-tensor scale, from the fp32 masters
+static void quant_weights(gpt_model* M, hipStream_t st) {
+  const Offsets& O = M->off;
+  unsigned* amax = M->at_off<unsigned>(O.amax);
+  float* wscale = M->at_off<float>(O.wscale);
+  const float* master = M->params() + M->nE;  // blocks | U
+  for (int w = 0; w <= 4 * M->cfg.depth; ++w) {
+    const WInfo wi = winfo(M, w);
+    const int slot = M->qslot++;
+    launch_amax(master + wi.off, ACT_F32, wi.rows, wi.cols, wi.cols, amax + slot, st);
+    launch_quant_e4m3(master + wi.off, ACT_F32, wi.rows, wi.cols, wi.cols, amax + slot,
+                      M->at_off<uint8_t>(O.wq8) + wi.off, wi.cols, M->at_off<uint8_t>(O.wtq8) + wi.off, wi.rows,
+                      wscale + w, st);
+  }
+  M->wq_dirty = false;
+}
+
+// quantise an activation-typed [rows][cols] tensor: q row-major and/or qt transposed
+static int quant_act(gpt_model* M, const void* x, int rows, int cols, long ldx, uint8_t* q, uint8_t* qt,
+                     hipStream_t st) {
+  const int slot = M->qslot++;
+  unsigned* amax = M->at_off<unsigned>(M->off.amax);
+  launch_amax(x, ACT_BF16, rows, cols, ldx, amax + slot, st);
+  launch_quant_e4m3(x, ACT_BF16, rows, cols, ldx, amax + slot, q, cols, qt, rows,
+                    M->at_off<float>(M->off.qinv) + slot, st);
+  return slot;
+}
+
+// Y = X W^T through weight w; p carries M, N (= rows of W), K, A/lda (X) and the epilogue
+static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st) {
+  const WInfo wi = winfo(M, w);
+  if (!M->fp8 || !(M->cfg.fp8_gemms & GPT_FP8_FWD)) {
+    p.B = w == 4 * M->cfg.depth ? M->uact() : M->wact(wi.off);
+    p.ldb = wi.cols;
+    return run_gemm(M, p, st, false);
+  }
+  uint8_t* q8a = M->at_off<uint8_t>(M->off.q8a);
+  const int sx = quant_act(M, p.A, p.M, p.K, p.lda, q8a, nullptr, st);
+  p.A = q8a; p.lda = p.K;
+  p.B = M->at_off<uint8_t>(M->off.wq8) + wi.off; p.ldb = wi.cols;
+  p.fp8 = true;
+  p.dq_a = M->at_off<float>(M->off.qinv) + sx;
+  p.dq_b = M->at_off<float>(M->off.wscale) + w;
+  return run_gemm(M, p, st, false);
+}
+
+// backward of Y = X W^T: dW = dY^T X into dW (ld = cols of W) and dX = dY W with the
+// epilogue in pd (M = tokens, N = cols of W, K = rows of W, outputs set by the caller)
+static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long ldx, int w, float* dW, GemmArgs pd,
+                   hipStream_t st) {
+  const WInfo wi = winfo(M, w);
+  const int N = M->N, nout = wi.rows, kin = wi.cols;
+  int rc;
+  GemmArgs pw;
+  pw.M = nout; pw.N = kin; pw.K = N;
+  pw.outF = dW; pw.ldo = kin;
+  const bool f8w = M->fp8 && (M->cfg.fp8_gemms & GPT_FP8_WGRAD);
+  const bool f8d = M->fp8 && (M->cfg.fp8_gemms & GPT_FP8_DGRAD);
+  uint8_t* q8a = M->at_off<uint8_t>(M->off.q8a);
+  uint8_t* q8b = M->at_off<uint8_t>(M->off.q8b);
+  uint8_t* q8c = M->at_off<uint8_t>(M->off.q8c);
+  const float* qinv = M->at_off<float>(M->off.qinv);
+  const int sy = (f8w || f8d) ? quant_act(M, dY, N, nout, ldy, f8d ? q8a : nullptr, f8w ? q8b : nullptr, st) : 0;
+  if (f8w) {
+    const int sx = quant_act(M, X, N, kin, ldx, nullptr, q8c, st);  // X^T
+    pw.A = q8b; pw.lda = N; pw.B = q8c; pw.ldb = N;                 // dY^T and X^T, reduction over tokens
+    pw.fp8 = true; pw.dq_a = qinv + sy; pw.dq_b = qinv + sx;
+  } else {
+    pw.A = dY; pw.lda = ldy; pw.a_kmaj = false;
+    pw.B = X; pw.ldb = ldx; pw.b_kmaj = false;
+  }
+  if ((rc = run_gemm(M, pw, st, true))) return rc;
+  if (f8d) {
+    pd.A = q8a; pd.lda = nout;
+    pd.B = M->at_off<uint8_t>(M->off.wtq8) + wi.off; pd.ldb = nout;
+    pd.fp8 = true; pd.dq_a = qinv + sy; pd.dq_b = M->at_off<float>(M->off.wscale) + w;
+  } else {
+    pd.A = dY; pd.lda = ldy;
+    pd.B = w == 4 * M->cfg.depth ? M->uact() : M->wact(wi.off); pd.ldb = kin; pd.b_kmaj = false;
+  }
+  return run_gemm(M, pd, st, false);
+}
+
 static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, hipStream_t st) {
   const gpt_cfg& c = M->cfg;
   const int N = M->N, d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth, H = c.n_head, hd = c.head_dim;
@@ -399,9 +527,14 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   int rc;
 
   launch_zero(err, 16, st);
+  if (M->fp8) {
+    M->qslot = 0;
+    launch_zero(M->base + O.amax, kQuantSlots(c) * 4, st);
+    if (M->wq_dirty) quant_weights(M, st);
+    else M->qslot = 4 * L + 1;
+  }
   launch_embed_gather(tok, M->params(), hsl(0), N, d, V, err, st);
   for (int l = 0; l < L; ++l) {
-    const size_t wl = (size_t)l * M->lo.stride;
     void* a = actp(O.a, (size_t)l * N * d);
     void* qkv = actp(O.qkv, (size_t)l * N * 3 * d);
     void* o = actp(O.o, (size_t)l * N * d);
@@ -413,37 +546,33 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
     launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
     {
-      GemmArgs p;
-      p.M = N; p.N = 3 * d; p.K = d;
-      p.A = a; p.lda = d; p.B = M->wact(wl + M->lo.q); p.ldb = d;
+      GemmArgs p;  // qkv = a Wqkv^T
+      p.M = N; p.N = 3 * d; p.K = d; p.A = a; p.lda = d;
       p.outA = qkv; p.ldoa = 3 * d;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 0, st))) return rc;
     }
     launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, eps, st);
     launch_attn_fwd(qkv, o, lse, at, B, T, H, hd, st);
     {
-      GemmArgs p;
-      p.M = N; p.N = d; p.K = d;
-      p.A = o; p.lda = d; p.B = M->wact(wl + M->lo.o); p.ldb = d;
+      GemmArgs p;  // h' = h + o Wo^T
+      p.M = N; p.N = d; p.K = d; p.A = o; p.lda = d;
       p.Cin = hsl(2 * l); p.ldcin = d; p.beta = 1.f;
       p.outF = hsl(2 * l + 1); p.ldo = d;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 1, st))) return rc;
     }
     launch_rmsnorm_fwd(hsl(2 * l + 1), m, at, M->at_off<float>(O.rstd_m) + (size_t)l * N, N, d, eps, st);
     {
-      GemmArgs p;
-      p.M = N; p.N = F; p.K = d;
-      p.A = m; p.lda = d; p.B = M->wact(wl + M->lo.w1); p.ldb = d;
+      GemmArgs p;  // u = m W1^T, g = relu(u)^2
+      p.M = N; p.N = F; p.K = d; p.A = m; p.lda = d;
       p.epi = EPI_RELU2; p.outA = u; p.out2 = g; p.ldoa = F;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 2, st))) return rc;
     }
     {
-      GemmArgs p;
-      p.M = N; p.N = d; p.K = F;
-      p.A = g; p.lda = F; p.B = M->wact(wl + M->lo.w2); p.ldb = F;
+      GemmArgs p;  // h'' = h' + g W2^T
+      p.M = N; p.N = d; p.K = F; p.A = g; p.lda = F;
       p.Cin = hsl(2 * l + 1); p.ldcin = d; p.beta = 1.f;
       p.outF = hsl(2 * l + 2); p.ldo = d;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 3, st))) return rc;
     }
   }
   void* r = M->base + O.r;
@@ -451,11 +580,10 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   float* logits = M->at_off<float>(O.logits);
   void* dlogits = M->base + O.dlogits;
   {
-    GemmArgs p;
-    p.M = N; p.N = V; p.K = d;
-    p.A = r; p.lda = d; p.B = M->uact(); p.ldb = d;
+    GemmArgs p;  // logits = r U^T
+    p.M = N; p.N = V; p.K = d; p.A = r; p.lda = d;
     p.outF = logits; p.ldo = V;
-    if ((rc = run_gemm(M, p, st, false))) return rc;
+    if ((rc = lin_fwd(M, p, 4 * L, st))) return rc;
   }
   launch_cross_entropy(logits, tgt, dlogits, at, M->at_off<float>(O.row_loss), M->at_off<int32_t>(O.argmax), N, V,
                        1.f / (float)N, err, st);
@@ -469,18 +597,10 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   void* dqkv = M->base + O.dqkv;
   void* do_act = M->base + O.do_act;
   {
-    GemmArgs p;  // dr = dz U
-    p.M = N; p.N = d; p.K = V;
-    p.A = dlogits; p.lda = V; p.B = M->uact(); p.ldb = d; p.b_kmaj = false;
-    p.outF = dtmp; p.ldo = d;
-    if ((rc = run_gemm(M, p, st, false))) return rc;
-  }
-  {
-    GemmArgs p;  // dU = dz^T r
-    p.M = V; p.N = d; p.K = N;
-    p.A = dlogits; p.lda = V; p.a_kmaj = false; p.B = r; p.ldb = d; p.b_kmaj = false;
-    p.outF = grads + M->nE + M->nBlk; p.ldo = d;
-    if ((rc = run_gemm(M, p, st, true))) return rc;
+    GemmArgs pd;  // dU = dz^T r ; dr = dz U
+    pd.M = N; pd.N = d; pd.K = V;
+    pd.outF = dtmp; pd.ldo = d;
+    if ((rc = lin_bwd(M, dlogits, V, r, d, 4 * L, grads + M->nE + M->nBlk, pd, st))) return rc;
   }
   launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps, st);
   int cur = 0;
@@ -496,65 +616,33 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     float* rk = M->at_off<float>(O.rk) + (size_t)l * N * H;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
     {
-      GemmArgs p;  // dW2 = dY^T g
-      p.M = d; p.N = F; p.K = N;
-      p.A = dh_act; p.lda = d; p.a_kmaj = false; p.B = g; p.ldb = F; p.b_kmaj = false;
-      p.outF = gblk + wl + M->lo.w2; p.ldo = F;
-      if ((rc = run_gemm(M, p, st, true))) return rc;
+      GemmArgs pd;  // dW2 = dY^T g ; du = (dY W2) * 2 relu(u)
+      pd.M = N; pd.N = F; pd.K = d;
+      pd.epi = EPI_DRELU2; pd.aux = u; pd.outA = dbig; pd.ldoa = F;
+      if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st))) return rc;
     }
     {
-      GemmArgs p;  // du = (dY W2) * 2 relu(u)
-      p.M = N; p.N = F; p.K = d;
-      p.A = dh_act; p.lda = d; p.B = M->wact(wl + M->lo.w2); p.ldb = F; p.b_kmaj = false;
-      p.epi = EPI_DRELU2; p.aux = u; p.outA = dbig; p.ldoa = F;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
-    }
-    {
-      GemmArgs p;  // dW1 = du^T m
-      p.M = F; p.N = d; p.K = N;
-      p.A = dbig; p.lda = F; p.a_kmaj = false; p.B = m; p.ldb = d; p.b_kmaj = false;
-      p.outF = gblk + wl + M->lo.w1; p.ldo = d;
-      if ((rc = run_gemm(M, p, st, true))) return rc;
-    }
-    {
-      GemmArgs p;  // dm = du W1
-      p.M = N; p.N = d; p.K = F;
-      p.A = dbig; p.lda = F; p.B = M->wact(wl + M->lo.w1); p.ldb = d; p.b_kmaj = false;
-      p.outF = dtmp; p.ldo = d;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      GemmArgs pd;  // dW1 = du^T m ; dm = du W1
+      pd.M = N; pd.N = d; pd.K = F;
+      pd.outF = dtmp; pd.ldo = d;
+      if ((rc = lin_bwd(M, dbig, F, m, d, 4 * l + 2, gblk + wl + M->lo.w1, pd, st))) return rc;
     }
     launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur], dh[cur ^ 1],
                        dh_act, at, N, d, eps, st);
     cur ^= 1;
     {
-      GemmArgs p;  // dWo = dY^T o
-      p.M = d; p.N = d; p.K = N;
-      p.A = dh_act; p.lda = d; p.a_kmaj = false; p.B = o; p.ldb = d; p.b_kmaj = false;
-      p.outF = gblk + wl + M->lo.o; p.ldo = d;
-      if ((rc = run_gemm(M, p, st, true))) return rc;
-    }
-    {
-      GemmArgs p;  // do = dY Wo
-      p.M = N; p.N = d; p.K = d;
-      p.A = dh_act; p.lda = d; p.B = M->wact(wl + M->lo.o); p.ldb = d; p.b_kmaj = false;
-      p.outA = do_act; p.ldoa = d;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      GemmArgs pd;  // dWo = dY^T o ; do = dY Wo
+      pd.M = N; pd.N = d; pd.K = d;
+      pd.outA = do_act; pd.ldoa = d;
+      if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st))) return rc;
     }
     launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, hd, st);
     launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, st);
     {
-      GemmArgs p;  // dWqkv = dqkv^T a
-      p.M = 3 * d; p.N = d; p.K = N;
-      p.A = dqkv; p.lda = 3 * d; p.a_kmaj = false; p.B = a; p.ldb = d; p.b_kmaj = false;
-      p.outF = gblk + wl + M->lo.q; p.ldo = d;
-      if ((rc = run_gemm(M, p, st, true))) return rc;
-    }
-    {
-      GemmArgs p;  // da = dqkv Wqkv
-      p.M = N; p.N = d; p.K = 3 * d;
-      p.A = dqkv; p.lda = 3 * d; p.B = M->wact(wl + M->lo.q); p.ldb = d; p.b_kmaj = false;
-      p.outF = dtmp; p.ldo = d;
-      if ((rc = run_gemm(M, p, st, false))) return rc;
+      GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
+      pd.M = N; pd.N = d; pd.K = 3 * d;
+      pd.outF = dtmp; pd.ldo = d;
+      if ((rc = lin_bwd(M, dqkv, 3 * d, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
     }
     launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur], dh[cur ^ 1], dh_act,
                        at, N, d, eps, st);
@@ -682,6 +770,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       launch_muon_apply(wblk + mo, M->at == ACT_BF16 ? M->wact(mo) : nullptr, M->at, xf + xdst(l, j), lr, rows, cols,
                         transposed(j), st);
     }
+  M->wq_dirty = true;
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
@@ -724,6 +813,7 @@ int gpt_set_params(gpt_model* M, int32_t id, const float* h, size_t n, void* s) 
   hipStream_t st = (hipStream_t)s;
   int rc = copy_tensor(M, id, M->params(), false, const_cast<float*>(h), n, st, false);
   if (rc) return rc;
+  M->wq_dirty = true;
   if (M->at == ACT_BF16) {
     size_t off;
     int r, c;
@@ -803,6 +893,30 @@ int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, cons
   p.A = Ah; p.A_lo = Al; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
   p.B = Bh; p.B_lo = Bl; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
   p.outF = C; p.ldo = ldc; p.strideO = sC;
+  const int rc = launch_gemm(p, (hipStream_t)stream);
+  if (rc) return rc == 1 ? GPT_ERR_ARG : GPT_ERR_SHAPE;
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_quant_e4m3(int dtype, const void* x, int rows, int cols, long ld, uint32_t* amax_slot, uint8_t* q, uint8_t* qt,
+                    float* inv_scale, void* stream) {
+  const int at = act_type(dtype);
+  if (at < 0) return GPT_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || ld < cols || !x || !amax_slot || !inv_scale || (!q && !qt)) return GPT_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  launch_zero(amax_slot, 4, st);
+  launch_amax(x, at, rows, cols, ld, amax_slot, st);
+  launch_quant_e4m3(x, at, rows, cols, ld, amax_slot, q, cols, qt, rows, inv_scale, st);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t* B, long ldb, const float* dq_a,
+                  const float* dq_b, float* C, long ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || !A || !B || !dq_a || !dq_b || !C) return GPT_ERR_ARG;
+  GemmArgs p;
+  p.M = M; p.N = N; p.K = K; p.fp8 = true; p.dtype = ACT_BF16;
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.dq_a = dq_a; p.dq_b = dq_b;
+  p.outF = C; p.ldo = ldc;
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc) return rc == 1 ? GPT_ERR_ARG : GPT_ERR_SHAPE;
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;

@@ -37,6 +37,11 @@ struct GemmArgs {
   const void* A_lo = nullptr;
   const void* B_lo = nullptr;
   void* outA_lo = nullptr;        // optional lo plane of outA (v - bf16(v)), same ld/stride
+  // fp8: A and B are e4m3 bytes (both with the reduction index contiguous); the
+  // accumulator is multiplied by (*dq_a) * (*dq_b) (device scalars) before the epilogue
+  bool fp8 = false;
+  const float* dq_a = nullptr;
+  const float* dq_b = nullptr;
 };
 
 // returns 0 on success, else an error code (argument/shape problems)
@@ -83,6 +88,14 @@ void launch_ns_normalize(const float* src, const double* sumsq, int mat, float e
                          bool transpose, float* xf, void* xa, void* xa_lo, int act_type, hipStream_t st);
 void launch_muon_apply(float* w, void* w_act, int act_type, const float* x, float lr, int rows,
                        int cols, bool transposed, hipStream_t st);
+
+// fp8 (OCP e4m3fn) per-tensor current scaling.  amax slot: one uint32 holding the bits of
+// max|x| (non-negative floats order as integers); must be zeroed before launch_amax.
+void launch_amax(const void* x, int in_type, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st);
+// q[r][c] = e4m3(x[r][c] * s) and (optionally) qt[c][r] = the same byte, s = 448/amax
+// (1 when amax = 0); inv_scale[0] = 1/s.  in_type: ACT_F32 or ACT_BF16.
+void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, const unsigned* amax_bits,
+                       uint8_t* q, long ldq, uint8_t* qt, long ldqt, float* inv_scale, hipStream_t st);
 
 // attention
 void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int hd,

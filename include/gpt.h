@@ -48,7 +48,10 @@ typedef enum {
 
 typedef enum { GPT_FP32 = 0, GPT_BF16 = 1, GPT_FP8 = 2 } gpt_precision;
 
-/* Model + step configuration.  depth is the one dial of the article's
+/* Model + step configuration (precision GPT_FP8: the Linear GEMMs -- QKV, output
+ * projection, MLP and LM head, forward and both backward products -- take e4m3
+ * operands with per-tensor current scaling and fp32 accumulation; everything else as
+ * GPT_BF16).  depth is the one dial of the article's
  * "Felsefe" section: gpt_cfg_from_depth derives the rest. */
 typedef struct gpt_cfg {
   int32_t depth;      /* L: decoder blocks */
@@ -70,8 +73,13 @@ typedef struct gpt_cfg {
   int64_t num_steps;  /* informational: steps at a tokens:params ratio of 8 with 2^20-token batches */
   int32_t ns_split_steps; /* bf16 precision: the first ns_split_steps iterations multiply fp32
                              operands split into bf16 hi + lo parts (3 MFMA products); default 3 */
-  int32_t reserved;
+  int32_t fp8_gemms;  /* precision GPT_FP8: which Linear GEMMs take per-tensor scaled e4m3
+                         operands, a mask of GPT_FP8_FWD (Y = X W^T), GPT_FP8_WGRAD
+                         (dW = dY^T X) and GPT_FP8_DGRAD (dX = dY W); default all three.
+                         Other bits: GPT_ERR_ARG. Ignored for the other precisions. */
 } gpt_cfg;
+
+enum { GPT_FP8_FWD = 1, GPT_FP8_WGRAD = 2, GPT_FP8_DGRAD = 4 };
 
 typedef struct gpt_model gpt_model; /* opaque */
 
@@ -159,6 +167,18 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
 int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* Ah, const void* Al, long lda,
                     long sA, const void* Bh, const void* Bl, long ldb, long sB, float* C, long ldc, long sC,
                     void* stream);
+
+/* fp8 (OCP e4m3fn) per-tensor current scaling of x [rows][cols] (row stride ld, fp32 or
+ * bf16 by dtype): s = 448 / max|x| (1 when x is all zero); q [rows][cols] and/or qt
+ * [cols][rows] receive e4m3(x * s) (round to nearest even, saturating at +-448);
+ * inv_scale[0] = 1/s.  amax_slot is one uint32 of scratch. */
+int gptk_quant_e4m3(int dtype, const void* x, int rows, int cols, long ld, uint32_t* amax_slot, uint8_t* q,
+                    uint8_t* qt, float* inv_scale, void* stream);
+
+/* C [M][N] fp32 = dq_a[0] * dq_b[0] * sum_k A[m][k] B[n][k] with e4m3 A [M][K], B [N][K]
+ * (reduction index contiguous, K, lda, ldb multiples of 16), on fp8 MFMA. */
+int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t* B, long ldb, const float* dq_a,
+                  const float* dq_b, float* C, long ldc, void* stream);
 
 /* name of the GEMM kernel instantiation gptk_gemm / gpt_step launch for these
  * layouts and sizes, e.g. "gemm_bf16_kernel<256,256,NT>" (NT: both operands have

@@ -28,12 +28,24 @@ W <- W - lr X) are listed with the design notes of this repository.
 
 Parity pins: every function here is pinned by a test under tests/ that does not
 re-type its formula (finite differences, closed forms, library routines,
-invariants).  fp8 quantisation is not modelled: the fp8 path is compared with
-this unquantised result.
+invariants).
+
+fp8 (cfg precision "fp8"): the Linear GEMMs named by the cfg's fp8_gemms mask
+(1 forward, 2 weight gradient, 4 input gradient) take per-tensor e4m3
+quantised operands (oracle/e4m3.py).  The backward then uses the quantised
+operands as if quantisation were the identity (the straight-through rule every
+fp8 training recipe uses), so the fp8 gradients are not the derivative of the
+fp8 loss.  Q, K and V form one Linear with the concatenated weight [Wq; Wk; Wv],
+so they share one weight scale and one gradient scale.  The e4m3 code of each
+element is a rounding decision; it is taken on the operand as stored (weights
+fp32, activations and output gradients bf16, the scale and the scaled value in
+fp32), so that both implementations decide it from the same number.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from oracle.e4m3 import quantise
 
 # ---------------------------------------------------------------------------
 # configuration / parameter table
@@ -138,9 +150,22 @@ def argmax_lowest(z):
 # forward / backward
 
 
+def _fp8_quantisers(cfg):
+    """Operand maps (activation or output gradient, weight) of the forward, the
+    weight-gradient and the input-gradient GEMMs: per-tensor e4m3
+    quantise-dequantise where the fp8 mask selects that GEMM, identity otherwise."""
+    ident = lambda t: t  # noqa: E731
+    act = lambda t: quantise(t, "bf16")  # noqa: E731
+    wgt = lambda t: quantise(t, "fp32")  # noqa: E731
+    on = cfg.get("precision") == "fp8"
+    mask = cfg.get("fp8_gemms", 7)
+    return tuple((act, wgt) if on and mask & bit else (ident, ident) for bit in (1, 2, 4))
+
+
 def forward(params, tokens, cfg, keep=True):
     """Forward pass.  Returns (logits [B,T,V], cache for backward)."""
     p = [np.asarray(w, dtype=np.float64) for w in params]
+    qf, qfw = _fp8_quantisers(cfg)[0]
     E, layers, U = unpack(p, cfg)
     eps = cfg.get("norm_eps", 1e-6)
     H, hd = cfg["n_head"], cfg["head_dim"]
@@ -152,24 +177,25 @@ def forward(params, tokens, cfg, keep=True):
     cache = {"tokens": tokens, "ang": ang, "layers": [], "p": p}
     for (Wq, Wk, Wv, Wo, W1, W2) in layers:
         a, ra = rms_norm(h, eps)
-        q = (a @ Wq.T).reshape(B, T, H, hd)
-        k = (a @ Wk.T).reshape(B, T, H, hd)
-        v = (a @ Wv.T).reshape(B, T, H, hd)
+        qkv = qf(a) @ qfw(np.concatenate([Wq, Wk, Wv])).T
+        q = qkv[..., :d].reshape(B, T, H, hd)
+        k = qkv[..., d:2 * d].reshape(B, T, H, hd)
+        v = qkv[..., 2 * d:].reshape(B, T, H, hd)
         qn, rq = rms_norm(rope(q, ang), eps)
         kn, rk = rms_norm(rope(k, ang), eps)
         o, _ = causal_attention(qn, kn, v)
         o2 = o.reshape(B, T, d)
-        h1 = h + o2 @ Wo.T
+        h1 = h + qf(o2) @ qfw(Wo).T
         m, rm = rms_norm(h1, eps)
-        u = m @ W1.T
+        u = qf(m) @ qfw(W1).T
         g = np.maximum(u, 0.0) ** 2
-        h2 = h1 + g @ W2.T
+        h2 = h1 + qf(g) @ qfw(W2).T
         if keep:
             cache["layers"].append(dict(h=h, a=a, ra=ra, qn=qn, rq=rq, kn=kn, rk=rk,
                                         v=v, o=o, h1=h1, m=m, rm=rm, u=u, g=g))
         h = h2
     r, rf = rms_norm(h, eps)
-    z = r @ U.T
+    z = qf(r) @ qfw(U).T
     cache.update(hL=h, r=r, rf=rf)
     return z, cache
 
@@ -203,35 +229,35 @@ def backward(z, targets, cache, cfg):
     tokens = cache["tokens"]
 
     dz = cross_entropy_grad(z, targets)
+    _, (qw, _), (qd, qdw) = _fp8_quantisers(cfg)
+
+    def lin_bwd(dy, x, W):
+        """Y = X W^T: (dW = dY^T X, dX = dY W) on the flattened token axis."""
+        dy2 = dy.reshape(N, -1)
+        return qw(dy2).T @ qw(x.reshape(N, -1)), qd(dy2) @ qdw(W)
 
     r = cache["r"]
-    dU = dz.reshape(N, V).T @ r.reshape(N, d)
-    dr = dz @ U
-    dh = rms_norm_bwd(dr, r, cache["rf"])
+    dU, dr = lin_bwd(dz, r, U)
+    dh = rms_norm_bwd(dr.reshape(B, T, d), r, cache["rf"])
 
     grads_layers = []
     for (Wq, Wk, Wv, Wo, W1, W2), c in zip(reversed(layers), reversed(cache["layers"])):
         # MLP block: h2 = h1 + g W2^T, g = relu(u)^2, u = m W1^T, m = rms(h1)
-        dW2 = dh.reshape(N, d).T @ c["g"].reshape(N, -1)
-        dg = dh @ W2
-        du = dg * 2.0 * np.maximum(c["u"], 0.0)
-        dW1 = du.reshape(N, -1).T @ c["m"].reshape(N, d)
-        dm = du @ W1
-        dh1 = dh + rms_norm_bwd(dm, c["m"], c["rm"])
+        dW2, dg = lin_bwd(dh, c["g"], W2)
+        du = dg.reshape(c["u"].shape) * 2.0 * np.maximum(c["u"], 0.0)
+        dW1, dm = lin_bwd(du, c["m"], W1)
+        dh1 = dh + rms_norm_bwd(dm.reshape(B, T, d), c["m"], c["rm"])
         # attention block: h1 = h + o Wo^T
-        o2 = c["o"].reshape(B, T, d)
-        dWo = dh1.reshape(N, d).T @ o2.reshape(N, d)
-        do = (dh1 @ Wo).reshape(B, T, H, hd)
+        dWo, do = lin_bwd(dh1, c["o"], Wo)
+        do = do.reshape(B, T, H, hd)
         dqn, dkn, dv = causal_attention_bwd(do, c["qn"], c["kn"], c["v"], c["o"])
         dq = rope(rms_norm_bwd(dqn, c["qn"], c["rq"]), ang, inverse=True).reshape(B, T, d)
         dk = rope(rms_norm_bwd(dkn, c["kn"], c["rk"]), ang, inverse=True).reshape(B, T, d)
         dv = dv.reshape(B, T, d)
-        a2 = c["a"].reshape(N, d)
-        dWq = dq.reshape(N, d).T @ a2
-        dWk = dk.reshape(N, d).T @ a2
-        dWv = dv.reshape(N, d).T @ a2
-        da = dq @ Wq + dk @ Wk + dv @ Wv
-        dh = dh1 + rms_norm_bwd(da, c["a"], c["ra"])
+        # one Linear with weight [Wq; Wk; Wv]: dY = [dq | dk | dv]
+        dWqkv, da = lin_bwd(np.concatenate([dq, dk, dv], axis=-1), c["a"], np.concatenate([Wq, Wk, Wv]))
+        dWq, dWk, dWv = dWqkv[:d], dWqkv[d:2 * d], dWqkv[2 * d:]
+        dh = dh1 + rms_norm_bwd(da.reshape(B, T, d), c["a"], c["ra"])
         grads_layers.append((dWq, dWk, dWv, dWo, dW1, dW2))
     grads_layers.reverse()
 

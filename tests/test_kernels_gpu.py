@@ -343,3 +343,81 @@ def test_embedding_gather_scatter(N, V, d, dist):
     B.embed_gather(torch.from_numpy(bad).cuda(), tE, h, N, d, V, err)
     torch.cuda.synchronize()
     assert err.cpu().numpy()[0] == 1
+
+
+# ----------------------------------------------------------------------------- fp8 (e4m3)
+
+
+def _e4m3_table():
+    """Values of all 256 OCP e4m3fn codes (NaN for 0x7F / 0xFF), from the format's fields."""
+    vals = np.empty(256)
+    for code in range(256):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            v = np.nan
+        elif e == 0:
+            v = m / 8 * 2.0 ** -6
+        else:
+            v = (1 + m / 8) * 2.0 ** (e - 7)
+        vals[code] = -v if s else v
+    return vals
+
+
+def _e4m3_encode_ref(x):
+    """Nearest representable value, ties to the even code (mantissa lsb 0), saturating at 448."""
+    tab = _e4m3_table()
+    pos = [c for c in range(128) if np.isfinite(tab[c])]
+    pv = tab[pos]
+    out = np.empty(x.shape, dtype=np.uint8)
+    for idx, v in np.ndenumerate(x):
+        a = min(abs(v), 448.0)
+        dist = np.abs(pv - a)
+        best = np.flatnonzero(dist == dist.min())
+        code = pos[best[0]] if len(best) == 1 else [pos[b] for b in best if pos[b] % 2 == 0][0]
+        out[idx] = code | (0x80 if v < 0 or (v == 0 and np.signbit(v)) else 0)
+    return out
+
+
+def test_quant_e4m3_matches_format():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((67, 129)) * np.exp(rng.uniform(-6, 4, (67, 129)))).astype(np.float32)
+    x[0, 0], x[0, 1], x[0, 2] = 0.0, -0.0, 1e-12
+    amax = np.abs(x).max()
+    s = np.float32(448.0) / np.float32(amax)
+    want = _e4m3_encode_ref((x * s).astype(np.float32))
+    tx = torch.from_numpy(x).cuda()
+    slot = torch.zeros(1, dtype=torch.int32, device="cuda")
+    inv = torch.zeros(1, device="cuda")
+    q = torch.zeros(67, 129, dtype=torch.uint8, device="cuda")
+    qt = torch.zeros(129, 67, dtype=torch.uint8, device="cuda")
+    B.quant_e4m3(B.GPT_FP32, tx, 67, 129, 129, slot, q, qt, inv)
+    torch.cuda.synchronize()
+    got = q.cpu().numpy()
+    nz = want & 0x7F != 0          # signed zero: either sign of the zero code is accepted
+    np.testing.assert_array_equal(got[nz], want[nz])
+    assert np.all(got[~nz] & 0x7F == 0)
+    np.testing.assert_array_equal(qt.cpu().numpy(), got.T)
+    assert inv.item() == pytest.approx(1.0 / s, rel=1e-6)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 160), (512, 768, 1024)])
+def test_gemm_fp8_exact_on_e4m3_values(M, N, K):
+    """e4m3 inputs decode exactly and every product of two e4m3 values is exact, so
+    the only error is the accumulation.  The fp8 matrix instruction does not add its
+    64 products in full fp32 (measured: up to ~7e-5 of max|C|), so the bound is
+    2^-12 of the sum of |products| of each output, per element."""
+    tab = _e4m3_table()
+    rng = np.random.default_rng(M)
+    finite = np.array([c for c in range(256) if np.isfinite(tab[c]) and abs(tab[c]) < 64], dtype=np.uint8)
+    A = rng.choice(finite, size=(M, K))
+    Bq = rng.choice(finite, size=(N, K))
+    ref = tab[A] @ tab[Bq].T * 0.5 * 0.25
+    C = torch.full((M, N), float("nan"), device="cuda")
+    dqa = torch.tensor([0.5], device="cuda")
+    dqb = torch.tensor([0.25], device="cuda")
+    B.gemm_fp8(M, N, K, torch.from_numpy(A).cuda(), K, torch.from_numpy(Bq).cuda(), K, dqa, dqb, C, N)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    mag = np.abs(tab[A]) @ np.abs(tab[Bq]).T * 0.5 * 0.25
+    assert np.all(np.abs(got - ref) <= 2.0 ** -12 * mag)
+    say(f"  fp8 accumulation error max {np.abs(got - ref).max():.3g} of max|C| {np.abs(ref).max():.3g}")

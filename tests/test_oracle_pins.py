@@ -452,3 +452,149 @@ def test_batch_row_swap_symmetry():
     np.testing.assert_allclose(p1, p0[perm], rtol=1e-13)
     for x, y in zip(g0, g1):
         np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# fp8: the e4m3 model and the fp8 oracle step
+
+
+def _e4m3_code_values():
+    """Decode all 126 non-negative finite e4m3fn codes from the bit fields
+    (bias 7, 3 fraction bits, exponent field 0 subnormal, code 0x7F NaN)."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def test_e4m3_round_matches_torch_cast():
+    from oracle.e4m3 import e4m3_round
+    grid = _e4m3_code_values()
+    assert grid[-1] == 448.0 and grid[1] == 2.0 ** -9 and np.all(np.diff(grid) > 0)
+    np.testing.assert_array_equal(e4m3_round(grid), grid)                # every value is a fixed point
+    np.testing.assert_array_equal(e4m3_round(-grid), -grid)
+    mids = (grid[:-1] + grid[1:]) / 2                                    # exact ties
+    rng = np.random.default_rng(5)
+    x = np.concatenate([mids, -mids, rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 2, 20000)])
+    x = np.clip(x, -440.0, 440.0).astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(x).float().to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(e4m3_round(x), want)
+    even = e4m3_round(mids)                                              # ties go to the even code
+    codes = np.searchsorted(grid, even)
+    assert np.all(codes % 2 == 0)
+
+
+def test_e4m3_saturation_and_quantise_invariants():
+    from oracle.e4m3 import e4m3_round, quantise
+    np.testing.assert_array_equal(e4m3_round(np.array([448.0, 463.9, 464.0, 1e6, -500.0])),
+                                  [448.0, 448.0, 448.0, 448.0, -448.0])
+    rng = np.random.default_rng(6)
+    t = rng.standard_normal((64, 48)) * 0.02
+    q = quantise(t)
+    i = np.unravel_index(np.argmax(np.abs(t)), t.shape)
+    assert q[i] == pytest.approx(t[i], rel=1e-15)                         # amax lands on 448 exactly
+    big = np.abs(t) >= np.abs(t[i]) * 2.0 ** -6 / 448                     # normal range after scaling
+    assert np.all(np.abs(q - t)[big] <= np.abs(t)[big] * 2.0 ** -4 + 1e-18)
+    np.testing.assert_array_equal(quantise(t * 2.0 ** 7), q * 2.0 ** 7)  # per-tensor scale invariance
+    np.testing.assert_array_equal(quantise(np.zeros((3, 4))), np.zeros((3, 4)))
+    assert len(np.unique(np.round(quantise(t) * 448 / np.abs(t[i]), 9))) <= 253
+
+
+def _tq(t, store):
+    """Per-tensor e4m3 quantise-dequantise with torch's own bfloat16 and float8
+    casts: the operand as stored (bf16 or fp32), s = 448/amax and t*s in fp32."""
+    x = t.to(torch.bfloat16).float() if store == "bf16" else t.float()
+    amax = x.abs().max()
+    s = torch.full((), 448.0) / amax if amax > 0 else torch.ones(())   # one rounded fp32 division
+    return (x * s).clamp(-448, 448).to(torch.float8_e4m3fn).to(t.dtype) / s.double()
+
+
+class _F8Linear(torch.autograd.Function):
+    """Y = X W^T with the straight-through fp8 rule: the GEMMs the mask selects
+    (1 forward, 2 weight gradient, 4 input gradient) see quantised operands."""
+
+    @staticmethod
+    def forward(ctx, x, w, mask):
+        ctx.save_for_backward(x, w)
+        ctx.mask = mask
+        on = bool(mask & 1)
+        return (_tq(x, "bf16") if on else x) @ (_tq(w, "fp32") if on else w).T
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, w = ctx.saved_tensors
+        g2, x2 = gy.reshape(-1, gy.shape[-1]), x.reshape(-1, x.shape[-1])
+        a = lambda t, bit: _tq(t, "bf16") if ctx.mask & bit else t  # noqa: E731
+        dw = a(g2, 2).T @ a(x2, 2)
+        dx = a(g2, 4) @ (_tq(w, "fp32") if ctx.mask & 4 else w)
+        return dx.reshape(x.shape), dw, None
+
+
+def _torch_fp8_loss(params, tok, tgt, cfg, mask):
+    E, U = params[0], params[-1]
+    L, H, hd, d = cfg["depth"], cfg["n_head"], cfg["head_dim"], cfg["d_model"]
+    B, T = tok.shape
+    eps = cfg["norm_eps"]
+    lin = lambda x, w: _F8Linear.apply(x, w, mask)  # noqa: E731
+    pos = torch.arange(T, dtype=torch.float64)
+    inv = cfg["rope_base"] ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    ang = pos[:, None] * inv[None, :]
+    cos = torch.cat([ang.cos(), ang.cos()], -1)[None, :, None, :]
+    sin = torch.cat([ang.sin(), ang.sin()], -1)[None, :, None, :]
+
+    def rot(x):
+        x1, x2 = x[..., : hd // 2], x[..., hd // 2:]
+        return x * cos + torch.cat([-x2, x1], -1) * sin
+
+    rms = lambda x: torch.nn.functional.rms_norm(x, (x.shape[-1],), eps=eps)  # noqa: E731
+    x = E[torch.from_numpy(tok).long()]
+    for l in range(L):
+        Wq, Wk, Wv, Wo, W1, W2 = params[1 + 6 * l: 7 + 6 * l]
+        qkv = lin(rms(x), torch.cat([Wq, Wk, Wv]))
+        q = rms(rot(qkv[..., :d].reshape(B, T, H, hd)))
+        k = rms(rot(qkv[..., d:2 * d].reshape(B, T, H, hd)))
+        v = qkv[..., 2 * d:].reshape(B, T, H, hd)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), is_causal=True)
+        x = x + lin(o.transpose(1, 2).reshape(B, T, d), Wo)
+        x = x + lin(torch.relu(lin(rms(x), W1)).square(), W2)
+    z = lin(rms(x), U)
+    return torch.nn.functional.cross_entropy(z.reshape(B * T, -1), torch.from_numpy(tgt).long().reshape(-1))
+
+
+@pytest.mark.parametrize("mask", [1, 2, 4, 7])
+def test_fp8_step_vs_torch_float8_autograd(mask):
+    """Each fp8 flag and all three together against torch autograd over torch's
+    own bfloat16 and float8 casts."""
+    cfg = dict(TINY, precision="fp8", fp8_gemms=mask, batch=2, seq_len=64)
+    params = _params(cfg, seed=41, std=0.1)
+    tok, tgt = _tokens(cfg, seed=42, dist="zipf")
+    loss, grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    tp = [torch.from_numpy(w.copy()).requires_grad_() for w in params]
+    tl = _torch_fp8_loss(tp, tok, tgt, cfg, mask)
+    tl.backward()
+    assert loss == pytest.approx(float(tl.detach()), rel=1e-12)
+    for g, t in zip(grads, tp):
+        rel = np.linalg.norm(g - t.grad.numpy()) / np.linalg.norm(t.grad.numpy())
+        assert rel < 1e-9
+
+
+def test_fp8_flags_reach_their_gemms():
+    base = dict(TINY, batch=2, seq_len=64)
+    params = _params(base, seed=43, std=0.1)
+    tok, tgt = _tokens(base, seed=44)
+    l0, g0, _, _ = O.loss_and_grads(params, tok, tgt, base)
+    res = {m: O.loss_and_grads(params, tok, tgt, dict(base, precision="fp8", fp8_gemms=m)) for m in (0, 1, 2, 4)}
+    assert res[0][0] == l0 and all(np.array_equal(a, b) for a, b in zip(res[0][1], g0))
+    for m in (2, 4):                      # backward-only flags leave the forward exact
+        assert res[m][0] == l0
+    assert 0 < abs(res[1][0] - l0) / l0 < 1e-2
+    for m in (1, 2, 4):
+        errs = [np.linalg.norm(a - b) / np.linalg.norm(b) for a, b in zip(res[m][1], g0)]
+        assert min(errs[1:-1]) > 1e-3 and max(errs) < 0.3, (m, errs)
+    # the input-gradient flag cannot touch the head's weight gradient, the weight-gradient one can
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)  # noqa: E731
+    assert rel(res[4][1][-1], g0[-1]) == 0 and rel(res[2][1][-1], g0[-1]) > 1e-3
+    # and only the weight-gradient flag leaves the embedding gradient exact
+    assert rel(res[2][1][0], g0[0]) == 0 and rel(res[4][1][0], g0[0]) > 1e-3

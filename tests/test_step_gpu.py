@@ -5,6 +5,14 @@ Bars: loss relative error <= 1e-3 and per-tensor gradient / update relative L2
 <= 2e-2 (bf16 and fp32); integer work bit-exact.  The tiny config runs in fp32
 and is also held to the tighter bounds fp32 arithmetic gives.  The d12 config
 runs at batch 1 (full width, depth, vocabulary and sequence length).
+
+fp8 (e4m3 operands on every Linear GEMM): loss <= 1e-2 and gradients <= 6e-2
+against the oracle that models the same quantisation, and loss <= 1e-2 against
+the unquantised oracle too.  The d26 width (1664, 13 heads) runs at depth 1; at
+depth >= 2 the Q/K projection gradients of any two fp8 computations that differ
+at bf16 rounding level drift further apart than 6e-2 (code flips at e4m3
+rounding boundaries are amplified layer by layer), so that case is held to the
+oracle's own spread under such a perturbation instead.
 """
 import numpy as np
 import pytest
@@ -29,7 +37,7 @@ def _gpu():
 
 
 def _setup(name, seed=0, **over):
-    cfg = configs.get(name, **over)
+    cfg = configs.get(name.replace("_fp8", ""), **over)
     model = binding.Model(cfg, seed=seed)
     params = inputs.init_weights(cfg, seed)
     model.set_all_params(params)
@@ -41,7 +49,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1})]
+STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8", {"precision": "fp8"}),
+              ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
 @pytest.mark.parametrize("name,over", STEP_CASES, ids=[c[0] for c in STEP_CASES])
@@ -52,22 +61,28 @@ def test_step_and_muon_parity(name, over):
     torch.cuda.synchronize()
     ref_loss, ref_grads, ref_am, ref_rows = O.loss_and_grads(params, tok, tgt, cfg)
     fp32 = cfg["precision"] == "fp32"
+    fp8 = cfg["precision"] == "fp8"
     lrel = abs(loss - ref_loss) / abs(ref_loss)
     say(f"  loss {loss:.7f} oracle {ref_loss:.7f} rel {lrel:.2e}")
-    assert lrel <= (1e-5 if fp32 else 1e-3)
+    assert lrel <= (1e-5 if fp32 else 1e-2 if fp8 else 1e-3)
+    if fp8:  # and against the result without quantisation
+        exact = O.loss_only(params, tok, tgt, dict(cfg, precision="bf16"))
+        say(f"  loss vs unquantised oracle rel {abs(loss - exact) / exact:.2e}")
+        assert abs(loss - exact) / exact <= 1e-2
     rows = model.row_loss().cpu().numpy().reshape(tok.shape)
-    assert rel_l2(rows, ref_rows) < (1e-5 if fp32 else 2e-3)
+    assert rel_l2(rows, ref_rows) < (1e-5 if fp32 else 2e-2 if fp8 else 2e-3)
     am = model.argmax().cpu().numpy().reshape(tok.shape)
-    assert np.mean(am == ref_am) > (0.999 if fp32 else 0.95)
-    worst = 0.0
+    assert np.mean(am == ref_am) > (0.999 if fp32 else 0.5 if fp8 else 0.95)
+    worst, worst_i = 0.0, -1
     grads = []
     for i, ref in enumerate(ref_grads):
         g = model.grads(i)
         grads.append(g)
         e = rel_l2(g, ref)
-        worst = max(worst, e)
-        assert e <= (1e-4 if fp32 else 2e-2), (i, e)
-    say(f"  worst grad rel L2 {worst:.2e}")
+        if e > worst:
+            worst, worst_i = e, i
+        assert e <= (1e-4 if fp32 else 6e-2 if fp8 else 2e-2), (i, e)
+    say(f"  worst grad rel L2 {worst:.2e} (tensor {worst_i})")
     # Muon fed the GPU's own gradients (and zero momentum) on both sides
     table, _ = PE.coefficients()
     L = cfg["depth"]
@@ -89,6 +104,25 @@ def test_step_and_muon_parity(name, over):
     # E and U untouched
     np.testing.assert_array_equal(model.get_params(0), params[0])
     np.testing.assert_array_equal(model.get_params(1 + 6 * L), params[-1])
+
+
+def test_fp8_two_layers_within_the_oracles_own_spread():
+    """d26 width at depth 2, fp8: each gradient is at most 6e-2, or no further from
+    the oracle than the oracle moves when every weight takes one bf16-sized
+    relative perturbation (N(0, 2^-9)), whichever is larger."""
+    cfg, model, params, tok, tgt = _setup("d26", batch=1, depth=2)
+    assert cfg["precision"] == "fp8"
+    loss = model.step(_dev(tok), _dev(tgt))
+    torch.cuda.synchronize()
+    ref_loss, ref_grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    assert abs(loss - ref_loss) / ref_loss <= 1e-2
+    rng = np.random.default_rng(17)
+    pert = [w.astype(np.float64) * (1 + 2.0 ** -9 * rng.standard_normal(w.shape)) for w in params]
+    _, pert_grads, _, _ = O.loss_and_grads(pert, tok, tgt, cfg)
+    for i, ref in enumerate(ref_grads):
+        e_gpu, e_self = rel_l2(model.grads(i), ref), rel_l2(pert_grads[i], ref)
+        say(f"  tensor {i}: gpu {e_gpu:.3f} oracle spread {e_self:.3f}")
+        assert e_gpu <= max(6e-2, e_self), (i, e_gpu, e_self)
 
 
 def test_second_muon_step_uses_momentum():
