@@ -76,7 +76,19 @@ def main() -> int:
     ap.add_argument("--config", default="d24")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant", default="gemm_bf16_kernel<256,256,NT>")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run three plain device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        torch.cuda.set_device(0)
+        x = torch.ones(args.copy_probe * 2 ** 20 // 4, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4, "copies": 3}), flush=True)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the step has no multi-GPU path in this build "
               "(run with --gpus 1)", file=sys.stderr)

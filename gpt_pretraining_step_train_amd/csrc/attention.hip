@@ -4,16 +4,21 @@
 // as the QKV projection writes it), o and dO [B*T][H*hd], lse and D [B][H][T] fp32.
 // lse is the natural-log log-sum-exp of the scaled scores q.k/sqrt(hd).
 //
-// Forward: a workgroup owns 128 queries (4 waves x 32) and streams 64-key tiles
-// through LDS (K as [key][d], V transposed to [d][key]).  Each wave computes
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so a lane owns one query and the
+// All three bf16 kernels stage 64-row tiles row-major in LDS (double-buffered,
+// the next tile prefetched into registers during the current one).  Products
+// that reduce over the head dimension read rows with ds_read_b128; products that
+// reduce over keys or queries read columns with the gfx950 LDS transpose read
+// (tr_operand), so no tile is ever transposed in registers.
+//
+// Forward: a workgroup owns 128 queries (4 waves x 32).  Each wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so a lane owns one query and its
 // softmax statistics are lane-local (plus one exchange with lane^32).  The
-// probabilities then feed O^T += V^T P^T straight from registers: the k index of
-// that product is a permutation of the 16 keys that matches the accumulator
-// layout, and V^T is read from LDS in the same permuted order.
+// probabilities feed O^T += V^T P^T straight from registers.  The running
+// maximum is only raised when a tile's maximum exceeds it by more than 2^8 in
+// probability (exponents stay <= 8), so the accumulator rescale is rare.
 //
 // Backward, without atomics: D = rowsum(dO*O); a dQ kernel per query block
-// (recomputing P and dP) and a dK/dV kernel per key block (over query blocks).
+// (recomputing P and dP) and a dK/dV kernel per key block (over query tiles).
 #include <math.h>
 
 #include "common.h"
@@ -23,12 +28,10 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold of the forward (log2 units)
 
 __device__ inline bf16x8_t pack8(const float* v) {
-  u32x4_t u;
+  uint4 u;
   u.x = pack_bf2(v[0], v[1]);
   u.y = pack_bf2(v[2], v[3]);
   u.z = pack_bf2(v[4], v[5]);
@@ -36,23 +39,39 @@ __device__ inline bf16x8_t pack8(const float* v) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// two 4-element (8-byte) pieces at p and p+8 -> one 8-element operand
-__device__ inline bf16x8_t ld_split8(const bf16_t* p) {
-  const u32x2_t a = *reinterpret_cast<const u32x2_t*>(p);
-  const u32x2_t b = *reinterpret_cast<const u32x2_t*>(p + 8);
-  u32x4_t u;
-  u.x = a.x; u.y = a.y; u.z = b.x; u.w = b.y;
-  return __builtin_bit_cast(bf16x8_t, u);
-}
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS tile of 64 rows x HD bf16.  For HD = 128 rows are unpadded and the 16-byte
+// chunk c of row r sits at chunk c ^ swz(r), swz(r) = (r%4)*4 + (r/4)%4: sixteen
+// consecutive rows read at one chunk (ds_read_b128) and four consecutive rows read
+// across four chunks (the transpose read) both land on distinct banks.  Other head
+// sizes use rows padded by 16 bytes.
 template <int HD>
 struct Tile {
-  static constexpr int R = 64;       // rows (keys or queries) per LDS tile
-  static constexpr int KS = HD + 8;  // [row][d] stride, elements
-  static constexpr int TS = R + 8;   // [d][row] stride, elements
+  static constexpr int ELEMS = HD == 128 ? 64 * 128 : 64 * (HD + 8);
+  __device__ static inline int off(int r, int d) {
+    if constexpr (HD == 128) {
+      const int swz = ((r & 3) << 2) | ((r >> 2) & 3);
+      return r * 128 + ((((d >> 3) ^ swz)) << 3) + (d & 7);
+    } else {
+      return r * (HD + 8) + d;
+    }
+  }
 };
 
-// [64 rows][HD] tile -> LDS [row][d]
+// tr_operand over a Tile: lane l receives column c0 + l%32 at rows
+// r0 + 4hl + {0..3} and r0 + 8 + 4hl + {0..3} (hl = l/32)
+template <int HD>
+__device__ inline bf16x8_t tile_tr_operand(const bf16_t* T, int r0, int c0, int lane) {
+  const int i = lane & 15;
+  const int r = r0 + 4 * (lane >> 5) + (i >> 2), c = c0 + ((lane >> 4) & 1) * 16 + 4 * (i & 3);
+  const i16x4_t a = lds_read_tr16(T + Tile<HD>::off(r, c));
+  const i16x4_t b = lds_read_tr16(T + Tile<HD>::off(r + 8, c));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// [64 rows][HD] bf16 tile: global -> registers -> LDS [row][d]
 template <int HD>
 struct RowStager {
   static constexpr int NCH = 64 * HD / 8;
@@ -70,53 +89,22 @@ struct RowStager {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * 256, row = c / (HD / 8), cc = c % (HD / 8);
-      *reinterpret_cast<uint4*>(lds + row * Tile<HD>::KS + cc * 8) = r[i];
+      *reinterpret_cast<uint4*>(lds + Tile<HD>::off(row, cc * 8)) = r[i];
     }
   }
 };
 
-// [64 rows][HD] tile -> LDS [d][row] through 8x8 register transposes
-template <int HD>
-struct TrStager {
-  static constexpr int NBLK = (64 / 8) * (HD / 8);
-  static constexpr int PER = (NBLK + 255) / 256;
-  uint4 r[PER * 8];
-  __device__ inline void load(const bf16_t* base, long ld, int row0, int T, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int bb = tid + i * 256, db = bb % (HD / 8), rb = bb / (HD / 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = row0 + rb * 8 + j;
-        r[i * 8 + j] = (bb < NBLK && row < T) ? *reinterpret_cast<const uint4*>(base + (long)row * ld + db * 8)
-                                              : make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ inline void store(bf16_t* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int bb = tid + i * 256, db = bb % (HD / 8), rb = bb / (HD / 8);
-      if (bb >= NBLK) continue;
-      uint4 in[8], out[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) in[j] = r[i * 8 + j];
-      transpose8x8_b16(in, out);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) *reinterpret_cast<uint4*>(lds + (db * 8 + k) * Tile<HD>::TS + rb * 8) = out[k];
-    }
-  }
-};
+__device__ inline bf16x8_t lds_row8(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
 // ---------------------------------------------------------------------------
 // forward
 
 template <int HD>
-__global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out,
-                                                            float* __restrict__ lse, int T, int H) {
-  constexpr int BQ = 128, BKV = 64, KS = Tile<HD>::KS, TS = Tile<HD>::TS, NDB = HD / 32, NKK = HD / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BKV * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][HD * TS];
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H) {
+  constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int nqb = (T + BQ - 1) / BQ;
   const int qb = nqb - 1 - (int)blockIdx.x;  // longest causal rows first
@@ -140,17 +128,16 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(const bf16_t* __rest
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running reference maximum (log2 units) and sum
   const float sl2 = LOG2E / sqrtf((float)HD);
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
 
-  RowStager<HD> ks;
-  TrStager<HD> vs;
+  RowStager<HD> ks, vs;
   ks.load(K, ld, 0, T, tid);
   vs.load(V, ld, 0, T, tid);
   ks.store(Ks[0], tid);
-  vs.store(Vt[0], tid);
+  vs.store(Vs[0], tid);
   __syncthreads();
 
   for (int it = 0; it < nkv; ++it) {
@@ -166,42 +153,46 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(const bf16_t* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(Ks[cur] + (kb2 * 32 + lq) * KS + kk * 16 + hl * 8);
-          s[kb2] = mfma32x32x16_bf16(ka, qf[kk], s[kb2]);
-        }
+        for (int kk = 0; kk < NKK; ++kk)
+          s[kb2] = mfma32x32x16_bf16(lds_row8(Ks[cur] + Tile<HD>::off(kb2 * 32 + lq, kk * 16 + hl * 8)), qf[kk],
+                                     s[kb2]);
+      }
+      if (k0 + BKV - 1 > q0 || k0 + BKV > T) {  // diagonal or ragged tile: mask
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb2 * 32 + acc_row(lane, r);
+            if (key > myq || key >= T) s[kb2][r] = -INFINITY;
+          }
       }
       float bmax = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb2 * 32 + acc_row(lane, r);
-          float v = s[kb2][r] * sl2;
-          if (key > myq || key >= T) v = -INFINITY;
-          s[kb2][r] = v;
-          bmax = fmaxf(bmax, v);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float mnew = fmaxf(m, bmax);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(m - muse);
+        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kb2][r]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64)) * sl2;
+      const bool raise = bmax > m + RESCALE_LOG2;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mnew = raise ? bmax : m;
+        const float alpha = fast_exp2(m - mnew);  // 0 on the first tile (m = -inf)
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        m = mnew;
+      }
       float rs = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[kb2][r] - muse);
+          const float p = fast_exp2(fmaf(s[kb2][r], sl2, -m));
           s[kb2][r] = p;
           rs += p;
         }
-      rs += __shfl_xor(rs, 32, 64);
-      l = l * alpha + rs;
-      m = mnew;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      l += rs + __shfl_xor(rs, 32, 64);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -211,15 +202,13 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(const bf16_t* __rest
           for (int j = 0; j < 8; ++j) pv[j] = s[kb2][8 * s_ + j];
           const bf16x8_t pb = pack8(pv);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8_t va = ld_split8(Vt[cur] + (db * 32 + lq) * TS + kb2 * 32 + 16 * s_ + hl * 4);
-            oacc[db] = mfma32x32x16_bf16(va, pb, oacc[db]);
-          }
+          for (int db = 0; db < NDB; ++db)
+            oacc[db] = mfma32x32x16_bf16(tile_tr_operand<HD>(Vs[cur], kb2 * 32 + 16 * s_, db * 32, lane), pb, oacc[db]);
         }
     }
     if (it + 1 < nkv) {
       ks.store(Ks[cur ^ 1], tid);
-      vs.store(Vt[cur ^ 1], tid);
+      vs.store(Vs[cur ^ 1], tid);
     }
     __syncthreads();
   }
@@ -265,15 +254,15 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const T* __restrict_
   }
 }
 
-// dQ: per 128-query block, over key tiles up to the diagonal
+// dQ: per 128-query block (4 waves x 32 queries, a lane owns a query), over key
+// tiles up to the diagonal.  dQ^T += K^T dS^T with K^T read by transpose.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
-                                                          const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                          bf16_t* __restrict__ dqkv, int T, int H) {
-  constexpr int BQ = 128, BKV = 64, KS = Tile<HD>::KS, TS = Tile<HD>::TS, NDB = HD / 32, NKK = HD / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[BKV * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[BKV * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[HD * TS];
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
+                   const float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H) {
+  constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int nqb = (T + BQ - 1) / BQ;
   const int qb = nqb - 1 - (int)blockIdx.x;
@@ -308,17 +297,19 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const bf16_t* __restri
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
   RowStager<HD> sk, sv;
-  TrStager<HD> st;
+  sk.load(K, ld, 0, T, tid);
+  sv.load(V, ld, 0, T, tid);
+  sk.store(Ks[0], tid);
+  sv.store(Vs[0], tid);
+  __syncthreads();
   for (int it = 0; it < nkv; ++it) {
-    const int k0 = it * BKV;
-    sk.load(K, ld, k0, T, tid);
-    sv.load(V, ld, k0, T, tid);
-    st.load(K, ld, k0, T, tid);
-    sk.store(Ks, tid);
-    sv.store(Vs, tid);
-    st.store(Kt, tid);
-    __syncthreads();
+    const int cur = it & 1, k0 = it * BKV;
+    if (it + 1 < nkv) {
+      sk.load(K, ld, k0 + BKV, T, tid);
+      sv.load(V, ld, k0 + BKV, T, tid);
+    }
     if (k0 <= q0 + 31 && q0 < T) {
+      const bool mask = k0 + BKV - 1 > q0 || k0 + BKV > T;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x16_t s, dp;
@@ -326,27 +317,32 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const bf16_t* __restri
         for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const int o = (kb2 * 32 + lq) * KS + kk * 16 + hl * 8;
-          s = mfma32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(Ks + o), qf[kk], s);
-          dp = mfma32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(Vs + o), gf[kk], dp);
+          const int o = Tile<HD>::off(kb2 * 32 + lq, kk * 16 + hl * 8);
+          s = mfma32x32x16_bf16(lds_row8(Ks[cur] + o), qf[kk], s);
+          dp = mfma32x32x16_bf16(lds_row8(Vs[cur] + o), gf[kk], dp);
+        }
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb2 * 32 + acc_row(lane, r);
+            if (key > myq || key >= T) s[r] = -INFINITY;
+          }
         }
         float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb2 * 32 + acc_row(lane, r);
-          const float p = (key <= myq && key < T && myq < T) ? exp2f(s[r] * sl2 - lse2) : 0.f;
-          ds[r] = p * (dp[r] - Dq);
-        }
+        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(fmaf(s[r], sl2, -lse2)) * (dp[r] - Dq);
 #pragma unroll
         for (int s_ = 0; s_ < 2; ++s_) {
           const bf16x8_t db8 = pack8(ds + 8 * s_);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8_t ka = ld_split8(Kt + (db * 32 + lq) * TS + kb2 * 32 + 16 * s_ + hl * 4);
-            acc[db] = mfma32x32x16_bf16(ka, db8, acc[db]);
-          }
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16_bf16(tile_tr_operand<HD>(Ks[cur], kb2 * 32 + 16 * s_, db * 32, lane), db8, acc[db]);
         }
       }
+    }
+    if (it + 1 < nkv) {
+      sk.store(Ks[cur ^ 1], tid);
+      sv.store(Vs[cur ^ 1], tid);
     }
     __syncthreads();
   }
@@ -365,18 +361,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(const bf16_t* __restri
   }
 }
 
-// dK, dV: per 128-key block (4 waves x 32 keys), over 64-query tiles from the diagonal on
+// dK, dV: per 128-key block (4 waves x 32 keys, a lane owns a key), over 64-query
+// tiles from the diagonal on.  dV += P^T dO and dK += dS^T Q with dO and Q read by
+// transpose from their row-major tiles.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const bf16_t* __restrict__ qkv,
                                                             const bf16_t* __restrict__ dO, const float* __restrict__ lse,
                                                             const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
                                                             int T, int H) {
-  constexpr int BKEY = 128, BQT = 64, KS = Tile<HD>::KS, TS = Tile<HD>::TS, NDB = HD / 32, NKK = HD / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[BQT * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[HD * TS];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[BQT * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Gt[HD * TS];
-  __shared__ float L2s[BQT], Ds[BQT];
+  constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
+  __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int kb = blockIdx.x;  // lowest key blocks carry the most query tiles: launched first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -406,45 +402,62 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const bf16_t* __rest
     for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
 
   const int nqt = (T + BQT - 1) / BQT;
+  const int qt0 = (kb * BKEY) / BQT;
   RowStager<HD> sq, sg;
-  TrStager<HD> tq, tg;
-  for (int qt = (kb * BKEY) / BQT; qt < nqt; ++qt) {
-    const int qb0 = qt * BQT;
-    sq.load(Q, ld, qb0, T, tid);
-    sg.load(G, ldo, qb0, T, tid);
-    tq.load(Q, ld, qb0, T, tid);
-    tg.load(G, ldo, qb0, T, tid);
-    sq.store(Qs, tid);
-    sg.store(Gs, tid);
-    tq.store(Qt, tid);
-    tg.store(Gt, tid);
+  auto stats = [&](int buf, int qb0) {
     if (tid < BQT) {
       const int q = qb0 + tid;
-      L2s[tid] = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
-      Ds[tid] = q < T ? Dv[(long)bh * T + q] : 0.f;
+      L2s[buf][tid] = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
+      Ds[buf][tid] = q < T ? Dv[(long)bh * T + q] : 0.f;
     }
-    __syncthreads();
+  };
+  if (qt0 < nqt) {
+    sq.load(Q, ld, qt0 * BQT, T, tid);
+    sg.load(G, ldo, qt0 * BQT, T, tid);
+    sq.store(Qs[0], tid);
+    sg.store(Gs[0], tid);
+    stats(0, qt0 * BQT);
+  }
+  __syncthreads();
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int cur = (qt - qt0) & 1, qb0 = qt * BQT;
+    if (qt + 1 < nqt) {
+      sq.load(Q, ld, qb0 + BQT, T, tid);
+      sg.load(G, ldo, qb0 + BQT, T, tid);
+    }
     if (qb0 + BQT - 1 >= key0 && key0 < T) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         if (qb0 + qs * 32 + 31 < key0) continue;
+        const bool mask = qb0 + qs * 32 < key0 + 31;
         f32x16_t s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const int o = (qs * 32 + lq) * KS + kk * 16 + hl * 8;
-          s = mfma32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(Qs + o), kf[kk], s);
-          dp = mfma32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(Gs + o), vf[kk], dp);
+          const int o = Tile<HD>::off(qs * 32 + lq, kk * 16 + hl * 8);
+          s = mfma32x32x16_bf16(lds_row8(Qs[cur] + o), kf[kk], s);
+          dp = mfma32x32x16_bf16(lds_row8(Gs[cur] + o), vf[kk], dp);
+        }
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qb0 + qs * 32 + acc_row(lane, r);
+            if (q < mykey) s[r] = -INFINITY;
+          }
         }
         float p[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = qs * 32 + acc_row(lane, r);
-          const int q = qb0 + ql;
-          const bool ok = (q >= mykey && q < T && mykey < T);
-          p[r] = ok ? exp2f(s[r] * sl2 - L2s[ql]) : 0.f;
-          ds[r] = p[r] * (dp[r] - Ds[ql]);
+        for (int g = 0; g < 4; ++g) {  // registers 4g..4g+3 hold query rows qs*32 + 8g + 4hl + 0..3
+          const int ql = qs * 32 + 8 * g + 4 * hl;
+          const float4 l4 = *reinterpret_cast<const float4*>(&L2s[cur][ql]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[4 * g + j] = fast_exp2(fmaf(s[4 * g + j], sl2, -lv[j]));
+            ds[4 * g + j] = p[4 * g + j] * (dp[4 * g + j] - dv4[j]);
+          }
         }
 #pragma unroll
         for (int s_ = 0; s_ < 2; ++s_) {
@@ -452,12 +465,16 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const bf16_t* __rest
           const bf16x8_t da = pack8(ds + 8 * s_);
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int o = (db * 32 + lq) * TS + qs * 32 + 16 * s_ + hl * 4;
-            dv[db] = mfma32x32x16_bf16(pa, ld_split8(Gt + o), dv[db]);
-            dk[db] = mfma32x32x16_bf16(da, ld_split8(Qt + o), dk[db]);
+            dv[db] = mfma32x32x16_bf16(pa, tile_tr_operand<HD>(Gs[cur], qs * 32 + 16 * s_, db * 32, lane), dv[db]);
+            dk[db] = mfma32x32x16_bf16(da, tile_tr_operand<HD>(Qs[cur], qs * 32 + 16 * s_, db * 32, lane), dk[db]);
           }
         }
       }
+    }
+    if (qt + 1 < nqt) {
+      sq.store(Qs[cur ^ 1], tid);
+      sg.store(Gs[cur ^ 1], tid);
+      stats(cur ^ 1, qb0 + BQT);
     }
     __syncthreads();
   }

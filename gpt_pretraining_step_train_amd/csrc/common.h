@@ -22,15 +22,25 @@ __device__ __host__ inline float bf2f(bf16_t v) {
 }
 
 __device__ __host__ inline bf16_t f2bf(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(bf16_t, (__bf16)f);  // v_cvt_pk_bf16_f32: round to nearest even
+#else
   uint32_t u;
   __builtin_memcpy(&u, &f, 4);
   if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (bf16_t)((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (bf16_t)(u >> 16);
+#endif
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> two bfloat16 (lo in the low half), one v_cvt_pk_bf16_f32
 __device__ inline uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -77,6 +87,33 @@ __device__ inline f32x16_t mfma32x32x16_bf16(const bf16x8_t& a, const bf16x8_t& 
 // 32x32 f32 accumulator layout (for lane l, register r):
 //   column = l % 32, row = (r / 4) * 8 + (l / 32) * 4 + (r % 4)
 __device__ inline int acc_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// LDS transpose reads (ds_read_b64_tr_b16).  In each group of 16 lanes, lane i
+// supplies the address of 4 consecutive 16-bit elements M[i][0..3]; it receives
+// M[i/4][i%4], M[i/4+4][i%4], M[i/4+8][i%4], M[i/4+12][i%4].
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ inline i16x4_t lds_read_tr16(const bf16_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lds_ptr);
+}
+
+// MFMA operand whose reduction index runs down the rows of a row-major LDS tile
+// T (row stride ld elements): lane l (hl = l/32) receives column c0 + l%32 at rows
+// r0 + 4hl + {0,1,2,3} (k = 0..3) and r0 + 8 + 4hl + {0,1,2,3} (k = 4..7).  That
+// is the row order in which a 32x32 accumulator holds rows r0..r0+15 of a lane's
+// column (registers 4..7 of a 16-row group follow registers 0..3 at +8 rows).
+__device__ inline bf16x8_t tr_operand(const bf16_t* T, int ld, int r0, int c0, int lane) {
+  const int i = lane & 15;
+  const bf16_t* p = T + (r0 + 4 * (lane >> 5) + (i >> 2)) * ld + c0 + ((lane >> 4) & 1) * 16 + 4 * (i & 3);
+  const i16x4_t a = lds_read_tr16(p);
+  const i16x4_t b = lds_read_tr16(p + 8 * ld);
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
 
 #define HIP_CHECK_RET(x)                                   \
   do {                                                     \
