@@ -75,7 +75,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d24")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dominant", default="gemm_bf16_kernel<256,256,NT>")
+    ap.add_argument("--dominant", default="gemm_bf16_dma_kernel<256,256,NT>")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run three plain device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()

@@ -1,12 +1,17 @@
 // GEMMs of the GPT step on gfx950.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with LDS double buffering.  Both operands
-// are staged in LDS as [rows][k] (k contiguous, rows padded by 16 bytes).  An
-// operand whose reduction index is its slow (row) index in memory is transposed
-// on the way in: each thread loads an 8x8 block (8 k-rows of 16 bytes), swaps it
-// in registers and stores 8 k-contiguous rows.  This serves the forward
-// (X W^T), data-gradient (dY W) and weight-gradient (dY^T X) products and the
-// Newton-Schulz products with one kernel.
+// bf16, large problems (gemm_bf16_dma_kernel): 256x256 tiles, 8 waves, operand
+// tiles copied global -> LDS by the buffer-load DMA path, transposed operands read
+// with the LDS transpose instruction (see the kernel's comment).
+//
+// bf16, small problems (gemm_bf16_kernel, 128x128): v_mfma_f32_32x32x16_bf16 with
+// LDS double buffering.  Both operands are staged in LDS as [rows][k] (k contiguous,
+// rows padded by 16 bytes).  An operand whose reduction index is its slow (row)
+// index in memory is transposed on the way in: each thread loads an 8x8 block
+// (8 k-rows of 16 bytes), swaps it in registers and stores 8 k-contiguous rows.
+//
+// Both serve the forward (X W^T), data-gradient (dY W) and weight-gradient
+// (dY^T X) products and the Newton-Schulz products.
 //
 // fp32 path: a plain LDS-tiled SIMT kernel (the all-fp32 configuration).
 #include "common.h"
@@ -338,6 +343,267 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 GEMM for large problems: 256x256 output tile, 8 waves (two per SIMD) of
+// 128x64, k tiles of BK in S LDS stages that are filled straight from global
+// memory by buffer_load_dwordx4 ... lds (16 bytes per lane, lane l at M0 + 16 l;
+// an offset past the buffer end writes zeros).  The tile for step t + S - 1 is
+// issued when step t starts, so a load has S - 1 steps of MFMA work to land.
+//
+// LDS operand tiles hold 16-byte chunks XOR-swizzled so that every fragment read
+// is bank-conflict free:
+//   K-major operand: [256 rows][BK], chunk c of row r at c ^ kswz(r); fragments
+//     are ds_read_b128 of one chunk of 32 rows.
+//   MN-major operand: [BK k-rows][256], chunk c of k-row r at c ^ 4(r%4);
+//     fragments are two LDS transpose reads (k = 8h..8h+3, then 8h+4..8h+7).
+
+typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x4v_t res_words(const void* base, uint32_t bytes) {
+  u32x4v_t r;
+  r.x = (uint32_t)(uintptr_t)base;
+  r.y = (uint32_t)((uintptr_t)base >> 32) & 0xFFFFu;
+  r.z = bytes;
+  r.w = 0x00020000u;
+  return r;
+}
+
+// written in assembly so that the compiler, which cannot tell the LDS stages
+// apart, does not wait for every outstanding DMA before each LDS read; the
+// pipeline's own waits are the explicit vmcnt waits below.  No VGPR is written.
+__device__ inline void lds_dma16(const u32x4v_t& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// vmcnt(N) lgkmcnt(0), then a workgroup barrier (no memory fence: the DMA
+// stages are ordered by the waits)
+template <int N>
+__device__ inline void dma_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool KMAJ, int BK>
+struct DmaOperand {
+  static constexpr int CPR = KMAJ ? BK / 8 : 32;  // 16-byte chunks per LDS row
+  static constexpr int ROWS = KMAJ ? 256 : BK;
+  static constexpr int CHUNKS = CPR * ROWS;
+  static constexpr int PER = CHUNKS / 512;        // DMA instructions per thread per k tile
+  static constexpr int BYTES = CHUNKS * 16;
+  static_assert(CHUNKS % 512 == 0, "tile must split into whole wave DMAs");
+  __device__ static inline int swz(int r) {
+    if constexpr (KMAJ) return (r / (16 / CPR)) % CPR;
+    else return 4 * (r & 3);
+  }
+};
+
+template <bool AK, bool BKM, bool SPLIT, int BK, int S>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_bf16_dma_kernel(GemmArgs p) {
+  constexpr int WN = 4, TM = 128, TN = 64, FM = TM / 32, FN = TN / 32, NKK = BK / 16;
+  using OA = DmaOperand<AK, BK>;
+  using OB = DmaOperand<BKM, BK>;
+  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int LPT = OA::PER + OB::PER;
+  static_assert((S - 2) * LPT < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int tilesM = (p.M + 255) / 256, tilesN = (p.N + 255) / 256;
+  int tm, tn;
+  tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
+  const int bz = blockIdx.y / p.splits, sk = blockIdx.y % p.splits;
+  const int m0 = tm * 256, n0 = tn * 256;
+  const int kper = ((p.K + p.splits - 1) / p.splits + BK - 1) / BK * BK;
+  const int kbeg = sk * kper;
+  const int kend = min(p.K, kbeg + kper);
+  const int nks = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int nk = nks * (SPLIT ? 3 : 1);
+
+  const bf16_t* Ah = reinterpret_cast<const bf16_t*>(p.A) + bz * p.strideA;
+  const bf16_t* Bh = reinterpret_cast<const bf16_t*>(p.B) + bz * p.strideB;
+  const uint32_t abytes = (uint32_t)((long)(AK ? p.M : p.K) * p.lda * 2);
+  const uint32_t bbytes = (uint32_t)((long)(BKM ? p.N : p.K) * p.ldb * 2);
+  const u32x4v_t rAh = res_words(Ah, abytes), rBh = res_words(Bh, bbytes);
+  const u32x4v_t rAl = SPLIT ? res_words(reinterpret_cast<const bf16_t*>(p.A_lo) + bz * p.strideA, abytes) : rAh;
+  const u32x4v_t rBl = SPLIT ? res_words(reinterpret_cast<const bf16_t*>(p.B_lo) + bz * p.strideB, bbytes) : rBh;
+
+  // per DMA instruction j: the chunk this lane fetches, as (byte offset without the
+  // k-tile origin, row validity, position along k inside the tile)
+  uint32_t aoff[OA::PER], boff[OB::PER];
+  int ak_in[OA::PER], bk_in[OB::PER];
+  bool aok[OA::PER], bok[OB::PER];
+#pragma unroll
+  for (int j = 0; j < OA::PER; ++j) {
+    const int P = (j * 8 + wave) * 64 + lane, row = P / OA::CPR, lc = (P % OA::CPR) ^ OA::swz(row);
+    if constexpr (AK) {
+      aok[j] = m0 + row < p.M; ak_in[j] = lc * 8;
+      aoff[j] = (uint32_t)(((long)(m0 + row) * p.lda + lc * 8) * 2);
+    } else {
+      aok[j] = m0 + lc * 8 < p.M; ak_in[j] = row;
+      aoff[j] = (uint32_t)(((long)row * p.lda + m0 + lc * 8) * 2);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < OB::PER; ++j) {
+    const int P = (j * 8 + wave) * 64 + lane, row = P / OB::CPR, lc = (P % OB::CPR) ^ OB::swz(row);
+    if constexpr (BKM) {
+      bok[j] = n0 + row < p.N; bk_in[j] = lc * 8;
+      boff[j] = (uint32_t)(((long)(n0 + row) * p.ldb + lc * 8) * 2);
+    } else {
+      bok[j] = n0 + lc * 8 < p.N; bk_in[j] = row;
+      boff[j] = (uint32_t)(((long)row * p.ldb + n0 + lc * 8) * 2);
+    }
+  }
+
+  // issue k tile t into stage st (t >= nk: zeros, which keeps the vmcnt arithmetic uniform)
+  auto issue = [&](int t, int st) {
+    const bool live = t < nk;
+    const int sg = live ? t / nks : 0;
+    const int k0 = live ? kbeg + (t % nks) * BK : 0;
+    const u32x4v_t ra = (SPLIT && sg == 2) ? rAl : rAh;
+    const u32x4v_t rb = (SPLIT && sg == 1) ? rBl : rBh;
+    const uint32_t sb = lds0 + st * STAGE;
+#pragma unroll
+    for (int j = 0; j < OA::PER; ++j) {
+      const bool ok = live && aok[j] && k0 + ak_in[j] < kend;
+      const uint32_t o = aoff[j] + (uint32_t)(AK ? k0 * 2 : (long)k0 * p.lda * 2);
+      lds_dma16(ra, sb + (j * 8 + wave) * 1024, ok ? o : OOB);
+    }
+#pragma unroll
+    for (int j = 0; j < OB::PER; ++j) {
+      const bool ok = live && bok[j] && k0 + bk_in[j] < kend;
+      const uint32_t o = boff[j] + (uint32_t)(BKM ? k0 * 2 : (long)k0 * p.ldb * 2);
+      lds_dma16(rb, sb + OA::BYTES + (j * 8 + wave) * 1024, ok ? o : OOB);
+    }
+  };
+
+  // fragment offsets inside a stage (bytes)
+  const int lr = lane & 31, hl = lane >> 5, i16 = lane & 15;
+  int afo[FM][NKK], bfo[FN][NKK];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if constexpr (AK) {
+        const int row = wm * TM + f * 32 + lr;
+        afo[f][kk] = row * (BK * 2) + (((2 * kk + hl) ^ OA::swz(row)) << 4);
+      } else {
+        const int r = kk * 16 + 8 * hl + (i16 >> 2);
+        const int m = wm * TM + f * 32 + ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+        afo[f][kk] = r * 512 + (((m >> 3) ^ OA::swz(r)) << 4) + (m & 7) * 2;
+      }
+    }
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if constexpr (BKM) {
+        const int row = wn * TN + f * 32 + lr;
+        bfo[f][kk] = OA::BYTES + row * (BK * 2) + (((2 * kk + hl) ^ OB::swz(row)) << 4);
+      } else {
+        const int r = kk * 16 + 8 * hl + (i16 >> 2);
+        const int n = wn * TN + f * 32 + ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+        bfo[f][kk] = OA::BYTES + r * 512 + (((n >> 3) ^ OB::swz(r)) << 4) + (n & 7) * 2;
+      }
+    }
+
+  auto frag = [&](const uint8_t* base, int off, bool kmaj) -> bf16x8_t {
+    if (kmaj) return *reinterpret_cast<const bf16x8_t*>(base + off);
+    const i16x4_t lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(base + off));
+    const i16x4_t hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(base + off + 4 * 512));
+    typedef short i16x8_t __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(t, t);
+  for (int t = 0; t < nk; ++t) {
+    dma_sync<(S - 2) * LPT>();  // tile t has landed for every wave; stage (t-1)%S is free
+    issue(t + S - 1, (t + S - 1) % S);
+    const uint8_t* sb = smem + (t % S) * STAGE;
+    bf16x8_t af[2][FM], bf[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = frag(sb, afo[i][0], AK);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[0][j] = frag(sb, bfo[j][0], BKM);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < NKK) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(sb, afo[i][kk + 1], AK);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(sb, bfo[j][kk + 1], BKM);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bf[c][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  dma_sync<0>();  // every DMA (including the zero tail) has landed; LDS is free for staging
+
+  // epilogue: each wave stages one 32-row block of its 128x64 tile in its own LDS
+  // area and writes it back by rows, four adjacent columns per lane
+  constexpr int CS = TN + 4;
+  constexpr int LPR = TN / 4, RPI = 64 / LPR;
+  static_assert(8 * 32 * CS * 4 <= S * STAGE, "staging must fit");
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * CS;
+  const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
+                   (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
+  const int lc = (lane % LPR) * 4, lrow = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r];
+    const int row0 = m0 + wm * TM + i * 32;
+    const int col = n0 + wn * TN + lc;
+    for (int rr = lrow; rr < 32; rr += RPI) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+      if (p.splits > 1) {
+        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
+        if (vec && col + 3 < p.N) {
+          *reinterpret_cast<float4*>(w) = a;
+        } else {
+          const float e[4] = {a.x, a.y, a.z, a.w};
+          for (int t = 0; t < 4; ++t)
+            if (col + t < p.N) w[t] = e[t];
+        }
+      } else if (vec && col + 3 < p.N) {
+        epilogue_vec4(p, bz, row, col, a);
+      } else {
+        const float e[4] = {a.x, a.y, a.z, a.w};
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp8 (e4m3) GEMM, both operands with the reduction index contiguous (the
 // quantisation pass writes transposed copies where a product needs them).
 // 256x256 tile, k-tiles of 128 bytes (same LDS footprint as the bf16 kernel),
@@ -592,6 +858,28 @@ void launch_bf16(const GemmArgs& p, hipStream_t st) {
     launch_bf16_s<BM, BN, WM, WN, false>(p, st);
 }
 
+template <bool SPLIT, int BK, int S>
+void launch_dma_s(const GemmArgs& p, hipStream_t st) {
+  const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  dim3 grid(tiles, p.batch * p.splits), block(512);
+  if (p.a_kmaj && p.b_kmaj)
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, true, SPLIT, BK, S>), grid, block, 0, st, p);
+  else if (p.a_kmaj && !p.b_kmaj)
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, false, SPLIT, BK, S>), grid, block, 0, st, p);
+  else if (!p.a_kmaj && !p.b_kmaj)
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, false, SPLIT, BK, S>), grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, true, SPLIT, BK, S>), grid, block, 0, st, p);
+}
+
+template <int BK, int S>
+void launch_dma(const GemmArgs& p, hipStream_t st) {
+  if (p.split)
+    launch_dma_s<true, BK, S>(p, st);
+  else
+    launch_dma_s<false, BK, S>(p, st);
+}
+
 void launch_f32(const GemmArgs& p, hipStream_t st) {
   const int tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
   dim3 grid(tiles, p.batch * p.splits), block(256);
@@ -606,7 +894,7 @@ void launch_f32(const GemmArgs& p, hipStream_t st) {
 }
 
 int pick_tile(const GemmArgs& p) {
-  if (p.tile) return p.tile == 2 ? 2 : 1;
+  if (p.tile) return p.tile == 2 ? 2 : 1;  // 1, 3, 4: 256x256 variants
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
   return big >= 128 ? 1 : 2;
 }
@@ -633,18 +921,18 @@ int gemm_auto_splits(const GemmArgs& p) {
 }
 
 // one name per kernel instantiation: tile and operand layouts (N = reduction index
-// contiguous, T = transposed on load), as "gemm_bf16_kernel<256,256,NT>"
+// contiguous, T = transposed on load), as "gemm_bf16_dma_kernel<256,256,NT>"
 const char* gemm_kernel_name(const GemmArgs& p) {
   static const char* names[3][4] = {
       {"gemm_f32_kernel<NT>", "gemm_f32_kernel<NN>", "gemm_f32_kernel<TN>", "gemm_f32_kernel<TT>"},
-      {"gemm_bf16_kernel<256,256,NT>", "gemm_bf16_kernel<256,256,NN>", "gemm_bf16_kernel<256,256,TN>",
-       "gemm_bf16_kernel<256,256,TT>"},
+      {"gemm_bf16_dma_kernel<256,256,NT>", "gemm_bf16_dma_kernel<256,256,NN>", "gemm_bf16_dma_kernel<256,256,TN>",
+       "gemm_bf16_dma_kernel<256,256,TT>"},
       {"gemm_bf16_kernel<128,128,NT>", "gemm_bf16_kernel<128,128,NN>", "gemm_bf16_kernel<128,128,TN>",
        "gemm_bf16_kernel<128,128,TT>"}};
   static const char* split_names[3][4] = {
       {"", "", "", ""},
-      {"gemm_bf16x3_kernel<256,256,NT>", "gemm_bf16x3_kernel<256,256,NN>", "gemm_bf16x3_kernel<256,256,TN>",
-       "gemm_bf16x3_kernel<256,256,TT>"},
+      {"gemm_bf16x3_dma_kernel<256,256,NT>", "gemm_bf16x3_dma_kernel<256,256,NN>",
+       "gemm_bf16x3_dma_kernel<256,256,TN>", "gemm_bf16x3_dma_kernel<256,256,TT>"},
       {"gemm_bf16x3_kernel<128,128,NT>", "gemm_bf16x3_kernel<128,128,NN>", "gemm_bf16x3_kernel<128,128,TN>",
        "gemm_bf16x3_kernel<128,128,TT>"}};
   if (p.fp8) return "gemm_fp8_kernel<256,256,NT>";
@@ -682,8 +970,12 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if ((p.a_kmaj && p.lda % 8) || (p.b_kmaj && p.ldb % 8)) return 2;
     if (pick_tile(p) == 2)
       launch_bf16<128, 128, 2, 2>(p, st);
-    else
+    else if (p.tile == 4)
       launch_bf16<256, 256, 2, 2>(p, st);
+    else if (p.tile == 3)
+      launch_dma<64, 2>(p, st);
+    else
+      launch_dma<32, 4>(p, st);
   } else {
     launch_f32(p, st);
   }

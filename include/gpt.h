@@ -181,7 +181,7 @@ int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t
                   const float* dq_b, float* C, long ldc, void* stream);
 
 /* name of the GEMM kernel instantiation gptk_gemm / gpt_step launch for these
- * layouts and sizes, e.g. "gemm_bf16_kernel<256,256,NT>" (NT: both operands have
+ * layouts and sizes, e.g. "gemm_bf16_dma_kernel<256,256,NT>" (NT: both operands have
  * the reduction index contiguous; NN: B transposed on load; TN: both) */
 const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch);
 

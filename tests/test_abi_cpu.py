@@ -103,8 +103,8 @@ def test_state_bytes_and_tensor_table(lib):
 
 
 def test_kernel_names(lib):
-    assert binding.gemm_kernel_name(1, 32768, 6144, 1536) == "gemm_bf16_kernel<256,256,NT>"
-    assert binding.gemm_kernel_name(1, 32768, 1536, 6144, b_kmaj=0) == "gemm_bf16_kernel<256,256,NN>"
+    assert binding.gemm_kernel_name(1, 32768, 6144, 1536) == "gemm_bf16_dma_kernel<256,256,NT>"
+    assert binding.gemm_kernel_name(1, 32768, 1536, 6144, b_kmaj=0) == "gemm_bf16_dma_kernel<256,256,NN>"
     assert binding.gemm_kernel_name(1, 512, 384, 128, a_kmaj=0, b_kmaj=0) == "gemm_bf16_kernel<128,128,TN>"
     assert binding.gemm_kernel_name(0, 512, 384, 128) == "gemm_f32_kernel<NT>"
 

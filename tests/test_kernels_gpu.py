@@ -41,6 +41,18 @@ GEMM_CASES = [
     ("bf16", 0, 1, 136, 300, 72, 1, 2, 1),
     ("bf16", 1, 1, 256, 384, 128, 3, 2, 1),
     ("bf16", 0, 0, 136, 200, 1032, 1, 2, 3),
+    # 256x256 direct-to-LDS kernel (tile 1: k tiles of 32 in 4 stages, tile 3: 64 in 2)
+    # and the register-staged 256x256 kernel (tile 4)
+    ("bf16", 1, 1, 520, 264, 200, 1, 3, 1),
+    ("bf16", 1, 0, 512, 520, 256, 1, 3, 1),
+    ("bf16", 0, 0, 264, 528, 520, 1, 3, 1),
+    ("bf16", 0, 1, 264, 300, 72, 1, 1, 1),
+    ("bf16", 0, 1, 264, 300, 72, 1, 3, 1),
+    ("bf16", 1, 1, 256, 384, 128, 3, 1, 1),
+    ("bf16", 0, 0, 136, 200, 1032, 1, 1, 3),
+    ("bf16", 1, 0, 1000, 776, 1000, 1, 1, 1),
+    ("bf16", 1, 1, 520, 264, 200, 1, 4, 1),
+    ("bf16", 0, 0, 264, 528, 520, 1, 4, 1),
     ("fp32", 1, 1, 100, 70, 33, 1, 0, 1),
     ("fp32", 1, 0, 96, 72, 40, 2, 0, 1),
     ("fp32", 0, 0, 72, 96, 200, 1, 0, 2),
@@ -71,7 +83,9 @@ def test_gemm_layouts_tails_batch_split(case):
     assert err < (1e-5 if dtype == "bf16" else 1e-5), err
 
 
-SPLIT_CASES = [(1, 1, 300, 200, 136, 1), (1, 0, 296, 264, 264, 2), (0, 0, 136, 200, 1032, 1), (0, 1, 128, 72, 72, 1)]
+SPLIT_CASES = [(1, 1, 300, 200, 136, 1), (1, 0, 296, 264, 264, 2), (0, 0, 136, 200, 1032, 1), (0, 1, 128, 72, 72, 1),
+               # batches large enough for the 256x256 kernel
+               (1, 1, 520, 264, 200, 64), (1, 0, 264, 520, 136, 64), (0, 0, 264, 264, 264, 128)]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES)
