@@ -219,6 +219,107 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(T* __restrict__ dq
   }
 }
 
+// bf16 versions with 16-byte accesses: a group of HD/16 lanes owns one head vector;
+// lane j holds elements 8j..8j+7 of the first half and their pair partners
+// HD/2+8j..HD/2+8j+7, and the group reduces the squared norm with shuffles.
+
+__device__ inline void unpack8(const uint4 u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf2f((bf16_t)(w[i] & 0xffffu));
+    f[2 * i + 1] = bf2f((bf16_t)(w[i] >> 16));
+  }
+}
+__device__ inline uint4 pack8f(const float (&f)[8]) {
+  return make_uint4(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]), pack_bf2(f[6], f[7]));
+}
+
+template <int HD>
+__device__ inline float group_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < HD / 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) rope_qknorm_fwd_vec_kernel(bf16_t* __restrict__ qkv, const float* __restrict__ cs,
+                                                                  float* __restrict__ rq, float* __restrict__ rk, int N,
+                                                                  int Tlen, int H, float eps) {
+  constexpr int G = HD / 16, HALF = HD / 2;
+  const long gid = ((long)blockIdx.x * 256 + threadIdx.x) / G;  // (token, q|k, head), heads fastest
+  const int j = threadIdx.x % G;
+  if (gid >= (long)N * 2 * H) return;  // whole groups leave together (G divides 64)
+  const int n = (int)(gid / (2 * H)), rem = (int)(gid % (2 * H)), which = rem / H, h = rem % H;
+  bf16_t* p = qkv + (long)n * 3 * H * HD + which * H * HD + h * HD;
+  float x1[8], x2[8];
+  unpack8(*reinterpret_cast<const uint4*>(p + 8 * j), x1);
+  unpack8(*reinterpret_cast<const uint4*>(p + HALF + 8 * j), x2);
+  const float4* c4 = reinterpret_cast<const float4*>(cs + 2 * ((long)(n % Tlen) * HALF + 8 * j));
+  float y1[8], y2[8], ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 cc = c4[q];  // (cos, sin) of pairs 2q and 2q+1
+    const float c[2] = {cc.x, cc.z}, sn[2] = {cc.y, cc.w};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * q + e;
+      y1[i] = x1[i] * c[e] - x2[i] * sn[e];
+      y2[i] = x1[i] * sn[e] + x2[i] * c[e];
+      ss += y1[i] * y1[i] + y2[i] * y2[i];
+    }
+  }
+  ss = group_sum<HD>(ss);
+  const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { y1[i] *= r; y2[i] *= r; }
+  *reinterpret_cast<uint4*>(p + 8 * j) = pack8f(y1);
+  *reinterpret_cast<uint4*>(p + HALF + 8 * j) = pack8f(y2);
+  if (j == 0) (which ? rk : rq)[(long)n * H + h] = r;
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) rope_qknorm_bwd_vec_kernel(bf16_t* __restrict__ dqkv,
+                                                                  const bf16_t* __restrict__ qkv,
+                                                                  const float* __restrict__ cs,
+                                                                  const float* __restrict__ rq,
+                                                                  const float* __restrict__ rk, int N, int Tlen, int H) {
+  constexpr int G = HD / 16, HALF = HD / 2;
+  const long gid = ((long)blockIdx.x * 256 + threadIdx.x) / G;
+  const int j = threadIdx.x % G;
+  if (gid >= (long)N * 2 * H) return;
+  const int n = (int)(gid / (2 * H)), rem = (int)(gid % (2 * H)), which = rem / H, h = rem % H;
+  const long off = (long)n * 3 * H * HD + which * H * HD + h * HD;
+  bf16_t* dp = dqkv + off;
+  const bf16_t* yp = qkv + off;
+  float g1[8], g2[8], a1[8], a2[8];
+  unpack8(*reinterpret_cast<const uint4*>(dp + 8 * j), g1);
+  unpack8(*reinterpret_cast<const uint4*>(dp + HALF + 8 * j), g2);
+  unpack8(*reinterpret_cast<const uint4*>(yp + 8 * j), a1);
+  unpack8(*reinterpret_cast<const uint4*>(yp + HALF + 8 * j), a2);
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dot += g1[i] * a1[i] + g2[i] * a2[i];
+  dot = group_sum<HD>(dot) / (float)HD;
+  const float r = (which ? rk : rq)[(long)n * H + h];
+  const float4* c4 = reinterpret_cast<const float4*>(cs + 2 * ((long)(n % Tlen) * HALF + 8 * j));
+  float o1[8], o2[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 cc = c4[q];
+    const float c[2] = {cc.x, cc.z}, sn[2] = {cc.y, cc.w};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * q + e;
+      const float z1 = r * (g1[i] - a1[i] * dot), z2 = r * (g2[i] - a2[i] * dot);
+      o1[i] = z1 * c[e] + z2 * sn[e];
+      o2[i] = -z1 * sn[e] + z2 * c[e];
+    }
+  }
+  *reinterpret_cast<uint4*>(dp + 8 * j) = pack8f(o1);
+  *reinterpret_cast<uint4*>(dp + HALF + 8 * j) = pack8f(o2);
+}
+
 // ---------------------------------------------------------------------------
 // fused softmax cross-entropy over a vocabulary row held in registers.
 // row_loss[n] = lse - z[y]; dz = (softmax - onehot) * inv_n; argmax (lowest index)
@@ -709,9 +810,31 @@ void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st) {
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, cs, T, hd, base);
 }
 
+template <int HD>
+static void rope_fwd_vec(bf16_t* qkv, const float* cs, float* rq, float* rk, int N, int T, int H, float eps,
+                         hipStream_t st) {
+  const long threads = (long)N * 2 * H * (HD / 16);
+  hipLaunchKernelGGL(rope_qknorm_fwd_vec_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, qkv, cs,
+                     rq, rk, N, T, H, eps);
+}
+
+template <int HD>
+static void rope_bwd_vec(bf16_t* dqkv, const bf16_t* qkv, const float* cs, const float* rq, const float* rk, int N,
+                         int T, int H, hipStream_t st) {
+  const long threads = (long)N * 2 * H * (HD / 16);
+  hipLaunchKernelGGL(rope_qknorm_bwd_vec_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dqkv,
+                     qkv, cs, rq, rk, N, T, H);
+}
+
 void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float* rk, int B, int T, int H, int hd,
                             float eps, hipStream_t st) {
   const int N = B * T;
+  if (at == ACT_BF16 && (hd == 128 || hd == 64 || hd == 32)) {
+    if (hd == 128) rope_fwd_vec<128>((bf16_t*)qkv, cs, rq, rk, N, T, H, eps, st);
+    else if (hd == 64) rope_fwd_vec<64>((bf16_t*)qkv, cs, rq, rk, N, T, H, eps, st);
+    else rope_fwd_vec<32>((bf16_t*)qkv, cs, rq, rk, N, T, H, eps, st);
+    return;
+  }
   dim3 g((N * H * 2 + 3) / 4), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)qkv, cs, rq, rk, N, T, H, hd, eps);
@@ -722,6 +845,12 @@ void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float
 void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs, const float* rq, const float* rk,
                             int B, int T, int H, int hd, hipStream_t st) {
   const int N = B * T;
+  if (at == ACT_BF16 && (hd == 128 || hd == 64 || hd == 32)) {
+    if (hd == 128) rope_bwd_vec<128>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, st);
+    else if (hd == 64) rope_bwd_vec<64>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, st);
+    else rope_bwd_vec<32>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, st);
+    return;
+  }
   dim3 g((N * H * 2 + 3) / 4), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(rope_qknorm_bwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N,

@@ -893,31 +893,33 @@ void launch_f32(const GemmArgs& p, hipStream_t st) {
     hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, block, 0, st, p);
 }
 
+// split-K factor for a tm x tn tiling: aim for >= 512 workgroups while every split
+// keeps >= 1024 of K
+int splits_for(const GemmArgs& p, int tm, int tn) {
+  if (p.epi != EPI_LINEAR) return 1;
+  const long tiles = (long)((p.M + tm - 1) / tm) * ((p.N + tn - 1) / tn) * p.batch;
+  int s = 1;
+  while (tiles * s < 512 && (long)p.K / (s * 2) >= 1024 && s < 32) s *= 2;
+  return s;
+}
+
+// 1: a 256x256 kernel, 2: the 128x128 kernel.  The 256 tile is used when the
+// problem has >= 128 such tiles, or when split-K over them reaches >= 256
+// workgroups (the long-reduction weight gradients); a pure function of the shape,
+// so the split factor and the kernel always agree.
 int pick_tile(const GemmArgs& p) {
   if (p.tile) return p.tile == 2 ? 2 : 1;  // 1, 3, 4: 256x256 variants
   const long big = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-  return big >= 128 ? 1 : 2;
+  if (big >= 128) return 1;
+  return big * splits_for(p, 256, 256) >= 256 ? 1 : 2;
 }
 
 }  // namespace
 
 int gemm_auto_splits(const GemmArgs& p) {
-  if (p.epi != EPI_LINEAR) return 1;
-  int tm, tn;
-  if (p.dtype == ACT_F32) {
-    tm = 64; tn = 64;
-  } else if (p.fp8 || pick_tile(p) != 2) {
-    tm = 256; tn = 256;
-  } else {
-    tm = 128; tn = 128;
-  }
-  const long tiles = (long)((p.M + tm - 1) / tm) * ((p.N + tn - 1) / tn) * p.batch;
-  const int kstep = p.dtype == ACT_F32 ? 16 : BK;
-  int s = 1;
-  // aim for >= 512 workgroups while every split keeps >= 1024 of K
-  while (tiles * s < 512 && (long)p.K / (s * 2) >= 1024 && s < 32) s *= 2;
-  (void)kstep;
-  return s;
+  if (p.dtype == ACT_F32) return splits_for(p, 64, 64);
+  if (p.fp8 || pick_tile(p) != 2) return splits_for(p, 256, 256);
+  return splits_for(p, 128, 128);
 }
 
 // one name per kernel instantiation: tile and operand layouts (N = reduction index

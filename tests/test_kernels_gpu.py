@@ -243,7 +243,8 @@ def test_rmsnorm_fwd_bwd(dtype, N, d):
 
 
 @pytest.mark.parametrize("dtype,Bn,T,H,hd", [("bf16", 2, 100, 3, 128), ("bf16", 1, 64, 2, 64),
-                                             ("fp32", 2, 40, 4, 32), ("bf16", 1, 2048, 1, 128)])
+                                             ("fp32", 2, 40, 4, 32), ("bf16", 1, 2048, 1, 128),
+                                             ("bf16", 3, 37, 5, 32), ("bf16", 1, 33, 7, 64)])
 def test_rope_qknorm_fwd_bwd(dtype, Bn, T, H, hd):
     rng = np.random.default_rng(T)
     d = H * hd
