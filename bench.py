@@ -23,6 +23,8 @@ METRIC = "training tokens/sec + MFU on 1 MI355X, d12 and d24 GPT at seq 2048"
 PEAK_BF16 = 2.5166e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12          # bytes/s
 LR = 0.02
+# rocprofv3 traffic summaries (FETCH_SIZE + WRITE_SIZE, copy-calibrated) per dominant kernel
+TRAFFIC = {"gemm_bf16_dma_kernel<256,256,NT>": "gemm_bf16_dma_kernel_NT__d24_step_traffic.md"}
 
 
 def cpu_baseline(cfg: dict) -> dict:
@@ -85,7 +87,7 @@ def main() -> int:
         x = torch.ones(args.copy_probe * 2 ** 20 // 4, device="cuda")
         y = torch.empty_like(x)
         for _ in range(3):
-            y.copy_(x)
+            torch.mul(x, 1.0, out=y)  # one elementwise kernel: reads and writes the bytes once
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4, "copies": 3}), flush=True)
         return 0
@@ -138,10 +140,17 @@ def main() -> int:
     fl = configs.step_flops(cfg)
     mfu = fl["total"] / (ms_step / 1e3) / PEAK_BF16
     achieved = k_flops / (k_ms / 1e3) if k_ms > 0 else None
+    from gpt_pretraining_step_train_amd import profiling
+    rec = None
+    if args.dominant in TRAFFIC and args.config == "d24":
+        rec = profiling.read_traffic(os.path.join(ROOT, "profiles", TRAFFIC[args.dominant]))
     roof = {
         "kernel": args.dominant, "bound": "mfma", "achieved": achieved / 1e12 if achieved else None,
         "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-        "frac": (achieved / PEAK_BF16) if achieved else None, "traffic": None,
+        "frac": (achieved / PEAK_BF16) if achieved else None,
+        "traffic": rec["bytes_per_launch"] if rec else None,
+        "traffic_detail": ({"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
+                            "source": "profiles/" + TRAFFIC[args.dominant]} if rec else None),
         "launches": n_launch, "avg_launch_us": 1e3 * k_ms / n_launch if n_launch else None,
         "share_of_step_time": (k_ms / gpu_ms) if gpu_ms > 0 else None,
     }
