@@ -169,21 +169,21 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
       if (p.outA_lo) {
         float h[4], l[4];
         ld4_act(q, h);
-        for (int t = 0; t < 4; ++t) l[t] = v[t] - h[t];
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) l[t] = v[t] - h[t];
         st4_act(reinterpret_cast<bf16_t*>(p.outA_lo) + o, l);
       }
     }
   } else if (p.epi == EPI_RELU2) {
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     float g[4];
-    for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
     st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
     st4_act(reinterpret_cast<bf16_t*>(p.out2) + o, g);
   } else {  // EPI_DRELU2
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     float u[4];
     ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + o, u);
-    for (int t = 0; t < 4; ++t) v[t] *= 2.f * fmaxf(u[t], 0.f);
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * fmaxf(u[t], 0.f);
     st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
   }
 }
@@ -388,14 +388,14 @@ __device__ inline void dma_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool KMAJ, int BK>
+template <bool KMAJ, int BK, int NTH = 512>
 struct DmaOperand {
   static constexpr int CPR = KMAJ ? BK / 8 : 32;  // 16-byte chunks per LDS row
   static constexpr int ROWS = KMAJ ? 256 : BK;
   static constexpr int CHUNKS = CPR * ROWS;
-  static constexpr int PER = CHUNKS / 512;        // DMA instructions per thread per k tile
+  static constexpr int PER = CHUNKS / NTH;        // DMA instructions per thread per k tile
   static constexpr int BYTES = CHUNKS * 16;
-  static_assert(CHUNKS % 512 == 0, "tile must split into whole wave DMAs");
+  static_assert(CHUNKS % NTH == 0, "tile must split into whole wave DMAs");
   __device__ static inline int swz(int r) {
     if constexpr (KMAJ) return (r / (16 / CPR)) % CPR;
     else return 4 * (r & 3);
@@ -408,10 +408,12 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   constexpr int WN = 4, TM = 128, TN = 64, FM = TM / 32, FN = TN / 32, NKK = BK / 16;
   using OA = DmaOperand<AK, BK>;
   using OB = DmaOperand<BKM, BK>;
-  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int ABASE = 0, BBASE = S * OA::BYTES;  // all A stages, then all B stages
   constexpr int LPT = OA::PER + OB::PER;
-  static_assert((S - 2) * LPT < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  static_assert(S >= 3 && (S - 2) * LPT < 64, "pipeline depth / vmcnt range");
+  static_assert(NKK % 2 == 0, "slice 0 of every k tile uses fragment buffer 0");
+  static_assert((S - 1) * OA::BYTES < 65536 && (S - 1) * OB::BYTES < 65536, "stage offsets must be immediates");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * (OA::BYTES + OB::BYTES)];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -427,6 +429,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   const int kend = min(p.K, kbeg + kper);
   const int nks = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int nk = nks * (SPLIT ? 3 : 1);
+  const int nkp = (nk + S - 1) / S * S;  // padded with all-zero tiles to whole unrolled rounds
 
   const bf16_t* Ah = reinterpret_cast<const bf16_t*>(p.A) + bz * p.strideA;
   const bf16_t* Bh = reinterpret_cast<const bf16_t*>(p.B) + bz * p.strideB;
@@ -464,29 +467,32 @@ gemm_bf16_dma_kernel(GemmArgs p) {
     }
   }
 
-  // issue k tile t into stage st (t >= nk: zeros, which keeps the vmcnt arithmetic uniform)
-  auto issue = [&](int t, int st) {
-    const bool live = t < nk;
-    const int sg = live ? t / nks : 0;
-    const int k0 = live ? kbeg + (t % nks) * BK : 0;
-    const u32x4v_t ra = (SPLIT && sg == 2) ? rAl : rAh;
-    const u32x4v_t rb = (SPLIT && sg == 1) ? rBl : rBh;
-    const uint32_t sb = lds0 + st * STAGE;
+  // the next k tile to issue: its index, segment (split planes) and k origin,
+  // advanced incrementally (no division in the loop)
+  int it_t = 0, it_sg = 0, it_k0 = kbeg;
+  auto issue = [&](int st) {
+    const bool live = it_t < nk;
+    const u32x4v_t ra = (SPLIT && it_sg == 2) ? rAl : rAh;
+    const u32x4v_t rb = (SPLIT && it_sg == 1) ? rBl : rBh;
+    const bool full = it_k0 + BK <= kend;  // no k tail inside this tile
+    const uint32_t ka = (uint32_t)(AK ? it_k0 * 2 : (long)it_k0 * p.lda * 2);
+    const uint32_t kb = (uint32_t)(BKM ? it_k0 * 2 : (long)it_k0 * p.ldb * 2);
 #pragma unroll
     for (int j = 0; j < OA::PER; ++j) {
-      const bool ok = live && aok[j] && k0 + ak_in[j] < kend;
-      const uint32_t o = aoff[j] + (uint32_t)(AK ? k0 * 2 : (long)k0 * p.lda * 2);
-      lds_dma16(ra, sb + (j * 8 + wave) * 1024, ok ? o : OOB);
+      const bool ok = live && aok[j] && (full || it_k0 + ak_in[j] < kend);
+      lds_dma16(ra, lds0 + ABASE + st * OA::BYTES + (j * 8 + wave) * 1024, ok ? aoff[j] + ka : OOB);
     }
 #pragma unroll
     for (int j = 0; j < OB::PER; ++j) {
-      const bool ok = live && bok[j] && k0 + bk_in[j] < kend;
-      const uint32_t o = boff[j] + (uint32_t)(BKM ? k0 * 2 : (long)k0 * p.ldb * 2);
-      lds_dma16(rb, sb + OA::BYTES + (j * 8 + wave) * 1024, ok ? o : OOB);
+      const bool ok = live && bok[j] && (full || it_k0 + bk_in[j] < kend);
+      lds_dma16(rb, lds0 + BBASE + st * OB::BYTES + (j * 8 + wave) * 1024, ok ? boff[j] + kb : OOB);
     }
+    ++it_t;
+    it_k0 += BK;
+    if (it_k0 >= kbeg + nks * BK) { it_k0 = kbeg; ++it_sg; }
   };
 
-  // fragment offsets inside a stage (bytes)
+  // fragment offsets inside stage 0 of each operand region (bytes)
   const int lr = lane & 31, hl = lane >> 5, i16 = lane & 15;
   int afo[FM][NKK], bfo[FN][NKK];
 #pragma unroll
@@ -495,11 +501,11 @@ gemm_bf16_dma_kernel(GemmArgs p) {
     for (int kk = 0; kk < NKK; ++kk) {
       if constexpr (AK) {
         const int row = wm * TM + f * 32 + lr;
-        afo[f][kk] = row * (BK * 2) + (((2 * kk + hl) ^ OA::swz(row)) << 4);
+        afo[f][kk] = ABASE + row * (BK * 2) + (((2 * kk + hl) ^ OA::swz(row)) << 4);
       } else {
         const int r = kk * 16 + 8 * hl + (i16 >> 2);
         const int m = wm * TM + f * 32 + ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
-        afo[f][kk] = r * 512 + (((m >> 3) ^ OA::swz(r)) << 4) + (m & 7) * 2;
+        afo[f][kk] = ABASE + r * 512 + (((m >> 3) ^ OA::swz(r)) << 4) + (m & 7) * 2;
       }
     }
 #pragma unroll
@@ -508,18 +514,20 @@ gemm_bf16_dma_kernel(GemmArgs p) {
     for (int kk = 0; kk < NKK; ++kk) {
       if constexpr (BKM) {
         const int row = wn * TN + f * 32 + lr;
-        bfo[f][kk] = OA::BYTES + row * (BK * 2) + (((2 * kk + hl) ^ OB::swz(row)) << 4);
+        bfo[f][kk] = BBASE + row * (BK * 2) + (((2 * kk + hl) ^ OB::swz(row)) << 4);
       } else {
         const int r = kk * 16 + 8 * hl + (i16 >> 2);
         const int n = wn * TN + f * 32 + ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
-        bfo[f][kk] = OA::BYTES + r * 512 + (((n >> 3) ^ OB::swz(r)) << 4) + (n & 7) * 2;
+        bfo[f][kk] = BBASE + r * 512 + (((n >> 3) ^ OB::swz(r)) << 4) + (n & 7) * 2;
       }
     }
 
-  auto frag = [&](const uint8_t* base, int off, bool kmaj) -> bf16x8_t {
-    if (kmaj) return *reinterpret_cast<const bf16x8_t*>(base + off);
-    const i16x4_t lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(base + off));
-    const i16x4_t hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(base + off + 4 * 512));
+  // fragment at byte offset off of stage st (st, and so the stage term, compile-time)
+  auto frag = [&](int off, int stage_bytes, int st, bool kmaj) -> bf16x8_t {
+    const uint8_t* base = smem + off + st * stage_bytes;
+    if (kmaj) return *reinterpret_cast<const bf16x8_t*>(base);
+    const i16x4_t lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(base));
+    const i16x4_t hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(base + 4 * 512));
     typedef short i16x8_t __attribute__((ext_vector_type(8)));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
@@ -532,41 +540,57 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  bf16x8_t af[2][FM], bf[2][FN];
+  // prologue: tiles 0..S-2 in flight; wait for tile 0 and fetch its first fragments
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t, t);
-  for (int t = 0; t < nk; ++t) {
-    dma_sync<(S - 2) * LPT>();  // tile t has landed for every wave; stage (t-1)%S is free
-    issue(t + S - 1, (t + S - 1) % S);
-    const uint8_t* sb = smem + (t % S) * STAGE;
-    bf16x8_t af[2][FM], bf[2][FN];
+  for (int st = 0; st < S - 1; ++st) issue(st);
+  dma_sync<(S - 2) * LPT>();
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[0][i] = frag(sb, afo[i][0], AK);
+  for (int i = 0; i < FM; ++i) af[0][i] = frag(afo[i][0], OA::BYTES, 0, AK);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bf[0][j] = frag(sb, bfo[j][0], BKM);
+  for (int j = 0; j < FN; ++j) bf[0][j] = frag(bfo[j][0], OB::BYTES, 0, BKM);
+
+  // k step t uses stage t % S.  Within it, the fragments of k slice kk+1 load under
+  // the MFMAs of slice kk; before the last slice the block syncs (tile t+1 has
+  // landed, every wave is past tile t-1), issues tile t+S-1 into the stage tile t-1
+  // used, and loads the first fragments of tile t+1 under the last slice's MFMAs.
+  for (int t0 = 0; t0 < nkp; t0 += S) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int c = kk & 1;
-      if (kk + 1 < NKK) {
+    for (int u = 0; u < S; ++u) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(sb, afo[i][kk + 1], AK);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int c = kk & 1;  // NKK even: slice 0 of every tile sits in buffer 0
+        if (kk + 1 < NKK) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(sb, bfo[j][kk + 1], BKM);
+          for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(afo[i][kk + 1], OA::BYTES, u, AK);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(bfo[j][kk + 1], OB::BYTES, u, BKM);
+        } else {
+          dma_sync<(S - 3) * LPT>();
+          issue((u + S - 1) % S);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(afo[i][0], OA::BYTES, (u + 1) % S, AK);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(bfo[j][0], OB::BYTES, (u + 1) % S, BKM);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bf[c][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bf[c][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  dma_sync<0>();  // every DMA (including the zero tail) has landed; LDS is free for staging
+  // every DMA, including the zero tail, must land before the workgroup's LDS is released
+  dma_sync<0>();
 
   // epilogue: each wave stages one 32-row block of its 128x64 tile in its own LDS
-  // area and writes it back by rows, four adjacent columns per lane
+  // area (constant register indices) and writes it back by rows, four adjacent
+  // columns per lane, sixteen lanes per row
   constexpr int CS = TN + 4;
   constexpr int LPR = TN / 4, RPI = 64 / LPR;
-  static_assert(8 * 32 * CS * 4 <= S * STAGE, "staging must fit");
+  static_assert(8 * 32 * CS * 4 <= S * (OA::BYTES + OB::BYTES), "staging must fit");
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * CS;
   const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
                    (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
@@ -975,7 +999,7 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     else if (p.tile == 4)
       launch_bf16<256, 256, 2, 2>(p, st);
     else if (p.tile == 3)
-      launch_dma<64, 2>(p, st);
+      launch_dma<32, 3>(p, st);
     else
       launch_dma<32, 4>(p, st);
   } else {
