@@ -420,8 +420,16 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int tilesM = (p.M + 255) / 256, tilesN = (p.N + 255) / 256;
+  const bool sym = p.sym && p.splits == 1 && p.M == p.N;
   int tm, tn;
-  tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
+  if (sym) {  // upper-triangular tiles, row by row
+    int id = blockIdx.x;
+    tm = 0;
+    while (id >= tilesM - tm) { id -= tilesM - tm; ++tm; }
+    tn = tm + id;
+  } else {
+    tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
+  }
   const int bz = blockIdx.y / p.splits, sk = blockIdx.y % p.splits;
   const int m0 = tm * 256, n0 = tn * 256;
   const int kper = ((p.K + p.splits - 1) / p.splits + BK - 1) / BK * BK;
@@ -595,37 +603,67 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
                    (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
   const int lc = (lane % LPR) * 4, lrow = lane / LPR;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r];
-    const int row0 = m0 + wm * TM + i * 32;
-    const int col = n0 + wn * TN + lc;
-    for (int rr = lrow; rr < 32; rr += RPI) {
-      const int row = row0 + rr;
-      if (row >= p.M) break;
-      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
-      if (p.splits > 1) {
-        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
-        if (vec && col + 3 < p.N) {
-          *reinterpret_cast<float4*>(w) = a;
-        } else {
-          const float e[4] = {a.x, a.y, a.z, a.w};
-          for (int t = 0; t < 4; ++t)
-            if (col + t < p.N) w[t] = e[t];
-        }
-      } else if (vec && col + 3 < p.N) {
-        epilogue_vec4(p, bz, row, col, a);
-      } else {
-        const float e[4] = {a.x, a.y, a.z, a.w};
-        for (int t = 0; t < 4; ++t)
-          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);
-      }
-    }
-  }
+  // one 32-row block of the wave tile per expansion (a literal block index keeps every
+  // accumulator access static)
+#define GEMM_EPI_BLOCK(I_)                                                                     \
+  do { \
+_Pragma("unroll") \
+    for (int j = 0; j < FN; ++j) \
+_Pragma("unroll") \
+      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[I_][j][r]; \
+    const int row0 = m0 + wm * TM + I_ * 32; \
+    const int col = n0 + wn * TN + lc; \
+    for (int rr = lrow; rr < 32; rr += RPI) { \
+      const int row = row0 + rr; \
+      if (row >= p.M) break; \
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc); \
+      if (p.splits > 1) { \
+        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col; \
+        if (vec && col + 3 < p.N) { \
+          *reinterpret_cast<float4*>(w) = a; \
+        } else { \
+          const float e[4] = {a.x, a.y, a.z, a.w}; \
+          for (int t = 0; t < 4; ++t) \
+            if (col + t < p.N) w[t] = e[t]; \
+        } \
+      } else if (vec && col + 3 < p.N) { \
+        epilogue_vec4(p, bz, row, col, a); \
+      } else { \
+        const float e[4] = {a.x, a.y, a.z, a.w}; \
+        for (int t = 0; t < 4; ++t) \
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]); \
+      } \
+    } \
+    if (sym && tm != tn) { \
+      /* mirror: element (row0 + r, n) also lands at (n, row0 + r); read the staged block */ \
+      /* by columns so each mirrored row gets 4-wide stores (8 lanes per 32-wide row) */ \
+      const int r4 = (lane & 7) * 4; \
+_Pragma("unroll") \
+      for (int q = 0; q < TN / 8; ++q) { \
+        const int cc = q * 8 + (lane >> 3); \
+        const int n = n0 + wn * TN + cc, m = row0 + r4; \
+        if (n >= p.M || m >= p.M) continue; \
+        const float4 a = make_float4(stage[(r4 + 0) * CS + cc], stage[(r4 + 1) * CS + cc], stage[(r4 + 2) * CS + cc], \
+                                     stage[(r4 + 3) * CS + cc]); \
+        if (vec && m + 3 < p.M) { \
+          epilogue_vec4(p, bz, n, m, a); \
+        } else { \
+          const float e[4] = {a.x, a.y, a.z, a.w}; \
+          for (int t = 0; t < 4; ++t) \
+            if (m + t < p.M) epilogue_elem<bf16_t>(p, bz, n, m + t, e[t]); \
+        } \
+      } \
+    } \
+   \
+  } while (0)
+  GEMM_EPI_BLOCK(0);
+  GEMM_EPI_BLOCK(1);
+  GEMM_EPI_BLOCK(2);
+  GEMM_EPI_BLOCK(3);
+  static_assert(FM == 4, "one expansion per 32-row block");
+#undef GEMM_EPI_BLOCK
 }
+
 
 // ---------------------------------------------------------------------------
 // fp8 (e4m3) GEMM, both operands with the reduction index contiguous (the
@@ -884,7 +922,8 @@ void launch_bf16(const GemmArgs& p, hipStream_t st) {
 
 template <bool SPLIT, int BK, int S>
 void launch_dma_s(const GemmArgs& p, hipStream_t st) {
-  const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const int tM = (p.M + 255) / 256;
+  const int tiles = (p.sym && p.splits == 1 && p.M == p.N) ? tM * (tM + 1) / 2 : tM * ((p.N + 255) / 256);
   dim3 grid(tiles, p.batch * p.splits), block(512);
   if (p.a_kmaj && p.b_kmaj)
     hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, true, SPLIT, BK, S>), grid, block, 0, st, p);

@@ -270,7 +270,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->norm_eps = 1e-6f;
   out->muon_momentum = 0.95f;
   out->ns_steps = 5;
-  out->ns_split_steps = 3;
+  out->ns_split_steps = 4;
   out->fp8_gemms = GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
@@ -727,6 +727,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       const void* xlo = xl[cur] + bt.off * es;
       {
         GemmArgs p;  // A = X X^T
+        p.sym = true;
         p.split = sp; p.A_lo = xlo; p.B_lo = xlo;
         p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
         p.A = xh; p.lda = bt.l; p.strideA = sl;
@@ -738,6 +739,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       }
       {
         GemmArgs p;  // Bm = b A + c A A   (A symmetric)
+        p.sym = true;
         p.split = sp; p.A_lo = Alo; p.B_lo = Alo;
         p.M = bt.s; p.N = bt.s; p.K = bt.s; p.batch = bt.nb;
         p.A = Aa; p.lda = bt.s; p.strideA = ss;
@@ -877,7 +879,8 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
   p.A = A; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
   p.B = B; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
   p.dtype = at; p.outF = C; p.ldo = ldc; p.strideO = sC;
-  p.tile = tile; p.splits = splits < 1 ? 1 : splits; p.ws = (float*)ws; p.ws_bytes = ws_bytes;
+  p.tile = tile & 15; p.sym = (tile & 16) != 0;
+  p.splits = splits < 1 ? 1 : splits; p.ws = (float*)ws; p.ws_bytes = ws_bytes;
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc == 1) return GPT_ERR_ARG;
   if (rc == 2) return GPT_ERR_SHAPE;

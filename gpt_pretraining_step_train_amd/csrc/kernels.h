@@ -42,6 +42,11 @@ struct GemmArgs {
   bool fp8 = false;
   const float* dq_a = nullptr;
   const float* dq_b = nullptr;
+  // sym: the caller guarantees C is symmetric (M == N, A and B giving C[m][n] = C[n][m]);
+  // the 256x256 kernel then computes the upper tiles only and mirrors them (the
+  // epilogue of element (n, m) runs with its own Cin/aux entries).  A hint: kernels
+  // that do not use it compute every tile.
+  bool sym = false;
 };
 
 // returns 0 on success, else an error code (argument/shape problems)

@@ -62,7 +62,7 @@ def test_default_ns_table(lib):
     c = binding.GptCfg()
     lib.gpt_cfg_from_depth(24, ctypes.byref(c))
     tab = c.coeffs()
-    assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 3 and c.fp8_gemms == 7
+    assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 4 and c.fp8_gemms == 7
     assert ctypes.sizeof(binding.GptCfg) == 136
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
     derived, _ = polar_express.coefficients()

@@ -83,6 +83,33 @@ def test_gemm_layouts_tails_batch_split(case):
     assert err < (1e-5 if dtype == "bf16" else 1e-5), err
 
 
+SYM_CASES = [  # a_kmaj, M, K, batch, tile (+16: symmetric hint), splits
+    (1, 520, 200, 2, 17, 1), (0, 264, 136, 1, 17, 1), (1, 1000, 64, 1, 19, 1), (1, 1002, 96, 1, 17, 1),
+    (1, 520, 2048, 1, 17, 2), (1, 300, 72, 3, 18, 1),
+]
+
+
+@pytest.mark.parametrize("case", SYM_CASES)
+def test_gemm_symmetric_hint(case):
+    """C = A A^T (or A^T A) with the symmetric hint: upper tiles computed, mirrored;
+    every element of both triangles against fp64 (split-K and the 128 kernel ignore it)."""
+    ak, M, K, batch, tile, splits = case
+    say("gemm sym", case)
+    rng = np.random.default_rng(M + K)
+    A = _round(rng.standard_normal((batch, M, K) if ak else (batch, K, M)), "bf16")
+    Am = A if ak else A.transpose(0, 2, 1)
+    ref = np.einsum("zmk,znk->zmn", Am.astype(np.float64), Am.astype(np.float64))
+    dA = to_dev(A, "bf16")
+    C = torch.full((batch, M, M), float("nan"), device="cuda")
+    ws = torch.empty(splits * batch * M * M, device="cuda") if splits > 1 else None
+    B.gemm(DT["bf16"], ak, ak, M, M, K, dA, K if ak else M, dA, K if ak else M, C, M, batch=batch,
+           sA=A[0].size, sB=A[0].size, sC=M * M, tile=tile, splits=splits, ws=ws)
+    torch.cuda.synchronize()
+    got = from_dev(C)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-5
+
+
 SPLIT_CASES = [(1, 1, 300, 200, 136, 1), (1, 0, 296, 264, 264, 2), (0, 0, 136, 200, 1032, 1), (0, 1, 128, 72, 72, 1),
                # batches large enough for the 256x256 kernel
                (1, 1, 520, 264, 200, 64), (1, 0, 264, 520, 136, 64), (0, 0, 264, 264, 264, 128)]

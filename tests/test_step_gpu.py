@@ -143,6 +143,29 @@ def test_second_muon_step_uses_momentum():
     assert rel_l2(w2.astype(np.float64) - w1, -LR * X2) < 2e-2
 
 
+@pytest.mark.parametrize("i", [1, 5])
+def test_muon_momentum_at_d24_width(i):
+    """Two Muon steps on Gaussian gradients for the d24 Wq [1536 x 1536] and W1
+    [6144 x 1536] (the default split-precision Newton-Schulz schedule), against the
+    oracle's heavy-ball momentum and NS; the plain-bf16 iterations are the error."""
+    cfg = configs.get("d24", batch=1, depth=1, seq_len=256)
+    model = binding.Model(cfg, seed=0)
+    table, _ = PE.coefficients()
+    rng = np.random.default_rng(11 + i)
+    shp = model.shape(i)
+    G1, G2 = rng.standard_normal(shp).astype(np.float32), rng.standard_normal(shp).astype(np.float32)
+    model.set_grads(i, G1)
+    model.muon_update(LR)
+    w1 = model.get_params(i)
+    model.set_grads(i, G2)
+    model.muon_update(LR)
+    w2 = model.get_params(i)
+    X2, _ = O.muon_matrix(G2, G1.astype(np.float64), table, mu=cfg["muon_momentum"])
+    e = rel_l2(w2.astype(np.float64) - w1, -LR * X2)
+    say(f"  d24 tensor {i} {shp}: Muon update rel L2 {e:.2e}")
+    assert e < 2e-2
+
+
 def test_step_is_deterministic_and_causal():
     cfg, model, params, tok, tgt = _setup("laptop", batch=8)
     l1 = model.step(_dev(tok), _dev(tgt))
