@@ -492,6 +492,152 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const bf16_t* __rest
     }
 }
 
+// dK, dV with the two accumulations in different waves: 8 waves per 128-key block,
+// waves 0-3 accumulate dV (S -> P, dV += P^T dO) and waves 4-7 dK (S, dP -> dS,
+// dK += dS^T Q) for the same 32 keys.  S is computed by both roles, but each wave
+// holds one 32x128 accumulator, so two waves fit on every SIMD; the Q and dO tiles
+// are staged once for all eight.  A lane owns a key.
+template <int HD>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
+                           const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
+                           int T, int H) {
+  constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
+  __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
+  const bool dk_role = wave >= 4;
+  const int kw = wave & 3;
+  const int kb = blockIdx.x;  // lowest key blocks carry the most query tiles: launched first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const long ld = 3L * H * HD, ldo = (long)H * HD;
+  const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
+  const bf16_t* K = Q + (long)H * HD;
+  const bf16_t* V = Q + 2L * H * HD;
+  const bf16_t* G = dO + (long)b * T * ldo + h * HD;
+  const int key0 = kb * BKEY + kw * 32, mykey = key0 + lq;
+
+  bf16x8_t kf[NKK], vf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    uint4 u = make_uint4(0, 0, 0, 0), w = u;
+    if (mykey < T) {
+      u = *reinterpret_cast<const uint4*>(K + (long)mykey * ld + kk * 16 + hl * 8);
+      if (dk_role) w = *reinterpret_cast<const uint4*>(V + (long)mykey * ld + kk * 16 + hl * 8);
+    }
+    kf[kk] = __builtin_bit_cast(bf16x8_t, u);
+    vf[kk] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  const int nqt = (T + BQT - 1) / BQT;
+  const int qt0 = (kb * BKEY) / BQT;
+  // 64-row tiles staged by 512 threads (two 16-byte chunks each per tile)
+  constexpr int NCH = 64 * HD / 8, PER = (NCH + 511) / 512;
+  uint4 rq[PER], rg[PER];
+  auto load = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 512, row = c / (HD / 8), cc = c % (HD / 8);
+      const bool ok = c < NCH && q0 + row < T;
+      rq[i] = ok ? *reinterpret_cast<const uint4*>(Q + (long)(q0 + row) * ld + cc * 8) : make_uint4(0, 0, 0, 0);
+      rg[i] = ok ? *reinterpret_cast<const uint4*>(G + (long)(q0 + row) * ldo + cc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf, int q0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 512, row = c / (HD / 8), cc = c % (HD / 8);
+      if (NCH % 512 != 0 && c >= NCH) continue;
+      *reinterpret_cast<uint4*>(Qs[buf] + Tile<HD>::off(row, cc * 8)) = rq[i];
+      *reinterpret_cast<uint4*>(Gs[buf] + Tile<HD>::off(row, cc * 8)) = rg[i];
+    }
+    if (tid < BQT) {
+      const int q = q0 + tid;
+      L2s[buf][tid] = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
+      Ds[buf][tid] = q < T ? Dv[(long)bh * T + q] : 0.f;
+    }
+  };
+  if (qt0 < nqt) {
+    load(qt0 * BQT);
+    store(0, qt0 * BQT);
+  }
+  __syncthreads();
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int cur = (qt - qt0) & 1, qb0 = qt * BQT;
+    if (qt + 1 < nqt) load(qb0 + BQT);
+    if (qb0 + BQT - 1 >= key0 && key0 < T) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (qb0 + qs * 32 + 31 < key0) continue;
+        const bool mask = qb0 + qs * 32 < key0 + 31;
+        f32x16_t sc, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          sc = mfma32x32x16_bf16(lds_row8(Qs[cur] + Tile<HD>::off(qs * 32 + lq, kk * 16 + hl * 8)), kf[kk], sc);
+        if (dk_role) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            dp = mfma32x32x16_bf16(lds_row8(Gs[cur] + Tile<HD>::off(qs * 32 + lq, kk * 16 + hl * 8)), vf[kk], dp);
+        }
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qb0 + qs * 32 + acc_row(lane, r);
+            if (q < mykey) sc[r] = -INFINITY;
+          }
+        }
+        float w[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {  // registers 4g..4g+3 hold query rows qs*32 + 8g + 4hl + 0..3
+          const int ql = qs * 32 + 8 * g + 4 * hl;
+          const float4 l4 = *reinterpret_cast<const float4*>(&L2s[cur][ql]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          if (dk_role) {
+            const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              w[4 * g + j] = fast_exp2(fmaf(sc[4 * g + j], sl2, -lv[j])) * (dp[4 * g + j] - dv4[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[4 * g + j] = fast_exp2(fmaf(sc[4 * g + j], sl2, -lv[j]));
+          }
+        }
+        // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves), the second operand read
+        // by transpose from its row-major tile
+        const bf16_t* src = dk_role ? Qs[cur] : Gs[cur];
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          const bf16x8_t wa = pack8(w + 8 * s_);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16_bf16(wa, tile_tr_operand<HD>(src, qs * 32 + 16 * s_, db * 32, lane), acc[db]);
+        }
+      }
+    }
+    if (qt + 1 < nqt) store(cur ^ 1, qb0 + BQT);
+    __syncthreads();
+  }
+  const float scale = dk_role ? 1.f / sqrtf((float)HD) : 1.f;
+  const long part = dk_role ? (long)H * HD : 2L * H * HD;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + acc_row(lane, r);
+      if (key < T) dqkv[((long)b * T + key) * ld + part + h * HD + db * 32 + lq] = f2bf(acc[db][r] * scale);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 attention (plain per-row loops; used by the all-fp32 configuration)
 
@@ -619,7 +765,7 @@ void bwd_dispatch(const void* qkv, const void* dO, const float* lse, const float
   if (at == ACT_BF16) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st, (const bf16_t*)qkv,
                        (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st,
+    hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(512), 0, st,
                        (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
