@@ -18,7 +18,8 @@
 // probability (exponents stay <= 8), so the accumulator rescale is rare.
 //
 // Backward, without atomics: D = rowsum(dO*O); a dQ kernel per query block
-// (recomputing P and dP) and a dK/dV kernel per key block (over query tiles).
+// (recomputing P and dP) and a dK/dV kernel per key block (over query tiles) whose
+// dK and dV accumulators live in different waves.
 #include <math.h>
 
 #include "common.h"
@@ -359,137 +360,6 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
         *reinterpret_cast<uint2*>(op + d) = u;
       }
   }
-}
-
-// dK, dV: per 128-key block (4 waves x 32 keys, a lane owns a key), over 64-query
-// tiles from the diagonal on.  dV += P^T dO and dK += dS^T Q with dO and Q read by
-// transpose from their row-major tiles.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(const bf16_t* __restrict__ qkv,
-                                                            const bf16_t* __restrict__ dO, const float* __restrict__ lse,
-                                                            const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
-                                                            int T, int H) {
-  constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
-  __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
-  const int kb = blockIdx.x;  // lowest key blocks carry the most query tiles: launched first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const long ld = 3L * H * HD, ldo = (long)H * HD;
-  const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
-  const bf16_t* K = Q + (long)H * HD;
-  const bf16_t* V = Q + 2L * H * HD;
-  const bf16_t* G = dO + (long)b * T * ldo + h * HD;
-  const int key0 = kb * BKEY + wave * 32, mykey = key0 + lq;
-
-  bf16x8_t kf[NKK], vf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    uint4 u = make_uint4(0, 0, 0, 0), w = u;
-    if (mykey < T) {
-      u = *reinterpret_cast<const uint4*>(K + (long)mykey * ld + kk * 16 + hl * 8);
-      w = *reinterpret_cast<const uint4*>(V + (long)mykey * ld + kk * 16 + hl * 8);
-    }
-    kf[kk] = __builtin_bit_cast(bf16x8_t, u);
-    vf[kk] = __builtin_bit_cast(bf16x8_t, w);
-  }
-  const float sl2 = LOG2E / sqrtf((float)HD);
-  f32x16_t dk[NDB], dv[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
-
-  const int nqt = (T + BQT - 1) / BQT;
-  const int qt0 = (kb * BKEY) / BQT;
-  RowStager<HD> sq, sg;
-  auto stats = [&](int buf, int qb0) {
-    if (tid < BQT) {
-      const int q = qb0 + tid;
-      L2s[buf][tid] = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
-      Ds[buf][tid] = q < T ? Dv[(long)bh * T + q] : 0.f;
-    }
-  };
-  if (qt0 < nqt) {
-    sq.load(Q, ld, qt0 * BQT, T, tid);
-    sg.load(G, ldo, qt0 * BQT, T, tid);
-    sq.store(Qs[0], tid);
-    sg.store(Gs[0], tid);
-    stats(0, qt0 * BQT);
-  }
-  __syncthreads();
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int cur = (qt - qt0) & 1, qb0 = qt * BQT;
-    if (qt + 1 < nqt) {
-      sq.load(Q, ld, qb0 + BQT, T, tid);
-      sg.load(G, ldo, qb0 + BQT, T, tid);
-    }
-    if (qb0 + BQT - 1 >= key0 && key0 < T) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        if (qb0 + qs * 32 + 31 < key0) continue;
-        const bool mask = qb0 + qs * 32 < key0 + 31;
-        f32x16_t s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const int o = Tile<HD>::off(qs * 32 + lq, kk * 16 + hl * 8);
-          s = mfma32x32x16_bf16(lds_row8(Qs[cur] + o), kf[kk], s);
-          dp = mfma32x32x16_bf16(lds_row8(Gs[cur] + o), vf[kk], dp);
-        }
-        if (mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = qb0 + qs * 32 + acc_row(lane, r);
-            if (q < mykey) s[r] = -INFINITY;
-          }
-        }
-        float p[16], ds[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {  // registers 4g..4g+3 hold query rows qs*32 + 8g + 4hl + 0..3
-          const int ql = qs * 32 + 8 * g + 4 * hl;
-          const float4 l4 = *reinterpret_cast<const float4*>(&L2s[cur][ql]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[4 * g + j] = fast_exp2(fmaf(s[4 * g + j], sl2, -lv[j]));
-            ds[4 * g + j] = p[4 * g + j] * (dp[4 * g + j] - dv4[j]);
-          }
-        }
-#pragma unroll
-        for (int s_ = 0; s_ < 2; ++s_) {
-          const bf16x8_t pa = pack8(p + 8 * s_);
-          const bf16x8_t da = pack8(ds + 8 * s_);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dv[db] = mfma32x32x16_bf16(pa, tile_tr_operand<HD>(Gs[cur], qs * 32 + 16 * s_, db * 32, lane), dv[db]);
-            dk[db] = mfma32x32x16_bf16(da, tile_tr_operand<HD>(Qs[cur], qs * 32 + 16 * s_, db * 32, lane), dk[db]);
-          }
-        }
-      }
-    }
-    if (qt + 1 < nqt) {
-      sq.store(Qs[cur ^ 1], tid);
-      sg.store(Gs[cur ^ 1], tid);
-      stats(cur ^ 1, qb0 + BQT);
-    }
-    __syncthreads();
-  }
-  const float sc = 1.f / sqrtf((float)HD);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + acc_row(lane, r);
-      if (key < T) {
-        bf16_t* rowp = dqkv + ((long)b * T + key) * ld + h * HD + db * 32 + lq;
-        rowp[(long)H * HD] = f2bf(dk[db][r] * sc);
-        rowp[2L * H * HD] = f2bf(dv[db][r]);
-      }
-    }
 }
 
 // dK, dV with the two accumulations in different waves: 8 waves per 128-key block,

@@ -410,7 +410,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   using OB = DmaOperand<BKM, BK>;
   constexpr int ABASE = 0, BBASE = S * OA::BYTES;  // all A stages, then all B stages
   constexpr int LPT = OA::PER + OB::PER;
-  static_assert(S >= 3 && (S - 2) * LPT < 64, "pipeline depth / vmcnt range");
+  static_assert(S >= 2 && (S - 2) * LPT < 64, "pipeline depth / vmcnt range");
   static_assert(NKK % 2 == 0, "slice 0 of every k tile uses fragment buffer 0");
   static_assert((S - 1) * OA::BYTES < 65536 && (S - 1) * OB::BYTES < 65536, "stage offsets must be immediates");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * (OA::BYTES + OB::BYTES)];
@@ -549,6 +549,37 @@ gemm_bf16_dma_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bf16x8_t af[2][FM], bf[2][FN];
+  if constexpr (S == 2) {
+    // two stages: tile t+1 is issued right after the barrier that opens tile t
+    issue(0);
+    for (int t0 = 0; t0 < nkp; t0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        dma_sync<0>();  // tile t landed everywhere; every wave is done with tile t-1
+        issue(u ^ 1);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[0][i] = frag(afo[i][0], OA::BYTES, u, AK);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[0][j] = frag(bfo[j][0], OB::BYTES, u, BKM);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int c = kk & 1;
+          if (kk + 1 < NKK) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(afo[i][kk + 1], OA::BYTES, u, AK);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(bfo[j][kk + 1], OB::BYTES, u, BKM);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bf[c][j], acc[i][j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else {
   // prologue: tiles 0..S-2 in flight; wait for tile 0 and fetch its first fragments
 #pragma unroll
   for (int st = 0; st < S - 1; ++st) issue(st);
@@ -589,6 +620,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
   }
   // every DMA, including the zero tail, must land before the workgroup's LDS is released
   dma_sync<0>();
@@ -1039,6 +1071,8 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
       launch_bf16<256, 256, 2, 2>(p, st);
     else if (p.tile == 3)
       launch_dma<32, 3>(p, st);
+    else if (p.tile == 5)
+      launch_dma<64, 2>(p, st);
     else
       launch_dma<32, 4>(p, st);
   } else {

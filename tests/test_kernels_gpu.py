@@ -41,7 +41,8 @@ GEMM_CASES = [
     ("bf16", 0, 1, 136, 300, 72, 1, 2, 1),
     ("bf16", 1, 1, 256, 384, 128, 3, 2, 1),
     ("bf16", 0, 0, 136, 200, 1032, 1, 2, 3),
-    # 256x256 direct-to-LDS kernel (tile 1: k tiles of 32 in 4 stages, tile 3: in 3 stages)
+    # 256x256 direct-to-LDS kernel (tile 1: k tiles of 32 in 4 stages, tile 3: in 3 stages,
+    # tile 5: k tiles of 64 in 2 stages)
     # and the register-staged 256x256 kernel (tile 4)
     ("bf16", 1, 1, 520, 264, 200, 1, 3, 1),
     ("bf16", 1, 0, 512, 520, 256, 1, 3, 1),
@@ -51,6 +52,12 @@ GEMM_CASES = [
     ("bf16", 1, 1, 256, 384, 128, 3, 1, 1),
     ("bf16", 0, 0, 136, 200, 1032, 1, 1, 3),
     ("bf16", 1, 0, 1000, 776, 1000, 1, 1, 1),
+    ("bf16", 1, 1, 520, 264, 200, 1, 5, 1),
+    ("bf16", 1, 0, 512, 520, 256, 1, 5, 1),
+    ("bf16", 0, 0, 264, 528, 520, 1, 5, 1),
+    ("bf16", 0, 1, 264, 300, 72, 1, 5, 1),
+    ("bf16", 1, 1, 256, 384, 128, 3, 5, 1),
+    ("bf16", 0, 0, 136, 200, 1032, 1, 5, 3),
     ("bf16", 1, 1, 520, 264, 200, 1, 4, 1),
     ("bf16", 0, 0, 264, 528, 520, 1, 4, 1),
     ("fp32", 1, 1, 100, 70, 33, 1, 0, 1),
@@ -85,7 +92,7 @@ def test_gemm_layouts_tails_batch_split(case):
 
 SYM_CASES = [  # a_kmaj, M, K, batch, tile (+16: symmetric hint), splits
     (1, 520, 200, 2, 17, 1), (0, 264, 136, 1, 17, 1), (1, 1000, 64, 1, 19, 1), (1, 1002, 96, 1, 17, 1),
-    (1, 520, 2048, 1, 17, 2), (1, 300, 72, 3, 18, 1),
+    (1, 520, 2048, 1, 17, 2), (1, 300, 72, 3, 18, 1), (1, 520, 200, 2, 21, 1), (0, 264, 136, 1, 21, 1),
 ]
 
 
