@@ -773,6 +773,107 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x
   }
 }
 
+// 16-byte versions (cols and the leading dimension multiples of 8).  The e4m3 code is
+// produced by v_cvt_pk_fp8_f32 (round to nearest even) on values first clamped to
+// +-448, which is the saturating encode above.
+
+template <typename T>
+__device__ inline void load8f(const T* p, float (&f)[8]);
+template <>
+__device__ inline void load8f<bf16_t>(const bf16_t* p, float (&f)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ inline void load8f<float>(const float* p, float (&f)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ inline uint2 e4m3x8(const float (&f)[8], float s) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(f[i] * s, -448.f), 448.f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) amax_vec_kernel(const T* __restrict__ x, long rows, long cols8, long ldx,
+                                                       unsigned* amax_bits) {
+  __shared__ float sm[4];
+  float m = 0.f;
+  const long n = rows * cols8;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const long r = i / cols8, c = (i - r * cols8) * 8;
+    float f[8];
+    load8f<T>(x + r * ldx + c, f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    atomicMax(amax_bits, __float_as_uint(m));
+  }
+}
+
+// a 64x64 tile per block: each thread converts two 8-wide row chunks; the transposed
+// copy is read back from LDS by columns, 16 bytes per thread
+template <typename T>
+__global__ void __launch_bounds__(256) quant_e4m3_vec_kernel(const T* __restrict__ x, int rows, int cols, long ldx,
+                                                             const unsigned* amax_bits, uint8_t* __restrict__ q,
+                                                             long ldq, uint8_t* __restrict__ qt, long ldqt,
+                                                             float* inv_scale) {
+  constexpr int TS = 72;  // LDS row stride in bytes (8-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * TS];
+  const float amax = __uint_as_float(*amax_bits);
+  const float s = amax > 0.f ? 448.f / amax : 1.f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x, c8 = (t & 7) * 8;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rl = (t >> 3) + 32 * j, r = r0 + rl, c = c0 + c8;
+    uint2 b = make_uint2(0, 0);
+    if (r < rows && c < cols) {
+      float f[8];
+      load8f<T>(x + (long)r * ldx + c, f);
+      b = e4m3x8(f, s);
+      if (q) *reinterpret_cast<uint2*>(q + (long)r * ldq + c) = b;
+    }
+    *reinterpret_cast<uint2*>(tile + rl * TS + c8) = b;
+  }
+  if (!qt) return;
+  __syncthreads();
+  const int cl = t >> 2, rs = (t & 3) * 16, c = c0 + cl, rb = r0 + rs;
+  if (c >= cols || rb >= rows) return;
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[(rs + 4 * k + e) * TS + cl] << (8 * e);
+    w[k] = v;
+  }
+  uint8_t* dst = qt + (long)c * ldqt + rb;
+  if (rb + 16 <= rows && (ldqt % 16) == 0 && (rb % 16) == 0) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    for (int e = 0; e < 16 && rb + e < rows; ++e) dst[e] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+  }
+}
+
 inline int grid_for(size_t n, int block = 256, int cap = 65536) {
   size_t g = (n + block - 1) / block;
   if (g > (size_t)cap) g = cap;
@@ -967,8 +1068,19 @@ void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int
 
 void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st) {
   const long n = rows * cols;
-  const int g = (int)std::min<long>((n + 255) / 256, 2048);
   if (n <= 0) return;
+  if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0) {
+    const long n8 = n / 8;
+    const int g8 = (int)std::min<long>((n8 + 255) / 256, 2048);
+    if (it == ACT_BF16)
+      hipLaunchKernelGGL(amax_vec_kernel<bf16_t>, dim3(g8), dim3(256), 0, st, (const bf16_t*)x, rows, cols / 8, ld,
+                         amax_bits);
+    else
+      hipLaunchKernelGGL(amax_vec_kernel<float>, dim3(g8), dim3(256), 0, st, (const float*)x, rows, cols / 8, ld,
+                         amax_bits);
+    return;
+  }
+  const int g = (int)std::min<long>((n + 255) / 256, 2048);
   if (it == ACT_BF16)
     hipLaunchKernelGGL(amax_kernel<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits);
   else
@@ -979,6 +1091,15 @@ void launch_quant_e4m3(const void* x, int it, int rows, int cols, long ld, const
                        long ldq, uint8_t* qt, long ldqt, float* inv_scale, hipStream_t st) {
   dim3 g((cols + 63) / 64, (rows + 63) / 64), b(256);
   if (rows <= 0 || cols <= 0) return;
+  if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0 && (!q || (ldq % 8 == 0 && (uintptr_t)q % 8 == 0))) {
+    if (it == ACT_BF16)
+      hipLaunchKernelGGL(quant_e4m3_vec_kernel<bf16_t>, g, b, 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits, q,
+                         ldq, qt, ldqt, inv_scale);
+    else
+      hipLaunchKernelGGL(quant_e4m3_vec_kernel<float>, g, b, 0, st, (const float*)x, rows, cols, ld, amax_bits, q,
+                         ldq, qt, ldqt, inv_scale);
+    return;
+  }
   if (it == ACT_BF16)
     hipLaunchKernelGGL(quant_e4m3_kernel<bf16_t>, g, b, 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits, q, ldq,
                        qt, ldqt, inv_scale);

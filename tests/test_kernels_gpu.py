@@ -427,19 +427,20 @@ def _e4m3_encode_ref(x):
     return out
 
 
-def test_quant_e4m3_matches_format():
-    rng = np.random.default_rng(21)
-    x = (rng.standard_normal((67, 129)) * np.exp(rng.uniform(-6, 4, (67, 129)))).astype(np.float32)
-    x[0, 0], x[0, 1], x[0, 2] = 0.0, -0.0, 1e-12
-    amax = np.abs(x).max()
+def _check_quant(x, dtype):
+    """Quantise x (rows x cols) through the library and compare every byte with the
+    format's round-to-nearest-even, saturating encode of x * (448 / amax) in fp32."""
+    rows, cols = x.shape
+    xr = bf16_round(x).astype(np.float32) if dtype == "bf16" else x.astype(np.float32)
+    amax = np.abs(xr).max()
     s = np.float32(448.0) / np.float32(amax)
-    want = _e4m3_encode_ref((x * s).astype(np.float32))
-    tx = torch.from_numpy(x).cuda()
+    want = _e4m3_encode_ref((xr * s).astype(np.float32))
+    tx = to_dev(xr, dtype)
     slot = torch.zeros(1, dtype=torch.int32, device="cuda")
     inv = torch.zeros(1, device="cuda")
-    q = torch.zeros(67, 129, dtype=torch.uint8, device="cuda")
-    qt = torch.zeros(129, 67, dtype=torch.uint8, device="cuda")
-    B.quant_e4m3(B.GPT_FP32, tx, 67, 129, 129, slot, q, qt, inv)
+    q = torch.zeros(rows, cols, dtype=torch.uint8, device="cuda")
+    qt = torch.zeros(cols, rows, dtype=torch.uint8, device="cuda")
+    B.quant_e4m3(DT[dtype], tx, rows, cols, cols, slot, q, qt, inv)
     torch.cuda.synchronize()
     got = q.cpu().numpy()
     nz = want & 0x7F != 0          # signed zero: either sign of the zero code is accepted
@@ -447,6 +448,31 @@ def test_quant_e4m3_matches_format():
     assert np.all(got[~nz] & 0x7F == 0)
     np.testing.assert_array_equal(qt.cpu().numpy(), got.T)
     assert inv.item() == pytest.approx(1.0 / s, rel=1e-6)
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [("fp32", 67, 129), ("fp32", 67, 136), ("bf16", 130, 200),
+                                             ("bf16", 64, 64), ("bf16", 1, 8)])
+def test_quant_e4m3_matches_format(dtype, rows, cols):
+    rng = np.random.default_rng(21 + cols)
+    x = rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-6, 4, (rows, cols)))
+    x.flat[:3] = [0.0, -0.0, 1e-12][: x.size]
+    _check_quant(x, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_quant_e4m3_ties_and_subnormals(dtype):
+    """amax = 448 makes the scale exactly 1: every midpoint between adjacent e4m3 values
+    (normal and subnormal) is an exact tie that must round to the even code."""
+    tab = _e4m3_table()
+    pos = np.sort(tab[np.isfinite(tab) & (tab >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([[448.0], mids, -mids, pos, -pos, mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20)])
+    if dtype == "bf16":  # keep only values bf16 holds exactly (ties survive the input rounding)
+        vals = vals[bf16_round(vals) == vals]
+    n = (len(vals) + 7) // 8 * 8
+    x = np.zeros(n)
+    x[: len(vals)] = vals
+    _check_quant(x.reshape(n // 8, 8), dtype)
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 200, 160), (512, 768, 1024)])
