@@ -21,6 +21,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "training tokens/sec + MFU on 1 MI355X, d12 and d24 GPT at seq 2048"
 PEAK_BF16 = 2.5166e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_FP8 = 5.0332e15       # MI355X dense fp8 MFMA, FLOP/s
 PEAK_HBM = 8.0e12          # bytes/s
 LR = 0.02
 # rocprofv3 traffic summaries (FETCH_SIZE + WRITE_SIZE, copy-calibrated) per dominant kernel
@@ -76,8 +77,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d24")
+    ap.add_argument("--fp8", action="store_true",
+                    help="e4m3 operands on every Linear GEMM (the configs' fp8 recipe); default bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dominant", default="gemm_bf16_dma_kernel<256,256,NT>")
+    ap.add_argument("--dominant", default=None,
+                    help="kernel timed for the roofline (default: the NT GEMM of the step's precision)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run three plain device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -102,8 +106,9 @@ def main() -> int:
     from gpt_pretraining_step_train_amd import binding, configs, inputs
 
     cfg = configs.get(args.config)
-    if cfg["precision"] == "fp8":
-        cfg["precision"] = "bf16"
+    if args.dominant is None:
+        args.dominant = "gemm_fp8_dma_kernel<256,256,NT>" if args.fp8 else "gemm_bf16_dma_kernel<256,256,NT>"
+    cfg["precision"] = "fp8" if args.fp8 else "bf16"
     torch.cuda.set_device(0)
     model = binding.Model(cfg, seed=0)
     B, T, V = cfg["batch"], cfg["seq_len"], cfg["vocab"]
@@ -139,15 +144,21 @@ def main() -> int:
     tps = n_tok / (ms_step / 1e3)
     fl = configs.step_flops(cfg)
     mfu = fl["total"] / (ms_step / 1e3) / PEAK_BF16
+    # fp8: the Linear GEMM flops run at the fp8 peak, the rest (attention, NS) at bf16
+    mfu_fp8 = None
+    if args.fp8:
+        t_ideal = (fl["linear"] + fl["head"]) / PEAK_FP8 + (fl["attn"] + fl["muon"]) / PEAK_BF16
+        mfu_fp8 = t_ideal / (ms_step / 1e3)
     achieved = k_flops / (k_ms / 1e3) if k_ms > 0 else None
     from gpt_pretraining_step_train_amd import profiling
     rec = None
     if args.dominant in TRAFFIC and args.config == "d24":
         rec = profiling.read_traffic(os.path.join(ROOT, "profiles", TRAFFIC[args.dominant]))
+    peak = PEAK_FP8 if "fp8" in args.dominant else PEAK_BF16  # a contraction takes its own dtype's peak
     roof = {
         "kernel": args.dominant, "bound": "mfma", "achieved": achieved / 1e12 if achieved else None,
-        "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-        "frac": (achieved / PEAK_BF16) if achieved else None,
+        "peak": peak / 1e12, "unit": "TFLOP/s",
+        "frac": (achieved / peak) if achieved else None,
         "traffic": rec["bytes_per_launch"] if rec else None,
         "traffic_detail": ({"fetch_bytes": rec["fetch_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
                             "source": "profiles/" + TRAFFIC[args.dominant]} if rec else None),
@@ -157,11 +168,12 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Zipf(1.1) token ids, 8 batches cycled)",
-        "config": {"workload": f"{args.config} GPT training step: fwd+bwd+Muon(5 NS) on B={B} x T={T}",
+        "vs_baseline": None, "dtype": "fp8-e4m3 linears, bf16 attention/NS" if args.fp8 else "bf16", "data": "synthetic (seeded Zipf(1.1) token ids, 8 batches cycled)",
+        "config": {"workload": f"{args.config} GPT training step{' (fp8 linears)' if args.fp8 else ''}: "
+                               f"fwd+bwd+Muon(5 NS) on B={B} x T={T}",
                    "depth": cfg["depth"], "d_model": cfg["d_model"], "n_head": cfg["n_head"],
                    "vocab": V, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "mfu": mfu, "flops_per_step": fl["total"], "wall_s": wall,
+        "mfu": mfu, "mfu_at_fp8_peak_for_linears": mfu_fp8, "flops_per_step": fl["total"], "wall_s": wall,
         "loss_first_last": [losses[0], losses[-1]],
         "roofline": roof,
     }

@@ -66,7 +66,7 @@ _SIGS = {
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
     "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _L, _L, _P, _L, _L, _P]),
     "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
-    "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _P]),
+    "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -259,9 +259,11 @@ def quant_e4m3(dtype, x, rows, cols, ld, amax_slot, q, qt, inv_scale):
                                 _ptr(qt) if qt is not None else nul, _ptr(inv_scale), _stream()), "gptk_quant_e4m3")
 
 
-def gemm_fp8(M, N, K, A, lda, B, ldb, dq_a, dq_b, C, ldc):
-    check(lib().gptk_gemm_fp8(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(dq_a), _ptr(dq_b), _ptr(C), ldc, _stream()),
-          "gptk_gemm_fp8")
+def gemm_fp8(M, N, K, A, lda, B, ldb, dq_a, dq_b, C, ldc, splits=1, ws=None):
+    ws_p = _ptr(ws) if ws is not None else ctypes.c_void_p()
+    ws_b = ws.numel() * ws.element_size() if ws is not None else 0
+    check(lib().gptk_gemm_fp8(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(dq_a), _ptr(dq_b), _ptr(C), ldc, splits, ws_p,
+                              ws_b, _stream()), "gptk_gemm_fp8")
 
 
 def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:

@@ -806,18 +806,35 @@ __device__ inline uint2 e4m3x8(const float (&f)[8], float s) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+// contiguous rows are one flat range of 8-element chunks, four loads in flight per
+// lane; strided rows go row by row (no index division either way)
 template <typename T>
 __global__ void __launch_bounds__(256) amax_vec_kernel(const T* __restrict__ x, long rows, long cols8, long ldx,
                                                        unsigned* amax_bits) {
   __shared__ float sm[4];
   float m = 0.f;
-  const long n = rows * cols8;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-    const long r = i / cols8, c = (i - r * cols8) * 8;
+  auto take = [&](const T* p) {
     float f[8];
-    load8f<T>(x + r * ldx + c, f);
+    load8f<T>(p, f);
 #pragma unroll
     for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
+  };
+  if (ldx == cols8 * 8) {
+    const long n = rows * cols8, stride = (long)gridDim.x * 256;
+    long i = blockIdx.x * 256L + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+      float f[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8f<T>(x + (i + u * stride) * 8, f[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[u][k]));
+    }
+    for (; i < n; i += stride) take(x + i * 8);
+  } else {
+    for (long r = blockIdx.x; r < rows; r += gridDim.x)
+      for (long c = threadIdx.x; c < cols8; c += 256) take(x + r * ldx + c * 8);
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;

@@ -377,13 +377,14 @@ __device__ inline void lds_dma16(const u32x4v_t& rsrc, uint32_t lds_addr, uint32
                : "memory", "m0");
 }
 
-// vmcnt(N) lgkmcnt(0), then a workgroup barrier (no memory fence: the DMA
-// stages are ordered by the waits)
-template <int N>
+// vmcnt(N) and (LGKM) lgkmcnt(0), then a workgroup barrier (no memory fence: the
+// DMA stages are ordered by the waits).  Without LGKM the wave's own LDS reads may
+// still be in flight: the compiler waits for each before its first use.
+template <int N, bool LGKM = true>
 __device__ inline void dma_sync() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (LGKM ? 0 : 15 << 8));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -698,67 +699,95 @@ _Pragma("unroll") \
 
 
 // ---------------------------------------------------------------------------
-// fp8 (e4m3) GEMM, both operands with the reduction index contiguous (the
-// quantisation pass writes transposed copies where a product needs them).
-// 256x256 tile, k-tiles of 128 bytes (same LDS footprint as the bf16 kernel),
-// v_mfma_f32_32x32x64_f8f6f4: lane half h of a 64-wide k step holds its 32 k bytes
-// contiguously, for A (row lane%32) and B (column lane%32) alike.
-
+// fp8 (e4m3) GEMM operands: 32 bytes of k per lane for v_mfma_f32_32x32x64_f8f6f4
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-template <int R, int NT>
-struct ByteTileLoader {
-  static constexpr int NUNIT = R * 8;  // 16-byte chunks of 128-byte rows
-  static constexpr int UPT = (NUNIT + NT - 1) / NT;
-  uint4 regs[UPT];
-  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, long ld, int row0, int rows, int k0, int kend, int tid) {
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * NT;
-      const int r = u >> 3, kc = u & 7;
-      const int gk = k0 + kc * 16;
-      const bool ok = u < NUNIT && gk < kend && row0 + r < rows;
-      regs[i] = buf_load16(rs, ok ? (uint32_t)((long)(row0 + r) * ld + gk) : OOB);
-    }
-  }
-  __device__ inline void store(uint8_t* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * NT;
-      if (NUNIT % NT != 0 && u >= NUNIT) continue;
-      *reinterpret_cast<uint4*>(lds + (u >> 3) * (LDSS * 2) + (u & 7) * 16) = regs[i];
-    }
-  }
-};
+// fp8 GEMM on the DMA path: the 256x256 tile of the bf16 kernel with 8 waves of 128x64,
+// both operands e4m3 with the reduction index contiguous, k tiles of BKB bytes in S
+// LDS stages (a 64-byte tile has the byte layout of a 32-deep bf16 K-major tile:
+// 16-byte chunk c of row r at c ^ kswz(r)).  Tile t + S - 1 is issued when tile t
+// starts.  A lane's fragment for one v_mfma_scale_f32_32x32x64_f8f6f4 is 32 bytes:
+// lane half h holds k bytes 32h..32h+31 of its row (any k mapping shared by A and B
+// gives the same sum).  The k slices of all tiles form one sequence: the B fragments
+// of the next slice load under the current slice's MFMAs, and each A fragment is
+// reloaded for the next slice as soon as its own MFMAs have issued.  The product is
+// multiplied by (*dq_a) * (*dq_b) as it is staged for the epilogue.
+template <int BKB, int S>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_fp8_dma_kernel(GemmArgs p) {
+  constexpr int WN = 4, TM = 128, TN = 64, FM = TM / 32, FN = TN / 32, NKK = BKB / 64;
+  using OP = DmaOperand<true, BKB / 2>;  // byte tile [256][BKB] = bf16 tile [256][BKB/2]
+  constexpr int OBYTES = OP::BYTES, PER = OP::PER, LPT = 2 * PER;
+  constexpr int ABASE = 0, BBASE = S * OBYTES;
+  static_assert(NKK >= 1 && BKB % 64 == 0, "whole 64-byte MFMA k steps per tile");
+  static_assert(S >= 3 && (S - 2) * LPT < 64, "pipeline depth / vmcnt range");
+  static_assert((S - 1) * OBYTES < 65536, "stage offsets must be immediates");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * S * OBYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(WM* WN * 64) gemm_fp8_kernel(GemmArgs p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int BKB = 128;           // k bytes per tile
-  constexpr int RS = LDSS * 2;       // LDS row stride in bytes (16-byte pad)
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * LDSS];
-  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int tilesM = (p.M + BM - 1) / BM, tilesN = (p.N + BN - 1) / BN;
+  const int tilesM = (p.M + 255) / 256, tilesN = (p.N + 255) / 256;
   int tm, tn;
   tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
   const int bz = blockIdx.y / p.splits, sk = blockIdx.y % p.splits;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * 256, n0 = tn * 256;
   const int kper = ((p.K + p.splits - 1) / p.splits + BKB - 1) / BKB * BKB;
   const int kbeg = sk * kper;
   const int kend = min(p.K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg + BKB - 1) / BKB : 0;
+  const int nkp = (nk + S - 1) / S * S;  // padded with all-zero tiles to whole unrolled rounds
   const uint8_t* A = reinterpret_cast<const uint8_t*>(p.A) + bz * p.strideA;
   const uint8_t* B = reinterpret_cast<const uint8_t*>(p.B) + bz * p.strideB;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)((long)p.M * p.lda));
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, (uint32_t)((long)p.N * p.ldb));
+  const u32x4v_t rA = res_words(A, (uint32_t)((long)p.M * p.lda)), rB = res_words(B, (uint32_t)((long)p.N * p.ldb));
   const float dq = p.dq_a[0] * p.dq_b[0];
 
-  ByteTileLoader<BM, NT> la0, la1;
-  ByteTileLoader<BN, NT> lb0, lb1;
+  uint32_t aoff[PER], boff[PER];
+  int kin[PER];
+  bool aok[PER], bok[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int P = (j * 8 + wave) * 64 + lane, row = P / OP::CPR, lc = (P % OP::CPR) ^ OP::swz(row);
+    kin[j] = lc * 16;
+    aok[j] = m0 + row < p.M;
+    bok[j] = n0 + row < p.N;
+    aoff[j] = (uint32_t)((long)(m0 + row) * p.lda + lc * 16);
+    boff[j] = (uint32_t)((long)(n0 + row) * p.ldb + lc * 16);
+  }
+  int it_t = 0, it_k0 = kbeg;
+  auto issue = [&](int st) {
+    const bool live = it_t < nk, full = it_k0 + BKB <= kend;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool kok = live && (full || it_k0 + kin[j] < kend);
+      lds_dma16(rA, lds0 + ABASE + st * OBYTES + (j * 8 + wave) * 1024, kok && aok[j] ? aoff[j] + it_k0 : OOB);
+      lds_dma16(rB, lds0 + BBASE + st * OBYTES + (j * 8 + wave) * 1024, kok && bok[j] ? boff[j] + it_k0 : OOB);
+    }
+    ++it_t;
+    it_k0 += BKB;
+  };
+
+  // kswz(row) depends on row only through (row / 4) % 4 or (row / 2) % 8, which every
+  // 32-row fragment of a lane shares: the chunk positions are per-lane constants and
+  // the fragment rows are immediate offsets from one base
+  const int lr = lane & 31, hl = lane >> 5, sw = OP::swz(lr);
+  static_assert(32 % (16 / OP::CPR) == 0 && (32 / (16 / OP::CPR)) % OP::CPR == 0, "swizzle repeats every 32 rows");
+  int cofs[NKK][2];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) cofs[kk][h] = ((4 * kk + 2 * hl + h) ^ sw) << 4;
+  const uint8_t* abase = smem + ABASE + (wm * TM + lr) * BKB;
+  const uint8_t* bbase = smem + BBASE + (wn * TN + lr) * BKB;
+  auto frag = [&](const uint8_t* rowp, int kk) -> i32x8_t {
+    const uint4 a = *reinterpret_cast<const uint4*>(rowp + cofs[kk][0]);
+    const uint4 b = *reinterpret_cast<const uint4*>(rowp + cofs[kk][1]);
+    u32x8_t v;
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    return __builtin_bit_cast(i32x8_t, v);
+  };
+
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -766,89 +795,95 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_fp8_kernel(GemmArgs p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int lr = lane & 31, lh = (lane >> 5) * 32;
 
-#define FP8_LOAD(LA, LB, T)                                                     \
-  do {                                                                          \
-    const int k_ = (T) < nk ? kbeg + (T) * BKB : kend;                          \
-    LA.load(rA, p.lda, m0, p.M, k_, kend, tid);                                 \
-    LB.load(rB, p.ldb, n0, p.N, k_, kend, tid);                                 \
-  } while (0)
-#define FP8_FRAG(PTR) __builtin_bit_cast(i32x8_t, *reinterpret_cast<const u32x8_t*>(PTR))
-#define FP8_COMPUTE(BUF)                                                                     \
-  do {                                                                                       \
-    const uint8_t* as_ = lds + (BUF) * (BM * RS) + (wm * TM + lr) * RS + lh;                 \
-    const uint8_t* bs_ = lds + 2 * BM * RS + (BUF) * (BN * RS) + (wn * TN + lr) * RS + lh;    \
-    _Pragma("unroll") for (int kk = 0; kk < BKB / 64; ++kk) {                                \
-      i32x8_t af_[FM], bf_[FN];                                                              \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) af_[i] = FP8_FRAG(as_ + i * 32 * RS + kk * 64); \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) bf_[j] = FP8_FRAG(bs_ + j * 32 * RS + kk * 64); \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                         \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af_[i], bf_[j], acc[i][j], 0, 0, 0, 0, 0, 0); \
-    }                                                                                        \
-  } while (0)
+  // prologue: tiles 0..S-2 in flight; wait for tile 0 and fetch its first fragments
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st);
+  dma_sync<(S - 2) * LPT>();
+  i32x8_t af[FM], bf[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) af[i] = frag(abase + i * 32 * BKB, 0);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bf[j] = frag(bbase + j * 32 * BKB, 0);
 
-  const int nk2 = (nk + 1) & ~1;
-  if (nk2 > 0) {
-    FP8_LOAD(la0, lb0, 0);
-    la0.store(lds, tid);
-    lb0.store(lds + 2 * BM * RS, tid);
-    FP8_LOAD(la1, lb1, 1);
-  }
-  __syncthreads();
-  for (int it = 0; it < nk2; it += 2) {
-    if (it + 2 < nk2) FP8_LOAD(la0, lb0, it + 2);
-    FP8_COMPUTE(0);
-    la1.store(lds + BM * RS, tid);
-    lb1.store(lds + 2 * BM * RS + BN * RS, tid);
-    __syncthreads();
-    if (it + 3 < nk2) FP8_LOAD(la1, lb1, it + 3);
-    FP8_COMPUTE(1);
-    if (it + 2 < nk2) {
-      la0.store(lds, tid);
-      lb0.store(lds + 2 * BM * RS, tid);
+  for (int t0 = 0; t0 < nkp; t0 += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bool last = kk == NKK - 1;
+        const int nst = last ? (u + 1) % S : u, nkk = last ? 0 : kk + 1;
+        if (last) {
+          // tile t+1 landed; every wave is past tile t-1, whose stage was last read
+          // (into registers the MFMAs of tile t-1 consumed) one tile earlier
+          dma_sync<(S - 3) * LPT, false>();
+          issue((u + S - 1) % S);
+        }
+        i32x8_t bn[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bn[j] = frag(bbase + nst * OBYTES + j * 32 * BKB, nkk);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+          af[i] = frag(abase + nst * OBYTES + i * 32 * BKB, nkk);
+        }
+        // one MFMA, then two fragment reads for the next slice, so that the reads
+        // spread over the slice instead of gathering before the next barrier
+        static_assert(FM * FN >= FM + FN, "a read pair per MFMA");
+#pragma unroll
+        for (int g = 0; g < FM + FN; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = bn[j];
+      }
     }
-    __syncthreads();
   }
-#undef FP8_LOAD
-#undef FP8_FRAG
-#undef FP8_COMPUTE
+  // every DMA, including the zero tail, must land before the workgroup's LDS is released
+  dma_sync<0>();
 
   constexpr int CS = TN + 4;
   constexpr int LPR = TN / 4, RPI = 64 / LPR;
+  static_assert(8 * 32 * CS * 4 <= 2 * S * OBYTES, "staging must fit");
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * CS;
   const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
                    (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
   const int lc = (lane % LPR) * 4, lrow = lane / LPR;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[i][j][r] * dq;
-    __syncthreads();
-    const int row0 = m0 + wm * TM + i * 32;
-    const int col = n0 + wn * TN + lc;
-    for (int rr = lrow; rr < 32; rr += RPI) {
-      const int row = row0 + rr;
-      if (row >= p.M) break;
-      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
-      if (p.splits > 1) {
-        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
-        const float e[4] = {a.x, a.y, a.z, a.w};
-        for (int t = 0; t < 4; ++t)
-          if (col + t < p.N) w[t] = e[t];
-      } else if (vec && col + 3 < p.N) {
-        epilogue_vec4(p, bz, row, col, a);
-      } else {
-        const float e[4] = {a.x, a.y, a.z, a.w};
-        for (int t = 0; t < 4; ++t)
-          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);
-      }
-    }
-    __syncthreads();
-  }
+#define FP8_EPI_BLOCK(I_)                                                                          \
+  do {                                                                                             \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                 \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r)                                               \
+        stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[I_][j][r] * dq;                           \
+    const int row0 = m0 + wm * TM + I_ * 32;                                                       \
+    const int col = n0 + wn * TN + lc;                                                             \
+    for (int rr = lrow; rr < 32; rr += RPI) {                                                      \
+      const int row = row0 + rr;                                                                   \
+      if (row >= p.M) break;                                                                       \
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);                     \
+      if (p.splits > 1) {                                                                          \
+        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;                              \
+        const float e[4] = {a.x, a.y, a.z, a.w};                                                   \
+        for (int t = 0; t < 4; ++t)                                                                \
+          if (col + t < p.N) w[t] = e[t];                                                          \
+      } else if (vec && col + 3 < p.N) {                                                           \
+        epilogue_vec4(p, bz, row, col, a);                                                         \
+      } else {                                                                                     \
+        const float e[4] = {a.x, a.y, a.z, a.w};                                                   \
+        for (int t = 0; t < 4; ++t)                                                                \
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);                     \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+  FP8_EPI_BLOCK(0);
+  FP8_EPI_BLOCK(1);
+  FP8_EPI_BLOCK(2);
+  FP8_EPI_BLOCK(3);
+  static_assert(FM == 4, "one expansion per 32-row block");
+#undef FP8_EPI_BLOCK
 }
 
 // ---------------------------------------------------------------------------
@@ -1032,7 +1067,7 @@ const char* gemm_kernel_name(const GemmArgs& p) {
        "gemm_bf16x3_dma_kernel<256,256,TN>", "gemm_bf16x3_dma_kernel<256,256,TT>"},
       {"gemm_bf16x3_kernel<128,128,NT>", "gemm_bf16x3_kernel<128,128,NN>", "gemm_bf16x3_kernel<128,128,TN>",
        "gemm_bf16x3_kernel<128,128,TT>"}};
-  if (p.fp8) return "gemm_fp8_kernel<256,256,NT>";
+  if (p.fp8) return "gemm_fp8_dma_kernel<256,256,NT>";
   const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
   const int t = p.dtype == ACT_F32 ? 0 : (pick_tile(p) == 2 ? 2 : 1);
   if (p.split && t) return split_names[t][lay];
@@ -1054,7 +1089,7 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if (p.K % 16 || p.lda % 16 || p.ldb % 16) return 2;
     if ((long)p.M * p.lda >= (long)0xFFFFFFF0u || (long)p.N * p.ldb >= (long)0xFFFFFFF0u) return 2;
     const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    hipLaunchKernelGGL((gemm_fp8_kernel<256, 256, 2, 2>), dim3(tiles, p.batch * p.splits), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_fp8_dma_kernel<64, 4>), dim3(tiles, p.batch * p.splits), dim3(512), 0, st, p);
   } else
   if (p.dtype == ACT_BF16) {
     // buffer loads address each operand matrix with 32-bit byte offsets

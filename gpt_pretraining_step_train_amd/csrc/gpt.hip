@@ -53,7 +53,7 @@ struct Offsets {
   size_t params, grads, mom, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      amax, qinv;
+      xq8t, amax, qinv;
   size_t splitws_bytes;
 };
 
@@ -61,6 +61,10 @@ constexpr int kSumsqParts = 64;
 // quantisation events of one fp8 step: weights (4 per layer + head), forward inputs
 // (4 per layer + head), backward output gradients and inputs (8 per layer + 2)
 inline size_t kQuantSlots(const gpt_cfg& c) { return 16 * (size_t)c.depth + 8; }
+// the forward's quantisation of each Linear input also serves its weight gradient
+inline bool keeps_xt(const gpt_cfg& c) {
+  return c.precision == GPT_FP8 && (c.fp8_gemms & GPT_FP8_FWD) && (c.fp8_gemms & GPT_FP8_WGRAD);
+}
 
 int act_of(const gpt_cfg& c) { return c.precision == GPT_FP32 ? ACT_F32 : ACT_BF16; }
 
@@ -136,16 +140,21 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.mat_size = P.add(6 * L * 8);
   if (c.precision == GPT_FP8) {
     const size_t wide = std::max(std::max(3 * d, F), V);
+    O.q8c = O.xq8t = 0;
     O.wq8 = P.add(nBlk + nU);
     O.wtq8 = P.add(nBlk + nU);
     O.wscale = P.add((4 * L + 1) * 4);
     O.q8a = P.add(N * wide);
     O.q8b = P.add(N * wide);
-    O.q8c = P.add(N * std::max(d, F));
+    // e4m3 codes of every Linear input, transposed, written by the forward's quantisation
+    // pass and read by the weight-gradient GEMM (same tensor, same scale): per layer
+    // a, o, m [d][N] and g [F][N], then the head input r [d][N]
+    if (keeps_xt(c)) O.xq8t = P.add(L * N * (3 * d + F) + N * d);
+    else O.q8c = P.add(N * std::max(d, F));
     O.amax = P.add(kQuantSlots(c) * 4);
     O.qinv = P.add(kQuantSlots(c) * 4);
   } else {
-    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.amax = O.qinv = 0;
+    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.xq8t = O.amax = O.qinv = 0;
   }
   O.rope = P.add(T * (c.head_dim / 2) * 2 * 4);
   O.loss = P.add(8);
@@ -171,6 +180,7 @@ struct gpt_model {
   bool fp8 = false;
   bool wq_dirty = true;  // fp8 weight copies must be refreshed before the next step
   int qslot = 0;         // next quantisation slot of the current step
+  std::vector<int> xslot;  // per weight: quantisation slot of its input in this step's forward
   // matrix table for Muon, in layer order (q, k, v, o, w1, w2)
   std::vector<long> moff, msize;
   // profiling
@@ -358,6 +368,7 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   M->at = act_of(*cfg);
   M->es = M->at == ACT_BF16 ? 2 : 4;
   M->fp8 = cfg->precision == GPT_FP8;
+  M->xslot.assign(4 * cfg->depth + 1, -1);
   M->N = cfg->batch * cfg->seq_len;
   M->lo = layer_offs(*cfg);
   M->nE = (size_t)cfg->vocab * cfg->d_model;
@@ -445,6 +456,13 @@ static void quant_weights(gpt_model* M, hipStream_t st) {
 }
 
 // quantise an activation-typed [rows][cols] tensor: q row-major and/or qt transposed
+// the kept transposed e4m3 input of weight w (per layer a, o, m [d][N], g [F][N]; head r [d][N])
+static uint8_t* xq8t_of(gpt_model* M, int w) {
+  const size_t N = M->N, d = M->cfg.d_model, F = M->cfg.d_ff;
+  const size_t l = w / 4, j = w % 4;
+  return M->at_off<uint8_t>(M->off.xq8t) + l * N * (3 * d + F) + j * N * d;
+}
+
 static int quant_act(gpt_model* M, const void* x, int rows, int cols, long ldx, uint8_t* q, uint8_t* qt,
                      hipStream_t st) {
   const int slot = M->qslot++;
@@ -464,7 +482,9 @@ static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st) {
     return run_gemm(M, p, st, false);
   }
   uint8_t* q8a = M->at_off<uint8_t>(M->off.q8a);
-  const int sx = quant_act(M, p.A, p.M, p.K, p.lda, q8a, nullptr, st);
+  uint8_t* xt = keeps_xt(M->cfg) ? xq8t_of(M, w) : nullptr;
+  const int sx = quant_act(M, p.A, p.M, p.K, p.lda, q8a, xt, st);
+  M->xslot[w] = xt ? sx : -1;
   p.A = q8a; p.lda = p.K;
   p.B = M->at_off<uint8_t>(M->off.wq8) + wi.off; p.ldb = wi.cols;
   p.fp8 = true;
@@ -491,8 +511,12 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
   const float* qinv = M->at_off<float>(M->off.qinv);
   const int sy = (f8w || f8d) ? quant_act(M, dY, N, nout, ldy, f8d ? q8a : nullptr, f8w ? q8b : nullptr, st) : 0;
   if (f8w) {
-    const int sx = quant_act(M, X, N, kin, ldx, nullptr, q8c, st);  // X^T
-    pw.A = q8b; pw.lda = N; pw.B = q8c; pw.ldb = N;                 // dY^T and X^T, reduction over tokens
+    // X^T: kept from the forward (the same tensor, so the same scale and codes), else quantised here
+    const bool kept = M->xslot[w] >= 0;
+    if (keeps_xt(M->cfg) && !kept) return GPT_ERR_ARG;  // the forward of this step did not run
+    uint8_t* xt = kept ? xq8t_of(M, w) : q8c;
+    const int sx = kept ? M->xslot[w] : quant_act(M, X, N, kin, ldx, nullptr, q8c, st);
+    pw.A = q8b; pw.lda = N; pw.B = xt; pw.ldb = N;  // dY^T and X^T, reduction over tokens
     pw.fp8 = true; pw.dq_a = qinv + sy; pw.dq_b = qinv + sx;
   } else {
     pw.A = dY; pw.lda = ldy; pw.a_kmaj = false;
@@ -914,12 +938,13 @@ int gptk_quant_e4m3(int dtype, const void* x, int rows, int cols, long ld, uint3
 }
 
 int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t* B, long ldb, const float* dq_a,
-                  const float* dq_b, float* C, long ldc, void* stream) {
+                  const float* dq_b, float* C, long ldc, int splits, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0 || !A || !B || !dq_a || !dq_b || !C) return GPT_ERR_ARG;
   GemmArgs p;
   p.M = M; p.N = N; p.K = K; p.fp8 = true; p.dtype = ACT_BF16;
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.dq_a = dq_a; p.dq_b = dq_b;
   p.outF = C; p.ldo = ldc;
+  p.splits = splits < 1 ? 1 : splits; p.ws = (float*)ws; p.ws_bytes = ws_bytes;
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc) return rc == 1 ? GPT_ERR_ARG : GPT_ERR_SHAPE;
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;

@@ -179,9 +179,11 @@ int gptk_quant_e4m3(int dtype, const void* x, int rows, int cols, long ld, uint3
                     uint8_t* qt, float* inv_scale, void* stream);
 
 /* C [M][N] fp32 = dq_a[0] * dq_b[0] * sum_k A[m][k] B[n][k] with e4m3 A [M][K], B [N][K]
- * (reduction index contiguous, K, lda, ldb multiples of 16), on fp8 MFMA. */
+ * (reduction index contiguous, K, lda, ldb multiples of 16), on fp8 MFMA.  splits > 1
+ * divides the reduction into that many parts (multiples of 64) whose fp32 partial
+ * products go to ws (splits*M*N floats, else GPT_ERR_ARG) and are then summed. */
 int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t* B, long ldb, const float* dq_a,
-                  const float* dq_b, float* C, long ldc, void* stream);
+                  const float* dq_b, float* C, long ldc, int splits, void* ws, size_t ws_bytes, void* stream);
 
 /* name of the GEMM kernel instantiation gptk_gemm / gpt_step launch for these
  * layouts and sizes, e.g. "gemm_bf16_dma_kernel<256,256,NT>" (NT: both operands have

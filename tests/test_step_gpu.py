@@ -37,7 +37,7 @@ def _gpu():
 
 
 def _setup(name, seed=0, **over):
-    cfg = configs.get(name.replace("_fp8", ""), **over)
+    cfg = configs.get(name.split("_")[0], **over)  # the case name starts with the config name
     model = binding.Model(cfg, seed=seed)
     params = inputs.init_weights(cfg, seed)
     model.set_all_params(params)
@@ -49,7 +49,12 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+# fp8_gemms selects the e4m3 GEMMs: 1 forward, 2 weight gradient, 4 input gradient.
+# With the forward and weight gradient both in e4m3 (the default 7), the weight
+# gradient reuses the forward's codes of its input; with 6 it quantises them itself.
 STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8", {"precision": "fp8"}),
+              ("laptop_fp8_bwd", {"precision": "fp8", "fp8_gemms": 6}),
+              ("laptop_fp8_fwd", {"precision": "fp8", "fp8_gemms": 1}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
