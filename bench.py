@@ -25,7 +25,8 @@ PEAK_FP8 = 5.0332e15       # MI355X dense fp8 MFMA, FLOP/s
 PEAK_HBM = 8.0e12          # bytes/s
 LR = 0.02
 # rocprofv3 traffic summaries (FETCH_SIZE + WRITE_SIZE, copy-calibrated) per dominant kernel
-TRAFFIC = {"gemm_bf16_dma_kernel<256,256,NT>": "gemm_bf16_dma_kernel_NT__d24_step_traffic.md"}
+TRAFFIC = {"gemm_bf16_dma_kernel<256,256,NT>": "gemm_bf16_dma_kernel_NT__d24_step_traffic.md",
+           "gemm_fp8_dma_kernel<256,256,NT>": "gemm_fp8_dma_kernel_NT__d24_fp8_step_traffic.md"}
 
 
 def cpu_baseline(cfg: dict) -> dict:

@@ -130,7 +130,8 @@ def main(argv=None) -> int:
     t = sub.add_parser("traffic")
     for k in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--name", "--command"):
         t.add_argument(k, required=True)
-    t.add_argument("--copy-kernel", default="elementwise|copy")
+    # the probe's torch.mul (the tensor fill before it reads nothing and must not count)
+    t.add_argument("--copy-kernel", default="AUnaryFunctor")
     t.add_argument("--copy-bytes", type=float, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
