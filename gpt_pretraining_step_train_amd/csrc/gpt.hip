@@ -709,9 +709,12 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   float* xf = M->at_off<float>(O.xf);
   char* xa[2] = {M->base + O.xa0, M->base + O.xa1};
   char* xl[2] = {M->base + O.xl0, M->base + O.xl1};
-  // the leading iterations multiply with operands carried as bf16 hi + lo planes
-  // (three MFMA products each): rounding errors of the early iterations are amplified
-  // by the later ones along small singular directions, those of the last are not
+  // the leading iterations multiply A A and B X with operands carried as bf16 hi + lo
+  // planes (three MFMA products each): rounding errors of the early iterations are
+  // amplified by the later ones along small singular directions, those of the last are
+  // not.  The Gram product X X^T stays plain bf16 in every iteration (its rounding
+  // costs far less accuracy than that of the other two; its fp32 result still feeds
+  // the split A A as hi + lo planes)
   const int nsplit = M->at == ACT_BF16 ? std::min(c.ns_split_steps, c.ns_steps) : 0;
   const size_t es = M->es;
   launch_momentum(mom, M->blk(M->grads()), c.muon_momentum, M->nBlk, st);
@@ -752,7 +755,6 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       {
         GemmArgs p;  // A = X X^T
         p.sym = true;
-        p.split = sp; p.A_lo = xlo; p.B_lo = xlo;
         p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
         p.A = xh; p.lda = bt.l; p.strideA = sl;
         p.B = xh; p.ldb = bt.l; p.strideB = sl;
