@@ -598,3 +598,52 @@ def test_fp8_flags_reach_their_gemms():
     assert rel(res[4][1][-1], g0[-1]) == 0 and rel(res[2][1][-1], g0[-1]) > 1e-3
     # and only the weight-gradient flag leaves the embedding gradient exact
     assert rel(res[2][1][0], g0[0]) == 0 and rel(res[4][1][0], g0[0]) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# AdamW (E and U)
+
+from oracle import adamw as AW  # noqa: E402
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_adamw_matches_torch_adamw(wd):
+    """Four steps against torch.optim.AdamW in fp64 (a library routine), with
+    gradients of mixed magnitude, some exactly zero."""
+    rng = np.random.default_rng(5)
+    w0 = rng.standard_normal((7, 11))
+    grads = [rng.standard_normal((7, 11)) * np.exp(rng.uniform(-8, 2, (7, 11))) for _ in range(4)]
+    grads[1][2] = 0.0
+    hp = dict(lr=3e-3, betas=(0.8, 0.95), eps=1e-10, weight_decay=wd)
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.AdamW([p], **hp, foreach=False)
+    w, m, v = w0, np.zeros_like(w0), np.zeros_like(w0)
+    for t, g in enumerate(grads, 1):
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        w, m, v = AW.adamw_step(w, g, m, v, t, hp["lr"], *hp["betas"], hp["eps"], wd)
+        np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_adamw_closed_forms():
+    """From zero moments the first step is w - lr wd w - lr g / (|g| + eps); a zero
+    gradient leaves the moments at zero and only decays the weight; the bias
+    corrections make a constant gradient give the same step at every t."""
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal(50)
+    g = rng.standard_normal(50)
+    lr, b1, b2, eps, wd = 1e-2, 0.9, 0.99, 1e-8, 0.05
+    w1, m1, v1 = AW.adamw_step(w, g, 0 * w, 0 * w, 1, lr, b1, b2, eps, wd)
+    np.testing.assert_allclose(w1, w - lr * wd * w - lr * g / (np.abs(g) + eps), rtol=1e-14)
+    np.testing.assert_allclose(m1, (1 - b1) * g, rtol=1e-15)
+    np.testing.assert_allclose(v1, (1 - b2) * g * g, rtol=1e-15)
+    w0, m0, v0 = AW.adamw_step(w, 0 * g, 0 * w, 0 * w, 1, lr, b1, b2, eps, wd)
+    np.testing.assert_array_equal(m0, 0 * w)
+    np.testing.assert_array_equal(v0, 0 * w)
+    np.testing.assert_allclose(w0, w * (1 - lr * wd), rtol=1e-15)
+    # constant gradient, no decay: m_hat = g and v_hat = g^2 at every t
+    wt, m, v = w.copy(), 0 * w, 0 * w
+    for t in range(1, 6):
+        prev = wt
+        wt, m, v = AW.adamw_step(wt, g, m, v, t, lr, b1, b2, eps, 0.0)
+        np.testing.assert_allclose(prev - wt, lr * g / (np.abs(g) + eps), rtol=1e-9)
