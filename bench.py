@@ -78,6 +78,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d24")
+    ap.add_argument("--accum", type=int, default=1, metavar="K",
+                    help="K micro-batches accumulated per optimizer update (gpt_step_accumulate, grad scale 1/K): "
+                         "one timed step is K forward/backward passes and one Muon update")
+    ap.add_argument("--adamw", action="store_true",
+                    help="also run AdamW on E and U in every step (lr 1e-3, betas 0.8/0.95, eps 1e-10: the "
+                         "pages print none; the values do not change the cost)")
     ap.add_argument("--fp8", action="store_true",
                     help="e4m3 operands on every Linear GEMM (the configs' fp8 recipe); default bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -119,10 +125,15 @@ def main() -> int:
         batches.append((torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda()))
     stream = torch.cuda.current_stream()
 
+    K = max(1, args.accum)
+
     def one(i):
-        tok, tgt = batches[i % len(batches)]
-        loss = model.step(tok, tgt)
+        for k in range(K):
+            tok, tgt = batches[(i * K + k) % len(batches)]
+            loss = model.step(tok, tgt, accumulate=k > 0, grad_scale=1.0 / K) if K > 1 else model.step(tok, tgt)
         model.muon_update(LR)
+        if args.adamw:
+            model.adamw_update(1e-3, 0.8, 0.95, 1e-10, 0.0)
         return loss
 
     for i in range(args.warmup):
@@ -141,9 +152,12 @@ def main() -> int:
     n_launch, k_ms, k_flops = model.prof_read()
     model.prof_enable(None)
     ms_step = gpu_ms / args.steps
-    n_tok = B * T
+    n_tok = B * T * K
     tps = n_tok / (ms_step / 1e3)
     fl = configs.step_flops(cfg)
+    if K > 1:  # K forward/backward passes per Muon update
+        fl = {k: (v if k == "muon" else K * v) for k, v in fl.items()}
+        fl["total"] = fl["linear"] + fl["head"] + fl["attn"] + fl["muon"]
     mfu = fl["total"] / (ms_step / 1e3) / PEAK_BF16
     # fp8: the Linear GEMM flops run at the fp8 peak, the rest (attention, NS) at bf16
     mfu_fp8 = None
@@ -171,9 +185,11 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8-e4m3 linears, bf16 attention/NS" if args.fp8 else "bf16", "data": "synthetic (seeded Zipf(1.1) token ids, 8 batches cycled)",
         "config": {"workload": f"{args.config} GPT training step{' (fp8 linears)' if args.fp8 else ''}: "
-                               f"fwd+bwd+Muon(5 NS) on B={B} x T={T}",
+                               + (f"{K} accumulated fwd+bwd micro-batches of B={B} x T={T}, then Muon(5 NS)"
+                                f"{'+AdamW(E,U)' if args.adamw else ''}" if K > 1 else
+                                f"fwd+bwd+Muon(5 NS){'+AdamW(E,U)' if args.adamw else ''} on B={B} x T={T}"),
                    "depth": cfg["depth"], "d_model": cfg["d_model"], "n_head": cfg["n_head"],
-                   "vocab": V, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+                   "vocab": V, "global_batch": B * K, "micro_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu, "mfu_at_fp8_peak_for_linears": mfu_fp8, "flops_per_step": fl["total"], "wall_s": wall,
         "loss_first_last": [losses[0], losses[-1]],
         "roofline": roof,

@@ -45,8 +45,10 @@ _SIGS = {
     "gpt_state_bytes": (_SZ, [ctypes.POINTER(GptCfg)]),
     "gpt_init": (_I, [ctypes.POINTER(GptCfg), ctypes.c_uint64, _P, _SZ, _P, ctypes.POINTER(_P)]),
     "gpt_step": (_F, [_P, _P, _P, ctypes.POINTER(GptCfg), _P]),
+    "gpt_step_accumulate": (_F, [_P, _P, _P, ctypes.POINTER(GptCfg), _I, _F, _P]),
     "gpt_grads": (_I, [_P, ctypes.c_int32, _P, _SZ, _P]),
     "muon_update": (_I, [_P, _F, _P]),
+    "adamw_update": (_I, [_P, _F, _F, _F, _F, _F, _P]),
     "gpt_argmax": (_I, [_P, _P, _P]),
     "gpt_row_loss": (_I, [_P, _P, _P]),
     "gpt_get_params": (_I, [_P, ctypes.c_int32, _P, _SZ, _P]),
@@ -172,16 +174,27 @@ class Model:
               "gpt_tensor_shape")
         return r.value, c.value
 
-    def step(self, tokens, targets) -> float:
-        """tokens/targets: int32 device tensors [batch, seq_len]."""
-        loss = lib().gpt_step(self._h, _ptr(tokens), _ptr(targets), ctypes.byref(self.cfg), _stream())
+    def step(self, tokens, targets, accumulate: bool = False, grad_scale: float = 1.0) -> float:
+        """tokens/targets: int32 device tensors [batch, seq_len].  With the defaults this
+        is gpt_step; otherwise gpt_step_accumulate."""
+        if not accumulate and grad_scale == 1.0:
+            loss = lib().gpt_step(self._h, _ptr(tokens), _ptr(targets), ctypes.byref(self.cfg), _stream())
+            what = "gpt_step"
+        else:
+            loss = lib().gpt_step_accumulate(self._h, _ptr(tokens), _ptr(targets), ctypes.byref(self.cfg),
+                                             int(bool(accumulate)), float(grad_scale), _stream())
+            what = "gpt_step_accumulate"
         st = lib().gpt_last_status(self._h)
         if st != 0:
-            raise GptError(f"gpt_step: {lib().gpt_status_str(st).decode()} ({st})")
+            raise GptError(f"{what}: {lib().gpt_status_str(st).decode()} ({st})")
         return loss
 
     def muon_update(self, lr: float):
         check(lib().muon_update(self._h, float(lr), _stream()), "muon_update")
+
+    def adamw_update(self, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float):
+        check(lib().adamw_update(self._h, float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                                 _stream()), "adamw_update")
 
     def _host_io(self, fn, tid, arr=None):
         r, c = self.shape(tid)

@@ -553,7 +553,8 @@ __global__ void __launch_bounds__(64) sc_segsum_kernel(const int32_t* tok, const
   }
 }
 
-__global__ void __launch_bounds__(64) sc_combine_kernel(const int* offsets, const float* partial, int d, float* dE) {
+__global__ void __launch_bounds__(64) sc_combine_kernel(const int* offsets, const float* partial, int d, float* dE,
+                                                        int accumulate) {
   const int v = blockIdx.x;
   const int c = blockIdx.y * 256 + threadIdx.x * 4;
   if (c >= d) return;
@@ -566,7 +567,12 @@ __global__ void __launch_bounds__(64) sc_combine_kernel(const int* offsets, cons
       acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
     }
   }
-  *reinterpret_cast<float4*>(dE + (long)v * d + c) = acc;
+  float4* out = reinterpret_cast<float4*>(dE + (long)v * d + c);
+  if (accumulate) {
+    const float4 o = *out;
+    acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+  }
+  *out = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -610,6 +616,45 @@ __global__ void momentum_kernel(float* __restrict__ m, const float* __restrict__
     reinterpret_cast<float4*>(m)[i] = a;
   }
   for (size_t i = n4 * 4 + t; i < n; i += stride) m[i] = mu * m[i] + g[i];
+}
+
+// AdamW on one flat fp32 tensor: m, v moments; rbc1 = 1 / (1 - b1^t), rbc2 = 1 / (1 - b2^t);
+// the decay acts on the weight before the step; wa (optional) receives the new weight
+// in the activation type
+template <typename T>
+__global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ w, const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v, T* __restrict__ wa,
+                                                    size_t n, float lr, float b1, float b2, float eps, float wd,
+                                                    float rbc1, float rbc2) {
+  auto one = [&](float& wi, float gi, float& mi, float& vi) {
+    mi = b1 * mi + (1.f - b1) * gi;
+    vi = b2 * vi + (1.f - b2) * gi * gi;
+    wi = wi - lr * wd * wi - lr * (mi * rbc1) / (sqrtf(vi * rbc2) + eps);
+  };
+  const size_t stride = (size_t)gridDim.x * blockDim.x, t = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t n4 = n / 4;
+  for (size_t i = t; i < n4; i += stride) {
+    float4 w4 = reinterpret_cast<float4*>(w)[i], m4 = reinterpret_cast<float4*>(m)[i],
+           v4 = reinterpret_cast<float4*>(v)[i];
+    const float4 g4 = reinterpret_cast<const float4*>(g)[i];
+    one(w4.x, g4.x, m4.x, v4.x);
+    one(w4.y, g4.y, m4.y, v4.y);
+    one(w4.z, g4.z, m4.z, v4.z);
+    one(w4.w, g4.w, m4.w, v4.w);
+    reinterpret_cast<float4*>(w)[i] = w4;
+    reinterpret_cast<float4*>(m)[i] = m4;
+    reinterpret_cast<float4*>(v)[i] = v4;
+    if (wa) {
+      st<T>(wa + 4 * i, w4.x);
+      st<T>(wa + 4 * i + 1, w4.y);
+      st<T>(wa + 4 * i + 2, w4.z);
+      st<T>(wa + 4 * i + 3, w4.w);
+    }
+  }
+  for (size_t i = n4 * 4 + t; i < n; i += stride) {
+    one(w[i], g[i], m[i], v[i]);
+    if (wa) st<T>(wa + i, w[i]);
+  }
 }
 
 __global__ void __launch_bounds__(256) sumsq_part_kernel(const float* __restrict__ x, const long* offs,
@@ -1015,7 +1060,7 @@ size_t embed_ws_bytes(int N, int V, int d) {
 }
 
 void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws,
-                          int32_t* sorted_out, hipStream_t st) {
+                          int32_t* sorted_out, hipStream_t st, bool accumulate) {
   const int P = (N + SC_CHUNK - 1) / SC_CHUNK;
   char* w = (char*)ws;
   int* table = (int*)w; w += al256((size_t)P * V * 4);
@@ -1034,7 +1079,8 @@ void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N,
     hipLaunchKernelGGL(sc_segsum_kernel, dim3((N + SC_SEG - 1) / SC_SEG, (d + 255) / 256), dim3(64), 0, st, tok,
                        sorted, offsets + V, dh, d, partial);
   }
-  hipLaunchKernelGGL(sc_combine_kernel, dim3(V, (d + 255) / 256), dim3(64), 0, st, offsets, partial, d, dE);
+  hipLaunchKernelGGL(sc_combine_kernel, dim3(V, (d + 255) / 256), dim3(64), 0, st, offsets, partial, d, dE,
+                     (int)accumulate);
 }
 
 void launch_cast_f32_to_act(const float* x, void* y, int at, size_t n, hipStream_t st) {
@@ -1081,6 +1127,18 @@ void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int
     hipLaunchKernelGGL(muon_apply_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, rows, cols, (int)tr);
   else
     hipLaunchKernelGGL(muon_apply_kernel<float>, g, b, 0, st, w, (float*)wa, x, lr, rows, cols, (int)tr);
+}
+
+void launch_adamw(float* w, const float* g, float* m, float* v, void* w_act, int act_type, size_t n, float lr,
+                  float b1, float b2, float eps, float wd, float rbc1, float rbc2, hipStream_t st) {
+  if (n == 0) return;
+  const dim3 grid(grid_for((n + 3) / 4)), block(256);
+  if (act_type == ACT_BF16)
+    hipLaunchKernelGGL(adamw_kernel<bf16_t>, grid, block, 0, st, w, g, m, v, (bf16_t*)w_act, n, lr, b1, b2, eps, wd,
+                       rbc1, rbc2);
+  else
+    hipLaunchKernelGGL(adamw_kernel<float>, grid, block, 0, st, w, g, m, v, (float*)w_act, n, lr, b1, b2, eps, wd,
+                       rbc1, rbc2);
 }
 
 void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st) {

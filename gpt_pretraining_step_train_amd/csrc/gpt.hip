@@ -50,7 +50,7 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 }
 
 struct Offsets {
-  size_t params, grads, mom, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
+  size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
       xq8t, amax, qinv;
@@ -92,6 +92,8 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.params = P.add((nE + nBlk + nU) * 4);
   O.grads = P.add((nE + nBlk + nU) * 4);
   O.mom = P.add(nBlk * 4);
+  O.adam_m = P.add((nE + nU) * 4);  // AdamW moments of E then U
+  O.adam_v = P.add((nE + nU) * 4);
   O.wact = es == 2 ? P.add(nBlk * es) : 0;
   O.uact = es == 2 ? P.add(nU * es) : 0;
   O.hs = P.add((2 * L + 1) * N * d * 4);
@@ -180,6 +182,8 @@ struct gpt_model {
   bool fp8 = false;
   bool wq_dirty = true;  // fp8 weight copies must be refreshed before the next step
   int qslot = 0;         // next quantisation slot of the current step
+  long adam_t = 0;       // AdamW steps taken (bias corrections use the next one)
+  bool acc_grads = false;  // the current step adds its gradients to the stored ones
   std::vector<int> xslot;  // per weight: quantisation slot of its input in this step's forward
   // matrix table for Muon, in layer order (q, k, v, o, w1, w2)
   std::vector<long> moff, msize;
@@ -394,6 +398,8 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
     launch_fill_normal(M->params() + off, (size_t)r * c, seed, (uint64_t)id, sd, st);
   }
   launch_zero(M->at_off<float>(O.mom), M->nBlk * 4, st);
+  launch_zero(M->at_off<float>(O.adam_m), (M->nE + M->nU) * 4, st);
+  launch_zero(M->at_off<float>(O.adam_v), (M->nE + M->nU) * 4, st);
   launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU) * 4, st);
   refresh_act(M, st);
   launch_rope_table(M->at_off<float>(O.rope), cfg->seq_len, cfg->head_dim, cfg->rope_base, st);
@@ -503,6 +509,7 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
   GemmArgs pw;
   pw.M = nout; pw.N = kin; pw.K = N;
   pw.outF = dW; pw.ldo = kin;
+  if (M->acc_grads) { pw.Cin = dW; pw.ldcin = kin; pw.beta = 1.f; }  // dW += dY^T X (same thread reads and writes)
   const bool f8w = M->fp8 && (M->cfg.fp8_gemms & GPT_FP8_WGRAD);
   const bool f8d = M->fp8 && (M->cfg.fp8_gemms & GPT_FP8_DGRAD);
   uint8_t* q8a = M->at_off<uint8_t>(M->off.q8a);
@@ -534,7 +541,7 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
   return run_gemm(M, pd, st, false);
 }
 
-static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, hipStream_t st) {
+static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
   const gpt_cfg& c = M->cfg;
   const int N = M->N, d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth, H = c.n_head, hd = c.head_dim;
   const int B = c.batch, T = c.seq_len;
@@ -609,8 +616,9 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     p.outF = logits; p.ldo = V;
     if ((rc = lin_fwd(M, p, 4 * L, st))) return rc;
   }
+  // the whole backward is linear in dlogits: grad_scale / N there scales every gradient
   launch_cross_entropy(logits, tgt, dlogits, at, M->at_off<float>(O.row_loss), M->at_off<int32_t>(O.argmax), N, V,
-                       1.f / (float)N, err, st);
+                       grad_scale / (float)N, err, st);
   launch_sum_rows(M->at_off<float>(O.row_loss), N, M->at_off<double>(O.loss), st);
 
   // ---------------- backward
@@ -672,16 +680,23 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
                        at, N, d, eps, st);
     cur ^= 1;
   }
-  launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st);
+  launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st, M->acc_grads);
   return GPT_OK;
 }
 
 float gpt_step(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg, void* stream) {
+  return gpt_step_accumulate(M, tok, tgt, cfg, 0, 1.f, stream);
+}
+
+float gpt_step_accumulate(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg,
+                          int32_t accumulate, float grad_scale, void* stream) {
   if (!M) return NAN;
-  if (!tok || !tgt) { M->last_status = GPT_ERR_ARG; return NAN; }
+  if (!tok || !tgt || !std::isfinite(grad_scale)) { M->last_status = GPT_ERR_ARG; return NAN; }
   if (cfg && !same_shape(*cfg, M->cfg)) { M->last_status = GPT_ERR_SHAPE; return NAN; }
   hipStream_t st = (hipStream_t)stream;
-  int rc = forward_backward(M, tok, tgt, st);
+  M->acc_grads = accumulate != 0;
+  int rc = forward_backward(M, tok, tgt, grad_scale, st);
+  M->acc_grads = false;
   if (rc) { M->last_status = rc; return NAN; }
   struct { double loss; int err[4]; } h;
   if (hipGetLastError() != hipSuccess ||
@@ -696,6 +711,26 @@ float gpt_step(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_c
   if (h.err[0] & 2) { M->last_status = GPT_ERR_NONFINITE; return NAN; }
   M->last_status = GPT_OK;
   return (float)(h.loss / (double)M->N);
+}
+
+int adamw_update(gpt_model* M, float lr, float beta1, float beta2, float eps, float weight_decay, void* stream) {
+  if (!M) return GPT_ERR_ARG;
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) || !std::isfinite(eps) ||
+      !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return GPT_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const long t = ++M->adam_t;
+  const float rbc1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)t)));
+  const float rbc2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)t)));
+  float* m = M->at_off<float>(M->off.adam_m);
+  float* v = M->at_off<float>(M->off.adam_v);
+  const size_t uo = M->nE + M->nBlk;  // U's offset in the parameter and gradient tables
+  launch_adamw(M->params(), M->grads(), m, v, nullptr, M->at, M->nE, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2,
+               st);
+  launch_adamw(M->params() + uo, M->grads() + uo, m + M->nE, v + M->nE, M->at == ACT_BF16 ? M->uact() : nullptr, M->at,
+               M->nU, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2, st);
+  M->wq_dirty = true;  // the e4m3 copies of U follow the master weights
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
 int muon_update(gpt_model* M, float lr, void* stream) {

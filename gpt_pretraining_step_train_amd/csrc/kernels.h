@@ -74,10 +74,10 @@ void launch_cross_entropy(const float* logits, const int32_t* targets, void* dlo
                           hipStream_t st);
 void launch_sum_rows(const float* x, int n, double* out, hipStream_t st);
 // deterministic embedding backward: dE[v] = sum over positions n with tok[n]==v of dh[n], summed in
-// increasing n.  ws must hold embed_ws_bytes(N, V, d).
+// increasing n (accumulate: added to dE's previous value).  ws must hold embed_ws_bytes(N, V, d).
 size_t embed_ws_bytes(int N, int V, int d);
 void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d,
-                          void* ws, int32_t* sorted_out, hipStream_t st);
+                          void* ws, int32_t* sorted_out, hipStream_t st, bool accumulate = false);
 void launch_cast_f32_to_act(const float* x, void* y, int act_type, size_t n, hipStream_t st);
 void launch_fill_normal(float* w, size_t n, uint64_t seed, uint64_t stream_id, float stddev,
                         hipStream_t st);
@@ -85,6 +85,10 @@ void launch_zero(void* p, size_t bytes, hipStream_t st);
 
 // Muon pieces
 void launch_momentum(float* mom, const float* g, float mu, size_t n, hipStream_t st);
+// AdamW on n fp32 weights with fp32 moments (rbc1/rbc2: reciprocal bias corrections);
+// w_act (optional, act_type) receives the updated weights
+void launch_adamw(float* w, const float* g, float* m, float* v, void* w_act, int act_type, size_t n, float lr,
+                  float b1, float b2, float eps, float wd, float rbc1, float rbc2, hipStream_t st);
 // per-matrix sum of squares of mom; matrix i occupies [offs[i], offs[i]+sizes[i])
 void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, int nmat, double* partial,
                          int parts, double* out, hipStream_t st);

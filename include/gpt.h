@@ -108,6 +108,18 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* d_arena, size_t arena_byte
  * match the model's configuration. */
 float gpt_step(gpt_model* m, const int32_t* d_tokens, const int32_t* d_targets, const gpt_cfg* cfg, void* stream);
 
+/* gpt_step for gradient accumulation over micro-batches (the single-GPU mode of the
+ * nanochat articles, which run the optimizer once per total batch): every gradient
+ * of this micro-batch's mean loss is multiplied by grad_scale (1/number of
+ * micro-batches gives the mean over the total batch) and, when accumulate != 0,
+ * added to the stored gradients instead of replacing them.  The scale enters at
+ * the loss gradient, which the whole backward is linear in.  Returns the
+ * micro-batch's own mean loss; NaN and GPT_ERR_ARG for a non-finite grad_scale.
+ * After an error the stored gradients are undefined.
+ * gpt_step(m, t, y, cfg, s) is gpt_step_accumulate(m, t, y, cfg, 0, 1, s). */
+float gpt_step_accumulate(gpt_model* m, const int32_t* d_tokens, const int32_t* d_targets, const gpt_cfg* cfg,
+                          int32_t accumulate, float grad_scale, void* stream);
+
 /* Copy the fp32 gradient of tensor `tensor_id` (n elements) to host memory. */
 int gpt_grads(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* stream);
 
@@ -116,6 +128,19 @@ int gpt_grads(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* str
  * A = X X^T, X <- a X + (b A + c A^2) X on the wide orientation; W <- W - lr X.
  * E and U are not touched.  Stream-ordered, no synchronisation. */
 int muon_update(gpt_model* m, float lr, void* stream);
+
+/* AdamW on the token embedding E and the LM head U (the tensors Muon leaves to it,
+ * per the parameter-type table of "2. Muon Optimize Edici" in the nanochat
+ * articles; they print no formula or hyperparameters, so Adam's bias-corrected
+ * moments with decoupled weight decay are used).  For the t-th call on this model,
+ * with g the gradient of the last gpt_step:
+ *   m <- beta1 m + (1-beta1) g;  v <- beta2 v + (1-beta2) g^2;
+ *   w <- w - lr wd w - lr (m / (1-beta1^t)) / (sqrt(v / (1-beta2^t)) + eps)
+ * on the fp32 masters (bf16 copies refreshed).  Moments live in the arena, zero
+ * after gpt_init.  GPT_ERR_ARG for a beta outside [0, 1), negative or non-finite
+ * eps, or non-finite lr / weight_decay (the step counter is not advanced then).
+ * Stream-ordered, no synchronisation. */
+int adamw_update(gpt_model* m, float lr, float beta1, float beta2, float eps, float weight_decay, void* stream);
 
 /* Device copy of the argmax over the vocabulary of every position's logits of the
  * last gpt_step (lowest index among equal maxima), int32 [batch*seq_len]. */
