@@ -22,6 +22,8 @@
 // dK and dV accumulators live in different waves.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,7 +51,8 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // sizes use rows padded by 16 bytes.
 template <int HD>
 struct Tile {
-  static constexpr int ELEMS = HD == 128 ? 64 * 128 : 64 * (HD + 8);
+  static constexpr int RS = HD == 128 ? 128 : HD + 8;  // row stride (elements)
+  static constexpr int ELEMS = 64 * RS;
   __device__ static inline int off(int r, int d) {
     if constexpr (HD == 128) {
       const int swz = ((r & 3) << 2) | ((r >> 2) & 3);
@@ -97,19 +100,101 @@ struct RowStager {
 
 __device__ inline bf16x8_t lds_row8(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
+// transpose-read operand from two precomputed LDS addresses (rows r and r + 8 of
+// the tile_tr_operand layout)
+__device__ inline bf16x8_t lds_tr_pair(const bf16_t* lo, const bf16_t* hi) {
+  const i16x4_t a = lds_read_tr16(lo);
+  const i16x4_t b = lds_read_tr16(hi);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Block coordinates (bx within a sequence-head, by = sequence-head) such that all
+// blocks of one sequence-head run on one XCD, one after another: workgroups go to the
+// 8 XCDs round-robin in linear launch order, so the K/V (or Q/dO) tiles every block of
+// a head streams stay in that XCD's L2.  Plain coordinates when gridDim.y % 8 != 0.
+__device__ inline void head_major_coords(int& bx, int& by) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  if (ny % 8 != 0) {
+    bx = blockIdx.x;
+    by = blockIdx.y;
+    return;
+  }
+  const int lin = blockIdx.y * nx + blockIdx.x, j = lin >> 3;
+  by = (j / nx) * 8 + (lin & 7);
+  bx = j % nx;
+}
+
+__device__ inline f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Buffer descriptor over rows [row0, T) of a row-major [T][ld] bf16 matrix of which
+// HD columns are read: a 16-byte load of a row at or past T returns zeros.
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const bf16_t* base, long ld, int row0, int T, int HD) {
+  const uint32_t bytes = row0 < T ? (uint32_t)(((long)(T - row0 - 1) * ld + HD) * 2) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base + (long)row0 * ld), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// two [64 rows][HD] bf16 tiles staged global -> registers -> LDS by NT threads; the
+// per-thread global byte offsets (from the tile's first row) and LDS offsets are
+// loop-invariant, each tile's rows come from a buffer descriptor that starts there
+template <int HD, int NT>
+struct PairStager {
+  static constexpr int CPR = HD / 8, NCH = 64 * CPR, PER = (NCH + NT - 1) / NT;
+  uint32_t vo[PER];
+  int lo[PER];
+  uint4 a[PER], b[PER];
+  __device__ inline void init(long ld, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = min(tid + i * NT, NCH - 1), row = c / CPR, cc = c % CPR;
+      vo[i] = (uint32_t)(((long)row * ld + cc * 8) * 2);
+      lo[i] = Tile<HD>::off(row, cc * 8);
+    }
+  }
+  __device__ inline void load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (NCH % NT != 0 && tid + i * NT >= NCH) continue;
+      a[i] = buf16(ra, vo[i]);
+      b[i] = buf16(rb, vo[i]);
+    }
+  }
+  __device__ inline void store(bf16_t* ta, bf16_t* tb, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (NCH % NT != 0 && tid + i * NT >= NCH) continue;
+      *reinterpret_cast<uint4*>(ta + lo[i]) = a[i];
+      *reinterpret_cast<uint4*>(tb + lo[i]) = b[i];
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // forward
 
 template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H) {
-  constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+  constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int nqb = (T + BQ - 1) / BQ;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // longest causal rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int bx, bh;
+  head_major_coords(bx, bh);
+  const int qb = nqb - 1 - bx;  // longest causal rows first
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * H * HD;
   const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
   const bf16_t* K = Q + (long)H * HD;
@@ -126,37 +211,45 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   }
   f32x16_t oacc[NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
   float m = -INFINITY, l = 0.f;  // running reference maximum (log2 units) and sum
   const float sl2 = LOG2E / sqrtf((float)HD);
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
 
-  RowStager<HD> ks, vs;
-  ks.load(K, ld, 0, T, tid);
-  vs.load(V, ld, 0, T, tid);
-  ks.store(Ks[0], tid);
-  vs.store(Vs[0], tid);
+  // Per-lane LDS element offsets, loop-invariant: every fragment's tile row origin is
+  // a multiple of 16, where the swizzle repeats, so it enters as an immediate.
+  int kro[NKK];  // K rows for S^T: row lq, columns kk*16 + 8hl ...
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int vro[NDB][2];  // V^T by transpose reads: rows trr and trr + 8 of a 16-row block
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    vro[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    vro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
+
+  PairStager<HD, 256> stg;
+  stg.init(ld, tid);
+  stg.load(rows_rsrc(K, ld, 0, T, HD), rows_rsrc(V, ld, 0, T, HD), tid);
+  stg.store(Ks[0], Vs[0], tid);
   __syncthreads();
 
-  for (int it = 0; it < nkv; ++it) {
-    const int cur = it & 1, k0 = it * BKV;
-    if (it + 1 < nkv) {
-      ks.load(K, ld, k0 + BKV, T, tid);
-      vs.load(V, ld, k0 + BKV, T, tid);
-    }
+  // one KV tile; the LDS buffer index is a compile-time constant (loop unrolled by 2)
+  auto body = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int k0 = it * BKV;
+    if (it + 1 < nkv) stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
     if (k0 <= q0 + 31 && q0 < T) {
       f32x16_t s[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16_t* kp = Ks[cur] + kb2 * 32 * RS;
+        s[kb2] = mfma32x32x16_bf16(lds_row8(kp + kro[0]), qf[0], zero16());
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          s[kb2] = mfma32x32x16_bf16(lds_row8(Ks[cur] + Tile<HD>::off(kb2 * 32 + lq, kk * 16 + hl * 8)), qf[kk],
-                                     s[kb2]);
+        for (int kk = 1; kk < NKK; ++kk) s[kb2] = mfma32x32x16_bf16(lds_row8(kp + kro[kk]), qf[kk], s[kb2]);
       }
       if (k0 + BKV - 1 > q0 || k0 + BKV > T) {  // diagonal or ragged tile: mask
 #pragma unroll
@@ -202,16 +295,18 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 #pragma unroll
           for (int j = 0; j < 8; ++j) pv[j] = s[kb2][8 * s_ + j];
           const bf16x8_t pb = pack8(pv);
+          const bf16_t* vp = Vs[cur] + (kb2 * 32 + 16 * s_) * RS;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            oacc[db] = mfma32x32x16_bf16(tile_tr_operand<HD>(Vs[cur], kb2 * 32 + 16 * s_, db * 32, lane), pb, oacc[db]);
+            oacc[db] = mfma32x32x16_bf16(lds_tr_pair(vp + vro[db][0], vp + vro[db][1]), pb, oacc[db]);
         }
     }
-    if (it + 1 < nkv) {
-      ks.store(Ks[cur ^ 1], tid);
-      vs.store(Vs[cur ^ 1], tid);
-    }
+    if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
     __syncthreads();
+  };
+  for (int it = 0; it < nkv; it += 2) {
+    body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
   if (myq < T) {
     const float inv = 1.f / l;
@@ -266,8 +361,10 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int nqb = (T + BQ - 1) / BQ;
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int bx, bh;
+  head_major_coords(bx, bh);
+  const int qb = nqb - 1 - bx;
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * H * HD, ldo = (long)H * HD;
   const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
   const bf16_t* K = Q + (long)H * HD;
@@ -379,8 +476,9 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const bool dk_role = wave >= 4;
   const int kw = wave & 3;
-  const int kb = blockIdx.x;  // lowest key blocks carry the most query tiles: launched first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int kb, bh;
+  head_major_coords(kb, bh);  // lowest key blocks carry the most query tiles: launched first
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * H * HD, ldo = (long)H * HD;
   const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
   const bf16_t* K = Q + (long)H * HD;
