@@ -17,9 +17,10 @@
 // maximum is only raised when a tile's maximum exceeds it by more than 2^8 in
 // probability (exponents stay <= 8), so the accumulator rescale is rare.
 //
-// Backward, without atomics: D = rowsum(dO*O); a dQ kernel per query block
-// (recomputing P and dP) and a dK/dV kernel per key block (over query tiles) whose
-// dK and dV accumulators live in different waves.
+// Backward, without atomics: a dQ kernel per query block (recomputing P and dP; it
+// also forms D = rowsum(dO*O) for its queries) and then a dK/dV kernel per key block
+// (over query tiles) whose dK and dV accumulators live in different waves.  Blocks
+// of one sequence-head run on one XCD, so the tiles they stream stay in its L2.
 #include <math.h>
 
 #include <type_traits>
@@ -151,14 +152,15 @@ __device__ inline uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 template <int HD, int NT>
 struct PairStager {
   static constexpr int CPR = HD / 8, NCH = 64 * CPR, PER = (NCH + NT - 1) / NT;
-  uint32_t vo[PER];
+  uint32_t voa[PER], vob[PER];
   int lo[PER];
   uint4 a[PER], b[PER];
-  __device__ inline void init(long ld, int tid) {
+  __device__ inline void init(long lda, long ldb, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = min(tid + i * NT, NCH - 1), row = c / CPR, cc = c % CPR;
-      vo[i] = (uint32_t)(((long)row * ld + cc * 8) * 2);
+      voa[i] = (uint32_t)(((long)row * lda + cc * 8) * 2);
+      vob[i] = (uint32_t)(((long)row * ldb + cc * 8) * 2);
       lo[i] = Tile<HD>::off(row, cc * 8);
     }
   }
@@ -166,8 +168,8 @@ struct PairStager {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (NCH % NT != 0 && tid + i * NT >= NCH) continue;
-      a[i] = buf16(ra, vo[i]);
-      b[i] = buf16(rb, vo[i]);
+      a[i] = buf16(ra, voa[i]);
+      b[i] = buf16(rb, vob[i]);
     }
   }
   __device__ inline void store(bf16_t* ta, bf16_t* tb, int tid) {
@@ -232,7 +234,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   }
 
   PairStager<HD, 256> stg;
-  stg.init(ld, tid);
+  stg.init(ld, ld, tid);
   stg.load(rows_rsrc(K, ld, 0, T, HD), rows_rsrc(V, ld, 0, T, HD), tid);
   stg.store(Ks[0], Vs[0], tid);
   __syncthreads();
@@ -354,9 +356,9 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const T* __restrict_
 // tiles up to the diagonal.  dQ^T += K^T dS^T with K^T read by transpose.
 template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
-                   const float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H) {
-  constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dO,
+                   const float* __restrict__ lse, float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H) {
+  constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
@@ -372,52 +374,71 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
   const bf16_t* G = dO + (long)b * T * ldo + h * HD;
   const int q0 = qb * BQ + wave * 32, myq = q0 + lq;
 
+  // the query's q and dO rows (lane half hl holds 8-element chunks 2kk + hl), and
+  // D = rowsum(dO * O), which this kernel also writes for the dK/dV kernel
+  const bf16_t* O = o + (long)b * T * ldo + h * HD;
   bf16x8_t qf[NKK], gf[NKK];
+  float dsum = 0.f;
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    uint4 u = make_uint4(0, 0, 0, 0), w = u;
+    uint4 u = make_uint4(0, 0, 0, 0), w = u, x = u;
     if (myq < T) {
       u = *reinterpret_cast<const uint4*>(Q + (long)myq * ld + kk * 16 + hl * 8);
       w = *reinterpret_cast<const uint4*>(G + (long)myq * ldo + kk * 16 + hl * 8);
+      x = *reinterpret_cast<const uint4*>(O + (long)myq * ldo + kk * 16 + hl * 8);
     }
     qf[kk] = __builtin_bit_cast(bf16x8_t, u);
     gf[kk] = __builtin_bit_cast(bf16x8_t, w);
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w}, xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dsum += __uint_as_float(wv[e] << 16) * __uint_as_float(xv[e] << 16) +
+              __uint_as_float(wv[e] & 0xFFFF0000u) * __uint_as_float(xv[e] & 0xFFFF0000u);
   }
+  const float Dq = dsum + __shfl_xor(dsum, 32, 64);
+  if (hl == 0 && myq < T) Dv[(long)bh * T + myq] = Dq;
   const float sl2 = LOG2E / sqrtf((float)HD);
   const float lse2 = myq < T ? lse[(long)bh * T + myq] * LOG2E : 0.f;
-  const float Dq = myq < T ? Dv[(long)bh * T + myq] : 0.f;
   f32x16_t acc[NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i)
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  // per-lane LDS element offsets, loop-invariant (row origins are multiples of 16)
+  int kro[NKK];  // K and V rows for S^T and dP^T
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int kk = 0; kk < NKK; ++kk) kro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int ktr[NDB][2];  // K^T by transpose reads
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ktr[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    ktr[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
 
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
-  RowStager<HD> sk, sv;
-  sk.load(K, ld, 0, T, tid);
-  sv.load(V, ld, 0, T, tid);
-  sk.store(Ks[0], tid);
-  sv.store(Vs[0], tid);
+  PairStager<HD, 256> stg;
+  stg.init(ld, ld, tid);
+  stg.load(rows_rsrc(K, ld, 0, T, HD), rows_rsrc(V, ld, 0, T, HD), tid);
+  stg.store(Ks[0], Vs[0], tid);
   __syncthreads();
-  for (int it = 0; it < nkv; ++it) {
-    const int cur = it & 1, k0 = it * BKV;
-    if (it + 1 < nkv) {
-      sk.load(K, ld, k0 + BKV, T, tid);
-      sv.load(V, ld, k0 + BKV, T, tid);
-    }
+  auto body = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int k0 = it * BKV;
+    if (it + 1 < nkv) stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
     if (k0 <= q0 + 31 && q0 < T) {
       const bool mask = k0 + BKV - 1 > q0 || k0 + BKV > T;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        f32x16_t s, dp;
+        const bf16_t* kp = Ks[cur] + kb2 * 32 * RS;
+        const bf16_t* vp = Vs[cur] + kb2 * 32 * RS;
+        f32x16_t s = mfma32x32x16_bf16(lds_row8(kp + kro[0]), qf[0], zero16());
+        f32x16_t dp = mfma32x32x16_bf16(lds_row8(vp + kro[0]), gf[0], zero16());
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const int o = Tile<HD>::off(kb2 * 32 + lq, kk * 16 + hl * 8);
-          s = mfma32x32x16_bf16(lds_row8(Ks[cur] + o), qf[kk], s);
-          dp = mfma32x32x16_bf16(lds_row8(Vs[cur] + o), gf[kk], dp);
+        for (int kk = 1; kk < NKK; ++kk) {
+          s = mfma32x32x16_bf16(lds_row8(kp + kro[kk]), qf[kk], s);
+          dp = mfma32x32x16_bf16(lds_row8(vp + kro[kk]), gf[kk], dp);
         }
         if (mask) {
 #pragma unroll
@@ -432,17 +453,19 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
 #pragma unroll
         for (int s_ = 0; s_ < 2; ++s_) {
           const bf16x8_t db8 = pack8(ds + 8 * s_);
+          const bf16_t* tp = kp + 16 * s_ * RS;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            acc[db] = mfma32x32x16_bf16(tile_tr_operand<HD>(Ks[cur], kb2 * 32 + 16 * s_, db * 32, lane), db8, acc[db]);
+            acc[db] = mfma32x32x16_bf16(lds_tr_pair(tp + ktr[db][0], tp + ktr[db][1]), db8, acc[db]);
         }
       }
     }
-    if (it + 1 < nkv) {
-      sk.store(Ks[cur ^ 1], tid);
-      sv.store(Vs[cur ^ 1], tid);
-    }
+    if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
     __syncthreads();
+  };
+  for (int it = 0; it < nkv; it += 2) {
+    body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
   if (myq < T) {
     const float sc = 1.f / sqrtf((float)HD);
@@ -469,7 +492,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
                            const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
                            int T, int H) {
-  constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, NDB = HD / 32, NKK = HD / 16;
+  constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
   __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
@@ -500,61 +523,66 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   const float sl2 = LOG2E / sqrtf((float)HD);
   f32x16_t acc[NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i)
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  // per-lane LDS element offsets, loop-invariant (row origins are multiples of 16)
+  int qro[NKK];  // Q and dO rows for S^T and dP^T
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int kk = 0; kk < NKK; ++kk) qro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int tro[NDB][2];  // dO (dV waves) or Q (dK waves) by transpose reads
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    tro[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    tro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
 
   const int nqt = (T + BQT - 1) / BQT;
   const int qt0 = (kb * BKEY) / BQT;
-  // 64-row tiles staged by 512 threads (two 16-byte chunks each per tile)
-  constexpr int NCH = 64 * HD / 8, PER = (NCH + 511) / 512;
-  uint4 rq[PER], rg[PER];
+  // 64-row Q and dO tiles and their lse / D values, prefetched one tile ahead
+  PairStager<HD, 512> stg;
+  stg.init(ld, ldo, tid);
+  float pl = 0.f, pd = 0.f;
   auto load = [&](int q0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 512, row = c / (HD / 8), cc = c % (HD / 8);
-      const bool ok = c < NCH && q0 + row < T;
-      rq[i] = ok ? *reinterpret_cast<const uint4*>(Q + (long)(q0 + row) * ld + cc * 8) : make_uint4(0, 0, 0, 0);
-      rg[i] = ok ? *reinterpret_cast<const uint4*>(G + (long)(q0 + row) * ldo + cc * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf, int q0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 512, row = c / (HD / 8), cc = c % (HD / 8);
-      if (NCH % 512 != 0 && c >= NCH) continue;
-      *reinterpret_cast<uint4*>(Qs[buf] + Tile<HD>::off(row, cc * 8)) = rq[i];
-      *reinterpret_cast<uint4*>(Gs[buf] + Tile<HD>::off(row, cc * 8)) = rg[i];
-    }
+    stg.load(rows_rsrc(Q, ld, q0, T, HD), rows_rsrc(G, ldo, q0, T, HD), tid);
     if (tid < BQT) {
       const int q = q0 + tid;
-      L2s[buf][tid] = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
-      Ds[buf][tid] = q < T ? Dv[(long)bh * T + q] : 0.f;
+      pl = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
+      pd = q < T ? Dv[(long)bh * T + q] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    stg.store(Qs[buf], Gs[buf], tid);
+    if (tid < BQT) {
+      L2s[buf][tid] = pl;
+      Ds[buf][tid] = pd;
     }
   };
   if (qt0 < nqt) {
     load(qt0 * BQT);
-    store(0, qt0 * BQT);
+    store(0);
   }
   __syncthreads();
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int cur = (qt - qt0) & 1, qb0 = qt * BQT;
+  auto body = [&](auto cur_c, int qt) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int qb0 = qt * BQT;
     if (qt + 1 < nqt) load(qb0 + BQT);
     if (qb0 + BQT - 1 >= key0 && key0 < T) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         if (qb0 + qs * 32 + 31 < key0) continue;
         const bool mask = qb0 + qs * 32 < key0 + 31;
-        f32x16_t sc, dp;
+        const bf16_t* qp = Qs[cur] + qs * 32 * RS;
+        const bf16_t* gp = Gs[cur] + qs * 32 * RS;
+        f32x16_t sc = mfma32x32x16_bf16(lds_row8(qp + qro[0]), kf[0], zero16());
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          sc = mfma32x32x16_bf16(lds_row8(Qs[cur] + Tile<HD>::off(qs * 32 + lq, kk * 16 + hl * 8)), kf[kk], sc);
+        for (int kk = 1; kk < NKK; ++kk) sc = mfma32x32x16_bf16(lds_row8(qp + qro[kk]), kf[kk], sc);
+        f32x16_t dp;
         if (dk_role) {
+          dp = mfma32x32x16_bf16(lds_row8(gp + qro[0]), vf[0], zero16());
 #pragma unroll
-          for (int kk = 0; kk < NKK; ++kk)
-            dp = mfma32x32x16_bf16(lds_row8(Gs[cur] + Tile<HD>::off(qs * 32 + lq, kk * 16 + hl * 8)), vf[kk], dp);
+          for (int kk = 1; kk < NKK; ++kk) dp = mfma32x32x16_bf16(lds_row8(gp + qro[kk]), vf[kk], dp);
         }
         if (mask) {
 #pragma unroll
@@ -582,18 +610,23 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
         }
         // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves), the second operand read
         // by transpose from its row-major tile
-        const bf16_t* src = dk_role ? Qs[cur] : Gs[cur];
+        const bf16_t* src = (dk_role ? Qs[cur] : Gs[cur]) + qs * 32 * RS;
 #pragma unroll
         for (int s_ = 0; s_ < 2; ++s_) {
           const bf16x8_t wa = pack8(w + 8 * s_);
+          const bf16_t* tp = src + 16 * s_ * RS;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            acc[db] = mfma32x32x16_bf16(wa, tile_tr_operand<HD>(src, qs * 32 + 16 * s_, db * 32, lane), acc[db]);
+            acc[db] = mfma32x32x16_bf16(wa, lds_tr_pair(tp + tro[db][0], tp + tro[db][1]), acc[db]);
         }
       }
     }
-    if (qt + 1 < nqt) store(cur ^ 1, qb0 + BQT);
+    if (qt + 1 < nqt) store(cur ^ 1);
     __syncthreads();
+  };
+  for (int qt = qt0; qt < nqt; qt += 2) {
+    body(std::integral_constant<int, 0>{}, qt);
+    if (qt + 1 < nqt) body(std::integral_constant<int, 1>{}, qt + 1);
   }
   const float scale = dk_role ? 1.f / sqrtf((float)HD) : 1.f;
   const long part = dk_role ? (long)H * HD : 2L * H * HD;
@@ -728,11 +761,12 @@ void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, in
 }
 
 template <int HD>
-void bwd_dispatch(const void* qkv, const void* dO, const float* lse, const float* D, void* dqkv, int at, int B, int T,
-                  int H, hipStream_t st) {
+void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
+                  int B, int T, int H, hipStream_t st) {
   if (at == ACT_BF16) {
+    // the dQ kernel also writes D = rowsum(dO * O) for the dK/dV kernel
     hipLaunchKernelGGL(attn_bwd_dq_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st, (const bf16_t*)qkv,
-                       (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
+                       (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
     hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(512), 0, st,
                        (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
   } else {
@@ -756,13 +790,10 @@ void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float
                      int B, int T, int H, int hd, hipStream_t st) {
   if (B * T * H == 0) return;
   const int N = B * T;
-  if (at == ACT_BF16)
-    hipLaunchKernelGGL(attn_bwd_prep_kernel<bf16_t>, dim3((N * H + 3) / 4), dim3(256), 0, st, (const bf16_t*)o,
-                       (const bf16_t*)dO, D, N, T, H, hd);
-  else
+  if (at != ACT_BF16)  // the bf16 dQ kernel forms D itself
     hipLaunchKernelGGL(attn_bwd_prep_kernel<float>, dim3((N * H + 3) / 4), dim3(256), 0, st, (const float*)o,
                        (const float*)dO, D, N, T, H, hd);
-  if (hd == 128) bwd_dispatch<128>(qkv, dO, lse, D, dqkv, at, B, T, H, st);
-  else if (hd == 64) bwd_dispatch<64>(qkv, dO, lse, D, dqkv, at, B, T, H, st);
-  else if (hd == 32) bwd_dispatch<32>(qkv, dO, lse, D, dqkv, at, B, T, H, st);
+  if (hd == 128) bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, st);
+  else if (hd == 64) bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, st);
+  else if (hd == 32) bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, st);
 }
