@@ -483,10 +483,11 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
 }
 
 // dK, dV with the two accumulations in different waves: 8 waves per 128-key block,
-// waves 0-3 accumulate dV (S -> P, dV += P^T dO) and waves 4-7 dK (S, dP -> dS,
-// dK += dS^T Q) for the same 32 keys.  S is computed by both roles, but each wave
-// holds one 32x128 accumulator, so two waves fit on every SIMD; the Q and dO tiles
-// are staged once for all eight.  A lane owns a key.
+// waves 0-3 accumulate dV (S -> P, dV += P^T dO) and waves 4-7 dK (dP, P -> dS,
+// dK += dS^T Q) for the same 32 keys, each role 32 MFMAs per 64-query tile.  P
+// passes from the dV waves to the dK waves through LDS; each wave holds one 32x128
+// accumulator, so two waves fit on every SIMD; the Q and dO tiles are staged once
+// for all eight.  A lane owns a key.
 template <int HD>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
@@ -496,6 +497,7 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
   __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
+  __shared__ __attribute__((aligned(16))) float Ps[2][4][4][64][4];  // [half][key wave][reg/4][lane][reg%4]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const bool dk_role = wave >= 4;
   const int kw = wave & 3;
@@ -564,61 +566,70 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     store(0);
   }
   __syncthreads();
+  // Per query tile, phase 1: the dV waves form S and P = exp(S - lse) for both
+  // 32-query halves and publish P (fp32, lane for lane: both roles hold the same keys
+  // and queries in the same accumulator layout) while the dK waves form dP; phase 2,
+  // after a barrier: dV += P^T dO, and dK += dS^T Q with dS = P (dP - D).
   auto body = [&](auto cur_c, int qt) {
     constexpr int cur = decltype(cur_c)::value;
     const int qb0 = qt * BQT;
     if (qt + 1 < nqt) load(qb0 + BQT);
-    if (qb0 + BQT - 1 >= key0 && key0 < T) {
+    const bool live = qb0 + BQT - 1 >= key0 && key0 < T;  // the same for both roles
+    f32x16_t pd[2];  // P (dV waves) or dP (dK waves) of each 32-query half
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        if (qb0 + qs * 32 + 31 < key0) continue;
-        const bool mask = qb0 + qs * 32 < key0 + 31;
-        const bf16_t* qp = Qs[cur] + qs * 32 * RS;
-        const bf16_t* gp = Gs[cur] + qs * 32 * RS;
-        f32x16_t sc = mfma32x32x16_bf16(lds_row8(qp + qro[0]), kf[0], zero16());
+    for (int qs = 0; qs < 2; ++qs) {
+      if (!live || qb0 + qs * 32 + 31 < key0) continue;
+      const bf16_t* rp = (dk_role ? Gs[cur] : Qs[cur]) + qs * 32 * RS;
+      const bf16x8_t* kv = dk_role ? vf : kf;
+      f32x16_t a = mfma32x32x16_bf16(lds_row8(rp + qro[0]), kv[0], zero16());
 #pragma unroll
-        for (int kk = 1; kk < NKK; ++kk) sc = mfma32x32x16_bf16(lds_row8(qp + qro[kk]), kf[kk], sc);
-        f32x16_t dp;
-        if (dk_role) {
-          dp = mfma32x32x16_bf16(lds_row8(gp + qro[0]), vf[0], zero16());
+      for (int kk = 1; kk < NKK; ++kk) a = mfma32x32x16_bf16(lds_row8(rp + qro[kk]), kv[kk], a);
+      if (!dk_role) {
+        if (qb0 + qs * 32 < key0 + 31) {  // diagonal block: queries before the key
 #pragma unroll
-          for (int kk = 1; kk < NKK; ++kk) dp = mfma32x32x16_bf16(lds_row8(gp + qro[kk]), vf[kk], dp);
+          for (int r = 0; r < 16; ++r)
+            if (qb0 + qs * 32 + acc_row(lane, r) < mykey) a[r] = -INFINITY;
         }
-        if (mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = qb0 + qs * 32 + acc_row(lane, r);
-            if (q < mykey) sc[r] = -INFINITY;
-          }
-        }
-        float w[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {  // registers 4g..4g+3 hold query rows qs*32 + 8g + 4hl + 0..3
-          const int ql = qs * 32 + 8 * g + 4 * hl;
-          const float4 l4 = *reinterpret_cast<const float4*>(&L2s[cur][ql]);
+          const float4 l4 = *reinterpret_cast<const float4*>(&L2s[cur][qs * 32 + 8 * g + 4 * hl]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          if (dk_role) {
-            const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
-            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              w[4 * g + j] = fast_exp2(fmaf(sc[4 * g + j], sl2, -lv[j])) * (dp[4 * g + j] - dv4[j]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[4 * g + j] = fast_exp2(fmaf(sc[4 * g + j], sl2, -lv[j]));
-          }
+          for (int j = 0; j < 4; ++j) a[4 * g + j] = fast_exp2(fmaf(a[4 * g + j], sl2, -lv[j]));
+          *reinterpret_cast<float4*>(&Ps[qs][kw][g][lane][0]) =
+              make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         }
-        // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves), the second operand read
-        // by transpose from its row-major tile
-        const bf16_t* src = (dk_role ? Qs[cur] : Gs[cur]) + qs * 32 * RS;
+      }
+      pd[qs] = a;
+    }
+    __syncthreads();  // P published
 #pragma unroll
-        for (int s_ = 0; s_ < 2; ++s_) {
-          const bf16x8_t wa = pack8(w + 8 * s_);
-          const bf16_t* tp = src + 16 * s_ * RS;
+    for (int qs = 0; qs < 2; ++qs) {
+      if (!live || qb0 + qs * 32 + 31 < key0) continue;
+      float w[16];
+      if (dk_role) {
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            acc[db] = mfma32x32x16_bf16(wa, lds_tr_pair(tp + tro[db][0], tp + tro[db][1]), acc[db]);
+        for (int g = 0; g < 4; ++g) {
+          const float4 p4 = *reinterpret_cast<const float4*>(&Ps[qs][kw][g][lane][0]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][qs * 32 + 8 * g + 4 * hl]);
+          const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[4 * g + j] = pv[j] * (pd[qs][4 * g + j] - dv4[j]);
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w[r] = pd[qs][r];
+      }
+      // dV += P^T dO (dV waves) or dK += dS^T Q (dK waves), the second operand read
+      // by transpose from its row-major tile
+      const bf16_t* src = (dk_role ? Qs[cur] : Gs[cur]) + qs * 32 * RS;
+#pragma unroll
+      for (int s_ = 0; s_ < 2; ++s_) {
+        const bf16x8_t wa = pack8(w + 8 * s_);
+        const bf16_t* tp = src + 16 * s_ * RS;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32x32x16_bf16(wa, lds_tr_pair(tp + tro[db][0], tp + tro[db][1]), acc[db]);
       }
     }
     if (qt + 1 < nqt) store(cur ^ 1);
