@@ -1033,6 +1033,34 @@ int splits_for(const GemmArgs& p, int tm, int tn) {
   return s;
 }
 
+// Split-K factor for the 256x256 kernels (one workgroup per CU, 256 CUs): the one
+// that minimises rounds of 256 workgroups times the k extent of a split, plus the cost
+// of the splits' fp32 partials, with at least 1024 of K per split; ties go to fewer
+// splits.  A last round that is almost empty costs as much as a full one, so e.g. 36
+// tiles take 7 splits (one round), not 16 (three rounds).  The partials (written by
+// the GEMM, read by the reduction: 8 bytes per output element and split at ~5 TB/s)
+// cost about 5.2e-5 of a k step of a bf16 tile round (~31 ns) per output element and
+// split, twice that against the faster fp8 k step; measured on the d24 weight
+// gradients, whose best factors (7, 7, 5, 5) this reproduces.
+int splits_256(const GemmArgs& p) {
+  if (p.epi != EPI_LINEAR) return 1;
+  constexpr long CUS = 256, KQ = 64;  // k extents are rounded to whole k tiles (<= 64)
+  const long tiles = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+  const double part = (p.fp8 ? 2.0 : 1.0) * 5.2e-5 * (double)p.M * p.N * p.batch;
+  double best = -1;
+  int bs = 1;
+  for (int s = 1; s <= 32; ++s) {
+    if (s > 1 && (long)p.K / s < 1024) break;
+    const long kper = ((p.K + s - 1) / s + KQ - 1) / KQ * KQ;
+    const double cost = (double)((tiles * s + CUS - 1) / CUS * kper) + (s > 1 ? s * part : 0.0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      bs = s;
+    }
+  }
+  return bs;
+}
+
 // 1: a 256x256 kernel, 2: the 128x128 kernel.  The 256 tile is used when the
 // problem has >= 128 such tiles, or when split-K over them reaches >= 256
 // workgroups (the long-reduction weight gradients); a pure function of the shape,
@@ -1048,7 +1076,7 @@ int pick_tile(const GemmArgs& p) {
 
 int gemm_auto_splits(const GemmArgs& p) {
   if (p.dtype == ACT_F32) return splits_for(p, 64, 64);
-  if (p.fp8 || pick_tile(p) != 2) return splits_for(p, 256, 256);
+  if (p.fp8 || pick_tile(p) != 2) return splits_256(p);
   return splits_for(p, 128, 128);
 }
 
