@@ -102,12 +102,20 @@ def rope(x, ang, inverse=False):
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
 
 
-def causal_attention(q, k, v):
-    """o[b,i,h] = sum_{j<=i} softmax_j(q_i . k_j / sqrt(hd)) v_j ; q,k,v [B,T,H,hd]."""
+def causal_attention(q, k, v, window=0):
+    """o[b,i,h] = sum_{j<=i} softmax_j(q_i . k_j / sqrt(hd)) v_j ; q,k,v [B,T,H,hd].
+
+    window > 0 restricts query i to the keys i - window < j <= i (sliding-window
+    attention: the articles list it among the model's features and pass a
+    window_size to the flash-attention call, "5. Flash Dikkat Mekanizmasi
+    Birlesimi", without a value; window counts the keys a query sees, itself
+    included, i.e. flash-attention's window_size = (window - 1, 0))."""
     B, T, H, hd = q.shape
     qh, kh, vh = (x.transpose(0, 2, 1, 3) for x in (q, k, v))      # [B,H,T,hd]
     S = (qh @ kh.transpose(0, 1, 3, 2)) / np.sqrt(hd)             # [B,H,T,T]
     mask = np.triu(np.ones((T, T), dtype=bool), 1)
+    if window > 0:
+        mask |= np.tril(np.ones((T, T), dtype=bool), -window)
     S = np.where(mask, -np.inf, S)
     S = S - S.max(axis=-1, keepdims=True)
     P = np.exp(S)
@@ -116,7 +124,7 @@ def causal_attention(q, k, v):
     return o, P
 
 
-def causal_attention_bwd(do, q, k, v, o, P=None):
+def causal_attention_bwd(do, q, k, v, o, P=None, window=0):
     """Backward of causal_attention.
 
     dP = dO v^T ; dS = P * (dP - rowsum(dO * O)) ; dq = dS k / sqrt(hd);
@@ -124,7 +132,7 @@ def causal_attention_bwd(do, q, k, v, o, P=None):
     """
     B, T, H, hd = q.shape
     if P is None:
-        _, P = causal_attention(q, k, v)
+        _, P = causal_attention(q, k, v, window)
     qh, kh, vh, doh, oh = (x.transpose(0, 2, 1, 3) for x in (q, k, v, do, o))
     dv = P.transpose(0, 1, 3, 2) @ doh
     dP = doh @ vh.transpose(0, 1, 3, 2)
@@ -183,7 +191,7 @@ def forward(params, tokens, cfg, keep=True):
         v = qkv[..., 2 * d:].reshape(B, T, H, hd)
         qn, rq = rms_norm(rope(q, ang), eps)
         kn, rk = rms_norm(rope(k, ang), eps)
-        o, _ = causal_attention(qn, kn, v)
+        o, _ = causal_attention(qn, kn, v, cfg.get("attn_window", 0))
         o2 = o.reshape(B, T, d)
         h1 = h + qf(o2) @ qfw(Wo).T
         m, rm = rms_norm(h1, eps)
@@ -250,7 +258,7 @@ def backward(z, targets, cache, cfg):
         # attention block: h1 = h + o Wo^T
         dWo, do = lin_bwd(dh1, c["o"], Wo)
         do = do.reshape(B, T, H, hd)
-        dqn, dkn, dv = causal_attention_bwd(do, c["qn"], c["kn"], c["v"], c["o"])
+        dqn, dkn, dv = causal_attention_bwd(do, c["qn"], c["kn"], c["v"], c["o"], window=cfg.get("attn_window", 0))
         dq = rope(rms_norm_bwd(dqn, c["qn"], c["rq"]), ang, inverse=True).reshape(B, T, d)
         dk = rope(rms_norm_bwd(dkn, c["kn"], c["rk"]), ang, inverse=True).reshape(B, T, d)
         dv = dv.reshape(B, T, d)

@@ -23,6 +23,7 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 MICRO = dict(depth=1, d_model=16, n_head=2, head_dim=8, d_ff=64, vocab=64, seq_len=8,
              batch=2, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
 MICRO2 = dict(MICRO, depth=2)
+MICRO_W = dict(MICRO2, attn_window=3)  # sliding window: each query sees 3 keys
 TINY = dict(depth=2, d_model=128, n_head=4, head_dim=32, d_ff=512, vocab=4096, seq_len=128,
             batch=4, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
 
@@ -42,7 +43,7 @@ def _tokens(cfg, seed=0, dist="uniform"):
 # P1: the whole backward against centred finite differences
 
 
-@pytest.mark.parametrize("cfg", [MICRO, MICRO2])
+@pytest.mark.parametrize("cfg", [MICRO, MICRO2, MICRO_W])
 def test_fd_gradient_every_element(cfg):
     params = _params(cfg, seed=1, std=0.5)          # large weights: non-linear regime
     tok, tgt = _tokens(cfg, seed=2)
@@ -181,6 +182,32 @@ def test_attention_special_cases_and_sdpa():
     w /= w.sum()
     np.testing.assert_allclose(o[b, i, h], sum(w[j] * v[b, j, h] for j in range(i + 1)),
                                rtol=1e-12)
+
+
+def test_sliding_window_attention_pins():
+    """window = 1: every query sees only itself (o = v); window >= T: plain causal
+    attention; and the window edge is exact: a key just outside query i's window
+    (j = i - window) leaves o_i unchanged, a key just inside (j = i - window + 1)
+    changes it."""
+    rng = np.random.default_rng(4)
+    B, T, H, hd = 2, 11, 2, 8
+    q, k, v = (rng.standard_normal((B, T, H, hd)) for _ in range(3))
+    o1, _ = O.causal_attention(q, k, v, window=1)
+    np.testing.assert_allclose(o1, v, rtol=1e-14, atol=1e-15)
+    full, _ = O.causal_attention(q, k, v)
+    for w in (T, T + 5):
+        ow, _ = O.causal_attention(q, k, v, window=w)
+        np.testing.assert_array_equal(ow, full)
+    W, i = 4, 8
+    base, _ = O.causal_attention(q, k, v, window=W)
+    for j, moves in ((i - W, False), (i - W + 1, True)):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, j] += 1.0
+        v2[:, j] += 1.0
+        o2, _ = O.causal_attention(q, k2, v2, window=W)
+        changed = not np.array_equal(o2[:, i], base[:, i])
+        assert changed == moves, (j, changed)
+    assert not np.array_equal(base, full)  # the window binds at T = 11
 
 
 def test_attention_backward_vs_autograd():
