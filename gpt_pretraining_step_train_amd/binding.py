@@ -26,7 +26,7 @@ class GptCfg(ctypes.Structure):
         ("init_std", ctypes.c_float), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("muon_momentum", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("ns_coeffs", (ctypes.c_float * 3) * 5), ("num_steps", ctypes.c_int64),
-        ("ns_split_steps", ctypes.c_int32), ("fp8_gemms", ctypes.c_int32),
+        ("ns_split_steps", ctypes.c_int32), ("fp8_gemms", ctypes.c_int32), ("attn_window", ctypes.c_int32),
     ]
 
     def coeffs(self):
@@ -70,8 +70,8 @@ _SIGS = {
     "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
     "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
-    "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _P]),
-    "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gptk_rmsnorm_fwd": (_I, [_I, _P, _P, _P, _I, _I, _F, _P]),
     "gptk_rmsnorm_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
     "gptk_rope_qknorm_fwd": (_I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P]),
@@ -126,6 +126,8 @@ def make_cfg(c: dict) -> GptCfg:
         cfg.ns_split_steps = int(c["ns_split_steps"])
     if "fp8_gemms" in c:
         cfg.fp8_gemms = int(c["fp8_gemms"])
+    if "attn_window" in c:
+        cfg.attn_window = int(c["attn_window"])
     if "ns_coeffs" in c:
         for i, abc in enumerate(c["ns_coeffs"]):
             for j in range(3):
@@ -283,13 +285,13 @@ def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
     return lib().gpt_gemm_kernel_name(dtype, a_kmaj, b_kmaj, M, N, K, batch).decode()
 
 
-def attn_fwd(dtype, qkv, o, lse, B, T, H, hd):
-    check(lib().gptk_attn_fwd(dtype, _ptr(qkv), _ptr(o), _ptr(lse), B, T, H, hd, _stream()), "gptk_attn_fwd")
+def attn_fwd(dtype, qkv, o, lse, B, T, H, hd, window=0):
+    check(lib().gptk_attn_fwd(dtype, _ptr(qkv), _ptr(o), _ptr(lse), B, T, H, hd, window, _stream()), "gptk_attn_fwd")
 
 
-def attn_bwd(dtype, qkv, o, dO, lse, D, dqkv, B, T, H, hd):
+def attn_bwd(dtype, qkv, o, dO, lse, D, dqkv, B, T, H, hd, window=0):
     check(lib().gptk_attn_bwd(dtype, _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(D), _ptr(dqkv), B, T, H, hd,
-                              _stream()), "gptk_attn_bwd")
+                              window, _stream()), "gptk_attn_bwd")
 
 
 def rmsnorm_fwd(dtype, x, y, rstd, N, d, eps):

@@ -23,7 +23,8 @@ CONFIGS = {
 }
 
 DEFAULTS = dict(init_std=0.02, rope_base=10000.0, norm_eps=1e-6, muon_momentum=0.95,
-                ns_steps=5, fp8_gemms=7)   # fp8: forward, weight- and input-gradient GEMMs
+                ns_steps=5, fp8_gemms=7,   # fp8: forward, weight- and input-gradient GEMMs
+                attn_window=0)             # sliding-window attention off (every earlier key)
 
 
 def get(name: str, **over) -> dict:

@@ -187,7 +187,8 @@ struct PairStager {
 
 template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H) {
+attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H,
+                     int W) {
   constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
@@ -214,10 +215,14 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
-  float m = -INFINITY, l = 0.f;  // running reference maximum (log2 units) and sum
+  // running reference maximum (log2 units) and sum; the maximum starts finite so that
+  // a lane whose keys in a tile are all masked (sliding window) gets p = 0, not NaN
+  float m = -1e30f, l = 0.f;
   const float sl2 = LOG2E / sqrtf((float)HD);
+  const int Wn = W > 0 ? W : T;  // keys a query sees, itself included
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
+  const int it0 = max(0, qb * BQ - Wn + 1) / BKV;  // first tile any query of the block sees
 
   // Per-lane LDS element offsets, loop-invariant: every fragment's tile row origin is
   // a multiple of 16, where the swizzle repeats, so it enters as an immediate.
@@ -235,7 +240,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 
   PairStager<HD, 256> stg;
   stg.init(ld, ld, tid);
-  stg.load(rows_rsrc(K, ld, 0, T, HD), rows_rsrc(V, ld, 0, T, HD), tid);
+  stg.load(rows_rsrc(K, ld, it0 * BKV, T, HD), rows_rsrc(V, ld, it0 * BKV, T, HD), tid);
   stg.store(Ks[0], Vs[0], tid);
   __syncthreads();
 
@@ -244,7 +249,8 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     constexpr int cur = decltype(cur_c)::value;
     const int k0 = it * BKV;
     if (it + 1 < nkv) stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
-    if (k0 <= q0 + 31 && q0 < T) {
+    // the wave's 32 queries see keys q0 - Wn + 1 .. q0 + 31
+    if (k0 <= q0 + 31 && k0 + BKV - 1 >= q0 - Wn + 1 && q0 < T) {
       f32x16_t s[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -253,13 +259,13 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 #pragma unroll
         for (int kk = 1; kk < NKK; ++kk) s[kb2] = mfma32x32x16_bf16(lds_row8(kp + kro[kk]), qf[kk], s[kb2]);
       }
-      if (k0 + BKV - 1 > q0 || k0 + BKV > T) {  // diagonal or ragged tile: mask
+      if (k0 + BKV - 1 > q0 || k0 + BKV > T || k0 <= q0 + 31 - Wn) {  // diagonal, ragged or window edge
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb2 * 32 + acc_row(lane, r);
-            if (key > myq || key >= T) s[kb2][r] = -INFINITY;
+            if (key > myq || key >= T || key <= myq - Wn) s[kb2][r] = -INFINITY;
           }
       }
       float bmax = -INFINITY;
@@ -271,7 +277,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
       const bool raise = bmax > m + RESCALE_LOG2;
       if (__builtin_amdgcn_ballot_w64(raise)) {
         const float mnew = raise ? bmax : m;
-        const float alpha = fast_exp2(m - mnew);  // 0 on the first tile (m = -inf)
+        const float alpha = fast_exp2(m - mnew);  // 0 on the first raise (m = -1e30)
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
@@ -306,7 +312,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
     __syncthreads();
   };
-  for (int it = 0; it < nkv; it += 2) {
+  for (int it = it0; it < nkv; it += 2) {
     body(std::integral_constant<int, 0>{}, it);
     if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
@@ -357,7 +363,8 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const T* __restrict_
 template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dO,
-                   const float* __restrict__ lse, float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H) {
+                   const float* __restrict__ lse, float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H,
+                   int W) {
   constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
@@ -416,19 +423,21 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
     ktr[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
   }
 
+  const int Wn = W > 0 ? W : T;  // keys a query sees, itself included
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
+  const int it0 = max(0, qb * BQ - Wn + 1) / BKV;  // first tile any query of the block sees
   PairStager<HD, 256> stg;
   stg.init(ld, ld, tid);
-  stg.load(rows_rsrc(K, ld, 0, T, HD), rows_rsrc(V, ld, 0, T, HD), tid);
+  stg.load(rows_rsrc(K, ld, it0 * BKV, T, HD), rows_rsrc(V, ld, it0 * BKV, T, HD), tid);
   stg.store(Ks[0], Vs[0], tid);
   __syncthreads();
   auto body = [&](auto cur_c, int it) {
     constexpr int cur = decltype(cur_c)::value;
     const int k0 = it * BKV;
     if (it + 1 < nkv) stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
-    if (k0 <= q0 + 31 && q0 < T) {
-      const bool mask = k0 + BKV - 1 > q0 || k0 + BKV > T;
+    if (k0 <= q0 + 31 && k0 + BKV - 1 >= q0 - Wn + 1 && q0 < T) {
+      const bool mask = k0 + BKV - 1 > q0 || k0 + BKV > T || k0 <= q0 + 31 - Wn;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const bf16_t* kp = Ks[cur] + kb2 * 32 * RS;
@@ -444,7 +453,7 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb2 * 32 + acc_row(lane, r);
-            if (key > myq || key >= T) s[r] = -INFINITY;
+            if (key > myq || key >= T || key <= myq - Wn) s[r] = -INFINITY;
           }
         }
         float ds[16];
@@ -463,7 +472,7 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
     if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
     __syncthreads();
   };
-  for (int it = 0; it < nkv; it += 2) {
+  for (int it = it0; it < nkv; it += 2) {
     body(std::integral_constant<int, 0>{}, it);
     if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
@@ -492,7 +501,7 @@ template <int HD>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
                            const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
-                           int T, int H) {
+                           int T, int H, int W) {
   constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
@@ -540,7 +549,9 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     tro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
   }
 
-  const int nqt = (T + BQT - 1) / BQT;
+  const int Wn = W > 0 ? W : T;  // keys a query sees, itself included
+  // query tiles from the block's first key to the last query that sees its last key
+  const int nqt = min((T + BQT - 1) / BQT, (kb * BKEY + BKEY - 1 + Wn - 1) / BQT + 1);
   const int qt0 = (kb * BKEY) / BQT;
   // 64-row Q and dO tiles and their lse / D values, prefetched one tile ahead
   PairStager<HD, 512> stg;
@@ -574,21 +585,25 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     constexpr int cur = decltype(cur_c)::value;
     const int qb0 = qt * BQT;
     if (qt + 1 < nqt) load(qb0 + BQT);
-    const bool live = qb0 + BQT - 1 >= key0 && key0 < T;  // the same for both roles
+    // the same for both roles: the tile holds a query that sees one of the wave's keys
+    const bool live = qb0 + BQT - 1 >= key0 && qb0 <= key0 + 31 + Wn - 1 && key0 < T;
     f32x16_t pd[2];  // P (dV waves) or dP (dK waves) of each 32-query half
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      if (!live || qb0 + qs * 32 + 31 < key0) continue;
+      if (!live || qb0 + qs * 32 + 31 < key0 || qb0 + qs * 32 > key0 + 31 + Wn - 1) continue;
       const bf16_t* rp = (dk_role ? Gs[cur] : Qs[cur]) + qs * 32 * RS;
       const bf16x8_t* kv = dk_role ? vf : kf;
       f32x16_t a = mfma32x32x16_bf16(lds_row8(rp + qro[0]), kv[0], zero16());
 #pragma unroll
       for (int kk = 1; kk < NKK; ++kk) a = mfma32x32x16_bf16(lds_row8(rp + qro[kk]), kv[kk], a);
       if (!dk_role) {
-        if (qb0 + qs * 32 < key0 + 31) {  // diagonal block: queries before the key
+        // diagonal block (queries before the key) or window edge (queries too far after)
+        if (qb0 + qs * 32 < key0 + 31 || qb0 + qs * 32 + 31 - key0 >= Wn) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (qb0 + qs * 32 + acc_row(lane, r) < mykey) a[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int q = qb0 + qs * 32 + acc_row(lane, r);
+            if (q < mykey || q - mykey >= Wn) a[r] = -INFINITY;
+          }
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {  // registers 4g..4g+3 hold query rows qs*32 + 8g + 4hl + 0..3
@@ -605,7 +620,7 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     __syncthreads();  // P published
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      if (!live || qb0 + qs * 32 + 31 < key0) continue;
+      if (!live || qb0 + qs * 32 + 31 < key0 || qb0 + qs * 32 > key0 + 31 + Wn - 1) continue;
       float w[16];
       if (dk_role) {
 #pragma unroll
@@ -655,7 +670,7 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
 
 template <int HD>
 __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out,
-                                                          float* __restrict__ lse, int T, int H) {
+                                                          float* __restrict__ lse, int T, int H, int W) {
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= T) return;
@@ -668,7 +683,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(const float* __restric
 #pragma unroll
   for (int d = 0; d < HD; ++d) { q[d] = Q[(long)i * ld + d]; o[d] = 0.f; }
   float m = -INFINITY, l = 0.f;
-  for (int j = 0; j <= i; ++j) {
+  for (int j = W > 0 ? max(0, i - W + 1) : 0; j <= i; ++j) {
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < HD; ++d) s = fmaf(q[d], K[(long)j * ld + d], s);
@@ -688,7 +703,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(const float* __restric
 template <int HD>
 __global__ void __launch_bounds__(64) attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const float* __restrict__ dO,
                                                              const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                             float* __restrict__ dqkv, int T, int H) {
+                                                             float* __restrict__ dqkv, int T, int H, int W) {
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= T) return;
@@ -702,7 +717,7 @@ __global__ void __launch_bounds__(64) attn_bwd_dq_f32_kernel(const float* __rest
 #pragma unroll
   for (int d = 0; d < HD; ++d) { q[d] = Q[(long)i * ld + d]; g[d] = G[(long)i * ldo + d]; dq[d] = 0.f; }
   const float L = lse[(long)bh * T + i], D = Dv[(long)bh * T + i];
-  for (int j = 0; j <= i; ++j) {
+  for (int j = W > 0 ? max(0, i - W + 1) : 0; j <= i; ++j) {
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < HD; ++d) {
@@ -723,7 +738,7 @@ __global__ void __launch_bounds__(64) attn_bwd_dkdv_f32_kernel(const float* __re
                                                                const float* __restrict__ dO,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ Dv, float* __restrict__ dqkv,
-                                                               int T, int H) {
+                                                               int T, int H, int W) {
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int j = blockIdx.x * 64 + threadIdx.x;
   if (j >= T) return;
@@ -738,7 +753,8 @@ __global__ void __launch_bounds__(64) attn_bwd_dkdv_f32_kernel(const float* __re
   for (int d = 0; d < HD; ++d) {
     k[d] = K[(long)j * ld + d]; v[d] = V[(long)j * ld + d]; dk[d] = 0.f; dv[d] = 0.f;
   }
-  for (int i = j; i < T; ++i) {
+  const int iend = W > 0 ? min(T, j + W) : T;  // queries that see key j
+  for (int i = j; i < iend; ++i) {
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < HD; ++d) {
@@ -762,49 +778,50 @@ __global__ void __launch_bounds__(64) attn_bwd_dkdv_f32_kernel(const float* __re
 }
 
 template <int HD>
-void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, hipStream_t st) {
+void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int W, hipStream_t st) {
   if (at == ACT_BF16)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st,
-                       (const bf16_t*)qkv, (bf16_t*)o, lse, T, H);
+                       (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, W);
   else
     hipLaunchKernelGGL(attn_fwd_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
-                       (float*)o, lse, T, H);
+                       (float*)o, lse, T, H, W);
 }
 
 template <int HD>
 void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
-                  int B, int T, int H, hipStream_t st) {
+                  int B, int T, int H, int W, hipStream_t st) {
   if (at == ACT_BF16) {
     // the dQ kernel also writes D = rowsum(dO * O) for the dK/dV kernel
     hipLaunchKernelGGL(attn_bwd_dq_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st, (const bf16_t*)qkv,
-                       (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
+                       (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, W);
     hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(512), 0, st,
-                       (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H);
+                       (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, W);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
-                       (const float*)dO, lse, D, (float*)dqkv, T, H);
+                       (const float*)dO, lse, D, (float*)dqkv, T, H, W);
     hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st,
-                       (const float*)qkv, (const float*)dO, lse, D, (float*)dqkv, T, H);
+                       (const float*)qkv, (const float*)dO, lse, D, (float*)dqkv, T, H, W);
   }
 }
 
 }  // namespace
 
-void launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int hd, hipStream_t st) {
+void launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int hd, int window,
+                     hipStream_t st) {
   if (B * T * H == 0) return;
-  if (hd == 128) fwd_dispatch<128>(qkv, o, lse, at, B, T, H, st);
-  else if (hd == 64) fwd_dispatch<64>(qkv, o, lse, at, B, T, H, st);
-  else if (hd == 32) fwd_dispatch<32>(qkv, o, lse, at, B, T, H, st);
+  if (hd == 128) fwd_dispatch<128>(qkv, o, lse, at, B, T, H, window, st);
+  else if (hd == 64) fwd_dispatch<64>(qkv, o, lse, at, B, T, H, window, st);
+  else if (hd == 32) fwd_dispatch<32>(qkv, o, lse, at, B, T, H, window, st);
 }
 
 void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
-                     int B, int T, int H, int hd, hipStream_t st) {
+                     int B, int T, int H, int hd, int window, hipStream_t st) {
   if (B * T * H == 0) return;
   const int N = B * T;
   if (at != ACT_BF16)  // the bf16 dQ kernel forms D itself
     hipLaunchKernelGGL(attn_bwd_prep_kernel<float>, dim3((N * H + 3) / 4), dim3(256), 0, st, (const float*)o,
                        (const float*)dO, D, N, T, H, hd);
-  if (hd == 128) bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, st);
-  else if (hd == 64) bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, st);
-  else if (hd == 32) bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, st);
+  if (hd == 128) bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, window, st);
+  else if (hd == 64) bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, window, st);
+  else if (hd == 32) bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, window, st);
 }

@@ -242,7 +242,7 @@ int run_gemm(gpt_model* M, GemmArgs p, hipStream_t st, bool allow_split) {
 bool same_shape(const gpt_cfg& a, const gpt_cfg& b) {
   return a.depth == b.depth && a.d_model == b.d_model && a.n_head == b.n_head && a.head_dim == b.head_dim &&
          a.d_ff == b.d_ff && a.vocab == b.vocab && a.seq_len == b.seq_len && a.batch == b.batch &&
-         a.precision == b.precision;
+         a.precision == b.precision && a.attn_window == b.attn_window;
 }
 
 // element offset of tensor id inside the parameter/gradient vector, and its shape
@@ -286,6 +286,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->ns_steps = 5;
   out->ns_split_steps = 4;
   out->fp8_gemms = GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD;
+  out->attn_window = 0;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
   out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
@@ -309,6 +310,7 @@ int gpt_cfg_validate(const gpt_cfg* c) {
     return GPT_ERR_SHAPE;
   if (c->ns_steps < 0 || c->ns_steps > 5 || c->ns_split_steps < 0) return GPT_ERR_ARG;
   if (c->fp8_gemms & ~(GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD)) return GPT_ERR_ARG;
+  if (c->attn_window < 0) return GPT_ERR_ARG;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
 }
@@ -583,7 +585,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       if ((rc = lin_fwd(M, p, 4 * l + 0, st))) return rc;
     }
     launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, eps, st);
-    launch_attn_fwd(qkv, o, lse, at, B, T, H, hd, st);
+    launch_attn_fwd(qkv, o, lse, at, B, T, H, hd, c.attn_window, st);
     {
       GemmArgs p;  // h' = h + o Wo^T
       p.M = N; p.N = d; p.K = d; p.A = o; p.lda = d;
@@ -668,7 +670,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       pd.outA = do_act; pd.ldoa = d;
       if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st))) return rc;
     }
-    launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, hd, st);
+    launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, hd, c.attn_window, st);
     launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, st);
     {
       GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
@@ -1000,20 +1002,21 @@ static int attn_ok(int dtype, int hd) {
   return GPT_OK;
 }
 
-int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, void* stream) {
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, int window,
+                  void* stream) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
-  if (B < 0 || T < 0 || H < 0 || !qkv || !o || !lse) return GPT_ERR_ARG;
-  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, hd, (hipStream_t)stream);
+  if (B < 0 || T < 0 || H < 0 || window < 0 || !qkv || !o || !lse) return GPT_ERR_ARG;
+  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, hd, window, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
 int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv,
-                  int B, int T, int H, int hd, void* stream) {
+                  int B, int T, int H, int hd, int window, void* stream) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
-  if (B < 0 || T < 0 || H < 0 || !qkv || !o || !dO || !lse || !D || !dqkv) return GPT_ERR_ARG;
-  launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, hd, (hipStream_t)stream);
+  if (B < 0 || T < 0 || H < 0 || window < 0 || !qkv || !o || !dO || !lse || !D || !dqkv) return GPT_ERR_ARG;
+  launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, hd, window, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 

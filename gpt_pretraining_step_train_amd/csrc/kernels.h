@@ -106,8 +106,8 @@ void launch_amax(const void* x, int in_type, long rows, long cols, long ld, unsi
 void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, const unsigned* amax_bits,
                        uint8_t* q, long ldq, uint8_t* qt, long ldqt, float* inv_scale, hipStream_t st);
 
-// attention
-void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int hd,
+// attention (window > 0: query i sees keys i - window < j <= i; 0: all j <= i)
+void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int hd, int window,
                      hipStream_t st);
 void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,
-                     void* dqkv, int act_type, int B, int T, int H, int hd, hipStream_t st);
+                     void* dqkv, int act_type, int B, int T, int H, int hd, int window, hipStream_t st);

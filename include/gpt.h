@@ -78,6 +78,9 @@ typedef struct gpt_cfg {
                          operands, a mask of GPT_FP8_FWD (Y = X W^T), GPT_FP8_WGRAD
                          (dW = dY^T X) and GPT_FP8_DGRAD (dX = dY W); default all three.
                          Other bits: GPT_ERR_ARG. Ignored for the other precisions. */
+  int32_t attn_window;  /* sliding-window attention: query i sees keys i - attn_window < j <= i
+                           (flash-attention's window_size = (attn_window - 1, 0)); 0 (the
+                           default) = every earlier key; negative: GPT_ERR_ARG */
 } gpt_cfg;
 
 enum { GPT_FP8_FWD = 1, GPT_FP8_WGRAD = 2, GPT_FP8_DGRAD = 4 };
@@ -217,12 +220,15 @@ int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t
 const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch);
 
 /* causal attention over qkv act [B*T][3*H*hd] -> o act [B*T][H*hd], lse fp32
- * [B][H][T] (natural log of the sum of exp of q.k/sqrt(hd)). hd in {32,64,128}. */
-int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, void* stream);
-/* backward: dqkv act [B*T][3*H*hd] from qkv, o, dO act [B*T][H*hd] and lse;
- * D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */
+ * [B][H][T] (natural log of the sum of exp of q.k/sqrt(hd)). hd in {32,64,128}.
+ * window > 0: query i attends to keys i - window < j <= i (sliding window); 0: all
+ * j <= i; negative: GPT_ERR_ARG. */
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, int window,
+                  void* stream);
+/* backward: dqkv act [B*T][3*H*hd] from qkv, o, dO act [B*T][H*hd] and lse, with
+ * the forward's window; D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */
 int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D,
-                  void* dqkv, int B, int T, int H, int hd, void* stream);
+                  void* dqkv, int B, int T, int H, int hd, int window, void* stream);
 
 /* y act = x / sqrt(mean(x^2) + eps) per row of x fp32 [N][d]; rstd fp32 [N] */
 int gptk_rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int N, int d, float eps, void* stream);

@@ -63,7 +63,8 @@ def test_default_ns_table(lib):
     lib.gpt_cfg_from_depth(24, ctypes.byref(c))
     tab = c.coeffs()
     assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 4 and c.fp8_gemms == 7
-    assert ctypes.sizeof(binding.GptCfg) == 136
+    assert c.attn_window == 0
+    assert ctypes.sizeof(binding.GptCfg) == 144
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
     derived, _ = polar_express.coefficients()
     np.testing.assert_allclose(tab[2:], derived[2:], rtol=0, atol=2e-5)
@@ -73,7 +74,8 @@ def test_validation_errors(lib):
     base = binding.make_cfg(configs.get("laptop"))
     assert lib.gpt_cfg_validate(ctypes.byref(base)) == 0
     for field, val, code in [("head_dim", 48, 6), ("n_head", 5, 2), ("d_model", 2056, 2), ("precision", 7, 6),
-                             ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2), ("fp8_gemms", 8, 1)]:
+                             ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2), ("fp8_gemms", 8, 1),
+                             ("attn_window", -1, 1)]:
         c = binding.make_cfg(configs.get("laptop"))
         setattr(c, field, val)
         assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, field

@@ -188,25 +188,31 @@ def _qkv(Bn, T, H, hd, seed, dtype):
     return qkv, q, k, v
 
 
-ATTN_CASES = [("bf16", 2, 300, 3, 128), ("bf16", 1, 256, 2, 64), ("bf16", 2, 130, 2, 32),
-              ("bf16", 1, 1, 1, 128), ("fp32", 2, 128, 4, 32), ("fp32", 1, 77, 2, 64)]
+# (dtype, B, T, H, hd, window): window > 0 is sliding-window attention (query i sees
+# keys i - window < j <= i): one key, windows at and across a 64-key tile edge, and
+# windows spanning several 128-query blocks
+ATTN_CASES = [("bf16", 2, 300, 3, 128, 0), ("bf16", 1, 256, 2, 64, 0), ("bf16", 2, 130, 2, 32, 0),
+              ("bf16", 1, 1, 1, 128, 0), ("fp32", 2, 128, 4, 32, 0), ("fp32", 1, 77, 2, 64, 0),
+              ("bf16", 2, 300, 3, 128, 1), ("bf16", 2, 300, 3, 128, 100), ("bf16", 1, 256, 2, 64, 64),
+              ("bf16", 1, 256, 2, 64, 65), ("bf16", 2, 130, 2, 32, 37), ("bf16", 1, 700, 2, 128, 200),
+              ("bf16", 1, 1024, 1, 128, 129), ("fp32", 2, 128, 4, 32, 17), ("fp32", 1, 77, 2, 64, 5)]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES)
 def test_attention_fwd_bwd(case):
-    dtype, Bn, T, H, hd = case
+    dtype, Bn, T, H, hd, win = case
     say("attention", case)
     qkv, q, k, v = _qkv(Bn, T, H, hd, 11, dtype)
-    o_ref, _ = O.causal_attention(q, k, v)
-    qh = q.transpose(0, 2, 1, 3)
-    S = qh @ k.transpose(0, 2, 3, 1) / np.sqrt(hd)
-    S = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, S)
-    lse_ref = O.logsumexp(S)                               # [B,H,T]
+    o_ref, P = O.causal_attention(q, k, v, window=win)
+    # lse from the oracle's probabilities: the diagonal key is always visible, and
+    # P_ii = exp(S_ii - lse_i)
+    S_ii = np.einsum("bihd,bihd->bhi", q, k) / np.sqrt(hd)
+    lse_ref = S_ii - np.log(np.diagonal(P, axis1=2, axis2=3))   # [B,H,T]
     d = H * hd
     dq = to_dev(qkv, dtype)
     o = torch.zeros(Bn * T, d, device="cuda", dtype=dq.dtype)
     lse = torch.zeros(Bn * H * T, device="cuda")
-    B.attn_fwd(DT[dtype], dq, o, lse, Bn, T, H, hd)
+    B.attn_fwd(DT[dtype], dq, o, lse, Bn, T, H, hd, win)
     torch.cuda.synchronize()
     o_got = from_dev(o).reshape(Bn, T, H, hd)
     tol = 1e-2 if dtype == "bf16" else 1e-5
@@ -216,11 +222,11 @@ def test_attention_fwd_bwd(case):
     rng = np.random.default_rng(12)
     dO = _round(rng.standard_normal((Bn, T, H, hd)), dtype)
     o_in = o_got
-    dq_ref, dk_ref, dv_ref = O.causal_attention_bwd(dO.astype(np.float64), q, k, v, o_in)
+    dq_ref, dk_ref, dv_ref = O.causal_attention_bwd(dO.astype(np.float64), q, k, v, o_in, window=win)
     ddo = to_dev(dO.reshape(Bn * T, d), dtype)
     D = torch.zeros(Bn * H * T, device="cuda")
     dqkv = torch.full((Bn * T, 3 * d), float("nan"), device="cuda", dtype=dq.dtype)
-    B.attn_bwd(DT[dtype], dq, o, ddo, lse, D, dqkv, Bn, T, H, hd)
+    B.attn_bwd(DT[dtype], dq, o, ddo, lse, D, dqkv, Bn, T, H, hd, win)
     torch.cuda.synchronize()
     g = from_dev(dqkv).reshape(Bn, T, 3, H, hd)
     gtol = 2e-2 if dtype == "bf16" else 1e-4

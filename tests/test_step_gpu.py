@@ -55,6 +55,7 @@ def _dev(a):
 STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8", {"precision": "fp8"}),
               ("laptop_fp8_bwd", {"precision": "fp8", "fp8_gemms": 6}),
               ("laptop_fp8_fwd", {"precision": "fp8", "fp8_gemms": 1}),
+              ("laptop_window", {"attn_window": 100}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
