@@ -22,15 +22,21 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h")
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h")
+GEMM_ARGS = ("csrc/kernels.h", "struct GemmArgs {", "\n};\n")  # the GEMM's argument block only
 BEGIN, END = "<!-- traffic-record", "-->"
 
 
-def sources_hash(files=GEMM_SOURCES) -> str:
+def sources_hash(files=GEMM_SOURCES, args=GEMM_ARGS) -> str:
+    """Hash of the GEMM kernel sources: its own files and the GemmArgs definition (the
+    rest of kernels.h declares other kernels and does not change the GEMM)."""
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(PKG, f), "rb") as fh:
             h.update(fh.read())
+    text = open(os.path.join(PKG, args[0])).read()
+    i = text.index(args[1])
+    h.update(text[i:text.index(args[2], i) + len(args[2])].encode())
     return h.hexdigest()[:16]
 
 
