@@ -24,7 +24,14 @@ CONFIGS = {
 
 DEFAULTS = dict(init_std=0.02, rope_base=10000.0, norm_eps=1e-6, muon_momentum=0.95,
                 ns_steps=5, fp8_gemms=7,   # fp8: forward, weight- and input-gradient GEMMs
-                attn_window=0)             # sliding-window attention off (every earlier key)
+                attn_window=0,             # sliding-window attention off (every earlier key)
+                n_kv_head=0)               # key/value heads; 0 = n_head (multi-head attention)
+
+
+def kv_heads(cfg: dict) -> int:
+    """Key/value heads: n_kv_head, or n_head when it is 0 / absent (grouped-query
+    attention shares each key/value head among n_head / n_kv_head query heads)."""
+    return int(cfg.get("n_kv_head") or cfg["n_head"])
 
 
 def get(name: str, **over) -> dict:
@@ -37,24 +44,27 @@ def get(name: str, **over) -> dict:
 
 def n_params(cfg: dict) -> int:
     d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
-    return 2 * V * d + L * (4 * d * d + 2 * F * d)
+    dkv = kv_heads(cfg) * cfg["head_dim"] if cfg.get("n_kv_head") else d  # Wk, Wv rows
+    return 2 * V * d + L * (2 * d * d + 2 * dkv * d + 2 * F * d)
 
 
 def step_flops(cfg: dict) -> dict:
     """Algorithmic FLOPs of one step: dense GEMMs, exact causal attention, Newton-Schulz.
 
-    fwd+bwd = 6 N (12 L d^2 + d V) when F = 4d (generally 6 N (4 L d^2 + 2 L d F + d V)),
-    plus causal attention 6 L d N (T+1) (fwd 2 d T (T+1) per sequence and layer, bwd 2x).
+    fwd+bwd = 6 N (12 L d^2 + d V) when F = 4d (generally 6 N (4 L d^2 + 2 L d F + d V);
+    with grouped-query attention Wk, Wv are dkv x d, dkv = n_kv_head * head_dim), plus
+    causal attention 6 L d N (T+1) (fwd 2 d T (T+1) per sequence and layer, bwd 2x).
     Muon = ns_steps * sum over block matrices of (4 s^2 l + 2 s^3), s = min dim, l = max dim.
     """
     d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
+    dkv = kv_heads(cfg) * cfg["head_dim"]
     B, T = cfg["batch"], cfg["seq_len"]
     N = B * T
-    linear = 6 * N * (4 * L * d * d + 2 * L * d * F)
+    linear = 6 * N * (2 * L * d * d + 2 * L * dkv * d + 2 * L * d * F)
     head = 6 * N * d * V
     attn = 6 * L * d * N * (T + 1)
     k = cfg.get("ns_steps", 5)
-    mats = [(d, d)] * 4 + [(F, d), (d, F)]
+    mats = [(d, d), (dkv, d), (dkv, d), (d, d), (F, d), (d, F)]
     muon = 0
     for (r, c) in mats:
         s, l = min(r, c), max(r, c)

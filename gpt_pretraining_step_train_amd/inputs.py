@@ -23,9 +23,10 @@ import numpy as np
 
 def tensor_shapes(cfg: dict) -> list[tuple[str, tuple[int, int]]]:
     d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
+    dkv = int(cfg.get("n_kv_head") or cfg["n_head"]) * cfg["head_dim"]  # key/value rows
     out = [("E", (V, d))]
     for l in range(L):
-        out += [(f"l{l}.Wq", (d, d)), (f"l{l}.Wk", (d, d)), (f"l{l}.Wv", (d, d)),
+        out += [(f"l{l}.Wq", (d, d)), (f"l{l}.Wk", (dkv, d)), (f"l{l}.Wv", (dkv, d)),
                 (f"l{l}.Wo", (d, d)), (f"l{l}.W1", (F, d)), (f"l{l}.W2", (d, F))]
     out.append(("U", (V, d)))
     return out

@@ -177,8 +177,9 @@ def forward(params, tokens, cfg, keep=True):
     E, layers, U = unpack(p, cfg)
     eps = cfg.get("norm_eps", 1e-6)
     H, hd = cfg["n_head"], cfg["head_dim"]
+    Hkv = int(cfg.get("n_kv_head") or H)
     B, T = tokens.shape
-    d = cfg["d_model"]
+    d, dkv = cfg["d_model"], Hkv * hd
     ang = rope_angles(T, hd, cfg.get("rope_base", 10000.0))
 
     h = E[tokens]                                         # [B,T,d]
@@ -187,11 +188,13 @@ def forward(params, tokens, cfg, keep=True):
         a, ra = rms_norm(h, eps)
         qkv = qf(a) @ qfw(np.concatenate([Wq, Wk, Wv])).T
         q = qkv[..., :d].reshape(B, T, H, hd)
-        k = qkv[..., d:2 * d].reshape(B, T, H, hd)
-        v = qkv[..., 2 * d:].reshape(B, T, H, hd)
+        k = qkv[..., d:d + dkv].reshape(B, T, Hkv, hd)
+        v = qkv[..., d + dkv:].reshape(B, T, Hkv, hd)
         qn, rq = rms_norm(rope(q, ang), eps)
         kn, rk = rms_norm(rope(k, ang), eps)
-        o, _ = causal_attention(qn, kn, v, cfg.get("attn_window", 0))
+        # grouped-query attention: query head h uses key/value head h // (H / Hkv)
+        o, _ = causal_attention(qn, np.repeat(kn, H // Hkv, axis=2), np.repeat(v, H // Hkv, axis=2),
+                                cfg.get("attn_window", 0))
         o2 = o.reshape(B, T, d)
         h1 = h + qf(o2) @ qfw(Wo).T
         m, rm = rms_norm(h1, eps)
@@ -232,6 +235,8 @@ def backward(z, targets, cache, cfg):
     H, hd = cfg["n_head"], cfg["head_dim"]
     B, T, V = z.shape
     d = cfg["d_model"]
+    Hkv = int(cfg.get("n_kv_head") or H)
+    G, dkv = H // Hkv, Hkv * hd
     N = B * T
     ang = cache["ang"]
     tokens = cache["tokens"]
@@ -258,13 +263,17 @@ def backward(z, targets, cache, cfg):
         # attention block: h1 = h + o Wo^T
         dWo, do = lin_bwd(dh1, c["o"], Wo)
         do = do.reshape(B, T, H, hd)
-        dqn, dkn, dv = causal_attention_bwd(do, c["qn"], c["kn"], c["v"], c["o"], window=cfg.get("attn_window", 0))
+        dqn, dkn, dv = causal_attention_bwd(do, c["qn"], np.repeat(c["kn"], G, axis=2), np.repeat(c["v"], G, axis=2),
+                                            c["o"], window=cfg.get("attn_window", 0))
+        # a key/value head's gradient is the sum over the G query heads sharing it
+        dkn = dkn.reshape(B, T, Hkv, G, hd).sum(axis=3)
+        dv = dv.reshape(B, T, Hkv, G, hd).sum(axis=3)
         dq = rope(rms_norm_bwd(dqn, c["qn"], c["rq"]), ang, inverse=True).reshape(B, T, d)
-        dk = rope(rms_norm_bwd(dkn, c["kn"], c["rk"]), ang, inverse=True).reshape(B, T, d)
-        dv = dv.reshape(B, T, d)
+        dk = rope(rms_norm_bwd(dkn, c["kn"], c["rk"]), ang, inverse=True).reshape(B, T, dkv)
+        dv = dv.reshape(B, T, dkv)
         # one Linear with weight [Wq; Wk; Wv]: dY = [dq | dk | dv]
         dWqkv, da = lin_bwd(np.concatenate([dq, dk, dv], axis=-1), c["a"], np.concatenate([Wq, Wk, Wv]))
-        dWq, dWk, dWv = dWqkv[:d], dWqkv[d:2 * d], dWqkv[2 * d:]
+        dWq, dWk, dWv = dWqkv[:d], dWqkv[d:d + dkv], dWqkv[d + dkv:]
         dh = dh1 + rms_norm_bwd(da.reshape(B, T, d), c["a"], c["ra"])
         grads_layers.append((dWq, dWk, dWv, dWo, dW1, dW2))
     grads_layers.reverse()

@@ -24,6 +24,7 @@ MICRO = dict(depth=1, d_model=16, n_head=2, head_dim=8, d_ff=64, vocab=64, seq_l
              batch=2, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
 MICRO2 = dict(MICRO, depth=2)
 MICRO_W = dict(MICRO2, attn_window=3)  # sliding window: each query sees 3 keys
+MICRO_G = dict(MICRO2, n_head=4, head_dim=4, n_kv_head=2)  # grouped-query attention, 2 heads per group
 TINY = dict(depth=2, d_model=128, n_head=4, head_dim=32, d_ff=512, vocab=4096, seq_len=128,
             batch=4, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
 
@@ -43,7 +44,7 @@ def _tokens(cfg, seed=0, dist="uniform"):
 # P1: the whole backward against centred finite differences
 
 
-@pytest.mark.parametrize("cfg", [MICRO, MICRO2, MICRO_W])
+@pytest.mark.parametrize("cfg", [MICRO, MICRO2, MICRO_W, MICRO_G])
 def test_fd_gradient_every_element(cfg):
     params = _params(cfg, seed=1, std=0.5)          # large weights: non-linear regime
     tok, tgt = _tokens(cfg, seed=2)
@@ -208,6 +209,29 @@ def test_sliding_window_attention_pins():
         changed = not np.array_equal(o2[:, i], base[:, i])
         assert changed == moves, (j, changed)
     assert not np.array_equal(base, full)  # the window binds at T = 11
+
+
+@pytest.mark.parametrize("n_kv", [1, 2])
+def test_grouped_query_attention_is_mha_with_shared_heads(n_kv):
+    """A model with n_kv key/value heads computes what the multi-head model computes
+    when each of its Wk/Wv head blocks is copied to the n_head / n_kv query heads
+    that share it; its Wk/Wv gradients are the sums of those copies' gradients and
+    every other gradient is the same."""
+    cfg = dict(MICRO2, n_head=4, head_dim=4, n_kv_head=n_kv)
+    mha = dict(cfg, n_kv_head=0)
+    H, hd, d, G = 4, 4, 16, 4 // n_kv
+    params = _params(cfg, seed=7, std=0.3)
+    tok, tgt = _tokens(cfg, seed=8)
+    widen = lambda W: np.repeat(W.reshape(n_kv, hd, d), G, axis=0).reshape(H * hd, d)
+    wide = [widen(w) if (i - 1) % 6 in (1, 2) and 0 < i < len(params) - 1 else w for i, w in enumerate(params)]
+    assert wide[2].shape == (H * hd, d) and params[2].shape == (n_kv * hd, d)
+    loss, grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
+    loss_m, grads_m, _, _ = O.loss_and_grads(wide, tok, tgt, mha)
+    assert loss == pytest.approx(loss_m, rel=1e-13)
+    for i, (g, gm) in enumerate(zip(grads, grads_m)):
+        if 0 < i < len(params) - 1 and (i - 1) % 6 in (1, 2):
+            gm = gm.reshape(n_kv, G, hd, d).sum(axis=1).reshape(n_kv * hd, d)
+        np.testing.assert_allclose(g, gm, rtol=1e-11, atol=1e-14, err_msg=f"tensor {i}")
 
 
 def test_attention_backward_vs_autograd():
