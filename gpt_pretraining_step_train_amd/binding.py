@@ -27,6 +27,7 @@ class GptCfg(ctypes.Structure):
         ("muon_momentum", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("ns_coeffs", (ctypes.c_float * 3) * 5), ("num_steps", ctypes.c_int64),
         ("ns_split_steps", ctypes.c_int32), ("fp8_gemms", ctypes.c_int32), ("attn_window", ctypes.c_int32),
+        ("n_kv_head", ctypes.c_int32),
     ]
 
     def coeffs(self):
@@ -70,12 +71,12 @@ _SIGS = {
     "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
     "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
-    "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
-    "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_rmsnorm_fwd": (_I, [_I, _P, _P, _P, _I, _I, _F, _P]),
     "gptk_rmsnorm_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
-    "gptk_rope_qknorm_fwd": (_I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P]),
-    "gptk_rope_qknorm_bwd": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "gptk_rope_qknorm_fwd": (_I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P]),
+    "gptk_rope_qknorm_bwd": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "gptk_cross_entropy": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _F, _P, _P]),
     "gptk_embed_gather": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "gptk_embed_ws_bytes": (_SZ, [_I, _I, _I]),
@@ -128,6 +129,8 @@ def make_cfg(c: dict) -> GptCfg:
         cfg.fp8_gemms = int(c["fp8_gemms"])
     if "attn_window" in c:
         cfg.attn_window = int(c["attn_window"])
+    if "n_kv_head" in c:
+        cfg.n_kv_head = int(c["n_kv_head"])
     if "ns_coeffs" in c:
         for i, abc in enumerate(c["ns_coeffs"]):
             for j in range(3):
@@ -285,12 +288,16 @@ def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
     return lib().gpt_gemm_kernel_name(dtype, a_kmaj, b_kmaj, M, N, K, batch).decode()
 
 
-def attn_fwd(dtype, qkv, o, lse, B, T, H, hd, window=0):
-    check(lib().gptk_attn_fwd(dtype, _ptr(qkv), _ptr(o), _ptr(lse), B, T, H, hd, window, _stream()), "gptk_attn_fwd")
+def attn_fwd(dtype, qkv, o, lse, B, T, H, hd, window=0, n_kv=None):
+    """n_kv: key/value heads (None: H)."""
+    hk = H if n_kv is None else n_kv
+    check(lib().gptk_attn_fwd(dtype, _ptr(qkv), _ptr(o), _ptr(lse), B, T, H, hk, hd, window, _stream()),
+          "gptk_attn_fwd")
 
 
-def attn_bwd(dtype, qkv, o, dO, lse, D, dqkv, B, T, H, hd, window=0):
-    check(lib().gptk_attn_bwd(dtype, _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(D), _ptr(dqkv), B, T, H, hd,
+def attn_bwd(dtype, qkv, o, dO, lse, D, dqkv, B, T, H, hd, window=0, n_kv=None):
+    hk = H if n_kv is None else n_kv
+    check(lib().gptk_attn_bwd(dtype, _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(D), _ptr(dqkv), B, T, H, hk, hd,
                               window, _stream()), "gptk_attn_bwd")
 
 
@@ -305,14 +312,16 @@ def rmsnorm_bwd(dtype, dy, x, rstd, dres, dx, dx_act, N, d):
           "gptk_rmsnorm_bwd")
 
 
-def rope_qknorm_fwd(dtype, qkv, cs, rq, rk, B, T, H, hd, base, eps):
-    check(lib().gptk_rope_qknorm_fwd(dtype, _ptr(qkv), _ptr(cs), _ptr(rq), _ptr(rk), B, T, H, hd, base, eps,
+def rope_qknorm_fwd(dtype, qkv, cs, rq, rk, B, T, H, hd, base, eps, n_kv=None):
+    hk = H if n_kv is None else n_kv
+    check(lib().gptk_rope_qknorm_fwd(dtype, _ptr(qkv), _ptr(cs), _ptr(rq), _ptr(rk), B, T, H, hk, hd, base, eps,
                                      _stream()), "gptk_rope_qknorm_fwd")
 
 
-def rope_qknorm_bwd(dtype, dqkv, qkv, cs, rq, rk, B, T, H, hd, base):
-    check(lib().gptk_rope_qknorm_bwd(dtype, _ptr(dqkv), _ptr(qkv), _ptr(cs), _ptr(rq), _ptr(rk), B, T, H, hd, base,
-                                     _stream()), "gptk_rope_qknorm_bwd")
+def rope_qknorm_bwd(dtype, dqkv, qkv, cs, rq, rk, B, T, H, hd, base, n_kv=None):
+    hk = H if n_kv is None else n_kv
+    check(lib().gptk_rope_qknorm_bwd(dtype, _ptr(dqkv), _ptr(qkv), _ptr(cs), _ptr(rq), _ptr(rk), B, T, H, hk, hd,
+                                     base, _stream()), "gptk_rope_qknorm_bwd")
 
 
 def cross_entropy(dtype, logits, targets, dlogits, row_loss, argmax, N, V, inv_n, err):

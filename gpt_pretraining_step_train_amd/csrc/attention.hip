@@ -1,7 +1,9 @@
 // Causal multi-head attention of the GPT step (flash form) on gfx950.
 //
-// Layouts: qkv [B*T][3*H*hd] (q at column h*hd, k at H*hd + h*hd, v at 2*H*hd + h*hd,
-// as the QKV projection writes it), o and dO [B*T][H*hd], lse and D [B][H][T] fp32.
+// Layouts: qkv [B*T][(H + 2 Hkv) hd] (query head h at column h hd, key head j at
+// H hd + j hd, value head j at (H + Hkv) hd + j hd, as the QKV projection writes it),
+// o and dO [B*T][H*hd], lse and D [B][H][T] fp32.  Query head h reads key/value head
+// h / G, G = H / Hkv (grouped-query attention; Hkv = H is multi-head attention).
 // lse is the natural-log log-sum-exp of the scaled scores q.k/sqrt(hd).
 //
 // All three bf16 kernels stage 64-row tiles row-major in LDS (double-buffered,
@@ -19,8 +21,10 @@
 //
 // Backward, without atomics: a dQ kernel per query block (recomputing P and dP; it
 // also forms D = rowsum(dO*O) for its queries) and then a dK/dV kernel per key block
-// (over query tiles) whose dK and dV accumulators live in different waves.  Blocks
-// of one sequence-head run on one XCD, so the tiles they stream stay in its L2.
+// (over query tiles, and over the G query heads of its key/value head) whose dK and
+// dV accumulators live in different waves.  Blocks of one sequence-head run on one
+// XCD, and so do the G query heads sharing a key/value head, so the tiles they
+// stream stay in its L2.
 #include <math.h>
 
 #include <type_traits>
@@ -112,16 +116,18 @@ __device__ inline bf16x8_t lds_tr_pair(const bf16_t* lo, const bf16_t* hi) {
 // Block coordinates (bx within a sequence-head, by = sequence-head) such that all
 // blocks of one sequence-head run on one XCD, one after another: workgroups go to the
 // 8 XCDs round-robin in linear launch order, so the K/V (or Q/dO) tiles every block of
-// a head streams stay in that XCD's L2.  Plain coordinates when gridDim.y % 8 != 0.
-__device__ inline void head_major_coords(int& bx, int& by) {
+// a head streams stay in that XCD's L2.  With G > 1 the G consecutive sequence-heads
+// that share one key/value head also follow each other on one XCD (when gridDim.y is
+// a multiple of 8 G).  Plain coordinates when gridDim.y % 8 != 0.
+__device__ inline void head_major_coords(int& bx, int& by, int G = 1) {
   const int nx = gridDim.x, ny = gridDim.y;
   if (ny % 8 != 0) {
     bx = blockIdx.x;
     by = blockIdx.y;
     return;
   }
-  const int lin = blockIdx.y * nx + blockIdx.x, j = lin >> 3;
-  by = (j / nx) * 8 + (lin & 7);
+  const int lin = blockIdx.y * nx + blockIdx.x, j = lin >> 3, r = j / nx, x = lin & 7;
+  by = ny % (8 * G) == 0 ? ((r / G) * 8 + x) * G + r % G : r * 8 + x;
   bx = j % nx;
 }
 
@@ -188,20 +194,21 @@ struct PairStager {
 template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H,
-                     int W) {
+                     int Hkv, int W) {
   constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int nqb = (T + BQ - 1) / BQ;
+  const int G = H / Hkv;
   int bx, bh;
-  head_major_coords(bx, bh);
+  head_major_coords(bx, bh, G);
   const int qb = nqb - 1 - bx;  // longest causal rows first
   const int b = bh / H, h = bh % H;
-  const long ld = 3L * H * HD;
+  const long ld = (long)(H + 2 * Hkv) * HD;
   const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
-  const bf16_t* K = Q + (long)H * HD;
-  const bf16_t* V = Q + 2L * H * HD;
+  const bf16_t* K = qkv + (long)b * T * ld + (long)(H + h / G) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
   const int q0 = qb * BQ + wave * 32;
   const int myq = q0 + lq;
 
@@ -364,20 +371,21 @@ template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dO,
                    const float* __restrict__ lse, float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H,
-                   int W) {
+                   int Hkv, int W) {
   constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const int nqb = (T + BQ - 1) / BQ;
+  const int Gq = H / Hkv;
   int bx, bh;
-  head_major_coords(bx, bh);
+  head_major_coords(bx, bh, Gq);
   const int qb = nqb - 1 - bx;
   const int b = bh / H, h = bh % H;
-  const long ld = 3L * H * HD, ldo = (long)H * HD;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
   const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
-  const bf16_t* K = Q + (long)H * HD;
-  const bf16_t* V = Q + 2L * H * HD;
+  const bf16_t* K = qkv + (long)b * T * ld + (long)(H + h / Gq) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
   const bf16_t* G = dO + (long)b * T * ldo + h * HD;
   const int q0 = qb * BQ + wave * 32, myq = q0 + lq;
 
@@ -496,12 +504,14 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
 // dK += dS^T Q) for the same 32 keys, each role 32 MFMAs per 64-query tile.  P
 // passes from the dV waves to the dK waves through LDS; each wave holds one 32x128
 // accumulator, so two waves fit on every SIMD; the Q and dO tiles are staged once
-// for all eight.  A lane owns a key.
+// for all eight.  A lane owns a key.  A block serves one key/value head: it walks the
+// query tiles of each of the G query heads that read it, one head after another,
+// into the same accumulators.
 template <int HD>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
                            const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
-                           int T, int H, int W) {
+                           int T, int H, int Hkv, int W) {
   constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
@@ -510,14 +520,15 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
   const bool dk_role = wave >= 4;
   const int kw = wave & 3;
-  int kb, bh;
-  head_major_coords(kb, bh);  // lowest key blocks carry the most query tiles: launched first
-  const int b = bh / H, h = bh % H;
-  const long ld = 3L * H * HD, ldo = (long)H * HD;
-  const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
-  const bf16_t* K = Q + (long)H * HD;
-  const bf16_t* V = Q + 2L * H * HD;
-  const bf16_t* G = dO + (long)b * T * ldo + h * HD;
+  int kb, bk;
+  head_major_coords(kb, bk);  // lowest key blocks carry the most query tiles: launched first
+  const int G = H / Hkv, b = bk / Hkv, hk = bk % Hkv;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
+  const bf16_t* Qb = qkv + (long)b * T * ld;  // query head qh at column qh * HD
+  const bf16_t* K = Qb + (long)(H + hk) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
+  const bf16_t* Gb = dO + (long)b * T * ldo;
+  const long lrow = (long)b * H * T;  // lse / D of query head qh at lrow + qh * T
   const int key0 = kb * BKEY + kw * 32, mykey = key0 + lq;
 
   bf16x8_t kf[NKK], vf[NKK];
@@ -553,16 +564,20 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   // query tiles from the block's first key to the last query that sees its last key
   const int nqt = min((T + BQT - 1) / BQT, (kb * BKEY + BKEY - 1 + Wn - 1) / BQT + 1);
   const int qt0 = (kb * BKEY) / BQT;
-  // 64-row Q and dO tiles and their lse / D values, prefetched one tile ahead
+  // steps: (query head hk G + s / nq, query tile qt0 + s % nq) for s < G nq
+  const int nq = nqt - qt0, nsteps = G * nq;
+  // 64-row Q and dO tiles and their lse / D values, prefetched one step ahead
   PairStager<HD, 512> stg;
   stg.init(ld, ldo, tid);
   float pl = 0.f, pd = 0.f;
-  auto load = [&](int q0) {
-    stg.load(rows_rsrc(Q, ld, q0, T, HD), rows_rsrc(G, ldo, q0, T, HD), tid);
+  auto load = [&](int sp) {
+    const int qh = hk * G + sp / nq, q0 = (qt0 + sp % nq) * BQT;
+    stg.load(rows_rsrc(Qb + qh * HD, ld, q0, T, HD), rows_rsrc(Gb + qh * HD, ldo, q0, T, HD), tid);
     if (tid < BQT) {
       const int q = q0 + tid;
-      pl = q < T ? lse[(long)bh * T + q] * LOG2E : 0.f;
-      pd = q < T ? Dv[(long)bh * T + q] : 0.f;
+      const long r = lrow + (long)qh * T + q;
+      pl = q < T ? lse[r] * LOG2E : 0.f;
+      pd = q < T ? Dv[r] : 0.f;
     }
   };
   auto store = [&](int buf) {
@@ -572,8 +587,8 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
       Ds[buf][tid] = pd;
     }
   };
-  if (qt0 < nqt) {
-    load(qt0 * BQT);
+  if (nsteps > 0) {
+    load(0);
     store(0);
   }
   __syncthreads();
@@ -581,10 +596,10 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   // 32-query halves and publish P (fp32, lane for lane: both roles hold the same keys
   // and queries in the same accumulator layout) while the dK waves form dP; phase 2,
   // after a barrier: dV += P^T dO, and dK += dS^T Q with dS = P (dP - D).
-  auto body = [&](auto cur_c, int qt) {
+  auto body = [&](auto cur_c, int sp) {
     constexpr int cur = decltype(cur_c)::value;
-    const int qb0 = qt * BQT;
-    if (qt + 1 < nqt) load(qb0 + BQT);
+    const int qb0 = (qt0 + sp % nq) * BQT;
+    if (sp + 1 < nsteps) load(sp + 1);
     // the same for both roles: the tile holds a query that sees one of the wave's keys
     const bool live = qb0 + BQT - 1 >= key0 && qb0 <= key0 + 31 + Wn - 1 && key0 < T;
     f32x16_t pd[2];  // P (dV waves) or dP (dK waves) of each 32-query half
@@ -647,21 +662,21 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
           acc[db] = mfma32x32x16_bf16(wa, lds_tr_pair(tp + tro[db][0], tp + tro[db][1]), acc[db]);
       }
     }
-    if (qt + 1 < nqt) store(cur ^ 1);
+    if (sp + 1 < nsteps) store(cur ^ 1);
     __syncthreads();
   };
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    body(std::integral_constant<int, 0>{}, qt);
-    if (qt + 1 < nqt) body(std::integral_constant<int, 1>{}, qt + 1);
+  for (int sp = 0; sp < nsteps; sp += 2) {
+    body(std::integral_constant<int, 0>{}, sp);
+    if (sp + 1 < nsteps) body(std::integral_constant<int, 1>{}, sp + 1);
   }
   const float scale = dk_role ? 1.f / sqrtf((float)HD) : 1.f;
-  const long part = dk_role ? (long)H * HD : 2L * H * HD;
+  const long col = (long)(dk_role ? H + hk : H + Hkv + hk) * HD;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = key0 + acc_row(lane, r);
-      if (key < T) dqkv[((long)b * T + key) * ld + part + h * HD + db * 32 + lq] = f2bf(acc[db][r] * scale);
+      if (key < T) dqkv[((long)b * T + key) * ld + col + db * 32 + lq] = f2bf(acc[db][r] * scale);
     }
 }
 
@@ -670,14 +685,14 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
 
 template <int HD>
 __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(const float* __restrict__ qkv, float* __restrict__ out,
-                                                          float* __restrict__ lse, int T, int H, int W) {
+                                                          float* __restrict__ lse, int T, int H, int Hkv, int W) {
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= T) return;
-  const long ld = 3L * H * HD;
+  const long ld = (long)(H + 2 * Hkv) * HD;
   const float* Q = qkv + (long)b * T * ld + h * HD;
-  const float* K = Q + (long)H * HD;
-  const float* V = Q + 2L * H * HD;
+  const float* K = qkv + (long)b * T * ld + (long)(H + h / (H / Hkv)) * HD;
+  const float* V = K + (long)Hkv * HD;
   const float sc = 1.f / sqrtf((float)HD);
   float q[HD], o[HD];
 #pragma unroll
@@ -703,14 +718,14 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(const float* __restric
 template <int HD>
 __global__ void __launch_bounds__(64) attn_bwd_dq_f32_kernel(const float* __restrict__ qkv, const float* __restrict__ dO,
                                                              const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                             float* __restrict__ dqkv, int T, int H, int W) {
+                                                             float* __restrict__ dqkv, int T, int H, int Hkv, int W) {
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= T) return;
-  const long ld = 3L * H * HD, ldo = (long)H * HD;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
   const float* Q = qkv + (long)b * T * ld + h * HD;
-  const float* K = Q + (long)H * HD;
-  const float* V = Q + 2L * H * HD;
+  const float* K = qkv + (long)b * T * ld + (long)(H + h / (H / Hkv)) * HD;
+  const float* V = K + (long)Hkv * HD;
   const float* G = dO + (long)b * T * ldo + h * HD;
   const float sc = 1.f / sqrtf((float)HD);
   float q[HD], g[HD], dq[HD];
@@ -733,20 +748,20 @@ __global__ void __launch_bounds__(64) attn_bwd_dq_f32_kernel(const float* __rest
   for (int d = 0; d < HD; ++d) op[d] = dq[d] * sc;
 }
 
+// one key per thread; the sums over queries run over the G query heads that read its
+// key/value head, one head after another
 template <int HD>
 __global__ void __launch_bounds__(64) attn_bwd_dkdv_f32_kernel(const float* __restrict__ qkv,
                                                                const float* __restrict__ dO,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ Dv, float* __restrict__ dqkv,
-                                                               int T, int H, int W) {
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+                                                               int T, int H, int Hkv, int W) {
+  const int bk = blockIdx.y, b = bk / Hkv, hk = bk % Hkv, G = H / Hkv;
   const int j = blockIdx.x * 64 + threadIdx.x;
   if (j >= T) return;
-  const long ld = 3L * H * HD, ldo = (long)H * HD;
-  const float* Q = qkv + (long)b * T * ld + h * HD;
-  const float* K = Q + (long)H * HD;
-  const float* V = Q + 2L * H * HD;
-  const float* G = dO + (long)b * T * ldo + h * HD;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
+  const float* K = qkv + (long)b * T * ld + (long)(H + hk) * HD;
+  const float* V = K + (long)Hkv * HD;
   const float sc = 1.f / sqrtf((float)HD);
   float k[HD], v[HD], dk[HD], dv[HD];
 #pragma unroll
@@ -754,74 +769,81 @@ __global__ void __launch_bounds__(64) attn_bwd_dkdv_f32_kernel(const float* __re
     k[d] = K[(long)j * ld + d]; v[d] = V[(long)j * ld + d]; dk[d] = 0.f; dv[d] = 0.f;
   }
   const int iend = W > 0 ? min(T, j + W) : T;  // queries that see key j
-  for (int i = j; i < iend; ++i) {
-    float s = 0.f, dp = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const int qh = hk * G + g;
+    const float* Q = qkv + (long)b * T * ld + qh * HD;
+    const float* Gr = dO + (long)b * T * ldo + qh * HD;
+    const long lrow = ((long)b * H + qh) * T;
+    for (int i = j; i < iend; ++i) {
+      float s = 0.f, dp = 0.f;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) {
-      s = fmaf(Q[(long)i * ld + d], k[d], s);
-      dp = fmaf(G[(long)i * ldo + d], v[d], dp);
-    }
-    const float p = expf(s * sc - lse[(long)bh * T + i]);
-    const float ds = p * (dp - Dv[(long)bh * T + i]);
+      for (int d = 0; d < HD; ++d) {
+        s = fmaf(Q[(long)i * ld + d], k[d], s);
+        dp = fmaf(Gr[(long)i * ldo + d], v[d], dp);
+      }
+      const float p = expf(s * sc - lse[lrow + i]);
+      const float ds = p * (dp - Dv[lrow + i]);
 #pragma unroll
-    for (int d = 0; d < HD; ++d) {
-      dv[d] = fmaf(p, G[(long)i * ldo + d], dv[d]);
-      dk[d] = fmaf(ds, Q[(long)i * ld + d], dk[d]);
+      for (int d = 0; d < HD; ++d) {
+        dv[d] = fmaf(p, Gr[(long)i * ldo + d], dv[d]);
+        dk[d] = fmaf(ds, Q[(long)i * ld + d], dk[d]);
+      }
     }
   }
-  float* rowp = dqkv + ((long)b * T + j) * ld + h * HD;
+  float* rowp = dqkv + ((long)b * T + j) * ld;
 #pragma unroll
   for (int d = 0; d < HD; ++d) {
-    rowp[(long)H * HD + d] = dk[d] * sc;
-    rowp[2L * H * HD + d] = dv[d];
+    rowp[(long)(H + hk) * HD + d] = dk[d] * sc;
+    rowp[(long)(H + Hkv + hk) * HD + d] = dv[d];
   }
 }
 
 template <int HD>
-void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int W, hipStream_t st) {
+void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int W, hipStream_t st) {
   if (at == ACT_BF16)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st,
-                       (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, W);
+                       (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, Hkv, W);
   else
     hipLaunchKernelGGL(attn_fwd_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
-                       (float*)o, lse, T, H, W);
+                       (float*)o, lse, T, H, Hkv, W);
 }
 
 template <int HD>
 void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
-                  int B, int T, int H, int W, hipStream_t st) {
+                  int B, int T, int H, int Hkv, int W, hipStream_t st) {
   if (at == ACT_BF16) {
     // the dQ kernel also writes D = rowsum(dO * O) for the dK/dV kernel
     hipLaunchKernelGGL(attn_bwd_dq_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st, (const bf16_t*)qkv,
-                       (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, W);
-    hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(512), 0, st,
-                       (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, W);
+                       (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
+    hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * Hkv), dim3(512), 0, st,
+                       (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
-                       (const float*)dO, lse, D, (float*)dqkv, T, H, W);
-    hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st,
-                       (const float*)qkv, (const float*)dO, lse, D, (float*)dqkv, T, H, W);
+                       (const float*)dO, lse, D, (float*)dqkv, T, H, Hkv, W);
+    hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<HD>, dim3((T + 63) / 64, B * Hkv), dim3(64), 0, st,
+                       (const float*)qkv, (const float*)dO, lse, D, (float*)dqkv, T, H, Hkv, W);
   }
 }
 
 }  // namespace
 
-void launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int hd, int window,
+// Hkv must divide H (the callers validate it)
+void launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int hd, int window,
                      hipStream_t st) {
   if (B * T * H == 0) return;
-  if (hd == 128) fwd_dispatch<128>(qkv, o, lse, at, B, T, H, window, st);
-  else if (hd == 64) fwd_dispatch<64>(qkv, o, lse, at, B, T, H, window, st);
-  else if (hd == 32) fwd_dispatch<32>(qkv, o, lse, at, B, T, H, window, st);
+  if (hd == 128) fwd_dispatch<128>(qkv, o, lse, at, B, T, H, Hkv, window, st);
+  else if (hd == 64) fwd_dispatch<64>(qkv, o, lse, at, B, T, H, Hkv, window, st);
+  else if (hd == 32) fwd_dispatch<32>(qkv, o, lse, at, B, T, H, Hkv, window, st);
 }
 
 void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
-                     int B, int T, int H, int hd, int window, hipStream_t st) {
+                     int B, int T, int H, int Hkv, int hd, int window, hipStream_t st) {
   if (B * T * H == 0) return;
   const int N = B * T;
   if (at != ACT_BF16)  // the bf16 dQ kernel forms D itself
     hipLaunchKernelGGL(attn_bwd_prep_kernel<float>, dim3((N * H + 3) / 4), dim3(256), 0, st, (const float*)o,
                        (const float*)dO, D, N, T, H, hd);
-  if (hd == 128) bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, window, st);
-  else if (hd == 64) bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, window, st);
-  else if (hd == 32) bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, window, st);
+  if (hd == 128) bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st);
+  else if (hd == 64) bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st);
+  else if (hd == 32) bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st);
 }

@@ -141,17 +141,25 @@ __global__ void rope_table_kernel(float* cs, int T, int hd, float base) {
 }
 
 // q and k of every (token, head): rotate half-split pairs, then RMS-normalise the
-// head vector; in place in the qkv buffer [B*T][3*H*hd]
+// head vector; in place in the qkv buffer [B*T][(H + 2 Hkv) hd] (q heads, then Hkv
+// k heads, then Hkv v heads).  A "slot" s < H + Hkv names one head vector to
+// normalise: s < H is query head s, s >= H key head s - H; it starts at column s hd.
+template <typename F>
+__device__ inline F* rstd_slot(F* rq, F* rk, long n, int s, int H, int Hkv) {
+  return s < H ? rq + n * H + s : rk + n * Hkv + (s - H);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(T* __restrict__ qkv, const float* __restrict__ cs,
                                                               float* __restrict__ rq, float* __restrict__ rk, int N,
-                                                              int Tlen, int H, int hd, float eps) {
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, head, q/k)
+                                                              int Tlen, int H, int Hkv, int hd, float eps) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, slot)
   const int lane = threadIdx.x & 63;
-  if (w >= N * H * 2) return;
-  const int which = w & 1, nh = w >> 1, n = nh / H, h = nh % H;
+  const int S = H + Hkv;
+  if (w >= N * S) return;
+  const int n = w / S, sl = w % S;
   const int t = n % Tlen, half = hd / 2;
-  T* p = qkv + (long)n * 3 * H * hd + which * H * hd + h * hd;
+  T* p = qkv + (long)n * (H + 2 * Hkv) * hd + (long)sl * hd;
   float y1[2], y2[2];
   float ss = 0.f;
 #pragma unroll
@@ -176,7 +184,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_fwd_kernel(T* __restrict__ qk
       st<T>(p + i + half, y2[j] * r);
     }
   }
-  if (lane == 0) (which ? rk : rq)[nh] = r;
+  if (lane == 0) *rstd_slot(rq, rk, n, sl, H, Hkv) = r;
 }
 
 // backward: dz = r (dy - y mean(dy y)) in the rotated frame, then rotate by -angle
@@ -184,16 +192,17 @@ template <typename T>
 __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
                                                               const float* __restrict__ cs, const float* __restrict__ rq,
                                                               const float* __restrict__ rk, int N, int Tlen, int H,
-                                                              int hd) {
+                                                              int Hkv, int hd) {
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (w >= N * H * 2) return;
-  const int which = w & 1, nh = w >> 1, n = nh / H, h = nh % H;
+  const int S = H + Hkv;
+  if (w >= N * S) return;
+  const int n = w / S, sl = w % S;
   const int t = n % Tlen, half = hd / 2;
-  const long off = (long)n * 3 * H * hd + which * H * hd + h * hd;
+  const long off = (long)n * (H + 2 * Hkv) * hd + (long)sl * hd;
   T* dp = dqkv + off;
   const T* yp = qkv + off;
-  const float r = (which ? rk : rq)[nh];
+  const float r = *rstd_slot(rq, rk, n, sl, H, Hkv);
   float g1[2], g2[2], a1[2], a2[2];
   float dot = 0.f;
 #pragma unroll
@@ -245,13 +254,14 @@ __device__ inline float group_sum(float v) {
 template <int HD>
 __global__ void __launch_bounds__(256) rope_qknorm_fwd_vec_kernel(bf16_t* __restrict__ qkv, const float* __restrict__ cs,
                                                                   float* __restrict__ rq, float* __restrict__ rk, int N,
-                                                                  int Tlen, int H, float eps) {
+                                                                  int Tlen, int H, int Hkv, float eps) {
   constexpr int G = HD / 16, HALF = HD / 2;
-  const long gid = ((long)blockIdx.x * 256 + threadIdx.x) / G;  // (token, q|k, head), heads fastest
+  const long gid = ((long)blockIdx.x * 256 + threadIdx.x) / G;  // (token, slot), slots fastest
   const int j = threadIdx.x % G;
-  if (gid >= (long)N * 2 * H) return;  // whole groups leave together (G divides 64)
-  const int n = (int)(gid / (2 * H)), rem = (int)(gid % (2 * H)), which = rem / H, h = rem % H;
-  bf16_t* p = qkv + (long)n * 3 * H * HD + which * H * HD + h * HD;
+  const int S = H + Hkv;
+  if (gid >= (long)N * S) return;  // whole groups leave together (G divides 64)
+  const int n = (int)(gid / S), sl = (int)(gid % S);
+  bf16_t* p = qkv + (long)n * (H + 2 * Hkv) * HD + (long)sl * HD;
   float x1[8], x2[8];
   unpack8(*reinterpret_cast<const uint4*>(p + 8 * j), x1);
   unpack8(*reinterpret_cast<const uint4*>(p + HALF + 8 * j), x2);
@@ -275,7 +285,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_fwd_vec_kernel(bf16_t* __rest
   for (int i = 0; i < 8; ++i) { y1[i] *= r; y2[i] *= r; }
   *reinterpret_cast<uint4*>(p + 8 * j) = pack8f(y1);
   *reinterpret_cast<uint4*>(p + HALF + 8 * j) = pack8f(y2);
-  if (j == 0) (which ? rk : rq)[(long)n * H + h] = r;
+  if (j == 0) *rstd_slot(rq, rk, n, sl, H, Hkv) = r;
 }
 
 template <int HD>
@@ -283,13 +293,15 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_vec_kernel(bf16_t* __rest
                                                                   const bf16_t* __restrict__ qkv,
                                                                   const float* __restrict__ cs,
                                                                   const float* __restrict__ rq,
-                                                                  const float* __restrict__ rk, int N, int Tlen, int H) {
+                                                                  const float* __restrict__ rk, int N, int Tlen, int H,
+                                                                  int Hkv) {
   constexpr int G = HD / 16, HALF = HD / 2;
   const long gid = ((long)blockIdx.x * 256 + threadIdx.x) / G;
   const int j = threadIdx.x % G;
-  if (gid >= (long)N * 2 * H) return;
-  const int n = (int)(gid / (2 * H)), rem = (int)(gid % (2 * H)), which = rem / H, h = rem % H;
-  const long off = (long)n * 3 * H * HD + which * H * HD + h * HD;
+  const int S = H + Hkv;
+  if (gid >= (long)N * S) return;
+  const int n = (int)(gid / S), sl = (int)(gid % S);
+  const long off = (long)n * (H + 2 * Hkv) * HD + (long)sl * HD;
   bf16_t* dp = dqkv + off;
   const bf16_t* yp = qkv + off;
   float g1[8], g2[8], a1[8], a2[8];
@@ -301,7 +313,7 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_vec_kernel(bf16_t* __rest
 #pragma unroll
   for (int i = 0; i < 8; ++i) dot += g1[i] * a1[i] + g2[i] * a2[i];
   dot = group_sum<HD>(dot) / (float)HD;
-  const float r = (which ? rk : rq)[(long)n * H + h];
+  const float r = *rstd_slot(rq, rk, n, sl, H, Hkv);
   const float4* c4 = reinterpret_cast<const float4*>(cs + 2 * ((long)(n % Tlen) * HALF + 8 * j));
   float o1[8], o2[8];
 #pragma unroll
@@ -974,53 +986,53 @@ void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st) {
 }
 
 template <int HD>
-static void rope_fwd_vec(bf16_t* qkv, const float* cs, float* rq, float* rk, int N, int T, int H, float eps,
+static void rope_fwd_vec(bf16_t* qkv, const float* cs, float* rq, float* rk, int N, int T, int H, int Hkv, float eps,
                          hipStream_t st) {
-  const long threads = (long)N * 2 * H * (HD / 16);
+  const long threads = (long)N * (H + Hkv) * (HD / 16);
   hipLaunchKernelGGL(rope_qknorm_fwd_vec_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, qkv, cs,
-                     rq, rk, N, T, H, eps);
+                     rq, rk, N, T, H, Hkv, eps);
 }
 
 template <int HD>
 static void rope_bwd_vec(bf16_t* dqkv, const bf16_t* qkv, const float* cs, const float* rq, const float* rk, int N,
-                         int T, int H, hipStream_t st) {
-  const long threads = (long)N * 2 * H * (HD / 16);
+                         int T, int H, int Hkv, hipStream_t st) {
+  const long threads = (long)N * (H + Hkv) * (HD / 16);
   hipLaunchKernelGGL(rope_qknorm_bwd_vec_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dqkv,
-                     qkv, cs, rq, rk, N, T, H);
+                     qkv, cs, rq, rk, N, T, H, Hkv);
 }
 
-void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float* rk, int B, int T, int H, int hd,
-                            float eps, hipStream_t st) {
+void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float* rk, int B, int T, int H, int Hkv,
+                            int hd, float eps, hipStream_t st) {
   const int N = B * T;
   if (at == ACT_BF16 && (hd == 128 || hd == 64 || hd == 32)) {
-    if (hd == 128) rope_fwd_vec<128>((bf16_t*)qkv, cs, rq, rk, N, T, H, eps, st);
-    else if (hd == 64) rope_fwd_vec<64>((bf16_t*)qkv, cs, rq, rk, N, T, H, eps, st);
-    else rope_fwd_vec<32>((bf16_t*)qkv, cs, rq, rk, N, T, H, eps, st);
+    if (hd == 128) rope_fwd_vec<128>((bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, eps, st);
+    else if (hd == 64) rope_fwd_vec<64>((bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, eps, st);
+    else rope_fwd_vec<32>((bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, eps, st);
     return;
   }
-  dim3 g((N * H * 2 + 3) / 4), b(256);
+  dim3 g((N * (H + Hkv) + 3) / 4), b(256);
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)qkv, cs, rq, rk, N, T, H, hd, eps);
+    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, hd, eps);
   else
-    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<float>, g, b, 0, st, (float*)qkv, cs, rq, rk, N, T, H, hd, eps);
+    hipLaunchKernelGGL(rope_qknorm_fwd_kernel<float>, g, b, 0, st, (float*)qkv, cs, rq, rk, N, T, H, Hkv, hd, eps);
 }
 
 void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs, const float* rq, const float* rk,
-                            int B, int T, int H, int hd, hipStream_t st) {
+                            int B, int T, int H, int Hkv, int hd, hipStream_t st) {
   const int N = B * T;
   if (at == ACT_BF16 && (hd == 128 || hd == 64 || hd == 32)) {
-    if (hd == 128) rope_bwd_vec<128>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, st);
-    else if (hd == 64) rope_bwd_vec<64>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, st);
-    else rope_bwd_vec<32>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, st);
+    if (hd == 128) rope_bwd_vec<128>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st);
+    else if (hd == 64) rope_bwd_vec<64>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st);
+    else rope_bwd_vec<32>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st);
     return;
   }
-  dim3 g((N * H * 2 + 3) / 4), b(256);
+  dim3 g((N * (H + Hkv) + 3) / 4), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(rope_qknorm_bwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N,
-                       T, H, hd);
+                       T, H, Hkv, hd);
   else
     hipLaunchKernelGGL(rope_qknorm_bwd_kernel<float>, g, b, 0, st, (float*)dqkv, (const float*)qkv, cs, rq, rk, N, T,
-                       H, hd);
+                       H, Hkv, hd);
 }
 
 template <typename T>

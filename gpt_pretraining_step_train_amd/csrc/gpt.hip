@@ -37,15 +37,22 @@ struct Plan {
   }
 };
 
+// key/value heads and the rows of Wk and Wv (grouped-query attention; n_kv_head = 0
+// means one key/value head per query head)
+inline int kv_heads(const gpt_cfg& c) { return c.n_kv_head > 0 ? c.n_kv_head : c.n_head; }
+inline size_t kv_dim(const gpt_cfg& c) { return (size_t)kv_heads(c) * c.head_dim; }
+// columns of the fused QKV projection output: q (d), k and v (kv_dim each)
+inline size_t qkv_dim(const gpt_cfg& c) { return (size_t)c.d_model + 2 * kv_dim(c); }
+
 // element offsets of the six block matrices inside one layer's slice
 struct LayerOffs {
   size_t q, k, v, o, w1, w2, stride;
 };
 inline LayerOffs layer_offs(const gpt_cfg& c) {
-  const size_t d = c.d_model, F = c.d_ff;
+  const size_t d = c.d_model, F = c.d_ff, dk = kv_dim(c);
   LayerOffs L;
-  L.q = 0; L.k = d * d; L.v = 2 * d * d; L.o = 3 * d * d; L.w1 = 4 * d * d; L.w2 = 4 * d * d + F * d;
-  L.stride = 4 * d * d + 2 * d * F;
+  L.q = 0; L.k = d * d; L.v = d * d + dk * d; L.o = d * d + 2 * dk * d; L.w1 = L.o + d * d; L.w2 = L.w1 + F * d;
+  L.stride = L.w2 + d * F;
   return L;
 }
 
@@ -70,7 +77,7 @@ int act_of(const gpt_cfg& c) { return c.precision == GPT_FP32 ? ACT_F32 : ACT_BF
 
 size_t wgrad_ws_bytes(const gpt_cfg& c) {
   const int N = c.batch * c.seq_len, d = c.d_model, F = c.d_ff, V = c.vocab;
-  const int shapes[5][2] = {{d, F}, {F, d}, {d, d}, {3 * d, d}, {V, d}};
+  const int shapes[5][2] = {{d, F}, {F, d}, {d, d}, {(int)qkv_dim(c), d}, {V, d}};
   size_t best = 0;
   for (auto& s : shapes) {
     GemmArgs p;
@@ -99,9 +106,9 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.hs = P.add((2 * L + 1) * N * d * 4);
   O.a = P.add(L * N * d * es);
   O.rstd_a = P.add(L * N * 4);
-  O.qkv = P.add(L * N * 3 * d * es);
+  O.qkv = P.add(L * N * qkv_dim(c) * es);
   O.rq = P.add(L * N * H * 4);
-  O.rk = P.add(L * N * H * 4);
+  O.rk = P.add(L * N * kv_heads(c) * 4);
   O.o = P.add(L * N * d * es);
   O.lse = P.add(L * B * H * T * 4);
   O.m = P.add(L * N * d * es);
@@ -119,7 +126,7 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.dh_act = P.add(N * d * es);
   O.dtmp = P.add(N * d * 4);
   O.dbig = P.add(N * F * es);
-  O.dqkv = P.add(N * 3 * d * es);
+  O.dqkv = P.add(N * qkv_dim(c) * es);
   O.do_act = P.add(N * d * es);
   O.Dbuf = P.add(B * H * T * 4);
   O.splitws_bytes = wgrad_ws_bytes(c);
@@ -141,7 +148,7 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.mat_off = P.add(6 * L * 8);
   O.mat_size = P.add(6 * L * 8);
   if (c.precision == GPT_FP8) {
-    const size_t wide = std::max(std::max(3 * d, F), V);
+    const size_t wide = std::max(std::max(qkv_dim(c), F), V);
     O.q8c = O.xq8t = 0;
     O.wq8 = P.add(nBlk + nU);
     O.wtq8 = P.add(nBlk + nU);
@@ -242,7 +249,7 @@ int run_gemm(gpt_model* M, GemmArgs p, hipStream_t st, bool allow_split) {
 bool same_shape(const gpt_cfg& a, const gpt_cfg& b) {
   return a.depth == b.depth && a.d_model == b.d_model && a.n_head == b.n_head && a.head_dim == b.head_dim &&
          a.d_ff == b.d_ff && a.vocab == b.vocab && a.seq_len == b.seq_len && a.batch == b.batch &&
-         a.precision == b.precision && a.attn_window == b.attn_window;
+         a.precision == b.precision && a.attn_window == b.attn_window && kv_heads(a) == kv_heads(b);
 }
 
 // element offset of tensor id inside the parameter/gradient vector, and its shape
@@ -256,7 +263,7 @@ bool tensor_loc(const gpt_cfg& c, int id, size_t* off, int* rows, int* cols) {
   const size_t b = V * d + l * lo.stride;
   const size_t o6[6] = {lo.q, lo.k, lo.v, lo.o, lo.w1, lo.w2};
   *off = b + o6[j];
-  *rows = j == 4 ? (int)F : (int)d;
+  *rows = j == 4 ? (int)F : (j == 1 || j == 2) ? (int)kv_dim(c) : (int)d;
   *cols = j == 5 ? (int)F : (int)d;
   return true;
 }
@@ -287,6 +294,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->ns_split_steps = 4;
   out->fp8_gemms = GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD;
   out->attn_window = 0;
+  out->n_kv_head = 0;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
   out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
@@ -311,6 +319,7 @@ int gpt_cfg_validate(const gpt_cfg* c) {
   if (c->ns_steps < 0 || c->ns_steps > 5 || c->ns_split_steps < 0) return GPT_ERR_ARG;
   if (c->fp8_gemms & ~(GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD)) return GPT_ERR_ARG;
   if (c->attn_window < 0) return GPT_ERR_ARG;
+  if (c->n_kv_head < 0 || c->n_kv_head > c->n_head || c->n_head % kv_heads(*c) != 0) return GPT_ERR_SHAPE;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
 }
@@ -386,7 +395,7 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
     const size_t o6[6] = {M->lo.q, M->lo.k, M->lo.v, M->lo.o, M->lo.w1, M->lo.w2};
     for (int j = 0; j < 6; ++j) {
       M->moff.push_back((long)(b + o6[j]));
-      M->msize.push_back(j < 4 ? (long)d * d : (long)d * F);
+      M->msize.push_back(j == 1 || j == 2 ? (long)kv_dim(*cfg) * d : j < 4 ? (long)d * d : (long)d * F);
     }
   }
   // weights: one counter-based stream per tensor id
@@ -438,7 +447,7 @@ static WInfo winfo(const gpt_model* M, int w) {
   const int l = w / 4, j = w % 4, d = c.d_model, F = c.d_ff;
   const size_t b = (size_t)l * M->lo.stride;
   switch (j) {
-    case 0: return {b + M->lo.q, 3 * d, d};
+    case 0: return {b + M->lo.q, (int)qkv_dim(c), d};
     case 1: return {b + M->lo.o, d, d};
     case 2: return {b + M->lo.w1, F, d};
     default: return {b + M->lo.w2, d, F};
@@ -546,6 +555,7 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
 static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
   const gpt_cfg& c = M->cfg;
   const int N = M->N, d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth, H = c.n_head, hd = c.head_dim;
+  const int Hkv = kv_heads(c), QD = (int)qkv_dim(c);  // key/value heads, fused QKV width
   const int B = c.batch, T = c.seq_len;
   const int at = M->at;
   const size_t es = M->es;
@@ -569,23 +579,23 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   launch_embed_gather(tok, M->params(), hsl(0), N, d, V, err, st);
   for (int l = 0; l < L; ++l) {
     void* a = actp(O.a, (size_t)l * N * d);
-    void* qkv = actp(O.qkv, (size_t)l * N * 3 * d);
+    void* qkv = actp(O.qkv, (size_t)l * N * QD);
     void* o = actp(O.o, (size_t)l * N * d);
     void* m = actp(O.m, (size_t)l * N * d);
     void* u = actp(O.u, (size_t)l * N * F);
     void* g = actp(O.g, (size_t)l * N * F);
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
-    float* rk = M->at_off<float>(O.rk) + (size_t)l * N * H;
+    float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
     launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
     {
       GemmArgs p;  // qkv = a Wqkv^T
-      p.M = N; p.N = 3 * d; p.K = d; p.A = a; p.lda = d;
-      p.outA = qkv; p.ldoa = 3 * d;
+      p.M = N; p.N = QD; p.K = d; p.A = a; p.lda = d;
+      p.outA = qkv; p.ldoa = QD;
       if ((rc = lin_fwd(M, p, 4 * l + 0, st))) return rc;
     }
-    launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, eps, st);
-    launch_attn_fwd(qkv, o, lse, at, B, T, H, hd, c.attn_window, st);
+    launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, eps, st);
+    launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st);
     {
       GemmArgs p;  // h' = h + o Wo^T
       p.M = N; p.N = d; p.K = d; p.A = o; p.lda = d;
@@ -641,13 +651,13 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   for (int l = L - 1; l >= 0; --l) {
     const size_t wl = (size_t)l * M->lo.stride;
     void* a = actp(O.a, (size_t)l * N * d);
-    void* qkv = actp(O.qkv, (size_t)l * N * 3 * d);
+    void* qkv = actp(O.qkv, (size_t)l * N * QD);
     void* o = actp(O.o, (size_t)l * N * d);
     void* m = actp(O.m, (size_t)l * N * d);
     void* u = actp(O.u, (size_t)l * N * F);
     void* g = actp(O.g, (size_t)l * N * F);
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
-    float* rk = M->at_off<float>(O.rk) + (size_t)l * N * H;
+    float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
     {
       GemmArgs pd;  // dW2 = dY^T g ; du = (dY W2) * 2 relu(u)
@@ -670,13 +680,13 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       pd.outA = do_act; pd.ldoa = d;
       if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st))) return rc;
     }
-    launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, hd, c.attn_window, st);
-    launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, hd, st);
+    launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, Hkv, hd, c.attn_window, st);
+    launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, st);
     {
       GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
-      pd.M = N; pd.N = d; pd.K = 3 * d;
+      pd.M = N; pd.N = d; pd.K = QD;
       pd.outF = dtmp; pd.ldo = d;
-      if ((rc = lin_bwd(M, dqkv, 3 * d, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
+      if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
     }
     launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur], dh[cur ^ 1], dh_act,
                        at, N, d, eps, st);
@@ -757,23 +767,34 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   launch_momentum(mom, M->blk(M->grads()), c.muon_momentum, M->nBlk, st);
   launch_matrix_sumsq(mom, M->at_off<long>(O.mat_off), M->at_off<long>(O.mat_size), 6 * L,
                       M->at_off<double>(O.ss_part), kSumsqParts, M->at_off<double>(O.ss), st);
-  // X0 into the NS workspace: squares first (q, k, v, o of each layer), then the
-  // d x F pairs, every matrix in its wide orientation
+  // X0 into the NS workspace, every matrix in its wide orientation, one batch per
+  // shape: the d x d squares (q, k, v, o of each layer; only q and o when grouped-query
+  // attention makes Wk, Wv kv x d, which then form their own batch), then the d x F
+  // pairs
+  const int kv = (int)kv_dim(c);
+  const bool kvsq = kv == d;  // k and v join the squares
+  const size_t nsq = (size_t)(kvsq ? 4 : 2) * L * d * d, nkv = kvsq ? 0 : (size_t)2 * L * kv * d;
   auto xdst = [&](int l, int j) -> size_t {
-    if (j < 4) return (size_t)(4 * l + j) * d * d;
-    return (size_t)4 * L * d * d + (size_t)(2 * l + (j - 4)) * s * lw;
+    if (j < 4 && kvsq) return (size_t)(4 * l + j) * d * d;
+    if (j == 0 || j == 3) return (size_t)(2 * l + (j == 3)) * d * d;
+    if (j < 4) return nsq + (size_t)(2 * l + (j - 1)) * kv * d;
+    return nsq + nkv + (size_t)(2 * l + (j - 4)) * s * lw;
   };
-  auto transposed = [&](int j) { return (j == 4 && F > d) || (j == 5 && d > F); };
+  auto mrows = [&](int j) { return j == 4 ? F : (j == 1 || j == 2) ? kv : d; };
+  auto transposed = [&](int j) { return (j == 4 && F > d) || (j == 5 && d > F); };  // kv <= d: k, v are wide
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
-      const int rows = j == 4 ? F : d, cols = j == 5 ? F : d;
+      const int rows = mrows(j), cols = j == 5 ? F : d;
       const size_t dst = xdst(l, j);
       launch_ns_normalize(mom + M->moff[6 * l + j], M->at_off<double>(O.ss), 6 * l + j, 1e-7f, rows, cols,
                           transposed(j), xf + dst, xa[0] + dst * es, nsplit > 0 ? xl[0] + dst * es : nullptr, M->at,
                           st);
     }
   struct Batch { int s, l, nb; size_t off; };
-  const Batch batches[2] = {{d, d, 4 * L, 0}, {s, lw, 2 * L, (size_t)4 * L * d * d}};
+  const Batch all_batches[3] = {{d, d, (kvsq ? 4 : 2) * L, 0}, {kv, d, 2 * L, nsq}, {s, lw, 2 * L, nsq + nkv}};
+  std::vector<Batch> batches = {all_batches[0]};
+  if (!kvsq) batches.push_back(all_batches[1]);
+  batches.push_back(all_batches[2]);
   float* Af = M->at_off<float>(O.Af);
   void* Aa = M->base + O.Aa;
   void* Ba = M->base + O.Ba;
@@ -830,7 +851,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   float* wblk = M->blk(M->params());
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
-      const int rows = j == 4 ? F : d, cols = j == 5 ? F : d;
+      const int rows = mrows(j), cols = j == 5 ? F : d;
       const size_t mo = M->moff[6 * l + j];
       launch_muon_apply(wblk + mo, M->at == ACT_BF16 ? M->wact(mo) : nullptr, M->at, xf + xdst(l, j), lr, rows, cols,
                         transposed(j), st);
@@ -1002,21 +1023,25 @@ static int attn_ok(int dtype, int hd) {
   return GPT_OK;
 }
 
-int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, int window,
+// key/value heads: 1 <= Hkv <= H with H % Hkv == 0 (any Hkv when H = 0)
+static bool kv_heads_ok(int H, int Hkv) { return H == 0 ? Hkv >= 0 : (Hkv >= 1 && Hkv <= H && H % Hkv == 0); }
+
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
                   void* stream) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
-  if (B < 0 || T < 0 || H < 0 || window < 0 || !qkv || !o || !lse) return GPT_ERR_ARG;
-  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, hd, window, (hipStream_t)stream);
+  if (B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv) || window < 0 || !qkv || !o || !lse) return GPT_ERR_ARG;
+  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, Hkv, hd, window, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
 int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv,
-                  int B, int T, int H, int hd, int window, void* stream) {
+                  int B, int T, int H, int Hkv, int hd, int window, void* stream) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
-  if (B < 0 || T < 0 || H < 0 || window < 0 || !qkv || !o || !dO || !lse || !D || !dqkv) return GPT_ERR_ARG;
-  launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, hd, window, (hipStream_t)stream);
+  if (B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv) || window < 0 || !qkv || !o || !dO || !lse || !D || !dqkv)
+    return GPT_ERR_ARG;
+  launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, Hkv, hd, window, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
@@ -1035,23 +1060,23 @@ int gptk_rmsnorm_bwd(int dtype, const float* dy, const float* x, const float* rs
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
-int gptk_rope_qknorm_fwd(int dtype, void* qkv, float* cs, float* rq, float* rk, int B, int T, int H, int hd,
+int gptk_rope_qknorm_fwd(int dtype, void* qkv, float* cs, float* rq, float* rk, int B, int T, int H, int Hkv, int hd,
                          float base, float eps, void* stream) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
-  if (!qkv || !cs || !rq || !rk || B < 0 || T < 0 || H < 0) return GPT_ERR_ARG;
+  if (!qkv || !cs || !rq || !rk || B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv)) return GPT_ERR_ARG;
   launch_rope_table(cs, T, hd, base, (hipStream_t)stream);
-  launch_rope_qknorm_fwd(qkv, act_type(dtype), cs, rq, rk, B, T, H, hd, eps, (hipStream_t)stream);
+  launch_rope_qknorm_fwd(qkv, act_type(dtype), cs, rq, rk, B, T, H, Hkv, hd, eps, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
 int gptk_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, float* cs, const float* rq, const float* rk, int B,
-                         int T, int H, int hd, float base, void* stream) {
+                         int T, int H, int Hkv, int hd, float base, void* stream) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
-  if (!dqkv || !qkv || !cs || !rq || !rk || B < 0 || T < 0 || H < 0) return GPT_ERR_ARG;
+  if (!dqkv || !qkv || !cs || !rq || !rk || B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv)) return GPT_ERR_ARG;
   launch_rope_table(cs, T, hd, base, (hipStream_t)stream);
-  launch_rope_qknorm_bwd(dqkv, qkv, act_type(dtype), cs, rq, rk, B, T, H, hd, (hipStream_t)stream);
+  launch_rope_qknorm_bwd(dqkv, qkv, act_type(dtype), cs, rq, rk, B, T, H, Hkv, hd, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 

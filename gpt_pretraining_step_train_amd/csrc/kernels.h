@@ -64,10 +64,11 @@ void launch_rmsnorm_fwd(const float* x, void* y, int ytype, float* rstd, int N, 
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres,
                         float* dx, void* dx_act, int act_type, int N, int d, float eps, hipStream_t st);
 void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st);
+// qkv rows are [H q heads | Hkv k heads | Hkv v heads] x hd; rstd_q is [B*T][H], rstd_k [B*T][Hkv]
 void launch_rope_qknorm_fwd(void* qkv, int act_type, const float* cs, float* rstd_q, float* rstd_k,
-                            int B, int T, int H, int hd, float eps, hipStream_t st);
+                            int B, int T, int H, int Hkv, int hd, float eps, hipStream_t st);
 void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int act_type, const float* cs,
-                            const float* rstd_q, const float* rstd_k, int B, int T, int H, int hd,
+                            const float* rstd_q, const float* rstd_k, int B, int T, int H, int Hkv, int hd,
                             hipStream_t st);
 void launch_cross_entropy(const float* logits, const int32_t* targets, void* dlogits, int act_type,
                           float* row_loss, int32_t* argmax, int N, int V, float inv_n, int* err_flag,
@@ -106,8 +107,9 @@ void launch_amax(const void* x, int in_type, long rows, long cols, long ld, unsi
 void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, const unsigned* amax_bits,
                        uint8_t* q, long ldq, uint8_t* qt, long ldqt, float* inv_scale, hipStream_t st);
 
-// attention (window > 0: query i sees keys i - window < j <= i; 0: all j <= i)
-void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int hd, int window,
-                     hipStream_t st);
+// attention (window > 0: query i sees keys i - window < j <= i; 0: all j <= i).  qkv rows are
+// [H q heads | Hkv k heads | Hkv v heads] x hd; query head h reads key/value head h / (H / Hkv).
+void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int Hkv, int hd,
+                     int window, hipStream_t st);
 void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,
-                     void* dqkv, int act_type, int B, int T, int H, int hd, int window, hipStream_t st);
+                     void* dqkv, int act_type, int B, int T, int H, int Hkv, int hd, int window, hipStream_t st);

@@ -81,6 +81,10 @@ typedef struct gpt_cfg {
   int32_t attn_window;  /* sliding-window attention: query i sees keys i - attn_window < j <= i
                            (flash-attention's window_size = (attn_window - 1, 0)); 0 (the
                            default) = every earlier key; negative: GPT_ERR_ARG */
+  int32_t n_kv_head;  /* grouped-query attention: key/value heads, each shared by n_head /
+                         n_kv_head query heads (query head h uses key/value head
+                         h / (n_head / n_kv_head)); Wk, Wv are (n_kv_head * head_dim) x d.
+                         0 (the default) = n_head; must divide n_head, else GPT_ERR_SHAPE */
 } gpt_cfg;
 
 enum { GPT_FP8_FWD = 1, GPT_FP8_WGRAD = 2, GPT_FP8_DGRAD = 4 };
@@ -219,16 +223,20 @@ int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t
  * the reduction index contiguous; NN: B transposed on load; TN: both) */
 const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch);
 
-/* causal attention over qkv act [B*T][3*H*hd] -> o act [B*T][H*hd], lse fp32
+/* causal attention over qkv act [B*T][(H + 2*Hkv)*hd] (H query heads, then Hkv key
+ * heads, then Hkv value heads, hd columns each) -> o act [B*T][H*hd], lse fp32
  * [B][H][T] (natural log of the sum of exp of q.k/sqrt(hd)). hd in {32,64,128}.
- * window > 0: query i attends to keys i - window < j <= i (sliding window); 0: all
- * j <= i; negative: GPT_ERR_ARG. */
-int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int hd, int window,
+ * Query head h attends with key/value head h / (H / Hkv): Hkv = H is multi-head
+ * attention, Hkv < H grouped-query attention (H % Hkv != 0, Hkv < 1 or Hkv > H:
+ * GPT_ERR_ARG).  window > 0: query i attends to keys i - window < j <= i (sliding
+ * window); 0: all j <= i; negative: GPT_ERR_ARG. */
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
                   void* stream);
-/* backward: dqkv act [B*T][3*H*hd] from qkv, o, dO act [B*T][H*hd] and lse, with
- * the forward's window; D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */
+/* backward: dqkv act [B*T][(H + 2*Hkv)*hd] from qkv, o, dO act [B*T][H*hd] and lse,
+ * with the forward's Hkv and window (dK and dV of a shared head sum over its query
+ * heads); D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */
 int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D,
-                  void* dqkv, int B, int T, int H, int hd, int window, void* stream);
+                  void* dqkv, int B, int T, int H, int Hkv, int hd, int window, void* stream);
 
 /* y act = x / sqrt(mean(x^2) + eps) per row of x fp32 [N][d]; rstd fp32 [N] */
 int gptk_rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int N, int d, float eps, void* stream);
@@ -237,14 +245,15 @@ int gptk_rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int N, int
 int gptk_rmsnorm_bwd(int dtype, const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
                      void* dx_act, int N, int d, void* stream);
 
-/* in place on the q and k parts of qkv act [B*T][3*H*hd]: rotate half-split pairs
- * by t*base^(-2i/hd) then RMS-normalise each head vector; rstd_q, rstd_k fp32
- * [B*T][H].  cs is fp32 scratch of T*hd floats (the rotation table). */
-int gptk_rope_qknorm_fwd(int dtype, void* qkv, float* cs, float* rstd_q, float* rstd_k, int B, int T, int H, int hd,
-                         float base, float eps, void* stream);
+/* in place on the H query and Hkv key head vectors of qkv act [B*T][(H + 2*Hkv)*hd]
+ * (layout as for gptk_attn_fwd): rotate half-split pairs by t*base^(-2i/hd) then
+ * RMS-normalise each head vector; rstd_q fp32 [B*T][H], rstd_k fp32 [B*T][Hkv].  cs
+ * is fp32 scratch of T*hd floats (the rotation table). */
+int gptk_rope_qknorm_fwd(int dtype, void* qkv, float* cs, float* rstd_q, float* rstd_k, int B, int T, int H, int Hkv,
+                         int hd, float base, float eps, void* stream);
 /* in place on the q and k parts of dqkv: gradient through the norm and rotation */
 int gptk_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, float* cs, const float* rstd_q,
-                         const float* rstd_k, int B, int T, int H, int hd, float base, void* stream);
+                         const float* rstd_k, int B, int T, int H, int Hkv, int hd, float base, void* stream);
 
 /* fused softmax cross-entropy over logits fp32 [N][V]: row_loss fp32 [N],
  * dlogits act [N][V] = (softmax - onehot(target)) * inv_n, argmax int32 [N]

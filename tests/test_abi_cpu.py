@@ -60,10 +60,11 @@ def test_param_counts_match_survey_shapes():
 def test_default_ns_table(lib):
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "ns_printed_coeffs.json")))
     c = binding.GptCfg()
+    c.attn_window, c.n_kv_head = 7, 3  # overwritten with the defaults
     lib.gpt_cfg_from_depth(24, ctypes.byref(c))
     tab = c.coeffs()
     assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 4 and c.fp8_gemms == 7
-    assert c.attn_window == 0
+    assert c.attn_window == 0 and c.n_kv_head == 0
     assert ctypes.sizeof(binding.GptCfg) == 144
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
     derived, _ = polar_express.coefficients()
@@ -75,7 +76,8 @@ def test_validation_errors(lib):
     assert lib.gpt_cfg_validate(ctypes.byref(base)) == 0
     for field, val, code in [("head_dim", 48, 6), ("n_head", 5, 2), ("d_model", 2056, 2), ("precision", 7, 6),
                              ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2), ("fp8_gemms", 8, 1),
-                             ("attn_window", -1, 1)]:
+                             ("attn_window", -1, 1), ("n_kv_head", 2, 2), ("n_kv_head", 4, 2),
+                             ("n_kv_head", -1, 2)]:
         c = binding.make_cfg(configs.get("laptop"))
         setattr(c, field, val)
         assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, field
@@ -84,9 +86,11 @@ def test_validation_errors(lib):
     assert lib.gpt_status_str(3).decode() == "token id out of range"
 
 
-def test_state_bytes_and_tensor_table(lib):
-    for name in ("tiny", "laptop", "d12", "d24"):
-        cfg = configs.get(name)
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {}), ("d12", {}), ("d24", {}),
+                                       ("tiny", {"n_kv_head": 2}), ("laptop", {"n_kv_head": 1}),
+                                       ("d24", {"n_kv_head": 4})])
+def test_state_bytes_and_tensor_table(lib, name, over):
+    for cfg in [configs.get(name, **over)]:
         c = binding.make_cfg(cfg)
         nb = lib.gpt_state_bytes(ctypes.byref(c))
         n = configs.n_params(cfg)
@@ -94,6 +98,7 @@ def test_state_bytes_and_tensor_table(lib):
         assert nb < 288 * 2 ** 30                # fits one MI355X
         assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"]
         shapes = inputs.tensor_shapes(cfg)
+        assert n == sum(r * k for _, (r, k) in shapes)
         for i, (nm, shp) in enumerate(shapes):
             r, k = ctypes.c_int32(), ctypes.c_int32()
             assert lib.gpt_tensor_shape(ctypes.byref(c), i, ctypes.byref(r), ctypes.byref(k)) == 0

@@ -172,47 +172,58 @@ def test_gemm_full_size_sampled():
 # ----------------------------------------------------------------------------- attention
 
 
-def _qkv(Bn, T, H, hd, seed, dtype):
+def _qkv(Bn, T, H, hd, seed, dtype, Hkv=None):
+    """Fused qkv rows [q: H heads | k: Hkv heads | v: Hkv heads] and the fp64 q, k, v."""
+    Hkv = H if Hkv is None else Hkv
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((Bn, T, H, hd))
-    k = rng.standard_normal((Bn, T, H, hd))
-    v = rng.standard_normal((Bn, T, H, hd))
+    k = rng.standard_normal((Bn, T, Hkv, hd))
+    v = rng.standard_normal((Bn, T, Hkv, hd))
     q, _ = O.rms_norm(q, 1e-6)          # unit-RMS heads, as after QK-norm
     k, _ = O.rms_norm(k, 1e-6)
     qkv = np.concatenate([q.reshape(Bn, T, -1), k.reshape(Bn, T, -1), v.reshape(Bn, T, -1)], -1)
     qkv = _round(qkv, dtype)
-    d = H * hd
+    d, dkv = H * hd, Hkv * hd
     q = qkv[..., :d].reshape(Bn, T, H, hd).astype(np.float64)
-    k = qkv[..., d:2 * d].reshape(Bn, T, H, hd).astype(np.float64)
-    v = qkv[..., 2 * d:].reshape(Bn, T, H, hd).astype(np.float64)
+    k = qkv[..., d:d + dkv].reshape(Bn, T, Hkv, hd).astype(np.float64)
+    v = qkv[..., d + dkv:].reshape(Bn, T, Hkv, hd).astype(np.float64)
     return qkv, q, k, v
 
 
-# (dtype, B, T, H, hd, window): window > 0 is sliding-window attention (query i sees
-# keys i - window < j <= i): one key, windows at and across a 64-key tile edge, and
-# windows spanning several 128-query blocks
+# (dtype, B, T, H, hd, window[, Hkv]): window > 0 is sliding-window attention (query i
+# sees keys i - window < j <= i): one key, windows at and across a 64-key tile edge, and
+# windows spanning several 128-query blocks.  Hkv < H is grouped-query attention (H / Hkv
+# query heads per key/value head): groups of 2, 4 and 6 (one key/value head), sequence-
+# head counts that do and do not fill the XCD-aware block order (multiples of 8 G).
 ATTN_CASES = [("bf16", 2, 300, 3, 128, 0), ("bf16", 1, 256, 2, 64, 0), ("bf16", 2, 130, 2, 32, 0),
               ("bf16", 1, 1, 1, 128, 0), ("fp32", 2, 128, 4, 32, 0), ("fp32", 1, 77, 2, 64, 0),
               ("bf16", 2, 300, 3, 128, 1), ("bf16", 2, 300, 3, 128, 100), ("bf16", 1, 256, 2, 64, 64),
               ("bf16", 1, 256, 2, 64, 65), ("bf16", 2, 130, 2, 32, 37), ("bf16", 1, 700, 2, 128, 200),
-              ("bf16", 1, 1024, 1, 128, 129), ("fp32", 2, 128, 4, 32, 17), ("fp32", 1, 77, 2, 64, 5)]
+              ("bf16", 1, 1024, 1, 128, 129), ("fp32", 2, 128, 4, 32, 17), ("fp32", 1, 77, 2, 64, 5),
+              ("bf16", 2, 300, 4, 128, 0, 2), ("bf16", 2, 256, 8, 64, 0, 2), ("bf16", 1, 300, 6, 128, 100, 1),
+              ("bf16", 4, 130, 4, 32, 0, 1), ("bf16", 2, 512, 16, 64, 0, 4), ("bf16", 1, 1, 4, 128, 0, 2),
+              ("fp32", 2, 128, 4, 32, 0, 2), ("fp32", 1, 77, 4, 64, 9, 1)]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES)
 def test_attention_fwd_bwd(case):
-    dtype, Bn, T, H, hd, win = case
+    dtype, Bn, T, H, hd, win = case[:6]
+    Hkv = case[6] if len(case) > 6 else H
+    G = H // Hkv
     say("attention", case)
-    qkv, q, k, v = _qkv(Bn, T, H, hd, 11, dtype)
-    o_ref, P = O.causal_attention(q, k, v, window=win)
+    qkv, q, k, v = _qkv(Bn, T, H, hd, 11, dtype, Hkv)
+    # query head h reads key/value head h // G
+    kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    o_ref, P = O.causal_attention(q, kr, vr, window=win)
     # lse from the oracle's probabilities: the diagonal key is always visible, and
     # P_ii = exp(S_ii - lse_i)
-    S_ii = np.einsum("bihd,bihd->bhi", q, k) / np.sqrt(hd)
+    S_ii = np.einsum("bihd,bihd->bhi", q, kr) / np.sqrt(hd)
     lse_ref = S_ii - np.log(np.diagonal(P, axis1=2, axis2=3))   # [B,H,T]
-    d = H * hd
+    d, dkv = H * hd, Hkv * hd
     dq = to_dev(qkv, dtype)
     o = torch.zeros(Bn * T, d, device="cuda", dtype=dq.dtype)
     lse = torch.zeros(Bn * H * T, device="cuda")
-    B.attn_fwd(DT[dtype], dq, o, lse, Bn, T, H, hd, win)
+    B.attn_fwd(DT[dtype], dq, o, lse, Bn, T, H, hd, win, n_kv=Hkv)
     torch.cuda.synchronize()
     o_got = from_dev(o).reshape(Bn, T, H, hd)
     tol = 1e-2 if dtype == "bf16" else 1e-5
@@ -222,19 +233,33 @@ def test_attention_fwd_bwd(case):
     rng = np.random.default_rng(12)
     dO = _round(rng.standard_normal((Bn, T, H, hd)), dtype)
     o_in = o_got
-    dq_ref, dk_ref, dv_ref = O.causal_attention_bwd(dO.astype(np.float64), q, k, v, o_in, window=win)
+    dq_ref, dk_ref, dv_ref = O.causal_attention_bwd(dO.astype(np.float64), q, kr, vr, o_in, window=win)
+    # a shared key/value head's gradient sums over its G query heads
+    dk_ref = dk_ref.reshape(Bn, T, Hkv, G, hd).sum(axis=3)
+    dv_ref = dv_ref.reshape(Bn, T, Hkv, G, hd).sum(axis=3)
     ddo = to_dev(dO.reshape(Bn * T, d), dtype)
     D = torch.zeros(Bn * H * T, device="cuda")
-    dqkv = torch.full((Bn * T, 3 * d), float("nan"), device="cuda", dtype=dq.dtype)
-    B.attn_bwd(DT[dtype], dq, o, ddo, lse, D, dqkv, Bn, T, H, hd, win)
+    dqkv = torch.full((Bn * T, d + 2 * dkv), float("nan"), device="cuda", dtype=dq.dtype)
+    B.attn_bwd(DT[dtype], dq, o, ddo, lse, D, dqkv, Bn, T, H, hd, win, n_kv=Hkv)
     torch.cuda.synchronize()
-    g = from_dev(dqkv).reshape(Bn, T, 3, H, hd)
+    g = from_dev(dqkv).reshape(Bn, T, d + 2 * dkv)
+    got = (g[..., :d].reshape(Bn, T, H, hd), g[..., d:d + dkv].reshape(Bn, T, Hkv, hd),
+           g[..., d + dkv:].reshape(Bn, T, Hkv, hd))
     gtol = 2e-2 if dtype == "bf16" else 1e-4
     # relative to the largest of the three references: at T = 1 dq and dk are exactly 0
     scale = max(np.linalg.norm(r) for r in (dq_ref, dk_ref, dv_ref))
     for i, ref in enumerate((dq_ref, dk_ref, dv_ref)):
-        e = np.linalg.norm(g[:, :, i] - ref) / max(np.linalg.norm(ref), 1e-3 * scale)
+        e = np.linalg.norm(got[i] - ref) / max(np.linalg.norm(ref), 1e-3 * scale)
         assert e < gtol, (i, e)
+
+
+def test_attention_rejects_bad_kv_heads():
+    t = torch.zeros(16, device="cuda")
+    for H, Hkv in [(4, 3), (4, 0), (4, 8), (3, -1)]:
+        with pytest.raises(B.GptError, match="argument"):
+            B.attn_fwd(B.GPT_BF16, t, t, t, 1, 1, H, 128, 0, n_kv=Hkv)
+        with pytest.raises(B.GptError, match="argument"):
+            B.rope_qknorm_fwd(B.GPT_BF16, t, t, t, t, 1, 1, H, 128, 10000.0, 1e-6, n_kv=Hkv)
 
 
 def test_attention_full_size_sampled_heads():
@@ -282,43 +307,50 @@ def test_rmsnorm_fwd_bwd(dtype, N, d):
     assert rel_l2(from_dev(dxa), dx_ref) < (4e-3 if dtype == "bf16" else 1e-5)
 
 
-@pytest.mark.parametrize("dtype,Bn,T,H,hd", [("bf16", 2, 100, 3, 128), ("bf16", 1, 64, 2, 64),
-                                             ("fp32", 2, 40, 4, 32), ("bf16", 1, 2048, 1, 128),
-                                             ("bf16", 3, 37, 5, 32), ("bf16", 1, 33, 7, 64)])
-def test_rope_qknorm_fwd_bwd(dtype, Bn, T, H, hd):
-    rng = np.random.default_rng(T)
-    d = H * hd
-    qkv = _round(rng.standard_normal((Bn, T, 3 * d)) * 0.7, dtype)
-    dqkv = _round(rng.standard_normal((Bn, T, 3 * d)), dtype)
+@pytest.mark.parametrize("dtype,Bn,T,H,hd,Hkv", [("bf16", 2, 100, 3, 128, 3), ("bf16", 1, 64, 2, 64, 2),
+                                                 ("fp32", 2, 40, 4, 32, 4), ("bf16", 1, 2048, 1, 128, 1),
+                                                 ("bf16", 3, 37, 5, 32, 5), ("bf16", 1, 33, 7, 64, 7),
+                                                 ("bf16", 2, 100, 6, 128, 2), ("bf16", 3, 37, 4, 32, 1),
+                                                 ("bf16", 1, 33, 4, 64, 2), ("fp32", 2, 40, 4, 32, 1),
+                                                 ("fp32", 1, 19, 6, 64, 3)])
+def test_rope_qknorm_fwd_bwd(dtype, Bn, T, H, hd, Hkv):
+    """Rows [q: H heads | k: Hkv heads | v: Hkv heads]; q and k are rotated and
+    normalised head by head, v is left as it is."""
+    rng = np.random.default_rng(T + Hkv)
+    d, dkv = H * hd, Hkv * hd
+    W = d + 2 * dkv
+    qkv = _round(rng.standard_normal((Bn, T, W)) * 0.7, dtype)
+    dqkv = _round(rng.standard_normal((Bn, T, W)), dtype)
     ang = O.rope_angles(T, hd, 10000.0)
     x = qkv.astype(np.float64)
-    outs, grads = [], []
-    for i in range(2):  # q, k
-        part = x[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd)
-        y, r = O.rms_norm(O.rope(part, ang), 1e-6)
+    spans = [(0, d, H), (d, d + dkv, Hkv)]  # q, k
+    outs = []
+    for a, b, nh in spans:
+        y, r = O.rms_norm(O.rope(x[..., a:b].reshape(Bn, T, nh, hd), ang), 1e-6)
         outs.append((y, r))
-    tq = to_dev(qkv.reshape(Bn * T, 3 * d), dtype)
+    tq = to_dev(qkv.reshape(Bn * T, W), dtype)
     cs = torch.empty(T * hd, device="cuda")
     rq = torch.empty(Bn * T * H, device="cuda")
-    rk = torch.empty(Bn * T * H, device="cuda")
-    B.rope_qknorm_fwd(DT[dtype], tq, cs, rq, rk, Bn, T, H, hd, 10000.0, 1e-6)
+    rk = torch.empty(Bn * T * Hkv, device="cuda")
+    B.rope_qknorm_fwd(DT[dtype], tq, cs, rq, rk, Bn, T, H, hd, 10000.0, 1e-6, n_kv=Hkv)
     torch.cuda.synchronize()
-    got = from_dev(tq).reshape(Bn, T, 3 * d)
+    got = from_dev(tq).reshape(Bn, T, W)
     tol = 5e-3 if dtype == "bf16" else 2e-6
-    for i, (y, r) in enumerate(outs):
-        assert rel_l2(got[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd), y) < tol
-    np.testing.assert_array_equal(got[..., 2 * d:], qkv[..., 2 * d:].astype(np.float64))   # v untouched
-    assert np.abs(rq.cpu().numpy().reshape(Bn, T, H) - outs[0][1][..., 0]).max() / outs[0][1].max() < 1e-5
+    for (a, b, nh), (y, r) in zip(spans, outs):
+        assert rel_l2(got[..., a:b].reshape(Bn, T, nh, hd), y) < tol
+    np.testing.assert_array_equal(got[..., d + dkv:], qkv[..., d + dkv:].astype(np.float64))   # v untouched
+    for rt, (y, r), nh in ((rq, outs[0], H), (rk, outs[1], Hkv)):
+        assert np.abs(rt.cpu().numpy().reshape(Bn, T, nh) - r[..., 0]).max() / r.max() < 1e-5
     # backward uses the kernel's normalised q, k as y (what the step saves)
-    ddq = to_dev(dqkv.reshape(Bn * T, 3 * d), dtype)
-    B.rope_qknorm_bwd(DT[dtype], ddq, tq, cs, rq, rk, Bn, T, H, hd, 10000.0)
+    ddq = to_dev(dqkv.reshape(Bn * T, W), dtype)
+    B.rope_qknorm_bwd(DT[dtype], ddq, tq, cs, rq, rk, Bn, T, H, hd, 10000.0, n_kv=Hkv)
     torch.cuda.synchronize()
-    gg = from_dev(ddq).reshape(Bn, T, 3 * d)
-    for i, (y, r) in enumerate(outs):
-        dy = dqkv[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd).astype(np.float64)
+    gg = from_dev(ddq).reshape(Bn, T, W)
+    for (a, b, nh), (y, r) in zip(spans, outs):
+        dy = dqkv[..., a:b].reshape(Bn, T, nh, hd).astype(np.float64)
         ref = O.rope(O.rms_norm_bwd(dy, y, r), ang, inverse=True)
-        assert rel_l2(gg[..., i * d:(i + 1) * d].reshape(Bn, T, H, hd), ref) < (1e-2 if dtype == "bf16" else 1e-5)
-    np.testing.assert_array_equal(gg[..., 2 * d:], dqkv[..., 2 * d:].astype(np.float64))
+        assert rel_l2(gg[..., a:b].reshape(Bn, T, nh, hd), ref) < (1e-2 if dtype == "bf16" else 1e-5)
+    np.testing.assert_array_equal(gg[..., d + dkv:], dqkv[..., d + dkv:].astype(np.float64))
 
 
 # ----------------------------------------------------------------------------- cross-entropy

@@ -52,10 +52,14 @@ def _dev(a):
 # fp8_gemms selects the e4m3 GEMMs: 1 forward, 2 weight gradient, 4 input gradient.
 # With the forward and weight gradient both in e4m3 (the default 7), the weight
 # gradient reuses the forward's codes of its input; with 6 it quantises them itself.
+# n_kv_head < n_head: grouped-query attention (Wk, Wv of n_kv_head * head_dim rows).
 STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8", {"precision": "fp8"}),
               ("laptop_fp8_bwd", {"precision": "fp8", "fp8_gemms": 6}),
               ("laptop_fp8_fwd", {"precision": "fp8", "fp8_gemms": 1}),
               ("laptop_window", {"attn_window": 100}),
+              ("tiny_gqa", {"n_kv_head": 2}), ("laptop_mqa", {"n_kv_head": 1}),
+              ("laptop_mqa_fp8", {"precision": "fp8", "n_kv_head": 1}),
+              ("d12_gqa", {"batch": 1, "n_kv_head": 2}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
