@@ -86,6 +86,10 @@ def main() -> int:
                          "pages print none; the values do not change the cost)")
     ap.add_argument("--fp8", action="store_true",
                     help="e4m3 operands on every Linear GEMM (the configs' fp8 recipe); default bf16")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="sliding-window attention: query i sees keys i-W < j <= i (0: full causal)")
+    ap.add_argument("--kv-heads", type=int, default=0, metavar="H",
+                    help="grouped-query attention with H key/value heads (0: one per query head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant", default=None,
                     help="kernel timed for the roofline (default: the NT GEMM of the step's precision)")
@@ -112,7 +116,7 @@ def main() -> int:
 
     from gpt_pretraining_step_train_amd import binding, configs, inputs
 
-    cfg = configs.get(args.config)
+    cfg = configs.get(args.config, attn_window=args.window, n_kv_head=args.kv_heads)
     if args.dominant is None:
         args.dominant = "gemm_fp8_dma_kernel<256,256,NT>" if args.fp8 else "gemm_bf16_dma_kernel<256,256,NT>"
     cfg["precision"] = "fp8" if args.fp8 else "bf16"
@@ -167,7 +171,7 @@ def main() -> int:
     achieved = k_flops / (k_ms / 1e3) if k_ms > 0 else None
     from gpt_pretraining_step_train_amd import profiling
     rec = None
-    if args.dominant in TRAFFIC and args.config == "d24":
+    if args.dominant in TRAFFIC and args.config == "d24" and not args.kv_heads:  # same GEMM launches
         rec = profiling.read_traffic(os.path.join(ROOT, "profiles", TRAFFIC[args.dominant]))
     peak = PEAK_FP8 if "fp8" in args.dominant else PEAK_BF16  # a contraction takes its own dtype's peak
     roof = {
@@ -187,8 +191,12 @@ def main() -> int:
         "config": {"workload": f"{args.config} GPT training step{' (fp8 linears)' if args.fp8 else ''}: "
                                + (f"{K} accumulated fwd+bwd micro-batches of B={B} x T={T}, then Muon(5 NS)"
                                 f"{'+AdamW(E,U)' if args.adamw else ''}" if K > 1 else
-                                f"fwd+bwd+Muon(5 NS){'+AdamW(E,U)' if args.adamw else ''} on B={B} x T={T}"),
+                                f"fwd+bwd+Muon(5 NS){'+AdamW(E,U)' if args.adamw else ''} on B={B} x T={T}")
+                               + (f", sliding-window attention W={args.window}" if args.window else "")
+                               + (f", grouped-query attention with {args.kv_heads} key/value heads"
+                                  if args.kv_heads else ""),
                    "depth": cfg["depth"], "d_model": cfg["d_model"], "n_head": cfg["n_head"],
+                   "n_kv_head": configs.kv_heads(cfg), "attn_window": args.window,
                    "vocab": V, "global_batch": B * K, "micro_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu, "mfu_at_fp8_peak_for_linears": mfu_fp8, "flops_per_step": fl["total"], "wall_s": wall,
         "loss_first_last": [losses[0], losses[-1]],

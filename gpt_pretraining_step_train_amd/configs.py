@@ -53,7 +53,9 @@ def step_flops(cfg: dict) -> dict:
 
     fwd+bwd = 6 N (12 L d^2 + d V) when F = 4d (generally 6 N (4 L d^2 + 2 L d F + d V);
     with grouped-query attention Wk, Wv are dkv x d, dkv = n_kv_head * head_dim), plus
-    causal attention 6 L d N (T+1) (fwd 2 d T (T+1) per sequence and layer, bwd 2x).
+    causal attention 12 L B d S, S = the (query, key) pairs of one sequence: T (T+1) / 2
+    for full causal attention (fwd 4 d S per sequence and layer, bwd 2x); a sliding
+    window W < T leaves W (W+1) / 2 + (T - W) W of them.
     Muon = ns_steps * sum over block matrices of (4 s^2 l + 2 s^3), s = min dim, l = max dim.
     """
     d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
@@ -62,7 +64,9 @@ def step_flops(cfg: dict) -> dict:
     N = B * T
     linear = 6 * N * (2 * L * d * d + 2 * L * dkv * d + 2 * L * d * F)
     head = 6 * N * d * V
-    attn = 6 * L * d * N * (T + 1)
+    W = cfg.get("attn_window", 0)
+    pairs = T * (T + 1) // 2 if not W or W >= T else W * (W + 1) // 2 + (T - W) * W
+    attn = 12 * L * B * d * pairs
     k = cfg.get("ns_steps", 5)
     mats = [(d, d), (dkv, d), (dkv, d), (d, d), (F, d), (d, F)]
     muon = 0

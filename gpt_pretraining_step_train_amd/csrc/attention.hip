@@ -564,20 +564,27 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   // query tiles from the block's first key to the last query that sees its last key
   const int nqt = min((T + BQT - 1) / BQT, (kb * BKEY + BKEY - 1 + Wn - 1) / BQT + 1);
   const int qt0 = (kb * BKEY) / BQT;
-  // steps: (query head hk G + s / nq, query tile qt0 + s % nq) for s < G nq
-  const int nq = nqt - qt0, nsteps = G * nq;
+  // G (nqt - qt0) steps: the query tiles qt0 .. nqt-1 of query head hk G, then of the
+  // next query head of the group, ...
+  const int nsteps = G * (nqt - qt0);
   // 64-row Q and dO tiles and their lse / D values, prefetched one step ahead
   PairStager<HD, 512> stg;
   stg.init(ld, ldo, tid);
   float pl = 0.f, pd = 0.f;
-  auto load = [&](int sp) {
-    const int qh = hk * G + sp / nq, q0 = (qt0 + sp % nq) * BQT;
-    stg.load(rows_rsrc(Qb + qh * HD, ld, q0, T, HD), rows_rsrc(Gb + qh * HD, ldo, q0, T, HD), tid);
+  int ld_h = hk * G, ld_t = qt0;  // (query head, query tile) of the step the next load fetches
+  int cur_t = qt0;                // query tile of the step being computed
+  auto load = [&]() {
+    const int q0 = ld_t * BQT;
+    stg.load(rows_rsrc(Qb + ld_h * HD, ld, q0, T, HD), rows_rsrc(Gb + ld_h * HD, ldo, q0, T, HD), tid);
     if (tid < BQT) {
       const int q = q0 + tid;
-      const long r = lrow + (long)qh * T + q;
+      const long r = lrow + (long)ld_h * T + q;
       pl = q < T ? lse[r] * LOG2E : 0.f;
       pd = q < T ? Dv[r] : 0.f;
+    }
+    if (++ld_t == nqt) {
+      ld_t = qt0;
+      ++ld_h;
     }
   };
   auto store = [&](int buf) {
@@ -588,7 +595,7 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     }
   };
   if (nsteps > 0) {
-    load(0);
+    load();
     store(0);
   }
   __syncthreads();
@@ -598,8 +605,8 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   // after a barrier: dV += P^T dO, and dK += dS^T Q with dS = P (dP - D).
   auto body = [&](auto cur_c, int sp) {
     constexpr int cur = decltype(cur_c)::value;
-    const int qb0 = (qt0 + sp % nq) * BQT;
-    if (sp + 1 < nsteps) load(sp + 1);
+    const int qb0 = cur_t * BQT;
+    if (sp + 1 < nsteps) load();
     // the same for both roles: the tile holds a query that sees one of the wave's keys
     const bool live = qb0 + BQT - 1 >= key0 && qb0 <= key0 + 31 + Wn - 1 && key0 < T;
     f32x16_t pd[2];  // P (dV waves) or dP (dK waves) of each 32-query half
@@ -664,6 +671,7 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     }
     if (sp + 1 < nsteps) store(cur ^ 1);
     __syncthreads();
+    cur_t = cur_t + 1 == nqt ? qt0 : cur_t + 1;
   };
   for (int sp = 0; sp < nsteps; sp += 2) {
     body(std::integral_constant<int, 0>{}, sp);

@@ -120,3 +120,12 @@ def test_configs_flops_formula():
     f = configs.step_flops(configs.get("d24"))
     assert abs(f["total"] - 1.844e14) / 1.844e14 < 3e-3
     assert abs(f["muon"] - 300 * 24 * 1536 ** 3) < 1
+    # attention: 12 L B d flops per visible (query, key) pair, counted by brute force
+    for W in (1, 7, 100, 2047, 2048, 5000):
+        c = configs.get("d24", attn_window=W)
+        pairs = sum(min(i + 1, W) for i in range(c["seq_len"]))
+        assert configs.step_flops(c)["attn"] == 12 * 24 * 16 * 1536 * pairs
+    assert configs.step_flops(configs.get("d24", attn_window=2048))["attn"] == f["attn"]
+    # grouped-query attention shrinks Wk, Wv (and their Newton-Schulz), not attention
+    g = configs.step_flops(configs.get("d24", n_kv_head=4))
+    assert g["attn"] == f["attn"] and g["linear"] < f["linear"] and g["muon"] < f["muon"]
