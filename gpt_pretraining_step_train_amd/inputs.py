@@ -13,8 +13,12 @@ token ids and initial weights.  Both sides receive the same arrays.
   projections (attention W_o and MLP W_2) scaled by 1/sqrt(2*depth).
 
 Tensor table order (the C ABI's tensor ids): 0 = E [V,d]; for layer l the
-ids 1+6l .. 1+6l+5 are Wq [d,d], Wk [d,d], Wv [d,d], Wo [d,d], W1 [F,d],
-W2 [d,F]; the last id 1+6L is the LM head U [V,d].
+ids 1+6l .. 1+6l+5 are Wq [d,d], Wk [dkv,d], Wv [dkv,d], Wo [d,d], W1 [F,d],
+W2 [d,F]; id 1+6L is the LM head U [V,d].  When the cfg switches on any of the
+extras, id 2+6L is S [1, 2L+26]: L per-layer residual scales, L per-layer x0
+scales, the smear scale, the backout scale and the 24 smear-gate weights.  S
+starts as the identity (residual scales 1, everything else 0), where the
+extras leave the model unchanged.
 """
 from __future__ import annotations
 
@@ -29,6 +33,8 @@ def tensor_shapes(cfg: dict) -> list[tuple[str, tuple[int, int]]]:
         out += [(f"l{l}.Wq", (d, d)), (f"l{l}.Wk", (dkv, d)), (f"l{l}.Wv", (dkv, d)),
                 (f"l{l}.Wo", (d, d)), (f"l{l}.W1", (F, d)), (f"l{l}.W2", (d, F))]
     out.append(("U", (V, d)))
+    if cfg.get("extras"):
+        out.append(("S", (1, 2 * L + 26)))
     return out
 
 
@@ -39,6 +45,11 @@ def init_weights(cfg: dict, seed: int = 0) -> list[np.ndarray]:
     out_scale = 1.0 / np.sqrt(2.0 * cfg["depth"])
     ws = []
     for name, shape in tensor_shapes(cfg):
+        if name == "S":
+            w = np.zeros(shape, dtype=np.float32)
+            w[0, :cfg["depth"]] = 1.0
+            ws.append(w)
+            continue
         s = std * (out_scale if name.endswith(".Wo") or name.endswith(".W2") else 1.0)
         w = rng.standard_normal(shape, dtype=np.float32)
         w *= np.float32(s)

@@ -40,6 +40,22 @@ so they share one weight scale and one gradient scale.  The e4m3 code of each
 element is a rounding decision; it is taken on the operand as stored (weights
 fp32, activations and output gradients bf16, the scale and the scaled value in
 fp32), so that both implementations decide it from the same number.
+
+Extras (cfg "extras", a bitmask; the efficiency tricks printed under "Verimlilik
+Puf Noktalari" in "1. GPT Modeli" of the Turkish page and its Arabic
+translation).  Their parameters form one more tensor S at the end of the table
+(the page's optimizer table puts scalar parameters with AdamW), laid out as in
+``extras_layout``:
+
+* 1, per-layer residual scaling: layer i's input is lr[i] x + l0[i] x0, where
+  x is the residual stream reaching the layer and x0 the stream entering the
+  first layer (after the embedding and the smear).
+* 2, smear: after the embedding lookup, x[t] += ls sigmoid(ws . x[t, :24]) x[t-1]
+  within each sequence (nothing is added at t = 0): the gate reads the first 24
+  channels of the current position, the added term is the previous position's
+  embedding before smearing.
+* 4, backout: the final norm reads x_L - lb x_mid, x_mid the residual stream
+  entering layer L // 2 (before that layer's residual scaling).
 """
 from __future__ import annotations
 
@@ -51,14 +67,31 @@ from oracle.e4m3 import quantise
 # configuration / parameter table
 
 
+EXTRA_RESID, EXTRA_SMEAR, EXTRA_BACKOUT = 1, 2, 4
+SMEAR_CHANNELS = 24  # channels of the current position the smear gate reads
+
+
+def extras_layout(L):
+    """Index of each extra parameter inside S (a flat vector of 2L + 2 + 24 values)."""
+    return dict(lr=np.arange(0, L), l0=np.arange(L, 2 * L), ls=2 * L, lb=2 * L + 1,
+                ws=np.arange(2 * L + 2, 2 * L + 2 + SMEAR_CHANNELS), size=2 * L + 2 + SMEAR_CHANNELS)
+
+
 def unpack(params, cfg):
-    """Split the flat tensor table [E, (Wq,Wk,Wv,Wo,W1,W2)*L, U] into parts."""
+    """Split the flat tensor table [E, (Wq,Wk,Wv,Wo,W1,W2)*L, U(, S)] into parts;
+    S (flattened) is None when no extra is switched on."""
     L = cfg["depth"]
-    assert len(params) == 2 + 6 * L
+    has_s = bool(cfg.get("extras", 0))
+    assert len(params) == 2 + 6 * L + has_s
     E = params[0]
     layers = [tuple(params[1 + 6 * l: 7 + 6 * l]) for l in range(L)]
     U = params[1 + 6 * L]
-    return E, layers, U
+    S = np.asarray(params[2 + 6 * L], dtype=np.float64).reshape(-1) if has_s else None
+    return E, layers, U, S
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
 
 
 # ---------------------------------------------------------------------------
@@ -174,17 +207,33 @@ def forward(params, tokens, cfg, keep=True):
     """Forward pass.  Returns (logits [B,T,V], cache for backward)."""
     p = [np.asarray(w, dtype=np.float64) for w in params]
     qf, qfw = _fp8_quantisers(cfg)[0]
-    E, layers, U = unpack(p, cfg)
+    E, layers, U, S = unpack(p, cfg)
     eps = cfg.get("norm_eps", 1e-6)
     H, hd = cfg["n_head"], cfg["head_dim"]
     Hkv = int(cfg.get("n_kv_head") or H)
     B, T = tokens.shape
     d, dkv = cfg["d_model"], Hkv * hd
     ang = rope_angles(T, hd, cfg.get("rope_base", 10000.0))
+    ex = cfg.get("extras", 0)
+    X = extras_layout(len(layers))
+    Lb = len(layers) // 2                                 # backout: stream entering this layer
 
     h = E[tokens]                                         # [B,T,d]
     cache = {"tokens": tokens, "ang": ang, "layers": [], "p": p}
-    for (Wq, Wk, Wv, Wo, W1, W2) in layers:
+    if ex & EXTRA_SMEAR:
+        prev = np.zeros_like(h)
+        prev[:, 1:] = h[:, :-1]                           # previous position, same sequence
+        zs = h[..., :SMEAR_CHANNELS] @ S[X["ws"]]         # [B,T]
+        cache.update(emb=h, prev=prev, zs=zs)
+        h = h + (S[X["ls"]] * sigmoid(zs))[..., None] * prev
+    x0 = h
+    cache["x0"] = x0
+    for li, (Wq, Wk, Wv, Wo, W1, W2) in enumerate(layers):
+        if ex & EXTRA_BACKOUT and li == Lb:
+            cache["x_mid"] = h
+        x_in = h
+        if ex & EXTRA_RESID:
+            h = S[X["lr"][li]] * h + S[X["l0"][li]] * x0
         a, ra = rms_norm(h, eps)
         qkv = qf(a) @ qfw(np.concatenate([Wq, Wk, Wv])).T
         q = qkv[..., :d].reshape(B, T, H, hd)
@@ -202,9 +251,11 @@ def forward(params, tokens, cfg, keep=True):
         g = np.maximum(u, 0.0) ** 2
         h2 = h1 + qf(g) @ qfw(W2).T
         if keep:
-            cache["layers"].append(dict(h=h, a=a, ra=ra, qn=qn, rq=rq, kn=kn, rk=rk,
+            cache["layers"].append(dict(h=h, x_in=x_in, a=a, ra=ra, qn=qn, rq=rq, kn=kn, rk=rk,
                                         v=v, o=o, h1=h1, m=m, rm=rm, u=u, g=g))
         h = h2
+    if ex & EXTRA_BACKOUT:
+        h = h - S[X["lb"]] * cache["x_mid"]
     r, rf = rms_norm(h, eps)
     z = qf(r) @ qfw(U).T
     cache.update(hL=h, r=r, rf=rf)
@@ -231,7 +282,11 @@ def cross_entropy_grad(z, targets):
 def backward(z, targets, cache, cfg):
     """Exact gradient of the mean cross-entropy w.r.t. every tensor of the table."""
     p = cache["p"]
-    E, layers, U = unpack(p, cfg)
+    E, layers, U, S = unpack(p, cfg)
+    ex = cfg.get("extras", 0)
+    X = extras_layout(len(layers))
+    Lb = len(layers) // 2
+    dS = np.zeros(X["size"]) if S is not None else None
     H, hd = cfg["n_head"], cfg["head_dim"]
     B, T, V = z.shape
     d = cfg["d_model"]
@@ -252,9 +307,14 @@ def backward(z, targets, cache, cfg):
     r = cache["r"]
     dU, dr = lin_bwd(dz, r, U)
     dh = rms_norm_bwd(dr.reshape(B, T, d), r, cache["rf"])
+    if ex & EXTRA_BACKOUT:                                # final input x_L - lb x_mid
+        d_mid = -S[X["lb"]] * dh
+        dS[X["lb"]] = -np.sum(dh * cache["x_mid"])
+    dx0 = np.zeros_like(dh)                               # through the l0 terms
 
     grads_layers = []
-    for (Wq, Wk, Wv, Wo, W1, W2), c in zip(reversed(layers), reversed(cache["layers"])):
+    for li, (Wq, Wk, Wv, Wo, W1, W2), c in zip(reversed(range(len(layers))), reversed(layers),
+                                                reversed(cache["layers"])):
         # MLP block: h2 = h1 + g W2^T, g = relu(u)^2, u = m W1^T, m = rms(h1)
         dW2, dg = lin_bwd(dh, c["g"], W2)
         du = dg.reshape(c["u"].shape) * 2.0 * np.maximum(c["u"], 0.0)
@@ -275,8 +335,26 @@ def backward(z, targets, cache, cfg):
         dWqkv, da = lin_bwd(np.concatenate([dq, dk, dv], axis=-1), c["a"], np.concatenate([Wq, Wk, Wv]))
         dWq, dWk, dWv = dWqkv[:d], dWqkv[d:d + dkv], dWqkv[d + dkv:]
         dh = dh1 + rms_norm_bwd(da.reshape(B, T, d), c["a"], c["ra"])
+        if ex & EXTRA_RESID:                              # layer input lr x_in + l0 x0
+            dS[X["lr"][li]] = np.sum(dh * c["x_in"])
+            dS[X["l0"][li]] = np.sum(dh * cache["x0"])
+            dx0 += S[X["l0"][li]] * dh
+            dh = S[X["lr"][li]] * dh
+        if ex & EXTRA_BACKOUT and li == Lb:
+            dh = dh + d_mid
         grads_layers.append((dWq, dWk, dWv, dWo, dW1, dW2))
     grads_layers.reverse()
+    dh = dh + dx0                                         # x0 is also the first layer's input
+    if ex & EXTRA_SMEAR:                                  # x = e + ls sigmoid(zs) prev(e)
+        sg = sigmoid(cache["zs"])
+        demb = dh.copy()
+        demb[:, :-1] += (S[X["ls"]] * sg)[:, 1:, None] * dh[:, 1:]
+        dgate = np.sum(dh * cache["prev"], axis=-1)       # d loss / d (ls sigmoid(zs))
+        dS[X["ls"]] = np.sum(dgate * sg)
+        dzs = dgate * S[X["ls"]] * sg * (1.0 - sg)
+        dS[X["ws"]] = np.einsum("bt,btc->c", dzs, cache["emb"][..., :SMEAR_CHANNELS])
+        demb[..., :SMEAR_CHANNELS] += dzs[..., None] * S[X["ws"]]
+        dh = demb
 
     dE = np.zeros_like(E)
     np.add.at(dE, tokens.reshape(-1), dh.reshape(N, d))
@@ -284,6 +362,8 @@ def backward(z, targets, cache, cfg):
     for gl in grads_layers:
         grads.extend(gl)
     grads.append(dU)
+    if dS is not None:
+        grads.append(dS.reshape(np.shape(p[2 + 6 * len(layers)])))
     return grads
 
 

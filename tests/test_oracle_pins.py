@@ -25,15 +25,23 @@ MICRO = dict(depth=1, d_model=16, n_head=2, head_dim=8, d_ff=64, vocab=64, seq_l
 MICRO2 = dict(MICRO, depth=2)
 MICRO_W = dict(MICRO2, attn_window=3)  # sliding window: each query sees 3 keys
 MICRO_G = dict(MICRO2, n_head=4, head_dim=4, n_kv_head=2)  # grouped-query attention, 2 heads per group
+# residual scaling + smear + backout; the smear gate reads 24 channels, so d = 32
+MICRO_X1 = dict(MICRO, d_model=32, head_dim=16, extras=7)   # one layer: backout reads x0
+MICRO_X = dict(MICRO_X1, depth=2)                           # backout reads layer 1's input
 TINY = dict(depth=2, d_model=128, n_head=4, head_dim=32, d_ff=512, vocab=4096, seq_len=128,
             batch=4, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
 
 
-def _params(cfg, seed=0, std=None):
+def _params(cfg, seed=0, std=None, random_s=True):
+    """Weights of the tensor table; the extras tensor S (when present) gets random
+    values around 0.5 instead of its identity start, so that every extra acts."""
     c = dict(cfg)
     if std is not None:
         c["init_std"] = std
-    return [w.astype(np.float64) for w in inputs.init_weights(c, seed)]
+    ws = [w.astype(np.float64) for w in inputs.init_weights(c, seed)]
+    if cfg.get("extras") and random_s:
+        ws[-1] = 0.5 + 0.3 * np.random.default_rng(seed + 1000).standard_normal(ws[-1].shape)
+    return ws
 
 
 def _tokens(cfg, seed=0, dist="uniform"):
@@ -44,7 +52,7 @@ def _tokens(cfg, seed=0, dist="uniform"):
 # P1: the whole backward against centred finite differences
 
 
-@pytest.mark.parametrize("cfg", [MICRO, MICRO2, MICRO_W, MICRO_G])
+@pytest.mark.parametrize("cfg", [MICRO, MICRO2, MICRO_W, MICRO_G, MICRO_X1, MICRO_X])
 def test_fd_gradient_every_element(cfg):
     params = _params(cfg, seed=1, std=0.5)          # large weights: non-linear regime
     tok, tgt = _tokens(cfg, seed=2)
@@ -146,8 +154,11 @@ def test_initial_loss_statistics():
 # P4: causality
 
 
-def test_causality_exact():
-    cfg = TINY
+@pytest.mark.parametrize("extras", [0, 7])
+def test_causality_exact(extras):
+    """Changing token t+1 leaves every logit up to position t unchanged (with the
+    extras: the smear mixes only the previous position into the current one)."""
+    cfg = dict(TINY, extras=extras)
     params = _params(cfg, seed=11, std=0.2)
     tok, _ = _tokens(cfg, seed=12)
     z0, _ = O.forward(params, tok, cfg, keep=False)
@@ -442,9 +453,21 @@ def _torch_loss(params, tok, tgt, cfg):
         return x * cos + torch.cat([-x2, x1], -1) * sin
 
     rms = lambda x: torch.nn.functional.rms_norm(x, (x.shape[-1],), eps=eps)
+    ex = cfg.get("extras", 0)
+    if ex:
+        E, U, S = params[0], params[-2], params[-1][0]
+        lam_r, lam_0, lam_s, lam_b, w_s = S[:L], S[L:2 * L], S[2 * L], S[2 * L + 1], S[2 * L + 2:]
     x = E[torch.from_numpy(tok).long()]
+    if ex & 2:   # previous position's embedding, zero-padded at the start of each sequence
+        shifted = torch.nn.functional.pad(x, (0, 0, 1, 0))[:, :-1]
+        x = x + lam_s * torch.sigmoid(x[..., :24] @ w_s)[..., None] * shifted
+    x0 = x
     for l in range(L):
         Wq, Wk, Wv, Wo, W1, W2 = params[1 + 6 * l: 7 + 6 * l]
+        if ex & 4 and l == L // 2:
+            x_mid = x
+        if ex & 1:
+            x = lam_r[l] * x + lam_0[l] * x0
         a = rms(x)
         q = rms(rot((a @ Wq.T).view(B, T, H, hd)))
         k = rms(rot((a @ Wk.T).view(B, T, H, hd)))
@@ -453,13 +476,16 @@ def _torch_loss(params, tok, tgt, cfg):
             q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), is_causal=True)
         x = x + o.transpose(1, 2).reshape(B, T, d) @ Wo.T
         x = x + torch.relu(rms(x) @ W1.T).square() @ W2.T
+    if ex & 4:
+        x = x - lam_b * x_mid
     z = rms(x) @ U.T
     return torch.nn.functional.cross_entropy(z.reshape(B * T, -1),
                                              torch.from_numpy(tgt).long().reshape(-1))
 
 
-def test_full_gradient_vs_torch_autograd():
-    cfg = TINY
+@pytest.mark.parametrize("extras", [0, 7])
+def test_full_gradient_vs_torch_autograd(extras):
+    cfg = dict(TINY, extras=extras)
     params = _params(cfg, seed=21, std=0.1)
     tok, tgt = _tokens(cfg, seed=22, dist="zipf")
     loss, grads, _, _ = O.loss_and_grads(params, tok, tgt, cfg)
@@ -485,6 +511,83 @@ def test_identity_blocks_reduce_to_embedding_head():
     np.testing.assert_allclose(z, r @ params[-1].T, rtol=1e-12, atol=1e-13)
     per = scipy.special.logsumexp(z, -1) - np.take_along_axis(z, tgt[..., None], -1)[..., 0]
     assert O.loss_from_logits(z, tgt)[0] == pytest.approx(per.mean(), rel=1e-14)
+
+
+# --------------------------------------------------------------------------
+# extras: residual scaling, smear, backout
+
+
+def test_extras_at_their_start_values_are_the_plain_model():
+    """S at its identity start (residual scales 1, the rest 0): loss and every
+    other gradient equal the plain model's bit for bit, whichever extras are on."""
+    base = dict(MICRO_X, extras=0)
+    pb = _params(base, seed=3, std=0.4)
+    tok, tgt = _tokens(base, seed=4)
+    lb, gb, _, _ = O.loss_and_grads(pb, tok, tgt, base)
+    for ex in (1, 2, 4, 7):
+        cfg = dict(MICRO_X, extras=ex)
+        p = _params(cfg, seed=3, std=0.4, random_s=False)
+        l, g, _, _ = O.loss_and_grads(p, tok, tgt, cfg)
+        assert l == lb
+        for x, y in zip(g[:-1], gb):
+            np.testing.assert_array_equal(x, y)
+
+
+def test_residual_scaling_can_skip_a_layer():
+    """lr = (1, 0), l0 = (0, 1): the second layer reads x0 alone and the first
+    layer's output is dropped, so the two-layer model is the one-layer plain model
+    built from the second layer's weights."""
+    cfg = dict(MICRO_X, extras=1)
+    p = _params(cfg, seed=5, std=0.4)
+    L = 2
+    S = np.zeros(2 * L + 26)
+    S[:L] = (1.0, 0.0)
+    S[L:2 * L] = (0.0, 1.0)
+    p[-1] = S[None, :]
+    one = dict(MICRO_X, depth=1, extras=0)
+    p1 = [p[0]] + p[7:13] + [p[13]]
+    tok, tgt = _tokens(cfg, seed=6)
+    z, _ = O.forward(p, tok, cfg)
+    z1, _ = O.forward(p1, tok, one)
+    np.testing.assert_allclose(z, z1, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_backout_subtracts_the_middle_stream(depth):
+    """lb = 1: the final norm reads x_L - x_mid, x_mid the stream entering layer
+    L // 2, both taken from the plain model's own forward."""
+    base = dict(MICRO_X, depth=depth, extras=0)
+    cfg = dict(base, extras=4)
+    p = _params(cfg, seed=7, std=0.4, random_s=False)
+    p[-1][0, 2 * depth + 1] = 1.0                     # backout scale
+    tok, tgt = _tokens(cfg, seed=8)
+    z, _ = O.forward(p, tok, cfg)
+    _, cache = O.forward(p[:-1], tok, base)
+    mid = cache["layers"][depth // 2]["h"]
+    x = cache["hL"] - mid
+    r = x / np.sqrt(np.mean(x * x, -1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(z, r @ p[-2].T, rtol=1e-12, atol=1e-14)
+
+
+def test_smear_with_a_constant_gate_is_a_bigram_embedding():
+    """Smear gate weights 0 (sigmoid = 1/2) and scale 2: position t reads
+    E[x_t] + E[x_(t-1)], which is the plain model on the pair ids x_(t-1) V + x_t
+    with the pair table E2[a V + b] = E[a] + E[b], and V^2 + x_0 for the first
+    position (E2 row E[x_0])."""
+    cfg = dict(MICRO_X, extras=2)
+    V, d = cfg["vocab"], cfg["d_model"]
+    p = _params(cfg, seed=9, std=0.4, random_s=False)
+    p[-1][0, 2 * cfg["depth"]] = 2.0                  # smear scale; gate weights stay 0
+    tok, tgt = _tokens(cfg, seed=10)
+    E = p[0]
+    E2 = np.concatenate([(E[:, None, :] + E[None, :, :]).reshape(V * V, d), E])
+    pair = np.empty_like(tok)
+    pair[:, 1:] = tok[:, :-1] * V + tok[:, 1:]
+    pair[:, 0] = V * V + tok[:, 0]
+    big = dict(cfg, extras=0, vocab=V * V + V)
+    z, _ = O.forward(p, tok, cfg)
+    z2, _ = O.forward([E2] + p[1:-1], pair, big)
+    np.testing.assert_allclose(z, z2, rtol=1e-13, atol=1e-15)
 
 
 # --------------------------------------------------------------------------
