@@ -27,7 +27,7 @@ class GptCfg(ctypes.Structure):
         ("muon_momentum", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("ns_coeffs", (ctypes.c_float * 3) * 5), ("num_steps", ctypes.c_int64),
         ("ns_split_steps", ctypes.c_int32), ("fp8_gemms", ctypes.c_int32), ("attn_window", ctypes.c_int32),
-        ("n_kv_head", ctypes.c_int32),
+        ("n_kv_head", ctypes.c_int32), ("extras", ctypes.c_int32),
     ]
 
     def coeffs(self):
@@ -58,6 +58,7 @@ _SIGS = {
     "gpt_get_momentum": (_I, [_P, ctypes.c_int32, _P, _SZ, _P]),
     "gpt_set_momentum": (_I, [_P, ctypes.c_int32, _P, _SZ, _P]),
     "gpt_tensor_count": (_I, [ctypes.POINTER(GptCfg)]),
+    "gpt_cfg_bytes": (_SZ, []),
     "gpt_tensor_shape": (_I, [ctypes.POINTER(GptCfg), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                               ctypes.POINTER(ctypes.c_int32)]),
     "gpt_last_status": (_I, [_P]),
@@ -131,6 +132,8 @@ def make_cfg(c: dict) -> GptCfg:
         cfg.attn_window = int(c["attn_window"])
     if "n_kv_head" in c:
         cfg.n_kv_head = int(c["n_kv_head"])
+    if "extras" in c:
+        cfg.extras = int(c["extras"])
     if "ns_coeffs" in c:
         for i, abc in enumerate(c["ns_coeffs"]):
             for j in range(3):

@@ -128,6 +128,270 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Extras: per-layer residual scaling, smear and backout.  Their scalars live in the
+// parameter vector on the device; a coefficient is mul * (*p), or mul when p is null.
+
+__device__ inline float coef(const float* p, float mul) { return p ? mul * *p : mul; }
+
+// m = a x + b z (z may be null when b = 0), stored fp32, then y = m / rms(m) as in
+// rmsnorm_fwd
+template <typename T>
+__global__ void __launch_bounds__(256) mix_rmsnorm_fwd_kernel(const float* __restrict__ x, const float* __restrict__ z,
+                                                              const float* pa, float ma, const float* pb, float mb,
+                                                              float* __restrict__ m, T* __restrict__ y,
+                                                              float* __restrict__ rstd, int N, int d, float eps) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const float a = coef(pa, ma), b = z ? coef(pb, mb) : 0.f;
+  const long off = (long)row * d;
+  const float4* xr = reinterpret_cast<const float4*>(x + off);
+  const float4* zr = reinterpret_cast<const float4*>(z ? z + off : x + off);
+  float4* mr = reinterpret_cast<float4*>(m + off);
+  const int n4 = d / 4;
+  float4 v[MAXV4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n4) {
+      const float4 p = xr[i], q = zr[i];
+      v[j] = make_float4(a * p.x + b * q.x, a * p.y + b * q.y, a * p.z + b * q.z, a * p.w + b * q.w);
+      mr[i] = v[j];
+    }
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  T* yr = y + off;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    if (i < n4) st4<T>(yr + 4 * i, make_float4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r));
+  }
+  if (lane == 0) rstd[row] = r;
+}
+
+// Backward of a norm whose input m = a x_a + b x_b was mixed:
+//   g = dres + rstd (dy - ym mean(dy ym)), ym = m rstd      (d loss / d m)
+//   out = a g + add1 + add2 (+ b g when b_to_out), fp32 and the activation copy
+//   acc += b g (when acc is given and not b_to_out)
+//   dots_a[row] = sa (g . x_a), dots_b[row] = sb (g . x_b)  (the scale gradients' rows)
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_mix_bwd_kernel(
+    const float* __restrict__ dy, const float* __restrict__ mx, const float* __restrict__ rstd,
+    const float* __restrict__ dres, const float* pa, float ma, const float* pb, float mb, int b_to_out,
+    const float* __restrict__ add1, const float* __restrict__ add2, float* __restrict__ acc,
+    const float* __restrict__ xa, float* __restrict__ dots_a, float sa, const float* __restrict__ xb,
+    float* __restrict__ dots_b, float sb, float* __restrict__ out, T* __restrict__ outa, int N, int d) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const float a = coef(pa, ma), b = coef(pb, mb);
+  const long off = (long)row * d;
+  const int n4 = d / 4;
+  const float r = rstd[row];
+  float4 yv[MAXV4], gv[MAXV4];
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f), g = v;
+    if (i < n4) {
+      v = reinterpret_cast<const float4*>(mx + off)[i];
+      g = reinterpret_cast<const float4*>(dy + off)[i];
+    }
+    yv[j] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+    gv[j] = g;
+    dot += g.x * yv[j].x + g.y * yv[j].y + g.z * yv[j].z + g.w * yv[j].w;
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float ao = b_to_out ? a + b : a;
+  float da = 0.f, db = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    if (i >= n4) continue;
+    float4 g;
+    g.x = r * (gv[j].x - yv[j].x * dot);
+    g.y = r * (gv[j].y - yv[j].y * dot);
+    g.z = r * (gv[j].z - yv[j].z * dot);
+    g.w = r * (gv[j].w - yv[j].w * dot);
+    if (dres) {
+      const float4 q = reinterpret_cast<const float4*>(dres + off)[i];
+      g.x += q.x; g.y += q.y; g.z += q.z; g.w += q.w;
+    }
+    if (xa) {
+      const float4 q = reinterpret_cast<const float4*>(xa + off)[i];
+      da += g.x * q.x + g.y * q.y + g.z * q.z + g.w * q.w;
+    }
+    if (xb) {
+      const float4 q = reinterpret_cast<const float4*>(xb + off)[i];
+      db += g.x * q.x + g.y * q.y + g.z * q.z + g.w * q.w;
+    }
+    if (acc && !b_to_out) {
+      float4 q = reinterpret_cast<float4*>(acc + off)[i];
+      q.x += b * g.x; q.y += b * g.y; q.z += b * g.z; q.w += b * g.w;
+      reinterpret_cast<float4*>(acc + off)[i] = q;
+    }
+    float4 o = make_float4(ao * g.x, ao * g.y, ao * g.z, ao * g.w);
+    if (add1) {
+      const float4 q = reinterpret_cast<const float4*>(add1 + off)[i];
+      o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+    }
+    if (add2) {
+      const float4 q = reinterpret_cast<const float4*>(add2 + off)[i];
+      o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+    }
+    reinterpret_cast<float4*>(out + off)[i] = o;
+    if (outa) st4<T>(outa + off + 4 * i, o);
+  }
+  if (xa) da = wave_sum(da);
+  if (xb) db = wave_sum(db);
+  if (lane == 0) {
+    if (xa) dots_a[row] = sa * da;
+    if (xb) dots_b[row] = sb * db;
+  }
+}
+
+constexpr int SMEAR_CH = 24;  // channels of the current position the smear gate reads
+
+__device__ inline float sigmoidf_(float z) { return 1.f / (1.f + expf(-z)); }
+
+// the smear-gate weights a lane < 6 pairs with its channels 4 lane .. 4 lane + 3 (ws sits
+// at an odd float pair inside the parameter vector, so it is read by scalars)
+__device__ inline float4 smear_w4(const float* __restrict__ ws, int lane) {
+  return make_float4(ws[4 * lane], ws[4 * lane + 1], ws[4 * lane + 2], ws[4 * lane + 3]);
+}
+
+// gate logit of row n: ws . e[n, 0:24] (lanes 0..5 hold channels 0..23 in v0)
+__device__ inline float smear_logit(const float4& v0, const float* __restrict__ ws, int lane) {
+  float z = 0.f;
+  if (lane < SMEAR_CH / 4) {
+    const float4 w = smear_w4(ws, lane);
+    z = v0.x * w.x + v0.y * w.y + v0.z * w.z + v0.w * w.w;
+  }
+  return wave_sum(z);
+}
+
+// x[n] = e[n] + ls sigmoid(ws . e[n, :24]) e[n-1]; nothing is added at the first
+// position of each sequence (n % T == 0)
+__global__ void __launch_bounds__(256) smear_fwd_kernel(const float* __restrict__ e, const float* __restrict__ pls,
+                                                        const float* __restrict__ ws, float* __restrict__ x, int N,
+                                                        int T, int d) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const long off = (long)row * d;
+  const int n4 = d / 4;
+  const float4* er = reinterpret_cast<const float4*>(e + off);
+  float4* xr = reinterpret_cast<float4*>(x + off);
+  // channels 0..23 sit in lanes 0..5 (d >= 24); lanes past the row load nothing
+  const float4 v0 = lane < n4 ? er[lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float gl = smear_logit(v0, ws, lane);
+  const bool first = row % T == 0;
+  const float g = first ? 0.f : *pls * sigmoidf_(gl);
+  const float4* pr = reinterpret_cast<const float4*>(e + off - (first ? 0 : d));
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    if (i >= n4) continue;
+    const float4 c = er[i];
+    const float4 q = first ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[i];
+    xr[i] = make_float4(c.x + g * q.x, c.y + g * q.y, c.z + g * q.z, c.w + g * q.w);
+  }
+}
+
+// backward of the smear for row n, dx = d loss / d x:
+//   de[n] = dx[n] + gate[n+1] dx[n+1] (same sequence) + dz[n] ws (channels < 24)
+//   dgate[n] = dx[n] . e[n-1],  dz[n] = dgate[n] ls s'(z[n]),  s = sigmoid
+//   part_ls[n] = dgate[n] s(z[n]),  part_ws[c][n] = dz[n] e[n, c]
+__global__ void __launch_bounds__(256) smear_bwd_kernel(const float* __restrict__ dx, const float* __restrict__ e,
+                                                        const float* __restrict__ pls, const float* __restrict__ ws,
+                                                        float* __restrict__ de, float* __restrict__ part_ls,
+                                                        float* __restrict__ part_ws, int N, int T, int d) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const long off = (long)row * d;
+  const int n4 = d / 4;
+  const float ls = *pls;
+  const bool first = row % T == 0, last = (row + 1) % T == 0;  // row + 1 < N unless last
+  const float4* gr = reinterpret_cast<const float4*>(dx + off);
+  const float4* er = reinterpret_cast<const float4*>(e + off);
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 e0 = lane < n4 ? er[lane] : zero4;
+  const float zn = smear_logit(e0, ws, lane);
+  const float sn = sigmoidf_(zn);
+  float gnext = 0.f;
+  if (!last) {
+    const float4 en = lane < n4 ? reinterpret_cast<const float4*>(e + off + d)[lane] : zero4;
+    gnext = ls * sigmoidf_(smear_logit(en, ws, lane));
+  }
+  float dg = 0.f;
+  float4 o[MAXV4];
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    o[j] = zero4;
+    if (i >= n4) continue;
+    const float4 g = gr[i];
+    o[j] = g;
+    if (!first) {
+      const float4 q = reinterpret_cast<const float4*>(e + off - d)[i];
+      dg += g.x * q.x + g.y * q.y + g.z * q.z + g.w * q.w;
+    }
+    if (!last) {
+      const float4 q = reinterpret_cast<const float4*>(dx + off + d)[i];
+      o[j].x += gnext * q.x; o[j].y += gnext * q.y; o[j].z += gnext * q.z; o[j].w += gnext * q.w;
+    }
+  }
+  dg = wave_sum(dg);
+  const float dz = dg * ls * sn * (1.f - sn);
+  if (lane < SMEAR_CH / 4) {
+    const float4 w = smear_w4(ws, lane);
+    o[0].x += dz * w.x; o[0].y += dz * w.y; o[0].z += dz * w.z; o[0].w += dz * w.w;
+    part_ws[(long)(4 * lane + 0) * N + row] = dz * e0.x;
+    part_ws[(long)(4 * lane + 1) * N + row] = dz * e0.y;
+    part_ws[(long)(4 * lane + 2) * N + row] = dz * e0.z;
+    part_ws[(long)(4 * lane + 3) * N + row] = dz * e0.w;
+  }
+  float4* dr = reinterpret_cast<float4*>(de + off);
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i = lane + j * 64;
+    if (i < n4) dr[i] = o[j];
+  }
+  if (lane == 0) part_ls[row] = dg * sn;
+}
+
+// dS[j] = sum over rows of part[j][row] (fixed order, fp64), for the entries of the
+// extras that are switched on; the other entries get 0.  accumulate: added to dS.
+__global__ void __launch_bounds__(256) extras_reduce_kernel(const float* __restrict__ part, int N, int L, int mask,
+                                                            float* __restrict__ dS, int accumulate) {
+  const int j = blockIdx.x;
+  const bool on = j < 2 * L ? (mask & 1) : j == 2 * L + 1 ? (mask & 4) : (mask & 2);
+  __shared__ double red[256];
+  double s = 0.0;
+  if (on)
+    for (int n = threadIdx.x; n < N; n += 256) s += (double)part[(long)j * N + n];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dS[j] = (float)(accumulate ? (double)dS[j] + red[0] : red[0]);
+}
+
+// S at its identity: residual scales 1, every other entry 0
+__global__ void extras_init_kernel(float* S, int L, int n) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < n) S[j] = j < L ? 1.f : 0.f;
+}
+
+// ---------------------------------------------------------------------------
 // RoPE table: cs[t][i] = (cos, sin)(t * base^(-2i/hd)), angles in double precision
 
 __global__ void rope_table_kernel(float* cs, int T, int hd, float base) {
@@ -1033,6 +1297,52 @@ void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs
   else
     hipLaunchKernelGGL(rope_qknorm_bwd_kernel<float>, g, b, 0, st, (float*)dqkv, (const float*)qkv, cs, rq, rk, N, T,
                        H, Hkv, hd);
+}
+
+void launch_mix_rmsnorm_fwd(const float* x, const float* z, const float* pa, float ma, const float* pb, float mb,
+                            float* m, void* y, int yt, float* rstd, int N, int d, float eps, hipStream_t st) {
+  dim3 g((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), b(256);
+  if (yt == ACT_BF16)
+    hipLaunchKernelGGL(mix_rmsnorm_fwd_kernel<bf16_t>, g, b, 0, st, x, z, pa, ma, pb, mb, m, (bf16_t*)y, rstd, N, d,
+                       eps);
+  else
+    hipLaunchKernelGGL(mix_rmsnorm_fwd_kernel<float>, g, b, 0, st, x, z, pa, ma, pb, mb, m, (float*)y, rstd, N, d,
+                       eps);
+}
+
+void launch_rmsnorm_mix_bwd(const float* dy, const float* m, const float* rstd, const float* dres, const float* pa,
+                            float ma, const float* pb, float mb, bool b_to_out, const float* add1, const float* add2,
+                            float* acc, const float* xa, float* dots_a, float sa, const float* xb, float* dots_b,
+                            float sb, float* out, void* outa, int at, int N, int d, hipStream_t st) {
+  dim3 g((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(rmsnorm_mix_bwd_kernel<bf16_t>, g, b, 0, st, dy, m, rstd, dres, pa, ma, pb, mb, (int)b_to_out,
+                       add1, add2, acc, xa, dots_a, sa, xb, dots_b, sb, out, (bf16_t*)outa, N, d);
+  else
+    hipLaunchKernelGGL(rmsnorm_mix_bwd_kernel<float>, g, b, 0, st, dy, m, rstd, dres, pa, ma, pb, mb, (int)b_to_out,
+                       add1, add2, acc, xa, dots_a, sa, xb, dots_b, sb, out, (float*)outa, N, d);
+}
+
+void launch_smear_fwd(const float* e, const float* pls, const float* ws, float* x, int N, int T, int d,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(smear_fwd_kernel, dim3((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), dim3(256), 0, st, e, pls, ws,
+                     x, N, T, d);
+}
+
+void launch_smear_bwd(const float* dx, const float* e, const float* pls, const float* ws, float* de, float* part_ls,
+                      float* part_ws, int N, int T, int d, hipStream_t st) {
+  hipLaunchKernelGGL(smear_bwd_kernel, dim3((N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), dim3(256), 0, st, dx, e, pls,
+                     ws, de, part_ls, part_ws, N, T, d);
+}
+
+void launch_extras_reduce(const float* part, int N, int L, int mask, float* dS, bool accumulate, hipStream_t st) {
+  hipLaunchKernelGGL(extras_reduce_kernel, dim3(2 * L + 2 + SMEAR_CH), dim3(256), 0, st, part, N, L, mask, dS,
+                     (int)accumulate);
+}
+
+void launch_extras_init(float* S, int L, hipStream_t st) {
+  const int n = 2 * L + 2 + SMEAR_CH;
+  hipLaunchKernelGGL(extras_init_kernel, dim3((n + 255) / 256), dim3(256), 0, st, S, L, n);
 }
 
 template <typename T>

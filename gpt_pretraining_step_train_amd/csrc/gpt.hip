@@ -43,6 +43,15 @@ inline int kv_heads(const gpt_cfg& c) { return c.n_kv_head > 0 ? c.n_kv_head : c
 inline size_t kv_dim(const gpt_cfg& c) { return (size_t)kv_heads(c) * c.head_dim; }
 // columns of the fused QKV projection output: q (d), k and v (kv_dim each)
 inline size_t qkv_dim(const gpt_cfg& c) { return (size_t)c.d_model + 2 * kv_dim(c); }
+// the extras' parameter vector S (when any extra is on): residual scales lr[L], x0
+// scales l0[L], the smear scale ls, the backout scale lb, the smear-gate weights ws[24]
+constexpr int kSmearCh = 24;
+inline size_t n_extras(const gpt_cfg& c) { return c.extras ? (size_t)2 * c.depth + 2 + kSmearCh : 0; }
+inline int s_lr(const gpt_cfg&, int l) { return l; }
+inline int s_l0(const gpt_cfg& c, int l) { return c.depth + l; }
+inline int s_ls(const gpt_cfg& c) { return 2 * c.depth; }
+inline int s_lb(const gpt_cfg& c) { return 2 * c.depth + 1; }
+inline int s_ws(const gpt_cfg& c) { return 2 * c.depth + 2; }
 
 // element offsets of the six block matrices inside one layer's slice
 struct LayerOffs {
@@ -60,7 +69,7 @@ struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      xq8t, amax, qinv;
+      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart;
   size_t splitws_bytes;
 };
 
@@ -96,11 +105,20 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   const size_t es = act_of(c) == ACT_BF16 ? 2 : 4;
   const size_t nE = V * d, nU = V * d, nBlk = L * layer_offs(c).stride;
   const size_t s = std::min(d, F), l = std::max(d, F);
-  O.params = P.add((nE + nBlk + nU) * 4);
-  O.grads = P.add((nE + nBlk + nU) * 4);
+  const size_t nS = n_extras(c);
+  O.params = P.add((nE + nBlk + nU + nS) * 4);  // E, blocks, U, S
+  O.grads = P.add((nE + nBlk + nU + nS) * 4);
   O.mom = P.add(nBlk * 4);
-  O.adam_m = P.add((nE + nU) * 4);  // AdamW moments of E then U
-  O.adam_v = P.add((nE + nU) * 4);
+  O.adam_m = P.add((nE + nU + nS) * 4);  // AdamW moments of E, U, then S
+  O.adam_v = P.add((nE + nU + nS) * 4);
+  // extras: mixed layer inputs, the final norm's input, the raw embedding, the gradient
+  // sums flowing to x0 and x_mid, and the per-row terms of dS
+  O.hx = c.extras & GPT_EXTRA_RESID ? P.add(L * N * d * 4) : 0;
+  O.dx0 = c.extras & GPT_EXTRA_RESID ? P.add(N * d * 4) : 0;
+  O.hfin = c.extras & GPT_EXTRA_BACKOUT ? P.add(N * d * 4) : 0;
+  O.dmid = c.extras & GPT_EXTRA_BACKOUT ? P.add(N * d * 4) : 0;
+  O.emb = c.extras & GPT_EXTRA_SMEAR ? P.add(N * d * 4) : 0;
+  O.xpart = nS ? P.add(nS * N * 4) : 0;
   O.wact = es == 2 ? P.add(nBlk * es) : 0;
   O.uact = es == 2 ? P.add(nU * es) : 0;
   O.hs = P.add((2 * L + 1) * N * d * 4);
@@ -182,7 +200,7 @@ struct gpt_model {
   int at = ACT_BF16;
   size_t es = 2;
   int N = 0;
-  size_t nE = 0, nBlk = 0, nU = 0;
+  size_t nE = 0, nBlk = 0, nU = 0, nS = 0;
   LayerOffs lo;
   int last_status = GPT_OK;
   bool stepped = false;
@@ -249,7 +267,8 @@ int run_gemm(gpt_model* M, GemmArgs p, hipStream_t st, bool allow_split) {
 bool same_shape(const gpt_cfg& a, const gpt_cfg& b) {
   return a.depth == b.depth && a.d_model == b.d_model && a.n_head == b.n_head && a.head_dim == b.head_dim &&
          a.d_ff == b.d_ff && a.vocab == b.vocab && a.seq_len == b.seq_len && a.batch == b.batch &&
-         a.precision == b.precision && a.attn_window == b.attn_window && kv_heads(a) == kv_heads(b);
+         a.precision == b.precision && a.attn_window == b.attn_window && kv_heads(a) == kv_heads(b) &&
+         a.extras == b.extras;
 }
 
 // element offset of tensor id inside the parameter/gradient vector, and its shape
@@ -258,6 +277,12 @@ bool tensor_loc(const gpt_cfg& c, int id, size_t* off, int* rows, int* cols) {
   const LayerOffs lo = layer_offs(c);
   if (id == 0) { *off = 0; *rows = (int)V; *cols = (int)d; return true; }
   if (id == (int)(1 + 6 * L)) { *off = V * d + L * lo.stride; *rows = (int)V; *cols = (int)d; return true; }
+  if (id == (int)(2 + 6 * L) && c.extras) {
+    *off = 2 * V * d + L * lo.stride;
+    *rows = 1;
+    *cols = (int)n_extras(c);
+    return true;
+  }
   if (id < 1 || id > (int)(6 * L)) return false;
   const int l = (id - 1) / 6, j = (id - 1) % 6;
   const size_t b = V * d + l * lo.stride;
@@ -295,6 +320,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->fp8_gemms = GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD;
   out->attn_window = 0;
   out->n_kv_head = 0;
+  out->extras = 0;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
   out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
@@ -320,6 +346,8 @@ int gpt_cfg_validate(const gpt_cfg* c) {
   if (c->fp8_gemms & ~(GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD)) return GPT_ERR_ARG;
   if (c->attn_window < 0) return GPT_ERR_ARG;
   if (c->n_kv_head < 0 || c->n_kv_head > c->n_head || c->n_head % kv_heads(*c) != 0) return GPT_ERR_SHAPE;
+  if (c->extras & ~(GPT_EXTRA_RESID | GPT_EXTRA_SMEAR | GPT_EXTRA_BACKOUT)) return GPT_ERR_ARG;
+  if ((c->extras & GPT_EXTRA_SMEAR) && c->d_model < kSmearCh) return GPT_ERR_SHAPE;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
 }
@@ -331,7 +359,9 @@ size_t gpt_state_bytes(const gpt_cfg* c) {
   return total;
 }
 
-int gpt_tensor_count(const gpt_cfg* c) { return c ? 2 + 6 * c->depth : 0; }
+size_t gpt_cfg_bytes(void) { return sizeof(gpt_cfg); }
+
+int gpt_tensor_count(const gpt_cfg* c) { return c ? 2 + 6 * c->depth + (c->extras ? 1 : 0) : 0; }
 
 int gpt_tensor_shape(const gpt_cfg* c, int32_t id, int32_t* rows, int32_t* cols) {
   if (!c || !rows || !cols) return GPT_ERR_ARG;
@@ -389,6 +419,7 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   M->nE = (size_t)cfg->vocab * cfg->d_model;
   M->nU = M->nE;
   M->nBlk = (size_t)cfg->depth * M->lo.stride;
+  M->nS = n_extras(*cfg);
   const int L = cfg->depth, d = cfg->d_model, F = cfg->d_ff;
   for (int l = 0; l < L; ++l) {
     const size_t b = (size_t)l * M->lo.stride;
@@ -408,10 +439,11 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
     const float sd = cfg->init_std * ((j == 3 || j == 5) ? 1.f / sqrtf(2.f * L) : 1.f);
     launch_fill_normal(M->params() + off, (size_t)r * c, seed, (uint64_t)id, sd, st);
   }
+  if (M->nS) launch_extras_init(M->params() + M->nE + M->nBlk + M->nU, L, st);
   launch_zero(M->at_off<float>(O.mom), M->nBlk * 4, st);
-  launch_zero(M->at_off<float>(O.adam_m), (M->nE + M->nU) * 4, st);
-  launch_zero(M->at_off<float>(O.adam_v), (M->nE + M->nU) * 4, st);
-  launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU) * 4, st);
+  launch_zero(M->at_off<float>(O.adam_m), (M->nE + M->nU + M->nS) * 4, st);
+  launch_zero(M->at_off<float>(O.adam_v), (M->nE + M->nU + M->nS) * 4, st);
+  launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU + M->nS) * 4, st);
   refresh_act(M, st);
   launch_rope_table(M->at_off<float>(O.rope), cfg->seq_len, cfg->head_dim, cfg->rope_base, st);
   if (hipMemcpyAsync(M->at_off<long>(O.mat_off), M->moff.data(), M->moff.size() * 8, hipMemcpyHostToDevice, st) !=
@@ -568,6 +600,14 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   auto actp = [&](size_t o, size_t elems) -> void* { return M->base + o + elems * es; };
   auto hsl = [&](int i) { return hs + (size_t)i * N * d; };
   int rc;
+  // extras: S on the device, and the buffers they need
+  const bool ex_resid = c.extras & GPT_EXTRA_RESID, ex_smear = c.extras & GPT_EXTRA_SMEAR,
+             ex_back = c.extras & GPT_EXTRA_BACKOUT;
+  const float* S = M->params() + M->nE + M->nBlk + M->nU;
+  const int Lb = L / 2;  // backout reads the stream entering this layer
+  float* xpart = M->at_off<float>(O.xpart);  // [2L+26][N] per-row terms of dS
+  // the stream layer l adds its blocks to (its mixed input under residual scaling)
+  auto xres = [&](int l) { return ex_resid ? M->at_off<float>(O.hx) + (size_t)l * N * d : hsl(2 * l); };
 
   launch_zero(err, 16, st);
   if (M->fp8) {
@@ -576,7 +616,13 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     if (M->wq_dirty) quant_weights(M, st);
     else M->qslot = 4 * L + 1;
   }
-  launch_embed_gather(tok, M->params(), hsl(0), N, d, V, err, st);
+  if (ex_smear) {
+    float* emb = M->at_off<float>(O.emb);
+    launch_embed_gather(tok, M->params(), emb, N, d, V, err, st);
+    launch_smear_fwd(emb, S + s_ls(c), S + s_ws(c), hsl(0), N, T, d, st);
+  } else {
+    launch_embed_gather(tok, M->params(), hsl(0), N, d, V, err, st);
+  }
   for (int l = 0; l < L; ++l) {
     void* a = actp(O.a, (size_t)l * N * d);
     void* qkv = actp(O.qkv, (size_t)l * N * QD);
@@ -587,7 +633,11 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
     float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
-    launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
+    if (ex_resid)  // layer input lr x + l0 x0
+      launch_mix_rmsnorm_fwd(hsl(2 * l), hsl(0), S + s_lr(c, l), 1.f, S + s_l0(c, l), 1.f, xres(l), a, at,
+                             M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
+    else
+      launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
     {
       GemmArgs p;  // qkv = a Wqkv^T
       p.M = N; p.N = QD; p.K = d; p.A = a; p.lda = d;
@@ -599,7 +649,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     {
       GemmArgs p;  // h' = h + o Wo^T
       p.M = N; p.N = d; p.K = d; p.A = o; p.lda = d;
-      p.Cin = hsl(2 * l); p.ldcin = d; p.beta = 1.f;
+      p.Cin = xres(l); p.ldcin = d; p.beta = 1.f;
       p.outF = hsl(2 * l + 1); p.ldo = d;
       if ((rc = lin_fwd(M, p, 4 * l + 1, st))) return rc;
     }
@@ -619,7 +669,11 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     }
   }
   void* r = M->base + O.r;
-  launch_rmsnorm_fwd(hsl(2 * L), r, at, M->at_off<float>(O.rstd_f), N, d, eps, st);
+  if (ex_back)  // the final norm reads x_L - lb x_mid
+    launch_mix_rmsnorm_fwd(hsl(2 * L), hsl(2 * Lb), nullptr, 1.f, S + s_lb(c), -1.f, M->at_off<float>(O.hfin), r, at,
+                           M->at_off<float>(O.rstd_f), N, d, eps, st);
+  else
+    launch_rmsnorm_fwd(hsl(2 * L), r, at, M->at_off<float>(O.rstd_f), N, d, eps, st);
   float* logits = M->at_off<float>(O.logits);
   void* dlogits = M->base + O.dlogits;
   {
@@ -646,7 +700,17 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     pd.outF = dtmp; pd.ldo = d;
     if ((rc = lin_bwd(M, dlogits, V, r, d, 4 * L, grads + M->nE + M->nBlk, pd, st))) return rc;
   }
-  launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps, st);
+  float* dmid = M->at_off<float>(O.dmid);  // d loss / d x_mid through the backout term
+  float* dx0 = M->at_off<float>(O.dx0);    // d loss / d x0 through the l0 terms of layers 1..L-1
+  if (ex_back) {
+    launch_zero(dmid, (size_t)N * d * 4, st);
+    launch_rmsnorm_mix_bwd(dtmp, M->at_off<float>(O.hfin), M->at_off<float>(O.rstd_f), nullptr, nullptr, 1.f,
+                           S + s_lb(c), -1.f, false, nullptr, nullptr, dmid, hsl(2 * Lb),
+                           xpart + (size_t)s_lb(c) * N, -1.f, nullptr, nullptr, 0.f, dh[0], dh_act, at, N, d, st);
+  } else {
+    launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps, st);
+  }
+  if (ex_resid) launch_zero(dx0, (size_t)N * d * 4, st);
   int cur = 0;
   for (int l = L - 1; l >= 0; --l) {
     const size_t wl = (size_t)l * M->lo.stride;
@@ -688,11 +752,31 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       pd.outF = dtmp; pd.ldo = d;
       if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
     }
-    launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur], dh[cur ^ 1], dh_act,
-                       at, N, d, eps, st);
+    if (ex_resid || (ex_back && l == Lb)) {
+      // g = d loss / d (layer input); the stream reaching the layer gets lr g (plus the
+      // backout's x_mid term at layer L/2), x0 collects l0 g (layer 0: added to its own
+      // stream, which is x0, together with the other layers' sum)
+      launch_rmsnorm_mix_bwd(dtmp, xres(l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur],
+                             ex_resid ? S + s_lr(c, l) : nullptr, 1.f, ex_resid ? S + s_l0(c, l) : nullptr,
+                             ex_resid ? 1.f : 0.f, l == 0, ex_back && l == Lb ? dmid : nullptr,
+                             ex_resid && l == 0 ? dx0 : nullptr, ex_resid && l > 0 ? dx0 : nullptr,
+                             ex_resid ? hsl(2 * l) : nullptr, xpart + (size_t)s_lr(c, l) * N, 1.f,
+                             ex_resid ? hsl(0) : nullptr, xpart + (size_t)s_l0(c, l) * N, 1.f, dh[cur ^ 1], dh_act,
+                             at, N, d, st);
+    } else {
+      launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur], dh[cur ^ 1], dh_act,
+                         at, N, d, eps, st);
+    }
+    cur ^= 1;
+  }
+  if (ex_smear) {  // back through x = e + gate * previous e
+    launch_smear_bwd(dh[cur], M->at_off<float>(O.emb), S + s_ls(c), S + s_ws(c), dh[cur ^ 1],
+                     xpart + (size_t)s_ls(c) * N, xpart + (size_t)s_ws(c) * N, N, T, d, st);
     cur ^= 1;
   }
   launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st, M->acc_grads);
+  if (c.extras)
+    launch_extras_reduce(xpart, N, L, c.extras, grads + M->nE + M->nBlk + M->nU, M->acc_grads, st);
   return GPT_OK;
 }
 
@@ -741,6 +825,9 @@ int adamw_update(gpt_model* M, float lr, float beta1, float beta2, float eps, fl
                st);
   launch_adamw(M->params() + uo, M->grads() + uo, m + M->nE, v + M->nE, M->at == ACT_BF16 ? M->uact() : nullptr, M->at,
                M->nU, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2, st);
+  if (M->nS)  // the extras' scalars follow U in every table
+    launch_adamw(M->params() + uo + M->nU, M->grads() + uo + M->nU, m + M->nE + M->nU, v + M->nE + M->nU, nullptr,
+                 ACT_F32, M->nS, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2, st);
   M->wq_dirty = true;  // the e4m3 copies of U follow the master weights
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
@@ -867,7 +954,7 @@ static int copy_tensor(gpt_model* M, int id, float* region, bool to_host, float*
   if (!M || !h || !tensor_loc(M->cfg, id, &off, &r, &c)) return GPT_ERR_ARG;
   if (n != (size_t)r * c) return GPT_ERR_ARG;
   if (blocks_only) {
-    if (id == 0 || id == 1 + 6 * M->cfg.depth) return GPT_ERR_ARG;
+    if (id == 0 || id >= 1 + 6 * M->cfg.depth) return GPT_ERR_ARG;
     off -= M->nE;
   }
   float* p = region + off;
@@ -906,7 +993,7 @@ int gpt_set_params(gpt_model* M, int32_t id, const float* h, size_t n, void* s) 
     tensor_loc(M->cfg, id, &off, &r, &c);
     if (id == 1 + 6 * M->cfg.depth)
       launch_cast_f32_to_act(M->params() + off, M->uact(), M->at, n, st);
-    else if (id != 0)
+    else if (id != 0 && id != 2 + 6 * M->cfg.depth)  // E and S have no act copies
       launch_cast_f32_to_act(M->params() + off, M->wact(off - M->nE), M->at, n, st);
   }
   return hipStreamSynchronize(st) == hipSuccess ? GPT_OK : GPT_ERR_HIP;

@@ -63,6 +63,26 @@ void launch_rmsnorm_fwd(const float* x, void* y, int ytype, float* rstd, int N, 
                         hipStream_t st);
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres,
                         float* dx, void* dx_act, int act_type, int N, int d, float eps, hipStream_t st);
+// extras (per-layer residual scaling, smear, backout).  A coefficient is mul * (*p), or mul
+// when p is null; p points into the parameter vector on the device.
+// m = a x + b z (fp32, z null: b = 0), y = m / rms(m), rstd as for launch_rmsnorm_fwd
+void launch_mix_rmsnorm_fwd(const float* x, const float* z, const float* pa, float ma, const float* pb, float mb,
+                            float* m, void* y, int yt, float* rstd, int N, int d, float eps, hipStream_t st);
+// g = dres + (norm backward of m); out = a g + add1 + add2 (+ b g if b_to_out) with its act copy;
+// acc += b g otherwise (if acc); dots_a[row] = sa g.xa, dots_b[row] = sb g.xb (if xa / xb)
+void launch_rmsnorm_mix_bwd(const float* dy, const float* m, const float* rstd, const float* dres, const float* pa,
+                            float ma, const float* pb, float mb, bool b_to_out, const float* add1, const float* add2,
+                            float* acc, const float* xa, float* dots_a, float sa, const float* xb, float* dots_b,
+                            float sb, float* out, void* outa, int at, int N, int d, hipStream_t st);
+// x[n] = e[n] + ls sigmoid(ws . e[n,:24]) e[n-1] within sequences of T rows (d >= 24)
+void launch_smear_fwd(const float* e, const float* pls, const float* ws, float* x, int N, int T, int d,
+                      hipStream_t st);
+// de from dx; part_ls [N] and part_ws [24][N] hold the per-row terms of dls and dws
+void launch_smear_bwd(const float* dx, const float* e, const float* pls, const float* ws, float* de, float* part_ls,
+                      float* part_ws, int N, int T, int d, hipStream_t st);
+// dS[j] (+)= sum_n part[j][n] for j < 2L + 26 (entries of extras not in mask: 0)
+void launch_extras_reduce(const float* part, int N, int L, int mask, float* dS, bool accumulate, hipStream_t st);
+void launch_extras_init(float* S, int L, hipStream_t st);
 void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st);
 // qkv rows are [H q heads | Hkv k heads | Hkv v heads] x hd; rstd_q is [B*T][H], rstd_k [B*T][Hkv]
 void launch_rope_qknorm_fwd(void* qkv, int act_type, const float* cs, float* rstd_q, float* rstd_k,

@@ -17,8 +17,11 @@
  *  - Matrices are row-major [rows][cols] float32 in the [out][in] convention of
  *    the article's Linear layer (F.linear with no bias).
  *  - Tensor ids (gpt_tensor_shape): 0 = E [V][d]; for layer l, ids 1+6l .. 6+6l
- *    are Wq [d][d], Wk [d][d], Wv [d][d], Wo [d][d], W1 [F][d], W2 [d][F];
- *    id 1+6L = U [V][d] (LM head).  Count = 2 + 6L.
+ *    are Wq [d][d], Wk [dkv][d], Wv [dkv][d], Wo [d][d], W1 [F][d], W2 [d][F]
+ *    (dkv = n_kv_head * head_dim); id 1+6L = U [V][d] (LM head).  With any
+ *    extras switched on, id 2+6L = S [1][2L+26]: the L residual scales, the L x0
+ *    scales, the smear scale, the backout scale and the 24 smear-gate weights.
+ *    Count = 2 + 6L (+1 with extras).
  *  - Ownership: the caller owns the arena, the token buffers and the stream and
  *    keeps them alive until the stream's work completes.  The library never
  *    allocates device memory; gpt_free releases host bookkeeping only.
@@ -85,9 +88,20 @@ typedef struct gpt_cfg {
                          n_kv_head query heads (query head h uses key/value head
                          h / (n_head / n_kv_head)); Wk, Wv are (n_kv_head * head_dim) x d.
                          0 (the default) = n_head; must divide n_head, else GPT_ERR_SHAPE */
+  int32_t extras;     /* a mask of the efficiency tricks printed under the GPT model section
+                         of the nanochat articles, with their parameters in tensor S:
+                         GPT_EXTRA_RESID: layer i reads lr[i] x + l0[i] x0 (x the stream
+                           reaching it, x0 the stream entering layer 0);
+                         GPT_EXTRA_SMEAR: after the embedding, x[t] += ls sigmoid(ws .
+                           x[t, 0:24]) x[t-1] within each sequence (d >= 24);
+                         GPT_EXTRA_BACKOUT: the final norm reads x_L - lb x_mid, x_mid the
+                           stream entering layer L/2.
+                         S starts at the identity (lr = 1, the rest 0); AdamW updates it.
+                         0 (the default) = none; other bits: GPT_ERR_ARG */
 } gpt_cfg;
 
 enum { GPT_FP8_FWD = 1, GPT_FP8_WGRAD = 2, GPT_FP8_DGRAD = 4 };
+enum { GPT_EXTRA_RESID = 1, GPT_EXTRA_SMEAR = 2, GPT_EXTRA_BACKOUT = 4 };
 
 typedef struct gpt_model gpt_model; /* opaque */
 
@@ -98,6 +112,9 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out);
 
 /* CPU-only consistency check of a configuration. */
 int gpt_cfg_validate(const gpt_cfg* cfg);
+
+/* sizeof(gpt_cfg) as compiled into the library (for bindings that mirror it). */
+size_t gpt_cfg_bytes(void);
 
 /* Bytes of device memory the model needs (parameters, gradients, momentum,
  * saved activations and workspaces); 0 when cfg is invalid. */
@@ -136,10 +153,10 @@ int gpt_grads(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* str
  * E and U are not touched.  Stream-ordered, no synchronisation. */
 int muon_update(gpt_model* m, float lr, void* stream);
 
-/* AdamW on the token embedding E and the LM head U (the tensors Muon leaves to it,
- * per the parameter-type table of "2. Muon Optimize Edici" in the nanochat
- * articles; they print no formula or hyperparameters, so Adam's bias-corrected
- * moments with decoupled weight decay are used).  For the t-th call on this model,
+/* AdamW on the token embedding E, the LM head U and the extras' scalars S (the
+ * tensors Muon leaves to it, per the parameter-type table of "2. Muon Optimize
+ * Edici" in the nanochat articles; they print no formula or hyperparameters, so
+ * Adam's bias-corrected moments with decoupled weight decay are used).  For the t-th call on this model,
  * with g the gradient of the last gpt_step:
  *   m <- beta1 m + (1-beta1) g;  v <- beta2 v + (1-beta2) g^2;
  *   w <- w - lr wd w - lr (m / (1-beta1^t)) / (sqrt(v / (1-beta2^t)) + eps)

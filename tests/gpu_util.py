@@ -20,6 +20,16 @@ def from_dev(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def random_extras(params, cfg, seed):
+    """Move the extras tensor S (last in the table, when the cfg has extras) off its
+    start values (which leave the extras inert) by 0.3 N(0, 1) per entry, as
+    training would."""
+    if cfg.get("extras"):
+        rng = np.random.default_rng(seed + 1000)
+        params[-1] = (params[-1] + 0.3 * rng.standard_normal(params[-1].shape)).astype(np.float32)
+    return params
+
+
 def rel_l2(x, ref) -> float:
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

@@ -60,12 +60,12 @@ def test_param_counts_match_survey_shapes():
 def test_default_ns_table(lib):
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "ns_printed_coeffs.json")))
     c = binding.GptCfg()
-    c.attn_window, c.n_kv_head = 7, 3  # overwritten with the defaults
+    c.attn_window, c.n_kv_head, c.extras = 7, 3, 5  # overwritten with the defaults
     lib.gpt_cfg_from_depth(24, ctypes.byref(c))
     tab = c.coeffs()
     assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 4 and c.fp8_gemms == 7
-    assert c.attn_window == 0 and c.n_kv_head == 0
-    assert ctypes.sizeof(binding.GptCfg) == 144
+    assert c.attn_window == 0 and c.n_kv_head == 0 and c.extras == 0
+    assert ctypes.sizeof(binding.GptCfg) == lib.gpt_cfg_bytes() == 152
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
     derived, _ = polar_express.coefficients()
     np.testing.assert_allclose(tab[2:], derived[2:], rtol=0, atol=2e-5)
@@ -77,7 +77,7 @@ def test_validation_errors(lib):
     for field, val, code in [("head_dim", 48, 6), ("n_head", 5, 2), ("d_model", 2056, 2), ("precision", 7, 6),
                              ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2), ("fp8_gemms", 8, 1),
                              ("attn_window", -1, 1), ("n_kv_head", 2, 2), ("n_kv_head", 4, 2),
-                             ("n_kv_head", -1, 2)]:
+                             ("n_kv_head", -1, 2), ("extras", 8, 1), ("extras", -1, 1)]:
         c = binding.make_cfg(configs.get("laptop"))
         setattr(c, field, val)
         assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, field
@@ -88,7 +88,8 @@ def test_validation_errors(lib):
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {}), ("d12", {}), ("d24", {}),
                                        ("tiny", {"n_kv_head": 2}), ("laptop", {"n_kv_head": 1}),
-                                       ("d24", {"n_kv_head": 4})])
+                                       ("d24", {"n_kv_head": 4}), ("tiny", {"extras": 7}),
+                                       ("laptop", {"extras": 2}), ("d24", {"extras": 7, "n_kv_head": 4})])
 def test_state_bytes_and_tensor_table(lib, name, over):
     for cfg in [configs.get(name, **over)]:
         c = binding.make_cfg(cfg)
@@ -96,7 +97,7 @@ def test_state_bytes_and_tensor_table(lib, name, over):
         n = configs.n_params(cfg)
         assert nb > 3 * 4 * n                     # params + grads + momentum at least
         assert nb < 288 * 2 ** 30                # fits one MI355X
-        assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"]
+        assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"] + (1 if cfg.get("extras") else 0)
         shapes = inputs.tensor_shapes(cfg)
         assert n == sum(r * k for _, (r, k) in shapes)
         for i, (nm, shp) in enumerate(shapes):

@@ -15,7 +15,7 @@ import torch
 
 from gpt_pretraining_step_train_amd import binding, configs, inputs
 from oracle import gpt_oracle as O
-from tests.gpu_util import rel_l2, say
+from tests.gpu_util import random_extras, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _gpu():
 def _model(name, **over):
     cfg = configs.get(name, **over)
     model = binding.Model(cfg, seed=0)
-    params = inputs.init_weights(cfg, 0)
+    params = random_extras(inputs.init_weights(cfg, 0), cfg, 0)
     model.set_all_params(params)
     return cfg, model, params
 
@@ -42,7 +42,8 @@ def _batch(cfg, seed):
 
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {"batch": 8}),
-                                       ("laptop", {"batch": 8, "precision": "fp8"})], ids=["fp32", "bf16", "fp8"])
+                                       ("laptop", {"batch": 8, "precision": "fp8"}),
+                                       ("laptop", {"batch": 8, "extras": 7})], ids=["fp32", "bf16", "fp8", "extras"])
 def test_grad_scale_is_exact(name, over):
     cfg, model, params = _model(name, **over)
     _, _, dt, dg = _batch(cfg, 3)
@@ -56,7 +57,8 @@ def test_grad_scale_is_exact(name, over):
 
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {"batch": 8}),
-                                       ("laptop", {"batch": 8, "precision": "fp8"})], ids=["fp32", "bf16", "fp8"])
+                                       ("laptop", {"batch": 8, "precision": "fp8"}),
+                                       ("laptop", {"batch": 8, "extras": 7})], ids=["fp32", "bf16", "fp8", "extras"])
 def test_accumulated_gradient_is_the_total_batch_gradient(name, over):
     cfg, model, params = _model(name, **over)
     n = 3

@@ -21,7 +21,7 @@ import torch
 from gpt_pretraining_step_train_amd import binding, configs, inputs
 from oracle import gpt_oracle as O
 from oracle import polar_express as PE
-from tests.gpu_util import rel_l2, say
+from tests.gpu_util import random_extras, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def _gpu():
 def _setup(name, seed=0, **over):
     cfg = configs.get(name.split("_")[0], **over)  # the case name starts with the config name
     model = binding.Model(cfg, seed=seed)
-    params = inputs.init_weights(cfg, seed)
+    params = random_extras(inputs.init_weights(cfg, seed), cfg, seed)
     model.set_all_params(params)
     tok, tgt = inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=seed)
     return cfg, model, params, tok, tgt
@@ -60,6 +60,10 @@ STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8"
               ("tiny_gqa", {"n_kv_head": 2}), ("laptop_mqa", {"n_kv_head": 1}),
               ("laptop_mqa_fp8", {"precision": "fp8", "n_kv_head": 1}),
               ("d12_gqa", {"batch": 1, "n_kv_head": 2}),
+              ("tiny_extras", {"extras": 7}), ("laptop_extras", {"extras": 7}),
+              ("laptop_resid", {"extras": 1}), ("laptop_smear", {"extras": 2}), ("laptop_backout", {"extras": 4}),
+              ("laptop_extras_fp8", {"precision": "fp8", "extras": 7}),
+              ("d12_extras", {"batch": 1, "extras": 7, "n_kv_head": 2}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
@@ -111,9 +115,10 @@ def test_step_and_muon_parity(name, over):
         assert e <= (1e-4 if fp32 else 2e-2), (i, e)
         np.testing.assert_array_equal(model.get_momentum(i), grads[i])
     say(f"  worst Muon update rel L2 {worst:.2e}")
-    # E and U untouched
+    # E, U (and the extras' S) untouched
     np.testing.assert_array_equal(model.get_params(0), params[0])
-    np.testing.assert_array_equal(model.get_params(1 + 6 * L), params[-1])
+    for i in range(1 + 6 * L, len(params)):
+        np.testing.assert_array_equal(model.get_params(i), params[i])
 
 
 def test_fp8_two_layers_within_the_oracles_own_spread():
