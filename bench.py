@@ -90,6 +90,9 @@ def main() -> int:
                     help="sliding-window attention: query i sees keys i-W < j <= i (0: full causal)")
     ap.add_argument("--kv-heads", type=int, default=0, metavar="H",
                     help="grouped-query attention with H key/value heads (0: one per query head)")
+    ap.add_argument("--extras", type=int, default=0, metavar="MASK",
+                    help="1 per-layer residual scaling, 2 smear, 4 backout (their scalars at the start values, "
+                         "which do not change the cost; AdamW updates them when --adamw is given)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant", default=None,
                     help="kernel timed for the roofline (default: the NT GEMM of the step's precision)")
@@ -116,7 +119,7 @@ def main() -> int:
 
     from gpt_pretraining_step_train_amd import binding, configs, inputs
 
-    cfg = configs.get(args.config, attn_window=args.window, n_kv_head=args.kv_heads)
+    cfg = configs.get(args.config, attn_window=args.window, n_kv_head=args.kv_heads, extras=args.extras)
     if args.dominant is None:
         args.dominant = "gemm_fp8_dma_kernel<256,256,NT>" if args.fp8 else "gemm_bf16_dma_kernel<256,256,NT>"
     cfg["precision"] = "fp8" if args.fp8 else "bf16"
@@ -194,9 +197,11 @@ def main() -> int:
                                 f"fwd+bwd+Muon(5 NS){'+AdamW(E,U)' if args.adamw else ''} on B={B} x T={T}")
                                + (f", sliding-window attention W={args.window}" if args.window else "")
                                + (f", grouped-query attention with {args.kv_heads} key/value heads"
-                                  if args.kv_heads else ""),
+                                  if args.kv_heads else "")
+                               + (f", extras mask {args.extras} (1 residual scaling, 2 smear, 4 backout)"
+                                  if args.extras else ""),
                    "depth": cfg["depth"], "d_model": cfg["d_model"], "n_head": cfg["n_head"],
-                   "n_kv_head": configs.kv_heads(cfg), "attn_window": args.window,
+                   "n_kv_head": configs.kv_heads(cfg), "attn_window": args.window, "extras": args.extras,
                    "vocab": V, "global_batch": B * K, "micro_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "mfu": mfu, "mfu_at_fp8_peak_for_linears": mfu_fp8, "flops_per_step": fl["total"], "wall_s": wall,
         "loss_first_last": [losses[0], losses[-1]],
