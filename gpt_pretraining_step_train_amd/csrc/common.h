@@ -84,6 +84,13 @@ __device__ inline f32x16_t mfma32x32x16_bf16(const bf16x8_t& a, const bf16x8_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// IEEE binary16 (fp16): same MFMA rate and operand layout as bf16, 11 significant bits
+typedef _Float16 f16_t;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ inline f32x16_t mfma32x32x16_f16(const f16x8_t& a, const f16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // 32x32 f32 accumulator layout (for lane l, register r):
 //   column = l % 32, row = (r / 4) * 8 + (l / 32) * 4 + (r % 4)
 __device__ inline int acc_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }

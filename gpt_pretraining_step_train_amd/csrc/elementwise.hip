@@ -21,6 +21,10 @@ template <>
 __device__ inline float ld<float>(const float* p) { return *p; }
 template <>
 __device__ inline float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <>
+__device__ inline void st<f16_t>(f16_t* p, float v) { *p = (f16_t)v; }
+template <>
+__device__ inline float ld<f16_t>(const f16_t* p) { return (float)*p; }
 
 template <typename T>
 __device__ inline void st4(T* p, float4 v) {
@@ -1437,6 +1441,9 @@ void launch_ns_normalize(const float* src, const double* sumsq, int mat, float e
   if (at == ACT_BF16)
     hipLaunchKernelGGL(ns_normalize_kernel<bf16_t>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
                        (bf16_t*)xa, (bf16_t*)xlo);
+  else if (at == ACT_F16)
+    hipLaunchKernelGGL(ns_normalize_kernel<f16_t>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
+                       (f16_t*)xa, (f16_t*)xlo);
   else
     hipLaunchKernelGGL(ns_normalize_kernel<float>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
                        (float*)xa, (float*)nullptr);

@@ -14,6 +14,8 @@
 // (dY^T X) products and the Newton-Schulz products.
 //
 // fp32 path: a plain LDS-tiled SIMT kernel (the all-fp32 configuration).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -127,8 +129,14 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
     if (p.outF) p.outF[bz * p.strideO + (long)row * p.ldo + col] = v;
     if (p.outA) {
       const long o = bz * p.strideOA + (long)row * p.ldoa + col;
-      store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
-      if (p.outA_lo) store_act<OutT>(reinterpret_cast<OutT*>(p.outA_lo) + o, v - load_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o));
+      if (std::is_same<OutT, bf16_t>::value && p.dtype == ACT_F16) {
+        _Float16* q = reinterpret_cast<_Float16*>(p.outA) + o;
+        *q = (_Float16)v;
+        if (p.outA_lo) reinterpret_cast<_Float16*>(p.outA_lo)[o] = (_Float16)(v - (float)*q);
+      } else {
+        store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
+        if (p.outA_lo) store_act<OutT>(reinterpret_cast<OutT*>(p.outA_lo) + o, v - load_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o));
+      }
     }
   } else if (p.epi == EPI_RELU2) {
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
@@ -143,11 +151,24 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
 }
 
 // four consecutive columns (col % 4 == 0, col + 3 < N, every leading dimension a
-// multiple of 4): one vector load/store per operand instead of four scalar ones
-__device__ inline void st4_act(bf16_t* q, const float (&v)[4]) {
+// multiple of 4): one vector load/store per operand instead of four scalar ones.
+// 16-bit act outputs are bf16, or fp16 when h (GemmArgs::dtype == ACT_F16)
+__device__ inline void st4_act(bf16_t* q, const float (&v)[4], bool h = false) {
+  if (h) {
+    typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+    const f16x4v x = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<f16x4v*>(q) = x;
+    return;
+  }
   *reinterpret_cast<uint2*>(q) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
 }
-__device__ inline void ld4_act(const bf16_t* q, float (&v)[4]) {
+__device__ inline void ld4_act(const bf16_t* q, float (&v)[4], bool h = false) {
+  if (h) {
+    typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+    const f16x4v x = *reinterpret_cast<const f16x4v*>(q);
+    v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
+    return;
+  }
   const uint2 u = *reinterpret_cast<const uint2*>(q);
   v[0] = bf2f((bf16_t)(u.x & 0xffff)); v[1] = bf2f((bf16_t)(u.x >> 16));
   v[2] = bf2f((bf16_t)(u.y & 0xffff)); v[3] = bf2f((bf16_t)(u.y >> 16));
@@ -163,14 +184,15 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
     if (p.outF)
       *reinterpret_cast<float4*>(p.outF + bz * p.strideO + (long)row * p.ldo + col) = make_float4(v[0], v[1], v[2], v[3]);
     if (p.outA) {
+      const bool f16 = p.dtype == ACT_F16;
       const long o = bz * p.strideOA + (long)row * p.ldoa + col;
       bf16_t* q = reinterpret_cast<bf16_t*>(p.outA) + o;
-      st4_act(q, v);
+      st4_act(q, v, f16);
       if (p.outA_lo) {
         float h[4], l[4];
-        ld4_act(q, h);
+        ld4_act(q, h, f16);
         _Pragma("unroll") for (int t = 0; t < 4; ++t) l[t] = v[t] - h[t];
-        st4_act(reinterpret_cast<bf16_t*>(p.outA_lo) + o, l);
+        st4_act(reinterpret_cast<bf16_t*>(p.outA_lo) + o, l, f16);
       }
     }
   } else if (p.epi == EPI_RELU2) {
@@ -403,7 +425,16 @@ struct DmaOperand {
   }
 };
 
-template <bool AK, bool BKM, bool SPLIT, int BK, int S>
+// one 32x32x16 MFMA on 16-bit operands held as raw bits: bf16, or fp16 when F16
+template <bool F16>
+__device__ inline f32x16_t mma16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  if constexpr (F16)
+    return mfma32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c);
+  else
+    return mfma32x32x16_bf16(a, b, c);
+}
+
+template <bool AK, bool BKM, bool SPLIT, int BK, int S, bool F16 = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_dma_kernel(GemmArgs p) {
   constexpr int WN = 4, TM = 128, TN = 64, FM = TM / 32, FN = TN / 32, NKK = BK / 16;
@@ -575,7 +606,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bf[c][j], acc[i][j]);
+            for (int j = 0; j < FN; ++j) acc[i][j] = mma16<F16>(af[c][i], bf[c][j], acc[i][j]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -617,7 +648,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16_bf16(af[c][i], bf[c][j], acc[i][j]);
+          for (int j = 0; j < FN; ++j) acc[i][j] = mma16<F16>(af[c][i], bf[c][j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1002,6 +1033,20 @@ void launch_dma_s(const GemmArgs& p, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, true, SPLIT, BK, S>), grid, block, 0, st, p);
 }
 
+void launch_dma_f16(const GemmArgs& p, hipStream_t st) {
+  const int tM = (p.M + 255) / 256;
+  const int tiles = (p.sym && p.M == p.N) ? tM * (tM + 1) / 2 : tM * ((p.N + 255) / 256);
+  dim3 grid(tiles, p.batch), block(512);
+  if (p.a_kmaj && p.b_kmaj)
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, true, false, 32, 4, true>), grid, block, 0, st, p);
+  else if (p.a_kmaj && !p.b_kmaj)
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, false, false, 32, 4, true>), grid, block, 0, st, p);
+  else if (!p.a_kmaj && !p.b_kmaj)
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, false, false, 32, 4, true>), grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, true, false, 32, 4, true>), grid, block, 0, st, p);
+}
+
 template <int BK, int S>
 void launch_dma(const GemmArgs& p, hipStream_t st) {
   if (p.split)
@@ -1095,8 +1140,11 @@ const char* gemm_kernel_name(const GemmArgs& p) {
        "gemm_bf16x3_dma_kernel<256,256,TN>", "gemm_bf16x3_dma_kernel<256,256,TT>"},
       {"gemm_bf16x3_kernel<128,128,NT>", "gemm_bf16x3_kernel<128,128,NN>", "gemm_bf16x3_kernel<128,128,TN>",
        "gemm_bf16x3_kernel<128,128,TT>"}};
+  static const char* f16_names[4] = {"gemm_f16_dma_kernel<256,256,NT>", "gemm_f16_dma_kernel<256,256,NN>",
+                                     "gemm_f16_dma_kernel<256,256,TN>", "gemm_f16_dma_kernel<256,256,TT>"};
   if (p.fp8) return "gemm_fp8_dma_kernel<256,256,NT>";
   const int lay = p.a_kmaj ? (p.b_kmaj ? 0 : 1) : (p.b_kmaj ? 3 : 2);
+  if (p.dtype == ACT_F16) return f16_names[lay];
   const int t = p.dtype == ACT_F32 ? 0 : (pick_tile(p) == 2 ? 2 : 1);
   if (p.split && t) return split_names[t][lay];
   return names[t][lay];
@@ -1112,6 +1160,7 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if ((size_t)p.splits * p.batch * p.M * p.N * sizeof(float) > p.ws_bytes) return 1;
   }
   if (p.split && (p.dtype != ACT_BF16 || p.splits != 1 || !p.A_lo || !p.B_lo)) return 1;
+  if (p.dtype == ACT_F16 && (p.splits != 1 || p.epi != EPI_LINEAR)) return 1;
   if (p.fp8) {
     if (!p.a_kmaj || !p.b_kmaj || p.split || !p.dq_a || !p.dq_b) return 1;
     if (p.K % 16 || p.lda % 16 || p.ldb % 16) return 2;
@@ -1119,7 +1168,7 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
     hipLaunchKernelGGL((gemm_fp8_dma_kernel<64, 4>), dim3(tiles, p.batch * p.splits), dim3(512), 0, st, p);
   } else
-  if (p.dtype == ACT_BF16) {
+  if (p.dtype == ACT_BF16 || p.dtype == ACT_F16) {
     // buffer loads address each operand matrix with 32-bit byte offsets
     const long abytes = (long)(p.a_kmaj ? p.M : p.K) * p.lda * 2, bbytes = (long)(p.b_kmaj ? p.N : p.K) * p.ldb * 2;
     if (abytes >= (long)0xFFFFFFF0u || bbytes >= (long)0xFFFFFFF0u) return 2;
@@ -1128,7 +1177,9 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if (!p.a_kmaj && (p.M % 8 || p.lda % 8)) return 2;
     if (!p.b_kmaj && (p.N % 8 || p.ldb % 8)) return 2;
     if ((p.a_kmaj && p.lda % 8) || (p.b_kmaj && p.ldb % 8)) return 2;
-    if (pick_tile(p) == 2)
+    if (p.dtype == ACT_F16)  // every size on the 256x256 kernel (ragged tiles read zeros)
+      launch_dma_f16(p, st);
+    else if (pick_tile(p) == 2)
       launch_bf16<128, 128, 2, 2>(p, st);
     else if (p.tile == 4)
       launch_bf16<256, 256, 2, 2>(p, st);

@@ -234,7 +234,7 @@ struct gpt_model {
 namespace {
 
 int run_gemm(gpt_model* M, GemmArgs p, hipStream_t st, bool allow_split) {
-  p.dtype = M->at;
+  if (p.dtype != ACT_F16) p.dtype = M->at;  // fp16 is chosen per product (Newton-Schulz)
   if (allow_split) {
     p.splits = gemm_auto_splits(p);
     p.ws = M->at_off<float>(M->off.splitws);
@@ -316,7 +316,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->norm_eps = 1e-6f;
   out->muon_momentum = 0.95f;
   out->ns_steps = 5;
-  out->ns_split_steps = 4;
+  out->ns_split_steps = 0;
   out->fp8_gemms = GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD;
   out->attn_window = 0;
   out->n_kv_head = 0;
@@ -843,13 +843,16 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   float* xf = M->at_off<float>(O.xf);
   char* xa[2] = {M->base + O.xa0, M->base + O.xa1};
   char* xl[2] = {M->base + O.xl0, M->base + O.xl1};
-  // the leading iterations multiply A A and B X with operands carried as bf16 hi + lo
-  // planes (three MFMA products each): rounding errors of the early iterations are
-  // amplified by the later ones along small singular directions, those of the last are
-  // not.  The Gram product X X^T stays plain bf16 in every iteration (its rounding
-  // costs far less accuracy than that of the other two; its fp32 result still feeds
-  // the split A A as hi + lo planes)
+  // 16-bit precisions: by default every product takes fp16 operands (11 significant
+  // bits, the bf16 MFMA rate; X, A and B stay well inside fp16's range), with X carried
+  // in fp32 for the a X term.  With ns_split_steps > 0 the products run on bf16 MFMA
+  // instead, and the leading iterations multiply A A and B X with operands carried as
+  // bf16 hi + lo planes (three MFMA products each): rounding errors of the early
+  // iterations are amplified by the later ones along small singular directions, those
+  // of the last are not.  The Gram product X X^T then stays plain bf16 in every
+  // iteration (its fp32 result still feeds the split A A as hi + lo planes)
   const int nsplit = M->at == ACT_BF16 ? std::min(c.ns_split_steps, c.ns_steps) : 0;
+  const int nat = M->at == ACT_BF16 && c.ns_split_steps == 0 ? ACT_F16 : M->at;  // NS operand type
   const size_t es = M->es;
   launch_momentum(mom, M->blk(M->grads()), c.muon_momentum, M->nBlk, st);
   launch_matrix_sumsq(mom, M->at_off<long>(O.mat_off), M->at_off<long>(O.mat_size), 6 * L,
@@ -874,7 +877,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       const int rows = mrows(j), cols = j == 5 ? F : d;
       const size_t dst = xdst(l, j);
       launch_ns_normalize(mom + M->moff[6 * l + j], M->at_off<double>(O.ss), 6 * l + j, 1e-7f, rows, cols,
-                          transposed(j), xf + dst, xa[0] + dst * es, nsplit > 0 ? xl[0] + dst * es : nullptr, M->at,
+                          transposed(j), xf + dst, xa[0] + dst * es, nsplit > 0 ? xl[0] + dst * es : nullptr, nat,
                           st);
     }
   struct Batch { int s, l, nb; size_t off; };
@@ -900,6 +903,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       {
         GemmArgs p;  // A = X X^T
         p.sym = true;
+        p.dtype = nat;
         p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
         p.A = xh; p.lda = bt.l; p.strideA = sl;
         p.B = xh; p.ldb = bt.l; p.strideB = sl;
@@ -911,6 +915,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       {
         GemmArgs p;  // Bm = b A + c A A   (A symmetric)
         p.sym = true;
+        p.dtype = nat;
         p.split = sp; p.A_lo = Alo; p.B_lo = Alo;
         p.M = bt.s; p.N = bt.s; p.K = bt.s; p.batch = bt.nb;
         p.A = Aa; p.lda = bt.s; p.strideA = ss;
@@ -922,6 +927,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       }
       {
         GemmArgs p;  // X <- a X + Bm X   (fp32 X read and written by the same thread)
+        p.dtype = nat;
         p.split = sp; p.A_lo = Blo; p.B_lo = xlo;
         p.M = bt.s; p.N = bt.l; p.K = bt.s; p.batch = bt.nb;
         p.A = Ba; p.lda = bt.s; p.strideA = ss;

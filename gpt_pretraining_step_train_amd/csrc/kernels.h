@@ -3,7 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+// ACT_F16 (fp16 operands and act outputs) is used by the Newton-Schulz products only
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1, ACT_F16 = 2 };
 
 enum GemmEpi {
   EPI_LINEAR = 0,  // v = alpha*acc + beta*Cin -> outF (fp32) and/or outA (act type)
@@ -19,7 +20,7 @@ struct GemmArgs {
   const void* A = nullptr; long lda = 0, strideA = 0;
   const void* B = nullptr; long ldb = 0, strideB = 0;
   bool a_kmaj = true, b_kmaj = true;
-  int dtype = ACT_BF16;           // operand type (and outA type)
+  int dtype = ACT_BF16;           // operand type (and outA type); ACT_F16: 256x256 kernel, no split
   int epi = EPI_LINEAR;
   float alpha = 1.f, beta = 0.f;
   const float* Cin = nullptr; long ldcin = 0, strideCin = 0;

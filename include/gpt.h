@@ -74,9 +74,11 @@ typedef struct gpt_cfg {
   int32_t ns_steps;   /* Newton-Schulz iterations, 0..5 */
   float ns_coeffs[5][3]; /* (a, b, c) per iteration */
   int64_t num_steps;  /* informational: steps at a tokens:params ratio of 8 with 2^20-token batches */
-  int32_t ns_split_steps; /* bf16 precision: the first ns_split_steps iterations form A A and
-                             B X from fp32 operands split into bf16 hi + lo parts (3 MFMA
-                             products; X X^T stays plain bf16); default 4 */
+  int32_t ns_split_steps; /* 16-bit precisions: 0 (the default) runs every Newton-Schulz
+                             product on fp16 operands (fp32 accumulate, X carried in fp32);
+                             n > 0 runs them on bf16 operands instead, the first n
+                             iterations forming A A and B X from fp32 operands split into
+                             bf16 hi + lo parts (3 MFMA products; X X^T stays plain bf16) */
   int32_t fp8_gemms;  /* precision GPT_FP8: which Linear GEMMs take per-tensor scaled e4m3
                          operands, a mask of GPT_FP8_FWD (Y = X W^T), GPT_FP8_WGRAD
                          (dW = dY^T X) and GPT_FP8_DGRAD (dX = dY W); default all three.

@@ -63,7 +63,7 @@ def test_default_ns_table(lib):
     c.attn_window, c.n_kv_head, c.extras = 7, 3, 5  # overwritten with the defaults
     lib.gpt_cfg_from_depth(24, ctypes.byref(c))
     tab = c.coeffs()
-    assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 4 and c.fp8_gemms == 7
+    assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 0 and c.fp8_gemms == 7
     assert c.attn_window == 0 and c.n_kv_head == 0 and c.extras == 0
     assert ctypes.sizeof(binding.GptCfg) == lib.gpt_cfg_bytes() == 152
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)

@@ -53,6 +53,7 @@ def _dev(a):
 # With the forward and weight gradient both in e4m3 (the default 7), the weight
 # gradient reuses the forward's codes of its input; with 6 it quantises them itself.
 # n_kv_head < n_head: grouped-query attention (Wk, Wv of n_kv_head * head_dim rows).
+# ns_split_steps > 0: Newton-Schulz on bf16 operands with hi/lo splits instead of fp16.
 STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8", {"precision": "fp8"}),
               ("laptop_fp8_bwd", {"precision": "fp8", "fp8_gemms": 6}),
               ("laptop_fp8_fwd", {"precision": "fp8", "fp8_gemms": 1}),
@@ -64,6 +65,7 @@ STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8"
               ("laptop_resid", {"extras": 1}), ("laptop_smear", {"extras": 2}), ("laptop_backout", {"extras": 4}),
               ("laptop_extras_fp8", {"precision": "fp8", "extras": 7}),
               ("d12_extras", {"batch": 1, "extras": 7, "n_kv_head": 2}),
+              ("laptop_nssplit", {"ns_split_steps": 4}), ("d12_nssplit", {"batch": 1, "ns_split_steps": 4}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
