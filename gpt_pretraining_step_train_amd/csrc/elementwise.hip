@@ -33,6 +33,12 @@ __device__ inline void st4(T* p, float4 v) {
 template <>
 __device__ inline void st4<float>(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 template <>
+__device__ inline void st4<f16_t>(f16_t* p, float4 v) {
+  typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+  const f16x4v h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+  *reinterpret_cast<f16x4v*>(p) = h;
+}
+template <>
 __device__ inline void st4<bf16_t>(bf16_t* p, float4 v) {
   uint2 u = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
   *reinterpret_cast<uint2*>(p) = u;
@@ -886,17 +892,6 @@ __global__ void fill_normal_kernel(float* w, size_t n, uint64_t seed, uint64_t s
   }
 }
 
-__global__ void momentum_kernel(float* __restrict__ m, const float* __restrict__ g, float mu, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x, t = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  const size_t n4 = n / 4;
-  for (size_t i = t; i < n4; i += stride) {
-    float4 a = reinterpret_cast<float4*>(m)[i];
-    const float4 b = reinterpret_cast<const float4*>(g)[i];
-    a.x = mu * a.x + b.x; a.y = mu * a.y + b.y; a.z = mu * a.z + b.z; a.w = mu * a.w + b.w;
-    reinterpret_cast<float4*>(m)[i] = a;
-  }
-  for (size_t i = n4 * 4 + t; i < n; i += stride) m[i] = mu * m[i] + g[i];
-}
 
 // AdamW on one flat fp32 tensor: m, v moments; rbc1 = 1 / (1 - b1^t), rbc2 = 1 / (1 - b2^t);
 // the decay acts on the weight before the step; wa (optional) receives the new weight
@@ -937,19 +932,33 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ w, const
   }
 }
 
-__global__ void __launch_bounds__(256) sumsq_part_kernel(const float* __restrict__ x, const long* offs,
-                                                         const long* sizes, int parts, double* partial) {
+
+// heavy-ball momentum m = mu m + g on every block matrix, and the per-part sums of the
+// new m^2 (fp64) for the Frobenius norms, in one pass; matrices start at multiples of
+// 4 floats, each part covers whole float4s (the last part also the scalar tail)
+__global__ void __launch_bounds__(256) momentum_sumsq_kernel(float* __restrict__ m, const float* __restrict__ g,
+                                                             float mu, const long* offs, const long* sizes, int parts,
+                                                             double* partial) {
   __shared__ double sd[4];
   const int mat = blockIdx.y, part = blockIdx.x;
-  const float* p = x + offs[mat];
-  const long n = sizes[mat];
-  const long per = (n + parts - 1) / parts;
-  const long b = part * per, e = min(n, b + per);
+  float* mp = m + offs[mat];
+  const float* gp = g + offs[mat];
+  const long n = sizes[mat], n4 = n / 4;
+  const long per = (n4 + parts - 1) / parts;
+  const long b = part * per, e = min(n4, b + per);
   double s = 0.0;
   for (long i = b + threadIdx.x; i < e; i += 256) {
-    const double v = p[i];
-    s += v * v;
+    float4 a = reinterpret_cast<float4*>(mp)[i];
+    const float4 q = reinterpret_cast<const float4*>(gp)[i];
+    a.x = mu * a.x + q.x; a.y = mu * a.y + q.y; a.z = mu * a.z + q.z; a.w = mu * a.w + q.w;
+    reinterpret_cast<float4*>(mp)[i] = a;
+    s += (double)a.x * a.x + (double)a.y * a.y + (double)a.z * a.z + (double)a.w * a.w;
   }
+  if (part == parts - 1)
+    for (long i = n4 * 4 + threadIdx.x; i < n; i += 256) {
+      mp[i] = mu * mp[i] + gp[i];
+      s += (double)mp[i] * mp[i];
+    }
   s = wave_sum_d(s);
   if ((threadIdx.x & 63) == 0) sd[threadIdx.x >> 6] = s;
   __syncthreads();
@@ -1003,6 +1012,38 @@ __global__ void __launch_bounds__(256) ns_normalize_kernel(const float* __restri
       xf[(long)c * rows + r] = v;
       st_hilo<T>(xa, xlo, (long)c * rows + r, v);
     }
+  }
+}
+
+// the same without a transpose, four consecutive elements per thread (n % 4 == 0)
+template <typename T>
+__global__ void __launch_bounds__(256) ns_normalize_vec_kernel(const float* __restrict__ src, const double* sumsq,
+                                                               int mat, float eps, long n4, float* __restrict__ xf,
+                                                               T* __restrict__ xa, T* __restrict__ xlo) {
+  const float scale = (float)(1.0 / (sqrt(sumsq[mat]) + (double)eps));
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    const float4 a = reinterpret_cast<const float4*>(src)[i];
+    const float4 v = make_float4(a.x * scale, a.y * scale, a.z * scale, a.w * scale);
+    reinterpret_cast<float4*>(xf)[i] = v;
+    st4<T>(xa + 4 * i, v);
+    if (xlo) {
+      const float4 h = make_float4(ld<T>(xa + 4 * i), ld<T>(xa + 4 * i + 1), ld<T>(xa + 4 * i + 2),
+                                   ld<T>(xa + 4 * i + 3));
+      st4<T>(xlo + 4 * i, make_float4(v.x - h.x, v.y - h.y, v.z - h.z, v.w - h.w));
+    }
+  }
+}
+
+// W -= lr * X without a transpose, four consecutive elements per thread
+template <typename T>
+__global__ void __launch_bounds__(256) muon_apply_vec_kernel(float* __restrict__ w, T* __restrict__ wa,
+                                                             const float* __restrict__ x, float lr, long n4) {
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    float4 a = reinterpret_cast<float4*>(w)[i];
+    const float4 q = reinterpret_cast<const float4*>(x)[i];
+    a.x -= lr * q.x; a.y -= lr * q.y; a.z -= lr * q.z; a.w -= lr * q.w;
+    reinterpret_cast<float4*>(w)[i] = a;
+    if (wa) st4<T>(wa + 4 * i, a);
   }
 }
 
@@ -1425,18 +1466,29 @@ void launch_fill_normal(float* w, size_t n, uint64_t seed, uint64_t sid, float s
   hipLaunchKernelGGL(fill_normal_kernel, dim3(grid_for(n)), dim3(256), 0, st, w, n, seed, sid, stddev);
 }
 
-void launch_momentum(float* m, const float* g, float mu, size_t n, hipStream_t st) {
-  hipLaunchKernelGGL(momentum_kernel, dim3(grid_for(n / 4 + 1)), dim3(256), 0, st, m, g, mu, n);
-}
 
-void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, int nmat, double* partial, int parts,
-                         double* out, hipStream_t st) {
-  hipLaunchKernelGGL(sumsq_part_kernel, dim3(parts, nmat), dim3(256), 0, st, x, offs, sizes, parts, partial);
+void launch_momentum_sumsq(float* m, const float* g, float mu, const long* offs, const long* sizes, int nmat,
+                           double* partial, int parts, double* out, hipStream_t st) {
+  hipLaunchKernelGGL(momentum_sumsq_kernel, dim3(parts, nmat), dim3(256), 0, st, m, g, mu, offs, sizes, parts,
+                     partial);
   hipLaunchKernelGGL(sumsq_final_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, partial, parts, nmat, out);
 }
 
+
 void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols, bool tr,
                          float* xf, void* xa, void* xlo, int at, hipStream_t st) {
+  const long n = (long)rows * cols;
+  if (!tr && n % 4 == 0 && at != ACT_F32) {
+    const long n4 = n / 4;
+    const dim3 gv((unsigned)std::min<long>((n4 + 255) / 256, 4096));
+    if (at == ACT_BF16)
+      hipLaunchKernelGGL(ns_normalize_vec_kernel<bf16_t>, gv, dim3(256), 0, st, src, sumsq, mat, eps, n4, xf,
+                         (bf16_t*)xa, (bf16_t*)xlo);
+    else
+      hipLaunchKernelGGL(ns_normalize_vec_kernel<f16_t>, gv, dim3(256), 0, st, src, sumsq, mat, eps, n4, xf,
+                         (f16_t*)xa, (f16_t*)xlo);
+    return;
+  }
   dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(ns_normalize_kernel<bf16_t>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
@@ -1451,6 +1503,16 @@ void launch_ns_normalize(const float* src, const double* sumsq, int mat, float e
 
 void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int rows, int cols, bool tr,
                        hipStream_t st) {
+  const long n = (long)rows * cols;
+  if (!tr && n % 4 == 0) {
+    const long n4 = n / 4;
+    const dim3 gv((unsigned)std::min<long>((n4 + 255) / 256, 4096));
+    if (at == ACT_BF16)
+      hipLaunchKernelGGL(muon_apply_vec_kernel<bf16_t>, gv, dim3(256), 0, st, w, (bf16_t*)wa, x, lr, n4);
+    else
+      hipLaunchKernelGGL(muon_apply_vec_kernel<float>, gv, dim3(256), 0, st, w, (float*)wa, x, lr, n4);
+    return;
+  }
   dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(muon_apply_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, rows, cols, (int)tr);

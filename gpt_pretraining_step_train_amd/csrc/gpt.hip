@@ -854,9 +854,11 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   const int nsplit = M->at == ACT_BF16 ? std::min(c.ns_split_steps, c.ns_steps) : 0;
   const int nat = M->at == ACT_BF16 && c.ns_split_steps == 0 ? ACT_F16 : M->at;  // NS operand type
   const size_t es = M->es;
-  launch_momentum(mom, M->blk(M->grads()), c.muon_momentum, M->nBlk, st);
-  launch_matrix_sumsq(mom, M->at_off<long>(O.mat_off), M->at_off<long>(O.mat_size), 6 * L,
-                      M->at_off<double>(O.ss_part), kSumsqParts, M->at_off<double>(O.ss), st);
+  // the matrix table covers the blocks region, so this is the momentum of every block
+  // matrix; offsets relative to the region (mom, and the gradients' blocks)
+  launch_momentum_sumsq(mom, M->blk(M->grads()), c.muon_momentum, M->at_off<long>(O.mat_off),
+                        M->at_off<long>(O.mat_size), 6 * L, M->at_off<double>(O.ss_part), kSumsqParts,
+                        M->at_off<double>(O.ss), st);
   // X0 into the NS workspace, every matrix in its wide orientation, one batch per
   // shape: the d x d squares (q, k, v, o of each layer; only q and o when grouped-query
   // attention makes Wk, Wv kv x d, which then form their own batch), then the d x F

@@ -106,14 +106,14 @@ void launch_fill_normal(float* w, size_t n, uint64_t seed, uint64_t stream_id, f
 void launch_zero(void* p, size_t bytes, hipStream_t st);
 
 // Muon pieces
-void launch_momentum(float* mom, const float* g, float mu, size_t n, hipStream_t st);
 // AdamW on n fp32 weights with fp32 moments (rbc1/rbc2: reciprocal bias corrections);
 // w_act (optional, act_type) receives the updated weights
 void launch_adamw(float* w, const float* g, float* m, float* v, void* w_act, int act_type, size_t n, float lr,
                   float b1, float b2, float eps, float wd, float rbc1, float rbc2, hipStream_t st);
-// per-matrix sum of squares of mom; matrix i occupies [offs[i], offs[i]+sizes[i])
-void launch_matrix_sumsq(const float* x, const long* offs, const long* sizes, int nmat, double* partial,
-                         int parts, double* out, hipStream_t st);
+// m = mu m + g on every listed matrix (matrix i occupies [offs[i], offs[i]+sizes[i]), offsets
+// multiples of 4) and the per-matrix sums of squares of the new m, in one pass
+void launch_momentum_sumsq(float* m, const float* g, float mu, const long* offs, const long* sizes, int nmat,
+                           double* partial, int parts, double* out, hipStream_t st);
 // X = src / (norm + eps) written (optionally transposed) into fp32 and act copies
 void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols,
                          bool transpose, float* xf, void* xa, void* xa_lo, int act_type, hipStream_t st);
