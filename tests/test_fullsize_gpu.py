@@ -12,6 +12,10 @@ configuration bench.py times), on outputs the oracle can compute one by one.
 
 fp8 (d26): the per-tensor e4m3 scales depend on the whole batch, so the sampled
 positions are compared with the unquantised oracle at the fp8 loss bar.
+
+The d24 variant with a sliding window (100 keys, so that it binds inside the sampled
+prefix), 4 key/value heads and all three extras stays causal (the smear only reads the
+previous position), so the same prefix argument holds.
 """
 import numpy as np
 import pytest
@@ -20,7 +24,7 @@ import torch
 from gpt_pretraining_step_train_amd import binding, configs, inputs
 from oracle import gpt_oracle as O
 from oracle import polar_express as PE
-from tests.gpu_util import rel_l2, say
+from tests.gpu_util import random_extras, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -36,11 +40,11 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def _full_step(name):
-    cfg = configs.get(name)
+def _full_step(name, **over):
+    cfg = configs.get(name, **over)
     assert (cfg["batch"], cfg["seq_len"]) == (16, 2048)
     model = binding.Model(cfg, seed=0)
-    params = inputs.init_weights(cfg, 0)
+    params = random_extras(inputs.init_weights(cfg, 0), cfg, 0)
     model.set_all_params(params)
     tok, tgt = inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=0)
     loss = model.step(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
@@ -97,6 +101,30 @@ def test_full_size_rows_and_muon(name):
         X, _ = O.muon_matrix(grads[i], np.zeros_like(grads[i]), table, mu=cfg["muon_momentum"])
         e = rel_l2(model.get_params(i).astype(np.float64) - before[i], -LR * X)
         say(f"  {name} tensor {i} {grads[i].shape}: Muon update rel L2 {e:.2e}")
+        assert e < 2e-2
+
+
+def test_full_size_window_gqa_extras():
+    over = dict(attn_window=100, n_kv_head=4, extras=7)
+    say("full-size step d24", over)
+    cfg, model, params, tok, tgt, loss, rows, am = _full_step("d24", **over)
+    for b in (0, 11):
+        ref, z = _prefix_rows(cfg, params, tok, tgt, b, "bf16")
+        e = rel_l2(rows[b, :PREFIX], ref)
+        frac_unique, match = _check_argmax(am[b, :PREFIX], z)
+        say(f"  seq {b}: first {PREFIX} row losses rel L2 {e:.2e}, argmax agreement {match:.3f} "
+            f"({frac_unique:.2f} of positions with a clear maximum, all equal)")
+        assert e < 2e-3
+    ids = [2, 1 + 6 * (cfg["depth"] - 1) + 4]  # layer 0 Wk (512 x 1536), last W1
+    grads = {i: model.grads(i) for i in ids}
+    before = {i: model.get_params(i) for i in ids}
+    model.muon_update(LR)
+    torch.cuda.synchronize()
+    table, _ = PE.coefficients()
+    for i in ids:
+        X, _ = O.muon_matrix(grads[i], np.zeros_like(grads[i]), table, mu=cfg["muon_momentum"])
+        e = rel_l2(model.get_params(i).astype(np.float64) - before[i], -LR * X)
+        say(f"  tensor {i} {grads[i].shape}: Muon update rel L2 {e:.2e}")
         assert e < 2e-2
 
 
