@@ -18,7 +18,9 @@ W2 [d,F]; id 1+6L is the LM head U [V,d].  When the cfg switches on any of the
 extras, id 2+6L is S [1, 2L+26]: L per-layer residual scales, L per-layer x0
 scales, the smear scale, the backout scale and the 24 smear-gate weights.  S
 starts as the identity (residual scales 1, everything else 0), where the
-extras leave the model unchanged.
+extras leave the model unchanged.  With value embeddings (extras bit 8) the
+ids 3+6L .. 2+7L are the per-layer tables VE_l [V, dkv] and id 3+7L is G
+[L*Hkv, 24], the gate weights (layer-major); both start at 0.
 """
 from __future__ import annotations
 
@@ -35,6 +37,9 @@ def tensor_shapes(cfg: dict) -> list[tuple[str, tuple[int, int]]]:
     out.append(("U", (V, d)))
     if cfg.get("extras"):
         out.append(("S", (1, 2 * L + 26)))
+    if cfg.get("extras", 0) & 8:
+        out += [(f"l{l}.VE", (V, dkv)) for l in range(L)]
+        out.append(("G", (L * int(cfg.get("n_kv_head") or cfg["n_head"]), 24)))
     return out
 
 
@@ -49,6 +54,9 @@ def init_weights(cfg: dict, seed: int = 0) -> list[np.ndarray]:
             w = np.zeros(shape, dtype=np.float32)
             w[0, :cfg["depth"]] = 1.0
             ws.append(w)
+            continue
+        if name == "G" or name.endswith(".VE"):
+            ws.append(np.zeros(shape, dtype=np.float32))
             continue
         s = std * (out_scale if name.endswith(".Wo") or name.endswith(".W2") else 1.0)
         w = rng.standard_normal(shape, dtype=np.float32)

@@ -56,6 +56,11 @@ translation).  Their parameters form one more tensor S at the end of the table
   embedding before smearing.
 * 4, backout: the final norm reads x_L - lb x_mid, x_mid the residual stream
   entering layer L // 2 (before that layer's residual scaling).
+* 8, value embeddings (the ResFormer snippet of the same section): every layer i
+  has its own table VE_i [V, Hkv hd] and gate weights Wg_i [Hkv, 24]; after the
+  QKV projection, v[t, h] += 3 sigmoid(Wg_i[h] . a[t, :24]) VE_i[token t, h], a the
+  attention block's normed input.  The tables follow S in the tensor table, then
+  one tensor G [L Hkv, 24] of the gate weights.
 """
 from __future__ import annotations
 
@@ -67,8 +72,9 @@ from oracle.e4m3 import quantise
 # configuration / parameter table
 
 
-EXTRA_RESID, EXTRA_SMEAR, EXTRA_BACKOUT = 1, 2, 4
+EXTRA_RESID, EXTRA_SMEAR, EXTRA_BACKOUT, EXTRA_VALUE_EMB = 1, 2, 4, 8
 SMEAR_CHANNELS = 24  # channels of the current position the smear gate reads
+VE_GATE_CHANNELS = 24  # channels of the block's normed input the value-embedding gate reads
 
 
 def extras_layout(L):
@@ -78,16 +84,22 @@ def extras_layout(L):
 
 
 def unpack(params, cfg):
-    """Split the flat tensor table [E, (Wq,Wk,Wv,Wo,W1,W2)*L, U(, S)] into parts;
-    S (flattened) is None when no extra is switched on."""
+    """Split the flat tensor table [E, (Wq,Wk,Wv,Wo,W1,W2)*L, U(, S)(, VE_0..VE_L-1, G)]
+    into (E, layers, U, S, VE, G); S (flattened) is None when no extra is switched on,
+    VE (a list) and G ([L, Hkv, 24]) are None without value embeddings."""
     L = cfg["depth"]
-    has_s = bool(cfg.get("extras", 0))
-    assert len(params) == 2 + 6 * L + has_s
+    ex = cfg.get("extras", 0)
+    has_s, has_ve = bool(ex), bool(ex & EXTRA_VALUE_EMB)
+    assert len(params) == 2 + 6 * L + has_s + (L + 1) * has_ve
     E = params[0]
     layers = [tuple(params[1 + 6 * l: 7 + 6 * l]) for l in range(L)]
     U = params[1 + 6 * L]
     S = np.asarray(params[2 + 6 * L], dtype=np.float64).reshape(-1) if has_s else None
-    return E, layers, U, S
+    VE = G = None
+    if has_ve:
+        VE = [np.asarray(w, dtype=np.float64) for w in params[3 + 6 * L: 3 + 7 * L]]
+        G = np.asarray(params[3 + 7 * L], dtype=np.float64).reshape(L, -1, VE_GATE_CHANNELS)
+    return E, layers, U, S, VE, G
 
 
 def sigmoid(x):
@@ -207,7 +219,7 @@ def forward(params, tokens, cfg, keep=True):
     """Forward pass.  Returns (logits [B,T,V], cache for backward)."""
     p = [np.asarray(w, dtype=np.float64) for w in params]
     qf, qfw = _fp8_quantisers(cfg)[0]
-    E, layers, U, S = unpack(p, cfg)
+    E, layers, U, S, VE, G = unpack(p, cfg)
     eps = cfg.get("norm_eps", 1e-6)
     H, hd = cfg["n_head"], cfg["head_dim"]
     Hkv = int(cfg.get("n_kv_head") or H)
@@ -239,6 +251,10 @@ def forward(params, tokens, cfg, keep=True):
         q = qkv[..., :d].reshape(B, T, H, hd)
         k = qkv[..., d:d + dkv].reshape(B, T, Hkv, hd)
         v = qkv[..., d + dkv:].reshape(B, T, Hkv, hd)
+        if ex & EXTRA_VALUE_EMB:                          # v += 3 sigmoid(gate) * VE[token]
+            ve = VE[li][tokens].reshape(B, T, Hkv, hd)
+            vg = 3.0 * sigmoid(a[..., :VE_GATE_CHANNELS] @ G[li].T)   # [B,T,Hkv]
+            v = v + vg[..., None] * ve
         qn, rq = rms_norm(rope(q, ang), eps)
         kn, rk = rms_norm(rope(k, ang), eps)
         # grouped-query attention: query head h uses key/value head h // (H / Hkv)
@@ -252,7 +268,9 @@ def forward(params, tokens, cfg, keep=True):
         h2 = h1 + qf(g) @ qfw(W2).T
         if keep:
             cache["layers"].append(dict(h=h, x_in=x_in, a=a, ra=ra, qn=qn, rq=rq, kn=kn, rk=rk,
-                                        v=v, o=o, h1=h1, m=m, rm=rm, u=u, g=g))
+                                        v=v, o=o, h1=h1, m=m, rm=rm, u=u, g=g,
+                                        ve=ve if ex & EXTRA_VALUE_EMB else None,
+                                        vg=vg if ex & EXTRA_VALUE_EMB else None))
         h = h2
     if ex & EXTRA_BACKOUT:
         h = h - S[X["lb"]] * cache["x_mid"]
@@ -282,7 +300,7 @@ def cross_entropy_grad(z, targets):
 def backward(z, targets, cache, cfg):
     """Exact gradient of the mean cross-entropy w.r.t. every tensor of the table."""
     p = cache["p"]
-    E, layers, U, S = unpack(p, cfg)
+    E, layers, U, S, VE, Gv = unpack(p, cfg)                # Gv: value-embedding gate weights
     ex = cfg.get("extras", 0)
     X = extras_layout(len(layers))
     Lb = len(layers) // 2
@@ -311,6 +329,8 @@ def backward(z, targets, cache, cfg):
         d_mid = -S[X["lb"]] * dh
         dS[X["lb"]] = -np.sum(dh * cache["x_mid"])
     dx0 = np.zeros_like(dh)                               # through the l0 terms
+    dVE = [np.zeros_like(t) for t in VE] if VE is not None else None
+    dG = np.zeros_like(Gv) if Gv is not None else None
 
     grads_layers = []
     for li, (Wq, Wk, Wv, Wo, W1, W2), c in zip(reversed(range(len(layers))), reversed(layers),
@@ -328,13 +348,20 @@ def backward(z, targets, cache, cfg):
         # a key/value head's gradient is the sum over the G query heads sharing it
         dkn = dkn.reshape(B, T, Hkv, G, hd).sum(axis=3)
         dv = dv.reshape(B, T, Hkv, G, hd).sum(axis=3)
+        da_ve = 0.0
+        if ex & EXTRA_VALUE_EMB:                          # v' = v + vg ve, vg = 3 sigmoid(z)
+            np.add.at(dVE[li], tokens.reshape(-1), (c["vg"][..., None] * dv).reshape(N, dkv))
+            dz = np.sum(dv * c["ve"], axis=-1) * c["vg"] * (1.0 - c["vg"] / 3.0)   # [B,T,Hkv]
+            dG[li] = np.einsum("bth,btc->hc", dz, c["a"][..., :VE_GATE_CHANNELS])
+            da_ve = np.zeros((B, T, d))
+            da_ve[..., :VE_GATE_CHANNELS] = dz @ Gv[li]
         dq = rope(rms_norm_bwd(dqn, c["qn"], c["rq"]), ang, inverse=True).reshape(B, T, d)
         dk = rope(rms_norm_bwd(dkn, c["kn"], c["rk"]), ang, inverse=True).reshape(B, T, dkv)
         dv = dv.reshape(B, T, dkv)
         # one Linear with weight [Wq; Wk; Wv]: dY = [dq | dk | dv]
         dWqkv, da = lin_bwd(np.concatenate([dq, dk, dv], axis=-1), c["a"], np.concatenate([Wq, Wk, Wv]))
         dWq, dWk, dWv = dWqkv[:d], dWqkv[d:d + dkv], dWqkv[d + dkv:]
-        dh = dh1 + rms_norm_bwd(da.reshape(B, T, d), c["a"], c["ra"])
+        dh = dh1 + rms_norm_bwd(da.reshape(B, T, d) + da_ve, c["a"], c["ra"])
         if ex & EXTRA_RESID:                              # layer input lr x_in + l0 x0
             dS[X["lr"][li]] = np.sum(dh * c["x_in"])
             dS[X["l0"][li]] = np.sum(dh * cache["x0"])
@@ -364,6 +391,9 @@ def backward(z, targets, cache, cfg):
     grads.append(dU)
     if dS is not None:
         grads.append(dS.reshape(np.shape(p[2 + 6 * len(layers)])))
+    if dVE is not None:
+        grads.extend(dVE)
+        grads.append(dG.reshape(np.shape(p[3 + 7 * len(layers)])))
     return grads
 
 

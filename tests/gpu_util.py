@@ -21,12 +21,17 @@ def from_dev(t) -> np.ndarray:
 
 
 def random_extras(params, cfg, seed):
-    """Move the extras tensor S (last in the table, when the cfg has extras) off its
-    start values (which leave the extras inert) by 0.3 N(0, 1) per entry, as
-    training would."""
+    """Move the extras' tensors off their start values (which leave the extras inert),
+    as training would: S and the value-embedding gate weights G by 0.3 N(0, 1) per
+    entry, the value-embedding tables to 0.5 N(0, 1) (the size of v's entries)."""
     if cfg.get("extras"):
+        from gpt_pretraining_step_train_amd import inputs
         rng = np.random.default_rng(seed + 1000)
-        params[-1] = (params[-1] + 0.3 * rng.standard_normal(params[-1].shape)).astype(np.float32)
+        for i, (name, shape) in enumerate(inputs.tensor_shapes(cfg)):
+            if name in ("S", "G"):
+                params[i] = (params[i] + 0.3 * rng.standard_normal(shape)).astype(np.float32)
+            elif name.endswith(".VE"):
+                params[i] = (0.5 * rng.standard_normal(shape)).astype(np.float32)
     return params
 
 

@@ -25,22 +25,29 @@ MICRO = dict(depth=1, d_model=16, n_head=2, head_dim=8, d_ff=64, vocab=64, seq_l
 MICRO2 = dict(MICRO, depth=2)
 MICRO_W = dict(MICRO2, attn_window=3)  # sliding window: each query sees 3 keys
 MICRO_G = dict(MICRO2, n_head=4, head_dim=4, n_kv_head=2)  # grouped-query attention, 2 heads per group
-# residual scaling + smear + backout; the smear gate reads 24 channels, so d = 32
-MICRO_X1 = dict(MICRO, d_model=32, head_dim=16, extras=7)   # one layer: backout reads x0
+# residual scaling + smear + backout + value embeddings; the gates read 24 channels,
+# so d = 32
+MICRO_X1 = dict(MICRO, d_model=32, head_dim=16, extras=15)  # one layer: backout reads x0
 MICRO_X = dict(MICRO_X1, depth=2)                           # backout reads layer 1's input
 TINY = dict(depth=2, d_model=128, n_head=4, head_dim=32, d_ff=512, vocab=4096, seq_len=128,
             batch=4, norm_eps=1e-6, rope_base=10000.0, init_std=0.02)
 
 
 def _params(cfg, seed=0, std=None, random_s=True):
-    """Weights of the tensor table; the extras tensor S (when present) gets random
-    values around 0.5 instead of its identity start, so that every extra acts."""
+    """Weights of the tensor table; the extras' tensors (when present) get random values
+    instead of their inert start (S and the gate weights around 0.5, the value-embedding
+    tables N(0, 0.5^2)), so that every extra acts."""
     c = dict(cfg)
     if std is not None:
         c["init_std"] = std
     ws = [w.astype(np.float64) for w in inputs.init_weights(c, seed)]
     if cfg.get("extras") and random_s:
-        ws[-1] = 0.5 + 0.3 * np.random.default_rng(seed + 1000).standard_normal(ws[-1].shape)
+        rng = np.random.default_rng(seed + 1000)
+        for i, (name, shape) in enumerate(inputs.tensor_shapes(cfg)):
+            if name in ("S", "G"):
+                ws[i] = 0.5 + 0.3 * rng.standard_normal(shape)
+            elif name.endswith(".VE"):
+                ws[i] = 0.5 * rng.standard_normal(shape)
     return ws
 
 
@@ -154,7 +161,7 @@ def test_initial_loss_statistics():
 # P4: causality
 
 
-@pytest.mark.parametrize("extras", [0, 7])
+@pytest.mark.parametrize("extras", [0, 15])
 def test_causality_exact(extras):
     """Changing token t+1 leaves every logit up to position t unchanged (with the
     extras: the smear mixes only the previous position into the current one)."""
@@ -455,8 +462,10 @@ def _torch_loss(params, tok, tgt, cfg):
     rms = lambda x: torch.nn.functional.rms_norm(x, (x.shape[-1],), eps=eps)
     ex = cfg.get("extras", 0)
     if ex:
-        E, U, S = params[0], params[-2], params[-1][0]
+        U, S = params[1 + 6 * L], params[2 + 6 * L][0]
         lam_r, lam_0, lam_s, lam_b, w_s = S[:L], S[L:2 * L], S[2 * L], S[2 * L + 1], S[2 * L + 2:]
+    if ex & 8:
+        ve_tabs, gates = params[3 + 6 * L: 3 + 7 * L], params[3 + 7 * L].view(L, H, 24)
     x = E[torch.from_numpy(tok).long()]
     if ex & 2:   # previous position's embedding, zero-padded at the start of each sequence
         shifted = torch.nn.functional.pad(x, (0, 0, 1, 0))[:, :-1]
@@ -472,6 +481,9 @@ def _torch_loss(params, tok, tgt, cfg):
         q = rms(rot((a @ Wq.T).view(B, T, H, hd)))
         k = rms(rot((a @ Wk.T).view(B, T, H, hd)))
         v = (a @ Wv.T).view(B, T, H, hd)
+        if ex & 8:  # torch.nn.functional.embedding lookup and a sigmoid gate per head
+            ve = torch.nn.functional.embedding(torch.from_numpy(tok).long(), ve_tabs[l]).view(B, T, H, hd)
+            v = v + (3 * torch.sigmoid(a[..., :24] @ gates[l].T)).unsqueeze(-1) * ve
         o = torch.nn.functional.scaled_dot_product_attention(
             q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), is_causal=True)
         x = x + o.transpose(1, 2).reshape(B, T, d) @ Wo.T
@@ -483,7 +495,7 @@ def _torch_loss(params, tok, tgt, cfg):
                                              torch.from_numpy(tgt).long().reshape(-1))
 
 
-@pytest.mark.parametrize("extras", [0, 7])
+@pytest.mark.parametrize("extras", [0, 15])
 def test_full_gradient_vs_torch_autograd(extras):
     cfg = dict(TINY, extras=extras)
     params = _params(cfg, seed=21, std=0.1)
@@ -524,12 +536,12 @@ def test_extras_at_their_start_values_are_the_plain_model():
     pb = _params(base, seed=3, std=0.4)
     tok, tgt = _tokens(base, seed=4)
     lb, gb, _, _ = O.loss_and_grads(pb, tok, tgt, base)
-    for ex in (1, 2, 4, 7):
+    for ex in (1, 2, 4, 7, 8, 15):
         cfg = dict(MICRO_X, extras=ex)
         p = _params(cfg, seed=3, std=0.4, random_s=False)
         l, g, _, _ = O.loss_and_grads(p, tok, tgt, cfg)
         assert l == lb
-        for x, y in zip(g[:-1], gb):
+        for x, y in zip(g, gb):  # the plain model's tensors lead the table
             np.testing.assert_array_equal(x, y)
 
 
@@ -567,6 +579,26 @@ def test_backout_subtracts_the_middle_stream(depth):
     x = cache["hL"] - mid
     r = x / np.sqrt(np.mean(x * x, -1, keepdims=True) + 1e-6)
     np.testing.assert_allclose(z, r @ p[-2].T, rtol=1e-12, atol=1e-14)
+
+
+def test_value_embedding_reproduces_the_first_layers_values():
+    """Layer 0 (no residual scaling, no smear) reads a = rms(E[token]), a function of the
+    token alone, so its values a Wv^T are a table lookup: with Wv = 0, gate weights 0
+    (gate 3 sigmoid(0) = 1.5) and VE_0 = rms(E) Wv^T / 1.5 (other layers' tables 0),
+    the value-embedding model computes the plain model's logits."""
+    base = dict(MICRO_X, extras=0)
+    cfg = dict(MICRO_X, extras=8)
+    p = _params(base, seed=11, std=0.4)
+    tok, tgt = _tokens(cfg, seed=12)
+    z, _ = O.forward(p, tok, base)
+    q = [w.copy() for w in _params(cfg, seed=11, std=0.4, random_s=False)]
+    E, Wv = p[0], p[3]
+    L = cfg["depth"]
+    r = E / np.sqrt(np.mean(E * E, -1, keepdims=True) + 1e-6)
+    q[3] = np.zeros_like(Wv)
+    q[3 + 6 * L] = (r @ Wv.T) / 1.5
+    z2, _ = O.forward(q, tok, cfg)
+    np.testing.assert_allclose(z2, z, rtol=1e-12, atol=1e-14)
 
 
 def test_smear_with_a_constant_gate_is_a_bigram_embedding():
