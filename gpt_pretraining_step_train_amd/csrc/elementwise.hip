@@ -402,6 +402,90 @@ __global__ void extras_init_kernel(float* S, int L, int n) {
 }
 
 // ---------------------------------------------------------------------------
+// Value embeddings: v[n, h] += 3 sigmoid(Wg[h] . a[n, 0:24]) VE[tok[n], h] for each key/
+// value head h, in place in the qkv rows [q (H hd) | k (Hkv hd) | v (Hkv hd)].  One wave
+// per (token, head); lanes 0..23 form the gate logit, every lane then owns hd/64 values.
+
+constexpr int VE_CH = 24;  // channels of the normed block input the gate reads
+
+template <typename T>
+__device__ inline float ve_gate_logit(const T* __restrict__ a_row, const float* __restrict__ wg_row, int lane) {
+  return wave_sum(lane < VE_CH ? ld<T>(a_row + lane) * wg_row[lane] : 0.f);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) ve_fwd_kernel(T* __restrict__ qkv, const T* __restrict__ a,
+                                                     const int32_t* __restrict__ tok, const float* __restrict__ ve,
+                                                     const float* __restrict__ wg, float* __restrict__ vg, int N,
+                                                     int V, int H, int Hkv, int hd, int d) {
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, head)
+  const int lane = threadIdx.x & 63;
+  if (w >= (long)N * Hkv) return;
+  const int n = (int)(w / Hkv), h = (int)(w % Hkv), t = tok[n];
+  const float g = 3.f * sigmoidf_(ve_gate_logit<T>(a + (long)n * d, wg + h * VE_CH, lane));
+  if (lane == 0) vg[w] = g;
+  if (t < 0 || t >= V) return;  // the gather flags the id; the step then fails
+  const float* er = ve + (long)t * Hkv * hd + (long)h * hd;
+  T* vr = qkv + (long)n * (H + 2 * Hkv) * hd + (long)(H + Hkv + h) * hd;
+  for (int j = lane; j < hd; j += 64) st<T>(vr + j, ld<T>(vr + j) + g * er[j]);
+}
+
+// backward, from dv = d loss / d v' (v' = v + g ve, g = 3 sigmoid(z)):
+//   dve[n, h] = g dv (rows for the table's scatter), dz[n, h] = (dv . ve) g (1 - g / 3),
+//   part[h * 24 + c][n] = dz a[n, c] (rows of the gate weights' gradient)
+template <typename T>
+__global__ void __launch_bounds__(256) ve_bwd_kernel(const T* __restrict__ dqkv, const T* __restrict__ a,
+                                                     const int32_t* __restrict__ tok, const float* __restrict__ ve,
+                                                     const float* __restrict__ vg, float* __restrict__ dve,
+                                                     float* __restrict__ dz, float* __restrict__ part, int N, int V,
+                                                     int H, int Hkv, int hd, int d) {
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= (long)N * Hkv) return;
+  const int n = (int)(w / Hkv), h = (int)(w % Hkv), t = tok[n];
+  const float g = vg[w];
+  const float* er = ve + (long)(t < 0 || t >= V ? 0 : t) * Hkv * hd + (long)h * hd;  // bad ids: flagged
+  const T* dr = dqkv + (long)n * (H + 2 * Hkv) * hd + (long)(H + Hkv + h) * hd;
+  float* out = dve + (long)n * Hkv * hd + (long)h * hd;
+  float dot = 0.f;
+  for (int j = lane; j < hd; j += 64) {
+    const float dv = ld<T>(dr + j);
+    out[j] = g * dv;
+    dot += dv * er[j];
+  }
+  const float z = wave_sum(dot) * g * (1.f - g / 3.f);
+  if (lane < VE_CH) part[(long)(h * VE_CH + lane) * N + n] = z * ld<T>(a + (long)n * d + lane);
+  if (lane == 0) dz[w] = z;
+}
+
+// da[n, c] += sum_h dz[n, h] Wg[h, c] for c < 24 (the gate's path into the block input)
+__global__ void __launch_bounds__(256) ve_da_kernel(float* __restrict__ da, const float* __restrict__ dz,
+                                                    const float* __restrict__ wg, int N, int Hkv, int d) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)N * VE_CH) return;
+  const int n = (int)(i / VE_CH), c = (int)(i % VE_CH);
+  float s = 0.f;
+  for (int h = 0; h < Hkv; ++h) s += dz[(long)n * Hkv + h] * wg[h * VE_CH + c];
+  da[(long)n * d + c] += s;
+}
+
+// out[j] (+)= sum over rows of part[j][row] in fixed order (fp64), one block per j
+__global__ void __launch_bounds__(256) rows_reduce_kernel(const float* __restrict__ part, int N,
+                                                          float* __restrict__ out, int accumulate) {
+  const int j = blockIdx.x;
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int n = threadIdx.x; n < N; n += 256) s += (double)part[(long)j * N + n];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[j] = (float)(accumulate ? (double)out[j] + red[0] : red[0]);
+}
+
+// ---------------------------------------------------------------------------
 // RoPE table: cs[t][i] = (cos, sin)(t * base^(-2i/hd)), angles in double precision
 
 __global__ void rope_table_kernel(float* cs, int T, int hd, float base) {
@@ -1388,6 +1472,38 @@ void launch_extras_reduce(const float* part, int N, int L, int mask, float* dS, 
 void launch_extras_init(float* S, int L, hipStream_t st) {
   const int n = 2 * L + 2 + SMEAR_CH;
   hipLaunchKernelGGL(extras_init_kernel, dim3((n + 255) / 256), dim3(256), 0, st, S, L, n);
+}
+
+void launch_ve_fwd(void* qkv, int at, const void* a, const int32_t* tok, const float* ve, const float* wg,
+                   float* vg, int N, int V, int H, int Hkv, int hd, int d, hipStream_t st) {
+  const dim3 g((unsigned)(((long)N * Hkv + 3) / 4)), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(ve_fwd_kernel<bf16_t>, g, b, 0, st, (bf16_t*)qkv, (const bf16_t*)a, tok, ve, wg, vg, N, V, H,
+                       Hkv, hd, d);
+  else
+    hipLaunchKernelGGL(ve_fwd_kernel<float>, g, b, 0, st, (float*)qkv, (const float*)a, tok, ve, wg, vg, N, V, H, Hkv,
+                       hd, d);
+}
+
+void launch_ve_bwd(const void* dqkv, int at, const void* a, const int32_t* tok, const float* ve, const float* vg,
+                   float* dve, float* dz, float* part, int N, int V, int H, int Hkv, int hd, int d,
+                   hipStream_t st) {
+  const dim3 g((unsigned)(((long)N * Hkv + 3) / 4)), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(ve_bwd_kernel<bf16_t>, g, b, 0, st, (const bf16_t*)dqkv, (const bf16_t*)a, tok, ve, vg, dve,
+                       dz, part, N, V, H, Hkv, hd, d);
+  else
+    hipLaunchKernelGGL(ve_bwd_kernel<float>, g, b, 0, st, (const float*)dqkv, (const float*)a, tok, ve, vg, dve, dz,
+                       part, N, V, H, Hkv, hd, d);
+}
+
+void launch_ve_da(float* da, const float* dz, const float* wg, int N, int Hkv, int d, hipStream_t st) {
+  hipLaunchKernelGGL(ve_da_kernel, dim3((unsigned)(((long)N * VE_CH + 255) / 256)), dim3(256), 0, st, da, dz, wg, N,
+                     Hkv, d);
+}
+
+void launch_rows_reduce(const float* part, int rows, int N, float* out, bool accumulate, hipStream_t st) {
+  if (rows > 0) hipLaunchKernelGGL(rows_reduce_kernel, dim3(rows), dim3(256), 0, st, part, N, out, (int)accumulate);
 }
 
 template <typename T>

@@ -52,6 +52,18 @@ inline int s_l0(const gpt_cfg& c, int l) { return c.depth + l; }
 inline int s_ls(const gpt_cfg& c) { return 2 * c.depth; }
 inline int s_lb(const gpt_cfg& c) { return 2 * c.depth + 1; }
 inline int s_ws(const gpt_cfg& c) { return 2 * c.depth + 2; }
+// S's region in the parameter vector, padded to whole float4s so that the value-embedding
+// tables (per layer [V][kv_dim], then the gate weights [L Hkv][24]) that follow are aligned
+constexpr int kVeCh = 24;
+inline size_t s_region(const gpt_cfg& c) { return (n_extras(c) + 3) / 4 * 4; }
+inline size_t n_ve(const gpt_cfg& c) {
+  return c.extras & GPT_EXTRA_VALUE_EMB ? (size_t)c.depth * c.vocab * kv_dim(c) : 0;
+}
+inline size_t n_vg(const gpt_cfg& c) {
+  return c.extras & GPT_EXTRA_VALUE_EMB ? (size_t)c.depth * kv_heads(c) * kVeCh : 0;
+}
+// parameters after U: S (padded), the value-embedding tables and their gate weights
+inline size_t n_tail(const gpt_cfg& c) { return s_region(c) + n_ve(c) + n_vg(c); }
 
 // element offsets of the six block matrices inside one layer's slice
 struct LayerOffs {
@@ -69,7 +81,7 @@ struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart;
+      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart;
   size_t splitws_bytes;
 };
 
@@ -105,12 +117,12 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   const size_t es = act_of(c) == ACT_BF16 ? 2 : 4;
   const size_t nE = V * d, nU = V * d, nBlk = L * layer_offs(c).stride;
   const size_t s = std::min(d, F), l = std::max(d, F);
-  const size_t nS = n_extras(c);
-  O.params = P.add((nE + nBlk + nU + nS) * 4);  // E, blocks, U, S
-  O.grads = P.add((nE + nBlk + nU + nS) * 4);
+  const size_t nS = n_extras(c), nT = n_tail(c);
+  O.params = P.add((nE + nBlk + nU + nT) * 4);  // E, blocks, U, S, value embeddings
+  O.grads = P.add((nE + nBlk + nU + nT) * 4);
   O.mom = P.add(nBlk * 4);
-  O.adam_m = P.add((nE + nU + nS) * 4);  // AdamW moments of E, U, then S
-  O.adam_v = P.add((nE + nU + nS) * 4);
+  O.adam_m = P.add((nE + nU + nT) * 4);  // AdamW moments of E, U, then the tail
+  O.adam_v = P.add((nE + nU + nT) * 4);
   // extras: mixed layer inputs, the final norm's input, the raw embedding, the gradient
   // sums flowing to x0 and x_mid, and the per-row terms of dS
   O.hx = c.extras & GPT_EXTRA_RESID ? P.add(L * N * d * 4) : 0;
@@ -119,6 +131,12 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.dmid = c.extras & GPT_EXTRA_BACKOUT ? P.add(N * d * 4) : 0;
   O.emb = c.extras & GPT_EXTRA_SMEAR ? P.add(N * d * 4) : 0;
   O.xpart = nS ? P.add(nS * N * 4) : 0;
+  // value embeddings: gate values per layer, and the backward's rows of dVE, dz and d(gate)
+  const bool ve = c.extras & GPT_EXTRA_VALUE_EMB;
+  O.vg = ve ? P.add(L * N * kv_heads(c) * 4) : 0;
+  O.dve = ve ? P.add(N * kv_dim(c) * 4) : 0;
+  O.vdz = ve ? P.add(N * kv_heads(c) * 4) : 0;
+  O.vpart = ve ? P.add((size_t)kv_heads(c) * kVeCh * N * 4) : 0;
   O.wact = es == 2 ? P.add(nBlk * es) : 0;
   O.uact = es == 2 ? P.add(nU * es) : 0;
   O.hs = P.add((2 * L + 1) * N * d * 4);
@@ -200,7 +218,7 @@ struct gpt_model {
   int at = ACT_BF16;
   size_t es = 2;
   int N = 0;
-  size_t nE = 0, nBlk = 0, nU = 0, nS = 0;
+  size_t nE = 0, nBlk = 0, nU = 0, nS = 0, nT = 0;  // nT: S (padded) and value embeddings
   LayerOffs lo;
   int last_status = GPT_OK;
   bool stepped = false;
@@ -283,6 +301,19 @@ bool tensor_loc(const gpt_cfg& c, int id, size_t* off, int* rows, int* cols) {
     *cols = (int)n_extras(c);
     return true;
   }
+  if ((c.extras & GPT_EXTRA_VALUE_EMB) && id >= (int)(3 + 6 * L) && id <= (int)(3 + 7 * L)) {
+    const size_t base = 2 * V * d + L * lo.stride + s_region(c);
+    if (id < (int)(3 + 7 * L)) {
+      *off = base + (size_t)(id - 3 - 6 * L) * V * kv_dim(c);
+      *rows = (int)V;
+      *cols = (int)kv_dim(c);
+    } else {
+      *off = base + n_ve(c);
+      *rows = (int)(L * kv_heads(c));
+      *cols = kVeCh;
+    }
+    return true;
+  }
   if (id < 1 || id > (int)(6 * L)) return false;
   const int l = (id - 1) / 6, j = (id - 1) % 6;
   const size_t b = V * d + l * lo.stride;
@@ -346,7 +377,7 @@ int gpt_cfg_validate(const gpt_cfg* c) {
   if (c->fp8_gemms & ~(GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD)) return GPT_ERR_ARG;
   if (c->attn_window < 0) return GPT_ERR_ARG;
   if (c->n_kv_head < 0 || c->n_kv_head > c->n_head || c->n_head % kv_heads(*c) != 0) return GPT_ERR_SHAPE;
-  if (c->extras & ~(GPT_EXTRA_RESID | GPT_EXTRA_SMEAR | GPT_EXTRA_BACKOUT)) return GPT_ERR_ARG;
+  if (c->extras & ~(GPT_EXTRA_RESID | GPT_EXTRA_SMEAR | GPT_EXTRA_BACKOUT | GPT_EXTRA_VALUE_EMB)) return GPT_ERR_ARG;
   if ((c->extras & GPT_EXTRA_SMEAR) && c->d_model < kSmearCh) return GPT_ERR_SHAPE;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
@@ -361,7 +392,10 @@ size_t gpt_state_bytes(const gpt_cfg* c) {
 
 size_t gpt_cfg_bytes(void) { return sizeof(gpt_cfg); }
 
-int gpt_tensor_count(const gpt_cfg* c) { return c ? 2 + 6 * c->depth + (c->extras ? 1 : 0) : 0; }
+int gpt_tensor_count(const gpt_cfg* c) {
+  if (!c) return 0;
+  return 2 + 6 * c->depth + (c->extras ? 1 : 0) + (c->extras & GPT_EXTRA_VALUE_EMB ? c->depth + 1 : 0);
+}
 
 int gpt_tensor_shape(const gpt_cfg* c, int32_t id, int32_t* rows, int32_t* cols) {
   if (!c || !rows || !cols) return GPT_ERR_ARG;
@@ -420,6 +454,7 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   M->nU = M->nE;
   M->nBlk = (size_t)cfg->depth * M->lo.stride;
   M->nS = n_extras(*cfg);
+  M->nT = n_tail(*cfg);
   const int L = cfg->depth, d = cfg->d_model, F = cfg->d_ff;
   for (int l = 0; l < L; ++l) {
     const size_t b = (size_t)l * M->lo.stride;
@@ -439,11 +474,14 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
     const float sd = cfg->init_std * ((j == 3 || j == 5) ? 1.f / sqrtf(2.f * L) : 1.f);
     launch_fill_normal(M->params() + off, (size_t)r * c, seed, (uint64_t)id, sd, st);
   }
-  if (M->nS) launch_extras_init(M->params() + M->nE + M->nBlk + M->nU, L, st);
+  if (M->nT) {  // S at the identity, value-embedding tables and gates at 0
+    launch_zero(M->params() + M->nE + M->nBlk + M->nU, M->nT * 4, st);
+    launch_extras_init(M->params() + M->nE + M->nBlk + M->nU, L, st);
+  }
   launch_zero(M->at_off<float>(O.mom), M->nBlk * 4, st);
-  launch_zero(M->at_off<float>(O.adam_m), (M->nE + M->nU + M->nS) * 4, st);
-  launch_zero(M->at_off<float>(O.adam_v), (M->nE + M->nU + M->nS) * 4, st);
-  launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU + M->nS) * 4, st);
+  launch_zero(M->at_off<float>(O.adam_m), (M->nE + M->nU + M->nT) * 4, st);
+  launch_zero(M->at_off<float>(O.adam_v), (M->nE + M->nU + M->nT) * 4, st);
+  launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU + M->nT) * 4, st);
   refresh_act(M, st);
   launch_rope_table(M->at_off<float>(O.rope), cfg->seq_len, cfg->head_dim, cfg->rope_base, st);
   if (hipMemcpyAsync(M->at_off<long>(O.mat_off), M->moff.data(), M->moff.size() * 8, hipMemcpyHostToDevice, st) !=
@@ -602,7 +640,12 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   int rc;
   // extras: S on the device, and the buffers they need
   const bool ex_resid = c.extras & GPT_EXTRA_RESID, ex_smear = c.extras & GPT_EXTRA_SMEAR,
-             ex_back = c.extras & GPT_EXTRA_BACKOUT;
+             ex_back = c.extras & GPT_EXTRA_BACKOUT, ex_ve = c.extras & GPT_EXTRA_VALUE_EMB;
+  // value embeddings: layer l's table and gate weights (parameters) and gate values
+  const size_t ve_base = M->nE + M->nBlk + M->nU + s_region(c), kvd = kv_dim(c);
+  auto ve_tab = [&](float* region, int l) { return region + ve_base + (size_t)l * V * kvd; };
+  auto ve_gate = [&](float* region, int l) { return region + ve_base + n_ve(c) + (size_t)l * Hkv * kVeCh; };
+  auto ve_g = [&](int l) { return M->at_off<float>(O.vg) + (size_t)l * N * Hkv; };
   const float* S = M->params() + M->nE + M->nBlk + M->nU;
   const int Lb = L / 2;  // backout reads the stream entering this layer
   float* xpart = M->at_off<float>(O.xpart);  // [2L+26][N] per-row terms of dS
@@ -644,6 +687,9 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       p.outA = qkv; p.ldoa = QD;
       if ((rc = lin_fwd(M, p, 4 * l + 0, st))) return rc;
     }
+    if (ex_ve)  // v += 3 sigmoid(gate) VE[token]
+      launch_ve_fwd(qkv, at, a, tok, ve_tab(M->params(), l), ve_gate(M->params(), l), ve_g(l), N, V, H, Hkv, hd, d,
+                    st);
     launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, eps, st);
     launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st);
     {
@@ -745,12 +791,21 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st))) return rc;
     }
     launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, Hkv, hd, c.attn_window, st);
+    if (ex_ve)  // dVE rows, the gate's dz and the rows of d(gate weights), from dv
+      launch_ve_bwd(dqkv, at, a, tok, ve_tab(M->params(), l), ve_g(l), M->at_off<float>(O.dve),
+                    M->at_off<float>(O.vdz), M->at_off<float>(O.vpart), N, V, H, Hkv, hd, d, st);
     launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, st);
     {
       GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
       pd.M = N; pd.N = d; pd.K = QD;
       pd.outF = dtmp; pd.ldo = d;
       if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
+    }
+    if (ex_ve) {  // the gate's path into the block input; the table's and gates' gradients
+      launch_ve_da(dtmp, M->at_off<float>(O.vdz), ve_gate(M->params(), l), N, Hkv, d, st);
+      launch_embed_scatter(tok, M->at_off<float>(O.dve), ve_tab(grads, l), N, V, (int)kvd, M->base + O.embws, nullptr,
+                           st, M->acc_grads);
+      launch_rows_reduce(M->at_off<float>(O.vpart), Hkv * kVeCh, N, ve_gate(grads, l), M->acc_grads, st);
     }
     if (ex_resid || (ex_back && l == Lb)) {
       // g = d loss / d (layer input); the stream reaching the layer gets lr g (plus the
@@ -825,9 +880,9 @@ int adamw_update(gpt_model* M, float lr, float beta1, float beta2, float eps, fl
                st);
   launch_adamw(M->params() + uo, M->grads() + uo, m + M->nE, v + M->nE, M->at == ACT_BF16 ? M->uact() : nullptr, M->at,
                M->nU, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2, st);
-  if (M->nS)  // the extras' scalars follow U in every table
+  if (M->nT)  // the extras' scalars and value embeddings follow U in every table
     launch_adamw(M->params() + uo + M->nU, M->grads() + uo + M->nU, m + M->nE + M->nU, v + M->nE + M->nU, nullptr,
-                 ACT_F32, M->nS, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2, st);
+                 ACT_F32, M->nT, lr, beta1, beta2, eps, weight_decay, rbc1, rbc2, st);
   M->wq_dirty = true;  // the e4m3 copies of U follow the master weights
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
@@ -1001,7 +1056,7 @@ int gpt_set_params(gpt_model* M, int32_t id, const float* h, size_t n, void* s) 
     tensor_loc(M->cfg, id, &off, &r, &c);
     if (id == 1 + 6 * M->cfg.depth)
       launch_cast_f32_to_act(M->params() + off, M->uact(), M->at, n, st);
-    else if (id != 0 && id != 2 + 6 * M->cfg.depth)  // E and S have no act copies
+    else if (id >= 1 && id <= 6 * M->cfg.depth)  // only the block matrices have act copies
       launch_cast_f32_to_act(M->params() + off, M->wact(off - M->nE), M->at, n, st);
   }
   return hipStreamSynchronize(st) == hipSuccess ? GPT_OK : GPT_ERR_HIP;

@@ -84,6 +84,18 @@ void launch_smear_bwd(const float* dx, const float* e, const float* pls, const f
 // dS[j] (+)= sum_n part[j][n] for j < 2L + 26 (entries of extras not in mask: 0)
 void launch_extras_reduce(const float* part, int N, int L, int mask, float* dS, bool accumulate, hipStream_t st);
 void launch_extras_init(float* S, int L, hipStream_t st);
+// value embeddings (qkv rows [q | k | v] as for the attention launchers; a is the block's
+// normed input [N][d]; ve the layer's table [V][Hkv hd]; wg its gate weights [Hkv][24]):
+// v += 3 sigmoid(wg . a[:24]) ve[tok] per head, the gate values to vg [N][Hkv]
+void launch_ve_fwd(void* qkv, int at, const void* a, const int32_t* tok, const float* ve, const float* wg,
+                   float* vg, int N, int V, int H, int Hkv, int hd, int d, hipStream_t st);
+// dve [N][Hkv hd] = g dv, dz [N][Hkv], part [Hkv*24][N] (rows of d wg) from dqkv's v part
+void launch_ve_bwd(const void* dqkv, int at, const void* a, const int32_t* tok, const float* ve, const float* vg,
+                   float* dve, float* dz, float* part, int N, int V, int H, int Hkv, int hd, int d, hipStream_t st);
+// da[:, :24] += dz wg
+void launch_ve_da(float* da, const float* dz, const float* wg, int N, int Hkv, int d, hipStream_t st);
+// out[j] (+)= sum_n part[j][n], fixed order, j < rows
+void launch_rows_reduce(const float* part, int rows, int N, float* out, bool accumulate, hipStream_t st);
 void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st);
 // qkv rows are [H q heads | Hkv k heads | Hkv v heads] x hd; rstd_q is [B*T][H], rstd_k [B*T][Hkv]
 void launch_rope_qknorm_fwd(void* qkv, int act_type, const float* cs, float* rstd_q, float* rstd_k,

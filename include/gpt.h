@@ -21,7 +21,9 @@
  *    (dkv = n_kv_head * head_dim); id 1+6L = U [V][d] (LM head).  With any
  *    extras switched on, id 2+6L = S [1][2L+26]: the L residual scales, the L x0
  *    scales, the smear scale, the backout scale and the 24 smear-gate weights.
- *    Count = 2 + 6L (+1 with extras).
+ *    With value embeddings, ids 3+6L .. 2+7L = VE_l [V][dkv] (one table per
+ *    layer) and id 3+7L = G [L*Hkv][24] (gate weights, layer-major).
+ *    Count = 2 + 6L (+1 with extras, +L+1 with value embeddings).
  *  - Ownership: the caller owns the arena, the token buffers and the stream and
  *    keeps them alive until the stream's work completes.  The library never
  *    allocates device memory; gpt_free releases host bookkeeping only.
@@ -97,13 +99,17 @@ typedef struct gpt_cfg {
                          GPT_EXTRA_SMEAR: after the embedding, x[t] += ls sigmoid(ws .
                            x[t, 0:24]) x[t-1] within each sequence (d >= 24);
                          GPT_EXTRA_BACKOUT: the final norm reads x_L - lb x_mid, x_mid the
-                           stream entering layer L/2.
-                         S starts at the identity (lr = 1, the rest 0); AdamW updates it.
+                           stream entering layer L/2;
+                         GPT_EXTRA_VALUE_EMB: after the QKV projection of layer i, v[t, h] +=
+                           3 sigmoid(Wg_i[h] . a[t, 0:24]) VE_i[token t, h], a the block's
+                           normed input (tensors VE_i and G).
+                         S starts at the identity (lr = 1, the rest 0), VE and G at 0; AdamW
+                         updates all of them.
                          0 (the default) = none; other bits: GPT_ERR_ARG */
 } gpt_cfg;
 
 enum { GPT_FP8_FWD = 1, GPT_FP8_WGRAD = 2, GPT_FP8_DGRAD = 4 };
-enum { GPT_EXTRA_RESID = 1, GPT_EXTRA_SMEAR = 2, GPT_EXTRA_BACKOUT = 4 };
+enum { GPT_EXTRA_RESID = 1, GPT_EXTRA_SMEAR = 2, GPT_EXTRA_BACKOUT = 4, GPT_EXTRA_VALUE_EMB = 8 };
 
 typedef struct gpt_model gpt_model; /* opaque */
 
@@ -155,7 +161,8 @@ int gpt_grads(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* str
  * E and U are not touched.  Stream-ordered, no synchronisation. */
 int muon_update(gpt_model* m, float lr, void* stream);
 
-/* AdamW on the token embedding E, the LM head U and the extras' scalars S (the
+/* AdamW on the token embedding E, the LM head U, the extras' scalars S and the
+ * value-embedding tables and gate weights (the
  * tensors Muon leaves to it, per the parameter-type table of "2. Muon Optimize
  * Edici" in the nanochat articles; they print no formula or hyperparameters, so
  * Adam's bias-corrected moments with decoupled weight decay are used).  For the t-th call on this model,

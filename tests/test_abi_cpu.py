@@ -77,7 +77,7 @@ def test_validation_errors(lib):
     for field, val, code in [("head_dim", 48, 6), ("n_head", 5, 2), ("d_model", 2056, 2), ("precision", 7, 6),
                              ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2), ("fp8_gemms", 8, 1),
                              ("attn_window", -1, 1), ("n_kv_head", 2, 2), ("n_kv_head", 4, 2),
-                             ("n_kv_head", -1, 2), ("extras", 8, 1), ("extras", -1, 1)]:
+                             ("n_kv_head", -1, 2), ("extras", 16, 1), ("extras", -1, 1)]:
         c = binding.make_cfg(configs.get("laptop"))
         setattr(c, field, val)
         assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, field
@@ -89,7 +89,9 @@ def test_validation_errors(lib):
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {}), ("d12", {}), ("d24", {}),
                                        ("tiny", {"n_kv_head": 2}), ("laptop", {"n_kv_head": 1}),
                                        ("d24", {"n_kv_head": 4}), ("tiny", {"extras": 7}),
-                                       ("laptop", {"extras": 2}), ("d24", {"extras": 7, "n_kv_head": 4})])
+                                       ("laptop", {"extras": 2}), ("d24", {"extras": 7, "n_kv_head": 4}),
+                                       ("tiny", {"extras": 15}), ("laptop", {"extras": 8, "n_kv_head": 1}),
+                                       ("d24", {"extras": 15, "n_kv_head": 4})])
 def test_state_bytes_and_tensor_table(lib, name, over):
     for cfg in [configs.get(name, **over)]:
         c = binding.make_cfg(cfg)
@@ -97,7 +99,8 @@ def test_state_bytes_and_tensor_table(lib, name, over):
         n = configs.n_params(cfg)
         assert nb > 3 * 4 * n                     # params + grads + momentum at least
         assert nb < 288 * 2 ** 30                # fits one MI355X
-        assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"] + (1 if cfg.get("extras") else 0)
+        ex = cfg.get("extras", 0)
+        assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"] + (ex > 0) + (cfg["depth"] + 1) * (ex >= 8)
         shapes = inputs.tensor_shapes(cfg)
         assert n == sum(r * k for _, (r, k) in shapes)
         for i, (nm, shp) in enumerate(shapes):

@@ -43,7 +43,7 @@ def _batch(cfg, seed):
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {"batch": 8}),
                                        ("laptop", {"batch": 8, "precision": "fp8"}),
-                                       ("laptop", {"batch": 8, "extras": 7})], ids=["fp32", "bf16", "fp8", "extras"])
+                                       ("laptop", {"batch": 8, "extras": 15})], ids=["fp32", "bf16", "fp8", "extras"])
 def test_grad_scale_is_exact(name, over):
     cfg, model, params = _model(name, **over)
     _, _, dt, dg = _batch(cfg, 3)
@@ -58,7 +58,7 @@ def test_grad_scale_is_exact(name, over):
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {"batch": 8}),
                                        ("laptop", {"batch": 8, "precision": "fp8"}),
-                                       ("laptop", {"batch": 8, "extras": 7})], ids=["fp32", "bf16", "fp8", "extras"])
+                                       ("laptop", {"batch": 8, "extras": 15})], ids=["fp32", "bf16", "fp8", "extras"])
 def test_accumulated_gradient_is_the_total_batch_gradient(name, over):
     cfg, model, params = _model(name, **over)
     n = 3

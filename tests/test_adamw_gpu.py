@@ -45,13 +45,15 @@ def _adamw_chain(w0, grads, hp):
     return w
 
 
-@pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {}), ("laptop", {"extras": 7})],
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {}), ("laptop", {"extras": 15})],
                          ids=["tiny", "laptop", "laptop_extras"])
 def test_adamw_matches_oracle(name, over):
     cfg, model, params = _model(name, **over)
     say("adamw parity", name, over)
     L = cfg["depth"]
-    ids = [0, 1 + 6 * L] + ([2 + 6 * L] if cfg.get("extras") else [])  # E, U (and the extras' S)
+    ids = [0, 1 + 6 * L]  # E, U, and the extras' S, a value-embedding table and the gate weights
+    if cfg.get("extras"):
+        ids += [2 + 6 * L, 3 + 6 * L, 3 + 7 * L]
     rng = np.random.default_rng(7)
     grads = {i: [] for i in ids}
     for step in range(3):

@@ -14,7 +14,7 @@ fp8 (d26): the per-tensor e4m3 scales depend on the whole batch, so the sampled
 positions are compared with the unquantised oracle at the fp8 loss bar.
 
 The d24 variant with a sliding window (100 keys, so that it binds inside the sampled
-prefix), 4 key/value heads and all three extras stays causal (the smear only reads the
+prefix), 4 key/value heads and all four extras stays causal (the smear only reads the
 previous position), so the same prefix argument holds.
 """
 import numpy as np
@@ -105,7 +105,7 @@ def test_full_size_rows_and_muon(name):
 
 
 def test_full_size_window_gqa_extras():
-    over = dict(attn_window=100, n_kv_head=4, extras=7)
+    over = dict(attn_window=100, n_kv_head=4, extras=15)
     say("full-size step d24", over)
     cfg, model, params, tok, tgt, loss, rows, am = _full_step("d24", **over)
     for b in (0, 11):

@@ -61,10 +61,11 @@ STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8"
               ("tiny_gqa", {"n_kv_head": 2}), ("laptop_mqa", {"n_kv_head": 1}),
               ("laptop_mqa_fp8", {"precision": "fp8", "n_kv_head": 1}),
               ("d12_gqa", {"batch": 1, "n_kv_head": 2}),
-              ("tiny_extras", {"extras": 7}), ("laptop_extras", {"extras": 7}),
+              ("tiny_extras", {"extras": 15}), ("laptop_extras", {"extras": 15}),
               ("laptop_resid", {"extras": 1}), ("laptop_smear", {"extras": 2}), ("laptop_backout", {"extras": 4}),
-              ("laptop_extras_fp8", {"precision": "fp8", "extras": 7}),
-              ("d12_extras", {"batch": 1, "extras": 7, "n_kv_head": 2}),
+              ("laptop_ve", {"extras": 8}), ("laptop_ve_mqa", {"extras": 8, "n_kv_head": 1}),
+              ("laptop_extras_fp8", {"precision": "fp8", "extras": 15}),
+              ("d12_extras", {"batch": 1, "extras": 15, "n_kv_head": 2}),
               ("laptop_nssplit", {"ns_split_steps": 4}), ("d12_nssplit", {"batch": 1, "ns_split_steps": 4}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
