@@ -404,7 +404,8 @@ __global__ void extras_init_kernel(float* S, int L, int n) {
 // ---------------------------------------------------------------------------
 // Value embeddings: v[n, h] += 3 sigmoid(Wg[h] . a[n, 0:24]) VE[tok[n], h] for each key/
 // value head h, in place in the qkv rows [q (H hd) | k (Hkv hd) | v (Hkv hd)].  One wave
-// per (token, head); lanes 0..23 form the gate logit, every lane then owns hd/64 values.
+// per (token, head); lanes 0..23 form the gate logit, then each lane owns pairs of
+// adjacent values (64 lanes cover 128 of them per pass).
 
 constexpr int VE_CH = 24;  // channels of the normed block input the gate reads
 
@@ -412,6 +413,23 @@ template <typename T>
 __device__ inline float ve_gate_logit(const T* __restrict__ a_row, const float* __restrict__ wg_row, int lane) {
   return wave_sum(lane < VE_CH ? ld<T>(a_row + lane) * wg_row[lane] : 0.f);
 }
+
+// two adjacent act-typed values (4- or 8-byte aligned pairs: hd and every row offset even)
+template <typename T>
+__device__ inline float2 ld2(const T* p);
+template <>
+__device__ inline float2 ld2<float>(const float* p) { return *reinterpret_cast<const float2*>(p); }
+template <>
+__device__ inline float2 ld2<bf16_t>(const bf16_t* p) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  return make_float2(bf2f((bf16_t)(u & 0xffffu)), bf2f((bf16_t)(u >> 16)));
+}
+template <typename T>
+__device__ inline void st2(T* p, float2 v);
+template <>
+__device__ inline void st2<float>(float* p, float2 v) { *reinterpret_cast<float2*>(p) = v; }
+template <>
+__device__ inline void st2<bf16_t>(bf16_t* p, float2 v) { *reinterpret_cast<uint32_t*>(p) = pack_bf2(v.x, v.y); }
 
 template <typename T>
 __global__ void __launch_bounds__(256) ve_fwd_kernel(T* __restrict__ qkv, const T* __restrict__ a,
@@ -427,12 +445,15 @@ __global__ void __launch_bounds__(256) ve_fwd_kernel(T* __restrict__ qkv, const 
   if (t < 0 || t >= V) return;  // the gather flags the id; the step then fails
   const float* er = ve + (long)t * Hkv * hd + (long)h * hd;
   T* vr = qkv + (long)n * (H + 2 * Hkv) * hd + (long)(H + Hkv + h) * hd;
-  for (int j = lane; j < hd; j += 64) st<T>(vr + j, ld<T>(vr + j) + g * er[j]);
+  for (int j = 2 * lane; j < hd; j += 128) {
+    const float2 v = ld2<T>(vr + j), e = *reinterpret_cast<const float2*>(er + j);
+    st2<T>(vr + j, make_float2(v.x + g * e.x, v.y + g * e.y));
+  }
 }
 
 // backward, from dv = d loss / d v' (v' = v + g ve, g = 3 sigmoid(z)):
 //   dve[n, h] = g dv (rows for the table's scatter), dz[n, h] = (dv . ve) g (1 - g / 3),
-//   part[h * 24 + c][n] = dz a[n, c] (rows of the gate weights' gradient)
+//   part[n][h * 24 + c] = dz a[n, c] (rows of the gate weights' gradient)
 template <typename T>
 __global__ void __launch_bounds__(256) ve_bwd_kernel(const T* __restrict__ dqkv, const T* __restrict__ a,
                                                      const int32_t* __restrict__ tok, const float* __restrict__ ve,
@@ -448,13 +469,13 @@ __global__ void __launch_bounds__(256) ve_bwd_kernel(const T* __restrict__ dqkv,
   const T* dr = dqkv + (long)n * (H + 2 * Hkv) * hd + (long)(H + Hkv + h) * hd;
   float* out = dve + (long)n * Hkv * hd + (long)h * hd;
   float dot = 0.f;
-  for (int j = lane; j < hd; j += 64) {
-    const float dv = ld<T>(dr + j);
-    out[j] = g * dv;
-    dot += dv * er[j];
+  for (int j = 2 * lane; j < hd; j += 128) {
+    const float2 dv = ld2<T>(dr + j), e = *reinterpret_cast<const float2*>(er + j);
+    *reinterpret_cast<float2*>(out + j) = make_float2(g * dv.x, g * dv.y);
+    dot += dv.x * e.x + dv.y * e.y;
   }
   const float z = wave_sum(dot) * g * (1.f - g / 3.f);
-  if (lane < VE_CH) part[(long)(h * VE_CH + lane) * N + n] = z * ld<T>(a + (long)n * d + lane);
+  if (lane < VE_CH) part[(long)n * Hkv * VE_CH + h * VE_CH + lane] = z * ld<T>(a + (long)n * d + lane);
   if (lane == 0) dz[w] = z;
 }
 
@@ -469,20 +490,30 @@ __global__ void __launch_bounds__(256) ve_da_kernel(float* __restrict__ da, cons
   da[(long)n * d + c] += s;
 }
 
-// out[j] (+)= sum over rows of part[j][row] in fixed order (fp64), one block per j
-__global__ void __launch_bounds__(256) rows_reduce_kernel(const float* __restrict__ part, int N,
-                                                          float* __restrict__ out, int accumulate) {
-  const int j = blockIdx.x;
-  __shared__ double red[256];
+// Column sums of part [N][R] in a fixed order (fp64): stage 1, block (column group of 64,
+// row chunk) -> chunk sums; stage 2, per column, the chunk sums in chunk order.
+constexpr int CS_CHUNKS = 256;
+__global__ void __launch_bounds__(256) colsum_chunk_kernel(const float* __restrict__ part, int N, int R,
+                                                           double* __restrict__ chunk) {
+  __shared__ double sm[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane, c = blockIdx.y;
+  const int per = (N + CS_CHUNKS - 1) / CS_CHUNKS, n0 = c * per, n1 = min(N, n0 + per);
   double s = 0.0;
-  for (int n = threadIdx.x; n < N; n += 256) s += (double)part[(long)j * N + n];
-  red[threadIdx.x] = s;
+  if (j < R)
+    for (int n = n0 + wave; n < n1; n += 4) s += (double)part[(long)n * R + j];
+  sm[wave][lane] = s;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) out[j] = (float)(accumulate ? (double)out[j] + red[0] : red[0]);
+  if (wave == 0 && j < R) chunk[(long)c * R + j] = (sm[0][lane] + sm[1][lane]) + (sm[2][lane] + sm[3][lane]);
+}
+
+__global__ void __launch_bounds__(256) colsum_final_kernel(const double* __restrict__ chunk, int R,
+                                                           float* __restrict__ out, int accumulate) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= R) return;
+  double s = 0.0;
+  for (int c = 0; c < CS_CHUNKS; ++c) s += chunk[(long)c * R + j];
+  out[j] = (float)(accumulate ? (double)out[j] + s : s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1502,8 +1533,13 @@ void launch_ve_da(float* da, const float* dz, const float* wg, int N, int Hkv, i
                      Hkv, d);
 }
 
-void launch_rows_reduce(const float* part, int rows, int N, float* out, bool accumulate, hipStream_t st) {
-  if (rows > 0) hipLaunchKernelGGL(rows_reduce_kernel, dim3(rows), dim3(256), 0, st, part, N, out, (int)accumulate);
+size_t colsum_ws_bytes(int R) { return (size_t)CS_CHUNKS * R * 8; }
+
+void launch_colsum(const float* part, int N, int R, void* ws, float* out, bool accumulate, hipStream_t st) {
+  if (R <= 0) return;
+  hipLaunchKernelGGL(colsum_chunk_kernel, dim3((R + 63) / 64, CS_CHUNKS), dim3(256), 0, st, part, N, R, (double*)ws);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((R + 255) / 256), dim3(256), 0, st, (const double*)ws, R, out,
+                     (int)accumulate);
 }
 
 template <typename T>
@@ -1542,28 +1578,47 @@ size_t embed_ws_bytes(int N, int V, int d) {
          al256((size_t)N * d * 4);
 }
 
-void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws,
-                          int32_t* sorted_out, hipStream_t st, bool accumulate) {
+// the sort of the token ids (counts per id, their offsets, positions grouped by id in
+// increasing order) in ws; launch_embed_scatter_sorted reuses it for any row width
+void launch_embed_sort(const int32_t* tok, int N, int V, void* ws, hipStream_t st) {
   const int P = (N + SC_CHUNK - 1) / SC_CHUNK;
   char* w = (char*)ws;
   int* table = (int*)w; w += al256((size_t)P * V * 4);
   int* counts = (int*)w; w += al256((size_t)V * 4);
   int* offsets = (int*)w; w += al256(((size_t)V + 1) * 4);
-  int* sorted = (int*)w; w += al256((size_t)N * 4);
-  float* partial = (float*)w;
-  if (sorted_out) sorted = sorted_out;
+  int* sorted = (int*)w;
   launch_zero(table, (size_t)P * V * 4, st);
   if (N > 0) hipLaunchKernelGGL(sc_hist_kernel, dim3(P), dim3(SC_CHUNK), 0, st, tok, N, V, table);
   hipLaunchKernelGGL(sc_colscan_kernel, dim3((V + 255) / 256), dim3(256), 0, st, table, P, V, counts);
   hipLaunchKernelGGL(sc_vscan_kernel, dim3(1), dim3(1024), 0, st, counts, V, offsets);
-  if (N > 0) {
-    hipLaunchKernelGGL(sc_fill_kernel, dim3(P), dim3(SC_CHUNK), 0, st, tok, N, V, table, offsets, sorted);
-    // every valid position has a slot; out-of-range ids were rejected by the gather
+  // every valid position gets a slot; out-of-range ids were flagged by the gather
+  if (N > 0) hipLaunchKernelGGL(sc_fill_kernel, dim3(P), dim3(SC_CHUNK), 0, st, tok, N, V, table, offsets, sorted);
+}
+
+void launch_embed_scatter_sorted(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws,
+                                 hipStream_t st, bool accumulate) {
+  const int P = (N + SC_CHUNK - 1) / SC_CHUNK;
+  char* w = (char*)ws;
+  w += al256((size_t)P * V * 4) + al256((size_t)V * 4);
+  int* offsets = (int*)w; w += al256(((size_t)V + 1) * 4);
+  int* sorted = (int*)w; w += al256((size_t)N * 4);
+  float* partial = (float*)w;
+  if (N > 0)
     hipLaunchKernelGGL(sc_segsum_kernel, dim3((N + SC_SEG - 1) / SC_SEG, (d + 255) / 256), dim3(64), 0, st, tok,
                        sorted, offsets + V, dh, d, partial);
-  }
   hipLaunchKernelGGL(sc_combine_kernel, dim3(V, (d + 255) / 256), dim3(64), 0, st, offsets, partial, d, dE,
                      (int)accumulate);
+}
+
+void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws,
+                          int32_t* sorted_out, hipStream_t st, bool accumulate) {
+  launch_embed_sort(tok, N, V, ws, st);
+  launch_embed_scatter_sorted(tok, dh, dE, N, V, d, ws, st, accumulate);
+  if (sorted_out && N > 0) {
+    const int P = (N + SC_CHUNK - 1) / SC_CHUNK;
+    const char* w = (const char*)ws + al256((size_t)P * V * 4) + al256((size_t)V * 4) + al256(((size_t)V + 1) * 4);
+    (void)hipMemcpyAsync(sorted_out, w, (size_t)N * 4, hipMemcpyDeviceToDevice, st);
+  }
 }
 
 void launch_cast_f32_to_act(const float* x, void* y, int at, size_t n, hipStream_t st) {

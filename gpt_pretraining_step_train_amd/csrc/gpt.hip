@@ -81,7 +81,7 @@ struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart;
+      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred;
   size_t splitws_bytes;
 };
 
@@ -137,6 +137,7 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.dve = ve ? P.add(N * kv_dim(c) * 4) : 0;
   O.vdz = ve ? P.add(N * kv_heads(c) * 4) : 0;
   O.vpart = ve ? P.add((size_t)kv_heads(c) * kVeCh * N * 4) : 0;
+  O.vred = ve ? P.add(colsum_ws_bytes(kv_heads(c) * kVeCh)) : 0;
   O.wact = es == 2 ? P.add(nBlk * es) : 0;
   O.uact = es == 2 ? P.add(nU * es) : 0;
   O.hs = P.add((2 * L + 1) * N * d * 4);
@@ -757,6 +758,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps, st);
   }
   if (ex_resid) launch_zero(dx0, (size_t)N * d * 4, st);
+  if (ex_ve) launch_embed_sort(tok, N, V, M->base + O.embws, st);  // shared by every scatter below
   int cur = 0;
   for (int l = L - 1; l >= 0; --l) {
     const size_t wl = (size_t)l * M->lo.stride;
@@ -803,9 +805,9 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     }
     if (ex_ve) {  // the gate's path into the block input; the table's and gates' gradients
       launch_ve_da(dtmp, M->at_off<float>(O.vdz), ve_gate(M->params(), l), N, Hkv, d, st);
-      launch_embed_scatter(tok, M->at_off<float>(O.dve), ve_tab(grads, l), N, V, (int)kvd, M->base + O.embws, nullptr,
-                           st, M->acc_grads);
-      launch_rows_reduce(M->at_off<float>(O.vpart), Hkv * kVeCh, N, ve_gate(grads, l), M->acc_grads, st);
+      launch_embed_scatter_sorted(tok, M->at_off<float>(O.dve), ve_tab(grads, l), N, V, (int)kvd, M->base + O.embws,
+                                  st, M->acc_grads);
+      launch_colsum(M->at_off<float>(O.vpart), N, Hkv * kVeCh, M->base + O.vred, ve_gate(grads, l), M->acc_grads, st);
     }
     if (ex_resid || (ex_back && l == Lb)) {
       // g = d loss / d (layer input); the stream reaching the layer gets lr g (plus the
@@ -829,7 +831,10 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
                      xpart + (size_t)s_ls(c) * N, xpart + (size_t)s_ws(c) * N, N, T, d, st);
     cur ^= 1;
   }
-  launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st, M->acc_grads);
+  if (ex_ve)
+    launch_embed_scatter_sorted(tok, dh[cur], grads, N, V, d, M->base + O.embws, st, M->acc_grads);
+  else
+    launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st, M->acc_grads);
   if (c.extras)
     launch_extras_reduce(xpart, N, L, c.extras, grads + M->nE + M->nBlk + M->nU, M->acc_grads, st);
   return GPT_OK;

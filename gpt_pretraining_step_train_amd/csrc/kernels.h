@@ -89,13 +89,14 @@ void launch_extras_init(float* S, int L, hipStream_t st);
 // v += 3 sigmoid(wg . a[:24]) ve[tok] per head, the gate values to vg [N][Hkv]
 void launch_ve_fwd(void* qkv, int at, const void* a, const int32_t* tok, const float* ve, const float* wg,
                    float* vg, int N, int V, int H, int Hkv, int hd, int d, hipStream_t st);
-// dve [N][Hkv hd] = g dv, dz [N][Hkv], part [Hkv*24][N] (rows of d wg) from dqkv's v part
+// dve [N][Hkv hd] = g dv, dz [N][Hkv], part [N][Hkv*24] (rows of d wg) from dqkv's v part
 void launch_ve_bwd(const void* dqkv, int at, const void* a, const int32_t* tok, const float* ve, const float* vg,
                    float* dve, float* dz, float* part, int N, int V, int H, int Hkv, int hd, int d, hipStream_t st);
 // da[:, :24] += dz wg
 void launch_ve_da(float* da, const float* dz, const float* wg, int N, int Hkv, int d, hipStream_t st);
-// out[j] (+)= sum_n part[j][n], fixed order, j < rows
-void launch_rows_reduce(const float* part, int rows, int N, float* out, bool accumulate, hipStream_t st);
+// out[j] (+)= sum_n part[n][j] for j < R, fixed order (fp64); ws holds colsum_ws_bytes(R)
+size_t colsum_ws_bytes(int R);
+void launch_colsum(const float* part, int N, int R, void* ws, float* out, bool accumulate, hipStream_t st);
 void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st);
 // qkv rows are [H q heads | Hkv k heads | Hkv v heads] x hd; rstd_q is [B*T][H], rstd_k [B*T][Hkv]
 void launch_rope_qknorm_fwd(void* qkv, int act_type, const float* cs, float* rstd_q, float* rstd_k,
@@ -112,6 +113,11 @@ void launch_sum_rows(const float* x, int n, double* out, hipStream_t st);
 size_t embed_ws_bytes(int N, int V, int d);
 void launch_embed_scatter(const int32_t* tok, const float* dh, float* dE, int N, int V, int d,
                           void* ws, int32_t* sorted_out, hipStream_t st, bool accumulate = false);
+// the same in two parts: the sort of the ids (once per token batch), then any number of
+// scatters of rows of any width <= d (the ws of embed_ws_bytes(N, V, d) keeps the sort)
+void launch_embed_sort(const int32_t* tok, int N, int V, void* ws, hipStream_t st);
+void launch_embed_scatter_sorted(const int32_t* tok, const float* dh, float* dE, int N, int V, int d, void* ws,
+                                 hipStream_t st, bool accumulate);
 void launch_cast_f32_to_act(const float* x, void* y, int act_type, size_t n, hipStream_t st);
 void launch_fill_normal(float* w, size_t n, uint64_t seed, uint64_t stream_id, float stddev,
                         hipStream_t st);
