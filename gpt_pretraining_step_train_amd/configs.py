@@ -26,7 +26,9 @@ DEFAULTS = dict(init_std=0.02, rope_base=10000.0, norm_eps=1e-6, muon_momentum=0
                 ns_steps=5, fp8_gemms=7,   # fp8: forward, weight- and input-gradient GEMMs
                 attn_window=0,             # sliding-window attention off (every earlier key)
                 n_kv_head=0,               # key/value heads; 0 = n_head (multi-head attention)
-                extras=0)                  # mask: 1 residual scaling, 2 smear, 4 backout, 8 value embeddings
+                extras=0,                  # mask: 1 residual scaling, 2 smear, 4 backout, 8 value embeddings,
+                                           # 16 NorMuon
+                normuon_beta2=0.95)        # NorMuon's second-moment decay
 
 
 def kv_heads(cfg: dict) -> int:
@@ -46,7 +48,7 @@ def get(name: str, **over) -> dict:
 def n_params(cfg: dict) -> int:
     d, F, V, L = cfg["d_model"], cfg["d_ff"], cfg["vocab"], cfg["depth"]
     dkv = kv_heads(cfg) * cfg["head_dim"] if cfg.get("n_kv_head") else d  # Wk, Wv rows
-    n_s = 2 * L + 26 if cfg.get("extras") else 0  # the extras' scalars
+    n_s = 2 * L + 26 if cfg.get("extras", 0) & 15 else 0  # the extras' scalars
     if cfg.get("extras", 0) & 8:  # value-embedding tables and gate weights
         n_s += L * V * kv_heads(cfg) * cfg["head_dim"] + L * kv_heads(cfg) * 24
     return 2 * V * d + L * (2 * d * d + 2 * dkv * d + 2 * F * d) + n_s

@@ -35,7 +35,7 @@ def tensor_shapes(cfg: dict) -> list[tuple[str, tuple[int, int]]]:
         out += [(f"l{l}.Wq", (d, d)), (f"l{l}.Wk", (dkv, d)), (f"l{l}.Wv", (dkv, d)),
                 (f"l{l}.Wo", (d, d)), (f"l{l}.W1", (F, d)), (f"l{l}.W2", (d, F))]
     out.append(("U", (V, d)))
-    if cfg.get("extras"):
+    if cfg.get("extras", 0) & 15:  # bit 16 (NorMuon) is an optimizer option without parameters
         out.append(("S", (1, 2 * L + 26)))
     if cfg.get("extras", 0) & 8:
         out += [(f"l{l}.VE", (V, dkv)) for l in range(L)]

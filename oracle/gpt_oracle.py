@@ -56,6 +56,8 @@ translation).  Their parameters form one more tensor S at the end of the table
   embedding before smearing.
 * 4, backout: the final norm reads x_L - lb x_mid, x_mid the residual stream
   entering layer L // 2 (before that layer's residual scaling).
+* 16, NorMuon: the Muon update of every block matrix goes through normuon()
+  (section "2. Muon Optimize Edici"); it adds no model parameters.
 * 8, value embeddings (the ResFormer snippet of the same section): every layer i
   has its own table VE_i [V, Hkv hd] and gate weights Wg_i [Hkv, 24]; after the
   QKV projection, v[t, h] += 3 sigmoid(Wg_i[h] . a[t, :24]) VE_i[token t, h], a the
@@ -73,6 +75,8 @@ from oracle.e4m3 import quantise
 
 
 EXTRA_RESID, EXTRA_SMEAR, EXTRA_BACKOUT, EXTRA_VALUE_EMB = 1, 2, 4, 8
+EXTRA_NORMUON = 16     # an optimizer option (normuon() below): no parameters of its own
+MODEL_EXTRAS = 15      # the bits that add the parameter tensor S
 SMEAR_CHANNELS = 24  # channels of the current position the smear gate reads
 VE_GATE_CHANNELS = 24  # channels of the block's normed input the value-embedding gate reads
 
@@ -89,7 +93,7 @@ def unpack(params, cfg):
     VE (a list) and G ([L, Hkv, 24]) are None without value embeddings."""
     L = cfg["depth"]
     ex = cfg.get("extras", 0)
-    has_s, has_ve = bool(ex), bool(ex & EXTRA_VALUE_EMB)
+    has_s, has_ve = bool(ex & MODEL_EXTRAS), bool(ex & EXTRA_VALUE_EMB)
     assert len(params) == 2 + 6 * L + has_s + (L + 1) * has_ve
     E = params[0]
     layers = [tuple(params[1 + 6 * l: 7 + 6 * l]) for l in range(L)]
@@ -436,6 +440,29 @@ def muon_matrix(G, Bm, coeffs, mu=0.95, eps=1e-7):
     Bm = mu * np.asarray(Bm, dtype=np.float64) + np.asarray(G, dtype=np.float64)
     X0 = Bm / (np.linalg.norm(Bm) + eps)
     return newton_schulz(X0, coeffs), Bm
+
+
+def normuon(X, V, beta2, eps=1e-10):
+    """NorMuon's per-neuron normalisation of one matrix's orthogonalised update X
+    [out, in] (the nanochat articles print its last four lines under "NorMuon Varyans
+    Azaltma" in "2. Muon Optimize Edici"; the rest follows the published method, Li et
+    al. 2025, "NorMuon: Making Muon more efficient and scalable"):
+
+        v_mean[i] = mean_j X[i, j]^2              one statistic per output neuron
+        V <- beta2 V + (1 - beta2) v_mean          running second moment (starts at 0)
+        step[i] = 1 / sqrt(max(V[i], eps))
+        v_norm = sqrt(sum_i v_mean[i]),  v_norm_new = sqrt(sum_i v_mean[i] step[i]^2)
+        X'[i, :] = X[i, :] step[i] v_norm / max(v_norm_new, eps)
+
+    so rows are rescaled by the inverse root of their running second moment while the
+    Frobenius norm of X is kept.  Returns (X', V')."""
+    X = np.asarray(X, dtype=np.float64)
+    v_mean = np.mean(X * X, axis=1)
+    V = beta2 * np.asarray(V, dtype=np.float64) + (1.0 - beta2) * v_mean
+    step = 1.0 / np.sqrt(np.maximum(V, eps))
+    v_norm = np.sqrt(np.sum(v_mean))
+    v_norm_new = np.sqrt(np.sum(v_mean * step * step))
+    return X * (step * v_norm / max(v_norm_new, eps))[:, None], V
 
 
 def muon_update(params, grads, moms, cfg, lr, coeffs):

@@ -24,7 +24,7 @@ def random_extras(params, cfg, seed):
     """Move the extras' tensors off their start values (which leave the extras inert),
     as training would: S and the value-embedding gate weights G by 0.3 N(0, 1) per
     entry, the value-embedding tables to 0.5 N(0, 1) (the size of v's entries)."""
-    if cfg.get("extras"):
+    if cfg.get("extras", 0) & 15:
         from gpt_pretraining_step_train_amd import inputs
         rng = np.random.default_rng(seed + 1000)
         for i, (name, shape) in enumerate(inputs.tensor_shapes(cfg)):

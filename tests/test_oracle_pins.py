@@ -41,7 +41,7 @@ def _params(cfg, seed=0, std=None, random_s=True):
     if std is not None:
         c["init_std"] = std
     ws = [w.astype(np.float64) for w in inputs.init_weights(c, seed)]
-    if cfg.get("extras") and random_s:
+    if cfg.get("extras", 0) & 15 and random_s:
         rng = np.random.default_rng(seed + 1000)
         for i, (name, shape) in enumerate(inputs.tensor_shapes(cfg)):
             if name in ("S", "G"):
@@ -620,6 +620,31 @@ def test_smear_with_a_constant_gate_is_a_bigram_embedding():
     z, _ = O.forward(p, tok, cfg)
     z2, _ = O.forward([E2] + p[1:-1], pair, big)
     np.testing.assert_allclose(z, z2, rtol=1e-13, atol=1e-15)
+
+
+def test_normuon_closed_forms():
+    """NorMuon keeps the Frobenius norm for any buffer and decay; with decay 0 every
+    row of the result has the same norm; a single row, or rows of equal mean square
+    with a buffer proportional to them, pass unchanged; and a frozen buffer (decay 1)
+    scales row i by 1/sqrt(V_i) up to the common factor that keeps the norm."""
+    rng = np.random.default_rng(41)
+    X = rng.standard_normal((9, 13)) * rng.uniform(0.05, 4.0, (9, 1))
+    for b2, V in ((0.0, np.zeros(9)), (0.9, rng.uniform(0, 3, 9)), (0.5, np.zeros(9))):
+        Y, _ = O.normuon(X, V, b2)
+        assert np.linalg.norm(Y) == pytest.approx(np.linalg.norm(X), rel=1e-13)
+    Y, V1 = O.normuon(X, np.zeros(9), 0.0)
+    np.testing.assert_allclose(np.linalg.norm(Y, axis=1), np.linalg.norm(X) / 3.0, rtol=1e-13)
+    np.testing.assert_allclose(V1, np.mean(X * X, axis=1), rtol=1e-15)
+    row = X[:1]
+    np.testing.assert_allclose(O.normuon(row, np.zeros(1), 0.3)[0], row, rtol=1e-13)
+    U = rng.standard_normal((6, 8))
+    U /= np.linalg.norm(U, axis=1, keepdims=True)                # equal mean squares
+    np.testing.assert_allclose(O.normuon(U, np.full(6, 0.7), 0.6)[0], U, rtol=1e-13)
+    V0 = rng.uniform(0.5, 2.0, 9)
+    Y, V2 = O.normuon(X, V0, 1.0)
+    np.testing.assert_array_equal(V2, V0)
+    Z = X / np.sqrt(V0)[:, None]
+    np.testing.assert_allclose(Y, Z * np.linalg.norm(X) / np.linalg.norm(Z), rtol=1e-13)
 
 
 # --------------------------------------------------------------------------
