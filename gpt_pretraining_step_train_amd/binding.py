@@ -27,7 +27,7 @@ class GptCfg(ctypes.Structure):
         ("muon_momentum", ctypes.c_float), ("ns_steps", ctypes.c_int32),
         ("ns_coeffs", (ctypes.c_float * 3) * 5), ("num_steps", ctypes.c_int64),
         ("ns_split_steps", ctypes.c_int32), ("fp8_gemms", ctypes.c_int32), ("attn_window", ctypes.c_int32),
-        ("n_kv_head", ctypes.c_int32), ("extras", ctypes.c_int32),
+        ("n_kv_head", ctypes.c_int32), ("extras", ctypes.c_int32), ("normuon_beta2", ctypes.c_float),
     ]
 
     def coeffs(self):
@@ -134,6 +134,8 @@ def make_cfg(c: dict) -> GptCfg:
         cfg.n_kv_head = int(c["n_kv_head"])
     if "extras" in c:
         cfg.extras = int(c["extras"])
+    if "normuon_beta2" in c:
+        cfg.normuon_beta2 = float(c["normuon_beta2"])
     if "ns_coeffs" in c:
         for i, abc in enumerate(c["ns_coeffs"]):
             for j in range(3):

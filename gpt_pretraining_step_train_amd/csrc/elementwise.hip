@@ -1152,21 +1152,24 @@ __global__ void __launch_bounds__(256) ns_normalize_vec_kernel(const float* __re
 // W -= lr * X without a transpose, four consecutive elements per thread
 template <typename T>
 __global__ void __launch_bounds__(256) muon_apply_vec_kernel(float* __restrict__ w, T* __restrict__ wa,
-                                                             const float* __restrict__ x, float lr, long n4) {
+                                                             const float* __restrict__ x, float lr, long n4,
+                                                             const float* __restrict__ row_scale, int cols) {
   for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
     float4 a = reinterpret_cast<float4*>(w)[i];
     const float4 q = reinterpret_cast<const float4*>(x)[i];
-    a.x -= lr * q.x; a.y -= lr * q.y; a.z -= lr * q.z; a.w -= lr * q.w;
+    const float f = row_scale ? lr * row_scale[4 * i / cols] : lr;  // cols % 4 == 0: one row
+    a.x -= f * q.x; a.y -= f * q.y; a.z -= f * q.z; a.w -= f * q.w;
     reinterpret_cast<float4*>(w)[i] = a;
     if (wa) st4<T>(wa + 4 * i, a);
   }
 }
 
-// W -= lr * X (X stored [cols][rows] when transposed); refresh the act copy of W
+// W -= lr * s[r] * X (X stored [cols][rows] when transposed; s the optional per-row scale);
+// refresh the act copy of W
 template <typename T>
 __global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, T* __restrict__ wa,
                                                          const float* __restrict__ x, float lr, int rows, int cols,
-                                                         int transposed) {
+                                                         int transposed, const float* __restrict__ row_scale) {
   __shared__ float tile[32][33];
   const int tr = blockIdx.y * 32, tc = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -1181,7 +1184,7 @@ __global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, 
     const int r = tr + i, c = tc + tx;
     if (r < rows && c < cols) {
       const float xv = transposed ? tile[tx][i] : x[(long)r * cols + c];
-      const float nw = w[(long)r * cols + c] - lr * xv;
+      const float nw = w[(long)r * cols + c] - (row_scale ? lr * row_scale[r] : lr) * xv;
       w[(long)r * cols + c] = nw;
       if (wa) st<T>(wa + (long)r * cols + c, nw);
     }
@@ -1673,22 +1676,94 @@ void launch_ns_normalize(const float* src, const double* sumsq, int mat, float e
 }
 
 void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int rows, int cols, bool tr,
-                       hipStream_t st) {
+                       hipStream_t st, const float* row_scale) {
   const long n = (long)rows * cols;
-  if (!tr && n % 4 == 0) {
+  if (!tr && cols % 4 == 0) {
     const long n4 = n / 4;
     const dim3 gv((unsigned)std::min<long>((n4 + 255) / 256, 4096));
     if (at == ACT_BF16)
-      hipLaunchKernelGGL(muon_apply_vec_kernel<bf16_t>, gv, dim3(256), 0, st, w, (bf16_t*)wa, x, lr, n4);
+      hipLaunchKernelGGL(muon_apply_vec_kernel<bf16_t>, gv, dim3(256), 0, st, w, (bf16_t*)wa, x, lr, n4, row_scale,
+                         cols);
     else
-      hipLaunchKernelGGL(muon_apply_vec_kernel<float>, gv, dim3(256), 0, st, w, (float*)wa, x, lr, n4);
+      hipLaunchKernelGGL(muon_apply_vec_kernel<float>, gv, dim3(256), 0, st, w, (float*)wa, x, lr, n4, row_scale,
+                         cols);
     return;
   }
   dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(muon_apply_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, rows, cols, (int)tr);
+    hipLaunchKernelGGL(muon_apply_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, rows, cols, (int)tr, row_scale);
   else
-    hipLaunchKernelGGL(muon_apply_kernel<float>, g, b, 0, st, w, (float*)wa, x, lr, rows, cols, (int)tr);
+    hipLaunchKernelGGL(muon_apply_kernel<float>, g, b, 0, st, w, (float*)wa, x, lr, rows, cols, (int)tr, row_scale);
+}
+
+// NorMuon.  Mean square of each output row of one matrix's update X ([rows][cols], or
+// stored [cols][rows] when transposed): a wave per row, or a thread per row reading
+// down a column of the transposed store.
+__global__ void __launch_bounds__(256) normuon_rowstats_kernel(const float* __restrict__ x, int rows, int cols,
+                                                               int transposed, float* __restrict__ vmean) {
+  if (transposed) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    float s = 0.f;
+    for (int c = 0; c < cols; ++c) {
+      const float v = x[(long)c * rows + r];
+      s += v * v;
+    }
+    vmean[r] = s / (float)cols;
+    return;
+  }
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  float s = 0.f;
+  for (int c = lane; c < cols; c += 64) {
+    const float v = x[(long)r * cols + c];
+    s += v * v;
+  }
+  s = wave_sum(s);
+  if (lane == 0) vmean[r] = s / (float)cols;
+}
+
+// one block per matrix (rows roff[m] .. roff[m+1] of the stacked row vectors):
+// V = b2 V + (1 - b2) vmean, step = 1 / sqrt(max(V, 1e-10)), and the row scales
+// step * sqrt(sum vmean) / max(sqrt(sum vmean step^2), 1e-10) (fixed-order fp64 sums)
+__global__ void __launch_bounds__(256) normuon_scale_kernel(const float* __restrict__ vmean, float* __restrict__ V,
+                                                            const long* __restrict__ roff, float b2,
+                                                            float* __restrict__ scale) {
+  __shared__ double red[2][256];
+  const long r0 = roff[blockIdx.x], r1 = roff[blockIdx.x + 1];
+  double s1 = 0.0, s2 = 0.0;
+  for (long r = r0 + threadIdx.x; r < r1; r += 256) {
+    const float v = b2 * V[r] + (1.f - b2) * vmean[r];
+    V[r] = v;
+    const float step = 1.f / sqrtf(fmaxf(v, 1e-10f));
+    scale[r] = step;
+    s1 += (double)vmean[r];
+    s2 += (double)vmean[r] * step * step;
+  }
+  red[0][threadIdx.x] = s1;
+  red[1][threadIdx.x] = s2;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  const float f = (float)(sqrt(red[0][0]) / fmax(sqrt(red[1][0]), 1e-10));
+  for (long r = r0 + threadIdx.x; r < r1; r += 256) scale[r] *= f;
+}
+
+void launch_normuon_rowstats(const float* x, int rows, int cols, bool transposed, float* vmean, hipStream_t st) {
+  if (transposed)
+    hipLaunchKernelGGL(normuon_rowstats_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, x, rows, cols, 1, vmean);
+  else
+    hipLaunchKernelGGL(normuon_rowstats_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, x, rows, cols, 0, vmean);
+}
+
+void launch_normuon_scale(const float* vmean, float* V, const long* roff, int nmat, float beta2, float* scale,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(normuon_scale_kernel, dim3(nmat), dim3(256), 0, st, vmean, V, roff, beta2, scale);
 }
 
 void launch_adamw(float* w, const float* g, float* m, float* v, void* w_act, int act_type, size_t n, float lr,

@@ -46,7 +46,8 @@ inline size_t qkv_dim(const gpt_cfg& c) { return (size_t)c.d_model + 2 * kv_dim(
 // the extras' parameter vector S (when any extra is on): residual scales lr[L], x0
 // scales l0[L], the smear scale ls, the backout scale lb, the smear-gate weights ws[24]
 constexpr int kSmearCh = 24;
-inline size_t n_extras(const gpt_cfg& c) { return c.extras ? (size_t)2 * c.depth + 2 + kSmearCh : 0; }
+constexpr int kModelExtras = GPT_EXTRA_RESID | GPT_EXTRA_SMEAR | GPT_EXTRA_BACKOUT | GPT_EXTRA_VALUE_EMB;
+inline size_t n_extras(const gpt_cfg& c) { return c.extras & kModelExtras ? (size_t)2 * c.depth + 2 + kSmearCh : 0; }
 inline int s_lr(const gpt_cfg&, int l) { return l; }
 inline int s_l0(const gpt_cfg& c, int l) { return c.depth + l; }
 inline int s_ls(const gpt_cfg& c) { return 2 * c.depth; }
@@ -81,7 +82,8 @@ struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred;
+      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
+      nm_roff;
   size_t splitws_bytes;
 };
 
@@ -138,6 +140,14 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.vdz = ve ? P.add(N * kv_heads(c) * 4) : 0;
   O.vpart = ve ? P.add((size_t)kv_heads(c) * kVeCh * N * 4) : 0;
   O.vred = ve ? P.add(colsum_ws_bytes(kv_heads(c) * kVeCh)) : 0;
+  // NorMuon: per output row of every block matrix, its running second moment, this
+  // update's mean square and scale; the row offsets of the matrices
+  const bool nm = c.extras & GPT_EXTRA_NORMUON;
+  const size_t nrows = L * (3 * d + 2 * kv_dim(c) + F);
+  O.nm_v = nm ? P.add(nrows * 4) : 0;
+  O.nm_mean = nm ? P.add(nrows * 4) : 0;
+  O.nm_scale = nm ? P.add(nrows * 4) : 0;
+  O.nm_roff = nm ? P.add((6 * L + 1) * 8) : 0;
   O.wact = es == 2 ? P.add(nBlk * es) : 0;
   O.uact = es == 2 ? P.add(nU * es) : 0;
   O.hs = P.add((2 * L + 1) * N * d * 4);
@@ -229,8 +239,9 @@ struct gpt_model {
   long adam_t = 0;       // AdamW steps taken (bias corrections use the next one)
   bool acc_grads = false;  // the current step adds its gradients to the stored ones
   std::vector<int> xslot;  // per weight: quantisation slot of its input in this step's forward
-  // matrix table for Muon, in layer order (q, k, v, o, w1, w2)
-  std::vector<long> moff, msize;
+  // matrix table for Muon, in layer order (q, k, v, o, w1, w2); the first row of each
+  // matrix in the stacked per-row NorMuon vectors (6L + 1 entries)
+  std::vector<long> moff, msize, nm_roff;
   // profiling
   std::string prof_name;
   std::vector<hipEvent_t> ev;
@@ -296,7 +307,7 @@ bool tensor_loc(const gpt_cfg& c, int id, size_t* off, int* rows, int* cols) {
   const LayerOffs lo = layer_offs(c);
   if (id == 0) { *off = 0; *rows = (int)V; *cols = (int)d; return true; }
   if (id == (int)(1 + 6 * L)) { *off = V * d + L * lo.stride; *rows = (int)V; *cols = (int)d; return true; }
-  if (id == (int)(2 + 6 * L) && c.extras) {
+  if (id == (int)(2 + 6 * L) && (c.extras & kModelExtras)) {
     *off = 2 * V * d + L * lo.stride;
     *rows = 1;
     *cols = (int)n_extras(c);
@@ -353,6 +364,7 @@ int gpt_cfg_from_depth(int32_t depth, gpt_cfg* out) {
   out->attn_window = 0;
   out->n_kv_head = 0;
   out->extras = 0;
+  out->normuon_beta2 = 0.95f;
   memcpy(out->ns_coeffs, kNsCoeffs, sizeof(kNsCoeffs));
   const double nparams = 2.0 * out->vocab * d + (double)depth * (4.0 * d * d + 2.0 * d * out->d_ff);
   out->num_steps = (int64_t)llround(8.0 * nparams / 1048576.0);
@@ -378,7 +390,8 @@ int gpt_cfg_validate(const gpt_cfg* c) {
   if (c->fp8_gemms & ~(GPT_FP8_FWD | GPT_FP8_WGRAD | GPT_FP8_DGRAD)) return GPT_ERR_ARG;
   if (c->attn_window < 0) return GPT_ERR_ARG;
   if (c->n_kv_head < 0 || c->n_kv_head > c->n_head || c->n_head % kv_heads(*c) != 0) return GPT_ERR_SHAPE;
-  if (c->extras & ~(GPT_EXTRA_RESID | GPT_EXTRA_SMEAR | GPT_EXTRA_BACKOUT | GPT_EXTRA_VALUE_EMB)) return GPT_ERR_ARG;
+  if (c->extras & ~(kModelExtras | GPT_EXTRA_NORMUON)) return GPT_ERR_ARG;
+  if ((c->extras & GPT_EXTRA_NORMUON) && !(c->normuon_beta2 >= 0.f && c->normuon_beta2 < 1.f)) return GPT_ERR_ARG;
   if ((c->extras & GPT_EXTRA_SMEAR) && c->d_model < kSmearCh) return GPT_ERR_SHAPE;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->init_std >= 0.f)) return GPT_ERR_ARG;
   return GPT_OK;
@@ -395,7 +408,7 @@ size_t gpt_cfg_bytes(void) { return sizeof(gpt_cfg); }
 
 int gpt_tensor_count(const gpt_cfg* c) {
   if (!c) return 0;
-  return 2 + 6 * c->depth + (c->extras ? 1 : 0) + (c->extras & GPT_EXTRA_VALUE_EMB ? c->depth + 1 : 0);
+  return 2 + 6 * c->depth + (c->extras & kModelExtras ? 1 : 0) + (c->extras & GPT_EXTRA_VALUE_EMB ? c->depth + 1 : 0);
 }
 
 int gpt_tensor_shape(const gpt_cfg* c, int32_t id, int32_t* rows, int32_t* cols) {
@@ -463,6 +476,9 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
     for (int j = 0; j < 6; ++j) {
       M->moff.push_back((long)(b + o6[j]));
       M->msize.push_back(j == 1 || j == 2 ? (long)kv_dim(*cfg) * d : j < 4 ? (long)d * d : (long)d * F);
+      if (M->nm_roff.empty()) M->nm_roff.push_back(0);
+      const long rows = j == 4 ? F : (j == 1 || j == 2) ? (long)kv_dim(*cfg) : d;  // output rows
+      M->nm_roff.push_back(M->nm_roff.back() + rows);
     }
   }
   // weights: one counter-based stream per tensor id
@@ -485,6 +501,14 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   launch_zero(M->at_off<float>(O.grads), (M->nE + M->nBlk + M->nU + M->nT) * 4, st);
   refresh_act(M, st);
   launch_rope_table(M->at_off<float>(O.rope), cfg->seq_len, cfg->head_dim, cfg->rope_base, st);
+  if (cfg->extras & GPT_EXTRA_NORMUON) {
+    launch_zero(M->at_off<float>(O.nm_v), (size_t)M->nm_roff.back() * 4, st);
+    if (hipMemcpyAsync(M->at_off<long>(O.nm_roff), M->nm_roff.data(), M->nm_roff.size() * 8, hipMemcpyHostToDevice,
+                       st) != hipSuccess) {
+      delete M;
+      return GPT_ERR_HIP;
+    }
+  }
   if (hipMemcpyAsync(M->at_off<long>(O.mat_off), M->moff.data(), M->moff.size() * 8, hipMemcpyHostToDevice, st) !=
           hipSuccess ||
       hipMemcpyAsync(M->at_off<long>(O.mat_size), M->msize.data(), M->msize.size() * 8, hipMemcpyHostToDevice,
@@ -1003,13 +1027,25 @@ int muon_update(gpt_model* M, float lr, void* stream) {
       cur ^= 1;
     }
   }
+  // NorMuon: per output row, the running second moment of the update; rows scaled by its
+  // inverse root, the update's Frobenius norm kept
+  const bool nm = c.extras & GPT_EXTRA_NORMUON;
+  float* nm_scale = M->at_off<float>(O.nm_scale);
+  if (nm) {
+    for (int l = 0; l < L; ++l)
+      for (int j = 0; j < 6; ++j)
+        launch_normuon_rowstats(xf + xdst(l, j), mrows(j), j == 5 ? F : d, transposed(j),
+                                M->at_off<float>(O.nm_mean) + M->nm_roff[6 * l + j], st);
+    launch_normuon_scale(M->at_off<float>(O.nm_mean), M->at_off<float>(O.nm_v), M->at_off<long>(O.nm_roff), 6 * L,
+                         c.normuon_beta2, nm_scale, st);
+  }
   float* wblk = M->blk(M->params());
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
       const int rows = mrows(j), cols = j == 5 ? F : d;
       const size_t mo = M->moff[6 * l + j];
       launch_muon_apply(wblk + mo, M->at == ACT_BF16 ? M->wact(mo) : nullptr, M->at, xf + xdst(l, j), lr, rows, cols,
-                        transposed(j), st);
+                        transposed(j), st, nm ? nm_scale + M->nm_roff[6 * l + j] : nullptr);
     }
   M->wq_dirty = true;
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;

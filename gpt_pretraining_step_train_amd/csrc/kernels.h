@@ -135,8 +135,15 @@ void launch_momentum_sumsq(float* m, const float* g, float mu, const long* offs,
 // X = src / (norm + eps) written (optionally transposed) into fp32 and act copies
 void launch_ns_normalize(const float* src, const double* sumsq, int mat, float eps, int rows, int cols,
                          bool transpose, float* xf, void* xa, void* xa_lo, int act_type, hipStream_t st);
+// W -= lr * s[r] * X, s an optional per-row scale (NorMuon)
 void launch_muon_apply(float* w, void* w_act, int act_type, const float* x, float lr, int rows,
-                       int cols, bool transposed, hipStream_t st);
+                       int cols, bool transposed, hipStream_t st, const float* row_scale = nullptr);
+// NorMuon: mean square of each output row of X (stored [cols][rows] when transposed), then
+// per matrix (rows roff[m] .. roff[m+1] of the stacked vectors) V = b2 V + (1-b2) vmean
+// and the row scales that divide by sqrt(V) and keep the update's Frobenius norm
+void launch_normuon_rowstats(const float* x, int rows, int cols, bool transposed, float* vmean, hipStream_t st);
+void launch_normuon_scale(const float* vmean, float* V, const long* roff, int nmat, float beta2, float* scale,
+                          hipStream_t st);
 
 // fp8 (OCP e4m3fn) per-tensor current scaling.  amax slot: one uint32 holding the bits of
 // max|x| (non-negative floats order as integers); must be zeroed before launch_amax.

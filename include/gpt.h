@@ -105,11 +105,17 @@ typedef struct gpt_cfg {
                            normed input (tensors VE_i and G).
                          S starts at the identity (lr = 1, the rest 0), VE and G at 0; AdamW
                          updates all of them.
+                         GPT_EXTRA_NORMUON: muon_update scales each output row of a matrix's
+                           orthogonalised update by 1/sqrt(V), V its running mean square
+                           (decay normuon_beta2, starts at 0), and rescales the update to its
+                           Frobenius norm (no parameters of its own).
                          0 (the default) = none; other bits: GPT_ERR_ARG */
+  float normuon_beta2;  /* NorMuon's second-moment decay in [0, 1) (else GPT_ERR_ARG when
+                           GPT_EXTRA_NORMUON is set); default 0.95 */
 } gpt_cfg;
 
 enum { GPT_FP8_FWD = 1, GPT_FP8_WGRAD = 2, GPT_FP8_DGRAD = 4 };
-enum { GPT_EXTRA_RESID = 1, GPT_EXTRA_SMEAR = 2, GPT_EXTRA_BACKOUT = 4, GPT_EXTRA_VALUE_EMB = 8 };
+enum { GPT_EXTRA_RESID = 1, GPT_EXTRA_SMEAR = 2, GPT_EXTRA_BACKOUT = 4, GPT_EXTRA_VALUE_EMB = 8, GPT_EXTRA_NORMUON = 16 };
 
 typedef struct gpt_model gpt_model; /* opaque */
 

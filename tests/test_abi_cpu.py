@@ -65,6 +65,7 @@ def test_default_ns_table(lib):
     tab = c.coeffs()
     assert c.ns_steps == gold["ns_steps"] and c.ns_split_steps == 0 and c.fp8_gemms == 7
     assert c.attn_window == 0 and c.n_kv_head == 0 and c.extras == 0
+    assert c.normuon_beta2 == pytest.approx(0.95)
     assert ctypes.sizeof(binding.GptCfg) == lib.gpt_cfg_bytes() == 152
     np.testing.assert_allclose(tab[:2], gold["printed"], rtol=0, atol=1e-6)
     derived, _ = polar_express.coefficients()
@@ -77,11 +78,15 @@ def test_validation_errors(lib):
     for field, val, code in [("head_dim", 48, 6), ("n_head", 5, 2), ("d_model", 2056, 2), ("precision", 7, 6),
                              ("ns_steps", 6, 1), ("batch", 0, 2), ("vocab", 4100, 2), ("fp8_gemms", 8, 1),
                              ("attn_window", -1, 1), ("n_kv_head", 2, 2), ("n_kv_head", 4, 2),
-                             ("n_kv_head", -1, 2), ("extras", 16, 1), ("extras", -1, 1)]:
+                             ("n_kv_head", -1, 2), ("extras", 32, 1), ("extras", -1, 1)]:
         c = binding.make_cfg(configs.get("laptop"))
         setattr(c, field, val)
         assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, field
         assert lib.gpt_state_bytes(ctypes.byref(c)) == 0
+    for b2, code in ((1.0, 1), (-0.1, 1), (float("nan"), 1), (0.0, 0)):  # NorMuon's decay, checked when on
+        c = binding.make_cfg(configs.get("laptop", extras=16))
+        c.normuon_beta2 = b2
+        assert lib.gpt_cfg_validate(ctypes.byref(c)) == code, b2
     assert lib.gpt_cfg_validate(None) == 1
     assert lib.gpt_status_str(3).decode() == "token id out of range"
 
@@ -91,7 +96,8 @@ def test_validation_errors(lib):
                                        ("d24", {"n_kv_head": 4}), ("tiny", {"extras": 7}),
                                        ("laptop", {"extras": 2}), ("d24", {"extras": 7, "n_kv_head": 4}),
                                        ("tiny", {"extras": 15}), ("laptop", {"extras": 8, "n_kv_head": 1}),
-                                       ("d24", {"extras": 15, "n_kv_head": 4})])
+                                       ("d24", {"extras": 15, "n_kv_head": 4}), ("laptop", {"extras": 16}),
+                                       ("tiny", {"extras": 31})])
 def test_state_bytes_and_tensor_table(lib, name, over):
     for cfg in [configs.get(name, **over)]:
         c = binding.make_cfg(cfg)
@@ -100,7 +106,8 @@ def test_state_bytes_and_tensor_table(lib, name, over):
         assert nb > 3 * 4 * n                     # params + grads + momentum at least
         assert nb < 288 * 2 ** 30                # fits one MI355X
         ex = cfg.get("extras", 0)
-        assert lib.gpt_tensor_count(ctypes.byref(c)) == 2 + 6 * cfg["depth"] + (ex > 0) + (cfg["depth"] + 1) * (ex >= 8)
+        assert lib.gpt_tensor_count(ctypes.byref(c)) == (2 + 6 * cfg["depth"] + bool(ex & 15)
+                                                         + (cfg["depth"] + 1) * bool(ex & 8))
         shapes = inputs.tensor_shapes(cfg)
         assert n == sum(r * k for _, (r, k) in shapes)
         for i, (nm, shp) in enumerate(shapes):

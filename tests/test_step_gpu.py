@@ -67,6 +67,7 @@ STEP_CASES = [("tiny", {}), ("laptop", {}), ("d12", {"batch": 1}), ("laptop_fp8"
               ("laptop_extras_fp8", {"precision": "fp8", "extras": 15}),
               ("d12_extras", {"batch": 1, "extras": 15, "n_kv_head": 2}),
               ("laptop_nssplit", {"ns_split_steps": 4}), ("d12_nssplit", {"batch": 1, "ns_split_steps": 4}),
+              ("laptop_normuon", {"extras": 16}), ("d12_normuon", {"batch": 1, "extras": 16, "n_kv_head": 2}),
               ("d26_fp8", {"batch": 1, "depth": 1})]
 
 
@@ -112,6 +113,8 @@ def test_step_and_muon_parity(name, over):
     worst = 0.0
     for i in ids:
         X, Bm = O.muon_matrix(grads[i], np.zeros_like(grads[i]), table, mu=cfg["muon_momentum"])
+        if cfg.get("extras", 0) & 16:  # NorMuon, from a zero second-moment buffer
+            X = O.normuon(X, np.zeros(X.shape[0]), cfg["normuon_beta2"])[0]
         upd = model.get_params(i).astype(np.float64) - before[i]
         e = rel_l2(upd, -LR * X)
         worst = max(worst, e)
@@ -141,6 +144,32 @@ def test_fp8_two_layers_within_the_oracles_own_spread():
         e_gpu, e_self = rel_l2(model.grads(i), ref), rel_l2(pert_grads[i], ref)
         say(f"  tensor {i}: gpu {e_gpu:.3f} oracle spread {e_self:.3f}")
         assert e_gpu <= max(6e-2, e_self), (i, e_gpu, e_self)
+
+
+@pytest.mark.parametrize("i", [2, 5, 6])  # Wk (d x d), W1 (F x d, stored transposed), W2 (d x F)
+def test_normuon_second_step_uses_its_buffer(i):
+    """Two NorMuon updates of one matrix: the second divides by the running second
+    moment that the first left, on top of the momentum."""
+    cfg, model, params, tok, tgt = _setup("laptop", batch=4, extras=16, normuon_beta2=0.8)
+    table, _ = PE.coefficients()
+    rng = np.random.default_rng(4 + i)
+    shp = model.shape(i)
+    G1, G2 = rng.standard_normal(shp).astype(np.float32), rng.standard_normal(shp).astype(np.float32)
+    w0 = model.get_params(i)
+    model.set_grads(i, G1)
+    model.muon_update(LR)
+    w1 = model.get_params(i)
+    model.set_grads(i, G2)
+    model.muon_update(LR)
+    w2 = model.get_params(i)
+    X1, B1 = O.muon_matrix(G1, np.zeros(shp), table, mu=cfg["muon_momentum"])
+    X1, V1 = O.normuon(X1, np.zeros(shp[0]), 0.8)
+    X2, _ = O.muon_matrix(G2, B1, table, mu=cfg["muon_momentum"])
+    X2, _ = O.normuon(X2, V1, 0.8)
+    assert rel_l2(w1.astype(np.float64) - w0, -LR * X1) < 2e-2
+    e = rel_l2(w2.astype(np.float64) - w1, -LR * X2)
+    say(f"  tensor {i} {shp}: second NorMuon update rel L2 {e:.2e}")
+    assert e < 2e-2
 
 
 def test_second_muon_step_uses_momentum():
