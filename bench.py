@@ -91,7 +91,7 @@ def main() -> int:
     ap.add_argument("--kv-heads", type=int, default=0, metavar="H",
                     help="grouped-query attention with H key/value heads (0: one per query head)")
     ap.add_argument("--extras", type=int, default=0, metavar="MASK",
-                    help="1 per-layer residual scaling, 2 smear, 4 backout, 8 value embeddings (parameters at their start values, "
+                    help="1 per-layer residual scaling, 2 smear, 4 backout, 8 value embeddings, 16 NorMuon (parameters at their start values, "
                          "which do not change the cost; AdamW updates them when --adamw is given)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dominant", default=None,
@@ -198,7 +198,7 @@ def main() -> int:
                                + (f", sliding-window attention W={args.window}" if args.window else "")
                                + (f", grouped-query attention with {args.kv_heads} key/value heads"
                                   if args.kv_heads else "")
-                               + (f", extras mask {args.extras} (1 residual scaling, 2 smear, 4 backout, 8 value embeddings)"
+                               + (f", extras mask {args.extras} (1 residual scaling, 2 smear, 4 backout, 8 value embeddings, 16 NorMuon)"
                                   if args.extras else ""),
                    "depth": cfg["depth"], "d_model": cfg["d_model"], "n_head": cfg["n_head"],
                    "n_kv_head": configs.kv_heads(cfg), "attn_window": args.window, "extras": args.extras,

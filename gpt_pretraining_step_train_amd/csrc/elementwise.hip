@@ -1697,21 +1697,38 @@ void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int
 }
 
 // NorMuon.  Mean square of each output row of one matrix's update X ([rows][cols], or
-// stored [cols][rows] when transposed): a wave per row, or a thread per row reading
-// down a column of the transposed store.
-__global__ void __launch_bounds__(256) normuon_rowstats_kernel(const float* __restrict__ x, int rows, int cols,
-                                                               int transposed, float* __restrict__ vmean) {
-  if (transposed) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= rows) return;
-    float s = 0.f;
-    for (int c = 0; c < cols; ++c) {
+// stored [cols][rows] when transposed).  Untransposed: a wave per row.  Transposed: a
+// block covers 64 rows (one per lane) and one of NM_CHUNKS column ranges (its 4 waves
+// interleaved), writing partial sums that a second pass adds in chunk order.
+constexpr int NM_CHUNKS = 16;
+__global__ void __launch_bounds__(256) normuon_colsq_kernel(const float* __restrict__ x, int rows, int cols,
+                                                            float* __restrict__ part) {
+  __shared__ float sm[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * 64 + lane, ch = blockIdx.y;
+  const int per = (cols + NM_CHUNKS - 1) / NM_CHUNKS, c0 = ch * per, c1 = min(cols, c0 + per);
+  float s = 0.f;
+  if (r < rows)
+    for (int c = c0 + wave; c < c1; c += 4) {
       const float v = x[(long)c * rows + r];
       s += v * v;
     }
-    vmean[r] = s / (float)cols;
-    return;
-  }
+  sm[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && r < rows) part[(long)ch * rows + r] = (sm[0][lane] + sm[1][lane]) + (sm[2][lane] + sm[3][lane]);
+}
+
+__global__ void __launch_bounds__(256) normuon_colsq_final_kernel(const float* __restrict__ part, int rows, int cols,
+                                                                  float* __restrict__ vmean) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  float s = 0.f;
+  for (int ch = 0; ch < NM_CHUNKS; ++ch) s += part[(long)ch * rows + r];
+  vmean[r] = s / (float)cols;
+}
+
+__global__ void __launch_bounds__(256) normuon_rowstats_kernel(const float* __restrict__ x, int rows, int cols,
+                                                               float* __restrict__ vmean) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= rows) return;
   float s = 0.f;
@@ -1754,11 +1771,18 @@ __global__ void __launch_bounds__(256) normuon_scale_kernel(const float* __restr
   for (long r = r0 + threadIdx.x; r < r1; r += 256) scale[r] *= f;
 }
 
-void launch_normuon_rowstats(const float* x, int rows, int cols, bool transposed, float* vmean, hipStream_t st) {
-  if (transposed)
-    hipLaunchKernelGGL(normuon_rowstats_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, x, rows, cols, 1, vmean);
-  else
-    hipLaunchKernelGGL(normuon_rowstats_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, x, rows, cols, 0, vmean);
+size_t normuon_ws_bytes(int max_rows) { return (size_t)NM_CHUNKS * max_rows * 4; }
+
+void launch_normuon_rowstats(const float* x, int rows, int cols, bool transposed, float* vmean, void* ws,
+                             hipStream_t st) {
+  if (transposed) {
+    hipLaunchKernelGGL(normuon_colsq_kernel, dim3((rows + 63) / 64, NM_CHUNKS), dim3(256), 0, st, x, rows, cols,
+                       (float*)ws);
+    hipLaunchKernelGGL(normuon_colsq_final_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, (const float*)ws, rows,
+                       cols, vmean);
+  } else {
+    hipLaunchKernelGGL(normuon_rowstats_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, x, rows, cols, vmean);
+  }
 }
 
 void launch_normuon_scale(const float* vmean, float* V, const long* roff, int nmat, float beta2, float* scale,

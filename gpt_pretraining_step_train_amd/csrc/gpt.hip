@@ -83,7 +83,7 @@ struct Offsets {
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
       xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
-      nm_roff;
+      nm_roff, nm_ws;
   size_t splitws_bytes;
 };
 
@@ -148,6 +148,7 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.nm_mean = nm ? P.add(nrows * 4) : 0;
   O.nm_scale = nm ? P.add(nrows * 4) : 0;
   O.nm_roff = nm ? P.add((6 * L + 1) * 8) : 0;
+  O.nm_ws = nm ? P.add(normuon_ws_bytes((int)std::max(d, F))) : 0;
   O.wact = es == 2 ? P.add(nBlk * es) : 0;
   O.uact = es == 2 ? P.add(nU * es) : 0;
   O.hs = P.add((2 * L + 1) * N * d * 4);
@@ -1035,7 +1036,7 @@ int muon_update(gpt_model* M, float lr, void* stream) {
     for (int l = 0; l < L; ++l)
       for (int j = 0; j < 6; ++j)
         launch_normuon_rowstats(xf + xdst(l, j), mrows(j), j == 5 ? F : d, transposed(j),
-                                M->at_off<float>(O.nm_mean) + M->nm_roff[6 * l + j], st);
+                                M->at_off<float>(O.nm_mean) + M->nm_roff[6 * l + j], M->base + O.nm_ws, st);
     launch_normuon_scale(M->at_off<float>(O.nm_mean), M->at_off<float>(O.nm_v), M->at_off<long>(O.nm_roff), 6 * L,
                          c.normuon_beta2, nm_scale, st);
   }

@@ -141,7 +141,10 @@ void launch_muon_apply(float* w, void* w_act, int act_type, const float* x, floa
 // NorMuon: mean square of each output row of X (stored [cols][rows] when transposed), then
 // per matrix (rows roff[m] .. roff[m+1] of the stacked vectors) V = b2 V + (1-b2) vmean
 // and the row scales that divide by sqrt(V) and keep the update's Frobenius norm
-void launch_normuon_rowstats(const float* x, int rows, int cols, bool transposed, float* vmean, hipStream_t st);
+// (ws: normuon_ws_bytes(rows) bytes, used for transposed stores)
+size_t normuon_ws_bytes(int max_rows);
+void launch_normuon_rowstats(const float* x, int rows, int cols, bool transposed, float* vmean, void* ws,
+                             hipStream_t st);
 void launch_normuon_scale(const float* vmean, float* V, const long* roff, int nmat, float beta2, float* scale,
                           hipStream_t st);
 
