@@ -532,7 +532,7 @@ void gpt_free(gpt_model* M) {
   delete M;
 }
 
-// Linear weights as GEMM operands: index w = 4l + {0: Wqkv [3d][d], 1: Wo, 2: W1, 3: W2}, w = 4L: U.
+// Linear weights as GEMM operands: index w = 4l + {0: Wqkv [d + 2 kv_dim][d], 1: Wo, 2: W1, 3: W2}, w = 4L: U.
 struct WInfo {
   size_t off;  // element offset inside the (blocks | U) part of the tensor table
   int rows, cols;

@@ -504,7 +504,7 @@ def test_full_gradient_vs_torch_autograd(extras):
     tp = [torch.from_numpy(w.copy()).requires_grad_() for w in params]
     tl = _torch_loss(tp, tok, tgt, cfg)
     tl.backward()
-    assert loss == pytest.approx(float(tl), rel=1e-12)
+    assert loss == pytest.approx(tl.item(), rel=1e-12)
     for g, t in zip(grads, tp):
         rel = np.linalg.norm(g - t.grad.numpy()) / np.linalg.norm(t.grad.numpy())
         assert rel < 1e-10
