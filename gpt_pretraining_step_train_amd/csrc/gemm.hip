@@ -1038,13 +1038,13 @@ void launch_dma_f16(const GemmArgs& p, hipStream_t st) {
   const int tiles = (p.sym && p.M == p.N) ? tM * (tM + 1) / 2 : tM * ((p.N + 255) / 256);
   dim3 grid(tiles, p.batch), block(512);
   if (p.a_kmaj && p.b_kmaj)
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, true, false, 32, 4, true>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, true, false, 64, 2, true>), grid, block, 0, st, p);
   else if (p.a_kmaj && !p.b_kmaj)
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, false, false, 32, 4, true>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<true, false, false, 64, 2, true>), grid, block, 0, st, p);
   else if (!p.a_kmaj && !p.b_kmaj)
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, false, false, 32, 4, true>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, false, false, 64, 2, true>), grid, block, 0, st, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, true, false, 32, 4, true>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<false, true, false, 64, 2, true>), grid, block, 0, st, p);
 }
 
 template <int BK, int S>
@@ -1186,9 +1186,9 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     else if (p.tile == 3)
       launch_dma<32, 3>(p, st);
     else if (p.tile == 5)
-      launch_dma<64, 2>(p, st);
-    else
       launch_dma<32, 4>(p, st);
+    else
+      launch_dma<64, 2>(p, st);
   } else {
     launch_f32(p, st);
   }

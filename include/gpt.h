@@ -219,8 +219,9 @@ int gpt_prof_read(gpt_model* m, int64_t* launches, double* ms, double* flops);
 
 /* C[b][m][n] (fp32) = sum_k A(m,k) B(n,k) for b < batch, where A(m,k) =
  * A[m*lda+k] if a_kmaj else A[k*lda+m], and likewise B.  Element strides
- * between batches sA, sB, sC.  tile (bf16): 0 auto, 1 = 256x256 (four LDS
- * stages), 3 = 256x256 (three stages), 4 = 256x256 register-staged, 2 = 128x128;
+ * between batches sA, sB, sC.  tile (bf16): 0 auto, 1 = 256x256 (k tiles of 64
+ * in two LDS stages), 3 = 256x256 (k tiles of 32, three stages), 5 = 256x256 (k
+ * tiles of 32, four stages), 4 = 256x256 register-staged, 2 = 128x128;
  * adding 16 declares C symmetric (M == N and A, B such that C[m][n] = C[n][m]):
  * the 256x256 kernels then compute the upper tiles and mirror them.
  * splits > 1 splits K and needs ws of splits*batch*M*N*4 bytes. */

@@ -41,8 +41,8 @@ GEMM_CASES = [
     ("bf16", 0, 1, 136, 300, 72, 1, 2, 1),
     ("bf16", 1, 1, 256, 384, 128, 3, 2, 1),
     ("bf16", 0, 0, 136, 200, 1032, 1, 2, 3),
-    # 256x256 direct-to-LDS kernel (tile 1: k tiles of 32 in 4 stages, tile 3: in 3 stages,
-    # tile 5: k tiles of 64 in 2 stages)
+    # 256x256 direct-to-LDS kernel (tile 1: k tiles of 64 in 2 stages, tile 3: k tiles of
+    # 32 in 3 stages, tile 5: k tiles of 32 in 4 stages)
     # and the register-staged 256x256 kernel (tile 4)
     ("bf16", 1, 1, 520, 264, 200, 1, 3, 1),
     ("bf16", 1, 0, 512, 520, 256, 1, 3, 1),
