@@ -517,15 +517,27 @@ gemm_bf16_dma_kernel(GemmArgs p) {
     const bool full = it_k0 + BK <= kend;  // no k tail inside this tile
     const uint32_t ka = (uint32_t)(AK ? it_k0 * 2 : (long)it_k0 * p.lda * 2);
     const uint32_t kb = (uint32_t)(BKM ? it_k0 * 2 : (long)it_k0 * p.ldb * 2);
+    if (live && full) {
+      // the whole k tile is in range (a wave-uniform test, so no per-lane branches):
+      // a row past M (N) starts past the end of its buffer and reads zeros, and an
+      // MN-major chunk past M (N) only feeds outputs that are never stored
 #pragma unroll
-    for (int j = 0; j < OA::PER; ++j) {
-      const bool ok = live && aok[j] && (full || it_k0 + ak_in[j] < kend);
-      lds_dma16(ra, lds0 + ABASE + st * OA::BYTES + (j * 8 + wave) * 1024, ok ? aoff[j] + ka : OOB);
-    }
+      for (int j = 0; j < OA::PER; ++j)
+        lds_dma16(ra, lds0 + ABASE + st * OA::BYTES + (j * 8 + wave) * 1024, aoff[j] + ka);
 #pragma unroll
-    for (int j = 0; j < OB::PER; ++j) {
-      const bool ok = live && bok[j] && (full || it_k0 + bk_in[j] < kend);
-      lds_dma16(rb, lds0 + BBASE + st * OB::BYTES + (j * 8 + wave) * 1024, ok ? boff[j] + kb : OOB);
+      for (int j = 0; j < OB::PER; ++j)
+        lds_dma16(rb, lds0 + BBASE + st * OB::BYTES + (j * 8 + wave) * 1024, boff[j] + kb);
+    } else {
+#pragma unroll
+      for (int j = 0; j < OA::PER; ++j) {
+        const bool ok = live && aok[j] && (full || it_k0 + ak_in[j] < kend);
+        lds_dma16(ra, lds0 + ABASE + st * OA::BYTES + (j * 8 + wave) * 1024, ok ? aoff[j] + ka : OOB);
+      }
+#pragma unroll
+      for (int j = 0; j < OB::PER; ++j) {
+        const bool ok = live && bok[j] && (full || it_k0 + bk_in[j] < kend);
+        lds_dma16(rb, lds0 + BBASE + st * OB::BYTES + (j * 8 + wave) * 1024, ok ? boff[j] + kb : OOB);
+      }
     }
     ++it_t;
     it_k0 += BK;
