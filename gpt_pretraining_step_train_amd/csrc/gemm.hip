@@ -594,17 +594,20 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 
   bf16x8_t af[2][FM], bf[2][FN];
   if constexpr (S == 2) {
-    // two stages: tile t+1 is issued right after the barrier that opens tile t
+    // two stages, two tiles in flight: before the last k slice of tile t the block
+    // syncs (tile t+1 has landed, and every wave holds tile t's last fragments in
+    // registers, so tile t's stage is free), issues tile t+2 into that stage and loads
+    // tile t+1's first fragments under the last slice's MFMAs
     issue(0);
+    issue(1);
+    dma_sync<LPT>();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = frag(afo[i][0], OA::BYTES, 0, AK);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[0][j] = frag(bfo[j][0], OB::BYTES, 0, BKM);
     for (int t0 = 0; t0 < nkp; t0 += 2) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        dma_sync<0>();  // tile t landed everywhere; every wave is done with tile t-1
-        issue(u ^ 1);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[0][i] = frag(afo[i][0], OA::BYTES, u, AK);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bf[0][j] = frag(bfo[j][0], OB::BYTES, u, BKM);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           const int c = kk & 1;
@@ -613,6 +616,13 @@ gemm_bf16_dma_kernel(GemmArgs p) {
             for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(afo[i][kk + 1], OA::BYTES, u, AK);
 #pragma unroll
             for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(bfo[j][kk + 1], OB::BYTES, u, BKM);
+          } else {
+            dma_sync<0>();
+            issue(u);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[c ^ 1][i] = frag(afo[i][0], OA::BYTES, u ^ 1, AK);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(bfo[j][0], OB::BYTES, u ^ 1, BKM);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -801,11 +811,19 @@ gemm_fp8_dma_kernel(GemmArgs p) {
   int it_t = 0, it_k0 = kbeg;
   auto issue = [&](int st) {
     const bool live = it_t < nk, full = it_k0 + BKB <= kend;
+    if (live && full) {  // whole k tile: rows past M (N) start past their buffer's end
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool kok = live && (full || it_k0 + kin[j] < kend);
-      lds_dma16(rA, lds0 + ABASE + st * OBYTES + (j * 8 + wave) * 1024, kok && aok[j] ? aoff[j] + it_k0 : OOB);
-      lds_dma16(rB, lds0 + BBASE + st * OBYTES + (j * 8 + wave) * 1024, kok && bok[j] ? boff[j] + it_k0 : OOB);
+      for (int j = 0; j < PER; ++j) {
+        lds_dma16(rA, lds0 + ABASE + st * OBYTES + (j * 8 + wave) * 1024, aoff[j] + it_k0);
+        lds_dma16(rB, lds0 + BBASE + st * OBYTES + (j * 8 + wave) * 1024, boff[j] + it_k0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const bool kok = live && (full || it_k0 + kin[j] < kend);
+        lds_dma16(rA, lds0 + ABASE + st * OBYTES + (j * 8 + wave) * 1024, kok && aok[j] ? aoff[j] + it_k0 : OOB);
+        lds_dma16(rB, lds0 + BBASE + st * OBYTES + (j * 8 + wave) * 1024, kok && bok[j] ? boff[j] + it_k0 : OOB);
+      }
     }
     ++it_t;
     it_k0 += BKB;
