@@ -202,7 +202,8 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   constexpr int BQ = 32 * NW, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int nqb = (T + BQ - 1) / BQ;
   const int G = H / Hkv;
   int bx, bh;
@@ -379,7 +380,8 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
   constexpr int BQ = 128, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int nqb = (T + BQ - 1) / BQ;
   const int Gq = H / Hkv;
   int bx, bh;
@@ -521,7 +523,8 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
   __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
   __shared__ __attribute__((aligned(16))) float Ps[2][4][4][64][4];  // [half][key wave][reg/4][lane][reg%4]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const bool dk_role = wave >= 4;
   const int kw = wave & 3;
   int kb, bk;
