@@ -92,11 +92,12 @@ struct TileLoader {
 };
 
 // map a linear workgroup id onto (tile_m, tile_n): XCD-contiguous ranges, grouped rows
+// (groups of 4 tile rows: the d24 step ran 1.5% faster than with 8, 2% faster than 16)
 __device__ inline void tile_coords(int lin, int tilesM, int tilesN, int& tm, int& tn) {
   const int total = tilesM * tilesN;
   int id = lin;
   if ((total & 7) == 0) id = (lin & 7) * (total >> 3) + (lin >> 3);
-  constexpr int G = 8;
+  constexpr int G = 4;
   const int per_group = G * tilesN;
   const int group = id / per_group;
   const int first = group * G;
