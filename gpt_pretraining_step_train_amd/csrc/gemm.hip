@@ -1123,15 +1123,15 @@ int splits_for(const GemmArgs& p, int tm, int tn) {
 // of the splits' fp32 partials, with at least 1024 of K per split; ties go to fewer
 // splits.  A last round that is almost empty costs as much as a full one, so e.g. 36
 // tiles take 7 splits (one round), not 16 (three rounds).  The partials (written by
-// the GEMM, read by the reduction: 8 bytes per output element and split at ~5 TB/s)
-// cost about 5.2e-5 of a k step of a bf16 tile round (~31 ns) per output element and
-// split, twice that against the faster fp8 k step; measured on the d24 weight
-// gradients, whose best factors (7, 7, 5, 5) this reproduces.
+// the GEMM with nontemporal stores, read back by the reduction) cost about 1.04e-4 of
+// a k step of a bf16 tile round per output element and split, twice that against the
+// faster fp8 k step: the coefficient that ran the d24 step fastest (factors 2, 7, 5, 5
+// for the bf16 weight gradients; 2, 7, 3, 3 for e4m3), against 0.5x and 1.5x of it.
 int splits_256(const GemmArgs& p) {
   if (p.epi != EPI_LINEAR) return 1;
   constexpr long CUS = 256, KQ = 64;  // k extents are rounded to whole k tiles (<= 64)
   const long tiles = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-  const double part = (p.fp8 ? 2.0 : 1.0) * 5.2e-5 * (double)p.M * p.N * p.batch;
+  const double part = (p.fp8 ? 2.0 : 1.0) * 1.04e-4 * (double)p.M * p.N * p.batch;
   double best = -1;
   int bs = 1;
   for (int s = 1; s <= 32; ++s) {
