@@ -632,11 +632,18 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) bf[c ^ 1][j] = frag(bfo[j][0], OB::BYTES, u ^ 1, BKM);
           }
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = mma16<F16>(af[c][i], bf[c][j], acc[i][j]);
+          // one fragment read after each of the first MFMAs (0.5% per d24 step over
+          // issuing all reads ahead of the MFMAs)
+#pragma unroll
+          for (int q = 0; q < FM + FN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
