@@ -1043,6 +1043,23 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
   }
 }
 
+// the same with four adjacent columns per thread (N and every leading dimension and
+// stride of the outputs a multiple of 4): one row per grid row, batch along z, so no
+// index division; float4 partial loads and the vectorised epilogue
+__global__ void __launch_bounds__(128) splitk_reduce_vec_kernel(GemmArgs p) {
+  const int c4 = blockIdx.x * 128 + threadIdx.x;
+  if (c4 >= p.N / 4) return;
+  const int row = blockIdx.y, bz = blockIdx.z;
+  const long MN = (long)p.M * p.N;
+  const float* w = p.ws + (long)bz * p.splits * MN + (long)row * p.N + 4 * c4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < p.splits; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(w + k * MN);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  epilogue_vec4(p, bz, row, 4 * c4, s);
+}
+
 template <int BM, int BN, int WM, int WN, bool SPLIT>
 void launch_bf16_s(const GemmArgs& p, hipStream_t st) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -1242,7 +1259,12 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
   if (p.splits > 1) {
     const long total = (long)p.M * p.N * p.batch;
     const int blocks = (int)std::min<long>((total + 255) / 256, 65536);
-    if (p.dtype == ACT_BF16)
+    const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
+                     (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0) && p.M <= 65535 &&
+                     p.batch <= 65535 && p.dtype == ACT_BF16;
+    if (vec)
+      hipLaunchKernelGGL(splitk_reduce_vec_kernel, dim3((p.N / 4 + 127) / 128, p.M, p.batch), dim3(128), 0, st, p);
+    else if (p.dtype == ACT_BF16)
       hipLaunchKernelGGL(splitk_reduce_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, p);
     else
       hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(blocks), dim3(256), 0, st, p);
