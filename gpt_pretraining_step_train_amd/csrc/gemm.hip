@@ -93,10 +93,10 @@ struct TileLoader {
 
 // map a linear workgroup id onto (tile_m, tile_n): XCD-contiguous ranges, grouped rows
 // (groups of 4 tile rows: the d24 step ran 1.5% faster than with 8, 2% faster than 16)
-__device__ inline void tile_coords(int lin, int tilesM, int tilesN, int& tm, int& tn) {
+__device__ inline void tile_coords(int lin, int tilesM, int tilesN, int& tm, int& tn, bool xcd = true) {
   const int total = tilesM * tilesN;
   int id = lin;
-  if ((total & 7) == 0) id = (lin & 7) * (total >> 3) + (lin >> 3);
+  if (xcd && (total & 7) == 0) id = (lin & 7) * (total >> 3) + (lin >> 3);
   constexpr int G = 4;
   const int per_group = G * tilesN;
   const int group = id / per_group;
@@ -461,16 +461,28 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   const int wm = wave / WN, wn = wave % WN;
   const int tilesM = (p.M + 255) / 256, tilesN = (p.N + 255) / 256;
   const bool sym = p.sym && p.splits == 1 && p.M == p.N;
+  // Workgroups reach the 8 XCDs round-robin in launch order.  A batched or split
+  // launch maps its linear id XCD-contiguously over the whole grid, so that one XCD
+  // works through whole matrices (splits) in turn and their panels stay in its L2.
+  int tl = blockIdx.x, yy = blockIdx.y;
+  const int nall = gridDim.x * gridDim.y;
+  const bool grid_xcd = gridDim.y > 1 && (nall & 7) == 0;
+  if (grid_xcd) {
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int id = (lin & 7) * (nall >> 3) + (lin >> 3);
+    yy = id / gridDim.x;
+    tl = id - yy * gridDim.x;
+  }
   int tm, tn;
   if (sym) {  // upper-triangular tiles, row by row
-    int id = blockIdx.x;
+    int id = tl;
     tm = 0;
     while (id >= tilesM - tm) { id -= tilesM - tm; ++tm; }
     tn = tm + id;
   } else {
-    tile_coords(blockIdx.x, tilesM, tilesN, tm, tn);
+    tile_coords(tl, tilesM, tilesN, tm, tn, !grid_xcd);
   }
-  const int bz = blockIdx.y / p.splits, sk = blockIdx.y % p.splits;
+  const int bz = yy / p.splits, sk = yy % p.splits;
   const int m0 = tm * 256, n0 = tn * 256;
   const int kper = ((p.K + p.splits - 1) / p.splits + BK - 1) / BK * BK;
   const int kbeg = sk * kper;
@@ -719,7 +731,7 @@ _Pragma("unroll") \
       if (row >= p.M) break; \
       const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc); \
       if (p.splits > 1) { \
-        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col; \
+        float* w = p.ws + ((long)yy * p.M + row) * p.N + col; \
         if (vec && col + 3 < p.N) { \
           typedef float f4v __attribute__((ext_vector_type(4))); \
           f4v x_ = {a.x, a.y, a.z, a.w}; \
