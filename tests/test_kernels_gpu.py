@@ -60,6 +60,11 @@ GEMM_CASES = [
     ("bf16", 0, 0, 136, 200, 1032, 1, 5, 3),
     ("bf16", 1, 1, 520, 264, 200, 1, 4, 1),
     ("bf16", 0, 0, 264, 528, 520, 1, 4, 1),
+    # batched / split-K launches of a multiple of 8 workgroups: the grid-wide XCD order
+    # (6 tiles x batch 4, x 4 splits with a ragged last split, x batch 2 x 2 splits)
+    ("bf16", 1, 1, 520, 264, 200, 4, 1, 1),
+    ("bf16", 0, 0, 264, 528, 2080, 1, 1, 4),
+    ("bf16", 1, 0, 264, 528, 1040, 2, 1, 2),
     ("fp32", 1, 1, 100, 70, 33, 1, 0, 1),
     ("fp32", 1, 0, 96, 72, 40, 2, 0, 1),
     ("fp32", 0, 0, 72, 96, 200, 1, 0, 2),
@@ -93,6 +98,7 @@ def test_gemm_layouts_tails_batch_split(case):
 SYM_CASES = [  # a_kmaj, M, K, batch, tile (+16: symmetric hint), splits
     (1, 520, 200, 2, 17, 1), (0, 264, 136, 1, 17, 1), (1, 1000, 64, 1, 19, 1), (1, 1002, 96, 1, 17, 1),
     (1, 520, 2048, 1, 17, 2), (1, 300, 72, 3, 18, 1), (1, 520, 200, 2, 21, 1), (0, 264, 136, 1, 21, 1),
+    (1, 520, 200, 4, 17, 1), (0, 264, 136, 8, 17, 1),  # 24 upper tiles in all: grid-wide XCD order
 ]
 
 
