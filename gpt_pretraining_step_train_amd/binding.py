@@ -67,6 +67,9 @@ _SIGS = {
     "gpt_prof_enable": (_I, [_P, ctypes.c_char_p]),
     "gpt_prof_read": (_I, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)]),
+    "gpt_capture_bytes": (_SZ, [ctypes.POINTER(GptCfg), ctypes.c_int32]),
+    "gpt_capture": (_I, [_P, ctypes.c_int32, _P, _SZ]),
+    "gptk_gemm_auto_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
     "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _L, _L, _P, _L, _L, _P]),
     "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
@@ -250,6 +253,43 @@ class Model:
         check(lib().gpt_row_loss(self._h, _ptr(out), _stream()), "gpt_row_loss")
         return out
 
+    # names and element types of gpt_capture's items, in buffer order
+    CAPTURE_BLOCK = [("a", "act", "d"), ("qkv", "act", "QD"), ("x", "f32", "d"), ("o", "act", "d"),
+                     ("h1", "f32", "d"), ("m", "act", "d"), ("u", "act", "F"), ("g", "act", "F"), ("h2", "f32", "d"),
+                     ("dh", "act", "d"), ("du", "act", "F"), ("dm", "f32", "d"), ("dh1", "act", "d"),
+                     ("do", "act", "d"), ("dqkv", "act", "QD"), ("da", "f32", "d")]
+    CAPTURE_HEAD = [("r", "act", "d"), ("logits", "f32", "V"), ("dlogits", "act", "V"), ("dr", "f32", "d")]
+
+    def capture_step(self, layer, tokens, targets):
+        """Run gpt_step with gpt_capture on `layer` (depth = the LM head) and return
+        (loss, {name: float64 numpy array [N][cols]}) of the captured items."""
+        import torch
+        nbytes = lib().gpt_capture_bytes(ctypes.byref(self.cfg), layer)
+        if nbytes == 0:
+            raise GptError(f"gpt_capture_bytes: invalid layer {layer}")
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.arena.device)
+        off = (-buf.data_ptr()) % 256
+        check(lib().gpt_capture(self._h, layer, ctypes.c_void_p(buf.data_ptr() + off), nbytes), "gpt_capture")
+        try:
+            loss = self.step(tokens, targets)
+            torch.cuda.synchronize()
+        finally:
+            check(lib().gpt_capture(self._h, 0, None, 0), "gpt_capture")
+        c = self.cfg
+        N = c.batch * c.seq_len
+        kv = (c.n_kv_head or c.n_head) * c.head_dim
+        width = {"d": c.d_model, "F": c.d_ff, "V": c.vocab, "QD": c.d_model + 2 * kv}
+        act16 = c.precision != GPT_FP32
+        out, pos = {}, off
+        for name, kind, w in (self.CAPTURE_HEAD if layer == c.depth else self.CAPTURE_BLOCK):
+            n = N * width[w]
+            es = 2 if (kind == "act" and act16) else 4
+            raw = buf[pos:pos + n * es]
+            t = raw.view(torch.bfloat16) if es == 2 else raw.view(torch.float32)
+            out[name] = t.float().cpu().numpy().astype(np.float64).reshape(N, width[w])
+            pos += (n * es + 255) // 256 * 256
+        return loss, out
+
     def prof_enable(self, name):
         check(lib().gpt_prof_enable(self._h, name.encode() if name else None), "gpt_prof_enable")
 
@@ -287,6 +327,10 @@ def gemm_fp8(M, N, K, A, lda, B, ldb, dq_a, dq_b, C, ldc, splits=1, ws=None):
     ws_b = ws.numel() * ws.element_size() if ws is not None else 0
     check(lib().gptk_gemm_fp8(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(dq_a), _ptr(dq_b), _ptr(C), ldc, splits, ws_p,
                               ws_b, _stream()), "gptk_gemm_fp8")
+
+
+def gemm_auto_splits(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> int:
+    return lib().gptk_gemm_auto_splits(dtype, int(a_kmaj), int(b_kmaj), M, N, K, batch)
 
 
 def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:

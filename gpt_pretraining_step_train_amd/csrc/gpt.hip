@@ -220,6 +220,32 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   return O;
 }
 
+// Operand capture (gpt_capture): the slots of one block layer's four Linear products,
+// or of the LM head, in byte sizes; each slot starts 256-byte aligned in the buffer.
+enum {
+  CAP_A, CAP_QKV, CAP_HIN, CAP_O, CAP_H1, CAP_M, CAP_U, CAP_G, CAP_H2,   // forward
+  CAP_DY2, CAP_DU, CAP_DM, CAP_DYO, CAP_DO, CAP_DQKV, CAP_DA,           // backward
+  CAP_BLOCK_SLOTS
+};
+enum { CAP_R, CAP_LOGITS, CAP_DLOGITS, CAP_DR, CAP_HEAD_SLOTS };
+std::vector<size_t> capture_sizes(const gpt_cfg& c, int layer) {
+  const size_t N = (size_t)c.batch * c.seq_len, d = c.d_model, F = c.d_ff, V = c.vocab, QD = qkv_dim(c);
+  const size_t es = act_of(c) == ACT_BF16 ? 2 : 4;
+  if (layer == c.depth) return {N * d * es, N * V * 4, N * V * es, N * d * 4};
+  return {N * d * es, N * QD * es, N * d * 4, N * d * es, N * d * 4, N * d * es, N * F * es, N * F * es, N * d * 4,
+          N * d * es, N * F * es, N * d * 4, N * d * es, N * d * es, N * QD * es, N * d * 4};
+}
+size_t capture_offset(const gpt_cfg& c, int layer, int slot, size_t* total = nullptr) {
+  const std::vector<size_t> sz = capture_sizes(c, layer);
+  size_t o = 0, at = 0;
+  for (size_t i = 0; i < sz.size(); ++i) {
+    if ((int)i == slot) at = o;
+    o += al256(sz[i]);
+  }
+  if (total) *total = o;
+  return at;
+}
+
 }  // namespace
 
 struct gpt_model {
@@ -240,6 +266,9 @@ struct gpt_model {
   long adam_t = 0;       // AdamW steps taken (bias corrections use the next one)
   bool acc_grads = false;  // the current step adds its gradients to the stored ones
   std::vector<int> xslot;  // per weight: quantisation slot of its input in this step's forward
+  // operand capture of one layer's Linear products for stage-isolated checks (gpt_capture)
+  char* cap_buf = nullptr;
+  int cap_layer = -1;
   // matrix table for Muon, in layer order (q, k, v, o, w1, w2); the first row of each
   // matrix in the stacked per-row NorMuon vectors (6L + 1 entries)
   std::vector<long> moff, msize, nm_roff;
@@ -677,6 +706,15 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   float* xpart = M->at_off<float>(O.xpart);  // [2L+26][N] per-row terms of dS
   // the stream layer l adds its blocks to (its mixed input under residual scaling)
   auto xres = [&](int l) { return ex_resid ? M->at_off<float>(O.hx) + (size_t)l * N * d : hsl(2 * l); };
+  // gpt_capture: copies of one layer's Linear operands and results, for stage-isolated checks
+  bool cap_failed = false;
+  auto cap = [&](int layer, int slot, const void* src) {
+    if (!M->cap_buf || layer != M->cap_layer) return;
+    const size_t bytes = capture_sizes(c, layer)[slot];
+    if (hipMemcpyAsync(M->cap_buf + capture_offset(c, layer, slot), src, bytes, hipMemcpyDeviceToDevice, st) !=
+        hipSuccess)
+      cap_failed = true;
+  };
 
   launch_zero(err, 16, st);
   if (M->fp8) {
@@ -707,17 +745,21 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
                              M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
     else
       launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
+    cap(l, CAP_A, a);
+    cap(l, CAP_HIN, xres(l));
     {
       GemmArgs p;  // qkv = a Wqkv^T
       p.M = N; p.N = QD; p.K = d; p.A = a; p.lda = d;
       p.outA = qkv; p.ldoa = QD;
       if ((rc = lin_fwd(M, p, 4 * l + 0, st))) return rc;
     }
+    cap(l, CAP_QKV, qkv);
     if (ex_ve)  // v += 3 sigmoid(gate) VE[token]
       launch_ve_fwd(qkv, at, a, tok, ve_tab(M->params(), l), ve_gate(M->params(), l), ve_g(l), N, V, H, Hkv, hd, d,
                     st);
     launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, eps, st);
     launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st);
+    cap(l, CAP_O, o);
     {
       GemmArgs p;  // h' = h + o Wo^T
       p.M = N; p.N = d; p.K = d; p.A = o; p.lda = d;
@@ -725,13 +767,17 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       p.outF = hsl(2 * l + 1); p.ldo = d;
       if ((rc = lin_fwd(M, p, 4 * l + 1, st))) return rc;
     }
+    cap(l, CAP_H1, hsl(2 * l + 1));
     launch_rmsnorm_fwd(hsl(2 * l + 1), m, at, M->at_off<float>(O.rstd_m) + (size_t)l * N, N, d, eps, st);
+    cap(l, CAP_M, m);
     {
       GemmArgs p;  // u = m W1^T, g = relu(u)^2
       p.M = N; p.N = F; p.K = d; p.A = m; p.lda = d;
       p.epi = EPI_RELU2; p.outA = u; p.out2 = g; p.ldoa = F;
       if ((rc = lin_fwd(M, p, 4 * l + 2, st))) return rc;
     }
+    cap(l, CAP_U, u);
+    cap(l, CAP_G, g);
     {
       GemmArgs p;  // h'' = h' + g W2^T
       p.M = N; p.N = d; p.K = F; p.A = g; p.lda = F;
@@ -739,6 +785,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       p.outF = hsl(2 * l + 2); p.ldo = d;
       if ((rc = lin_fwd(M, p, 4 * l + 3, st))) return rc;
     }
+    cap(l, CAP_H2, hsl(2 * l + 2));
   }
   void* r = M->base + O.r;
   if (ex_back)  // the final norm reads x_L - lb x_mid
@@ -746,6 +793,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
                            M->at_off<float>(O.rstd_f), N, d, eps, st);
   else
     launch_rmsnorm_fwd(hsl(2 * L), r, at, M->at_off<float>(O.rstd_f), N, d, eps, st);
+  cap(L, CAP_R, r);
   float* logits = M->at_off<float>(O.logits);
   void* dlogits = M->base + O.dlogits;
   {
@@ -754,10 +802,12 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     p.outF = logits; p.ldo = V;
     if ((rc = lin_fwd(M, p, 4 * L, st))) return rc;
   }
+  cap(L, CAP_LOGITS, logits);
   // the whole backward is linear in dlogits: grad_scale / N there scales every gradient
   launch_cross_entropy(logits, tgt, dlogits, at, M->at_off<float>(O.row_loss), M->at_off<int32_t>(O.argmax), N, V,
                        grad_scale / (float)N, err, st);
   launch_sum_rows(M->at_off<float>(O.row_loss), N, M->at_off<double>(O.loss), st);
+  cap(L, CAP_DLOGITS, dlogits);
 
   // ---------------- backward
   float* dtmp = M->at_off<float>(O.dtmp);
@@ -772,6 +822,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     pd.outF = dtmp; pd.ldo = d;
     if ((rc = lin_bwd(M, dlogits, V, r, d, 4 * L, grads + M->nE + M->nBlk, pd, st))) return rc;
   }
+  cap(L, CAP_DR, dtmp);
   float* dmid = M->at_off<float>(O.dmid);  // d loss / d x_mid through the backout term
   float* dx0 = M->at_off<float>(O.dx0);    // d loss / d x0 through the l0 terms of layers 1..L-1
   if (ex_back) {
@@ -796,38 +847,45 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
     float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
+    cap(l, CAP_DY2, dh_act);
     {
       GemmArgs pd;  // dW2 = dY^T g ; du = (dY W2) * 2 relu(u)
       pd.M = N; pd.N = F; pd.K = d;
       pd.epi = EPI_DRELU2; pd.aux = u; pd.outA = dbig; pd.ldoa = F;
       if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st))) return rc;
     }
+    cap(l, CAP_DU, dbig);
     {
       GemmArgs pd;  // dW1 = du^T m ; dm = du W1
       pd.M = N; pd.N = d; pd.K = F;
       pd.outF = dtmp; pd.ldo = d;
       if ((rc = lin_bwd(M, dbig, F, m, d, 4 * l + 2, gblk + wl + M->lo.w1, pd, st))) return rc;
     }
+    cap(l, CAP_DM, dtmp);
     launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur], dh[cur ^ 1],
                        dh_act, at, N, d, eps, st);
     cur ^= 1;
+    cap(l, CAP_DYO, dh_act);
     {
       GemmArgs pd;  // dWo = dY^T o ; do = dY Wo
       pd.M = N; pd.N = d; pd.K = d;
       pd.outA = do_act; pd.ldoa = d;
       if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st))) return rc;
     }
+    cap(l, CAP_DO, do_act);
     launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, Hkv, hd, c.attn_window, st);
     if (ex_ve)  // dVE rows, the gate's dz and the rows of d(gate weights), from dv
       launch_ve_bwd(dqkv, at, a, tok, ve_tab(M->params(), l), ve_g(l), M->at_off<float>(O.dve),
                     M->at_off<float>(O.vdz), M->at_off<float>(O.vpart), N, V, H, Hkv, hd, d, st);
     launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, st);
+    cap(l, CAP_DQKV, dqkv);
     {
       GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
       pd.M = N; pd.N = d; pd.K = QD;
       pd.outF = dtmp; pd.ldo = d;
       if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
     }
+    cap(l, CAP_DA, dtmp);
     if (ex_ve) {  // the gate's path into the block input; the table's and gates' gradients
       launch_ve_da(dtmp, M->at_off<float>(O.vdz), ve_gate(M->params(), l), N, Hkv, d, st);
       launch_embed_scatter_sorted(tok, M->at_off<float>(O.dve), ve_tab(grads, l), N, V, (int)kvd, M->base + O.embws,
@@ -862,7 +920,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     launch_embed_scatter(tok, dh[cur], grads, N, V, d, M->base + O.embws, nullptr, st, M->acc_grads);
   if (c.extras)
     launch_extras_reduce(xpart, N, L, c.extras, grads + M->nE + M->nBlk + M->nU, M->acc_grads, st);
-  return GPT_OK;
+  return cap_failed ? GPT_ERR_HIP : GPT_OK;
 }
 
 float gpt_step(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg, void* stream) {
@@ -1139,10 +1197,54 @@ int gpt_prof_read(gpt_model* M, int64_t* launches, double* ms, double* flops) {
   return GPT_OK;
 }
 
+size_t gpt_capture_bytes(const gpt_cfg* c, int32_t layer) {
+  if (gpt_cfg_validate(c) != GPT_OK || layer < 0 || layer > c->depth) return 0;
+  size_t total = 0;
+  capture_offset(*c, layer, -1, &total);
+  return total;
+}
+
+int gpt_capture(gpt_model* M, int32_t layer, void* d_buf, size_t bytes) {
+  if (!M) return GPT_ERR_ARG;
+  if (!d_buf) {
+    M->cap_buf = nullptr;
+    M->cap_layer = -1;
+    return GPT_OK;
+  }
+  if (layer < 0 || layer > M->cfg.depth || bytes < gpt_capture_bytes(&M->cfg, layer) || ((uintptr_t)d_buf & 255))
+    return GPT_ERR_ARG;
+  M->cap_buf = (char*)d_buf;
+  M->cap_layer = layer;
+  return GPT_OK;
+}
+
 // ---------------------------------------------------------------------------
 // kernel-level entry points
 
 static int act_type(int dtype) { return dtype == GPT_FP32 ? ACT_F32 : dtype == GPT_BF16 ? ACT_BF16 : -1; }
+
+// Leading dimensions cover one row of each stored matrix (A(m,k) = A[m lda + k] when
+// k-major, A[k lda + m] otherwise), and batch strides are non-negative and cover one
+// whole matrix (0 shares an operand between the batch entries; never the output's).
+static bool gemm_layout_ok(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, long lda, long sA, long ldb,
+                           long sB, long ldc, long sC) {
+  if (M == 0 || N == 0 || batch == 0) return true;  // nothing is read or written
+  if (lda < (a_kmaj ? K : M) || lda < 1 || ldb < (b_kmaj ? K : N) || ldb < 1 || ldc < N) return false;
+  if (batch > 1) {
+    const long ea = (long)(a_kmaj ? M : K) * lda, eb = (long)(b_kmaj ? N : K) * ldb, ec = (long)M * ldc;
+    if (sA < 0 || sB < 0 || (sA && sA < ea) || (sB && sB < eb) || sC < ec) return false;
+  }
+  return true;
+}
+
+int gptk_gemm_auto_splits(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch) {
+  const int at = act_type(dtype);
+  if (at < 0 || M < 0 || N < 0 || K < 0 || batch < 0) return 0;
+  GemmArgs p;
+  p.M = M; p.N = N; p.K = K; p.batch = batch; p.dtype = at;
+  p.a_kmaj = a_kmaj != 0; p.b_kmaj = b_kmaj != 0;
+  return gemm_auto_splits(p);
+}
 
 int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* A, long lda, long sA,
               const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits, void* ws,
@@ -1150,13 +1252,16 @@ int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch,
   const int at = act_type(dtype);
   if (at < 0) return GPT_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || batch < 0 || !C) return GPT_ERR_ARG;
+  if (!gemm_layout_ok(a_kmaj, b_kmaj, M, N, K, batch, lda, sA, ldb, sB, ldc, sC)) return GPT_ERR_ARG;
   GemmArgs p;
   p.M = M; p.N = N; p.K = K; p.batch = batch;
   p.A = A; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
   p.B = B; p.ldb = ldb; p.strideB = sB; p.b_kmaj = b_kmaj != 0;
   p.dtype = at; p.outF = C; p.ldo = ldc; p.strideO = sC;
   p.tile = tile & 15; p.sym = (tile & 16) != 0;
-  p.splits = splits < 1 ? 1 : splits; p.ws = (float*)ws; p.ws_bytes = ws_bytes;
+  p.splits = splits < 0 ? gemm_auto_splits(p) : splits < 1 ? 1 : splits;
+  p.ws = (float*)ws; p.ws_bytes = ws_bytes;
+  if ((long)p.batch * p.splits > 65535) return GPT_ERR_ARG;  // grid rows
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc == 1) return GPT_ERR_ARG;
   if (rc == 2) return GPT_ERR_SHAPE;
@@ -1167,6 +1272,7 @@ int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, cons
                     long sA, const void* Bh, const void* Bl, long ldb, long sB, float* C, long ldc, long sC,
                     void* stream) {
   if (M < 0 || N < 0 || K < 0 || batch < 0 || !C || !Ah || !Al || !Bh || !Bl) return GPT_ERR_ARG;
+  if (!gemm_layout_ok(a_kmaj, b_kmaj, M, N, K, batch, lda, sA, ldb, sB, ldc, sC) || batch > 65535) return GPT_ERR_ARG;
   GemmArgs p;
   p.M = M; p.N = N; p.K = K; p.batch = batch; p.split = true; p.dtype = ACT_BF16;
   p.A = Ah; p.A_lo = Al; p.lda = lda; p.strideA = sA; p.a_kmaj = a_kmaj != 0;
@@ -1192,6 +1298,7 @@ int gptk_quant_e4m3(int dtype, const void* x, int rows, int cols, long ld, uint3
 int gptk_gemm_fp8(int M, int N, int K, const uint8_t* A, long lda, const uint8_t* B, long ldb, const float* dq_a,
                   const float* dq_b, float* C, long ldc, int splits, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0 || !A || !B || !dq_a || !dq_b || !C) return GPT_ERR_ARG;
+  if (!gemm_layout_ok(1, 1, M, N, K, 1, lda, 0, ldb, 0, ldc, 0) || splits > 65535) return GPT_ERR_ARG;
   GemmArgs p;
   p.M = M; p.N = N; p.K = K; p.fp8 = true; p.dtype = ACT_BF16;
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.dq_a = dq_a; p.dq_b = dq_b;

@@ -210,6 +210,29 @@ void gpt_free(gpt_model* m);
 int gpt_prof_enable(gpt_model* m, const char* name);
 int gpt_prof_read(gpt_model* m, int64_t* launches, double* ms, double* flops);
 
+/* Operand capture for stage-isolated checks of the Linear products (the QKV, output,
+ * fc and proj projections of a block, each Y = X W^T with dW = dY^T X and dX = dY W,
+ * and the LM head).  With d_buf non-NULL (device memory, 256-byte aligned, at least
+ * gpt_capture_bytes(cfg, layer) bytes, owned by the caller and kept alive while set),
+ * every later gpt_step copies what layer `layer` (0 <= layer < depth) or, with layer ==
+ * depth, the LM head feeds to and gets from its GEMMs into d_buf, each item starting
+ * on a 256-byte boundary in this order ("act" = the step's activation type, bf16 or
+ * fp32; N = batch*seq_len, QD = d + 2 n_kv_head head_dim):
+ *   block layer: a [N][d] act (QKV input), qkv [N][QD] act (QKV output, before RoPE /
+ *     QK-norm / value embeddings), x [N][d] fp32 (the residual stream the layer adds to),
+ *     o [N][d] act (output-projection input), h1 [N][d] fp32 (= x + o Wo^T), m [N][d] act,
+ *     u [N][F] act (= m W1^T), g [N][F] act (= relu(u)^2), h2 [N][d] fp32 (= h1 + g W2^T);
+ *     backward: dh [N][d] act (proj output gradient), du [N][F] act (= (dh W2) 2 relu(u)),
+ *     dm [N][d] fp32 (= du W1), dh1 [N][d] act (output-projection output gradient),
+ *     do [N][d] act (= dh1 Wo), dqkv [N][QD] act (QKV output gradient), da [N][d] fp32
+ *     (= dqkv [Wq; Wk; Wv]);
+ *   LM head: r [N][d] act, logits [N][V] fp32, dlogits [N][V] act, dr [N][d] fp32.
+ * The weight gradients are the ones gpt_grads returns.  d_buf == NULL switches the
+ * capture off.  GPT_ERR_ARG for a layer out of range, a short or misaligned buffer.
+ * gpt_capture_bytes returns 0 for an invalid cfg or layer. */
+size_t gpt_capture_bytes(const gpt_cfg* cfg, int32_t layer);
+int gpt_capture(gpt_model* m, int32_t layer, void* d_buf, size_t bytes);
+
 /* ------------------------------------------------------------------------
  * Kernel-level entry points for stage-isolated checks.  All pointers are
  * device pointers owned by the caller; `dtype` is GPT_FP32 or GPT_BF16 and
@@ -224,10 +247,20 @@ int gpt_prof_read(gpt_model* m, int64_t* launches, double* ms, double* flops);
  * tiles of 32, four stages), 4 = 256x256 register-staged, 2 = 128x128;
  * adding 16 declares C symmetric (M == N and A, B such that C[m][n] = C[n][m]):
  * the 256x256 kernels then compute the upper tiles and mirror them.
- * splits > 1 splits K and needs ws of splits*batch*M*N*4 bytes. */
+ * splits > 1 splits K and needs ws of splits*batch*M*N*4 bytes; splits < 0 takes the
+ * factor gpt_step's launches choose for this shape (gptk_gemm_auto_splits).
+ * GPT_ERR_ARG when lda (ldb) is below the stored row length (K for a k-major operand,
+ * else M (N)), ldc < N, a batch stride is negative, an input stride is neither 0 (one
+ * matrix shared by the batch) nor at least one whole matrix, the output stride is
+ * below M*ldc with batch > 1, or batch*splits > 65535; the workspace is too small; or a
+ * shape/alignment the kernels do not take (GPT_ERR_SHAPE).  Checks run before any
+ * launch. */
 int gptk_gemm(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* A, long lda,
               long sA, const void* B, long ldb, long sB, float* C, long ldc, long sC, int tile, int splits,
               void* ws, size_t ws_bytes, void* stream);
+
+/* the split-K factor gptk_gemm with splits < 0 (and gpt_step) uses for this shape */
+int gptk_gemm_auto_splits(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K, int batch);
 
 /* as gptk_gemm (bf16) with each operand given as two bf16 planes, a high part
  * (Ah, Bh) and the residual of an fp32 value (Al, Bl), same layout and strides:

@@ -43,3 +43,20 @@ def rel_l2(x, ref) -> float:
 
 def say(*a):
     print(*a, flush=True)
+
+
+def check_argmax_margin(am, z, margin):
+    """am [n] (the GPU's argmax) against the oracle's logits z [n][V]: positions whose
+    top logit leads the runner-up by more than `margin` must agree exactly (lowest index
+    on ties); elsewhere the GPU's pick must be within `margin` of the maximum.  Returns
+    (fraction of positions with a clear maximum, fraction that agree exactly)."""
+    from oracle import gpt_oracle as O
+    am = np.asarray(am).reshape(-1)
+    top2 = np.partition(z, -2, axis=-1)[:, -2:]
+    lead = top2[:, 1] - top2[:, 0]
+    unique = lead > margin
+    ref = O.argmax_lowest(z)
+    np.testing.assert_array_equal(am[unique], ref[unique])
+    picked = np.take_along_axis(z, am[:, None].astype(np.int64), -1)[:, 0]
+    assert np.all(picked >= z.max(axis=-1) - margin)
+    return float(unique.mean()), float(np.mean(am == ref))

@@ -140,3 +140,70 @@ def test_configs_flops_formula():
     # grouped-query attention shrinks Wk, Wv (and their Newton-Schulz), not attention
     g = configs.step_flops(configs.get("d24", n_kv_head=4))
     assert g["attn"] == f["attn"] and g["linear"] < f["linear"] and g["muon"] < f["muon"]
+
+
+def test_arena_too_small_is_rejected_before_any_device_call(lib):
+    """gpt_init checks the arena against gpt_state_bytes (and its alignment) before it
+    touches the device, so a short or misaligned arena is GPT_ERR_ARG on any host."""
+    c = binding.make_cfg(configs.get("laptop"))
+    need = lib.gpt_state_bytes(ctypes.byref(c))
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: the checks come first
+    out = ctypes.c_void_p()
+    assert lib.gpt_init(ctypes.byref(c), 0, fake, need - 1, None, ctypes.byref(out)) == 1
+    assert lib.gpt_init(ctypes.byref(c), 0, ctypes.c_void_p((1 << 20) + 16), need, None, ctypes.byref(out)) == 1
+    assert lib.gpt_init(ctypes.byref(c), 0, None, need, None, ctypes.byref(out)) == 1
+    assert not out.value
+    bad = binding.make_cfg(configs.get("laptop", head_dim=48))
+    assert lib.gpt_init(ctypes.byref(bad), 0, fake, need, None, ctypes.byref(out)) == 6
+
+
+def test_gemm_argument_checks_run_before_any_launch(lib):
+    """gptk_gemm rejects leading dimensions shorter than a stored row, negative or short
+    batch strides and grids beyond 65535 rows before launching anything."""
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced
+
+    def call(ak=1, bk=1, M=64, N=64, K=64, batch=1, lda=64, sA=0, ldb=64, sB=0, ldc=64, sC=0, splits=1):
+        return lib.gptk_gemm(1, ak, bk, M, N, K, batch, p, lda, sA, p, ldb, sB, p, ldc, sC, 0, splits, p, 0, None)
+    assert call(lda=63) == 1                       # k-major A needs lda >= K
+    assert call(ak=0, M=128, lda=100) == 1         # transposed A needs lda >= M
+    assert call(ldb=32) == 1
+    assert call(bk=0, N=128, ldb=64) == 1
+    assert call(ldc=63) == 1
+    assert call(batch=2, sA=-1, sC=64 * 64) == 1
+    assert call(batch=2, sA=100, sC=64 * 64) == 1  # neither shared (0) nor a whole matrix
+    assert call(batch=2, sB=64, sC=64 * 64) == 1
+    assert call(batch=2, sC=64 * 63) == 1          # outputs of two batch entries would overlap
+    assert call(batch=40000, sC=64 * 64, splits=2) == 1   # grid rows
+    assert call(M=-1) == 1
+    assert lib.gptk_gemm(7, 1, 1, 64, 64, 64, 1, p, 64, 0, p, 64, 0, p, 64, 0, 0, 1, p, 0, None) == 6
+    assert lib.gptk_gemm_fp8(64, 64, 64, p, 32, p, 64, p, p, p, 64, 1, p, 0, None) == 1
+    assert lib.gptk_gemm_split(1, 1, 64, 64, 64, 1, p, p, 64, 0, p, p, 64, 0, p, 32, 0, None) == 1
+
+
+def test_auto_split_factors_of_the_d24_weight_gradients(lib):
+    """The factors gpt_step's d24 weight-gradient launches take over K = 32768 tokens
+    (the GPU test checks those launches against fp64)."""
+    f = {(m, n): binding.gemm_auto_splits(1, m, n, 32768, 1, 0, 0)
+         for m, n in [(4608, 1536), (1536, 1536), (6144, 1536), (1536, 6144), (32768, 1536)]}
+    assert f[(4608, 1536)] == 2 and f[(1536, 1536)] == 7 and f[(6144, 1536)] == 5 and f[(1536, 6144)] == 5
+    assert f[(32768, 1536)] == 1
+
+
+def test_capture_sizes(lib):
+    """gpt_capture_bytes: 16 items of a block layer, 4 of the LM head, 256-byte aligned."""
+    cfg = configs.get("d24", batch=1)
+    c = binding.make_cfg(cfg)
+    N, d, F, V = 2048, 1536, 6144, 32768
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    QD = 3 * d
+    block = [N * d * 2, N * QD * 2, N * d * 4, N * d * 2, N * d * 4, N * d * 2, N * F * 2, N * F * 2, N * d * 4,
+             N * d * 2, N * F * 2, N * d * 4, N * d * 2, N * d * 2, N * QD * 2, N * d * 4]
+    head = [N * d * 2, N * V * 4, N * V * 2, N * d * 4]
+    assert lib.gpt_capture_bytes(ctypes.byref(c), 0) == sum(al(x) for x in block)
+    assert lib.gpt_capture_bytes(ctypes.byref(c), 23) == sum(al(x) for x in block)
+    assert lib.gpt_capture_bytes(ctypes.byref(c), 24) == sum(al(x) for x in head)
+    assert lib.gpt_capture_bytes(ctypes.byref(c), 25) == 0
+    assert lib.gpt_capture_bytes(ctypes.byref(c), -1) == 0
+    assert lib.gpt_capture(None, 0, None, 0) == 1
+    names = [n for n, _, _ in binding.Model.CAPTURE_BLOCK]
+    assert len(names) == len(block) and len(binding.Model.CAPTURE_HEAD) == len(head)

@@ -24,7 +24,7 @@ import torch
 from gpt_pretraining_step_train_amd import binding, configs, inputs
 from oracle import gpt_oracle as O
 from oracle import polar_express as PE
-from tests.gpu_util import random_extras, rel_l2, say
+from tests.gpu_util import check_argmax_margin, random_extras, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -69,13 +69,7 @@ MARGIN = 0.05  # logits at init have std ~0.8; bf16-level logit error is ~1e-2 o
 def _check_argmax(am, z):
     """Positions whose top-1 logit leads by more than MARGIN must agree exactly; at the
     others the GPU's choice must be a near-maximum of the oracle's logits."""
-    top2 = np.sort(z, axis=-1)[:, -2:]
-    unique = top2[:, 1] - top2[:, 0] > MARGIN
-    ref = O.argmax_lowest(z)
-    np.testing.assert_array_equal(am[unique], ref[unique])
-    picked = np.take_along_axis(z, am[:, None].astype(np.int64), -1)[:, 0]
-    assert np.all(picked >= top2[:, 1] - MARGIN)
-    return unique.mean(), np.mean(am == ref)
+    return check_argmax_margin(am, z, MARGIN)
 
 
 @pytest.mark.parametrize("name", ["d12", "d24"])

@@ -175,6 +175,42 @@ def test_gemm_full_size_sampled():
     assert np.abs(got - ref).max() < 1e-4 * np.sqrt(K) * 4
 
 
+# d24 weight-gradient products dW = dY^T X over the 32768 tokens of a B = 16, T = 2048
+# micro-batch (both operands token-major, so both are transposed on load): (rows of W,
+# cols of W) for the stacked QKV weight, Wo, W1, W2 and the LM head
+D24_WGRAD = [(4608, 1536), (1536, 1536), (6144, 1536), (1536, 6144), (32768, 1536)]
+
+
+@pytest.mark.parametrize("nout,kin", D24_WGRAD, ids=[f"{a}x{b}" for a, b in D24_WGRAD])
+def test_gemm_d24_weight_gradients_with_the_steps_split(nout, kin):
+    """The launcher's own split-K factor (gptk_gemm with splits < 0, the factor gpt_step
+    picks for these shapes) over K = 32768: 2048 sampled outputs recomputed one by one
+    in fp64 from the same bf16 operands, the first and last rows and columns included."""
+    K = 32768
+    splits = B.gemm_auto_splits(B.GPT_BF16, nout, kin, K, 1, 0, 0)
+    say(f"  d24 weight gradient {nout}x{kin}x{K}: {splits} splits, kernel "
+        f"{B.gemm_kernel_name(B.GPT_BF16, nout, kin, K, 1, 0, 0)}")
+    g = torch.Generator(device="cuda").manual_seed(nout + kin)
+    dY = torch.randn(K, nout, device="cuda", generator=g).bfloat16()
+    X = torch.randn(K, kin, device="cuda", generator=g).bfloat16()
+    C = torch.empty(nout, kin, device="cuda")
+    ws = torch.empty(max(splits, 1) * nout * kin if splits > 1 else 64, device="cuda")
+    B.gemm(B.GPT_BF16, 0, 0, nout, kin, K, dY, nout, X, kin, C, kin, splits=-1, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(nout)
+    rows = rng.integers(0, nout, 2048)
+    cols = rng.integers(0, kin, 2048)
+    rows[:4], cols[:4] = [0, nout - 1, 0, nout - 1], [0, kin - 1, kin - 1, 0]
+    a = dY[:, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    b = X[:, torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64)
+    ref = np.sum(a * b, axis=0)
+    scale = np.sum(np.abs(a * b), axis=0)  # fp32 accumulation error grows with the sum of |terms|
+    got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    err = np.abs(got - ref) / scale
+    say(f"    max |err| / sum|a b| = {err.max():.2e}")
+    assert err.max() < 1e-5
+
+
 # ----------------------------------------------------------------------------- attention
 
 
