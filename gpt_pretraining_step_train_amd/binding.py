@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgptmi.so")
+# GPTMI_LIB selects another build of the same library (the host-sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("GPTMI_LIB") or os.path.join(HERE, "libgptmi.so")
 
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 PREC = {"fp32": GPT_FP32, "bf16": GPT_BF16, "fp8": GPT_FP8}
@@ -75,6 +76,7 @@ _SIGS = {
     "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
     "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
+    "gptk_attn_variant": (_I, [_I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_rmsnorm_fwd": (_I, [_I, _P, _P, _P, _I, _I, _F, _P]),
@@ -255,7 +257,7 @@ class Model:
 
     # names and element types of gpt_capture's items, in buffer order
     CAPTURE_BLOCK = [("a", "act", "d"), ("qkv", "act", "QD"), ("x", "f32", "d"), ("o", "act", "d"),
-                     ("h1", "f32", "d"), ("m", "act", "d"), ("u", "act", "F"), ("g", "act", "F"), ("h2", "f32", "d"),
+                     ("h1", "f32", "d"), ("m", "act", "d"), ("g", "act", "F"), ("h2", "f32", "d"),
                      ("dh", "act", "d"), ("du", "act", "F"), ("dm", "f32", "d"), ("dh1", "act", "d"),
                      ("do", "act", "d"), ("dqkv", "act", "QD"), ("da", "f32", "d")]
     CAPTURE_HEAD = [("r", "act", "d"), ("logits", "f32", "V"), ("dlogits", "act", "V"), ("dr", "f32", "d")]
@@ -335,6 +337,10 @@ def gemm_auto_splits(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> int:
 
 def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
     return lib().gpt_gemm_kernel_name(dtype, a_kmaj, b_kmaj, M, N, K, batch).decode()
+
+
+def attn_variant(pass_, variant):
+    check(lib().gptk_attn_variant(pass_, variant), "gptk_attn_variant")
 
 
 def attn_fwd(dtype, qkv, o, lse, B, T, H, hd, window=0, n_kv=None):

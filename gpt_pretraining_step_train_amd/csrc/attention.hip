@@ -344,6 +344,241 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   }
 }
 
+// Buffer-load DMA of 16-byte chunks straight into LDS (no registers): lane l of one
+// instruction writes LDS bytes M0 + 16 l .. + 15.  Written in assembly (as in the GEMM)
+// so that the compiler does not wait for every DMA before each LDS read; the waits are
+// explicit (dma_wait_sync).
+typedef unsigned int u32x4w_t __attribute__((ext_vector_type(4)));
+__device__ inline u32x4w_t rows_words(const bf16_t* base, long ld, int row0, int T, int HD) {
+  const uint32_t bytes = row0 < T ? (uint32_t)(((long)(T - row0 - 1) * ld + HD) * 2) : 0u;
+  const uintptr_t a = (uintptr_t)(base + (long)row0 * ld);
+  u32x4w_t r;
+  r.x = (uint32_t)a;
+  r.y = (uint32_t)(a >> 32) & 0xFFFFu;
+  r.z = bytes;
+  r.w = 0x00020000u;
+  return r;
+}
+__device__ inline void attn_dma16(const u32x4w_t& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// every DMA of this wave landed (vmcnt 0) and its LDS reads done, then a workgroup barrier
+__device__ inline void dma_wait_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K and V tiles [64 rows][128] (Tile<128> layout) by DMA from NT threads: instruction j
+// of thread tid fills LDS chunk p = j NT + tid, i.e. row p / 16 and physical chunk p % 16,
+// which holds logical chunk (p % 16) ^ swz(row).  Rows at or past T read zeros (the
+// descriptor ends at the sequence's last row).
+template <int NT>
+struct DmaTilePair {
+  static constexpr int PER = 64 * 16 / NT;
+  uint32_t voff[PER];
+  __device__ inline void init(long ld, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int pch = j * NT + tid, row = pch >> 4, c = (pch & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+      voff[j] = (uint32_t)(((long)row * ld + c * 8) * 2);
+    }
+  }
+  __device__ inline void issue(const u32x4w_t& rk, const u32x4w_t& rv, const bf16_t* ks, const bf16_t* vs, int wave) {
+    const uint32_t kl = (uint32_t)(uintptr_t)ks, vl = (uint32_t)(uintptr_t)vs;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      attn_dma16(rk, kl + (j * NT + wave * 64) * 16, voff[j]);
+      attn_dma16(rv, vl + (j * NT + wave * 64) * 16, voff[j]);
+    }
+  }
+};
+
+// Forward with 64 queries per wave (two 32-query column blocks): every K and V
+// fragment read from LDS feeds two MFMAs, half the LDS traffic per flop of the 32-query
+// form.  The state (O^T 2 x 4 accumulators, two S^T tiles, Q fragments of 64 queries)
+// needs one wave per SIMD: 4 waves, 256 queries per block.  Same tile staging, masking,
+// lazy rescale and output as attn_fwd_bf16_kernel.
+template <int HD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_q64_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H,
+                    int Hkv, int W) {
+  constexpr int NW = 4, BQ = 64 * NW, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32,
+                NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = (T + BQ - 1) / BQ;
+  const int G = H / Hkv;
+  int bx, bh;
+  head_major_coords(bx, bh, G);
+  const int qb = nqb - 1 - bx;  // longest causal rows first
+  const int b = bh / H, h = bh % H;
+  const long ld = (long)(H + 2 * Hkv) * HD;
+  const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
+  const bf16_t* K = qkv + (long)b * T * ld + (long)(H + h / G) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
+  const int q0 = qb * BQ + wave * 64;  // the wave's queries q0 .. q0 + 63, column block c: q0 + 32c + lq
+
+  bf16x8_t qf[2][NKK];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int q = q0 + 32 * c + lq;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (q < T) u = *reinterpret_cast<const uint4*>(Q + (long)q * ld + kk * 16 + hl * 8);
+      qf[c][kk] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  f32x16_t oacc[2][NDB];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[c][i] = zero16();
+  float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  const int Wn = W > 0 ? W : T;
+  const int kv_end = min(T, (qb + 1) * BQ);
+  const int nkv = (kv_end + BKV - 1) / BKV;
+  const int it0 = max(0, qb * BQ - Wn + 1) / BKV;
+
+  int kro[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int vro[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    vro[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    vro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
+
+  static_assert(HD == 128, "DMA tile layout is Tile<128>");
+  DmaTilePair<NW * 64> dma;
+  dma.init(ld, tid);
+  dma.issue(rows_words(K, ld, it0 * BKV, T, HD), rows_words(V, ld, it0 * BKV, T, HD), Ks[0], Vs[0], wave);
+  dma_wait_sync();
+
+  auto body = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int k0 = it * BKV;
+    // the next tile into the other stage, which every wave finished reading before the
+    // barrier that ended the previous tile
+    if (it + 1 < nkv)
+      dma.issue(rows_words(K, ld, k0 + BKV, T, HD), rows_words(V, ld, k0 + BKV, T, HD), Ks[cur ^ 1], Vs[cur ^ 1],
+                wave);
+    // the wave's 64 queries see keys q0 - Wn + 1 .. q0 + 63
+    if (k0 <= q0 + 63 && k0 + BKV - 1 >= q0 - Wn + 1 && q0 < T) {
+      f32x16_t s[2][2];  // [key block][query column block]
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16_t* kp = Ks[cur] + kb2 * 32 * RS;
+        bf16x8_t kf = lds_row8(kp + kro[0]);
+        s[kb2][0] = mfma32x32x16_bf16(kf, qf[0][0], zero16());
+        s[kb2][1] = mfma32x32x16_bf16(kf, qf[1][0], zero16());
+#pragma unroll
+        for (int kk = 1; kk < NKK; ++kk) {
+          kf = lds_row8(kp + kro[kk]);
+          s[kb2][0] = mfma32x32x16_bf16(kf, qf[0][kk], s[kb2][0]);
+          s[kb2][1] = mfma32x32x16_bf16(kf, qf[1][kk], s[kb2][1]);
+        }
+      }
+      if (k0 + BKV - 1 > q0 || k0 + BKV > T || k0 <= q0 + 63 - Wn) {  // diagonal, ragged or window edge
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int myq = q0 + 32 * c + lq;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kb2 * 32 + acc_row(lane, r);
+              if (key > myq || key >= T || key <= myq - Wn) s[kb2][c][r] = -INFINITY;
+            }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kb2][c][r]);
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64)) * sl2;
+        const bool raise = bmax > m[c] + RESCALE_LOG2;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+          const float mnew = raise ? bmax : m[c];
+          const float alpha = fast_exp2(m[c] - mnew);
+          l[c] *= alpha;
+#pragma unroll
+          for (int i = 0; i < NDB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[c][i][r] *= alpha;
+          m[c] = mnew;
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(fmaf(s[kb2][c][r], sl2, -m[c]));
+            s[kb2][c][r] = pr;
+            rs += pr;
+          }
+        l[c] += rs + __shfl_xor(rs, 32, 64);
+      }
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          bf16x8_t pb[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float pv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pv[j] = s[kb2][c][8 * s_ + j];
+            pb[c] = pack8(pv);
+          }
+          const bf16_t* vp = Vs[cur] + (kb2 * 32 + 16 * s_) * RS;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8_t vf = lds_tr_pair(vp + vro[db][0], vp + vro[db][1]);
+            oacc[0][db] = mfma32x32x16_bf16(vf, pb[0], oacc[0][db]);
+            oacc[1][db] = mfma32x32x16_bf16(vf, pb[1], oacc[1][db]);
+          }
+        }
+    }
+    dma_wait_sync();
+  };
+  for (int it = it0; it < nkv; it += 2) {
+    body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int myq = q0 + 32 * c + lq;
+    if (myq < T) {
+      const float inv = 1.f / l[c];
+      bf16_t* op = out + ((long)b * T + myq) * ((long)H * HD) + h * HD;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + g * 8 + hl * 4;
+          uint2 u = make_uint2(pack_bf2(oacc[c][db][4 * g] * inv, oacc[c][db][4 * g + 1] * inv),
+                               pack_bf2(oacc[c][db][4 * g + 2] * inv, oacc[c][db][4 * g + 3] * inv));
+          *reinterpret_cast<uint2*>(op + d) = u;
+        }
+      if (hl == 0) lse[(long)bh * T + myq] = (m[c] + log2f(l[c])) * LN2;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // backward: D = rowsum(dO * O)
 
@@ -502,6 +737,175 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
                              pack_bf2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc));
         *reinterpret_cast<uint2*>(op + d) = u;
       }
+  }
+}
+
+// dQ with 64 queries per wave (two 32-query column blocks), one wave per SIMD, 256
+// queries per block: every K, V and K^T fragment read from LDS feeds two MFMAs.  K/V
+// tiles by buffer-load DMA, double-buffered.  Also writes D = rowsum(dO * O).
+template <int HD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dq_q64_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dO,
+                       const float* __restrict__ lse, float* __restrict__ Dv, bf16_t* __restrict__ dqkv, int T, int H,
+                       int Hkv, int W) {
+  static_assert(HD == 128, "DMA tile layout is Tile<128>");
+  constexpr int NW = 4, BQ = 64 * NW, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32,
+                NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = (T + BQ - 1) / BQ;
+  const int Gq = H / Hkv;
+  int bx, bh;
+  head_major_coords(bx, bh, Gq);
+  const int qb = nqb - 1 - bx;
+  const int b = bh / H, h = bh % H;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
+  const bf16_t* Q = qkv + (long)b * T * ld + h * HD;
+  const bf16_t* K = qkv + (long)b * T * ld + (long)(H + h / Gq) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
+  const bf16_t* G = dO + (long)b * T * ldo + h * HD;
+  const bf16_t* O = o + (long)b * T * ldo + h * HD;
+  const int q0 = qb * BQ + wave * 64;  // the wave's queries: column block c holds q0 + 32c + lq
+
+  bf16x8_t qf[2][NKK], gf[2][NKK];
+  float Dq[2], lse2[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int myq = q0 + 32 * c + lq;
+    float dsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 u = make_uint4(0, 0, 0, 0), w = u, x = u;
+      if (myq < T) {
+        u = *reinterpret_cast<const uint4*>(Q + (long)myq * ld + kk * 16 + hl * 8);
+        w = *reinterpret_cast<const uint4*>(G + (long)myq * ldo + kk * 16 + hl * 8);
+        x = *reinterpret_cast<const uint4*>(O + (long)myq * ldo + kk * 16 + hl * 8);
+      }
+      qf[c][kk] = __builtin_bit_cast(bf16x8_t, u);
+      gf[c][kk] = __builtin_bit_cast(bf16x8_t, w);
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w}, xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dsum += __uint_as_float(wv[e] << 16) * __uint_as_float(xv[e] << 16) +
+                __uint_as_float(wv[e] & 0xFFFF0000u) * __uint_as_float(xv[e] & 0xFFFF0000u);
+    }
+    Dq[c] = dsum + __shfl_xor(dsum, 32, 64);
+    if (hl == 0 && myq < T) Dv[(long)bh * T + myq] = Dq[c];
+    lse2[c] = myq < T ? lse[(long)bh * T + myq] * LOG2E : 0.f;
+  }
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  f32x16_t acc[2][NDB];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[c][i] = zero16();
+  int kro[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int ktr[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ktr[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    ktr[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
+  const int Wn = W > 0 ? W : T;
+  const int kv_end = min(T, (qb + 1) * BQ);
+  const int nkv = (kv_end + BKV - 1) / BKV;
+  const int it0 = max(0, qb * BQ - Wn + 1) / BKV;
+  DmaTilePair<NW * 64> dma;
+  dma.init(ld, tid);
+  dma.issue(rows_words(K, ld, it0 * BKV, T, HD), rows_words(V, ld, it0 * BKV, T, HD), Ks[0], Vs[0], wave);
+  dma_wait_sync();
+  auto body = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int k0 = it * BKV;
+    if (it + 1 < nkv)
+      dma.issue(rows_words(K, ld, k0 + BKV, T, HD), rows_words(V, ld, k0 + BKV, T, HD), Ks[cur ^ 1], Vs[cur ^ 1],
+                wave);
+    if (k0 <= q0 + 63 && k0 + BKV - 1 >= q0 - Wn + 1 && q0 < T) {
+      const bool mask = k0 + BKV - 1 > q0 || k0 + BKV > T || k0 <= q0 + 63 - Wn;
+#pragma unroll 1
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16_t* kp = Ks[cur] + kb2 * 32 * RS;
+        const bf16_t* vp = Vs[cur] + kb2 * 32 * RS;
+        f32x16_t sv[2], dp[2];  // [query column block]: S^T and dP^T [key rows][query = lane]
+        {
+          bf16x8_t ka = lds_row8(kp + kro[0]), va = lds_row8(vp + kro[0]);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            sv[c] = mfma32x32x16_bf16(ka, qf[c][0], zero16());
+            dp[c] = mfma32x32x16_bf16(va, gf[c][0], zero16());
+          }
+#pragma unroll
+          for (int kk = 1; kk < NKK; ++kk) {
+            ka = lds_row8(kp + kro[kk]);
+            va = lds_row8(vp + kro[kk]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              sv[c] = mfma32x32x16_bf16(ka, qf[c][kk], sv[c]);
+              dp[c] = mfma32x32x16_bf16(va, gf[c][kk], dp[c]);
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int myq = q0 + 32 * c + lq;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = sv[c][r];
+            if (mask) {
+              const int key = k0 + kb2 * 32 + acc_row(lane, r);
+              if (key > myq || key >= T || key <= myq - Wn) x = -INFINITY;
+            }
+            dp[c][r] = fast_exp2(fmaf(x, sl2, -lse2[c])) * (dp[c][r] - Dq[c]);  // dS
+          }
+        }
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          bf16x8_t da[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float w8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w8[j] = dp[c][8 * s_ + j];
+            da[c] = pack8(w8);
+          }
+          const bf16_t* tp = kp + 16 * s_ * RS;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8_t kt = lds_tr_pair(tp + ktr[db][0], tp + ktr[db][1]);
+            acc[0][db] = mfma32x32x16_bf16(kt, da[0], acc[0][db]);
+            acc[1][db] = mfma32x32x16_bf16(kt, da[1], acc[1][db]);
+          }
+        }
+      }
+    }
+    dma_wait_sync();
+  };
+  for (int it = it0; it < nkv; it += 2) {
+    body(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
+  }
+  const float sc = 1.f / sqrtf((float)HD);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int myq = q0 + 32 * c + lq;
+    if (myq < T) {
+      bf16_t* op = dqkv + ((long)b * T + myq) * ld + h * HD;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + g * 8 + hl * 4;
+          uint2 u = make_uint2(pack_bf2(acc[c][db][4 * g] * sc, acc[c][db][4 * g + 1] * sc),
+                               pack_bf2(acc[c][db][4 * g + 2] * sc, acc[c][db][4 * g + 3] * sc));
+          *reinterpret_cast<uint2*>(op + d) = u;
+        }
+    }
   }
 }
 
@@ -695,6 +1099,230 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
     }
 }
 
+// dK and dV with 64 keys per wave (two 32-key blocks), one wave per SIMD: a wave forms
+// S, P, dP and dS for its own keys and accumulates both dK and dV (2 x 4 accumulators
+// each, 256 registers), so P never leaves registers and every Q / dO fragment read from
+// LDS feeds two MFMAs.  4 waves, 256 keys per block; the 64-query Q and dO tiles arrive
+// by buffer-load DMA, double-buffered, with their lse / D values.  A block serves one
+// key/value head and walks the query tiles of each of its G query heads in turn.
+template <int HD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dkdv_k64_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
+                         const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
+                         int T, int H, int Hkv, int W) {
+  static_assert(HD == 128, "DMA tile layout is Tile<128>");
+  constexpr int NW = 4, BKEY = 64 * NW, BQT = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32,
+                NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
+  __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
+  __shared__ __attribute__((aligned(16))) bf16_t Vk[NW * TE];  // V rows of the block's keys, Tile<128> layout
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int kb, bk;
+  head_major_coords(kb, bk);
+  const int G = H / Hkv, b = bk / Hkv, hk = bk % Hkv;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
+  const bf16_t* Qb = qkv + (long)b * T * ld;
+  const bf16_t* K = Qb + (long)(H + hk) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
+  const bf16_t* Gb = dO + (long)b * T * ldo;
+  const long lrow = (long)b * H * T;
+  const int key0 = kb * BKEY + wave * 64;  // the wave's keys key0 + 32 kb2 + lq
+
+  bf16x8_t kf[2][NKK];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int key = key0 + 32 * k2 + lq;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (key < T) u = *reinterpret_cast<const uint4*>(K + (long)key * ld + kk * 16 + hl * 8);
+      kf[k2][kk] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  f32x16_t dva[2][NDB], dka[2][NDB];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      dva[k2][i] = zero16();
+      dka[k2][i] = zero16();
+    }
+  int qro[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int tro[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    tro[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    tro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
+
+  const int Wn = W > 0 ? W : T;
+  const int nqt = min((T + BQT - 1) / BQT, (kb * BKEY + BKEY - 1 + Wn - 1) / BQT + 1);
+  const int qt0 = (kb * BKEY) / BQT;
+  const int nsteps = G * max(0, nqt - qt0);
+  DmaTilePair<NW * 64> dma;  // chunk maps of Q rows (stride ld) and dO rows (stride ldo)
+  DmaTilePair<NW * 64> dmo;
+  dma.init(ld, tid);
+  dmo.init(ldo, tid);
+  // the block's V rows, 64 per wave: each wave fetches its own four 1 KB row groups per
+  // 64-row tile (the chunk map of Q, whose row stride is also ld)
+#pragma unroll
+  for (int t4 = 0; t4 < NW; ++t4) {
+    const u32x4w_t rv = rows_words(V, ld, min(kb * BKEY + 64 * t4, T - 1), T, HD);
+    const uint32_t vl = (uint32_t)(uintptr_t)(Vk + t4 * TE);
+    if (kb * BKEY + 64 * t4 < T) {
+#pragma unroll
+      for (int j = 0; j < DmaTilePair<NW * 64>::PER; ++j) attn_dma16(rv, vl + (j * NW * 64 + wave * 64) * 16, dma.voff[j]);
+    }
+  }
+  int vko[2][NKK];  // this lane's V row (key) fragments in Vk
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) vko[k2][kk] = wave * TE + Tile<HD>::off(32 * k2 + lq, kk * 16 + hl * 8);
+  float pl = 0.f, pd = 0.f;
+  int ld_h = hk * G, ld_t = qt0, cur_t = qt0;
+  auto load = [&](int buf) {
+    const int q0 = ld_t * BQT;
+    const u32x4w_t rq = rows_words(Qb + ld_h * HD, ld, q0, T, HD), rg = rows_words(Gb + ld_h * HD, ldo, q0, T, HD);
+    const uint32_t ql = (uint32_t)(uintptr_t)Qs[buf], gl = (uint32_t)(uintptr_t)Gs[buf];
+#pragma unroll
+    for (int j = 0; j < DmaTilePair<NW * 64>::PER; ++j) {
+      attn_dma16(rq, ql + (j * NW * 64 + wave * 64) * 16, dma.voff[j]);
+      attn_dma16(rg, gl + (j * NW * 64 + wave * 64) * 16, dmo.voff[j]);
+    }
+    if (tid < BQT) {
+      const int q = q0 + tid;
+      const long r = lrow + (long)ld_h * T + q;
+      pl = q < T ? lse[r] * LOG2E : 0.f;
+      pd = q < T ? Dv[r] : 0.f;
+    }
+    if (++ld_t == nqt) {
+      ld_t = qt0;
+      ++ld_h;
+    }
+  };
+  auto store_ld = [&](int buf) {
+    if (tid < BQT) {
+      L2s[buf][tid] = pl;
+      Ds[buf][tid] = pd;
+    }
+  };
+  if (nsteps > 0) {
+    load(0);
+    store_ld(0);
+  }
+  dma_wait_sync();
+  auto body = [&](auto cur_c, int sp) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int qb0 = cur_t * BQT;
+    if (sp + 1 < nsteps) load(cur ^ 1);
+    const bool live = qb0 + BQT - 1 >= key0 && qb0 <= key0 + 63 + Wn - 1 && key0 < T;
+#pragma unroll 1
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qh0 = qb0 + qs * 32;  // the half's queries qh0 .. qh0 + 31
+      if (!live || qh0 + 31 < key0 || qh0 > key0 + 63 + Wn - 1) continue;
+      const bf16_t* qp = Qs[cur] + qs * 32 * RS;
+      const bf16_t* gp = Gs[cur] + qs * 32 * RS;
+      f32x16_t sa[2], dp[2];  // [key block]: S and dP [query rows][key column = lane]
+      {
+        bf16x8_t qa = lds_row8(qp + qro[0]), ga = lds_row8(gp + qro[0]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          sa[k2] = mfma32x32x16_bf16(qa, kf[k2][0], zero16());
+          dp[k2] = mfma32x32x16_bf16(ga, lds_row8(Vk + vko[k2][0]), zero16());
+        }
+#pragma unroll
+        for (int kk = 1; kk < NKK; ++kk) {
+          qa = lds_row8(qp + qro[kk]);
+          ga = lds_row8(gp + qro[kk]);
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            sa[k2] = mfma32x32x16_bf16(qa, kf[k2][kk], sa[k2]);
+            dp[k2] = mfma32x32x16_bf16(ga, lds_row8(Vk + vko[k2][kk]), dp[k2]);
+          }
+        }
+      }
+      const bool edge = qh0 < key0 + 63 || qh0 + 31 - key0 >= Wn;  // diagonal or window edge
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {  // registers 4g..4g+3 hold query rows 8g + 4hl + 0..3 of the half
+        const float4 l4 = *reinterpret_cast<const float4*>(&L2s[cur][qs * 32 + 8 * g + 4 * hl]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][qs * 32 + 8 * g + 4 * hl]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float sv = sa[k2][4 * g + j];
+            if (edge) {
+              const int q = qh0 + 8 * g + 4 * hl + j, key = key0 + 32 * k2 + lq;
+              if (q < key || q - key >= Wn) sv = -INFINITY;
+            }
+            const float pr = fast_exp2(fmaf(sv, sl2, -lv[j]));
+            sa[k2][4 * g + j] = pr;                                   // P
+            dp[k2][4 * g + j] = pr * (dp[k2][4 * g + j] - dv4[j]);   // dS
+          }
+      }
+      // dV += P^T dO and dK += dS^T Q: the dO / Q fragment (read by transpose) is shared
+      // by both key blocks
+#pragma unroll
+      for (int s_ = 0; s_ < 2; ++s_) {
+        bf16x8_t pa[2], da[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          float pv[8], dsv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            pv[j] = sa[k2][8 * s_ + j];
+            dsv[j] = dp[k2][8 * s_ + j];
+          }
+          pa[k2] = pack8(pv);
+          da[k2] = pack8(dsv);
+        }
+        const bf16_t* gt = gp + 16 * s_ * RS;
+        const bf16_t* qt = qp + 16 * s_ * RS;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8_t gfr = lds_tr_pair(gt + tro[db][0], gt + tro[db][1]);
+          const bf16x8_t qfr = lds_tr_pair(qt + tro[db][0], qt + tro[db][1]);
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            dva[k2][db] = mfma32x32x16_bf16(pa[k2], gfr, dva[k2][db]);
+            dka[k2][db] = mfma32x32x16_bf16(da[k2], qfr, dka[k2][db]);
+          }
+        }
+      }
+    }
+    if (sp + 1 < nsteps) store_ld(cur ^ 1);
+    dma_wait_sync();
+    cur_t = cur_t + 1 == nqt ? qt0 : cur_t + 1;
+  };
+  for (int sp = 0; sp < nsteps; sp += 2) {
+    body(std::integral_constant<int, 0>{}, sp);
+    if (sp + 1 < nsteps) body(std::integral_constant<int, 1>{}, sp + 1);
+  }
+  const float scale = 1.f / sqrtf((float)HD);
+  const long ck = (long)(H + hk) * HD, cv = (long)(H + Hkv + hk) * HD;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * k2 + acc_row(lane, r);
+        if (key < T) {
+          bf16_t* rowp = dqkv + ((long)b * T + key) * ld;
+          rowp[ck + db * 32 + lq] = f2bf(dka[k2][db][r] * scale);
+          rowp[cv + db * 32 + lq] = f2bf(dva[k2][db][r]);
+        }
+      }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 attention (plain per-row loops; used by the all-fp32 configuration)
 
@@ -813,9 +1441,24 @@ __global__ void __launch_bounds__(64) attn_bwd_dkdv_f32_kernel(const float* __re
   }
 }
 
+// forward kernel variant for bf16, hd 128: 0 = 32 queries per wave (4 waves of 32, two
+// waves per SIMD), 1 = 64 queries per wave (4 waves of 64, one wave per SIMD)
+int g_attn_fwd_variant = 0;
+// backward (bf16, hd 128): 0 = dQ by 4 waves of 32 queries and dK/dV by 8 waves of 32
+// keys (dV and dK in different waves), 1 = dQ by 4 waves of 64 queries and dK/dV by 4
+// waves of 64 keys (both in one wave)
+int g_attn_bwd_variant = 0;
+
 template <int HD>
 void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int W, hipStream_t st) {
   constexpr int NW = kFwdWaves;
+  if constexpr (HD == 128) {
+    if (at == ACT_BF16 && g_attn_fwd_variant == 1) {
+      hipLaunchKernelGGL((attn_fwd_q64_kernel<HD>), dim3((T + 255) / 256, B * H), dim3(256), 0, st,
+                         (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, Hkv, W);
+      return;
+    }
+  }
   if (at == ACT_BF16)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD, NW>), dim3((T + 32 * NW - 1) / (32 * NW), B * H), dim3(NW * 64), 0,
                        st, (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, Hkv, W);
@@ -829,10 +1472,29 @@ void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* l
                   int B, int T, int H, int Hkv, int W, hipStream_t st) {
   if (at == ACT_BF16) {
     // the dQ kernel also writes D = rowsum(dO * O) for the dK/dV kernel
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st, (const bf16_t*)qkv,
-                       (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
-    hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * Hkv), dim3(512), 0, st,
-                       (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
+    bool done_q = false;
+    if constexpr (HD == 128) {
+      if (g_attn_bwd_variant == 1) {
+        hipLaunchKernelGGL(attn_bwd_dq_q64_kernel<HD>, dim3((T + 255) / 256, B * H), dim3(256), 0, st,
+                           (const bf16_t*)qkv, (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv,
+                           W);
+        done_q = true;
+      }
+    }
+    if (!done_q)
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<HD>, dim3((T + 127) / 128, B * H), dim3(256), 0, st, (const bf16_t*)qkv,
+                         (const bf16_t*)o, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
+    bool done = false;
+    if constexpr (HD == 128) {
+      if (g_attn_bwd_variant == 1) {
+        hipLaunchKernelGGL(attn_bwd_dkdv_k64_kernel<HD>, dim3((T + 255) / 256, B * Hkv), dim3(256), 0, st,
+                           (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
+        done = true;
+      }
+    }
+    if (!done)
+      hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * Hkv), dim3(512), 0, st,
+                         (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
                        (const float*)dO, lse, D, (float*)dqkv, T, H, Hkv, W);
@@ -842,6 +1504,9 @@ void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* l
 }
 
 }  // namespace
+
+void set_attn_fwd_variant(int v) { g_attn_fwd_variant = v; }
+void set_attn_bwd_variant(int v) { g_attn_bwd_variant = v; }
 
 // Hkv must divide H (the callers validate it)
 void launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int hd, int window,

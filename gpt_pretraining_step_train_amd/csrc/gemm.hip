@@ -141,13 +141,13 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
     }
   } else if (p.epi == EPI_RELU2) {
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
-    store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
+    if (p.outA) store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
     const float r = fmaxf(v, 0.f);
     store_act<OutT>(reinterpret_cast<OutT*>(p.out2) + o, r * r);
-  } else {  // EPI_DRELU2
+  } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u)
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
-    const float u = load_act<OutT>(reinterpret_cast<const OutT*>(p.aux) + o);
-    store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v * 2.f * fmaxf(u, 0.f));
+    const float g = load_act<OutT>(reinterpret_cast<const OutT*>(p.aux) + o);
+    store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v * 2.f * sqrtf(fmaxf(g, 0.f)));
   }
 }
 
@@ -207,13 +207,13 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     float g[4];
     _Pragma("unroll") for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
-    st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
+    if (p.outA) st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
     st4_act(reinterpret_cast<bf16_t*>(p.out2) + o, g);
-  } else {  // EPI_DRELU2
+  } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u)
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
-    float u[4];
-    ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + o, u);
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * fmaxf(u[t], 0.f);
+    float g[4];
+    ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + o, g);
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * sqrtf(fmaxf(g[t], 0.f));
     st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
   }
 }

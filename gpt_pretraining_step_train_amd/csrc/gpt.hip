@@ -79,7 +79,7 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 }
 
 struct Offsets {
-  size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, u, g, r, rstd_f, logits,
+  size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
       xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
@@ -161,7 +161,6 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.lse = P.add(L * B * H * T * 4);
   O.m = P.add(L * N * d * es);
   O.rstd_m = P.add(L * N * 4);
-  O.u = P.add(L * N * F * es);
   O.g = P.add(L * N * F * es);
   O.r = P.add(N * d * es);
   O.rstd_f = P.add(N * 4);
@@ -223,7 +222,7 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
 // Operand capture (gpt_capture): the slots of one block layer's four Linear products,
 // or of the LM head, in byte sizes; each slot starts 256-byte aligned in the buffer.
 enum {
-  CAP_A, CAP_QKV, CAP_HIN, CAP_O, CAP_H1, CAP_M, CAP_U, CAP_G, CAP_H2,   // forward
+  CAP_A, CAP_QKV, CAP_HIN, CAP_O, CAP_H1, CAP_M, CAP_G, CAP_H2,   // forward
   CAP_DY2, CAP_DU, CAP_DM, CAP_DYO, CAP_DO, CAP_DQKV, CAP_DA,           // backward
   CAP_BLOCK_SLOTS
 };
@@ -232,7 +231,7 @@ std::vector<size_t> capture_sizes(const gpt_cfg& c, int layer) {
   const size_t N = (size_t)c.batch * c.seq_len, d = c.d_model, F = c.d_ff, V = c.vocab, QD = qkv_dim(c);
   const size_t es = act_of(c) == ACT_BF16 ? 2 : 4;
   if (layer == c.depth) return {N * d * es, N * V * 4, N * V * es, N * d * 4};
-  return {N * d * es, N * QD * es, N * d * 4, N * d * es, N * d * 4, N * d * es, N * F * es, N * F * es, N * d * 4,
+  return {N * d * es, N * QD * es, N * d * 4, N * d * es, N * d * 4, N * d * es, N * F * es, N * d * 4,
           N * d * es, N * F * es, N * d * 4, N * d * es, N * d * es, N * QD * es, N * d * 4};
 }
 size_t capture_offset(const gpt_cfg& c, int layer, int slot, size_t* total = nullptr) {
@@ -735,7 +734,6 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     void* qkv = actp(O.qkv, (size_t)l * N * QD);
     void* o = actp(O.o, (size_t)l * N * d);
     void* m = actp(O.m, (size_t)l * N * d);
-    void* u = actp(O.u, (size_t)l * N * F);
     void* g = actp(O.g, (size_t)l * N * F);
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
     float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
@@ -771,12 +769,11 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     launch_rmsnorm_fwd(hsl(2 * l + 1), m, at, M->at_off<float>(O.rstd_m) + (size_t)l * N, N, d, eps, st);
     cap(l, CAP_M, m);
     {
-      GemmArgs p;  // u = m W1^T, g = relu(u)^2
+      GemmArgs p;  // g = relu(m W1^T)^2 (the pre-activation itself is not kept: relu(u) = sqrt(g))
       p.M = N; p.N = F; p.K = d; p.A = m; p.lda = d;
-      p.epi = EPI_RELU2; p.outA = u; p.out2 = g; p.ldoa = F;
+      p.epi = EPI_RELU2; p.out2 = g; p.ldoa = F;
       if ((rc = lin_fwd(M, p, 4 * l + 2, st))) return rc;
     }
-    cap(l, CAP_U, u);
     cap(l, CAP_G, g);
     {
       GemmArgs p;  // h'' = h' + g W2^T
@@ -842,16 +839,15 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     void* qkv = actp(O.qkv, (size_t)l * N * QD);
     void* o = actp(O.o, (size_t)l * N * d);
     void* m = actp(O.m, (size_t)l * N * d);
-    void* u = actp(O.u, (size_t)l * N * F);
     void* g = actp(O.g, (size_t)l * N * F);
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
     float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
     cap(l, CAP_DY2, dh_act);
     {
-      GemmArgs pd;  // dW2 = dY^T g ; du = (dY W2) * 2 relu(u)
+      GemmArgs pd;  // dW2 = dY^T g ; du = (dY W2) * 2 relu(u), relu(u) = sqrt(g)
       pd.M = N; pd.N = F; pd.K = d;
-      pd.epi = EPI_DRELU2; pd.aux = u; pd.outA = dbig; pd.ldoa = F;
+      pd.epi = EPI_DRELU2; pd.aux = g; pd.outA = dbig; pd.ldoa = F;
       if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st))) return rc;
     }
     cap(l, CAP_DU, dbig);
@@ -1324,6 +1320,13 @@ static int attn_ok(int dtype, int hd) {
 
 // key/value heads: 1 <= Hkv <= H with H % Hkv == 0 (any Hkv when H = 0)
 static bool kv_heads_ok(int H, int Hkv) { return H == 0 ? Hkv >= 0 : (Hkv >= 1 && Hkv <= H && H % Hkv == 0); }
+
+int gptk_attn_variant(int pass, int variant) {
+  if (pass < 0 || pass > 1 || variant < 0 || variant > 1) return GPT_ERR_ARG;
+  if (pass == 0) set_attn_fwd_variant(variant);
+  else set_attn_bwd_variant(variant);
+  return GPT_OK;
+}
 
 int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
                   void* stream) {

@@ -8,8 +8,8 @@ enum ActType { ACT_F32 = 0, ACT_BF16 = 1, ACT_F16 = 2 };
 
 enum GemmEpi {
   EPI_LINEAR = 0,  // v = alpha*acc + beta*Cin -> outF (fp32) and/or outA (act type)
-  EPI_RELU2 = 1,   // u = alpha*acc -> outA ; g = max(u,0)^2 -> out2
-  EPI_DRELU2 = 2,  // v = alpha*acc * 2*max(aux,0) -> outA
+  EPI_RELU2 = 1,   // u = alpha*acc -> outA (when set) ; g = max(u,0)^2 -> out2
+  EPI_DRELU2 = 2,  // v = alpha*acc * 2*sqrt(max(aux,0)) -> outA, aux = g = max(u,0)^2 (so the root is max(u,0))
 };
 
 // C[M,N] = sum_k A(m,k) B(n,k), batched over `batch` with element strides.
@@ -158,6 +158,9 @@ void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, 
 
 // attention (window > 0: query i sees keys i - window < j <= i; 0: all j <= i).  qkv rows are
 // [H q heads | Hkv k heads | Hkv v heads] x hd; query head h reads key/value head h / (H / Hkv).
+// process-wide choice of the bf16 hd-128 attention kernels (see gptk_attn_variant)
+void set_attn_fwd_variant(int v);
+void set_attn_bwd_variant(int v);
 void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int Hkv, int hd,
                      int window, hipStream_t st);
 void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,

@@ -221,8 +221,10 @@ int gpt_prof_read(gpt_model* m, int64_t* launches, double* ms, double* flops);
  *   block layer: a [N][d] act (QKV input), qkv [N][QD] act (QKV output, before RoPE /
  *     QK-norm / value embeddings), x [N][d] fp32 (the residual stream the layer adds to),
  *     o [N][d] act (output-projection input), h1 [N][d] fp32 (= x + o Wo^T), m [N][d] act,
- *     u [N][F] act (= m W1^T), g [N][F] act (= relu(u)^2), h2 [N][d] fp32 (= h1 + g W2^T);
- *     backward: dh [N][d] act (proj output gradient), du [N][F] act (= (dh W2) 2 relu(u)),
+ *     g [N][F] act (= relu(u)^2 with u = m W1^T; u itself is not kept), h2 [N][d] fp32
+ *     (= h1 + g W2^T);
+ *     backward: dh [N][d] act (proj output gradient), du [N][F] act (= (dh W2) 2 relu(u),
+ *     with relu(u) taken as sqrt(g)),
  *     dm [N][d] fp32 (= du W1), dh1 [N][d] act (output-projection output gradient),
  *     do [N][d] act (= dh1 Wo), dqkv [N][QD] act (QKV output gradient), da [N][d] fp32
  *     (= dqkv [Wq; Wk; Wv]);
@@ -298,6 +300,16 @@ const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N
  * window); 0: all j <= i; negative: GPT_ERR_ARG. */
 int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
                   void* stream);
+/* Process-wide choice among the bf16 head_dim-128 attention kernels, for A/B
+ * measurements (every variant computes the same result; the default is the fastest
+ * measured).  pass 0 = forward: variant 0 = 32 queries per wave (two waves per SIMD),
+ * 1 = 64 queries per wave (one wave per SIMD); pass 1 = backward: variant 0 = dQ by
+ * waves of 32 queries and dK/dV by 8 waves of 32 keys (dV and dK accumulated by different
+ * waves), 1 = dQ by waves of 64 queries and dK/dV by 4 waves of 64 keys (one wave
+ * accumulates both).  GPT_ERR_ARG for another pass/variant.
+ * Not thread-safe against concurrent launches. */
+int gptk_attn_variant(int pass, int variant);
+
 /* backward: dqkv act [B*T][(H + 2*Hkv)*hd] from qkv, o, dO act [B*T][H*hd] and lse,
  * with the forward's Hkv and window (dK and dV of a shared head sum over its query
  * heads); D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */

@@ -60,3 +60,18 @@ def check_argmax_margin(am, z, margin):
     picked = np.take_along_axis(z, am[:, None].astype(np.int64), -1)[:, 0]
     assert np.all(picked >= z.max(axis=-1) - margin)
     return float(unique.mean()), float(np.mean(am == ref))
+
+
+def check_argmax_on_gpu_logits(am, z_gpu, z_ref):
+    """The argmax is integer work on the step's own logits: am must equal the lowest-index
+    argmax of z_gpu [n][V] exactly.  Against the oracle's logits z_ref the pick must be
+    consistent with the logits' own difference: with d = max_j |z_gpu - z_ref| on a row,
+    z_ref[am] >= max z_ref - 2 d (it cannot be further below the oracle's maximum than
+    the two rows disagree).  Returns (agreement with the oracle's argmax, largest d)."""
+    from oracle import gpt_oracle as O
+    am = np.asarray(am).reshape(-1)
+    np.testing.assert_array_equal(am, O.argmax_lowest(z_gpu))
+    dz = np.max(np.abs(z_gpu - z_ref), axis=-1)
+    picked = np.take_along_axis(z_ref, am[:, None].astype(np.int64), -1)[:, 0]
+    assert np.all(picked >= z_ref.max(axis=-1) - 2 * dz - 1e-6)
+    return float(np.mean(am == O.argmax_lowest(z_ref))), float(dz.max())
