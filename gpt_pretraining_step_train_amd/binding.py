@@ -79,6 +79,7 @@ _SIGS = {
     "gptk_attn_variant": (_I, [_I, _I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "gptk_attn_bwd_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_rmsnorm_fwd": (_I, [_I, _P, _P, _P, _I, _I, _F, _P]),
     "gptk_rmsnorm_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
     "gptk_rope_qknorm_fwd": (_I, [_I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P]),
@@ -354,6 +355,13 @@ def attn_bwd(dtype, qkv, o, dO, lse, D, dqkv, B, T, H, hd, window=0, n_kv=None):
     hk = H if n_kv is None else n_kv
     check(lib().gptk_attn_bwd(dtype, _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(D), _ptr(dqkv), B, T, H, hk, hd,
                               window, _stream()), "gptk_attn_bwd")
+
+
+def attn_bwd_noalloc(dtype, qkv, o, dO, lse, dqkv, B, T, H, hd, window=0, n_kv=None):
+    """attn_bwd with the library's own device scratch for rowsum(dO*O) (no D argument)."""
+    hk = H if n_kv is None else n_kv
+    check(lib().gptk_attn_bwd_noalloc(dtype, _ptr(qkv), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dqkv), B, T, H, hk, hd,
+                                      window, _stream()), "gptk_attn_bwd_noalloc")
 
 
 def rmsnorm_fwd(dtype, x, y, rstd, N, d, eps):

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1343,6 +1344,44 @@ int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, con
   if (rc) return rc;
   if (B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv) || window < 0 || !qkv || !o || !dO || !lse || !D || !dqkv)
     return GPT_ERR_ARG;
+  launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, Hkv, hd, window, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+// Allocation-free attention backward: the rowsum(dO * O) scratch that gptk_attn_bwd
+// takes as an argument lives here in a file-scope device array instead (each GPU holds
+// its own copy until the process ends).  Host code never passes the array's name to a
+// kernel: it resolves the device address once per device with hipGetSymbolAddress and
+// uses that pointer.
+constexpr size_t kAttnScratchFloats = (size_t)1 << 20;  // 4 MiB: B * H * T <= 1,048,576
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) float scratch[kAttnScratchFloats];
+static std::mutex g_scratch_mu;
+static float* g_scratch_ptr[kMaxDevices] = {};
+
+static int scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GPT_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GPT_ERR_HIP;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPT_OK;
+}
+
+int gptk_attn_bwd_noalloc(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, void* dqkv,
+                          int B, int T, int H, int Hkv, int hd, int window, void* stream) {
+  int rc = attn_ok(dtype, hd);
+  if (rc) return rc;
+  if (B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv) || window < 0 || !qkv || !o || !dO || !lse || !dqkv)
+    return GPT_ERR_ARG;
+  if ((double)B * H * T > (double)kAttnScratchFloats) return GPT_ERR_ARG;
+  float* D = nullptr;
+  if ((rc = scratch_of_current_device(&D))) return rc;
+  // every (b, h, t) of D is written by the backward before it is read: nothing to clear
   launch_attn_bwd(qkv, o, dO, lse, D, dqkv, act_type(dtype), B, T, H, Hkv, hd, window, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }

@@ -316,6 +316,18 @@ int gptk_attn_variant(int pass, int variant);
 int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D,
                   void* dqkv, int B, int T, int H, int Hkv, int hd, int window, void* stream);
 
+/* gptk_attn_bwd without the D argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight loops, harnesses that forbid hipMalloc): the
+ * rowsum(dO*O) scratch is a file-scope device array of the library, 4 MiB per GPU
+ * (B*H*T <= 1048576, else GPT_ERR_ARG), held until the process ends; its device address
+ * is looked up once per device on the first call there (GPT_ERR_HIP if that fails).
+ * Calls on one GPU share that array and keep what the last one left in it, so calls
+ * that overlap on one GPU (different streams or threads) race; calls ordered on one
+ * stream do not.  No hipMalloc, hipFree or allocating library call is made.  Other
+ * arguments, results and errors as gptk_attn_bwd. */
+int gptk_attn_bwd_noalloc(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, void* dqkv,
+                          int B, int T, int H, int Hkv, int hd, int window, void* stream);
+
 /* y act = x / sqrt(mean(x^2) + eps) per row of x fp32 [N][d]; rstd fp32 [N] */
 int gptk_rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int N, int d, float eps, void* stream);
 /* dx fp32 (and act copy if dx_act) = dres + rstd*(dy - y*mean(dy*y)), y = x*rstd;
