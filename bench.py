@@ -163,16 +163,42 @@ def other_configs(steps, warmup) -> dict:
     for name, over, k in plan:
         cfg = configs.get(name, **over)
         model = binding.Model(cfg, seed=0)
-        ms, losses = time_steps(model, cfg, make_batches(cfg), k, warmup)
+        batches = make_batches(cfg)
+        ms, losses = time_steps(model, cfg, batches, k, warmup)
         n_tok = cfg["batch"] * cfg["seq_len"]
         key = name + ("_fp8" if cfg["precision"] == "fp8" else "")
         out[key] = {"value": n_tok / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms, "steps": k,
                     "dtype": cfg["precision"], "global_batch": cfg["batch"], "seq_len": cfg["seq_len"],
                     "depth": cfg["depth"], "d_model": cfg["d_model"],
                     **mfu_fields(cfg, ms, cfg["precision"] == "fp8"), "loss_first_last": [losses[0], losses[-1]]}
+        if name in ("tiny", "laptop"):  # launch-bound: the same step replayed from a HIP graph
+            gms = time_graph_steps(model, batches[0], k, warmup)
+            out[key]["hip_graph"] = {"value": n_tok / (gms / 1e3), "unit": "tokens/s", "ms_per_step": gms,
+                                     "what": "gpt_step_async + muon_update captured once, replayed on one resident batch"}
         del model
         torch.cuda.empty_cache()
     return out
+
+
+def time_graph_steps(model, batch, steps, warmup):
+    """Mean ms per replay of one captured step (gpt_step_async + muon_update)."""
+    import torch
+    tok, tgt = batch
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        model.step_async(tok, tgt)
+        model.muon_update(LR)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    model.step_result()  # the last replay's loss and error flags
+    return ev0.elapsed_time(ev1) / steps
 
 
 def main() -> int:

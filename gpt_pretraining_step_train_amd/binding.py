@@ -48,6 +48,8 @@ _SIGS = {
     "gpt_init": (_I, [ctypes.POINTER(GptCfg), ctypes.c_uint64, _P, _SZ, _P, ctypes.POINTER(_P)]),
     "gpt_step": (_F, [_P, _P, _P, ctypes.POINTER(GptCfg), _P]),
     "gpt_step_accumulate": (_F, [_P, _P, _P, ctypes.POINTER(GptCfg), _I, _F, _P]),
+    "gpt_step_async": (_I, [_P, _P, _P, ctypes.POINTER(GptCfg), _I, _F, _P]),
+    "gpt_step_result": (_F, [_P, _P]),
     "gpt_grads": (_I, [_P, ctypes.c_int32, _P, _SZ, _P]),
     "muon_update": (_I, [_P, _F, _P]),
     "adamw_update": (_I, [_P, _F, _F, _F, _F, _F, _P]),
@@ -73,6 +75,8 @@ _SIGS = {
     "gptk_gemm_auto_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_gemm": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _L, _L, _P, _L, _L, _P, _L, _L, _I, _I, _P, _SZ, _P]),
     "gptk_gemm_split": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _L, _L, _P, _P, _L, _L, _P, _L, _L, _P]),
+    "gptk_ns_ws_bytes": (_SZ, [_I, _I]),
+    "gptk_newton_schulz": (_I, [_I, _P, _I, _I, _P, _I, _P, _P, _SZ, _P]),
     "gptk_quant_e4m3": (_I, [_I, _P, _I, _I, _L, _P, _P, _P, _P, _P]),
     "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
@@ -205,6 +209,19 @@ class Model:
             raise GptError(f"{what}: {lib().gpt_status_str(st).decode()} ({st})")
         return loss
 
+    def step_async(self, tokens, targets, accumulate: bool = False, grad_scale: float = 1.0):
+        """gpt_step_async: enqueue the step on the current stream (no synchronisation)."""
+        check(lib().gpt_step_async(self._h, _ptr(tokens), _ptr(targets), ctypes.byref(self.cfg),
+                                   int(bool(accumulate)), float(grad_scale), _stream()), "gpt_step_async")
+
+    def step_result(self) -> float:
+        """gpt_step_result: synchronise and return the last enqueued step's loss."""
+        loss = lib().gpt_step_result(self._h, _stream())
+        st = lib().gpt_last_status(self._h)
+        if st != 0:
+            raise GptError(f"gpt_step_result: {lib().gpt_status_str(st).decode()} ({st})")
+        return loss
+
     def muon_update(self, lr: float):
         check(lib().muon_update(self._h, float(lr), _stream()), "muon_update")
 
@@ -317,6 +334,18 @@ def gemm(dtype, a_kmaj, b_kmaj, M, N, K, A, lda, B, ldb, C, ldc, batch=1, sA=0, 
 def gemm_split(a_kmaj, b_kmaj, M, N, K, Ah, Al, lda, Bh, Bl, ldb, C, ldc, batch=1, sA=0, sB=0, sC=0):
     check(lib().gptk_gemm_split(int(a_kmaj), int(b_kmaj), M, N, K, batch, _ptr(Ah), _ptr(Al), lda, sA, _ptr(Bh),
                                 _ptr(Bl), ldb, sB, _ptr(C), ldc, sC, _stream()), "gptk_gemm_split")
+
+
+def newton_schulz(dtype, G, rows, cols, coeffs, steps, X):
+    """gptk_newton_schulz on device tensors G, X (fp32 [rows][cols]); coeffs: (a, b, c) rows."""
+    import torch
+    nbytes = lib().gptk_ns_ws_bytes(rows, cols)
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=G.device)
+    off = (-ws.data_ptr()) % 256
+    cf = (ctypes.c_float * 15)(*[float(v) for abc in coeffs for v in abc][:15])
+    check(lib().gptk_newton_schulz(dtype, _ptr(G), rows, cols, cf, steps, _ptr(X),
+                                   ctypes.c_void_p(ws.data_ptr() + off), nbytes, _stream()), "gptk_newton_schulz")
+    torch.cuda.synchronize()  # the workspace is released when this returns
 
 
 def quant_e4m3(dtype, x, rows, cols, ld, amax_slot, q, qt, inv_scale):

@@ -1149,6 +1149,53 @@ __global__ void __launch_bounds__(256) ns_normalize_vec_kernel(const float* __re
   }
 }
 
+// the same over many matrices in one launch: blockIdx.y picks the job
+template <typename T>
+__global__ void __launch_bounds__(256) ns_normalize_batched_kernel(const float* __restrict__ src,
+                                                                   const double* sumsq, float eps,
+                                                                   const MuonVecJob* __restrict__ jobs,
+                                                                   float* __restrict__ xf, T* __restrict__ xa,
+                                                                   T* __restrict__ xlo) {
+  const MuonVecJob jb = jobs[blockIdx.y];
+  const float scale = (float)(1.0 / (sqrt(sumsq[jb.mat]) + (double)eps));
+  const float4* s4 = reinterpret_cast<const float4*>(src + jb.src);
+  float4* f4 = reinterpret_cast<float4*>(xf + jb.dst);
+  T* a = xa + jb.dst;
+  T* lo = xlo ? xlo + jb.dst : nullptr;
+  const long n4 = jb.n / 4;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    const float4 u = s4[i];
+    const float4 v = make_float4(u.x * scale, u.y * scale, u.z * scale, u.w * scale);
+    f4[i] = v;
+    st4<T>(a + 4 * i, v);
+    if (lo) {
+      const float4 h = make_float4(ld<T>(a + 4 * i), ld<T>(a + 4 * i + 1), ld<T>(a + 4 * i + 2), ld<T>(a + 4 * i + 3));
+      st4<T>(lo + 4 * i, make_float4(v.x - h.x, v.y - h.y, v.z - h.z, v.w - h.w));
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) muon_apply_batched_kernel(float* __restrict__ w, T* __restrict__ wa,
+                                                                 const float* __restrict__ x, float lr,
+                                                                 const MuonVecJob* __restrict__ jobs,
+                                                                 const float* __restrict__ row_scale) {
+  const MuonVecJob jb = jobs[blockIdx.y];
+  float4* w4 = reinterpret_cast<float4*>(w + jb.src);
+  const float4* x4 = reinterpret_cast<const float4*>(x + jb.dst);
+  T* a = wa ? wa + jb.wact : nullptr;
+  const float* rs = row_scale ? row_scale + jb.srow : nullptr;
+  const long n4 = jb.n / 4;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    float4 v = w4[i];
+    const float4 q = x4[i];
+    const float f = rs ? lr * rs[4 * i / jb.cols] : lr;  // cols % 4 == 0: one row
+    v.x -= f * q.x; v.y -= f * q.y; v.z -= f * q.z; v.w -= f * q.w;
+    w4[i] = v;
+    if (a) st4<T>(a + 4 * i, v);
+  }
+}
+
 // W -= lr * X without a transpose, four consecutive elements per thread
 template <typename T>
 __global__ void __launch_bounds__(256) muon_apply_vec_kernel(float* __restrict__ w, T* __restrict__ wa,
@@ -1325,6 +1372,58 @@ __global__ void __launch_bounds__(256) amax_vec_kernel(const T* __restrict__ x, 
   __syncthreads();
   if (threadIdx.x == 0) {
     m = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    atomicMax(amax_bits, __float_as_uint(m));
+  }
+}
+
+// two-stage form: each block's max into partials[blockIdx.x] (plain stores), then one
+// block folds the partials into the slot with a single atomic.  Thousands of atomics on
+// one address from every XCD serialise; this keeps the pass bandwidth-bound.
+template <typename T>
+__global__ void __launch_bounds__(256) amax_part_kernel(const T* __restrict__ x, long rows, long cols8, long ldx,
+                                                        float* __restrict__ partials) {
+  __shared__ float sm[4];
+  float m = 0.f;
+  auto take = [&](const T* p) {
+    float f[8];
+    load8f<T>(p, f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[k]));
+  };
+  if (ldx == cols8 * 8) {
+    const long n = rows * cols8, stride = (long)gridDim.x * 256;
+    long i = blockIdx.x * 256L + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+      float f[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8f<T>(x + (i + u * stride) * 8, f[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[u][k]));
+    }
+    for (; i < n; i += stride) take(x + i * 8);
+  } else {
+    for (long r = blockIdx.x; r < rows; r += gridDim.x)
+      for (long c = threadIdx.x; c < cols8; c += 256) take(x + r * ldx + c * 8);
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+
+__global__ void __launch_bounds__(1024) amax_final_kernel(const float* __restrict__ partials, int n,
+                                                          unsigned* amax_bits) {
+  __shared__ float sm[16];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, partials[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; ++w) m = fmaxf(m, sm[w]);
+    m = fmaxf(m, sm[0]);
     atomicMax(amax_bits, __float_as_uint(m));
   }
 }
@@ -1675,6 +1774,31 @@ void launch_ns_normalize(const float* src, const double* sumsq, int mat, float e
                        (float*)xa, (float*)nullptr);
 }
 
+void launch_ns_normalize_batched(const float* src, const double* sumsq, float eps, const MuonVecJob* jobs, int njobs,
+                                 float* xf, void* xa, void* xlo, int at, hipStream_t st) {
+  if (njobs <= 0) return;
+  const dim3 g(64, njobs), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(ns_normalize_batched_kernel<bf16_t>, g, b, 0, st, src, sumsq, eps, jobs, xf, (bf16_t*)xa,
+                       (bf16_t*)xlo);
+  else if (at == ACT_F16)
+    hipLaunchKernelGGL(ns_normalize_batched_kernel<f16_t>, g, b, 0, st, src, sumsq, eps, jobs, xf, (f16_t*)xa,
+                       (f16_t*)xlo);
+  else
+    hipLaunchKernelGGL(ns_normalize_batched_kernel<float>, g, b, 0, st, src, sumsq, eps, jobs, xf, (float*)xa,
+                       (float*)nullptr);
+}
+
+void launch_muon_apply_batched(float* w, void* wa, int at, const float* x, float lr, const MuonVecJob* jobs,
+                               int njobs, const float* row_scale, hipStream_t st) {
+  if (njobs <= 0) return;
+  const dim3 g(64, njobs), b(256);
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(muon_apply_batched_kernel<bf16_t>, g, b, 0, st, w, (bf16_t*)wa, x, lr, jobs, row_scale);
+  else
+    hipLaunchKernelGGL(muon_apply_batched_kernel<float>, g, b, 0, st, w, (float*)wa, x, lr, jobs, row_scale);
+}
+
 void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int rows, int cols, bool tr,
                        hipStream_t st, const float* row_scale) {
   const long n = (long)rows * cols;
@@ -1802,9 +1926,22 @@ void launch_adamw(float* w, const float* g, float* m, float* v, void* w_act, int
                        rbc1, rbc2);
 }
 
-void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st) {
+void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st,
+                 float* partials) {
   const long n = rows * cols;
   if (n <= 0) return;
+  if (partials && cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0) {
+    const long n8 = n / 8;
+    const int g = (int)std::min<long>((n8 + 256L * 8 - 1) / (256L * 8), kAmaxParts);
+    if (it == ACT_BF16)
+      hipLaunchKernelGGL(amax_part_kernel<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t*)x, rows, cols / 8, ld,
+                         partials);
+    else
+      hipLaunchKernelGGL(amax_part_kernel<float>, dim3(g), dim3(256), 0, st, (const float*)x, rows, cols / 8, ld,
+                         partials);
+    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(1024), 0, st, partials, g, amax_bits);
+    return;
+  }
   if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0) {
     const long n8 = n / 8;
     const int g8 = (int)std::min<long>((n8 + 255) / 256, 2048);

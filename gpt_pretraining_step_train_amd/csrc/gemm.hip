@@ -127,6 +127,11 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
   float v = p.alpha * acc;
   if (p.epi == EPI_LINEAR) {
     if (p.Cin) v += p.beta * p.Cin[bz * p.strideCin + (long)row * p.ldcin + col];
+    else if (p.CinA) {
+      const long o = bz * p.strideCin + (long)row * p.ldcin + col;
+      v += p.beta * (p.dtype == ACT_F16 ? (float)reinterpret_cast<const _Float16*>(p.CinA)[o]
+                                        : load_act<OutT>(reinterpret_cast<const OutT*>(p.CinA) + o));
+    }
     if (p.outF) p.outF[bz * p.strideO + (long)row * p.ldo + col] = v;
     if (p.outA) {
       const long o = bz * p.strideOA + (long)row * p.ldoa + col;
@@ -144,10 +149,11 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
     if (p.outA) store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
     const float r = fmaxf(v, 0.f);
     store_act<OutT>(reinterpret_cast<OutT*>(p.out2) + o, r * r);
-  } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u)
+  } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u) (the hardware square
+           // root, within an ulp of fp32, far below the bf16 rounding of g itself)
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     const float g = load_act<OutT>(reinterpret_cast<const OutT*>(p.aux) + o);
-    store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v * 2.f * sqrtf(fmaxf(g, 0.f)));
+    store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v * 2.f * __builtin_amdgcn_sqrtf(fmaxf(g, 0.f)));
   }
 }
 
@@ -185,6 +191,11 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
     if (p.Cin) {
       const float4 c = *reinterpret_cast<const float4*>(p.Cin + bz * p.strideCin + (long)row * p.ldcin + col);
       v[0] += p.beta * c.x; v[1] += p.beta * c.y; v[2] += p.beta * c.z; v[3] += p.beta * c.w;
+    } else if (p.CinA) {
+      float c[4];
+      ld4_act(reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin + (long)row * p.ldcin + col, c,
+              p.dtype == ACT_F16);
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] += p.beta * c[t];
     }
     if (p.outF) {
       typedef float f4v __attribute__((ext_vector_type(4)));
@@ -213,7 +224,7 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     float g[4];
     ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + o, g);
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * sqrtf(fmaxf(g[t], 0.f));
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * __builtin_amdgcn_sqrtf(fmaxf(g[t], 0.f));
     st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
   }
 }

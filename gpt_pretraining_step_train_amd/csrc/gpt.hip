@@ -29,9 +29,14 @@ namespace {
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+#ifndef GPT_SLICE_ALIGN
+#define GPT_SLICE_ALIGN 256
+#endif
 struct Plan {
   size_t total = 0;
   size_t add(size_t bytes) {
+    // slices of 2 MiB and more start on a GPT_SLICE_ALIGN boundary (relative to the arena)
+    if (bytes >= ((size_t)2 << 20)) total = (total + GPT_SLICE_ALIGN - 1) / GPT_SLICE_ALIGN * GPT_SLICE_ALIGN;
     const size_t o = total;
     total += al256(bytes);
     return o;
@@ -82,8 +87,8 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
-      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      xq8t, amax, qinv, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
+      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, mv_jobs, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
+      xq8t, amax, qinv, amax_part, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
       nm_roff, nm_ws;
   size_t splitws_bytes;
 };
@@ -195,6 +200,7 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.ss = P.add(6 * L * 8);
   O.mat_off = P.add(6 * L * 8);
   O.mat_size = P.add(6 * L * 8);
+  O.mv_jobs = P.add(6 * L * sizeof(MuonVecJob));
   if (c.precision == GPT_FP8) {
     const size_t wide = std::max(std::max(qkv_dim(c), F), V);
     O.q8c = O.xq8t = 0;
@@ -210,8 +216,9 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
     else O.q8c = P.add(N * std::max(d, F));
     O.amax = P.add(kQuantSlots(c) * 4);
     O.qinv = P.add(kQuantSlots(c) * 4);
+    O.amax_part = P.add(kAmaxParts * 4);  // per-block maxima of the amax pass (reused, stream-ordered)
   } else {
-    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.xq8t = O.amax = O.qinv = 0;
+    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.xq8t = O.amax = O.qinv = O.amax_part = 0;
   }
   O.rope = P.add(T * (c.head_dim / 2) * 2 * 4);
   O.loss = P.add(8);
@@ -219,6 +226,30 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   *total = P.total;
   return O;
 }
+
+// Newton-Schulz workspace layout: every block matrix in its wide orientation, one batch
+// per shape: the d x d squares (q, k, v, o of each layer; only q and o when grouped-query
+// attention makes Wk, Wv kv x d, which then form their own batch), then the d x F pairs
+struct NsLayout {
+  int d, F, kv, s, lw;
+  bool kvsq;
+  size_t nsq, nkv;
+  explicit NsLayout(const gpt_cfg& c)
+      : d(c.d_model), F(c.d_ff), kv((int)kv_dim(c)), s(std::min(c.d_model, c.d_ff)), lw(std::max(c.d_model, c.d_ff)) {
+    kvsq = kv == d;
+    nsq = (size_t)(kvsq ? 4 : 2) * c.depth * d * d;
+    nkv = kvsq ? 0 : (size_t)2 * c.depth * kv * d;
+  }
+  size_t xdst(int l, int j) const {
+    if (j < 4 && kvsq) return (size_t)(4 * l + j) * d * d;
+    if (j == 0 || j == 3) return (size_t)(2 * l + (j == 3)) * d * d;
+    if (j < 4) return nsq + (size_t)(2 * l + (j - 1)) * kv * d;
+    return nsq + nkv + (size_t)(2 * l + (j - 4)) * s * lw;
+  }
+  int mrows(int j) const { return j == 4 ? F : (j == 1 || j == 2) ? kv : d; }
+  int mcols(int j) const { return j == 5 ? F : d; }
+  bool transposed(int j) const { return (j == 4 && F > d) || (j == 5 && d > F); }  // kv <= d: k, v are wide
+};
 
 // Operand capture (gpt_capture): the slots of one block layer's four Linear products,
 // or of the LM head, in byte sizes; each slot starts 256-byte aligned in the buffer.
@@ -272,6 +303,7 @@ struct gpt_model {
   // matrix table for Muon, in layer order (q, k, v, o, w1, w2); the first row of each
   // matrix in the stacked per-row NorMuon vectors (6L + 1 entries)
   std::vector<long> moff, msize, nm_roff;
+  std::vector<MuonVecJob> mv_jobs;  // batched normalise / apply jobs (uploaded by gpt_init)
   // profiling
   std::string prof_name;
   std::vector<hipEvent_t> ev;
@@ -539,7 +571,25 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
       return GPT_ERR_HIP;
     }
   }
-  if (hipMemcpyAsync(M->at_off<long>(O.mat_off), M->moff.data(), M->moff.size() * 8, hipMemcpyHostToDevice, st) !=
+  {
+    const NsLayout nsl(*cfg);
+    for (int l = 0; l < L; ++l)
+      for (int j = 0; j < 6; ++j)
+        if (!nsl.transposed(j)) {
+          MuonVecJob jb;
+          jb.src = M->moff[6 * l + j];
+          jb.dst = (long)nsl.xdst(l, j);
+          jb.wact = M->moff[6 * l + j];
+          jb.n = (long)nsl.mrows(j) * nsl.mcols(j);
+          jb.srow = M->nm_roff[6 * l + j];
+          jb.mat = 6 * l + j;
+          jb.cols = nsl.mcols(j);
+          M->mv_jobs.push_back(jb);
+        }
+  }
+  if (hipMemcpyAsync(M->at_off<MuonVecJob>(O.mv_jobs), M->mv_jobs.data(), M->mv_jobs.size() * sizeof(MuonVecJob),
+                     hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(M->at_off<long>(O.mat_off), M->moff.data(), M->moff.size() * 8, hipMemcpyHostToDevice, st) !=
           hipSuccess ||
       hipMemcpyAsync(M->at_off<long>(O.mat_size), M->msize.data(), M->msize.size() * 8, hipMemcpyHostToDevice,
                      st) != hipSuccess ||
@@ -589,7 +639,7 @@ static void quant_weights(gpt_model* M, hipStream_t st) {
   for (int w = 0; w <= 4 * M->cfg.depth; ++w) {
     const WInfo wi = winfo(M, w);
     const int slot = M->qslot++;
-    launch_amax(master + wi.off, ACT_F32, wi.rows, wi.cols, wi.cols, amax + slot, st);
+    launch_amax(master + wi.off, ACT_F32, wi.rows, wi.cols, wi.cols, amax + slot, st, M->at_off<float>(O.amax_part));
     launch_quant_e4m3(master + wi.off, ACT_F32, wi.rows, wi.cols, wi.cols, amax + slot,
                       M->at_off<uint8_t>(O.wq8) + wi.off, wi.cols, M->at_off<uint8_t>(O.wtq8) + wi.off, wi.rows,
                       wscale + w, st);
@@ -609,7 +659,7 @@ static int quant_act(gpt_model* M, const void* x, int rows, int cols, long ldx, 
                      hipStream_t st) {
   const int slot = M->qslot++;
   unsigned* amax = M->at_off<unsigned>(M->off.amax);
-  launch_amax(x, ACT_BF16, rows, cols, ldx, amax + slot, st);
+  launch_amax(x, ACT_BF16, rows, cols, ldx, amax + slot, st, M->at_off<float>(M->off.amax_part));
   launch_quant_e4m3(x, ACT_BF16, rows, cols, ldx, amax + slot, q, cols, qt, rows,
                     M->at_off<float>(M->off.qinv) + slot, st);
   return slot;
@@ -924,29 +974,43 @@ float gpt_step(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_c
   return gpt_step_accumulate(M, tok, tgt, cfg, 0, 1.f, stream);
 }
 
-float gpt_step_accumulate(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg,
-                          int32_t accumulate, float grad_scale, void* stream) {
-  if (!M) return NAN;
-  if (!tok || !tgt || !std::isfinite(grad_scale)) { M->last_status = GPT_ERR_ARG; return NAN; }
-  if (cfg && !same_shape(*cfg, M->cfg)) { M->last_status = GPT_ERR_SHAPE; return NAN; }
+int gpt_step_async(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg, int32_t accumulate,
+                   float grad_scale, void* stream) {
+  if (!M) return GPT_ERR_ARG;
+  if (!tok || !tgt || !std::isfinite(grad_scale)) return M->last_status = GPT_ERR_ARG;
+  if (cfg && !same_shape(*cfg, M->cfg)) return M->last_status = GPT_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
   M->acc_grads = accumulate != 0;
   int rc = forward_backward(M, tok, tgt, grad_scale, st);
   M->acc_grads = false;
-  if (rc) { M->last_status = rc; return NAN; }
+  if (!rc && hipGetLastError() != hipSuccess) rc = GPT_ERR_HIP;
+  if (rc) return M->last_status = rc;
+  M->stepped = true;
+  return M->last_status = GPT_OK;
+}
+
+float gpt_step_result(gpt_model* M, void* stream) {
+  if (!M) return NAN;
+  if (!M->stepped) { M->last_status = GPT_ERR_ARG; return NAN; }
+  hipStream_t st = (hipStream_t)stream;
   struct { double loss; int err[4]; } h;
-  if (hipGetLastError() != hipSuccess ||
-      hipMemcpyAsync(&h.loss, M->base + M->off.loss, 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+  if (hipMemcpyAsync(&h.loss, M->base + M->off.loss, 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipMemcpyAsync(h.err, M->base + M->off.err, 16, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
     M->last_status = GPT_ERR_HIP;
     return NAN;
   }
-  M->stepped = true;
   if (h.err[0] & 1) { M->last_status = GPT_ERR_TOKEN_RANGE; return NAN; }
   if (h.err[0] & 2) { M->last_status = GPT_ERR_NONFINITE; return NAN; }
   M->last_status = GPT_OK;
   return (float)(h.loss / (double)M->N);
+}
+
+float gpt_step_accumulate(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg,
+                          int32_t accumulate, float grad_scale, void* stream) {
+  if (!M) return NAN;
+  if (gpt_step_async(M, tok, tgt, cfg, accumulate, grad_scale, stream) != GPT_OK) return NAN;
+  return gpt_step_result(M, stream);
 }
 
 int adamw_update(gpt_model* M, float lr, float beta1, float beta2, float eps, float weight_decay, void* stream) {
@@ -972,6 +1036,78 @@ int adamw_update(gpt_model* M, float lr, float beta1, float beta2, float eps, fl
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 
+extern "C++" {
+// The Newton-Schulz iterations on a batch of nb matrices X [s][l] (wide orientation)
+// stored one after another from element offset off: A = X X^T, B = b A + c A A, X <- a X
+// + B X, every product on MFMA with operands of type nat (fp16 by default; bf16 with hi /
+// lo planes in the first nsplit iterations; fp32 for the all-fp32 configuration) and fp32
+// accumulation, X carried in fp32 (xf) and as operand planes (xa, xl, ping-ponged).
+struct NsBuffers {
+  float* xf;
+  char* xa[2];
+  char* xl[2];
+  size_t es;
+  float* Af;
+  void *Aa, *Ba, *Alo, *Blo;
+};
+template <typename Run>
+static int ns_iterate(int nat, int nsplit, int steps, const float (*coeffs)[3], int s, int l, int nb_, size_t off,
+                      const NsBuffers& nb, Run&& run) {
+  int cur = 0, rc;
+  const long ss = (long)s * s, sl = (long)s * l;
+  const size_t es = nb.es;
+  for (int it = 0; it < steps; ++it) {
+    const float a = coeffs[it][0], b = coeffs[it][1], cc = coeffs[it][2];
+    const bool sp = it < nsplit;           // this iteration multiplies hi/lo planes
+    const bool next_sp = it + 1 < nsplit;  // the next one needs X's lo plane
+    const void* xh = nb.xa[cur] + off * es;
+    const void* xlo = nb.xl[cur] ? nb.xl[cur] + off * es : nullptr;
+    {
+      GemmArgs p;  // A = X X^T
+      p.sym = true;
+      p.dtype = nat;
+      p.M = s; p.N = s; p.K = l; p.batch = nb_;
+      p.A = xh; p.lda = l; p.strideA = sl;
+      p.B = xh; p.ldb = l; p.strideB = sl;
+      if (nat != ACT_F16) { p.outF = nb.Af; p.ldo = s; p.strideO = ss; }  // fp16: the b A term reads Aa
+      p.outA = nb.Aa; p.ldoa = s; p.strideOA = ss;
+      if (sp) p.outA_lo = nb.Alo;
+      if ((rc = run(p))) return rc;
+    }
+    {
+      GemmArgs p;  // Bm = b A + c A A   (A symmetric)
+      p.sym = true;
+      p.dtype = nat;
+      p.split = sp; p.A_lo = nb.Alo; p.B_lo = nb.Alo;
+      p.M = s; p.N = s; p.K = s; p.batch = nb_;
+      p.A = nb.Aa; p.lda = s; p.strideA = ss;
+      p.B = nb.Aa; p.ldb = s; p.strideB = ss;
+      p.alpha = cc; p.beta = b; p.ldcin = s; p.strideCin = ss;
+      if (nat == ACT_F16) p.CinA = nb.Aa;
+      else p.Cin = nb.Af;
+      p.outA = nb.Ba; p.ldoa = s; p.strideOA = ss;
+      if (sp) p.outA_lo = nb.Blo;
+      if ((rc = run(p))) return rc;
+    }
+    {
+      GemmArgs p;  // X <- a X + Bm X   (fp32 X read and written by the same thread)
+      p.dtype = nat;
+      p.split = sp; p.A_lo = nb.Blo; p.B_lo = xlo;
+      p.M = s; p.N = l; p.K = s; p.batch = nb_;
+      p.A = nb.Ba; p.lda = s; p.strideA = ss;
+      p.B = xh; p.ldb = l; p.strideB = sl; p.b_kmaj = false;
+      p.beta = a; p.Cin = nb.xf + off; p.ldcin = l; p.strideCin = sl;
+      p.outF = nb.xf + off; p.ldo = l; p.strideO = sl;
+      p.outA = nb.xa[cur ^ 1] + off * es; p.ldoa = l; p.strideOA = sl;
+      if (next_sp) p.outA_lo = nb.xl[cur ^ 1] + off * es;
+      if ((rc = run(p))) return rc;
+    }
+    cur ^= 1;
+  }
+  return GPT_OK;
+}
+}  // extern "C++"
+
 int muon_update(gpt_model* M, float lr, void* stream) {
   if (!M) return GPT_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
@@ -985,7 +1121,9 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   char* xl[2] = {M->base + O.xl0, M->base + O.xl1};
   // 16-bit precisions: by default every product takes fp16 operands (11 significant
   // bits, the bf16 MFMA rate; X, A and B stay well inside fp16's range), with X carried
-  // in fp32 for the a X term.  With ns_split_steps > 0 the products run on bf16 MFMA
+  // in fp32 for the a X term (an fp16 carry loses the small entries of low-rank-plus-noise
+  // momenta to fp16's subnormals) and the b A term read from A's fp16 plane (as accurate
+  // as an fp32 A in a numpy model of the iteration, and 4 bytes per element less).  With ns_split_steps > 0 the products run on bf16 MFMA
   // instead, and the leading iterations multiply A A and B X with operands carried as
   // bf16 hi + lo planes (three MFMA products each): rounding errors of the early
   // iterations are amplified by the later ones along small singular directions, those
@@ -1003,24 +1141,26 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   // shape: the d x d squares (q, k, v, o of each layer; only q and o when grouped-query
   // attention makes Wk, Wv kv x d, which then form their own batch), then the d x F
   // pairs
-  const int kv = (int)kv_dim(c);
-  const bool kvsq = kv == d;  // k and v join the squares
-  const size_t nsq = (size_t)(kvsq ? 4 : 2) * L * d * d, nkv = kvsq ? 0 : (size_t)2 * L * kv * d;
-  auto xdst = [&](int l, int j) -> size_t {
-    if (j < 4 && kvsq) return (size_t)(4 * l + j) * d * d;
-    if (j == 0 || j == 3) return (size_t)(2 * l + (j == 3)) * d * d;
-    if (j < 4) return nsq + (size_t)(2 * l + (j - 1)) * kv * d;
-    return nsq + nkv + (size_t)(2 * l + (j - 4)) * s * lw;
-  };
-  auto mrows = [&](int j) { return j == 4 ? F : (j == 1 || j == 2) ? kv : d; };
-  auto transposed = [&](int j) { return (j == 4 && F > d) || (j == 5 && d > F); };  // kv <= d: k, v are wide
+  const NsLayout nsl(c);
+  const int kv = nsl.kv;
+  const bool kvsq = nsl.kvsq;  // k and v join the squares
+  const size_t nsq = nsl.nsq, nkv = nsl.nkv;
+  auto xdst = [&](int l, int j) { return nsl.xdst(l, j); };
+  auto mrows = [&](int j) { return nsl.mrows(j); };
+  auto transposed = [&](int j) { return nsl.transposed(j); };
+  // the untransposed matrices (all but W1 when F > d) in one launch per pass, from the job
+  // table gpt_init uploaded; the transposed ones one by one
+  const MuonVecJob* jobs = M->at_off<MuonVecJob>(O.mv_jobs);
+  const int njobs = (int)M->mv_jobs.size();
+  launch_ns_normalize_batched(mom, M->at_off<double>(O.ss), 1e-7f, jobs, njobs, xf, xa[0],
+                              nsplit > 0 ? xl[0] : nullptr, nat, st);
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
+      if (!transposed(j)) continue;
       const int rows = mrows(j), cols = j == 5 ? F : d;
       const size_t dst = xdst(l, j);
       launch_ns_normalize(mom + M->moff[6 * l + j], M->at_off<double>(O.ss), 6 * l + j, 1e-7f, rows, cols,
-                          transposed(j), xf + dst, xa[0] + dst * es, nsplit > 0 ? xl[0] + dst * es : nullptr, nat,
-                          st);
+                          true, xf + dst, xa[0] + dst * es, nsplit > 0 ? xl[0] + dst * es : nullptr, nat, st);
     }
   struct Batch { int s, l, nb; size_t off; };
   const Batch all_batches[3] = {{d, d, (kvsq ? 4 : 2) * L, 0}, {kv, d, 2 * L, nsq}, {s, lw, 2 * L, nsq + nkv}};
@@ -1033,56 +1173,10 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   void* Alo = M->base + O.Al;
   void* Blo = M->base + O.Bl;
   int rc;
-  for (const Batch& bt : batches) {
-    int cur = 0;
-    const long ss = (long)bt.s * bt.s, sl = (long)bt.s * bt.l;
-    for (int it = 0; it < c.ns_steps; ++it) {
-      const float a = c.ns_coeffs[it][0], b = c.ns_coeffs[it][1], cc = c.ns_coeffs[it][2];
-      const bool sp = it < nsplit;                      // this iteration multiplies hi/lo planes
-      const bool next_sp = it + 1 < nsplit;             // the next one needs X's lo plane
-      const void* xh = xa[cur] + bt.off * es;
-      const void* xlo = xl[cur] + bt.off * es;
-      {
-        GemmArgs p;  // A = X X^T
-        p.sym = true;
-        p.dtype = nat;
-        p.M = bt.s; p.N = bt.s; p.K = bt.l; p.batch = bt.nb;
-        p.A = xh; p.lda = bt.l; p.strideA = sl;
-        p.B = xh; p.ldb = bt.l; p.strideB = sl;
-        p.outF = Af; p.ldo = bt.s; p.strideO = ss;
-        p.outA = Aa; p.ldoa = bt.s; p.strideOA = ss;
-        if (sp) p.outA_lo = Alo;
-        if ((rc = run_gemm(M, p, st, false))) return rc;
-      }
-      {
-        GemmArgs p;  // Bm = b A + c A A   (A symmetric)
-        p.sym = true;
-        p.dtype = nat;
-        p.split = sp; p.A_lo = Alo; p.B_lo = Alo;
-        p.M = bt.s; p.N = bt.s; p.K = bt.s; p.batch = bt.nb;
-        p.A = Aa; p.lda = bt.s; p.strideA = ss;
-        p.B = Aa; p.ldb = bt.s; p.strideB = ss;
-        p.alpha = cc; p.beta = b; p.Cin = Af; p.ldcin = bt.s; p.strideCin = ss;
-        p.outA = Ba; p.ldoa = bt.s; p.strideOA = ss;
-        if (sp) p.outA_lo = Blo;
-        if ((rc = run_gemm(M, p, st, false))) return rc;
-      }
-      {
-        GemmArgs p;  // X <- a X + Bm X   (fp32 X read and written by the same thread)
-        p.dtype = nat;
-        p.split = sp; p.A_lo = Blo; p.B_lo = xlo;
-        p.M = bt.s; p.N = bt.l; p.K = bt.s; p.batch = bt.nb;
-        p.A = Ba; p.lda = bt.s; p.strideA = ss;
-        p.B = xh; p.ldb = bt.l; p.strideB = sl; p.b_kmaj = false;
-        p.beta = a; p.Cin = xf + bt.off; p.ldcin = bt.l; p.strideCin = sl;
-        p.outF = xf + bt.off; p.ldo = bt.l; p.strideO = sl;
-        p.outA = xa[cur ^ 1] + bt.off * es; p.ldoa = bt.l; p.strideOA = sl;
-        if (next_sp) p.outA_lo = xl[cur ^ 1] + bt.off * es;
-        if ((rc = run_gemm(M, p, st, false))) return rc;
-      }
-      cur ^= 1;
-    }
-  }
+  const NsBuffers nb{xf, {xa[0], xa[1]}, {xl[0], xl[1]}, es, Af, Aa, Ba, Alo, Blo};
+  auto run = [&](const GemmArgs& p) { return run_gemm(M, p, st, false); };
+  for (const Batch& bt : batches)
+    if ((rc = ns_iterate(nat, nsplit, c.ns_steps, c.ns_coeffs, bt.s, bt.l, bt.nb, bt.off, nb, run))) return rc;
   // NorMuon: per output row, the running second moment of the update; rows scaled by its
   // inverse root, the update's Frobenius norm kept
   const bool nm = c.extras & GPT_EXTRA_NORMUON;
@@ -1096,12 +1190,15 @@ int muon_update(gpt_model* M, float lr, void* stream) {
                          c.normuon_beta2, nm_scale, st);
   }
   float* wblk = M->blk(M->params());
+  launch_muon_apply_batched(wblk, M->at == ACT_BF16 ? M->wact(0) : nullptr, M->at, xf, lr, jobs, njobs,
+                            nm ? nm_scale : nullptr, st);
   for (int l = 0; l < L; ++l)
     for (int j = 0; j < 6; ++j) {
+      if (!transposed(j)) continue;
       const int rows = mrows(j), cols = j == 5 ? F : d;
       const size_t mo = M->moff[6 * l + j];
       launch_muon_apply(wblk + mo, M->at == ACT_BF16 ? M->wact(mo) : nullptr, M->at, xf + xdst(l, j), lr, rows, cols,
-                        transposed(j), st, nm ? nm_scale + M->nm_roff[6 * l + j] : nullptr);
+                        true, st, nm ? nm_scale + M->nm_roff[6 * l + j] : nullptr);
     }
   M->wq_dirty = true;
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
@@ -1277,6 +1374,74 @@ int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, cons
   p.outF = C; p.ldo = ldc; p.strideO = sC;
   const int rc = launch_gemm(p, (hipStream_t)stream);
   if (rc) return rc == 1 ? GPT_ERR_ARG : GPT_ERR_SHAPE;
+  return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+// workspace of gptk_newton_schulz: the copy whose Frobenius norm is taken, the fp32
+// carried X, two operand planes of X, A and B (fp32 A too for the fp32 path), the
+// sum-of-squares partials and the one-matrix table
+static size_t ns_ws_layout(int rows, int cols, size_t* o) {
+  const size_t n = (size_t)rows * cols, s = std::min(rows, cols);
+  Plan P;
+  o[0] = P.add(n * 4);                // copy of G
+  o[1] = P.add(n * 4);                // xf
+  o[2] = P.add(n * 4);                // xa0 (fp32 path: 4 bytes per element)
+  o[3] = P.add(n * 4);                // xa1
+  o[4] = P.add(s * s * 4);            // Af
+  o[5] = P.add(s * s * 4);            // Aa
+  o[6] = P.add(s * s * 4);            // Ba
+  o[7] = P.add(kSumsqParts * 8 + 8);  // sum-of-squares partials and total
+  o[8] = P.add(16);                   // offset and size of the one matrix
+  return P.total;
+}
+
+size_t gptk_ns_ws_bytes(int rows, int cols) {
+  if (rows < 1 || cols < 1) return 0;
+  size_t o[9];
+  return ns_ws_layout(rows, cols, o);
+}
+
+int gptk_newton_schulz(int dtype, const float* G, int rows, int cols, const float* coeffs, int steps, float* X,
+                       void* ws, size_t ws_bytes, void* stream) {
+  const int at = act_type(dtype);
+  if (at < 0) return GPT_ERR_UNSUPPORTED;
+  if (!G || !X || !coeffs || !ws || rows < 1 || cols < 1 || steps < 0 || steps > 5 || ((uintptr_t)ws & 255))
+    return GPT_ERR_ARG;
+  if (rows % 8 || cols % 8) return GPT_ERR_SHAPE;  // the 16-bit operand planes take 8-element rows
+  size_t o[9];
+  if (ws_bytes < ns_ws_layout(rows, cols, o)) return GPT_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const bool tr = rows > cols;  // a tall G is orthogonalised as G^T
+  const int s = std::min(rows, cols), l = std::max(rows, cols);
+  const int nat = at == ACT_BF16 ? ACT_F16 : ACT_F32;
+  const size_t es = nat == ACT_F16 ? 2 : 4;
+  float* copy = (float*)(w + o[0]);
+  float* xf = (float*)(w + o[1]);
+  double* part = (double*)(w + o[7]);
+  double* ss = part + kSumsqParts;
+  const long table[2] = {0, (long)rows * cols};  // pageable: copied before hipMemcpyAsync returns
+  if (hipMemcpyAsync(w + o[8], table, sizeof(table), hipMemcpyHostToDevice, st) != hipSuccess) return GPT_ERR_HIP;
+  // copy = 0 * copy + G (a momentum update with mu = 0), and its sum of squares
+  launch_zero(copy, (size_t)rows * cols * 4, st);
+  launch_momentum_sumsq(copy, G, 0.f, (const long*)(w + o[8]), (const long*)(w + o[8]) + 1, 1, part, kSumsqParts, ss,
+                        st);
+  launch_ns_normalize(copy, ss, 0, 1e-7f, rows, cols, tr, xf, w + o[2], nullptr, nat, st);
+  float cf[5][3];
+  for (int i = 0; i < steps; ++i)
+    for (int j = 0; j < 3; ++j) cf[i][j] = coeffs[3 * i + j];
+  const NsBuffers nb{xf, {w + o[2], w + o[3]}, {nullptr, nullptr}, es, (float*)(w + o[4]), w + o[5], w + o[6], nullptr,
+                     nullptr};
+  auto run = [&](const GemmArgs& p0) {
+    GemmArgs p = p0;
+    p.splits = 1;
+    return launch_gemm(p, st) ? GPT_ERR_SHAPE : GPT_OK;
+  };
+  int rc = ns_iterate(nat, 0, steps, cf, s, l, 1, 0, nb, run);
+  if (rc) return rc;
+  // X = the result in G's orientation: X = 0 - (-1) xf (transposed back for a tall G)
+  launch_zero(X, (size_t)rows * cols * 4, st);
+  launch_muon_apply(X, nullptr, ACT_F32, xf, -1.f, rows, cols, tr, st, nullptr);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
 }
 

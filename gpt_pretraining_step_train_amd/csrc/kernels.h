@@ -24,6 +24,7 @@ struct GemmArgs {
   int epi = EPI_LINEAR;
   float alpha = 1.f, beta = 0.f;
   const float* Cin = nullptr; long ldcin = 0, strideCin = 0;
+  const void* CinA = nullptr;     // Cin in the operand's 16-bit type instead (when Cin is null; same ld/stride)
   float* outF = nullptr; long ldo = 0, strideO = 0;
   void* outA = nullptr; long ldoa = 0, strideOA = 0;
   void* out2 = nullptr;           // EPI_RELU2 second output (same ld/stride as outA)
@@ -130,6 +131,22 @@ void launch_adamw(float* w, const float* g, float* m, float* v, void* w_act, int
                   float b1, float b2, float eps, float wd, float rbc1, float rbc2, hipStream_t st);
 // m = mu m + g on every listed matrix (matrix i occupies [offs[i], offs[i]+sizes[i]), offsets
 // multiples of 4) and the per-matrix sums of squares of the new m, in one pass
+// one matrix of the batched Muon elementwise passes (normalise, apply): element offsets of
+// its source (momentum / fp32 master) and destination (NS workspace) in their regions and
+// of its act-typed weight copy, its size (a multiple of 4), its sum-of-squares index, its
+// columns and the first of its NorMuon row scales
+struct MuonVecJob {
+  long src, dst, wact, n;
+  long srow;
+  int mat, cols;
+};
+// X0 = src / (sqrt(sumsq[mat]) + eps) for every job (no transposes): xf fp32, xa (and xlo)
+// act typed (at: ACT_BF16 or ACT_F16)
+void launch_ns_normalize_batched(const float* src, const double* sumsq, float eps, const MuonVecJob* jobs, int njobs,
+                                 float* xf, void* xa, void* xlo, int at, hipStream_t st);
+// W -= lr (s[row]) X for every job (no transposes), act copy refreshed when wa
+void launch_muon_apply_batched(float* w, void* wa, int at, const float* x, float lr, const MuonVecJob* jobs,
+                               int njobs, const float* row_scale, hipStream_t st);
 void launch_momentum_sumsq(float* m, const float* g, float mu, const long* offs, const long* sizes, int nmat,
                            double* partial, int parts, double* out, hipStream_t st);
 // X = src / (norm + eps) written (optionally transposed) into fp32 and act copies
@@ -150,7 +167,10 @@ void launch_normuon_scale(const float* vmean, float* V, const long* roff, int nm
 
 // fp8 (OCP e4m3fn) per-tensor current scaling.  amax slot: one uint32 holding the bits of
 // max|x| (non-negative floats order as integers); must be zeroed before launch_amax.
-void launch_amax(const void* x, int in_type, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st);
+// partials (kAmaxParts floats of scratch, or null): the two-stage form, one atomic in all.
+constexpr int kAmaxParts = 1024;
+void launch_amax(const void* x, int in_type, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st,
+                 float* partials = nullptr);
 // q[r][c] = e4m3(x[r][c] * s) and (optionally) qt[c][r] = the same byte, s = 448/amax
 // (1 when amax = 0); inv_scale[0] = 1/s.  in_type: ACT_F32 or ACT_BF16.
 void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, const unsigned* amax_bits,

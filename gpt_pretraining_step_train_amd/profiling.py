@@ -1,11 +1,13 @@
 """Summaries of rocprofv3 output for the step's kernels.
 
 python -m gpt_pretraining_step_train_amd.profiling stats TRACE_DIR STEPS "COMMAND" > summary.md
+python -m gpt_pretraining_step_train_amd.profiling steps TRACE_DIR "COMMAND" > summary.md
 python -m gpt_pretraining_step_train_amd.profiling traffic --kernel REGEX --fetch DIR --write DIR \
     --copy-fetch DIR --copy-write DIR --copy-bytes N --name NAME --command "..." > traffic.md
 
 `stats` turns a `rocprofv3 --kernel-trace --stats` directory into a per-step
-table.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a
+table (totals over every dispatch); `steps` does the same from the kernel trace with
+the model's set-up kernels excluded.  `traffic` turns two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a
 program, and the same two counters over a plain device copy of known size, into
 calibrated HBM bytes per launch of one kernel; the result block carries a hash
 of the kernel sources so that `bench.py` reports it only while they are unchanged.
@@ -63,6 +65,39 @@ def stats_table(trace_dir: str, steps: int, command: str, top: int = 24) -> str:
     out.sort(reverse=True)
     lines = [f"Command: `{command}`", "",
              f"Kernel time per step (totals divided by {steps} step calls, warm-up included).", "",
+             "| kernel | launches/step | avg us | ms/step | share |", "|---|---|---|---|---|"]
+    for t, n, c, a in out[:top]:
+        lines.append(f"| `{n}` | {c:.0f} | {a:.1f} | {t:.2f} | {100 * t / total:.1f}% |")
+    lines.append(f"| (all kernels) | | | {total:.1f} | 100% |")
+    return "\n".join(lines) + "\n"
+
+
+# the first kernel of every gpt_step (the token-embedding gather) and its one-per-step
+# kernel (the fused cross-entropy): the model's set-up kernels run before the first
+STEP_FIRST = "embed_gather"
+STEP_MARK = "ce_kernel"
+
+
+def step_table(trace_dir: str, command: str, top: int = 28) -> str:
+    """Per-step kernel time from a `--kernel-trace` CSV: only dispatches from the first
+    step's first kernel on (gpt_init's weight fill, zeroing and casts excluded), divided
+    by the number of steps (cross-entropy dispatches)."""
+    rows = list(csv.DictReader(open(_one(trace_dir, "*kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    first = next(i for i, r in enumerate(rows) if STEP_FIRST in r["Kernel_Name"])
+    rows = rows[first:]
+    steps = sum(1 for r in rows if STEP_MARK in r["Kernel_Name"])
+    agg = {}
+    for r in rows:
+        n = _short(r["Kernel_Name"])
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        c, s_ = agg.get(n, (0, 0.0))
+        agg[n] = (c + 1, s_ + t)
+    total = sum(v[1] for v in agg.values()) / steps
+    out = sorted(((s_ / steps, n, c / steps, 1e3 * s_ / c) for n, (c, s_) in agg.items()), reverse=True)
+    lines = [f"Command: `{command}`", "",
+             f"Kernel time per step over {steps} steps (every dispatch from the first step's first kernel on;",
+             "the model's set-up kernels excluded).", "",
              "| kernel | launches/step | avg us | ms/step | share |", "|---|---|---|---|---|"]
     for t, n, c, a in out[:top]:
         lines.append(f"| `{n}` | {c:.0f} | {a:.1f} | {t:.2f} | {100 * t / total:.1f}% |")
@@ -133,6 +168,9 @@ def main(argv=None) -> int:
     s.add_argument("trace_dir")
     s.add_argument("steps", type=int)
     s.add_argument("command")
+    q = sub.add_parser("steps")
+    q.add_argument("trace_dir")
+    q.add_argument("command")
     t = sub.add_parser("traffic")
     for k in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--name", "--command"):
         t.add_argument(k, required=True)
@@ -142,6 +180,8 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_table(a.trace_dir, a.steps, a.command))
+    elif a.cmd == "steps":
+        sys.stdout.write(step_table(a.trace_dir, a.command))
     else:
         sys.stdout.write(traffic_block(a))
     return 0

@@ -158,6 +158,23 @@ float gpt_step(gpt_model* m, const int32_t* d_tokens, const int32_t* d_targets, 
 float gpt_step_accumulate(gpt_model* m, const int32_t* d_tokens, const int32_t* d_targets, const gpt_cfg* cfg,
                           int32_t accumulate, float grad_scale, void* stream);
 
+/* gpt_step_accumulate in two halves, for callers that enqueue several steps before
+ * reading a loss, or record the step (with muon_update) into a HIP graph:
+ * gpt_step_async enqueues the forward and backward on the stream and returns at once
+ * (argument and launch errors as a gpt_status; no synchronisation, no device memory
+ * allocated, no memset node: every buffer the step clears is cleared by a kernel);
+ * gpt_step_result synchronises the stream and returns the mean loss of the last
+ * enqueued step, or NaN with gpt_last_status set (token range, non-finite logits).
+ * In a graph, the loss and error flags of the last replay stay on the device until
+ * gpt_step_result reads them.  A graph records the host-side choices made while it is
+ * captured: the e4m3 weight refresh of an fp8 step is recorded only when the weights
+ * changed before the capture (capture muon_update and the next step together), and
+ * adamw_update's step counter is fixed at capture, so AdamW does not belong in a
+ * replayed graph. */
+int gpt_step_async(gpt_model* m, const int32_t* d_tokens, const int32_t* d_targets, const gpt_cfg* cfg,
+                   int32_t accumulate, float grad_scale, void* stream);
+float gpt_step_result(gpt_model* m, void* stream);
+
 /* Copy the fp32 gradient of tensor `tensor_id` (n elements) to host memory. */
 int gpt_grads(gpt_model* m, int32_t tensor_id, float* h_out, size_t n, void* stream);
 
@@ -271,6 +288,18 @@ int gptk_gemm_auto_splits(int dtype, int a_kmaj, int b_kmaj, int M, int N, int K
 int gptk_gemm_split(int a_kmaj, int b_kmaj, int M, int N, int K, int batch, const void* Ah, const void* Al, long lda,
                     long sA, const void* Bh, const void* Bl, long ldb, long sB, float* C, long ldc, long sC,
                     void* stream);
+
+/* Muon's orthogonalisation of one matrix, exactly as muon_update runs it on every
+ * block matrix ("2. Muon Optimize Edici": X0 = G / (|G|_F + 1e-7), then `steps` (<= 5)
+ * Polar-Express iterations with the table coeffs = [a0 b0 c0 a1 b1 c1 ...]): on the wide
+ * orientation (a tall G is orthogonalised as G^T and transposed back), A = X X^T,
+ * B = b A + c A A, X <- a X + B X, every product on MFMA with fp32 accumulation and X
+ * carried in fp32; dtype GPT_BF16 = the 16-bit schedule (fp16 operands), GPT_FP32 = fp32
+ * operands.  G, X fp32 [rows][cols] (rows, cols multiples of 8, else GPT_ERR_SHAPE), ws
+ * device scratch of gptk_ns_ws_bytes(rows, cols) bytes, 256-byte aligned. */
+size_t gptk_ns_ws_bytes(int rows, int cols);
+int gptk_newton_schulz(int dtype, const float* G, int rows, int cols, const float* coeffs, int steps, float* X,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* fp8 (OCP e4m3fn) per-tensor current scaling of x [rows][cols] (row stride ld, fp32 or
  * bf16 by dtype): s = 448 / max|x| (1 when x is all zero); q [rows][cols] and/or qt

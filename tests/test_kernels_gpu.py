@@ -630,3 +630,34 @@ def test_gemm_fp8_on_e4m3_values(M, N, K, splits):
     assert np.all(err <= bound)
     say(f"  fp8 accumulation error max {err.max():.3g} (max err/bound {np.max(err / bound):.2f}) of max|C| "
         f"{np.abs(ref).max():.3g}")
+
+
+# ----------------------------------------------------------------------------- Newton-Schulz
+
+# (dtype, rows, cols, kind): the d24 square, grouped-query Wk (wide), W1 (tall: run as its
+# transpose) and W2 shapes, small ragged ones, and a low-rank-plus-noise momentum (the
+# case whose small singular directions the fp32-carried X must keep)
+NS_CASES = [("bf16", 1536, 1536, "gauss"), ("bf16", 512, 1536, "gauss"), ("bf16", 6144, 1536, "gauss"),
+            ("bf16", 1536, 6144, "lowrank"), ("bf16", 136, 264, "gauss"), ("bf16", 264, 136, "lowrank"),
+            ("fp32", 128, 512, "gauss"), ("fp32", 512, 128, "lowrank")]
+
+
+@pytest.mark.parametrize("case", NS_CASES)
+def test_newton_schulz_matches_the_oracle(case):
+    """gptk_newton_schulz (the orthogonalisation muon_update runs on every block matrix)
+    against the oracle's normalisation + Polar-Express iterations on the same matrix."""
+    from oracle import polar_express as PE
+    dtype, rows, cols, kind = case
+    rng = np.random.default_rng(rows + 7 * cols)
+    if kind == "gauss":
+        G = rng.standard_normal((rows, cols))
+    else:
+        G = rng.standard_normal((rows, 16)) @ rng.standard_normal((16, cols)) + 0.05 * rng.standard_normal((rows, cols))
+    G = G.astype(np.float32)
+    table, _ = PE.coefficients()
+    X = torch.empty(rows, cols, device="cuda")
+    B.newton_schulz(DT[dtype], torch.from_numpy(G).cuda(), rows, cols, table, 5, X)
+    ref, _ = O.muon_matrix(G, np.zeros_like(G, dtype=np.float64), table, mu=0.0)
+    e = rel_l2(from_dev(X), ref)
+    say(f"  NS {case}: rel L2 {e:.2e}")
+    assert e < (1e-4 if dtype == "fp32" else 2e-2)
