@@ -127,11 +127,6 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
   float v = p.alpha * acc;
   if (p.epi == EPI_LINEAR) {
     if (p.Cin) v += p.beta * p.Cin[bz * p.strideCin + (long)row * p.ldcin + col];
-    else if (p.CinA) {
-      const long o = bz * p.strideCin + (long)row * p.ldcin + col;
-      v += p.beta * (p.dtype == ACT_F16 ? (float)reinterpret_cast<const _Float16*>(p.CinA)[o]
-                                        : load_act<OutT>(reinterpret_cast<const OutT*>(p.CinA) + o));
-    }
     if (p.outF) p.outF[bz * p.strideO + (long)row * p.ldo + col] = v;
     if (p.outA) {
       const long o = bz * p.strideOA + (long)row * p.ldoa + col;
@@ -146,7 +141,6 @@ __device__ inline void epilogue_elem(const GemmArgs& p, int bz, int row, int col
     }
   } else if (p.epi == EPI_RELU2) {
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
-    if (p.outA) store_act<OutT>(reinterpret_cast<OutT*>(p.outA) + o, v);
     const float r = fmaxf(v, 0.f);
     store_act<OutT>(reinterpret_cast<OutT*>(p.out2) + o, r * r);
   } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u) (the hardware square
@@ -185,17 +179,24 @@ __device__ inline void ld4_act(const bf16_t* q, float (&v)[4], bool h = false) {
 
 // Outputs leave with nontemporal stores: written once per launch, they need not
 // displace the operands' lines (the epilogue's cost per tile fell 8-13%).
+// element t of a float4 by selects (a runtime index into a local array would live in scratch)
+__device__ inline float pick4(const float4& a, int t) { return t == 0 ? a.x : t == 1 ? a.y : t == 2 ? a.z : a.w; }
+
+// HALF: the fp16-operand NT instantiations (the Newton-Schulz A A product), the only ones that
+// read CinA
+template <bool HALF = false>
 __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col, float4 a) {
   float v[4] = {p.alpha * a.x, p.alpha * a.y, p.alpha * a.z, p.alpha * a.w};
   if (p.epi == EPI_LINEAR) {
     if (p.Cin) {
       const float4 c = *reinterpret_cast<const float4*>(p.Cin + bz * p.strideCin + (long)row * p.ldcin + col);
       v[0] += p.beta * c.x; v[1] += p.beta * c.y; v[2] += p.beta * c.z; v[3] += p.beta * c.w;
-    } else if (p.CinA) {
-      float c[4];
-      ld4_act(reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin + (long)row * p.ldcin + col, c,
-              p.dtype == ACT_F16);
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] += p.beta * c[t];
+    } else if constexpr (HALF) {
+      if (p.CinA) {
+        float c[4];
+        ld4_act(reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin + (long)row * p.ldcin + col, c, true);
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] += p.beta * c[t];
+      }
     }
     if (p.outF) {
       typedef float f4v __attribute__((ext_vector_type(4)));
@@ -218,7 +219,6 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     float g[4];
     _Pragma("unroll") for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
-    if (p.outA) st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
     st4_act(reinterpret_cast<bf16_t*>(p.out2) + o, g);
   } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u)
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
@@ -727,67 +727,71 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
                    (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
   const int lc = (lane % LPR) * 4, lrow = lane / LPR;
-  // one 32-row block of the wave tile per expansion (a literal block index keeps every
-  // accumulator access static)
-#define GEMM_EPI_BLOCK(I_)                                                                     \
-  do { \
-_Pragma("unroll") \
-    for (int j = 0; j < FN; ++j) \
-_Pragma("unroll") \
-      for (int r = 0; r < 16; ++r) stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[I_][j][r]; \
-    const int row0 = m0 + wm * TM + I_ * 32; \
-    const int col = n0 + wn * TN + lc; \
-    for (int rr = lrow; rr < 32; rr += RPI) { \
-      const int row = row0 + rr; \
-      if (row >= p.M) break; \
-      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc); \
-      if (p.splits > 1) { \
-        float* w = p.ws + ((long)yy * p.M + row) * p.N + col; \
-        if (vec && col + 3 < p.N) { \
-          typedef float f4v __attribute__((ext_vector_type(4))); \
-          f4v x_ = {a.x, a.y, a.z, a.w}; \
-          __builtin_nontemporal_store(x_, reinterpret_cast<f4v*>(w)); \
-        } else { \
-          const float e[4] = {a.x, a.y, a.z, a.w}; \
-          for (int t = 0; t < 4; ++t) \
-            if (col + t < p.N) w[t] = e[t]; \
-        } \
-      } else if (vec && col + 3 < p.N) { \
-        epilogue_vec4(p, bz, row, col, a); \
-      } else { \
-        const float e[4] = {a.x, a.y, a.z, a.w}; \
-        for (int t = 0; t < 4; ++t) \
-          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]); \
-      } \
-    } \
-    if (sym && tm != tn) { \
-      /* mirror: element (row0 + r, n) also lands at (n, row0 + r); read the staged block */ \
-      /* by columns so each mirrored row gets 4-wide stores (8 lanes per 32-wide row) */ \
-      const int r4 = (lane & 7) * 4; \
-_Pragma("unroll") \
-      for (int q = 0; q < TN / 8; ++q) { \
-        const int cc = q * 8 + (lane >> 3); \
-        const int n = n0 + wn * TN + cc, m = row0 + r4; \
-        if (n >= p.M || m >= p.M) continue; \
-        const float4 a = make_float4(stage[(r4 + 0) * CS + cc], stage[(r4 + 1) * CS + cc], stage[(r4 + 2) * CS + cc], \
-                                     stage[(r4 + 3) * CS + cc]); \
-        if (vec && m + 3 < p.M) { \
-          epilogue_vec4(p, bz, n, m, a); \
-        } else { \
-          const float e[4] = {a.x, a.y, a.z, a.w}; \
-          for (int t = 0; t < 4; ++t) \
-            if (m + t < p.M) epilogue_elem<bf16_t>(p, bz, n, m + t, e[t]); \
-        } \
-      } \
-    } \
-   \
-  } while (0)
-  GEMM_EPI_BLOCK(0);
-  GEMM_EPI_BLOCK(1);
-  GEMM_EPI_BLOCK(2);
-  GEMM_EPI_BLOCK(3);
-  static_assert(FM == 4, "one expansion per 32-row block");
-#undef GEMM_EPI_BLOCK
+  // Stage one 32-row block of the wave tile (a literal block index per case keeps every
+  // accumulator access static), then write it back from LDS with one rolled copy of the
+  // store code for all four blocks: the epilogue stays a few hundred instructions, so
+  // the k loop of the next tile still finds its code in the instruction cache (the
+  // unrolled form was ~20k instructions per kernel and measurably slowed the k loop).
+  static_assert(FM == 4, "one case per 32-row block");
+#pragma unroll 1
+  for (int ib = 0; ib < FM; ++ib) {
+#define GEMM_STAGE(I_)                                                                          \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) _Pragma("unroll") for (int r = 0; r < 16; ++r) \
+      stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[I_][j][r];
+    switch (ib) {
+      case 0: GEMM_STAGE(0) break;
+      case 1: GEMM_STAGE(1) break;
+      case 2: GEMM_STAGE(2) break;
+      default: GEMM_STAGE(3) break;
+    }
+#undef GEMM_STAGE
+    const int row0 = m0 + wm * TM + ib * 32;
+    const int col = n0 + wn * TN + lc;
+#pragma unroll 2
+    for (int rr = lrow; rr < 32; rr += RPI) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+      if (p.splits > 1) {
+        float* w = p.ws + ((long)yy * p.M + row) * p.N + col;
+        if (vec && col + 3 < p.N) {
+          typedef float f4v __attribute__((ext_vector_type(4)));
+          f4v x_ = {a.x, a.y, a.z, a.w};
+          __builtin_nontemporal_store(x_, reinterpret_cast<f4v*>(w));
+        } else {
+#pragma unroll 1
+          for (int t = 0; t < 4; ++t)
+            if (col + t < p.N) w[t] = pick4(a, t);
+        }
+      } else if (vec && col + 3 < p.N) {
+        epilogue_vec4<F16 && BKM>(p, bz, row, col, a);
+      } else {
+#pragma unroll 1
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, pick4(a, t));
+      }
+    }
+    if (sym && tm != tn) {
+      // mirror: element (row0 + r, n) also lands at (n, row0 + r); read the staged block
+      // by columns so each mirrored row gets 4-wide stores (8 lanes per 32-wide row)
+      const int r4 = (lane & 7) * 4;
+#pragma unroll 2
+      for (int q = 0; q < TN / 8; ++q) {
+        const int cc = q * 8 + (lane >> 3);
+        const int n = n0 + wn * TN + cc, m = row0 + r4;
+        if (n >= p.M || m >= p.M) continue;
+        const float4 a = make_float4(stage[(r4 + 0) * CS + cc], stage[(r4 + 1) * CS + cc], stage[(r4 + 2) * CS + cc],
+                                     stage[(r4 + 3) * CS + cc]);
+        if (vec && m + 3 < p.M) {
+          epilogue_vec4<F16 && BKM>(p, bz, n, m, a);
+        } else {
+#pragma unroll 1
+          for (int t = 0; t < 4; ++t)
+            if (m + t < p.M) epilogue_elem<bf16_t>(p, bz, n, m + t, pick4(a, t));
+        }
+      }
+    }
+  }
 }
 
 
@@ -954,37 +958,41 @@ gemm_fp8_dma_kernel(GemmArgs p) {
   const bool vec = (p.N % 4 == 0) && (p.ldo % 4 == 0) && (p.ldoa % 4 == 0) && (p.ldcin % 4 == 0) &&
                    (p.strideO % 4 == 0) && (p.strideOA % 4 == 0) && (p.strideCin % 4 == 0);
   const int lc = (lane % LPR) * 4, lrow = lane / LPR;
-#define FP8_EPI_BLOCK(I_)                                                                          \
-  do {                                                                                             \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                 \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r)                                               \
-        stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[I_][j][r] * dq;                           \
-    const int row0 = m0 + wm * TM + I_ * 32;                                                       \
-    const int col = n0 + wn * TN + lc;                                                             \
-    for (int rr = lrow; rr < 32; rr += RPI) {                                                      \
-      const int row = row0 + rr;                                                                   \
-      if (row >= p.M) break;                                                                       \
-      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);                     \
-      if (p.splits > 1) {                                                                          \
-        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;                              \
-        const float e[4] = {a.x, a.y, a.z, a.w};                                                   \
-        for (int t = 0; t < 4; ++t)                                                                \
-          if (col + t < p.N) w[t] = e[t];                                                          \
-      } else if (vec && col + 3 < p.N) {                                                           \
-        epilogue_vec4(p, bz, row, col, a);                                                         \
-      } else {                                                                                     \
-        const float e[4] = {a.x, a.y, a.z, a.w};                                                   \
-        for (int t = 0; t < 4; ++t)                                                                \
-          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, e[t]);                     \
-      }                                                                                            \
-    }                                                                                              \
-  } while (0)
-  FP8_EPI_BLOCK(0);
-  FP8_EPI_BLOCK(1);
-  FP8_EPI_BLOCK(2);
-  FP8_EPI_BLOCK(3);
-  static_assert(FM == 4, "one expansion per 32-row block");
-#undef FP8_EPI_BLOCK
+  // staging by a literal block index, stores by one rolled copy (as in the bf16 kernel)
+  static_assert(FM == 4, "one case per 32-row block");
+#pragma unroll 1
+  for (int ib = 0; ib < FM; ++ib) {
+#define FP8_STAGE(I_)                                                                           \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) _Pragma("unroll") for (int r = 0; r < 16; ++r) \
+      stage[acc_row(lane, r) * CS + j * 32 + lr] = acc[I_][j][r] * dq;
+    switch (ib) {
+      case 0: FP8_STAGE(0) break;
+      case 1: FP8_STAGE(1) break;
+      case 2: FP8_STAGE(2) break;
+      default: FP8_STAGE(3) break;
+    }
+#undef FP8_STAGE
+    const int row0 = m0 + wm * TM + ib * 32;
+    const int col = n0 + wn * TN + lc;
+#pragma unroll 2
+    for (int rr = lrow; rr < 32; rr += RPI) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+      if (p.splits > 1) {
+        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
+#pragma unroll 1
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) w[t] = pick4(a, t);
+      } else if (vec && col + 3 < p.N) {
+        epilogue_vec4(p, bz, row, col, a);
+      } else {
+#pragma unroll 1
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, pick4(a, t));
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1247,6 +1255,12 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if ((size_t)p.splits * p.batch * p.M * p.N * sizeof(float) > p.ws_bytes) return 1;
   }
   if (p.split && (p.dtype != ACT_BF16 || p.splits != 1 || !p.A_lo || !p.B_lo)) return 1;
+  // CinA is read by the vectorised epilogue of the fp16 NT kernels only: every row and
+  // column in groups of four
+  if (p.CinA && (p.dtype != ACT_F16 || !p.a_kmaj || !p.b_kmaj || p.Cin || p.M % 4 || p.N % 4 || p.ldcin % 4 ||
+                 p.strideCin % 4 ||
+                 p.ldo % 4 || p.ldoa % 4 || p.strideO % 4 || p.strideOA % 4))
+    return 1;
   if (p.dtype == ACT_F16 && (p.splits != 1 || p.epi != EPI_LINEAR)) return 1;
   if (p.fp8) {
     if (!p.a_kmaj || !p.b_kmaj || p.split || !p.dq_a || !p.dq_b) return 1;

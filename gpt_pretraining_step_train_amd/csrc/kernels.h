@@ -8,7 +8,7 @@ enum ActType { ACT_F32 = 0, ACT_BF16 = 1, ACT_F16 = 2 };
 
 enum GemmEpi {
   EPI_LINEAR = 0,  // v = alpha*acc + beta*Cin -> outF (fp32) and/or outA (act type)
-  EPI_RELU2 = 1,   // u = alpha*acc -> outA (when set) ; g = max(u,0)^2 -> out2
+  EPI_RELU2 = 1,   // g = max(alpha*acc, 0)^2 -> out2 (ld / stride of outA); the pre-activation is not kept
   EPI_DRELU2 = 2,  // v = alpha*acc * 2*sqrt(max(aux,0)) -> outA, aux = g = max(u,0)^2 (so the root is max(u,0))
 };
 
@@ -24,10 +24,11 @@ struct GemmArgs {
   int epi = EPI_LINEAR;
   float alpha = 1.f, beta = 0.f;
   const float* Cin = nullptr; long ldcin = 0, strideCin = 0;
-  const void* CinA = nullptr;     // Cin in the operand's 16-bit type instead (when Cin is null; same ld/stride)
+  const void* CinA = nullptr;     // fp16 NT kernels only: Cin as fp16 instead (Cin null; same ld/stride; M, N and
+                                  // every leading dimension / stride multiples of 4, else launch_gemm fails)
   float* outF = nullptr; long ldo = 0, strideO = 0;
   void* outA = nullptr; long ldoa = 0, strideOA = 0;
-  void* out2 = nullptr;           // EPI_RELU2 second output (same ld/stride as outA)
+  void* out2 = nullptr;           // EPI_RELU2 output (ld / stride: ldoa, strideOA)
   const void* aux = nullptr;      // EPI_DRELU2 input (same ld/stride as outA)
   int splits = 1;                 // split-K factor; >1 needs ws
   float* ws = nullptr; size_t ws_bytes = 0;
