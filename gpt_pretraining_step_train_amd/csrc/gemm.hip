@@ -181,23 +181,49 @@ __device__ inline void ld4_act(const bf16_t* q, float (&v)[4], bool h = false) {
 // displace the operands' lines (the epilogue's cost per tile fell 8-13%).
 // element t of a float4 by selects (a runtime index into a local array would live in scratch)
 __device__ inline float pick4(const float4& a, int t) { return t == 0 ? a.x : t == 1 ? a.y : t == 2 ? a.z : a.w; }
+__device__ inline long o_act(const GemmArgs& p, int bz, int row, int col) {
+  return bz * p.strideOA + (long)row * p.ldoa + col;
+}
 
 // HALF: the fp16-operand NT instantiations (the Newton-Schulz A A product), the only ones that
 // read CinA
 template <bool HALF = false>
-__device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col, float4 a) {
-  float v[4] = {p.alpha * a.x, p.alpha * a.y, p.alpha * a.z, p.alpha * a.w};
+__device__ inline bool epi_has_in(const GemmArgs& p) {
+  return p.epi == EPI_DRELU2 || (p.epi == EPI_LINEAR && (p.Cin || (HALF && p.CinA)));
+}
+
+// the element-wise input of four consecutive outputs: beta * Cin (or CinA), or the EPI_DRELU2
+// aux values; zeros where the epilogue has none
+template <bool HALF = false>
+__device__ inline float4 epi_in4(const GemmArgs& p, int bz, int row, int col) {
+  if (p.epi == EPI_DRELU2) {
+    float g[4];
+    ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + bz * p.strideOA + (long)row * p.ldoa + col, g);
+    return make_float4(g[0], g[1], g[2], g[3]);
+  }
   if (p.epi == EPI_LINEAR) {
     if (p.Cin) {
       const float4 c = *reinterpret_cast<const float4*>(p.Cin + bz * p.strideCin + (long)row * p.ldcin + col);
-      v[0] += p.beta * c.x; v[1] += p.beta * c.y; v[2] += p.beta * c.z; v[3] += p.beta * c.w;
-    } else if constexpr (HALF) {
+      return make_float4(p.beta * c.x, p.beta * c.y, p.beta * c.z, p.beta * c.w);
+    }
+    if constexpr (HALF) {
       if (p.CinA) {
         float c[4];
         ld4_act(reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin + (long)row * p.ldcin + col, c, true);
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] += p.beta * c[t];
+        return make_float4(p.beta * c[0], p.beta * c[1], p.beta * c[2], p.beta * c[3]);
       }
     }
+  }
+  return make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// the epilogue of four consecutive outputs a (accumulators) with their input in (epi_in4;
+// used when has_in)
+template <bool HALF = false>
+__device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col, float4 a, float4 in, bool has_in) {
+  float v[4] = {p.alpha * a.x, p.alpha * a.y, p.alpha * a.z, p.alpha * a.w};
+  if (p.epi == EPI_LINEAR) {
+    if (has_in) { v[0] += in.x; v[1] += in.y; v[2] += in.z; v[3] += in.w; }
     if (p.outF) {
       typedef float f4v __attribute__((ext_vector_type(4)));
       f4v x = {v[0], v[1], v[2], v[3]};
@@ -220,12 +246,95 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
     float g[4];
     _Pragma("unroll") for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
     st4_act(reinterpret_cast<bf16_t*>(p.out2) + o, g);
-  } else {  // EPI_DRELU2: aux holds g = relu(u)^2, whose root is relu(u)
-    const long o = bz * p.strideOA + (long)row * p.ldoa + col;
-    float g[4];
-    ld4_act(reinterpret_cast<const bf16_t*>(p.aux) + o, g);
+  } else {  // EPI_DRELU2: the input is g = relu(u)^2, whose root is relu(u)
+    const float g[4] = {in.x, in.y, in.z, in.w};
     _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * __builtin_amdgcn_sqrtf(fmaxf(g[t], 0.f));
-    st4_act(reinterpret_cast<bf16_t*>(p.outA) + o, v);
+    st4_act(reinterpret_cast<bf16_t*>(p.outA) + o_act(p, bz, row, col), v);
+  }
+}
+
+// Writes back one 32-row block of a wave's 128x64 tile staged in LDS (stage: 32 rows of CS
+// floats; the lane owns columns col..col+3 of rows lrow, lrow + RPI, ...): split-K partials
+// to ws_blk (this launch slice's M x N plane), else the epilogue.  On the vector path the
+// element-wise inputs of all the lane's rows are loaded before the first is used, so the
+// block waits for their latency once instead of once per row.
+template <bool HALF, int CS, int RPI>
+__device__ inline void write_block(const GemmArgs& p, int bz, int row0, int col, int lrow, int lc, bool vec,
+                                   const float* stage, float* ws_blk) {
+  constexpr int NR = 32 / RPI;
+  if (p.splits > 1) {
+#pragma unroll 2
+    for (int rr = lrow; rr < 32; rr += RPI) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+      float* w = ws_blk + (long)row * p.N + col;
+      if (vec && col + 3 < p.N) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        f4v x_ = {a.x, a.y, a.z, a.w};
+        __builtin_nontemporal_store(x_, reinterpret_cast<f4v*>(w));
+      } else {
+#pragma unroll 1
+        for (int t = 0; t < 4; ++t)
+          if (col + t < p.N) w[t] = pick4(a, t);
+      }
+    }
+  } else if (vec && col + 3 < p.N) {
+    // the element-wise input (uniform): 1 = fp32 Cin, 2 = bf16 aux of EPI_DRELU2, 3 = fp16
+    // CinA.  One branch around all the loads and clamped rows (a row past M loads row M-1,
+    // unused) keep them back to back: per-row branches made the compiler wait for each.
+    const int kind = p.epi == EPI_DRELU2                          ? 2
+                     : p.epi != EPI_LINEAR                        ? 0
+                     : p.Cin                                      ? 1
+                     : (HALF && p.CinA)                           ? 3
+                                                                  : 0;
+    uint4 raw[NR];
+    if (kind == 1) {
+      const float* b = p.Cin + bz * p.strideCin + col;
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        raw[i] = *reinterpret_cast<const uint4*>(b + (long)min(row0 + lrow + i * RPI, p.M - 1) * p.ldcin);
+    } else if (kind != 0) {
+      const bf16_t* b = (kind == 2 ? reinterpret_cast<const bf16_t*>(p.aux) + bz * p.strideOA
+                                   : reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin) + col;
+      const long ld = kind == 2 ? p.ldoa : p.ldcin;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const uint2 u = *reinterpret_cast<const uint2*>(b + (long)min(row0 + lrow + i * RPI, p.M - 1) * ld);
+        raw[i] = make_uint4(u.x, u.y, 0u, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int rr = lrow + i * RPI, row = row0 + rr;
+      if (row >= p.M) break;
+      float4 in;
+      if (kind == 1) {
+        in = make_float4(p.beta * __uint_as_float(raw[i].x), p.beta * __uint_as_float(raw[i].y),
+                         p.beta * __uint_as_float(raw[i].z), p.beta * __uint_as_float(raw[i].w));
+      } else if (kind == 2) {
+        in = make_float4(bf2f((bf16_t)(raw[i].x & 0xffff)), bf2f((bf16_t)(raw[i].x >> 16)),
+                         bf2f((bf16_t)(raw[i].y & 0xffff)), bf2f((bf16_t)(raw[i].y >> 16)));
+      } else {
+        typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+        const f16x4v h = __builtin_bit_cast(f16x4v, make_uint2(raw[i].x, raw[i].y));
+        in = make_float4(p.beta * (float)h[0], p.beta * (float)h[1], p.beta * (float)h[2], p.beta * (float)h[3]);
+      }
+      epilogue_vec4<HALF>(p, bz, row, col, *reinterpret_cast<const float4*>(stage + rr * CS + lc), in, kind != 0);
+    }
+  } else {
+#pragma unroll 1
+    for (int rr = lrow; rr < 32; rr += RPI) {
+      const int row = row0 + rr;
+      if (row >= p.M) break;
+      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
+#pragma unroll 1
+      for (int t = 0; t < 4; ++t)
+        if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, pick4(a, t));
+    }
   }
 }
 
@@ -372,7 +481,7 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
             if (col + t < p.N) w[t] = e[t];
         }
       } else if (vec && col + 3 < p.N) {
-        epilogue_vec4(p, bz, row, col, a);
+        epilogue_vec4(p, bz, row, col, a, epi_in4(p, bz, row, col), epi_has_in(p));
       } else {
         const float e[4] = {a.x, a.y, a.z, a.w};
         for (int t = 0; t < 4; ++t)
@@ -747,30 +856,8 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 #undef GEMM_STAGE
     const int row0 = m0 + wm * TM + ib * 32;
     const int col = n0 + wn * TN + lc;
-#pragma unroll 2
-    for (int rr = lrow; rr < 32; rr += RPI) {
-      const int row = row0 + rr;
-      if (row >= p.M) break;
-      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
-      if (p.splits > 1) {
-        float* w = p.ws + ((long)yy * p.M + row) * p.N + col;
-        if (vec && col + 3 < p.N) {
-          typedef float f4v __attribute__((ext_vector_type(4)));
-          f4v x_ = {a.x, a.y, a.z, a.w};
-          __builtin_nontemporal_store(x_, reinterpret_cast<f4v*>(w));
-        } else {
-#pragma unroll 1
-          for (int t = 0; t < 4; ++t)
-            if (col + t < p.N) w[t] = pick4(a, t);
-        }
-      } else if (vec && col + 3 < p.N) {
-        epilogue_vec4<F16 && BKM>(p, bz, row, col, a);
-      } else {
-#pragma unroll 1
-        for (int t = 0; t < 4; ++t)
-          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, pick4(a, t));
-      }
-    }
+    write_block<F16 && BKM, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
+                                     p.splits > 1 ? p.ws + (long)yy * p.M * p.N : nullptr);
     if (sym && tm != tn) {
       // mirror: element (row0 + r, n) also lands at (n, row0 + r); read the staged block
       // by columns so each mirrored row gets 4-wide stores (8 lanes per 32-wide row)
@@ -783,7 +870,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
         const float4 a = make_float4(stage[(r4 + 0) * CS + cc], stage[(r4 + 1) * CS + cc], stage[(r4 + 2) * CS + cc],
                                      stage[(r4 + 3) * CS + cc]);
         if (vec && m + 3 < p.M) {
-          epilogue_vec4<F16 && BKM>(p, bz, n, m, a);
+          epilogue_vec4<F16 && BKM>(p, bz, n, m, a, epi_in4<F16 && BKM>(p, bz, n, m), epi_has_in<F16 && BKM>(p));
         } else {
 #pragma unroll 1
           for (int t = 0; t < 4; ++t)
@@ -974,24 +1061,8 @@ gemm_fp8_dma_kernel(GemmArgs p) {
 #undef FP8_STAGE
     const int row0 = m0 + wm * TM + ib * 32;
     const int col = n0 + wn * TN + lc;
-#pragma unroll 2
-    for (int rr = lrow; rr < 32; rr += RPI) {
-      const int row = row0 + rr;
-      if (row >= p.M) break;
-      const float4 a = *reinterpret_cast<const float4*>(stage + rr * CS + lc);
-      if (p.splits > 1) {
-        float* w = p.ws + ((long)blockIdx.y * p.M + row) * p.N + col;
-#pragma unroll 1
-        for (int t = 0; t < 4; ++t)
-          if (col + t < p.N) w[t] = pick4(a, t);
-      } else if (vec && col + 3 < p.N) {
-        epilogue_vec4(p, bz, row, col, a);
-      } else {
-#pragma unroll 1
-        for (int t = 0; t < 4; ++t)
-          if (col + t < p.N) epilogue_elem<bf16_t>(p, bz, row, col + t, pick4(a, t));
-      }
-    }
+    write_block<false, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
+                               p.splits > 1 ? p.ws + (long)blockIdx.y * p.M * p.N : nullptr);
   }
 }
 
@@ -1083,12 +1154,13 @@ __global__ void __launch_bounds__(128) splitk_reduce_vec_kernel(GemmArgs p) {
   const int row = blockIdx.y, bz = blockIdx.z;
   const long MN = (long)p.M * p.N;
   const float* w = p.ws + (long)bz * p.splits * MN + (long)row * p.N + 4 * c4;
+  const float4 in = epi_in4(p, bz, row, 4 * c4);  // issued ahead of the partial sums
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int k = 0; k < p.splits; ++k) {
     const float4 v = *reinterpret_cast<const float4*>(w + k * MN);
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
-  epilogue_vec4(p, bz, row, 4 * c4, s);
+  epilogue_vec4(p, bz, row, 4 * c4, s, in, epi_has_in(p));
 }
 
 template <int BM, int BN, int WM, int WN, bool SPLIT>
