@@ -253,14 +253,59 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
   }
 }
 
+// The element-wise input of the vector epilogue (uniform): 1 = fp32 Cin, 2 = bf16 aux of
+// EPI_DRELU2, 3 = fp16 CinA, 0 = none
+template <bool HALF>
+__device__ inline int epi_kind(const GemmArgs& p) {
+  return p.epi == EPI_DRELU2 ? 2 : p.epi != EPI_LINEAR ? 0 : p.Cin ? 1 : (HALF && p.CinA) ? 3 : 0;
+}
+
+// Loads the raw element-wise inputs of one 32-row block for a lane (columns col..col+3 of
+// rows row0 + lrow + i RPI): one uniform branch around all the loads and clamped rows (a
+// row past M loads row M-1, unused) keep them back to back; per-row branches made the
+// compiler wait for each.
+template <int NR, int RPI>
+__device__ inline void epi_load(const GemmArgs& p, int kind, int bz, int row0, int col, int lrow, uint4 (&raw)[NR]) {
+  if (kind == 1) {
+    const float* b = p.Cin + bz * p.strideCin + col;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(b + (long)min(row0 + lrow + i * RPI, p.M - 1) * p.ldcin);
+  } else if (kind != 0) {
+    const bf16_t* b = (kind == 2 ? reinterpret_cast<const bf16_t*>(p.aux) + bz * p.strideOA
+                                 : reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin) + col;
+    const long ld = kind == 2 ? p.ldoa : p.ldcin;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const uint2 u = *reinterpret_cast<const uint2*>(b + (long)min(row0 + lrow + i * RPI, p.M - 1) * ld);
+      raw[i] = make_uint4(u.x, u.y, 0u, 0u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// the input values of one row from its raw words (beta applied to Cin / CinA)
+__device__ inline float4 epi_decode(const GemmArgs& p, int kind, const uint4& r) {
+  if (kind == 1)
+    return make_float4(p.beta * __uint_as_float(r.x), p.beta * __uint_as_float(r.y), p.beta * __uint_as_float(r.z),
+                       p.beta * __uint_as_float(r.w));
+  if (kind == 2)
+    return make_float4(bf2f((bf16_t)(r.x & 0xffff)), bf2f((bf16_t)(r.x >> 16)), bf2f((bf16_t)(r.y & 0xffff)),
+                       bf2f((bf16_t)(r.y >> 16)));
+  typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+  const f16x4v h = __builtin_bit_cast(f16x4v, make_uint2(r.x, r.y));
+  return make_float4(p.beta * (float)h[0], p.beta * (float)h[1], p.beta * (float)h[2], p.beta * (float)h[3]);
+}
+
 // Writes back one 32-row block of a wave's 128x64 tile staged in LDS (stage: 32 rows of CS
 // floats; the lane owns columns col..col+3 of rows lrow, lrow + RPI, ...): split-K partials
-// to ws_blk (this launch slice's M x N plane), else the epilogue.  On the vector path the
-// element-wise inputs of all the lane's rows are loaded before the first is used, so the
-// block waits for their latency once instead of once per row.
+// to ws_blk (this launch slice's M x N plane), else the epilogue, with the block's
+// element-wise inputs in raw (epi_load; the vector path only).
 template <bool HALF, int CS, int RPI>
 __device__ inline void write_block(const GemmArgs& p, int bz, int row0, int col, int lrow, int lc, bool vec,
-                                   const float* stage, float* ws_blk) {
+                                   const float* stage, float* ws_blk, int kind, const uint4 (&raw)[32 / RPI]) {
   constexpr int NR = 32 / RPI;
   if (p.splits > 1) {
 #pragma unroll 2
@@ -280,50 +325,12 @@ __device__ inline void write_block(const GemmArgs& p, int bz, int row0, int col,
       }
     }
   } else if (vec && col + 3 < p.N) {
-    // the element-wise input (uniform): 1 = fp32 Cin, 2 = bf16 aux of EPI_DRELU2, 3 = fp16
-    // CinA.  One branch around all the loads and clamped rows (a row past M loads row M-1,
-    // unused) keep them back to back: per-row branches made the compiler wait for each.
-    const int kind = p.epi == EPI_DRELU2                          ? 2
-                     : p.epi != EPI_LINEAR                        ? 0
-                     : p.Cin                                      ? 1
-                     : (HALF && p.CinA)                           ? 3
-                                                                  : 0;
-    uint4 raw[NR];
-    if (kind == 1) {
-      const float* b = p.Cin + bz * p.strideCin + col;
-#pragma unroll
-      for (int i = 0; i < NR; ++i)
-        raw[i] = *reinterpret_cast<const uint4*>(b + (long)min(row0 + lrow + i * RPI, p.M - 1) * p.ldcin);
-    } else if (kind != 0) {
-      const bf16_t* b = (kind == 2 ? reinterpret_cast<const bf16_t*>(p.aux) + bz * p.strideOA
-                                   : reinterpret_cast<const bf16_t*>(p.CinA) + bz * p.strideCin) + col;
-      const long ld = kind == 2 ? p.ldoa : p.ldcin;
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const uint2 u = *reinterpret_cast<const uint2*>(b + (long)min(row0 + lrow + i * RPI, p.M - 1) * ld);
-        raw[i] = make_uint4(u.x, u.y, 0u, 0u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) raw[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int rr = lrow + i * RPI, row = row0 + rr;
       if (row >= p.M) break;
-      float4 in;
-      if (kind == 1) {
-        in = make_float4(p.beta * __uint_as_float(raw[i].x), p.beta * __uint_as_float(raw[i].y),
-                         p.beta * __uint_as_float(raw[i].z), p.beta * __uint_as_float(raw[i].w));
-      } else if (kind == 2) {
-        in = make_float4(bf2f((bf16_t)(raw[i].x & 0xffff)), bf2f((bf16_t)(raw[i].x >> 16)),
-                         bf2f((bf16_t)(raw[i].y & 0xffff)), bf2f((bf16_t)(raw[i].y >> 16)));
-      } else {
-        typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
-        const f16x4v h = __builtin_bit_cast(f16x4v, make_uint2(raw[i].x, raw[i].y));
-        in = make_float4(p.beta * (float)h[0], p.beta * (float)h[1], p.beta * (float)h[2], p.beta * (float)h[3]);
-      }
-      epilogue_vec4<HALF>(p, bz, row, col, *reinterpret_cast<const float4*>(stage + rr * CS + lc), in, kind != 0);
+      epilogue_vec4<HALF>(p, bz, row, col, *reinterpret_cast<const float4*>(stage + rr * CS + lc),
+                          kind ? epi_decode(p, kind, raw[i]) : make_float4(0.f, 0.f, 0.f, 0.f), kind != 0);
     }
   } else {
 #pragma unroll 1
@@ -842,6 +849,12 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   // the k loop of the next tile still finds its code in the instruction cache (the
   // unrolled form was ~20k instructions per kernel and measurably slowed the k loop).
   static_assert(FM == 4, "one case per 32-row block");
+  // the element-wise inputs of the vector path, one row block ahead: the loads of block
+  // ib + 1 are in flight while block ib is written
+  constexpr int NR = 32 / RPI;
+  const int ekind = p.splits == 1 && vec && n0 + wn * TN + lc + 3 < p.N ? epi_kind<F16 && BKM>(p) : 0;
+  uint4 rin[NR];
+  epi_load<NR, RPI>(p, ekind, bz, m0 + wm * TM, n0 + wn * TN + lc, lrow, rin);
 #pragma unroll 1
   for (int ib = 0; ib < FM; ++ib) {
 #define GEMM_STAGE(I_)                                                                          \
@@ -856,8 +869,12 @@ gemm_bf16_dma_kernel(GemmArgs p) {
 #undef GEMM_STAGE
     const int row0 = m0 + wm * TM + ib * 32;
     const int col = n0 + wn * TN + lc;
+    uint4 rnext[NR];
+    epi_load<NR, RPI>(p, ib + 1 < FM ? ekind : 0, bz, row0 + 32, col, lrow, rnext);
     write_block<F16 && BKM, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
-                                     p.splits > 1 ? p.ws + (long)yy * p.M * p.N : nullptr);
+                                     p.splits > 1 ? p.ws + (long)yy * p.M * p.N : nullptr, ekind, rin);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) rin[i] = rnext[i];
     if (sym && tm != tn) {
       // mirror: element (row0 + r, n) also lands at (n, row0 + r); read the staged block
       // by columns so each mirrored row gets 4-wide stores (8 lanes per 32-wide row)
@@ -1047,6 +1064,10 @@ gemm_fp8_dma_kernel(GemmArgs p) {
   const int lc = (lane % LPR) * 4, lrow = lane / LPR;
   // staging by a literal block index, stores by one rolled copy (as in the bf16 kernel)
   static_assert(FM == 4, "one case per 32-row block");
+  constexpr int NR = 32 / RPI;  // inputs one row block ahead, as in the bf16 kernel
+  const int ekind = p.splits == 1 && vec && n0 + wn * TN + lc + 3 < p.N ? epi_kind<false>(p) : 0;
+  uint4 rin[NR];
+  epi_load<NR, RPI>(p, ekind, bz, m0 + wm * TM, n0 + wn * TN + lc, lrow, rin);
 #pragma unroll 1
   for (int ib = 0; ib < FM; ++ib) {
 #define FP8_STAGE(I_)                                                                           \
@@ -1061,8 +1082,12 @@ gemm_fp8_dma_kernel(GemmArgs p) {
 #undef FP8_STAGE
     const int row0 = m0 + wm * TM + ib * 32;
     const int col = n0 + wn * TN + lc;
+    uint4 rnext[NR];
+    epi_load<NR, RPI>(p, ib + 1 < FM ? ekind : 0, bz, row0 + 32, col, lrow, rnext);
     write_block<false, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
-                               p.splits > 1 ? p.ws + (long)blockIdx.y * p.M * p.N : nullptr);
+                               p.splits > 1 ? p.ws + (long)blockIdx.y * p.M * p.N : nullptr, ekind, rin);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) rin[i] = rnext[i];
   }
 }
 
