@@ -81,6 +81,7 @@ _SIGS = {
     "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_variant": (_I, [_I, _I]),
+    "gptk_fp8_fused_amax": (_I, [_I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -371,6 +372,11 @@ def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
 
 def attn_variant(pass_, variant):
     check(lib().gptk_attn_variant(pass_, variant), "gptk_attn_variant")
+
+
+def fp8_fused_amax(on: int = -1) -> int:
+    """gptk_fp8_fused_amax: set (0/1) or query (-1); returns the previous setting."""
+    return lib().gptk_fp8_fused_amax(int(on))
 
 
 def attn_fwd(dtype, qkv, o, lse, B, T, H, hd, window=0, n_kv=None):

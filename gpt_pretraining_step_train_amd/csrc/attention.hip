@@ -198,7 +198,7 @@ struct PairStager {
 template <int HD, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H,
-                     int Hkv, int W) {
+                     int Hkv, int W, float* __restrict__ amax_part) {
   constexpr int BQ = 32 * NW, BKV = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TE];
@@ -328,6 +328,7 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     body(std::integral_constant<int, 0>{}, it);
     if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
+  float mo = 0.f;  // max |o| of the lane as stored (amax_part)
   if (myq < T) {
     const float inv = 1.f / l;
     bf16_t* op = out + ((long)b * T + myq) * ((long)H * HD) + h * HD;
@@ -336,11 +337,19 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 32 + g * 8 + hl * 4;
-        uint2 u = make_uint2(pack_bf2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                             pack_bf2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = u;
+        float ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[e] = oacc[db][4 * g + e] * inv;
+          mo = fmaxf(mo, fabsf(ov[e]));
+        }
+        *reinterpret_cast<uint2*>(op + d) = make_uint2(pack_bf2(ov[0], ov[1]), pack_bf2(ov[2], ov[3]));
       }
     if (hl == 0) lse[(long)bh * T + myq] = (m + log2f(l)) * LN2;
+  }
+  if (amax_part) {  // one entry per wave
+    mo = wave_max(mo);
+    if (lane == 0) amax_part[((long)blockIdx.y * gridDim.x + blockIdx.x) * NW + wave] = bf16_round(mo);
   }
 }
 
@@ -921,7 +930,7 @@ template <int HD>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
                            const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
-                           int T, int H, int Hkv, int W) {
+                           int T, int H, int Hkv, int W, float* __restrict__ amax_part) {
   constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
@@ -1090,13 +1099,22 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   }
   const float scale = dk_role ? 1.f / sqrtf((float)HD) : 1.f;
   const long col = (long)(dk_role ? H + hk : H + Hkv + hk) * HD;
+  float mo = 0.f;  // max |dv| of the lane as stored (amax_part; dK is rewritten later, by the rope backward)
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = key0 + acc_row(lane, r);
-      if (key < T) dqkv[((long)b * T + key) * ld + col + db * 32 + lq] = f2bf(acc[db][r] * scale);
+      if (key < T) {
+        const float v = acc[db][r] * scale;
+        dqkv[((long)b * T + key) * ld + col + db * 32 + lq] = f2bf(v);
+        if (!dk_role) mo = fmaxf(mo, fabsf(v));
+      }
     }
+  if (amax_part) {  // one entry per wave (0 from the dK waves)
+    mo = wave_max(mo);
+    if (lane == 0) amax_part[((long)blockIdx.y * gridDim.x + blockIdx.x) * 8 + wave] = bf16_round(mo);
+  }
 }
 
 // dK and dV with 64 keys per wave (two 32-key blocks), one wave per SIMD: a wave forms
@@ -1449,27 +1467,35 @@ int g_attn_fwd_variant = 0;
 // waves of 64 keys (both in one wave)
 int g_attn_bwd_variant = 0;
 
+// returns the number of amax partials written (0: none)
 template <int HD>
-void fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int W, hipStream_t st) {
+int fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int W, hipStream_t st,
+                 float* amax_part, long amax_cap) {
   constexpr int NW = kFwdWaves;
   if constexpr (HD == 128) {
     if (at == ACT_BF16 && g_attn_fwd_variant == 1) {
       hipLaunchKernelGGL((attn_fwd_q64_kernel<HD>), dim3((T + 255) / 256, B * H), dim3(256), 0, st,
                          (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, Hkv, W);
-      return;
+      return 0;
     }
   }
-  if (at == ACT_BF16)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD, NW>), dim3((T + 32 * NW - 1) / (32 * NW), B * H), dim3(NW * 64), 0,
-                       st, (const bf16_t*)qkv, (bf16_t*)o, lse, T, H, Hkv, W);
-  else
-    hipLaunchKernelGGL(attn_fwd_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
-                       (float*)o, lse, T, H, Hkv, W);
+  if (at == ACT_BF16) {
+    const dim3 g((T + 32 * NW - 1) / (32 * NW), B * H);
+    const long parts = (long)g.x * g.y * NW;
+    if (!amax_part || parts > amax_cap) amax_part = nullptr;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD, NW>), g, dim3(NW * 64), 0, st, (const bf16_t*)qkv, (bf16_t*)o, lse,
+                       T, H, Hkv, W, amax_part);
+    return amax_part ? (int)parts : 0;
+  }
+  hipLaunchKernelGGL(attn_fwd_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
+                     (float*)o, lse, T, H, Hkv, W);
+  return 0;
 }
 
 template <int HD>
-void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
-                  int B, int T, int H, int Hkv, int W, hipStream_t st) {
+int bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
+                 int B, int T, int H, int Hkv, int W, hipStream_t st, float* amax_part, long amax_cap) {
+  int parts = 0;
   if (at == ACT_BF16) {
     // the dQ kernel also writes D = rowsum(dO * O) for the dK/dV kernel
     bool done_q = false;
@@ -1492,15 +1518,21 @@ void bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* l
         done = true;
       }
     }
-    if (!done)
-      hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, dim3((T + 127) / 128, B * Hkv), dim3(512), 0, st,
-                         (const bf16_t*)qkv, (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W);
+    if (!done) {
+      const dim3 g((T + 127) / 128, B * Hkv);
+      const long np = (long)g.x * g.y * 8;
+      if (!amax_part || np > amax_cap) amax_part = nullptr;
+      hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, g, dim3(512), 0, st, (const bf16_t*)qkv,
+                         (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W, amax_part);
+      parts = amax_part ? (int)np : 0;
+    }
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
                        (const float*)dO, lse, D, (float*)dqkv, T, H, Hkv, W);
     hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<HD>, dim3((T + 63) / 64, B * Hkv), dim3(64), 0, st,
                        (const float*)qkv, (const float*)dO, lse, D, (float*)dqkv, T, H, Hkv, W);
   }
+  return parts;
 }
 
 }  // namespace
@@ -1509,22 +1541,25 @@ void set_attn_fwd_variant(int v) { g_attn_fwd_variant = v; }
 void set_attn_bwd_variant(int v) { g_attn_bwd_variant = v; }
 
 // Hkv must divide H (the callers validate it)
-void launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int hd, int window,
-                     hipStream_t st) {
-  if (B * T * H == 0) return;
-  if (hd == 128) fwd_dispatch<128>(qkv, o, lse, at, B, T, H, Hkv, window, st);
-  else if (hd == 64) fwd_dispatch<64>(qkv, o, lse, at, B, T, H, Hkv, window, st);
-  else if (hd == 32) fwd_dispatch<32>(qkv, o, lse, at, B, T, H, Hkv, window, st);
+int launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int hd, int window,
+                    hipStream_t st, float* amax_part, long amax_cap) {
+  if (B * T * H == 0) return 0;
+  if (hd == 128) return fwd_dispatch<128>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  if (hd == 64) return fwd_dispatch<64>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  if (hd == 32) return fwd_dispatch<32>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  return 0;
 }
 
-void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
-                     int B, int T, int H, int Hkv, int hd, int window, hipStream_t st) {
-  if (B * T * H == 0) return;
+int launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv, int at,
+                    int B, int T, int H, int Hkv, int hd, int window, hipStream_t st, float* amax_part,
+                    long amax_cap) {
+  if (B * T * H == 0) return 0;
   const int N = B * T;
   if (at != ACT_BF16)  // the bf16 dQ kernel forms D itself
     hipLaunchKernelGGL(attn_bwd_prep_kernel<float>, dim3((N * H + 3) / 4), dim3(256), 0, st, (const float*)o,
                        (const float*)dO, D, N, T, H, hd);
-  if (hd == 128) bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st);
-  else if (hd == 64) bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st);
-  else if (hd == 32) bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st);
+  if (hd == 128) return bwd_dispatch<128>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  if (hd == 64) return bwd_dispatch<64>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  if (hd == 32) return bwd_dispatch<32>(qkv, o, dO, lse, D, dqkv, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  return 0;
 }

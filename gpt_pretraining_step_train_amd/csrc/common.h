@@ -43,6 +43,11 @@ __device__ inline uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// x as a bf16 store rounds it.  Rounding to nearest is monotonic and odd, so the largest
+// magnitude among stored bf16 values is bf16_round of the largest fp32 magnitude: a
+// producer's running max of |value| gives the amax its stored tensor has.
+__device__ inline float bf16_round(float x) { return bf2f(f2bf(x)); }
+
 // ---------------------------------------------------------------------------
 // wave reductions (wave64)
 

@@ -44,6 +44,13 @@ __device__ inline void st4<bf16_t>(bf16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
+// the magnitude m as a store of type T holds it (see bf16_round)
+template <typename T>
+__device__ inline float round_act(float m) { return m; }
+template <>
+__device__ inline float round_act<bf16_t>(float m) { return bf16_round(m); }
+__device__ inline float max4abs(const float4& v) { return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))); }
+
 constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 256 threads
 constexpr int MAXV4 = 8;           // float4 per lane -> d <= 2048
 
@@ -67,21 +74,25 @@ __global__ void __launch_bounds__(256) embed_gather_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 // RMSNorm (no gain): y = x / sqrt(mean(x^2) + eps)
 
+// amax_part (or null): amax_part[row] = max |y[row][:]| as stored (an fp8 quantiser's amax
+// without a pass of its own)
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
-                                                          float* __restrict__ rstd, int N, int d, float eps) {
+                                                          float* __restrict__ rstd, int N, int d, float eps,
+                                                          float* __restrict__ amax_part) {
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
   const float4* xr = reinterpret_cast<const float4*>(x + (long)row * d);
   const int n4 = d / 4;
   float4 v[MAXV4];
-  float ss = 0.f;
+  float ss = 0.f, ma = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXV4; ++j) {
     const int i = lane + j * 64;
     v[j] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    ma = fmaxf(ma, max4abs(v[j]));
   }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
@@ -92,13 +103,18 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
     if (i < n4) st4<T>(yr + 4 * i, make_float4(v[j].x * r, v[j].y * r, v[j].z * r, v[j].w * r));
   }
   if (lane == 0) rstd[row] = r;
+  if (amax_part) {  // max over j of |v_j| r is the rounded product of the largest |v_j| (r > 0)
+    ma = wave_max(ma);
+    if (lane == 0) amax_part[row] = round_act<T>(ma * r);
+  }
 }
 
 // dx = dres + r * (dy - y * mean(dy * y)),  y = x * r
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                           const float* __restrict__ rstd, const float* __restrict__ dres,
-                                                          float* __restrict__ dx, T* __restrict__ dxa, int N, int d) {
+                                                          float* __restrict__ dx, T* __restrict__ dxa, int N, int d,
+                                                          float* __restrict__ amax_part) {
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
@@ -119,6 +135,7 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
     dot += g.x * yv[j].x + g.y * yv[j].y + g.z * yv[j].z + g.w * yv[j].w;
   }
   dot = wave_sum(dot) / (float)d;
+  float mo = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXV4; ++j) {
     const int i = lane + j * 64;
@@ -134,6 +151,11 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
     }
     reinterpret_cast<float4*>(dx + off)[i] = o;
     if (dxa) st4<T>(dxa + off + 4 * i, o);
+    mo = fmaxf(mo, max4abs(o));
+  }
+  if (amax_part) {  // amax_part[row] = max |dxa[row][:]| as stored
+    mo = wave_max(mo);
+    if (lane == 0) amax_part[row] = round_act<T>(mo);
   }
 }
 
@@ -683,12 +705,15 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_vec_kernel(bf16_t* __rest
                                                                   const float* __restrict__ cs,
                                                                   const float* __restrict__ rq,
                                                                   const float* __restrict__ rk, int N, int Tlen, int H,
-                                                                  int Hkv) {
+                                                                  int Hkv, float* __restrict__ amax_part) {
   constexpr int G = HD / 16, HALF = HD / 2;
   const long gid = ((long)blockIdx.x * 256 + threadIdx.x) / G;
   const int j = threadIdx.x % G;
   const int S = H + Hkv;
-  if (gid >= (long)N * S) return;
+  // amax_part (or null): one entry per wave, max |dq|, |dk| as stored (whole waves stay to
+  // reduce it; a thread group is wholly inside or past the end)
+  float mo = 0.f;
+  if (gid < (long)N * S) {
   const int n = (int)(gid / S), sl = (int)(gid % S);
   const long off = (long)n * (H + 2 * Hkv) * HD + (long)sl * HD;
   bf16_t* dp = dqkv + off;
@@ -719,6 +744,13 @@ __global__ void __launch_bounds__(256) rope_qknorm_bwd_vec_kernel(bf16_t* __rest
   }
   *reinterpret_cast<uint4*>(dp + 8 * j) = pack8f(o1);
   *reinterpret_cast<uint4*>(dp + HALF + 8 * j) = pack8f(o2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mo = fmaxf(mo, fmaxf(fabsf(o1[i]), fabsf(o2[i])));
+  }
+  if (amax_part) {
+    mo = wave_max(mo);
+    if ((threadIdx.x & 63) == 0) amax_part[blockIdx.x * 4 + (threadIdx.x >> 6)] = bf16_round(mo);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -754,10 +786,12 @@ __device__ inline float blk_sum(float v, float* sv) {
   return s;
 }
 
+// dz_part (or null): dz_part[4 n + wave] = max |dz| over the wave's part of row n, as stored
 template <typename T, int C>  // C float4 per thread, 256 threads -> V = 1024*C
 __global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ tgt,
                                                  T* __restrict__ dz, float* __restrict__ row_loss,
-                                                 int32_t* __restrict__ amax, int V, float inv_n, int* err) {
+                                                 int32_t* __restrict__ amax, int V, float inv_n, int* err,
+                                                 float* __restrict__ dz_part) {
   __shared__ float sv[4];
   __shared__ int si[4];
   const long n = blockIdx.x;
@@ -791,6 +825,7 @@ __global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ z, co
   const float inv = 1.f / s;
   const float sc = inv * inv_n;
   T* dr = dz + n * V;
+  float mp = 0.f;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int i4 = threadIdx.x + c * 256;
@@ -800,6 +835,11 @@ __global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ z, co
       if (k == 0) p.x -= inv_n; else if (k == 1) p.y -= inv_n; else if (k == 2) p.z -= inv_n; else p.w -= inv_n;
     }
     st4<T>(dr + 4 * i4, p);
+    mp = fmaxf(mp, max4abs(p));
+  }
+  if (dz_part) {
+    mp = wave_max(mp);
+    if ((threadIdx.x & 63) == 0) dz_part[n * 4 + (threadIdx.x >> 6)] = round_act<T>(mp);
   }
   if (threadIdx.x == 0) {
     const float zy = yok ? z[n * V + y] : 0.f;
@@ -814,7 +854,8 @@ __global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ z, co
 template <typename T>
 __global__ void __launch_bounds__(256) ce_generic_kernel(const float* __restrict__ z, const int32_t* __restrict__ tgt,
                                                          T* __restrict__ dz, float* __restrict__ row_loss,
-                                                         int32_t* __restrict__ amax, int V, float inv_n, int* err) {
+                                                         int32_t* __restrict__ amax, int V, float inv_n, int* err,
+                                                         float* __restrict__ dz_part) {
   __shared__ float sv[4];
   __shared__ int si[4];
   const long n = blockIdx.x;
@@ -834,10 +875,16 @@ __global__ void __launch_bounds__(256) ce_generic_kernel(const float* __restrict
   const int y = tgt[n];
   const bool yok = (y >= 0 && y < V);
   const float inv = 1.f / s;
+  float mp = 0.f;
   for (int i = threadIdx.x; i < V; i += 256) {
     float p = __expf(zr[i] - mx) * inv * inv_n;
     if (i == y) p -= inv_n;
     st<T>(dz + n * V + i, p);
+    mp = fmaxf(mp, fabsf(p));
+  }
+  if (dz_part) {
+    mp = wave_max(mp);
+    if ((threadIdx.x & 63) == 0) dz_part[n * 4 + (threadIdx.x >> 6)] = round_act<T>(mp);
   }
   if (threadIdx.x == 0) {
     row_loss[n] = (mx + logf(s)) - (yok ? zr[y] : 0.f);
@@ -1488,22 +1535,27 @@ void launch_embed_gather(const int32_t* tok, const float* E, float* h, int N, in
   hipLaunchKernelGGL(embed_gather_kernel, dim3((N + 3) / 4), dim3(256), 0, st, tok, E, h, N, d, V, err);
 }
 
-void launch_rmsnorm_fwd(const float* x, void* y, int yt, float* rstd, int N, int d, float eps, hipStream_t st) {
+int launch_rmsnorm_fwd(const float* x, void* y, int yt, float* rstd, int N, int d, float eps, hipStream_t st,
+                       float* amax_part, long amax_cap) {
   dim3 g((N + 3) / 4), b(256);
+  if (!amax_part || N > amax_cap) amax_part = nullptr;
   if (yt == ACT_BF16)
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, g, b, 0, st, x, (bf16_t*)y, rstd, N, d, eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, g, b, 0, st, x, (bf16_t*)y, rstd, N, d, eps, amax_part);
   else
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, b, 0, st, x, (float*)y, rstd, N, d, eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, b, 0, st, x, (float*)y, rstd, N, d, eps, amax_part);
+  return amax_part ? N : 0;
 }
 
-void launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
-                        void* dxa, int at, int N, int d, float eps, hipStream_t st) {
+int launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
+                       void* dxa, int at, int N, int d, float eps, hipStream_t st, float* amax_part, long amax_cap) {
   (void)eps;
   dim3 g((N + 3) / 4), b(256);
+  if (!amax_part || !dxa || N > amax_cap) amax_part = nullptr;
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, g, b, 0, st, dy, x, rstd, dres, dx, (bf16_t*)dxa, N, d);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, g, b, 0, st, dy, x, rstd, dres, dx, (bf16_t*)dxa, N, d, amax_part);
   else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, b, 0, st, dy, x, rstd, dres, dx, (float*)dxa, N, d);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, b, 0, st, dy, x, rstd, dres, dx, (float*)dxa, N, d, amax_part);
+  return amax_part ? N : 0;
 }
 
 void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st) {
@@ -1520,11 +1572,14 @@ static void rope_fwd_vec(bf16_t* qkv, const float* cs, float* rq, float* rk, int
 }
 
 template <int HD>
-static void rope_bwd_vec(bf16_t* dqkv, const bf16_t* qkv, const float* cs, const float* rq, const float* rk, int N,
-                         int T, int H, int Hkv, hipStream_t st) {
+static int rope_bwd_vec(bf16_t* dqkv, const bf16_t* qkv, const float* cs, const float* rq, const float* rk, int N,
+                        int T, int H, int Hkv, hipStream_t st, float* amax_part, long amax_cap) {
   const long threads = (long)N * (H + Hkv) * (HD / 16);
-  hipLaunchKernelGGL(rope_qknorm_bwd_vec_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dqkv,
-                     qkv, cs, rq, rk, N, T, H, Hkv);
+  const long blocks = (threads + 255) / 256;
+  if (!amax_part || 4 * blocks > amax_cap) amax_part = nullptr;
+  hipLaunchKernelGGL(rope_qknorm_bwd_vec_kernel<HD>, dim3((unsigned)blocks), dim3(256), 0, st, dqkv, qkv, cs, rq, rk,
+                     N, T, H, Hkv, amax_part);
+  return amax_part ? (int)(4 * blocks) : 0;
 }
 
 void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float* rk, int B, int T, int H, int Hkv,
@@ -1543,14 +1598,15 @@ void launch_rope_qknorm_fwd(void* qkv, int at, const float* cs, float* rq, float
     hipLaunchKernelGGL(rope_qknorm_fwd_kernel<float>, g, b, 0, st, (float*)qkv, cs, rq, rk, N, T, H, Hkv, hd, eps);
 }
 
-void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs, const float* rq, const float* rk,
-                            int B, int T, int H, int Hkv, int hd, hipStream_t st) {
+int launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs, const float* rq, const float* rk,
+                           int B, int T, int H, int Hkv, int hd, hipStream_t st, float* amax_part, long amax_cap) {
   const int N = B * T;
   if (at == ACT_BF16 && (hd == 128 || hd == 64 || hd == 32)) {
-    if (hd == 128) rope_bwd_vec<128>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st);
-    else if (hd == 64) rope_bwd_vec<64>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st);
-    else rope_bwd_vec<32>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st);
-    return;
+    if (hd == 128)
+      return rope_bwd_vec<128>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st, amax_part, amax_cap);
+    if (hd == 64)
+      return rope_bwd_vec<64>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st, amax_part, amax_cap);
+    return rope_bwd_vec<32>((bf16_t*)dqkv, (const bf16_t*)qkv, cs, rq, rk, N, T, H, Hkv, st, amax_part, amax_cap);
   }
   dim3 g((N * (H + Hkv) + 3) / 4), b(256);
   if (at == ACT_BF16)
@@ -1559,6 +1615,7 @@ void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int at, const float* cs
   else
     hipLaunchKernelGGL(rope_qknorm_bwd_kernel<float>, g, b, 0, st, (float*)dqkv, (const float*)qkv, cs, rq, rk, N, T,
                        H, Hkv, hd);
+  return 0;
 }
 
 void launch_mix_rmsnorm_fwd(const float* x, const float* z, const float* pa, float ma, const float* pb, float mb,
@@ -1646,26 +1703,28 @@ void launch_colsum(const float* part, int N, int R, void* ws, float* out, bool a
 
 template <typename T>
 static void ce_dispatch(const float* z, const int32_t* tgt, T* dz, float* rl, int32_t* am, int N, int V, float inv_n,
-                        int* err, hipStream_t st) {
+                        int* err, hipStream_t st, float* pt) {
   dim3 g(N), b(256);
   switch (V % 1024 == 0 ? V / 1024 : -1) {
-    case 1: hipLaunchKernelGGL((ce_kernel<T, 1>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
-    case 2: hipLaunchKernelGGL((ce_kernel<T, 2>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
-    case 4: hipLaunchKernelGGL((ce_kernel<T, 4>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
-    case 8: hipLaunchKernelGGL((ce_kernel<T, 8>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
-    case 16: hipLaunchKernelGGL((ce_kernel<T, 16>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
-    case 32: hipLaunchKernelGGL((ce_kernel<T, 32>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
-    default: hipLaunchKernelGGL(ce_generic_kernel<T>, g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err); break;
+    case 1: hipLaunchKernelGGL((ce_kernel<T, 1>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
+    case 2: hipLaunchKernelGGL((ce_kernel<T, 2>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
+    case 4: hipLaunchKernelGGL((ce_kernel<T, 4>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
+    case 8: hipLaunchKernelGGL((ce_kernel<T, 8>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
+    case 16: hipLaunchKernelGGL((ce_kernel<T, 16>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
+    case 32: hipLaunchKernelGGL((ce_kernel<T, 32>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
+    default: hipLaunchKernelGGL(ce_generic_kernel<T>, g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
   }
 }
 
-void launch_cross_entropy(const float* z, const int32_t* tgt, void* dz, int at, float* rl, int32_t* am, int N, int V,
-                          float inv_n, int* err, hipStream_t st) {
-  if (N <= 0) return;
+int launch_cross_entropy(const float* z, const int32_t* tgt, void* dz, int at, float* rl, int32_t* am, int N, int V,
+                         float inv_n, int* err, hipStream_t st, float* dz_part, long part_cap) {
+  if (N <= 0) return 0;
+  if (!dz_part || 4L * N > part_cap) dz_part = nullptr;
   if (at == ACT_BF16)
-    ce_dispatch<bf16_t>(z, tgt, (bf16_t*)dz, rl, am, N, V, inv_n, err, st);
+    ce_dispatch<bf16_t>(z, tgt, (bf16_t*)dz, rl, am, N, V, inv_n, err, st, dz_part);
   else
-    ce_dispatch<float>(z, tgt, (float*)dz, rl, am, N, V, inv_n, err, st);
+    ce_dispatch<float>(z, tgt, (float*)dz, rl, am, N, V, inv_n, err, st, dz_part);
+  return dz_part ? 4 * N : 0;
 }
 
 void launch_sum_rows(const float* x, int n, double* out, hipStream_t st) {
@@ -1958,6 +2017,10 @@ void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned*
     hipLaunchKernelGGL(amax_kernel<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits);
   else
     hipLaunchKernelGGL(amax_kernel<float>, dim3(g), dim3(256), 0, st, (const float*)x, rows, cols, ld, amax_bits);
+}
+
+void launch_amax_fold(const float* partials, int n, unsigned* amax_bits, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(1024), 0, st, partials, n, amax_bits);
 }
 
 void launch_quant_e4m3(const void* x, int it, int rows, int cols, long ld, const unsigned* amax_bits, uint8_t* q,

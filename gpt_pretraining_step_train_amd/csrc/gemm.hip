@@ -220,7 +220,8 @@ __device__ inline float4 epi_in4(const GemmArgs& p, int bz, int row, int col) {
 // the epilogue of four consecutive outputs a (accumulators) with their input in (epi_in4;
 // used when has_in)
 template <bool HALF = false>
-__device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col, float4 a, float4 in, bool has_in) {
+__device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col, float4 a, float4 in, bool has_in,
+                                     float& mx) {  // mx: running max |stored value| of the RELU2 / DRELU2 outputs
   float v[4] = {p.alpha * a.x, p.alpha * a.y, p.alpha * a.z, p.alpha * a.w};
   if (p.epi == EPI_LINEAR) {
     if (has_in) { v[0] += in.x; v[1] += in.y; v[2] += in.z; v[3] += in.w; }
@@ -244,11 +245,14 @@ __device__ inline void epilogue_vec4(const GemmArgs& p, int bz, int row, int col
   } else if (p.epi == EPI_RELU2) {
     const long o = bz * p.strideOA + (long)row * p.ldoa + col;
     float g[4];
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; }
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) { const float r = fmaxf(v[t], 0.f); g[t] = r * r; mx = fmaxf(mx, g[t]); }
     st4_act(reinterpret_cast<bf16_t*>(p.out2) + o, g);
   } else {  // EPI_DRELU2: the input is g = relu(u)^2, whose root is relu(u)
     const float g[4] = {in.x, in.y, in.z, in.w};
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) v[t] *= 2.f * __builtin_amdgcn_sqrtf(fmaxf(g[t], 0.f));
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) {
+      v[t] *= 2.f * __builtin_amdgcn_sqrtf(fmaxf(g[t], 0.f));
+      mx = fmaxf(mx, fabsf(v[t]));
+    }
     st4_act(reinterpret_cast<bf16_t*>(p.outA) + o_act(p, bz, row, col), v);
   }
 }
@@ -305,7 +309,8 @@ __device__ inline float4 epi_decode(const GemmArgs& p, int kind, const uint4& r)
 // element-wise inputs in raw (epi_load; the vector path only).
 template <bool HALF, int CS, int RPI>
 __device__ inline void write_block(const GemmArgs& p, int bz, int row0, int col, int lrow, int lc, bool vec,
-                                   const float* stage, float* ws_blk, int kind, const uint4 (&raw)[32 / RPI]) {
+                                   const float* stage, float* ws_blk, int kind, const uint4 (&raw)[32 / RPI],
+                                   float& mx) {
   constexpr int NR = 32 / RPI;
   if (p.splits > 1) {
 #pragma unroll 2
@@ -330,7 +335,7 @@ __device__ inline void write_block(const GemmArgs& p, int bz, int row0, int col,
       const int rr = lrow + i * RPI, row = row0 + rr;
       if (row >= p.M) break;
       epilogue_vec4<HALF>(p, bz, row, col, *reinterpret_cast<const float4*>(stage + rr * CS + lc),
-                          kind ? epi_decode(p, kind, raw[i]) : make_float4(0.f, 0.f, 0.f, 0.f), kind != 0);
+                          kind ? epi_decode(p, kind, raw[i]) : make_float4(0.f, 0.f, 0.f, 0.f), kind != 0, mx);
     }
   } else {
 #pragma unroll 1
@@ -488,7 +493,8 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_bf16_kernel(GemmArgs p) {
             if (col + t < p.N) w[t] = e[t];
         }
       } else if (vec && col + 3 < p.N) {
-        epilogue_vec4(p, bz, row, col, a, epi_in4(p, bz, row, col), epi_has_in(p));
+        float mx_ = 0.f;
+        epilogue_vec4(p, bz, row, col, a, epi_in4(p, bz, row, col), epi_has_in(p), mx_);
       } else {
         const float e[4] = {a.x, a.y, a.z, a.w};
         for (int t = 0; t < 4; ++t)
@@ -855,6 +861,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   const int ekind = p.splits == 1 && vec && n0 + wn * TN + lc + 3 < p.N ? epi_kind<F16 && BKM>(p) : 0;
   uint4 rin[NR];
   epi_load<NR, RPI>(p, ekind, bz, m0 + wm * TM, n0 + wn * TN + lc, lrow, rin);
+  float emx = 0.f;  // max |stored output| of the lane (amax_part)
 #pragma unroll 1
   for (int ib = 0; ib < FM; ++ib) {
 #define GEMM_STAGE(I_)                                                                          \
@@ -872,7 +879,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
     uint4 rnext[NR];
     epi_load<NR, RPI>(p, ib + 1 < FM ? ekind : 0, bz, row0 + 32, col, lrow, rnext);
     write_block<F16 && BKM, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
-                                     p.splits > 1 ? p.ws + (long)yy * p.M * p.N : nullptr, ekind, rin);
+                                     p.splits > 1 ? p.ws + (long)yy * p.M * p.N : nullptr, ekind, rin, emx);
 #pragma unroll
     for (int i = 0; i < NR; ++i) rin[i] = rnext[i];
     if (sym && tm != tn) {
@@ -887,7 +894,9 @@ gemm_bf16_dma_kernel(GemmArgs p) {
         const float4 a = make_float4(stage[(r4 + 0) * CS + cc], stage[(r4 + 1) * CS + cc], stage[(r4 + 2) * CS + cc],
                                      stage[(r4 + 3) * CS + cc]);
         if (vec && m + 3 < p.M) {
-          epilogue_vec4<F16 && BKM>(p, bz, n, m, a, epi_in4<F16 && BKM>(p, bz, n, m), epi_has_in<F16 && BKM>(p));
+          float mx_ = 0.f;
+          epilogue_vec4<F16 && BKM>(p, bz, n, m, a, epi_in4<F16 && BKM>(p, bz, n, m), epi_has_in<F16 && BKM>(p),
+                                    mx_);
         } else {
 #pragma unroll 1
           for (int t = 0; t < 4; ++t)
@@ -895,6 +904,10 @@ gemm_bf16_dma_kernel(GemmArgs p) {
         }
       }
     }
+  }
+  if (p.amax_part) {  // one entry per wave (single-matrix, unsplit launches: blockIdx.x is the tile)
+    emx = wave_max(emx);
+    if (lane == 0) p.amax_part[blockIdx.x * 8 + wave] = bf16_round(emx);
   }
 }
 
@@ -1068,6 +1081,7 @@ gemm_fp8_dma_kernel(GemmArgs p) {
   const int ekind = p.splits == 1 && vec && n0 + wn * TN + lc + 3 < p.N ? epi_kind<false>(p) : 0;
   uint4 rin[NR];
   epi_load<NR, RPI>(p, ekind, bz, m0 + wm * TM, n0 + wn * TN + lc, lrow, rin);
+  float emx = 0.f;
 #pragma unroll 1
   for (int ib = 0; ib < FM; ++ib) {
 #define FP8_STAGE(I_)                                                                           \
@@ -1085,9 +1099,13 @@ gemm_fp8_dma_kernel(GemmArgs p) {
     uint4 rnext[NR];
     epi_load<NR, RPI>(p, ib + 1 < FM ? ekind : 0, bz, row0 + 32, col, lrow, rnext);
     write_block<false, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
-                               p.splits > 1 ? p.ws + (long)blockIdx.y * p.M * p.N : nullptr, ekind, rin);
+                               p.splits > 1 ? p.ws + (long)blockIdx.y * p.M * p.N : nullptr, ekind, rin, emx);
 #pragma unroll
     for (int i = 0; i < NR; ++i) rin[i] = rnext[i];
+  }
+  if (p.amax_part) {
+    emx = wave_max(emx);
+    if (lane == 0) p.amax_part[blockIdx.x * 8 + wave] = bf16_round(emx);
   }
 }
 
@@ -1185,7 +1203,8 @@ __global__ void __launch_bounds__(128) splitk_reduce_vec_kernel(GemmArgs p) {
     const float4 v = *reinterpret_cast<const float4*>(w + k * MN);
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
-  epilogue_vec4(p, bz, row, 4 * c4, s, in, epi_has_in(p));
+  float mx_ = 0.f;
+  epilogue_vec4(p, bz, row, 4 * c4, s, in, epi_has_in(p), mx_);
 }
 
 template <int BM, int BN, int WM, int WN, bool SPLIT>
@@ -1311,6 +1330,16 @@ int pick_tile(const GemmArgs& p) {
 
 }  // namespace
 
+int gemm_amax_parts(const GemmArgs& p) {
+  if (p.epi != EPI_RELU2 && p.epi != EPI_DRELU2) return 0;
+  if (p.batch != 1 || p.splits > 1 || p.sym || p.split || p.dtype != ACT_BF16) return 0;
+  if (p.N % 4 || p.ldo % 4 || p.ldoa % 4 || p.ldcin % 4 || p.strideO % 4 || p.strideOA % 4 || p.strideCin % 4)
+    return 0;  // the vector epilogue (which tracks the maximum) must take every output
+  if (!p.fp8 && (pick_tile(p) != 1 || p.tile == 4)) return 0;  // the DMA kernels only
+  const long n = (long)((p.M + 255) / 256) * ((p.N + 255) / 256) * 8;
+  return n <= (1L << 30) ? (int)n : 0;
+}
+
 int gemm_auto_splits(const GemmArgs& p) {
   if (p.dtype == ACT_F32) return splits_for(p, 64, 64);
   if (p.fp8 || pick_tile(p) != 2) return splits_256(p);
@@ -1359,6 +1388,7 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
                  p.ldo % 4 || p.ldoa % 4 || p.strideO % 4 || p.strideOA % 4))
     return 1;
   if (p.dtype == ACT_F16 && (p.splits != 1 || p.epi != EPI_LINEAR)) return 1;
+  if (p.amax_part && gemm_amax_parts(p) == 0) return 1;
   if (p.fp8) {
     if (!p.a_kmaj || !p.b_kmaj || p.split || !p.dq_a || !p.dq_b) return 1;
     if (p.K % 16 || p.lda % 16 || p.ldb % 16) return 2;

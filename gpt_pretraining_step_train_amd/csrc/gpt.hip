@@ -88,7 +88,7 @@ struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
       xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, mv_jobs, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
-      xq8t, amax, qinv, amax_part, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
+      xq8t, amax, qinv, amax_part, amax_fuse, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
       nm_roff, nm_ws;
   size_t splitws_bytes;
 };
@@ -97,6 +97,16 @@ constexpr int kSumsqParts = 64;
 // quantisation events of one fp8 step: weights (4 per layer + head), forward inputs
 // (4 per layer + head), backward output gradients and inputs (8 per layer + 2)
 inline size_t kQuantSlots(const gpt_cfg& c) { return 16 * (size_t)c.depth + 8; }
+// process-wide: fp8 steps take the amax of their quantised activations and gradients from
+// the producing kernels (gptk_fp8_fused_amax)
+static int g_fp8_fused_amax = 1;
+// capacity (floats) for the per-wave amax partials the producers of a quantised tensor
+// write: the loss gradient's 4 per row, the dV and RoPE waves of dqkv, the fc / dReLU2
+// GEMMs' 8 per tile (a producer that would need more falls back to the amax pass)
+inline size_t kFuseParts(const gpt_cfg& c) {
+  const size_t N = (size_t)c.batch * c.seq_len;
+  return 4 * N + N * qkv_dim(c) / 512 + 65536;
+}
 // the forward's quantisation of each Linear input also serves its weight gradient
 inline bool keeps_xt(const gpt_cfg& c) {
   return c.precision == GPT_FP8 && (c.fp8_gemms & GPT_FP8_FWD) && (c.fp8_gemms & GPT_FP8_WGRAD);
@@ -217,8 +227,9 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
     O.amax = P.add(kQuantSlots(c) * 4);
     O.qinv = P.add(kQuantSlots(c) * 4);
     O.amax_part = P.add(kAmaxParts * 4);  // per-block maxima of the amax pass (reused, stream-ordered)
+    O.amax_fuse = P.add(kFuseParts(c) * 4);  // the producers' per-wave maxima (reused, stream-ordered)
   } else {
-    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.xq8t = O.amax = O.qinv = O.amax_part = 0;
+    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.xq8t = O.amax = O.qinv = O.amax_part = O.amax_fuse = 0;
   }
   O.rope = P.add(T * (c.head_dim / 2) * 2 * 4);
   O.loss = P.add(8);
@@ -294,6 +305,7 @@ struct gpt_model {
   bool fp8 = false;
   bool wq_dirty = true;  // fp8 weight copies must be refreshed before the next step
   int qslot = 0;         // next quantisation slot of the current step
+  int gemm_parts = 0;    // amax partials written by the last GEMM launched with amax_part
   long adam_t = 0;       // AdamW steps taken (bias corrections use the next one)
   bool acc_grads = false;  // the current step adds its gradients to the stored ones
   std::vector<int> xslot;  // per weight: quantisation slot of its input in this step's forward
@@ -334,6 +346,11 @@ int run_gemm(gpt_model* M, GemmArgs p, hipStream_t st, bool allow_split) {
     if ((size_t)p.splits * p.batch * p.M * p.N * 4 > p.ws_bytes) p.splits = 1;
   } else {
     p.splits = 1;
+  }
+  if (p.amax_part) {  // the output's amax partials, where this launch can write them
+    const int n = gemm_amax_parts(p);
+    if (n == 0 || (size_t)n > kFuseParts(M->cfg)) p.amax_part = nullptr;
+    M->gemm_parts = p.amax_part ? n : 0;
   }
   const bool prof = !M->prof_name.empty() && M->prof_name == gemm_kernel_name(p);
   if (prof) {
@@ -655,18 +672,22 @@ static uint8_t* xq8t_of(gpt_model* M, int w) {
   return M->at_off<uint8_t>(M->off.xq8t) + l * N * (3 * d + F) + j * N * d;
 }
 
+// (slot >= 0: the tensor's amax is already in that slot, folded from its producer's partials)
 static int quant_act(gpt_model* M, const void* x, int rows, int cols, long ldx, uint8_t* q, uint8_t* qt,
-                     hipStream_t st) {
-  const int slot = M->qslot++;
+                     hipStream_t st, int slot = -1) {
   unsigned* amax = M->at_off<unsigned>(M->off.amax);
-  launch_amax(x, ACT_BF16, rows, cols, ldx, amax + slot, st, M->at_off<float>(M->off.amax_part));
+  if (slot < 0) {
+    slot = M->qslot++;
+    launch_amax(x, ACT_BF16, rows, cols, ldx, amax + slot, st, M->at_off<float>(M->off.amax_part));
+  }
   launch_quant_e4m3(x, ACT_BF16, rows, cols, ldx, amax + slot, q, cols, qt, rows,
                     M->at_off<float>(M->off.qinv) + slot, st);
   return slot;
 }
 
 // Y = X W^T through weight w; p carries M, N (= rows of W), K, A/lda (X) and the epilogue
-static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st) {
+// (xslot >= 0: the quantisation slot already holding X's amax)
+static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st, int xslot = -1) {
   const WInfo wi = winfo(M, w);
   if (!M->fp8 || !(M->cfg.fp8_gemms & GPT_FP8_FWD)) {
     p.B = w == 4 * M->cfg.depth ? M->uact() : M->wact(wi.off);
@@ -675,7 +696,7 @@ static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st) {
   }
   uint8_t* q8a = M->at_off<uint8_t>(M->off.q8a);
   uint8_t* xt = keeps_xt(M->cfg) ? xq8t_of(M, w) : nullptr;
-  const int sx = quant_act(M, p.A, p.M, p.K, p.lda, q8a, xt, st);
+  const int sx = quant_act(M, p.A, p.M, p.K, p.lda, q8a, xt, st, xslot);
   M->xslot[w] = xt ? sx : -1;
   p.A = q8a; p.lda = p.K;
   p.B = M->at_off<uint8_t>(M->off.wq8) + wi.off; p.ldb = wi.cols;
@@ -688,7 +709,7 @@ static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st) {
 // backward of Y = X W^T: dW = dY^T X into dW (ld = cols of W) and dX = dY W with the
 // epilogue in pd (M = tokens, N = cols of W, K = rows of W, outputs set by the caller)
 static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long ldx, int w, float* dW, GemmArgs pd,
-                   hipStream_t st) {
+                   hipStream_t st, int yslot = -1) {
   const WInfo wi = winfo(M, w);
   const int N = M->N, nout = wi.rows, kin = wi.cols;
   int rc;
@@ -702,7 +723,8 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
   uint8_t* q8b = M->at_off<uint8_t>(M->off.q8b);
   uint8_t* q8c = M->at_off<uint8_t>(M->off.q8c);
   const float* qinv = M->at_off<float>(M->off.qinv);
-  const int sy = (f8w || f8d) ? quant_act(M, dY, N, nout, ldy, f8d ? q8a : nullptr, f8w ? q8b : nullptr, st) : 0;
+  const int sy =
+      (f8w || f8d) ? quant_act(M, dY, N, nout, ldy, f8d ? q8a : nullptr, f8w ? q8b : nullptr, st, yslot) : 0;
   if (f8w) {
     // X^T: kept from the forward (the same tensor, so the same scale and codes), else quantised here
     const bool kept = M->xslot[w] >= 0;
@@ -766,6 +788,19 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       cap_failed = true;
   };
 
+  // fp8: the producers of quantised tensors write per-wave amax partials (fpart), folded
+  // into the tensor's quantisation slot, so that its quantisation reads it only once
+  const bool fuse = M->fp8 && g_fp8_fused_amax && c.extras == 0 && (c.fp8_gemms & GPT_FP8_FWD) &&
+                    (c.fp8_gemms & GPT_FP8_DGRAD) && (c.fp8_gemms & GPT_FP8_WGRAD);
+  float* fpart = fuse ? M->at_off<float>(O.amax_fuse) : nullptr;
+  const long fcap = fuse ? (long)kFuseParts(c) : 0;
+  auto fold = [&](int n) -> int {  // the slot of a tensor whose producer wrote n partials; -1: none
+    if (n <= 0) return -1;
+    const int slot = M->qslot++;
+    launch_amax_fold(fpart, n, M->at_off<unsigned>(O.amax) + slot, st);
+    return slot;
+  };
+
   launch_zero(err, 16, st);
   if (M->fp8) {
     M->qslot = 0;
@@ -789,58 +824,65 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     float* rq = M->at_off<float>(O.rq) + (size_t)l * N * H;
     float* rk = M->at_off<float>(O.rk) + (size_t)l * N * Hkv;
     float* lse = M->at_off<float>(O.lse) + (size_t)l * B * H * T;
+    int sa = -1;     // quantisation slots with the amax already folded (fp8 steps), else -1
     if (ex_resid)  // layer input lr x + l0 x0
       launch_mix_rmsnorm_fwd(hsl(2 * l), hsl(0), S + s_lr(c, l), 1.f, S + s_l0(c, l), 1.f, xres(l), a, at,
                              M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
     else
-      launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st);
+      sa = fold(launch_rmsnorm_fwd(hsl(2 * l), a, at, M->at_off<float>(O.rstd_a) + (size_t)l * N, N, d, eps, st,
+                                   fpart, fcap));
     cap(l, CAP_A, a);
     cap(l, CAP_HIN, xres(l));
     {
       GemmArgs p;  // qkv = a Wqkv^T
       p.M = N; p.N = QD; p.K = d; p.A = a; p.lda = d;
       p.outA = qkv; p.ldoa = QD;
-      if ((rc = lin_fwd(M, p, 4 * l + 0, st))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 0, st, sa))) return rc;
     }
     cap(l, CAP_QKV, qkv);
     if (ex_ve)  // v += 3 sigmoid(gate) VE[token]
       launch_ve_fwd(qkv, at, a, tok, ve_tab(M->params(), l), ve_gate(M->params(), l), ve_g(l), N, V, H, Hkv, hd, d,
                     st);
     launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, eps, st);
-    launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st);
+    const int so = fold(launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st, fpart, fcap));
     cap(l, CAP_O, o);
     {
       GemmArgs p;  // h' = h + o Wo^T
       p.M = N; p.N = d; p.K = d; p.A = o; p.lda = d;
       p.Cin = xres(l); p.ldcin = d; p.beta = 1.f;
       p.outF = hsl(2 * l + 1); p.ldo = d;
-      if ((rc = lin_fwd(M, p, 4 * l + 1, st))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 1, st, so))) return rc;
     }
     cap(l, CAP_H1, hsl(2 * l + 1));
-    launch_rmsnorm_fwd(hsl(2 * l + 1), m, at, M->at_off<float>(O.rstd_m) + (size_t)l * N, N, d, eps, st);
+    const int sm = fold(launch_rmsnorm_fwd(hsl(2 * l + 1), m, at, M->at_off<float>(O.rstd_m) + (size_t)l * N, N, d,
+                                           eps, st, fpart, fcap));
     cap(l, CAP_M, m);
     {
       GemmArgs p;  // g = relu(m W1^T)^2 (the pre-activation itself is not kept: relu(u) = sqrt(g))
       p.M = N; p.N = F; p.K = d; p.A = m; p.lda = d;
       p.epi = EPI_RELU2; p.out2 = g; p.ldoa = F;
-      if ((rc = lin_fwd(M, p, 4 * l + 2, st))) return rc;
+      p.amax_part = fpart;
+      M->gemm_parts = 0;
+      if ((rc = lin_fwd(M, p, 4 * l + 2, st, sm))) return rc;
     }
+    const int sg = fold(M->gemm_parts);
     cap(l, CAP_G, g);
     {
       GemmArgs p;  // h'' = h' + g W2^T
       p.M = N; p.N = d; p.K = F; p.A = g; p.lda = F;
       p.Cin = hsl(2 * l + 1); p.ldcin = d; p.beta = 1.f;
       p.outF = hsl(2 * l + 2); p.ldo = d;
-      if ((rc = lin_fwd(M, p, 4 * l + 3, st))) return rc;
+      if ((rc = lin_fwd(M, p, 4 * l + 3, st, sg))) return rc;
     }
     cap(l, CAP_H2, hsl(2 * l + 2));
   }
   void* r = M->base + O.r;
+  int sr = -1;
   if (ex_back)  // the final norm reads x_L - lb x_mid
     launch_mix_rmsnorm_fwd(hsl(2 * L), hsl(2 * Lb), nullptr, 1.f, S + s_lb(c), -1.f, M->at_off<float>(O.hfin), r, at,
                            M->at_off<float>(O.rstd_f), N, d, eps, st);
   else
-    launch_rmsnorm_fwd(hsl(2 * L), r, at, M->at_off<float>(O.rstd_f), N, d, eps, st);
+    sr = fold(launch_rmsnorm_fwd(hsl(2 * L), r, at, M->at_off<float>(O.rstd_f), N, d, eps, st, fpart, fcap));
   cap(L, CAP_R, r);
   float* logits = M->at_off<float>(O.logits);
   void* dlogits = M->base + O.dlogits;
@@ -848,12 +890,13 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     GemmArgs p;  // logits = r U^T
     p.M = N; p.N = V; p.K = d; p.A = r; p.lda = d;
     p.outF = logits; p.ldo = V;
-    if ((rc = lin_fwd(M, p, 4 * L, st))) return rc;
+    if ((rc = lin_fwd(M, p, 4 * L, st, sr))) return rc;
   }
   cap(L, CAP_LOGITS, logits);
   // the whole backward is linear in dlogits: grad_scale / N there scales every gradient
-  launch_cross_entropy(logits, tgt, dlogits, at, M->at_off<float>(O.row_loss), M->at_off<int32_t>(O.argmax), N, V,
-                       grad_scale / (float)N, err, st);
+  const int sz = fold(launch_cross_entropy(logits, tgt, dlogits, at, M->at_off<float>(O.row_loss),
+                                           M->at_off<int32_t>(O.argmax), N, V, grad_scale / (float)N, err, st, fpart,
+                                           fcap));
   launch_sum_rows(M->at_off<float>(O.row_loss), N, M->at_off<double>(O.loss), st);
   cap(L, CAP_DLOGITS, dlogits);
 
@@ -868,7 +911,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     GemmArgs pd;  // dU = dz^T r ; dr = dz U
     pd.M = N; pd.N = d; pd.K = V;
     pd.outF = dtmp; pd.ldo = d;
-    if ((rc = lin_bwd(M, dlogits, V, r, d, 4 * L, grads + M->nE + M->nBlk, pd, st))) return rc;
+    if ((rc = lin_bwd(M, dlogits, V, r, d, 4 * L, grads + M->nE + M->nBlk, pd, st, sz))) return rc;
   }
   cap(L, CAP_DR, dtmp);
   float* dmid = M->at_off<float>(O.dmid);  // d loss / d x_mid through the backout term
@@ -878,9 +921,11 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
     launch_rmsnorm_mix_bwd(dtmp, M->at_off<float>(O.hfin), M->at_off<float>(O.rstd_f), nullptr, nullptr, 1.f,
                            S + s_lb(c), -1.f, false, nullptr, nullptr, dmid, hsl(2 * Lb),
                            xpart + (size_t)s_lb(c) * N, -1.f, nullptr, nullptr, 0.f, dh[0], dh_act, at, N, d, st);
-  } else {
-    launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps, st);
   }
+  int sdh = -1;  // slot of the output gradient entering the next block's W2 (dh_act)
+  if (!ex_back)
+    sdh = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps,
+                                  st, fpart, fcap));
   if (ex_resid) launch_zero(dx0, (size_t)N * d * 4, st);
   if (ex_ve) launch_embed_sort(tok, N, V, M->base + O.embws, st);  // shared by every scatter below
   int cur = 0;
@@ -899,38 +944,45 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       GemmArgs pd;  // dW2 = dY^T g ; du = (dY W2) * 2 relu(u), relu(u) = sqrt(g)
       pd.M = N; pd.N = F; pd.K = d;
       pd.epi = EPI_DRELU2; pd.aux = g; pd.outA = dbig; pd.ldoa = F;
-      if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st))) return rc;
+      pd.amax_part = fpart;
+      M->gemm_parts = 0;
+      if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st, sdh))) return rc;
     }
+    const int su = fold(M->gemm_parts);
     cap(l, CAP_DU, dbig);
     {
       GemmArgs pd;  // dW1 = du^T m ; dm = du W1
       pd.M = N; pd.N = d; pd.K = F;
       pd.outF = dtmp; pd.ldo = d;
-      if ((rc = lin_bwd(M, dbig, F, m, d, 4 * l + 2, gblk + wl + M->lo.w1, pd, st))) return rc;
+      if ((rc = lin_bwd(M, dbig, F, m, d, 4 * l + 2, gblk + wl + M->lo.w1, pd, st, su))) return rc;
     }
     cap(l, CAP_DM, dtmp);
-    launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur], dh[cur ^ 1],
-                       dh_act, at, N, d, eps, st);
+    const int sdo = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur],
+                                            dh[cur ^ 1], dh_act, at, N, d, eps, st, fpart, fcap));
     cur ^= 1;
     cap(l, CAP_DYO, dh_act);
     {
       GemmArgs pd;  // dWo = dY^T o ; do = dY Wo
       pd.M = N; pd.N = d; pd.K = d;
       pd.outA = do_act; pd.ldoa = d;
-      if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st))) return rc;
+      if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st, sdo))) return rc;
     }
     cap(l, CAP_DO, do_act);
-    launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, Hkv, hd, c.attn_window, st);
+    // dqkv's partials: the dV waves first, then the RoPE backward's (dQ, dK)
+    const int nq1 = launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, Hkv, hd,
+                                    c.attn_window, st, fpart, fcap);
     if (ex_ve)  // dVE rows, the gate's dz and the rows of d(gate weights), from dv
       launch_ve_bwd(dqkv, at, a, tok, ve_tab(M->params(), l), ve_g(l), M->at_off<float>(O.dve),
                     M->at_off<float>(O.vdz), M->at_off<float>(O.vpart), N, V, H, Hkv, hd, d, st);
-    launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, st);
+    const int nq2 = launch_rope_qknorm_bwd(dqkv, qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, st,
+                                           nq1 > 0 ? fpart + nq1 : nullptr, fcap - nq1);
+    const int sq = nq1 > 0 && nq2 > 0 ? fold(nq1 + nq2) : -1;
     cap(l, CAP_DQKV, dqkv);
     {
       GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
       pd.M = N; pd.N = d; pd.K = QD;
       pd.outF = dtmp; pd.ldo = d;
-      if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st))) return rc;
+      if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st, sq))) return rc;
     }
     cap(l, CAP_DA, dtmp);
     if (ex_ve) {  // the gate's path into the block input; the table's and gates' gradients
@@ -950,9 +1002,10 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
                              ex_resid ? hsl(2 * l) : nullptr, xpart + (size_t)s_lr(c, l) * N, 1.f,
                              ex_resid ? hsl(0) : nullptr, xpart + (size_t)s_l0(c, l) * N, 1.f, dh[cur ^ 1], dh_act,
                              at, N, d, st);
-    } else {
-      launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur], dh[cur ^ 1], dh_act,
-                         at, N, d, eps, st);
+      sdh = -1;
+    } else {  // (layer 0's output feeds the embedding, no Linear: no partials)
+      sdh = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur],
+                                    dh[cur ^ 1], dh_act, at, N, d, eps, st, l > 0 ? fpart : nullptr, fcap));
     }
     cur ^= 1;
   }
@@ -1486,6 +1539,12 @@ static int attn_ok(int dtype, int hd) {
 
 // key/value heads: 1 <= Hkv <= H with H % Hkv == 0 (any Hkv when H = 0)
 static bool kv_heads_ok(int H, int Hkv) { return H == 0 ? Hkv >= 0 : (Hkv >= 1 && Hkv <= H && H % Hkv == 0); }
+
+int gptk_fp8_fused_amax(int on) {
+  const int prev = g_fp8_fused_amax;
+  if (on >= 0) g_fp8_fused_amax = on ? 1 : 0;
+  return prev;
+}
 
 int gptk_attn_variant(int pass, int variant) {
   if (pass < 0 || pass > 1 || variant < 0 || variant > 1) return GPT_ERR_ARG;

@@ -50,22 +50,32 @@ struct GemmArgs {
   // epilogue of element (n, m) runs with its own Cin/aux entries).  A hint: kernels
   // that do not use it compute every tile.
   bool sym = false;
+  // amax_part (or null): per-wave maxima of |stored output| of an EPI_RELU2 / EPI_DRELU2
+  // launch, gemm_amax_parts(args) entries (launch_gemm fails where that is 0)
+  float* amax_part = nullptr;
 };
 
 // returns 0 on success, else an error code (argument/shape problems)
 int launch_gemm(const GemmArgs& p, hipStream_t st);
 // split-K factor the launcher would use for these arguments (for workspace sizing)
 int gemm_auto_splits(const GemmArgs& p);
+// number of amax_part entries this launch writes when given the buffer (0: not supported)
+int gemm_amax_parts(const GemmArgs& p);
 const char* gemm_kernel_name(const GemmArgs& p);
 
 // ---------------------------------------------------------------------------
 // elementwise / reduction kernels
 void launch_embed_gather(const int32_t* tok, const float* E, float* h, int N, int d, int V,
                          int* err_flag, hipStream_t st);
-void launch_rmsnorm_fwd(const float* x, void* y, int ytype, float* rstd, int N, int d, float eps,
-                        hipStream_t st);
-void launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres,
-                        float* dx, void* dx_act, int act_type, int N, int d, float eps, hipStream_t st);
+// Producers of tensors an fp8 step quantises take amax_part (scratch of amax_cap floats, or
+// null) and return how many entries they wrote there (0: none, the buffer being null, too
+// small or the path unsupported): per-wave maxima of |value| as stored, whose maximum
+// (launch_amax_fold) is the tensor's amax without a pass of its own.
+int launch_rmsnorm_fwd(const float* x, void* y, int ytype, float* rstd, int N, int d, float eps,
+                       hipStream_t st, float* amax_part = nullptr, long amax_cap = 0);
+int launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres,
+                       float* dx, void* dx_act, int act_type, int N, int d, float eps, hipStream_t st,
+                       float* amax_part = nullptr, long amax_cap = 0);  // partials of dx_act
 // extras (per-layer residual scaling, smear, backout).  A coefficient is mul * (*p), or mul
 // when p is null; p points into the parameter vector on the device.
 // m = a x + b z (fp32, z null: b = 0), y = m / rms(m), rstd as for launch_rmsnorm_fwd
@@ -103,12 +113,12 @@ void launch_rope_table(float* cs, int T, int hd, float base, hipStream_t st);
 // qkv rows are [H q heads | Hkv k heads | Hkv v heads] x hd; rstd_q is [B*T][H], rstd_k [B*T][Hkv]
 void launch_rope_qknorm_fwd(void* qkv, int act_type, const float* cs, float* rstd_q, float* rstd_k,
                             int B, int T, int H, int Hkv, int hd, float eps, hipStream_t st);
-void launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int act_type, const float* cs,
-                            const float* rstd_q, const float* rstd_k, int B, int T, int H, int Hkv, int hd,
-                            hipStream_t st);
-void launch_cross_entropy(const float* logits, const int32_t* targets, void* dlogits, int act_type,
-                          float* row_loss, int32_t* argmax, int N, int V, float inv_n, int* err_flag,
-                          hipStream_t st);
+int launch_rope_qknorm_bwd(void* dqkv, const void* qkv, int act_type, const float* cs,
+                           const float* rstd_q, const float* rstd_k, int B, int T, int H, int Hkv, int hd,
+                           hipStream_t st, float* amax_part = nullptr, long amax_cap = 0);  // partials of dq, dk
+int launch_cross_entropy(const float* logits, const int32_t* targets, void* dlogits, int act_type,
+                         float* row_loss, int32_t* argmax, int N, int V, float inv_n, int* err_flag,
+                         hipStream_t st, float* dlogits_part = nullptr, long part_cap = 0);
 void launch_sum_rows(const float* x, int n, double* out, hipStream_t st);
 // deterministic embedding backward: dE[v] = sum over positions n with tok[n]==v of dh[n], summed in
 // increasing n (accumulate: added to dE's previous value).  ws must hold embed_ws_bytes(N, V, d).
@@ -172,6 +182,8 @@ void launch_normuon_scale(const float* vmean, float* V, const long* roff, int nm
 constexpr int kAmaxParts = 1024;
 void launch_amax(const void* x, int in_type, long rows, long cols, long ld, unsigned* amax_bits, hipStream_t st,
                  float* partials = nullptr);
+// the slot (zeroed) receives the maximum of n producer partials
+void launch_amax_fold(const float* partials, int n, unsigned* amax_bits, hipStream_t st);
 // q[r][c] = e4m3(x[r][c] * s) and (optionally) qt[c][r] = the same byte, s = 448/amax
 // (1 when amax = 0); inv_scale[0] = 1/s.  in_type: ACT_F32 or ACT_BF16.
 void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, const unsigned* amax_bits,
@@ -182,7 +194,8 @@ void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, 
 // process-wide choice of the bf16 hd-128 attention kernels (see gptk_attn_variant)
 void set_attn_fwd_variant(int v);
 void set_attn_bwd_variant(int v);
-void launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int Hkv, int hd,
-                     int window, hipStream_t st);
-void launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,
-                     void* dqkv, int act_type, int B, int T, int H, int Hkv, int hd, int window, hipStream_t st);
+int launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int Hkv, int hd,
+                    int window, hipStream_t st, float* amax_part = nullptr, long amax_cap = 0);  // partials of o
+int launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,
+                    void* dqkv, int act_type, int B, int T, int H, int Hkv, int hd, int window, hipStream_t st,
+                    float* amax_part = nullptr, long amax_cap = 0);  // partials of dv

@@ -339,6 +339,18 @@ int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T,
  * Not thread-safe against concurrent launches. */
 int gptk_attn_variant(int pass, int variant);
 
+/* Process-wide choice of where fp8 steps take the per-tensor amax of the activations and
+ * output gradients they quantise ("3. Hassasiyet Yönetimi", the --fp8 recipe: per-tensor
+ * scales from the current max|x|): on = 1 (the default), the kernels that produce each
+ * such tensor (RMSNorm, attention, the fc and dReLU^2 GEMM epilogues, the RoPE backward,
+ * the cross-entropy gradient) also write per-wave maxima of the values as they store
+ * them, which one small launch folds into the tensor's slot; off = 0, a separate pass
+ * reads the stored tensor.  Both give the same amax bit for bit (bf16 rounding is
+ * monotonic), so the same codes and results.  Configurations with extras, or with some
+ * Linears outside fp8, always take the separate pass.  on < 0 only queries.  Returns the
+ * previous setting.  Not thread-safe against concurrent steps. */
+int gptk_fp8_fused_amax(int on);
+
 /* backward: dqkv act [B*T][(H + 2*Hkv)*hd] from qkv, o, dO act [B*T][H*hd] and lse,
  * with the forward's Hkv and window (dK and dV of a shared head sum over its query
  * heads); D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */

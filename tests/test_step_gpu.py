@@ -438,3 +438,52 @@ def test_device_init_statistics():
     loss = model.step(_dev(tok), _dev(tgt))
     want = np.log(cfg["vocab"]) + 0.5 * 0.02 ** 2 * cfg["d_model"]
     assert abs(loss - want) < 0.05
+
+
+def _two_fp8_steps(cfg, params, batches):
+    model = binding.Model(cfg, seed=0)
+    model.set_all_params(params)
+    out = []
+    for tk, tg in batches:
+        loss = model.step(_dev(tk), _dev(tg))
+        torch.cuda.synchronize()
+        out.append((loss, model.row_loss().cpu().numpy(), model.argmax().cpu().numpy(),
+                    [model.grads(i) for i in range(len(params))]))
+        model.muon_update(LR)
+    out.append([model.get_params(i) for i in range(len(params))])
+    del model
+    return out
+
+
+@pytest.mark.parametrize("name,over", [("laptop", {"precision": "fp8", "batch": 8}),
+                                       ("d26", {"batch": 1, "depth": 2}),
+                                       ("laptop", {"precision": "fp8", "batch": 8, "n_kv_head": 1,
+                                                   "attn_window": 100})],
+                         ids=["laptop_fp8", "d26_L2", "laptop_fp8_mqa_window"])
+def test_fp8_fused_amax_is_bit_identical(name, over):
+    """fp8 steps take each quantised tensor's amax from the kernels that produce it
+    (per-wave maxima of the values as stored) instead of a separate pass over the stored
+    tensor.  Rounding to bf16 is monotonic, so both give the same amax, hence the same
+    scales, codes and results: two steps with a Muon update between them (the second
+    step reuses the quantised weights' refresh) must be bit-identical either way."""
+    cfg = configs.get(name, **over)
+    assert cfg["precision"] == "fp8"
+    params = random_extras(inputs.init_weights(cfg, 0), cfg, 0)
+    batches = [inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=s)
+               for s in range(2)]
+    prev = binding.fp8_fused_amax(1)
+    try:
+        fused = _two_fp8_steps(cfg, params, batches)
+        binding.fp8_fused_amax(0)
+        sep = _two_fp8_steps(cfg, params, batches)
+    finally:
+        binding.fp8_fused_amax(prev)
+    for s in range(2):
+        assert fused[s][0] == sep[s][0]
+        np.testing.assert_array_equal(fused[s][1], sep[s][1])
+        np.testing.assert_array_equal(fused[s][2], sep[s][2])
+        for a, b in zip(fused[s][3], sep[s][3]):
+            np.testing.assert_array_equal(a, b)
+    for a, b in zip(fused[2], sep[2]):
+        np.testing.assert_array_equal(a, b)
+    say(f"  {name} {over}: losses {fused[0][0]:.6f}, {fused[1][0]:.6f}; fused and separate amax bit-identical")
