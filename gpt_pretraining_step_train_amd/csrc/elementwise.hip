@@ -1475,6 +1475,68 @@ __global__ void __launch_bounds__(1024) amax_final_kernel(const float* __restric
   }
 }
 
+// the slot (zeroed) <- max of n non-negative partials: up to 64 blocks over strided chunks,
+// one atomic each (max is order-free, so the result is exact and repeatable)
+__global__ void __launch_bounds__(256) amax_fold_kernel(const float* __restrict__ part, int n,
+                                                        unsigned* amax_bits) {
+  __shared__ float sm[4];
+  float m = 0.f;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) m = fmaxf(m, part[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]))));
+}
+
+// a 128x128 tile per block: rows of q and of qt leave as whole 128-byte lines.  Each
+// thread converts eight 8-wide row chunks (16 threads per row); qt is read back from
+// LDS by columns, a wave per 64 columns and half of the rows, 64 bytes per thread.
+template <typename T>
+__global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restrict__ x, int rows, int cols, long ldx,
+                                                              const unsigned* amax_bits, uint8_t* __restrict__ q,
+                                                              long ldq, uint8_t* __restrict__ qt, long ldqt,
+                                                              float* inv_scale) {
+  constexpr int TS = 136;  // LDS row stride in bytes (8-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * TS];
+  const float amax = __uint_as_float(*amax_bits);
+  const float s = amax > 0.f ? 448.f / amax : 1.f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
+  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+  const int t = threadIdx.x, c8 = (t & 15) * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rl = (t >> 4) + 16 * j, r = r0 + rl, c = c0 + c8;
+    uint2 b = make_uint2(0, 0);
+    if (r < rows && c < cols) {
+      float f[8];
+      load8f<T>(x + (long)r * ldx + c, f);
+      b = e4m3x8(f, s);
+      if (q) *reinterpret_cast<uint2*>(q + (long)r * ldq + c) = b;
+    }
+    if (qt) *reinterpret_cast<uint2*>(tile + rl * TS + c8) = b;
+  }
+  if (!qt) return;
+  __syncthreads();
+  const int cl = t & 127, rs = (t >> 7) * 64, c = c0 + cl, rb = r0 + rs;
+  if (c >= cols || rb >= rows) return;
+  uint32_t w[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[(rs + 4 * k + e) * TS + cl] << (8 * e);
+    w[k] = v;
+  }
+  uint8_t* dst = qt + (long)c * ldqt + rb;
+  if (rb + 64 <= rows && (ldqt % 16) == 0 && (rb % 16) == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      reinterpret_cast<uint4*>(dst)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+  } else {
+    for (int e = 0; e < 64 && rb + e < rows; ++e) dst[e] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+  }
+}
+
 // a 64x64 tile per block: each thread converts two 8-wide row chunks; the transposed
 // copy is read back from LDS by columns, 16 bytes per thread
 template <typename T>
@@ -2020,13 +2082,26 @@ void launch_amax(const void* x, int it, long rows, long cols, long ld, unsigned*
 }
 
 void launch_amax_fold(const float* partials, int n, unsigned* amax_bits, hipStream_t st) {
-  if (n > 0) hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(1024), 0, st, partials, n, amax_bits);
+  if (n <= 0) return;
+  const int blocks = std::min(64, (n + 2047) / 2048);
+  hipLaunchKernelGGL(amax_fold_kernel, dim3(blocks), dim3(256), 0, st, partials, n, amax_bits);
 }
 
 void launch_quant_e4m3(const void* x, int it, int rows, int cols, long ld, const unsigned* amax_bits, uint8_t* q,
                        long ldq, uint8_t* qt, long ldqt, float* inv_scale, hipStream_t st) {
   dim3 g((cols + 63) / 64, (rows + 63) / 64), b(256);
   if (rows <= 0 || cols <= 0) return;
+  if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0 && (!q || (ldq % 8 == 0 && (uintptr_t)q % 8 == 0)) &&
+      rows >= 128 && cols >= 128) {
+    const dim3 g2((cols + 127) / 128, (rows + 127) / 128);
+    if (it == ACT_BF16)
+      hipLaunchKernelGGL(quant_e4m3_t128_kernel<bf16_t>, g2, b, 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits, q,
+                         ldq, qt, ldqt, inv_scale);
+    else
+      hipLaunchKernelGGL(quant_e4m3_t128_kernel<float>, g2, b, 0, st, (const float*)x, rows, cols, ld, amax_bits, q,
+                         ldq, qt, ldqt, inv_scale);
+    return;
+  }
   if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0 && (!q || (ldq % 8 == 0 && (uintptr_t)q % 8 == 0))) {
     if (it == ACT_BF16)
       hipLaunchKernelGGL(quant_e4m3_vec_kernel<bf16_t>, g, b, 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits, q,

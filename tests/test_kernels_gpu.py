@@ -539,7 +539,8 @@ def _check_quant(x, dtype, pad=0, sample=None):
 
 @pytest.mark.parametrize("dtype,rows,cols,pad", [("fp32", 67, 129, 0), ("fp32", 67, 136, 0), ("bf16", 130, 200, 0),
                                                  ("bf16", 64, 64, 0), ("bf16", 1, 8, 0), ("bf16", 300, 128, 8),
-                                                 ("fp32", 70, 64, 16), ("bf16", 33, 72, 3)])
+                                                 ("fp32", 70, 64, 16), ("bf16", 33, 72, 3), ("bf16", 129, 136, 0),
+                                                 ("fp32", 256, 384, 0)])
 def test_quant_e4m3_matches_format(dtype, rows, cols, pad):
     rng = np.random.default_rng(21 + cols)
     x = rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-6, 4, (rows, cols)))
