@@ -918,9 +918,13 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // fp8 GEMM on the DMA path: the 256x256 tile of the bf16 kernel with 8 waves of 128x64,
 // both operands e4m3 with the reduction index contiguous, k tiles of BKB bytes in S
-// LDS stages (a 64-byte tile has the byte layout of a 32-deep bf16 K-major tile:
-// 16-byte chunk c of row r at c ^ kswz(r)).  Tile t + S - 1 is issued when tile t
-// starts.  A lane's fragment for one v_mfma_scale_f32_32x32x64_f8f6f4 is 32 bytes:
+// LDS stages (a 64-byte tile has the byte layout of a 32-deep bf16 K-major tile, a
+// 128-byte one that of a 64-deep tile: 16-byte chunk c of row r at c ^ kswz(r)).  With
+// S >= 3 tile t + S - 1 is issued before the last k slice of tile t, into the stage
+// tile t - 1 used; with S = 2 (128-byte tiles: every row of a tile is one whole
+// 128-byte line, half the DMA requests of 64-byte tiles) tile t + 2 goes into tile t's
+// own stage, after the block has waited for tile t + 1 and for its own LDS reads of
+// tile t, whose last slice is then in registers.  A lane's fragment for one v_mfma_scale_f32_32x32x64_f8f6f4 is 32 bytes:
 // lane half h holds k bytes 32h..32h+31 of its row (any k mapping shared by A and B
 // gives the same sum).  The k slices of all tiles form one sequence: the B fragments
 // of the next slice load under the current slice's MFMAs, and each A fragment is
@@ -934,7 +938,7 @@ gemm_fp8_dma_kernel(GemmArgs p) {
   constexpr int OBYTES = OP::BYTES, PER = OP::PER, LPT = 2 * PER;
   constexpr int ABASE = 0, BBASE = S * OBYTES;
   static_assert(NKK >= 1 && BKB % 64 == 0, "whole 64-byte MFMA k steps per tile");
-  static_assert(S >= 3 && (S - 2) * LPT < 64, "pipeline depth / vmcnt range");
+  static_assert(S >= 2 && (S - 2) * LPT < 64 && LPT < 64, "pipeline depth / vmcnt range");
   static_assert((S - 1) * OBYTES < 65536, "stage offsets must be immediates");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * S * OBYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -1018,10 +1022,17 @@ gemm_fp8_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // prologue: tiles 0..S-2 in flight; wait for tile 0 and fetch its first fragments
+  // prologue: tiles 0..S-2 in flight (0 and 1 for S = 2); wait for tile 0 and fetch its
+  // first fragments
+  if constexpr (S == 2) {
+    issue(0);
+    issue(1);
+    dma_sync<LPT>();
+  } else {
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue(st);
-  dma_sync<(S - 2) * LPT>();
+    for (int st = 0; st < S - 1; ++st) issue(st);
+    dma_sync<(S - 2) * LPT>();
+  }
   i32x8_t af[FM], bf[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) af[i] = frag(abase + i * 32 * BKB, 0);
@@ -1036,10 +1047,16 @@ gemm_fp8_dma_kernel(GemmArgs p) {
         const bool last = kk == NKK - 1;
         const int nst = last ? (u + 1) % S : u, nkk = last ? 0 : kk + 1;
         if (last) {
-          // tile t+1 landed; every wave is past tile t-1, whose stage was last read
-          // (into registers the MFMAs of tile t-1 consumed) one tile earlier
-          dma_sync<(S - 3) * LPT, false>();
-          issue((u + S - 1) % S);
+          if constexpr (S == 2) {
+            // tile t+1 landed and every wave's reads of tile t are done: tile t+2 into its stage
+            dma_sync<0>();
+            issue(u);
+          } else {
+            // tile t+1 landed; every wave is past tile t-1, whose stage was last read
+            // (into registers the MFMAs of tile t-1 consumed) one tile earlier
+            dma_sync<(S > 2 ? (S - 3) * LPT : 0), false>();
+            issue((u + S - 1) % S);
+          }
         }
         i32x8_t bn[FN];
 #pragma unroll
@@ -1394,7 +1411,10 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if (p.K % 16 || p.lda % 16 || p.ldb % 16) return 2;
     if ((long)p.M * p.lda >= (long)0xFFFFFFF0u || (long)p.N * p.ldb >= (long)0xFFFFFFF0u) return 2;
     const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    hipLaunchKernelGGL((gemm_fp8_dma_kernel<64, 4>), dim3(tiles, p.batch * p.splits), dim3(512), 0, st, p);
+    if (p.tile == 6)  // 64-byte k tiles in four stages (the form before 128-byte tiles)
+      hipLaunchKernelGGL((gemm_fp8_dma_kernel<64, 4>), dim3(tiles, p.batch * p.splits), dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_fp8_dma_kernel<128, 2>), dim3(tiles, p.batch * p.splits), dim3(512), 0, st, p);
   } else
   if (p.dtype == ACT_BF16 || p.dtype == ACT_F16) {
     // buffer loads address each operand matrix with 32-bit byte offsets
