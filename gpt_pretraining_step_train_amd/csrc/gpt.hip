@@ -1151,8 +1151,10 @@ static int ns_iterate(int nat, int nsplit, int steps, const float (*coeffs)[3], 
       p.B = xh; p.ldb = l; p.strideB = sl; p.b_kmaj = false;
       p.beta = a; p.Cin = nb.xf + off; p.ldcin = l; p.strideCin = sl;
       p.outF = nb.xf + off; p.ldo = l; p.strideO = sl;
-      p.outA = nb.xa[cur ^ 1] + off * es; p.ldoa = l; p.strideOA = sl;
-      if (next_sp) p.outA_lo = nb.xl[cur ^ 1] + off * es;
+      if (it + 1 < steps) {  // the operand planes of the next iteration (the last X is read in fp32 only)
+        p.outA = nb.xa[cur ^ 1] + off * es; p.ldoa = l; p.strideOA = sl;
+        if (next_sp) p.outA_lo = nb.xl[cur ^ 1] + off * es;
+      }
       if ((rc = run(p))) return rc;
     }
     cur ^= 1;
