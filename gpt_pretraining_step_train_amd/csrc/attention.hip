@@ -921,7 +921,8 @@ attn_bwd_dq_q64_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict_
 // dK, dV with the two accumulations in different waves: 8 waves per 128-key block,
 // waves 0-3 accumulate dV (S -> P, dV += P^T dO) and waves 4-7 dK (dP, P -> dS,
 // dK += dS^T Q) for the same 32 keys, each role 32 MFMAs per 64-query tile.  P
-// passes from the dV waves to the dK waves through LDS; each wave holds one 32x128
+// passes from the dV waves to the dK waves through LDS in bf16 (the precision the dV
+// waves' own MFMA takes it in); each wave holds one 32x128
 // accumulator, so two waves fit on every SIMD; the Q and dO tiles are staged once
 // for all eight.  A lane owns a key.  A block serves one key/value head: it walks the
 // query tiles of each of the G query heads that read it, one head after another,
@@ -935,7 +936,7 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TE];
   __shared__ __attribute__((aligned(16))) bf16_t Gs[2][TE];
   __shared__ __attribute__((aligned(16))) float L2s[2][BQT], Ds[2][BQT];
-  __shared__ __attribute__((aligned(16))) float Ps[2][4][4][64][4];  // [half][key wave][reg/4][lane][reg%4]
+  __shared__ __attribute__((aligned(16))) uint2 Ps[2][4][4][64];  // bf16 P: [half][key wave][reg/4][lane] x 4
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const bool dk_role = wave >= 4;
@@ -1053,8 +1054,8 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) a[4 * g + j] = fast_exp2(fmaf(a[4 * g + j], sl2, -lv[j]));
-          *reinterpret_cast<float4*>(&Ps[qs][kw][g][lane][0]) =
-              make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+          // bf16, as the dV waves' own MFMA takes P
+          Ps[qs][kw][g][lane] = make_uint2(pack_bf2(a[4 * g], a[4 * g + 1]), pack_bf2(a[4 * g + 2], a[4 * g + 3]));
         }
       }
       pd[qs] = a;
@@ -1067,9 +1068,11 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
       if (dk_role) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 p4 = *reinterpret_cast<const float4*>(&Ps[qs][kw][g][lane][0]);
+          const uint2 p2 = Ps[qs][kw][g][lane];
           const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][qs * 32 + 8 * g + 4 * hl]);
-          const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float pv[4] = {bf2f((bf16_t)(p2.x & 0xffff)), bf2f((bf16_t)(p2.x >> 16)), bf2f((bf16_t)(p2.y & 0xffff)),
+                               bf2f((bf16_t)(p2.y >> 16))};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) w[4 * g + j] = pv[j] * (pd[qs][4 * g + j] - dv4[j]);
         }
