@@ -1120,6 +1120,251 @@ attn_bwd_dkdv_split_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restr
   }
 }
 
+// The dK/dV kernel above, software-pipelined: in the split form every 64-query step
+// runs S -> P on the dV waves, a barrier, then dS on the dK waves (which wait for P) and
+// the two accumulations, so each role idles for part of every step.  Here the dV waves
+// form P of step t + 1 while the dK waves turn step t's P into dS: step t publishes
+// P[t + 1] (bf16, double-buffered) and accumulates dV += P[t]^T dO[t] from the P it
+// formed one step earlier (read back from LDS, as the dK waves read it), while the dK waves form dP[t], read
+// P[t] and accumulate dK += dS[t]^T Q[t].  Each step needs the Q / dO tiles of t and
+// t + 1, so the tiles are triple-buffered (the one for t + 2 is staged during step t
+// into the buffer of t - 1; head_dim 128 by buffer-load DMA, other sizes through
+// registers), and one barrier per step orders everything.
+template <int HD>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_pipe_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
+                          const float* __restrict__ lse, const float* __restrict__ Dv, bf16_t* __restrict__ dqkv,
+                          int T, int H, int Hkv, int W, float* __restrict__ amax_part) {
+  constexpr int BKEY = 128, BQT = 64, TE = Tile<HD>::ELEMS, RS = Tile<HD>::RS, NDB = HD / 32, NKK = HD / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[3][TE];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[3][TE];
+  __shared__ __attribute__((aligned(16))) float L2s[3][BQT], Ds[3][BQT];
+  __shared__ __attribute__((aligned(16))) uint2 Ps[2][2][4][4][64];  // [step%2][half][key wave][reg/4][lane]
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool dk_role = wave >= 4;
+  const int kw = wave & 3;
+  int kb, bk;
+  head_major_coords(kb, bk);
+  const int G = H / Hkv, b = bk / Hkv, hk = bk % Hkv;
+  const long ld = (long)(H + 2 * Hkv) * HD, ldo = (long)H * HD;
+  const bf16_t* Qb = qkv + (long)b * T * ld;
+  const bf16_t* K = Qb + (long)(H + hk) * HD;
+  const bf16_t* V = K + (long)Hkv * HD;
+  const bf16_t* Gb = dO + (long)b * T * ldo;
+  const long lrow = (long)b * H * T;
+  const int key0 = kb * BKEY + kw * 32, mykey = key0 + lq;
+
+  // the dV waves hold K (for S), the dK waves V (for dP)
+  bf16x8_t kvf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (mykey < T) u = *reinterpret_cast<const uint4*>((dk_role ? V : K) + (long)mykey * ld + kk * 16 + hl * 8);
+    kvf[kk] = __builtin_bit_cast(bf16x8_t, u);
+  }
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  int qro[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qro[kk] = Tile<HD>::off(lq, kk * 16 + hl * 8);
+  const int i16 = lane & 15;
+  const int trr = 4 * hl + (i16 >> 2), trc = ((lane >> 4) & 1) * 16 + 4 * (i16 & 3);
+  int tro[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    tro[db][0] = Tile<HD>::off(trr, db * 32 + trc);
+    tro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
+  }
+
+  const int Wn = W > 0 ? W : T;
+  const int nqt = min((T + BQT - 1) / BQT, (kb * BKEY + BKEY - 1 + Wn - 1) / BQT + 1);
+  const int qt0 = (kb * BKEY) / BQT;
+  const int ntile = nqt - qt0;
+  const int nsteps = G * ntile;
+  // step sp covers query tile qt0 + sp % ntile of query head hk G + sp / ntile
+  auto step_q0 = [&](int sp) { return (qt0 + sp % ntile) * BQT; };
+  auto step_h = [&](int sp) { return hk * G + sp / ntile; };
+  // whether 32-query half qs of step sp holds a query that sees one of the wave's keys
+  auto half_live = [&](int sp, int qs) {
+    const int q0 = step_q0(sp) + qs * 32;
+    return key0 < T && q0 + 31 >= key0 && q0 <= key0 + 31 + Wn - 1;
+  };
+
+  // staging of step sp's tiles into buffer buf: load (DMA straight into LDS for head_dim
+  // 128, else into registers) early, store (registers -> LDS, and lse / D) late
+  PairStager<HD == 128 ? 8 : HD, 512> stg;  // unused for head_dim 128
+  DmaTilePair<512> dma, dmo;                 // chunk maps of Q rows (stride ld) and dO rows (stride ldo)
+  if constexpr (HD == 128) {
+    dma.init(ld, tid);
+    dmo.init(ldo, tid);
+  } else {
+    stg.init(ld, ldo, tid);
+  }
+  float pl = 0.f, pd = 0.f;
+  auto load = [&](int sp, int buf) {
+    const int q0 = step_q0(sp), h = step_h(sp);
+    if constexpr (HD == 128) {
+      const u32x4w_t rq = rows_words(Qb + h * HD, ld, q0, T, HD), rg = rows_words(Gb + h * HD, ldo, q0, T, HD);
+      const uint32_t ql = (uint32_t)(uintptr_t)Qs[buf], gl = (uint32_t)(uintptr_t)Gs[buf];
+#pragma unroll
+      for (int j = 0; j < DmaTilePair<512>::PER; ++j) {
+        attn_dma16(rq, ql + (j * 512 + wave * 64) * 16, dma.voff[j]);
+        attn_dma16(rg, gl + (j * 512 + wave * 64) * 16, dmo.voff[j]);
+      }
+    } else {
+      stg.load(rows_rsrc(Qb + h * HD, ld, q0, T, HD), rows_rsrc(Gb + h * HD, ldo, q0, T, HD), tid);
+    }
+    if (tid < BQT) {
+      const int q = q0 + tid;
+      const long r = lrow + (long)h * T + q;
+      pl = q < T ? lse[r] * LOG2E : 0.f;
+      pd = q < T ? Dv[r] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    if constexpr (HD != 128) stg.store(Qs[buf], Gs[buf], tid);
+    if (tid < BQT) {
+      L2s[buf][tid] = pl;
+      Ds[buf][tid] = pd;
+    }
+  };
+  // every wave's DMA and LDS reads done, then the block barrier
+  auto step_sync = [&]() {
+    if constexpr (HD == 128) dma_wait_sync();
+    else __syncthreads();
+  };
+  // dV waves: S^T = K Q^T of step sp (buffer qb) -> P, published to Ps[sp & 1] (bf16,
+  // the dV MFMA's operand)
+  auto form_p = [&](auto par_c, int sp, int qb) {  // par_c: sp & 1 as a compile-time constant
+    constexpr int par = decltype(par_c)::value;
+    const int qb0 = step_q0(sp);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      if (!half_live(sp, qs)) continue;
+      const bf16_t* rp = Qs[qb] + qs * 32 * RS;
+      f32x16_t a = mfma32x32x16_bf16(lds_row8(rp + qro[0]), kvf[0], zero16());
+#pragma unroll
+      for (int kk = 1; kk < NKK; ++kk) a = mfma32x32x16_bf16(lds_row8(rp + qro[kk]), kvf[kk], a);
+      if (qb0 + qs * 32 < key0 + 31 || qb0 + qs * 32 + 31 - key0 >= Wn) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb0 + qs * 32 + acc_row(lane, r);
+          if (q < mykey || q - mykey >= Wn) a[r] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&L2s[qb][qs * 32 + 8 * g + 4 * hl]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = fast_exp2(fmaf(a[4 * g + j], sl2, -lv[j]));
+        Ps[par][qs][kw][g][lane] = make_uint2(pack_bf2(e[0], e[1]), pack_bf2(e[2], e[3]));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one half at a time (registers)
+    }
+  };
+
+  if (nsteps > 0) {
+    load(0, 0);
+    store(0);
+    if (nsteps > 1) {
+      load(1, 1);
+      store(1);
+    }
+  }
+  step_sync();
+  if (!dk_role && nsteps > 0) form_p(std::integral_constant<int, 0>{}, 0, 0);
+  step_sync();  // P of step 0 published
+
+  // one step; par_c = sp & 1 at compile time (the loop is unrolled by two)
+  auto step = [&](auto par_c, int sp) {
+    constexpr int par = decltype(par_c)::value;
+    const int cb = sp % 3, nb = (sp + 1) % 3;
+    if (sp + 2 < nsteps) load(sp + 2, (sp + 2) % 3);  // into the buffer of step sp - 1
+    if (!dk_role) {
+      if (sp + 1 < nsteps) form_p(std::integral_constant<int, par ^ 1>{}, sp + 1, nb);
+      __builtin_amdgcn_sched_barrier(0);  // keep the two parts' registers apart
+      // dV += P^T dO of step sp
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (!half_live(sp, qs)) continue;
+        const bf16_t* tp0 = Gs[cb] + qs * 32 * RS;
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          const uint2 lo = Ps[par][qs][kw][2 * s_][lane], hi = Ps[par][qs][kw][2 * s_ + 1][lane];
+          const bf16x8_t wa = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const bf16_t* tp = tp0 + 16 * s_ * RS;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16_bf16(wa, lds_tr_pair(tp + tro[db][0], tp + tro[db][1]), acc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (!half_live(sp, qs)) continue;
+        // dP^T = V dO^T of step sp
+        const bf16_t* rp = Gs[cb] + qs * 32 * RS;
+        f32x16_t a = mfma32x32x16_bf16(lds_row8(rp + qro[0]), kvf[0], zero16());
+#pragma unroll
+        for (int kk = 1; kk < NKK; ++kk) a = mfma32x32x16_bf16(lds_row8(rp + qro[kk]), kvf[kk], a);
+        // dS = P (dP - D), then dK += dS^T Q
+        float w[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint2 p2 = Ps[par][qs][kw][g][lane];
+          const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cb][qs * 32 + 8 * g + 4 * hl]);
+          const float pv[4] = {bf2f((bf16_t)(p2.x & 0xffff)), bf2f((bf16_t)(p2.x >> 16)),
+                               bf2f((bf16_t)(p2.y & 0xffff)), bf2f((bf16_t)(p2.y >> 16))};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[4 * g + j] = pv[j] * (a[4 * g + j] - dv4[j]);
+        }
+        const bf16_t* tp0 = Qs[cb] + qs * 32 * RS;
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          const bf16x8_t wa = pack8(w + 8 * s_);
+          const bf16_t* tp = tp0 + 16 * s_ * RS;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16_bf16(wa, lds_tr_pair(tp + tro[db][0], tp + tro[db][1]), acc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (sp + 2 < nsteps) store((sp + 2) % 3);
+    step_sync();
+  };
+  for (int sp = 0; sp < nsteps; sp += 2) {
+    step(std::integral_constant<int, 0>{}, sp);
+    if (sp + 1 < nsteps) step(std::integral_constant<int, 1>{}, sp + 1);
+  }
+  const float scale = dk_role ? 1.f / sqrtf((float)HD) : 1.f;
+  const long col = (long)(dk_role ? H + hk : H + Hkv + hk) * HD;
+  float mo = 0.f;  // max |dv| of the lane as stored (amax_part)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + acc_row(lane, r);
+      if (key < T) {
+        const float v = acc[db][r] * scale;
+        dqkv[((long)b * T + key) * ld + col + db * 32 + lq] = f2bf(v);
+        if (!dk_role) mo = fmaxf(mo, fabsf(v));
+      }
+    }
+  if (amax_part) {
+    mo = wave_max(mo);
+    if (lane == 0) amax_part[((long)blockIdx.y * gridDim.x + blockIdx.x) * 8 + wave] = bf16_round(mo);
+  }
+}
+
 // dK and dV with 64 keys per wave (two 32-key blocks), one wave per SIMD: a wave forms
 // S, P, dP and dS for its own keys and accumulates both dK and dV (2 x 4 accumulators
 // each, 256 registers), so P never leaves registers and every Q / dO fragment read from
@@ -1525,8 +1770,12 @@ int bwd_dispatch(const void* qkv, const void* o, const void* dO, const float* ls
       const dim3 g((T + 127) / 128, B * Hkv);
       const long np = (long)g.x * g.y * 8;
       if (!amax_part || np > amax_cap) amax_part = nullptr;
-      hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, g, dim3(512), 0, st, (const bf16_t*)qkv,
-                         (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W, amax_part);
+      if (g_attn_bwd_variant == 2)
+        hipLaunchKernelGGL(attn_bwd_dkdv_split_kernel<HD>, g, dim3(512), 0, st, (const bf16_t*)qkv,
+                           (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W, amax_part);
+      else
+        hipLaunchKernelGGL(attn_bwd_dkdv_pipe_kernel<HD>, g, dim3(512), 0, st, (const bf16_t*)qkv,
+                           (const bf16_t*)dO, lse, D, (bf16_t*)dqkv, T, H, Hkv, W, amax_part);
       parts = amax_part ? (int)np : 0;
     }
   } else {

@@ -1549,7 +1549,7 @@ int gptk_fp8_fused_amax(int on) {
 }
 
 int gptk_attn_variant(int pass, int variant) {
-  if (pass < 0 || pass > 1 || variant < 0 || variant > 1) return GPT_ERR_ARG;
+  if (pass < 0 || pass > 1 || variant < 0 || variant > (pass == 1 ? 2 : 1)) return GPT_ERR_ARG;
   if (pass == 0) set_attn_fwd_variant(variant);
   else set_attn_bwd_variant(variant);
   return GPT_OK;

@@ -334,8 +334,10 @@ int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T,
  * measured).  pass 0 = forward: variant 0 = 32 queries per wave (two waves per SIMD),
  * 1 = 64 queries per wave (one wave per SIMD); pass 1 = backward: variant 0 = dQ by
  * waves of 32 queries and dK/dV by 8 waves of 32 keys (dV and dK accumulated by different
- * waves), 1 = dQ by waves of 64 queries and dK/dV by 4 waves of 64 keys (one wave
- * accumulates both).  GPT_ERR_ARG for another pass/variant.
+ * waves), software-pipelined (P of the next query tile formed while the current one's
+ * dS is), 1 = dQ by waves of 64 queries and dK/dV by 4 waves of 64 keys (one wave
+ * accumulates both), 2 = variant 0 without the pipelining (S -> P, a barrier, then
+ * dS within each query tile).  GPT_ERR_ARG for another pass/variant.
  * Not thread-safe against concurrent launches. */
 int gptk_attn_variant(int pass, int variant);
 

@@ -295,6 +295,44 @@ def test_attention_fwd_bwd(case):
         assert e < gtol, (i, e)
 
 
+# the backward's kernel variants (gptk_attn_variant pass 1): the pipelined dK/dV kernel
+# (0, the default) and the unpipelined one (2) take the same steps in the same order, so
+# their results must be bit-identical; the 64-key form (1, head_dim 128 only; run here on
+# whole 256-query blocks of causal multi-head attention) is held to the kernel tolerance
+BWD_VARIANT_CASES = [("bf16", 2, 300, 3, 128, 0), ("bf16", 1, 256, 2, 64, 0), ("bf16", 2, 130, 2, 32, 37),
+                     ("bf16", 1, 700, 2, 128, 200), ("bf16", 2, 300, 4, 128, 0, 2), ("bf16", 1, 300, 6, 128, 100, 1),
+                     ("bf16", 1, 1, 4, 128, 0, 2), ("bf16", 1, 64, 2, 128, 0), ("bf16", 1, 2048, 2, 128, 0)]
+
+
+@pytest.mark.parametrize("case", BWD_VARIANT_CASES)
+def test_attention_bwd_variants_agree(case):
+    dtype, Bn, T, H, hd, win = case[:6]
+    Hkv = case[6] if len(case) > 6 else H
+    qkv, _, _, _ = _qkv(Bn, T, H, hd, 13, dtype, Hkv)
+    d, dkv = H * hd, Hkv * hd
+    dq = to_dev(qkv, dtype)
+    o = torch.zeros(Bn * T, d, device="cuda", dtype=dq.dtype)
+    lse = torch.zeros(Bn * H * T, device="cuda")
+    B.attn_fwd(DT[dtype], dq, o, lse, Bn, T, H, hd, win, n_kv=Hkv)
+    rng = np.random.default_rng(14)
+    ddo = to_dev(_round(rng.standard_normal((Bn * T, d)), dtype), dtype)
+    out = {}
+    try:
+        for var in ([0, 2, 1] if hd == 128 and T % 256 == 0 and win == 0 and Hkv == H else [0, 2]):
+            B.attn_variant(1, var)
+            D = torch.zeros(Bn * H * T, device="cuda")
+            dqkv = torch.full((Bn * T, d + 2 * dkv), float("nan"), device="cuda", dtype=dq.dtype)
+            B.attn_bwd(DT[dtype], dq, o, ddo, lse, D, dqkv, Bn, T, H, hd, win, n_kv=Hkv)
+            torch.cuda.synchronize()
+            out[var] = from_dev(dqkv)
+    finally:
+        B.attn_variant(1, 0)
+    np.testing.assert_array_equal(out[0], out[2])
+    assert np.isfinite(out[0]).all()
+    if 1 in out:
+        assert rel_l2(out[1], out[0]) < 1e-2
+
+
 def test_attention_rejects_bad_kv_heads():
     t = torch.zeros(16, device="cuda")
     for H, Hkv in [(4, 3), (4, 0), (4, 8), (3, -1)]:
