@@ -191,6 +191,60 @@ struct PairStager {
   }
 };
 
+// Buffer-load DMA of 16-byte chunks straight into LDS (no registers): lane l of one
+// instruction writes LDS bytes M0 + 16 l .. + 15.  Written in assembly (as in the GEMM)
+// so that the compiler does not wait for every DMA before each LDS read; the waits are
+// explicit (dma_wait_sync).
+typedef unsigned int u32x4w_t __attribute__((ext_vector_type(4)));
+__device__ inline u32x4w_t rows_words(const bf16_t* base, long ld, int row0, int T, int HD) {
+  const uint32_t bytes = row0 < T ? (uint32_t)(((long)(T - row0 - 1) * ld + HD) * 2) : 0u;
+  const uintptr_t a = (uintptr_t)(base + (long)row0 * ld);
+  u32x4w_t r;
+  r.x = (uint32_t)a;
+  r.y = (uint32_t)(a >> 32) & 0xFFFFu;
+  r.z = bytes;
+  r.w = 0x00020000u;
+  return r;
+}
+__device__ inline void attn_dma16(const u32x4w_t& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// every DMA of this wave landed (vmcnt 0) and its LDS reads done, then a workgroup barrier
+__device__ inline void dma_wait_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K and V tiles [64 rows][128] (Tile<128> layout) by DMA from NT threads: instruction j
+// of thread tid fills LDS chunk p = j NT + tid, i.e. row p / 16 and physical chunk p % 16,
+// which holds logical chunk (p % 16) ^ swz(row).  Rows at or past T read zeros (the
+// descriptor ends at the sequence's last row).
+template <int NT>
+struct DmaTilePair {
+  static constexpr int PER = 64 * 16 / NT;
+  uint32_t voff[PER];
+  __device__ inline void init(long ld, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int pch = j * NT + tid, row = pch >> 4, c = (pch & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+      voff[j] = (uint32_t)(((long)row * ld + c * 8) * 2);
+    }
+  }
+  __device__ inline void issue(const u32x4w_t& rk, const u32x4w_t& rv, const bf16_t* ks, const bf16_t* vs, int wave) {
+    const uint32_t kl = (uint32_t)(uintptr_t)ks, vl = (uint32_t)(uintptr_t)vs;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      attn_dma16(rk, kl + (j * NT + wave * 64) * 16, voff[j]);
+      attn_dma16(rv, vl + (j * NT + wave * 64) * 16, voff[j]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // forward
 
@@ -250,17 +304,31 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     vro[db][1] = Tile<HD>::off(trr + 8, db * 32 + trc);
   }
 
-  PairStager<HD, NW * 64> stg;
-  stg.init(ld, ld, tid);
-  stg.load(rows_rsrc(K, ld, it0 * BKV, T, HD), rows_rsrc(V, ld, it0 * BKV, T, HD), tid);
-  stg.store(Ks[0], Vs[0], tid);
-  __syncthreads();
+  // K/V tiles: head_dim 128 by buffer-load DMA straight into LDS, other sizes through registers
+  PairStager<HD == 128 ? 8 : HD, NW * 64> stg;  // unused for head_dim 128
+  DmaTilePair<NW * 64> dma;
+  if constexpr (HD == 128) {
+    dma.init(ld, tid);
+    dma.issue(rows_words(K, ld, it0 * BKV, T, HD), rows_words(V, ld, it0 * BKV, T, HD), Ks[0], Vs[0], wave);
+    dma_wait_sync();
+  } else {
+    stg.init(ld, ld, tid);
+    stg.load(rows_rsrc(K, ld, it0 * BKV, T, HD), rows_rsrc(V, ld, it0 * BKV, T, HD), tid);
+    stg.store(Ks[0], Vs[0], tid);
+    __syncthreads();
+  }
 
   // one KV tile; the LDS buffer index is a compile-time constant (loop unrolled by 2)
   auto body = [&](auto cur_c, int it) {
     constexpr int cur = decltype(cur_c)::value;
     const int k0 = it * BKV;
-    if (it + 1 < nkv) stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
+    if (it + 1 < nkv) {  // the other buffer was last read in the previous tile, before its barrier
+      if constexpr (HD == 128)
+        dma.issue(rows_words(K, ld, k0 + BKV, T, HD), rows_words(V, ld, k0 + BKV, T, HD), Ks[cur ^ 1], Vs[cur ^ 1],
+                  wave);
+      else
+        stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
+    }
     // the wave's 32 queries see keys q0 - Wn + 1 .. q0 + 31
     if (k0 <= q0 + 31 && k0 + BKV - 1 >= q0 - Wn + 1 && q0 < T) {
       f32x16_t s[2];
@@ -321,8 +389,12 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
             oacc[db] = mfma32x32x16_bf16(lds_tr_pair(vp + vro[db][0], vp + vro[db][1]), pb, oacc[db]);
         }
     }
-    if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
-    __syncthreads();
+    if constexpr (HD == 128) {
+      dma_wait_sync();
+    } else {
+      if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
+      __syncthreads();
+    }
   };
   for (int it = it0; it < nkv; it += 2) {
     body(std::integral_constant<int, 0>{}, it);
@@ -352,60 +424,6 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     if (lane == 0) amax_part[((long)blockIdx.y * gridDim.x + blockIdx.x) * NW + wave] = bf16_round(mo);
   }
 }
-
-// Buffer-load DMA of 16-byte chunks straight into LDS (no registers): lane l of one
-// instruction writes LDS bytes M0 + 16 l .. + 15.  Written in assembly (as in the GEMM)
-// so that the compiler does not wait for every DMA before each LDS read; the waits are
-// explicit (dma_wait_sync).
-typedef unsigned int u32x4w_t __attribute__((ext_vector_type(4)));
-__device__ inline u32x4w_t rows_words(const bf16_t* base, long ld, int row0, int T, int HD) {
-  const uint32_t bytes = row0 < T ? (uint32_t)(((long)(T - row0 - 1) * ld + HD) * 2) : 0u;
-  const uintptr_t a = (uintptr_t)(base + (long)row0 * ld);
-  u32x4w_t r;
-  r.x = (uint32_t)a;
-  r.y = (uint32_t)(a >> 32) & 0xFFFFu;
-  r.z = bytes;
-  r.w = 0x00020000u;
-  return r;
-}
-__device__ inline void attn_dma16(const u32x4w_t& rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-// every DMA of this wave landed (vmcnt 0) and its LDS reads done, then a workgroup barrier
-__device__ inline void dma_wait_sync() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (0 << 8));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// K and V tiles [64 rows][128] (Tile<128> layout) by DMA from NT threads: instruction j
-// of thread tid fills LDS chunk p = j NT + tid, i.e. row p / 16 and physical chunk p % 16,
-// which holds logical chunk (p % 16) ^ swz(row).  Rows at or past T read zeros (the
-// descriptor ends at the sequence's last row).
-template <int NT>
-struct DmaTilePair {
-  static constexpr int PER = 64 * 16 / NT;
-  uint32_t voff[PER];
-  __device__ inline void init(long ld, int tid) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int pch = j * NT + tid, row = pch >> 4, c = (pch & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
-      voff[j] = (uint32_t)(((long)row * ld + c * 8) * 2);
-    }
-  }
-  __device__ inline void issue(const u32x4w_t& rk, const u32x4w_t& rv, const bf16_t* ks, const bf16_t* vs, int wave) {
-    const uint32_t kl = (uint32_t)(uintptr_t)ks, vl = (uint32_t)(uintptr_t)vs;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      attn_dma16(rk, kl + (j * NT + wave * 64) * 16, voff[j]);
-      attn_dma16(rv, vl + (j * NT + wave * 64) * 16, voff[j]);
-    }
-  }
-};
 
 // Forward with 64 queries per wave (two 32-query column blocks): every K and V
 // fragment read from LDS feeds two MFMAs, half the LDS traffic per flop of the 32-query
@@ -685,15 +703,30 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
   const int kv_end = min(T, (qb + 1) * BQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
   const int it0 = max(0, qb * BQ - Wn + 1) / BKV;  // first tile any query of the block sees
-  PairStager<HD, 256> stg;
-  stg.init(ld, ld, tid);
-  stg.load(rows_rsrc(K, ld, it0 * BKV, T, HD), rows_rsrc(V, ld, it0 * BKV, T, HD), tid);
-  stg.store(Ks[0], Vs[0], tid);
-  __syncthreads();
+  // K/V tiles: head_dim 128 by buffer-load DMA straight into LDS (no registers held
+  // across the tile), other sizes through registers
+  PairStager<HD == 128 ? 8 : HD, 256> stg;  // unused for head_dim 128
+  DmaTilePair<256> dma;
+  if constexpr (HD == 128) {
+    dma.init(ld, tid);
+    dma.issue(rows_words(K, ld, it0 * BKV, T, HD), rows_words(V, ld, it0 * BKV, T, HD), Ks[0], Vs[0], wave);
+    dma_wait_sync();
+  } else {
+    stg.init(ld, ld, tid);
+    stg.load(rows_rsrc(K, ld, it0 * BKV, T, HD), rows_rsrc(V, ld, it0 * BKV, T, HD), tid);
+    stg.store(Ks[0], Vs[0], tid);
+    __syncthreads();
+  }
   auto body = [&](auto cur_c, int it) {
     constexpr int cur = decltype(cur_c)::value;
     const int k0 = it * BKV;
-    if (it + 1 < nkv) stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
+    if (it + 1 < nkv) {  // the other buffer was last read in the previous tile, before its barrier
+      if constexpr (HD == 128)
+        dma.issue(rows_words(K, ld, k0 + BKV, T, HD), rows_words(V, ld, k0 + BKV, T, HD), Ks[cur ^ 1], Vs[cur ^ 1],
+                  wave);
+      else
+        stg.load(rows_rsrc(K, ld, k0 + BKV, T, HD), rows_rsrc(V, ld, k0 + BKV, T, HD), tid);
+    }
     if (k0 <= q0 + 31 && k0 + BKV - 1 >= q0 - Wn + 1 && q0 < T) {
       const bool mask = k0 + BKV - 1 > q0 || k0 + BKV > T || k0 <= q0 + 31 - Wn;
 #pragma unroll
@@ -727,8 +760,12 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
         }
       }
     }
-    if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
-    __syncthreads();
+    if constexpr (HD == 128) {
+      dma_wait_sync();
+    } else {
+      if (it + 1 < nkv) stg.store(Ks[cur ^ 1], Vs[cur ^ 1], tid);
+      __syncthreads();
+    }
   };
   for (int it = it0; it < nkv; it += 2) {
     body(std::integral_constant<int, 0>{}, it);
