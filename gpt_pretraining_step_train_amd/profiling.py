@@ -75,7 +75,7 @@ def stats_table(trace_dir: str, steps: int, command: str, top: int = 24) -> str:
 # the first kernel of every gpt_step (the token-embedding gather) and its one-per-step
 # kernel (the fused cross-entropy): the model's set-up kernels run before the first
 STEP_FIRST = "embed_gather"
-STEP_MARK = "ce_kernel"
+STEP_MARK = re.compile(r"::ce_(generic_)?kernel<")  # the cross-entropy kernel, once per step
 
 
 def step_table(trace_dir: str, command: str, top: int = 28) -> str:
@@ -86,7 +86,7 @@ def step_table(trace_dir: str, command: str, top: int = 28) -> str:
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     first = next(i for i, r in enumerate(rows) if STEP_FIRST in r["Kernel_Name"])
     rows = rows[first:]
-    steps = sum(1 for r in rows if STEP_MARK in r["Kernel_Name"])
+    steps = sum(1 for r in rows if STEP_MARK.search(r["Kernel_Name"]))
     agg = {}
     for r in rows:
         n = _short(r["Kernel_Name"])
