@@ -124,6 +124,12 @@ size_t wgrad_ws_bytes(const gpt_cfg& c) {
     const int sp = gemm_auto_splits(p);
     if (sp > 1) best = std::max(best, (size_t)sp * s[0] * s[1] * 4);
   }
+  if (V >= 8192) {  // the LM head's data gradient (dr = dz U, reduction over the vocabulary)
+    GemmArgs p;
+    p.M = N; p.N = d; p.K = V; p.dtype = act_of(c); p.b_kmaj = false;
+    const int sp = gemm_auto_splits(p);
+    if (sp > 1) best = std::max(best, (size_t)sp * N * d * 4);
+  }
   return best;
 }
 
@@ -746,7 +752,10 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
     pd.A = dY; pd.lda = ldy;
     pd.B = w == 4 * M->cfg.depth ? M->uact() : M->wact(wi.off); pd.ldb = kin; pd.b_kmaj = false;
   }
-  return run_gemm(M, pd, st, false);
+  // split-K where the reduction is long (the LM head's, over the vocabulary): at d = 768 its
+  // 384 output tiles are 1.5 rounds of 256 workgroups, two splits make them 3 rounds of half
+  // the length.  Short reductions never gain enough to pay for the extra reduction launch.
+  return run_gemm(M, pd, st, pd.K >= 8192);
 }
 
 static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
