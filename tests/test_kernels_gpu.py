@@ -211,6 +211,37 @@ def test_gemm_d24_weight_gradients_with_the_steps_split(nout, kin):
     assert err.max() < 1e-5
 
 
+@pytest.mark.parametrize("d", [768, 1664])
+def test_gemm_lm_head_data_gradient_with_the_steps_split(d):
+    """dr = dz U of the LM head at the full step size (32768 tokens, vocabulary 32768,
+    d = 768 as in d12 and 1664 as in d26): dz token-major (K-major), U [V][d] read
+    transposed, with the launcher's own split-K factor (gpt_step lets this long-reduction
+    data gradient split).  Sampled outputs recomputed one by one in fp64."""
+    M, N, K = 32768, d, 32768
+    splits = B.gemm_auto_splits(B.GPT_BF16, M, N, K, 1, 1, 0)
+    say(f"  LM-head data gradient {M}x{N}x{K}: {splits} splits")
+    assert splits > 1  # the 1.5- and 3.5-round tilings are the ones the split is for
+    g = torch.Generator(device="cuda").manual_seed(d)
+    dz = (torch.randn(M, K, device="cuda", generator=g) * 1e-3).bfloat16()
+    U = torch.randn(K, N, device="cuda", generator=g).bfloat16()
+    C = torch.empty(M, N, device="cuda")
+    ws = torch.empty(splits * M * N, device="cuda")
+    B.gemm(B.GPT_BF16, 1, 0, M, N, K, dz, K, U, N, C, N, splits=-1, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(d)
+    rows = rng.integers(0, M, 512)
+    cols = rng.integers(0, N, 512)
+    rows[:4], cols[:4] = [0, M - 1, 0, M - 1], [0, N - 1, N - 1, 0]
+    a = dz[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    b = U[:, torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64).T
+    ref = np.sum(a * b, axis=1)
+    scale = np.sum(np.abs(a * b), axis=1)
+    got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    err = np.abs(got - ref) / scale
+    say(f"    max |err| / sum|a b| = {err.max():.2e}")
+    assert err.max() < 1e-5
+
+
 # ----------------------------------------------------------------------------- attention
 
 
