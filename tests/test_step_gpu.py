@@ -353,8 +353,9 @@ def test_second_muon_step_uses_momentum():
 @pytest.mark.parametrize("i", [1, 5])
 def test_muon_momentum_at_d24_width(i):
     """Two Muon steps on Gaussian gradients for the d24 Wq [1536 x 1536] and W1
-    [6144 x 1536] (the default split-precision Newton-Schulz schedule), against the
-    oracle's heavy-ball momentum and NS; the plain-bf16 iterations are the error."""
+    [6144 x 1536] (the default Newton-Schulz schedule: fp16 operands on MFMA with fp32
+    accumulation, X carried in fp32), against the oracle's heavy-ball momentum and NS;
+    the fp16 rounding of the products' operands is the error."""
     cfg = configs.get("d24", batch=1, depth=1, seq_len=256)
     model = binding.Model(cfg, seed=0)
     table, _ = PE.coefficients()
