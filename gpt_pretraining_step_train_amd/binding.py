@@ -82,6 +82,7 @@ _SIGS = {
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_variant": (_I, [_I, _I]),
     "gptk_fp8_fused_amax": (_I, [_I]),
+    "gptk_side_stream": (_I, [_I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -372,6 +373,11 @@ def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
 
 def attn_variant(pass_, variant):
     check(lib().gptk_attn_variant(pass_, variant), "gptk_attn_variant")
+
+
+def side_stream(on: int = -1) -> int:
+    """gptk_side_stream: set (0/1) or query (-1); returns the previous setting."""
+    return lib().gptk_side_stream(int(on))
 
 
 def fp8_fused_amax(on: int = -1) -> int:

@@ -100,6 +100,8 @@ inline size_t kQuantSlots(const gpt_cfg& c) { return 16 * (size_t)c.depth + 8; }
 // process-wide: fp8 steps take the amax of their quantised activations and gradients from
 // the producing kernels (gptk_fp8_fused_amax)
 static int g_fp8_fused_amax = 1;
+// backward weight gradients on the model's side stream (gptk_side_stream)
+static int g_side_stream = 1;
 // capacity (floats) for the per-wave amax partials the producers of a quantised tensor
 // write: the loss gradient's 4 per row, the dV and RoPE waves of dqkv, the fc / dReLU2
 // GEMMs' 8 per tile (a producer that would need more falls back to the amax pass)
@@ -322,6 +324,15 @@ struct gpt_model {
   // matrix in the stacked per-row NorMuon vectors (6L + 1 entries)
   std::vector<long> moff, msize, nm_roff;
   std::vector<MuonVecJob> mv_jobs;  // batched normalise / apply jobs (uploaded by gpt_init)
+  // A second stream for the backward's weight-gradient products (dW = dY^T X): each
+  // only has to finish before its dY buffer is overwritten and before the step ends, so
+  // it runs beside the data-gradient chain and fills that chain's idle CUs (launch
+  // tails, bandwidth-bound kernels).  Events order the two streams: fork (the main stream
+  // has produced dY), one per dY buffer (its last reader on the side stream) and join.
+  hipStream_t side = nullptr;
+  hipEvent_t sev_fork = nullptr, sev_join = nullptr, sev_rd[3] = {};
+  bool sev_pending[3] = {};
+  bool use_side = false;  // this step puts weight gradients on the side stream
   // profiling
   std::string prof_name;
   std::vector<hipEvent_t> ev;
@@ -527,6 +538,12 @@ static void refresh_act(gpt_model* M, hipStream_t st) {
   launch_cast_f32_to_act(M->params() + M->nE + M->nBlk, M->uact(), M->at, M->nU, st);
 }
 
+static void free_side(gpt_model* M) {
+  for (hipEvent_t* e : {&M->sev_fork, &M->sev_join, &M->sev_rd[0], &M->sev_rd[1], &M->sev_rd[2]})
+    if (*e) { (void)hipEventDestroy(*e); *e = nullptr; }
+  if (M->side) { (void)hipStreamDestroy(M->side); M->side = nullptr; }
+}
+
 int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes, void* stream, gpt_model** out) {
   if (!out) return GPT_ERR_ARG;
   *out = nullptr;
@@ -624,6 +641,15 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
     delete M;
     return GPT_ERR_HIP;
   }
+  // the side stream (default priority) and its events; without them every product stays on
+  // the caller's stream
+  bool side_ok = hipStreamCreateWithFlags(&M->side, hipStreamNonBlocking) == hipSuccess;
+  for (hipEvent_t* e : {&M->sev_fork, &M->sev_join, &M->sev_rd[0], &M->sev_rd[1], &M->sev_rd[2]})
+    side_ok = side_ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+  if (!side_ok) {
+    (void)hipGetLastError();
+    free_side(M);
+  }
   *out = M;
   return GPT_OK;
 }
@@ -631,6 +657,7 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
 void gpt_free(gpt_model* M) {
   if (!M) return;
   for (auto e : M->ev) (void)hipEventDestroy(e);
+  free_side(M);
   delete M;
 }
 
@@ -712,10 +739,23 @@ static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st, int xslot = 
   return run_gemm(M, p, st, false);
 }
 
+// dY buffers of the backward that weight-gradient products on the side stream read
+enum { RD_DH = 0, RD_DBIG = 1, RD_DQKV = 2 };
+
+// the main stream waits for the side stream's last reader of dY buffer rd (before it
+// overwrites that buffer)
+static int side_wait(gpt_model* M, int rd, hipStream_t st) {
+  if (rd < 0 || !M->sev_pending[rd]) return GPT_OK;
+  M->sev_pending[rd] = false;
+  return hipStreamWaitEvent(st, M->sev_rd[rd], 0) == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
 // backward of Y = X W^T: dW = dY^T X into dW (ld = cols of W) and dX = dY W with the
-// epilogue in pd (M = tokens, N = cols of W, K = rows of W, outputs set by the caller)
+// epilogue in pd (M = tokens, N = cols of W, K = rows of W, outputs set by the caller).
+// rd >= 0: dY is that buffer and dW goes to the side stream (when the step uses it); wr >= 0:
+// dX overwrites that buffer, so the side stream's last reader of it must be done first
 static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long ldx, int w, float* dW, GemmArgs pd,
-                   hipStream_t st, int yslot = -1) {
+                   hipStream_t st, int yslot = -1, int rd = -1, int wr = -1) {
   const WInfo wi = winfo(M, w);
   const int N = M->N, nout = wi.rows, kin = wi.cols;
   int rc;
@@ -743,7 +783,16 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
     pw.A = dY; pw.lda = ldy; pw.a_kmaj = false;
     pw.B = X; pw.ldb = ldx; pw.b_kmaj = false;
   }
-  if ((rc = run_gemm(M, pw, st, true))) return rc;
+  if (rd >= 0 && M->use_side) {  // dY and X are ready on the main stream
+    if (hipEventRecord(M->sev_fork, st) != hipSuccess || hipStreamWaitEvent(M->side, M->sev_fork, 0) != hipSuccess)
+      return GPT_ERR_HIP;
+    if ((rc = run_gemm(M, pw, M->side, true))) return rc;
+    if (hipEventRecord(M->sev_rd[rd], M->side) != hipSuccess) return GPT_ERR_HIP;
+    M->sev_pending[rd] = true;
+  } else if ((rc = run_gemm(M, pw, st, true))) {
+    return rc;
+  }
+  if ((rc = side_wait(M, wr, st))) return rc;
   if (f8d) {
     pd.A = q8a; pd.lda = nout;
     pd.B = M->at_off<uint8_t>(M->off.wtq8) + wi.off; pd.ldb = nout;
@@ -758,7 +807,8 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
   return run_gemm(M, pd, st, pd.K >= 8192);
 }
 
-static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
+static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale,
+                               hipStream_t st) {
   const gpt_cfg& c = M->cfg;
   const int N = M->N, d = c.d_model, F = c.d_ff, V = c.vocab, L = c.depth, H = c.n_head, hd = c.head_dim;
   const int Hkv = kv_heads(c), QD = (int)qkv_dim(c);  // key/value heads, fused QKV width
@@ -955,7 +1005,7 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       pd.epi = EPI_DRELU2; pd.aux = g; pd.outA = dbig; pd.ldoa = F;
       pd.amax_part = fpart;
       M->gemm_parts = 0;
-      if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st, sdh))) return rc;
+      if ((rc = lin_bwd(M, dh_act, d, g, F, 4 * l + 3, gblk + wl + M->lo.w2, pd, st, sdh, RD_DH, RD_DBIG))) return rc;
     }
     const int su = fold(M->gemm_parts);
     cap(l, CAP_DU, dbig);
@@ -963,9 +1013,10 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       GemmArgs pd;  // dW1 = du^T m ; dm = du W1
       pd.M = N; pd.N = d; pd.K = F;
       pd.outF = dtmp; pd.ldo = d;
-      if ((rc = lin_bwd(M, dbig, F, m, d, 4 * l + 2, gblk + wl + M->lo.w1, pd, st, su))) return rc;
+      if ((rc = lin_bwd(M, dbig, F, m, d, 4 * l + 2, gblk + wl + M->lo.w1, pd, st, su, RD_DBIG))) return rc;
     }
     cap(l, CAP_DM, dtmp);
+    if ((rc = side_wait(M, RD_DH, st))) return rc;  // dh_act is rewritten here
     const int sdo = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur],
                                             dh[cur ^ 1], dh_act, at, N, d, eps, st, fpart, fcap));
     cur ^= 1;
@@ -974,10 +1025,11 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       GemmArgs pd;  // dWo = dY^T o ; do = dY Wo
       pd.M = N; pd.N = d; pd.K = d;
       pd.outA = do_act; pd.ldoa = d;
-      if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st, sdo))) return rc;
+      if ((rc = lin_bwd(M, dh_act, d, o, d, 4 * l + 1, gblk + wl + M->lo.o, pd, st, sdo, RD_DH))) return rc;
     }
     cap(l, CAP_DO, do_act);
     // dqkv's partials: the dV waves first, then the RoPE backward's (dQ, dK)
+    if ((rc = side_wait(M, RD_DQKV, st))) return rc;  // dqkv is rewritten here
     const int nq1 = launch_attn_bwd(qkv, o, do_act, lse, M->at_off<float>(O.Dbuf), dqkv, at, B, T, H, Hkv, hd,
                                     c.attn_window, st, fpart, fcap);
     if (ex_ve)  // dVE rows, the gate's dz and the rows of d(gate weights), from dv
@@ -991,9 +1043,10 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
       GemmArgs pd;  // dWqkv = dqkv^T a ; da = dqkv Wqkv
       pd.M = N; pd.N = d; pd.K = QD;
       pd.outF = dtmp; pd.ldo = d;
-      if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st, sq))) return rc;
+      if ((rc = lin_bwd(M, dqkv, QD, a, d, 4 * l + 0, gblk + wl + M->lo.q, pd, st, sq, RD_DQKV))) return rc;
     }
     cap(l, CAP_DA, dtmp);
+    if ((rc = side_wait(M, RD_DH, st))) return rc;  // the layer's input gradient rewrites dh_act below
     if (ex_ve) {  // the gate's path into the block input; the table's and gates' gradients
       launch_ve_da(dtmp, M->at_off<float>(O.vdz), ve_gate(M->params(), l), N, Hkv, d, st);
       launch_embed_scatter_sorted(tok, M->at_off<float>(O.dve), ve_tab(grads, l), N, V, (int)kvd, M->base + O.embws,
@@ -1030,6 +1083,21 @@ static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt
   if (c.extras)
     launch_extras_reduce(xpart, N, L, c.extras, grads + M->nE + M->nBlk + M->nU, M->acc_grads, st);
   return cap_failed ? GPT_ERR_HIP : GPT_OK;
+}
+
+// one forward + backward on stream st; the side stream (weight gradients) joins st before
+// this returns, on every path
+static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
+  // fp8 steps share quantised-operand scratch between the two products of a Linear
+  M->use_side = g_side_stream && M->side && !M->fp8;
+  for (bool& b : M->sev_pending) b = false;
+  int rc = forward_backward_on(M, tok, tgt, grad_scale, st);
+  if (M->use_side) {
+    if (hipEventRecord(M->sev_join, M->side) != hipSuccess || hipStreamWaitEvent(st, M->sev_join, 0) != hipSuccess)
+      rc = rc ? rc : GPT_ERR_HIP;
+    for (bool& b : M->sev_pending) b = false;
+  }
+  return rc;
 }
 
 float gpt_step(gpt_model* M, const int32_t* tok, const int32_t* tgt, const gpt_cfg* cfg, void* stream) {
@@ -1550,6 +1618,12 @@ static int attn_ok(int dtype, int hd) {
 
 // key/value heads: 1 <= Hkv <= H with H % Hkv == 0 (any Hkv when H = 0)
 static bool kv_heads_ok(int H, int Hkv) { return H == 0 ? Hkv >= 0 : (Hkv >= 1 && Hkv <= H && H % Hkv == 0); }
+
+int gptk_side_stream(int on) {
+  const int prev = g_side_stream;
+  if (on >= 0) g_side_stream = on ? 1 : 0;
+  return prev;
+}
 
 int gptk_fp8_fused_amax(int on) {
   const int prev = g_fp8_fused_amax;

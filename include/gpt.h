@@ -353,6 +353,18 @@ int gptk_attn_variant(int pass, int variant);
  * previous setting.  Not thread-safe against concurrent steps. */
 int gptk_fp8_fused_amax(int on);
 
+/* Where the backward's weight-gradient products run (P1, "2. Muon Optimize Edici": the
+ * gradients of one step feed one optimizer update, so each dW = dY^T X only has to exist
+ * by the end of the step).  on = 1 (the default): on a second stream the model owns, beside
+ * the data-gradient chain, with events so that each dY buffer is rewritten only after its
+ * weight-gradient product has read it and the caller's stream waits for all of them before
+ * gpt_step returns (or, for gpt_step_async, before any later work on that stream); the LM
+ * head's and fp8 steps' products stay on the caller's stream.  on = 0: every product on the
+ * caller's stream.  Both give the same results bit for bit (each product is computed the
+ * same way, only its start time moves).  on < 0 only queries.  Returns the previous
+ * setting.  Process-wide, not thread-safe against concurrent steps. */
+int gptk_side_stream(int on);
+
 /* backward: dqkv act [B*T][(H + 2*Hkv)*hd] from qkv, o, dO act [B*T][H*hd] and lse,
  * with the forward's Hkv and window (dK and dV of a shared head sum over its query
  * heads); D is fp32 scratch [B][H][T] (receives rowsum(dO*O)). */

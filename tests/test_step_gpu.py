@@ -488,3 +488,52 @@ def test_fp8_fused_amax_is_bit_identical(name, over):
     for a, b in zip(fused[2], sep[2]):
         np.testing.assert_array_equal(a, b)
     say(f"  {name} {over}: losses {fused[0][0]:.6f}, {fused[1][0]:.6f}; fused and separate amax bit-identical")
+
+
+def _bf16_steps(cfg, params, batches):
+    """Two steps with a Muon update between them; the second accumulates a half-scaled
+    micro-batch onto the first's gradients before the update is taken again."""
+    model = binding.Model(cfg, seed=0)
+    model.set_all_params(params)
+    out = []
+    for s, (tk, tg) in enumerate(batches):
+        loss = model.step(_dev(tk), _dev(tg))
+        if s == 1:
+            loss = (loss, model.step(_dev(tg), _dev(tk), accumulate=True, grad_scale=0.5))
+        torch.cuda.synchronize()
+        out.append((loss, model.row_loss().cpu().numpy(), [model.grads(i) for i in range(len(params))]))
+        model.muon_update(LR)
+    out.append([model.get_params(i) for i in range(len(params))])
+    del model
+    return out
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {"batch": 8}),
+                                       ("d12", {"batch": 2, "depth": 2}),
+                                       ("laptop", {"batch": 8, "extras": 31, "n_kv_head": 1, "attn_window": 100})],
+                         ids=["tiny", "laptop", "d12_L2", "laptop_extras_mqa_window"])
+def test_side_stream_is_bit_identical(name, over):
+    """The backward's weight-gradient products run on a second stream beside the
+    data-gradient chain (each dY buffer rewritten only after its product has read it).
+    Every product is computed exactly as on one stream, so two steps (the second with an
+    accumulated micro-batch) and the Muon updates after them must be bit-identical
+    with the side stream on and off."""
+    cfg = configs.get(name, **over)
+    params = random_extras(inputs.init_weights(cfg, 0), cfg, 0)
+    batches = [inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=s)
+               for s in range(2)]
+    prev = binding.side_stream(1)
+    try:
+        two = _bf16_steps(cfg, params, batches)
+        binding.side_stream(0)
+        one = _bf16_steps(cfg, params, batches)
+    finally:
+        binding.side_stream(prev)
+    for s in range(2):
+        assert two[s][0] == one[s][0]
+        np.testing.assert_array_equal(two[s][1], one[s][1])
+        for a, b in zip(two[s][2], one[s][2]):
+            np.testing.assert_array_equal(a, b)
+    for a, b in zip(two[2], one[2]):
+        np.testing.assert_array_equal(a, b)
+    say(f"  {name} {over}: losses {two[0][0]}, {two[1][0]}; one and two streams bit-identical")
