@@ -81,6 +81,7 @@ _SIGS = {
     "gptk_gemm_fp8": (_I, [_I, _I, _I, _P, _L, _P, _L, _P, _P, _P, _L, _I, _P, _SZ, _P]),
     "gpt_gemm_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I, _I]),
     "gptk_attn_variant": (_I, [_I, _I]),
+    "gptk_ce_variant": (_I, [_I]),
     "gptk_fp8_fused_amax": (_I, [_I]),
     "gptk_side_stream": (_I, [_I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -373,6 +374,10 @@ def gemm_kernel_name(dtype, M, N, K, batch=1, a_kmaj=1, b_kmaj=1) -> str:
 
 def attn_variant(pass_, variant):
     check(lib().gptk_attn_variant(pass_, variant), "gptk_attn_variant")
+
+
+def ce_variant(variant):
+    check(lib().gptk_ce_variant(variant), "gptk_ce_variant")
 
 
 def side_stream(on: int = -1) -> int:

@@ -850,6 +850,89 @@ __global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ z, co
   if (bad) atomicOr(err, 2);
 }
 
+// V a multiple of 4096: two passes over the row with few registers, so that two rows
+// share a CU and one row's reductions and stores overlap the other's loads (the
+// register-resident ce_kernel holds a whole row per CU at 256 VGPRs, one wave per SIMD,
+// and its load, reduce and store phases leave HBM idle in turn).  Pass 1 streams the row
+// in groups of CE_G float4 per thread with an online maximum and sum of exponentials
+// (the per-thread sum is rescaled when a group raises the maximum), and the lowest-index
+// argmax; the per-thread sums are combined at the row maximum.  Pass 2 re-reads the row,
+// which the first pass has just brought into the caches (the launch reserves LDS so that
+// at most two rows are in flight per CU), and writes dz.
+constexpr int CE_G = 16;
+constexpr int CE_LDS_RESERVE = 56 * 1024;  // three would exceed the CU's 160 KB
+template <typename T>
+__global__ void __launch_bounds__(256) ce_stream_kernel(const float* __restrict__ z, const int32_t* __restrict__ tgt,
+                                                        T* __restrict__ dz, float* __restrict__ row_loss,
+                                                        int32_t* __restrict__ amax, int V, float inv_n, int* err,
+                                                        float* __restrict__ dz_part) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const long n = blockIdx.x;
+  const float4* zr = reinterpret_cast<const float4*>(z + n * V);
+  const int ng = V / (1024 * CE_G);  // groups per thread
+  float mx = -INFINITY, ts = 0.f;    // running maximum and sum of exp(x - mx) of the thread
+  int mi = 0x7fffffff;
+  bool bad = false;
+  for (int gi = 0; gi < ng; ++gi) {
+    float4 v[CE_G];
+#pragma unroll
+    for (int c = 0; c < CE_G; ++c) v[c] = zr[threadIdx.x + (gi * CE_G + c) * 256];
+    float gm = mx;
+#pragma unroll
+    for (int c = 0; c < CE_G; ++c) {
+      const int i4 = threadIdx.x + (gi * CE_G + c) * 256;
+      const float e[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bad |= !isfinite(e[k]);
+        if (e[k] > gm) { gm = e[k]; mi = 4 * i4 + k; }
+      }
+    }
+    if (gm > mx) { ts *= __expf(mx - gm); mx = gm; }  // exp(-inf) = 0 before the first group
+#pragma unroll
+    for (int c = 0; c < CE_G; ++c)
+      ts += (__expf(v[c].x - mx) + __expf(v[c].y - mx)) + (__expf(v[c].z - mx) + __expf(v[c].w - mx));
+  }
+  float rm = mx;
+  int ri = mi;
+  blk_argmax(rm, ri, sv, si);
+  const float s = blk_sum(ts * __expf(mx - rm), sv);
+  const int y = tgt[n];
+  const bool yok = (y >= 0 && y < V);
+  const float sc = (1.f / s) * inv_n;
+  T* dr = dz + n * V;
+  float mp = 0.f;
+  for (int gi = 0; gi < ng; ++gi) {
+    float4 v[CE_G];
+#pragma unroll
+    for (int c = 0; c < CE_G; ++c) v[c] = zr[threadIdx.x + (gi * CE_G + c) * 256];
+#pragma unroll
+    for (int c = 0; c < CE_G; ++c) {
+      const int i4 = threadIdx.x + (gi * CE_G + c) * 256;
+      float4 p = make_float4(__expf(v[c].x - rm) * sc, __expf(v[c].y - rm) * sc, __expf(v[c].z - rm) * sc,
+                             __expf(v[c].w - rm) * sc);
+      if (yok && (y >> 2) == i4) {
+        const int k = y & 3;
+        if (k == 0) p.x -= inv_n; else if (k == 1) p.y -= inv_n; else if (k == 2) p.z -= inv_n; else p.w -= inv_n;
+      }
+      st4<T>(dr + 4 * i4, p);
+      mp = fmaxf(mp, max4abs(p));
+    }
+  }
+  if (dz_part) {
+    mp = wave_max(mp);
+    if ((threadIdx.x & 63) == 0) dz_part[n * 4 + (threadIdx.x >> 6)] = round_act<T>(mp);
+  }
+  if (threadIdx.x == 0) {
+    const float zy = yok ? z[n * V + y] : 0.f;
+    row_loss[n] = (rm + logf(s)) - zy;
+    amax[n] = ri;
+    if (!yok) atomicOr(err, 1);
+  }
+  if (bad) atomicOr(err, 2);
+}
+
 // any V: three passes over the row from memory
 template <typename T>
 __global__ void __launch_bounds__(256) ce_generic_kernel(const float* __restrict__ z, const int32_t* __restrict__ tgt,
@@ -1763,10 +1846,19 @@ void launch_colsum(const float* part, int N, int R, void* ws, float* out, bool a
                      (int)accumulate);
 }
 
+// cross-entropy kernel for V a multiple of 16384: 0 = two-pass streaming (ce_stream_kernel),
+// 1 = the row held in registers (ce_kernel); both give the same argmax and, up to the
+// order of the exponential sums, the same loss and dz
+int g_ce_variant = 0;
+
 template <typename T>
 static void ce_dispatch(const float* z, const int32_t* tgt, T* dz, float* rl, int32_t* am, int N, int V, float inv_n,
                         int* err, hipStream_t st, float* pt) {
   dim3 g(N), b(256);
+  if (g_ce_variant == 0 && V % (1024 * CE_G) == 0) {
+    hipLaunchKernelGGL(ce_stream_kernel<T>, g, b, CE_LDS_RESERVE, st, z, tgt, dz, rl, am, V, inv_n, err, pt);
+    return;
+  }
   switch (V % 1024 == 0 ? V / 1024 : -1) {
     case 1: hipLaunchKernelGGL((ce_kernel<T, 1>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
     case 2: hipLaunchKernelGGL((ce_kernel<T, 2>), g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
@@ -1777,6 +1869,8 @@ static void ce_dispatch(const float* z, const int32_t* tgt, T* dz, float* rl, in
     default: hipLaunchKernelGGL(ce_generic_kernel<T>, g, b, 0, st, z, tgt, dz, rl, am, V, inv_n, err, pt); break;
   }
 }
+
+void set_ce_variant(int v) { g_ce_variant = v; }
 
 int launch_cross_entropy(const float* z, const int32_t* tgt, void* dz, int at, float* rl, int32_t* am, int N, int V,
                          float inv_n, int* err, hipStream_t st, float* dz_part, long part_cap) {

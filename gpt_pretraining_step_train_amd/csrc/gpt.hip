@@ -1619,6 +1619,12 @@ static int attn_ok(int dtype, int hd) {
 // key/value heads: 1 <= Hkv <= H with H % Hkv == 0 (any Hkv when H = 0)
 static bool kv_heads_ok(int H, int Hkv) { return H == 0 ? Hkv >= 0 : (Hkv >= 1 && Hkv <= H && H % Hkv == 0); }
 
+int gptk_ce_variant(int variant) {
+  if (variant < 0 || variant > 1) return GPT_ERR_ARG;
+  set_ce_variant(variant);
+  return GPT_OK;
+}
+
 int gptk_side_stream(int on) {
   const int prev = g_side_stream;
   if (on >= 0) g_side_stream = on ? 1 : 0;

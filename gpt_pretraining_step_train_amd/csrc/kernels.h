@@ -194,6 +194,7 @@ void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, 
 // process-wide choice of the bf16 hd-128 attention kernels (see gptk_attn_variant)
 void set_attn_fwd_variant(int v);
 void set_attn_bwd_variant(int v);
+void set_ce_variant(int v);
 int launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int Hkv, int hd,
                     int window, hipStream_t st, float* amax_part = nullptr, long amax_cap = 0);  // partials of o
 int launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,

@@ -341,6 +341,15 @@ int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T,
  * Not thread-safe against concurrent launches. */
 int gptk_attn_variant(int pass, int variant);
 
+/* Which cross-entropy kernel later steps and gptk_ce take when V is a multiple of 16384
+ * (P1, "1. GPT Modeli": the loss over the 32,768-entry vocabulary).  variant 0 (the
+ * default) = two passes over each row with few registers, two rows in flight per CU;
+ * 1 = the row held in registers, one row per CU.  Both give the same argmax (lowest index
+ * among equal maxima) and, up to the order of the exponential sums, the same loss and
+ * gradient.  GPT_ERR_ARG for another variant.  Process-wide, not thread-safe against
+ * concurrent launches. */
+int gptk_ce_variant(int variant);
+
 /* Process-wide choice of where fp8 steps take the per-tensor amax of the activations and
  * output gradients they quantise ("3. Hassasiyet Yönetimi", the --fp8 recipe: per-tensor
  * scales from the current max|x|): on = 1 (the default), the kernels that produce each

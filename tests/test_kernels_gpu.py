@@ -467,14 +467,19 @@ def test_rope_qknorm_fwd_bwd(dtype, Bn, T, H, hd, Hkv):
 # ----------------------------------------------------------------------------- cross-entropy
 
 
-@pytest.mark.parametrize("dtype,N,V", [("bf16", 40, 4096), ("fp32", 33, 4096), ("bf16", 9, 32768),
-                                       ("fp32", 7, 1000)])
-def test_cross_entropy_and_argmax(dtype, N, V):
+# variant 0 takes the two-pass streaming kernel for V a multiple of 16384 (one or more
+# groups of 16 float4 per thread; a later group raising the maximum rescales the sum),
+# variant 1 the register-resident kernel
+@pytest.mark.parametrize("dtype,N,V,variant", [("bf16", 40, 4096, 0), ("fp32", 33, 4096, 0), ("bf16", 9, 32768, 0),
+                                               ("bf16", 9, 32768, 1), ("fp32", 9, 16384, 0), ("fp32", 9, 65536, 0),
+                                               ("fp32", 7, 1000, 0)])
+def test_cross_entropy_and_argmax(dtype, N, V, variant):
     rng = np.random.default_rng(V + N)
     z = (rng.standard_normal((N, V)) * 3).astype(np.float32)
     z[0, :] = 1.25                       # all tied -> index 0
     z[1, [7, 300, 901]] = 50.0           # tie among three -> 7
     z[2, V - 1] = 60.0                   # max at the last index
+    z[6, [V // 2 + 5, V - 3]] = 40.0     # tie across the halves of the row -> the first
     y = rng.integers(0, V, N).astype(np.int32)
     y[3] = V - 1
     per_ref = O.loss_from_logits(z.astype(np.float64), y)[1]
@@ -485,7 +490,11 @@ def test_cross_entropy_and_argmax(dtype, N, V):
     rl = torch.empty(N, device="cuda")
     am = torch.empty(N, device="cuda", dtype=torch.int32)
     err = torch.zeros(4, device="cuda", dtype=torch.int32)
-    B.cross_entropy(DT[dtype], tz, ty, dz, rl, am, N, V, 1.0 / N, err)
+    B.ce_variant(variant)
+    try:
+        B.cross_entropy(DT[dtype], tz, ty, dz, rl, am, N, V, 1.0 / N, err)
+    finally:
+        B.ce_variant(0)
     torch.cuda.synchronize()
     assert err.cpu().numpy()[0] == 0
     np.testing.assert_array_equal(am.cpu().numpy(), am_ref)
