@@ -381,7 +381,8 @@ def ce_variant(variant):
 
 
 def side_stream(on: int = -1) -> int:
-    """gptk_side_stream: set (0/1) or query (-1); returns the previous setting."""
+    """gptk_side_stream: set (0 never, 1 where it fills idle CUs, 2 always) or query (-1);
+    returns the previous setting."""
     return lib().gptk_side_stream(int(on))
 
 

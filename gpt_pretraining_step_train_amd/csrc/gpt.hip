@@ -100,7 +100,8 @@ inline size_t kQuantSlots(const gpt_cfg& c) { return 16 * (size_t)c.depth + 8; }
 // process-wide: fp8 steps take the amax of their quantised activations and gradients from
 // the producing kernels (gptk_fp8_fused_amax)
 static int g_fp8_fused_amax = 1;
-// backward weight gradients on the model's side stream (gptk_side_stream)
+// backward weight gradients on the model's side stream (gptk_side_stream): 0 never, 1 where
+// the model's data-gradient launches leave part of a round of tiles idle, 2 always
 static int g_side_stream = 1;
 // capacity (floats) for the per-wave amax partials the producers of a quantised tensor
 // write: the loss gradient's 4 per row, the dV and RoPE waves of dqkv, the fc / dReLU2
@@ -333,6 +334,10 @@ struct gpt_model {
   hipEvent_t sev_fork = nullptr, sev_join = nullptr, sev_rd[3] = {};
   bool sev_pending[3] = {};
   bool use_side = false;  // this step puts weight gradients on the side stream
+  // the data-gradient launches leave part of a round of 256x256 tiles on the device's CUs
+  // idle (set by gpt_init); only then does the side stream gain: a GEMM workgroup holds a
+  // whole CU, so two GEMMs over whole rounds only share the same CUs
+  bool side_pays = false;
   // profiling
   std::string prof_name;
   std::vector<hipEvent_t> ev;
@@ -649,6 +654,17 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   if (!side_ok) {
     (void)hipGetLastError();
     free_side(M);
+  }
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+      auto tiles = [](long m, long n) { return ((m + 255) / 256) * ((n + 255) / 256); };
+      const long Nt = M->N;  // the data gradients' rows: [N][d] (dm, do, da) and [N][F] (du)
+      M->side_pays = tiles(Nt, cfg->d_model) % cus != 0 || tiles(Nt, cfg->d_ff) % cus != 0;
+    } else {
+      (void)hipGetLastError();
+    }
   }
   *out = M;
   return GPT_OK;
@@ -1089,7 +1105,7 @@ static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* 
 // this returns, on every path
 static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
   // fp8 steps share quantised-operand scratch between the two products of a Linear
-  M->use_side = g_side_stream && M->side && !M->fp8;
+  M->use_side = g_side_stream && M->side && !M->fp8 && (M->side_pays || g_side_stream == 2);
   for (bool& b : M->sev_pending) b = false;
   int rc = forward_backward_on(M, tok, tgt, grad_scale, st);
   if (M->use_side) {
@@ -1627,7 +1643,7 @@ int gptk_ce_variant(int variant) {
 
 int gptk_side_stream(int on) {
   const int prev = g_side_stream;
-  if (on >= 0) g_side_stream = on ? 1 : 0;
+  if (on >= 0) g_side_stream = on > 2 ? 2 : on;
   return prev;
 }
 

@@ -364,12 +364,15 @@ int gptk_fp8_fused_amax(int on);
 
 /* Where the backward's weight-gradient products run (P1, "2. Muon Optimize Edici": the
  * gradients of one step feed one optimizer update, so each dW = dY^T X only has to exist
- * by the end of the step).  on = 1 (the default): on a second stream the model owns, beside
+ * by the end of the step).  On the side stream: a second stream the model owns, beside
  * the data-gradient chain, with events so that each dY buffer is rewritten only after its
  * weight-gradient product has read it and the caller's stream waits for all of them before
  * gpt_step returns (or, for gpt_step_async, before any later work on that stream); the LM
- * head's and fp8 steps' products stay on the caller's stream.  on = 0: every product on the
- * caller's stream.  Both give the same results bit for bit (each product is computed the
+ * head's and fp8 steps' products always stay on the caller's stream.  on = 1 (the
+ * default): the side stream for models whose data-gradient products ([B*T][d], [B*T][F])
+ * leave part of a round of 256x256 tiles on the device's CUs idle, which the weight
+ * gradients then fill; 2: the side stream for every model; 0: every product on the
+ * caller's stream.  All give the same results bit for bit (each product is computed the
  * same way, only its start time moves).  on < 0 only queries.  Returns the previous
  * setting.  Process-wide, not thread-safe against concurrent steps. */
 int gptk_side_stream(int on);

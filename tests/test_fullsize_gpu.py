@@ -133,3 +133,45 @@ def test_full_size_fp8_rows():
         say(f"  d26 fp8 seq {b}: first {PREFIX} row losses rel L2 {e:.2e}, mean rel {m:.2e} (unquantised oracle)")
         assert m < 1e-2
         assert e < 2e-2
+
+
+@pytest.mark.parametrize("name", ["d12", "d24"])
+def test_full_size_gradients_are_per_sequence_means(name):
+    """The loss is the mean over all B*T positions, so the full-batch gradient is the
+    mean of the B per-sequence gradients, at any batch size.  One sequence's gradients
+    are held to the oracle tensor by tensor (the B = 1 step cases); here the full-size
+    step (B = 16: the launch shapes bench.py times, the K = 32768 weight-gradient
+    splits, the side stream) must give every gradient tensor as the sum of 16 B = 1
+    steps accumulated with grad_scale 1/16 (a power of two, so each micro-batch's
+    loss gradient equals the full batch's bit for bit).  What differs is fp32 summation
+    order: the weight gradients' split factors and accumulation, and the LM head's data
+    gradient, whose reduction over the vocabulary is split differently at 2048 and
+    32768 rows.  The backward rounds activations and gradients to bf16, so those
+    differences flip occasional bf16 roundings, which the first layers' attention
+    gradients amplify (d12: 1.7e-3 on layer 0's Wqkv, the largest).  A missing or
+    doubled sequence, or a wrong split-K partial, moves a tensor by several per cent;
+    the bar is 1e-2 per tensor, half the bf16 parity bar."""
+    cfg = configs.get(name)
+    B = cfg["batch"]
+    model = binding.Model(cfg, seed=0)
+    params = inputs.init_weights(cfg, 0)
+    model.set_all_params(params)
+    tok, tgt = inputs.token_batch(B, cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=3)
+    loss = model.step(torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda())
+    one = binding.Model(dict(cfg, batch=1), seed=1)
+    one.set_all_params(params)
+    del params
+    losses = []
+    for b in range(B):
+        losses.append(one.step(torch.from_numpy(np.ascontiguousarray(tok[b:b + 1])).cuda(),
+                               torch.from_numpy(np.ascontiguousarray(tgt[b:b + 1])).cuda(),
+                               accumulate=b > 0, grad_scale=1.0 / B))
+    torch.cuda.synchronize()
+    assert abs(np.mean(losses) - loss) <= 1e-5 * loss
+    errs = [rel_l2(model.grads(i), one.grads(i)) for i in range(2 + 6 * cfg["depth"])]
+    at = int(np.argmax(errs))
+    L = cfg["depth"]
+    say(f"  {name}: loss {loss:.6f}, mean of per-sequence losses {np.mean(losses):.6f}; worst gradient rel L2 "
+        f"{errs[at]:.2e} (tensor {at}); E {errs[0]:.1e}, layer 0 {max(errs[1:7]):.1e}, layer {L - 1} "
+        f"{max(errs[1 + 6 * (L - 1):1 + 6 * L]):.1e}, U {errs[-1]:.1e}")
+    assert errs[at] <= 1e-2, (errs[at], at)

@@ -522,7 +522,7 @@ def test_side_stream_is_bit_identical(name, over):
     params = random_extras(inputs.init_weights(cfg, 0), cfg, 0)
     batches = [inputs.token_batch(cfg["batch"], cfg["seq_len"], cfg["vocab"], dist=cfg["tokens"], seed=s)
                for s in range(2)]
-    prev = binding.side_stream(1)
+    prev = binding.side_stream(2)
     try:
         two = _bf16_steps(cfg, params, batches)
         binding.side_stream(0)
