@@ -1586,14 +1586,23 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
   const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
   const int t = threadIdx.x, c8 = (t & 15) * 8;
+  // the thread's eight 8-element chunks are all loaded before the first is converted (a
+  // chunk outside the matrix reads element 0 and is zeroed), so that eight loads per
+  // thread are in flight instead of one load-convert-store chain at a time
+  float f[8][8];
+  bool ok[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = r0 + (t >> 4) + 16 * j, c = c0 + c8;
+    ok[j] = r < rows && c < cols;
+    load8f<T>(x + (ok[j] ? (long)r * ldx + c : 0L), f[j]);
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int rl = (t >> 4) + 16 * j, r = r0 + rl, c = c0 + c8;
     uint2 b = make_uint2(0, 0);
-    if (r < rows && c < cols) {
-      float f[8];
-      load8f<T>(x + (long)r * ldx + c, f);
-      b = e4m3x8(f, s);
+    if (ok[j]) {
+      b = e4m3x8(f[j], s);
       if (q) *reinterpret_cast<uint2*>(q + (long)r * ldq + c) = b;
     }
     if (qt) *reinterpret_cast<uint2*>(tile + rl * TS + c8) = b;
