@@ -87,7 +87,7 @@ inline LayerOffs layer_offs(const gpt_cfg& c) {
 struct Offsets {
   size_t params, grads, mom, adam_m, adam_v, wact, uact, hs, a, rstd_a, qkv, rq, rk, o, lse, m, rstd_m, g, r, rstd_f, logits,
       dlogits, row_loss, argmax, dh0, dh1, dh_act, dtmp, dbig, dqkv, do_act, Dbuf, splitws, embws, xf, xa0, xa1, xl0,
-      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, mv_jobs, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8c,
+      xl1, Af, Aa, Ba, Al, Bl, ss_part, ss, mat_off, mat_size, mv_jobs, rope, loss, err, wq8, wtq8, wscale, q8a, q8b, q8b2, q8c,
       xq8t, amax, qinv, amax_part, amax_fuse, hx, hfin, emb, dx0, dmid, xpart, vg, dve, vdz, vpart, vred, nm_v, nm_mean, nm_scale,
       nm_roff, nm_ws;
   size_t splitws_bytes;
@@ -231,14 +231,22 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
     // e4m3 codes of every Linear input, transposed, written by the forward's quantisation
     // pass and read by the weight-gradient GEMM (same tensor, same scale): per layer
     // a, o, m [d][N] and g [F][N], then the head input r [d][N]
-    if (keeps_xt(c)) O.xq8t = P.add(L * N * (3 * d + F) + N * d);
-    else O.q8c = P.add(N * std::max(d, F));
+    if (keeps_xt(c)) {
+      O.xq8t = P.add(L * N * (3 * d + F) + N * d);
+      // a second buffer for the block Linears' transposed dY codes: the weight gradient on
+      // the backward's side stream reads one while the next Linear's dY is quantised into
+      // the other
+      O.q8b2 = P.add(N * std::max(qkv_dim(c), F));
+    } else {
+      O.q8c = P.add(N * std::max(d, F));
+    }
     O.amax = P.add(kQuantSlots(c) * 4);
     O.qinv = P.add(kQuantSlots(c) * 4);
     O.amax_part = P.add(kAmaxParts * 4);  // per-block maxima of the amax pass (reused, stream-ordered)
     O.amax_fuse = P.add(kFuseParts(c) * 4);  // the producers' per-wave maxima (reused, stream-ordered)
   } else {
-    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8c = O.xq8t = O.amax = O.qinv = O.amax_part = O.amax_fuse = 0;
+    O.wq8 = O.wtq8 = O.wscale = O.q8a = O.q8b = O.q8b2 = O.q8c = O.xq8t = O.amax = O.qinv = O.amax_part =
+        O.amax_fuse = 0;
   }
   O.rope = P.add(T * (c.head_dim / 2) * 2 * 4);
   O.loss = P.add(8);
@@ -331,8 +339,9 @@ struct gpt_model {
   // tails, bandwidth-bound kernels).  Events order the two streams: fork (the main stream
   // has produced dY), one per dY buffer (its last reader on the side stream) and join.
   hipStream_t side = nullptr;
-  hipEvent_t sev_fork = nullptr, sev_join = nullptr, sev_rd[3] = {};
-  bool sev_pending[3] = {};
+  hipEvent_t sev_fork = nullptr, sev_join = nullptr, sev_rd[5] = {};
+  bool sev_pending[5] = {};
+  int q8b_cur = 0;  // fp8: the transposed-dY code buffer the next side-stream weight gradient reads
   bool use_side = false;  // this step puts weight gradients on the side stream
   // the data-gradient launches leave part of a round of 256x256 tiles on the device's CUs
   // idle (set by gpt_init); only then does the side stream gain: a GEMM workgroup holds a
@@ -544,7 +553,8 @@ static void refresh_act(gpt_model* M, hipStream_t st) {
 }
 
 static void free_side(gpt_model* M) {
-  for (hipEvent_t* e : {&M->sev_fork, &M->sev_join, &M->sev_rd[0], &M->sev_rd[1], &M->sev_rd[2]})
+  for (hipEvent_t* e : {&M->sev_fork, &M->sev_join, &M->sev_rd[0], &M->sev_rd[1], &M->sev_rd[2], &M->sev_rd[3],
+                        &M->sev_rd[4]})
     if (*e) { (void)hipEventDestroy(*e); *e = nullptr; }
   if (M->side) { (void)hipStreamDestroy(M->side); M->side = nullptr; }
 }
@@ -649,7 +659,8 @@ int gpt_init(const gpt_cfg* cfg, uint64_t seed, void* arena, size_t arena_bytes,
   // the side stream (default priority) and its events; without them every product stays on
   // the caller's stream
   bool side_ok = hipStreamCreateWithFlags(&M->side, hipStreamNonBlocking) == hipSuccess;
-  for (hipEvent_t* e : {&M->sev_fork, &M->sev_join, &M->sev_rd[0], &M->sev_rd[1], &M->sev_rd[2]})
+  for (hipEvent_t* e : {&M->sev_fork, &M->sev_join, &M->sev_rd[0], &M->sev_rd[1], &M->sev_rd[2], &M->sev_rd[3],
+                        &M->sev_rd[4]})
     side_ok = side_ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
   if (!side_ok) {
     (void)hipGetLastError();
@@ -755,8 +766,9 @@ static int lin_fwd(gpt_model* M, GemmArgs p, int w, hipStream_t st, int xslot = 
   return run_gemm(M, p, st, false);
 }
 
-// dY buffers of the backward that weight-gradient products on the side stream read
-enum { RD_DH = 0, RD_DBIG = 1, RD_DQKV = 2 };
+// buffers of the backward that weight-gradient products on the side stream read: the dY
+// buffers (bf16 products) and the two transposed-dY code buffers (e4m3 products)
+enum { RD_DH = 0, RD_DBIG = 1, RD_DQKV = 2, RD_Q8B = 3 };
 
 // the main stream waits for the side stream's last reader of dY buffer rd (before it
 // overwrites that buffer)
@@ -785,6 +797,16 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
   uint8_t* q8b = M->at_off<uint8_t>(M->off.q8b);
   uint8_t* q8c = M->at_off<uint8_t>(M->off.q8c);
   const float* qinv = M->at_off<float>(M->off.qinv);
+  const bool side = rd >= 0 && M->use_side;
+  // the buffer the side stream's weight gradient reads: its transposed dY codes (e4m3),
+  // alternating between two buffers, else dY itself
+  int rbuf = rd;
+  if (side && f8w) {
+    rbuf = RD_Q8B + M->q8b_cur;
+    if (M->q8b_cur) q8b = M->at_off<uint8_t>(M->off.q8b2);
+    M->q8b_cur ^= 1;
+    if ((rc = side_wait(M, rbuf, st))) return rc;  // its previous reader is done
+  }
   const int sy =
       (f8w || f8d) ? quant_act(M, dY, N, nout, ldy, f8d ? q8a : nullptr, f8w ? q8b : nullptr, st, yslot) : 0;
   if (f8w) {
@@ -799,12 +821,12 @@ static int lin_bwd(gpt_model* M, const void* dY, long ldy, const void* X, long l
     pw.A = dY; pw.lda = ldy; pw.a_kmaj = false;
     pw.B = X; pw.ldb = ldx; pw.b_kmaj = false;
   }
-  if (rd >= 0 && M->use_side) {  // dY and X are ready on the main stream
+  if (side) {  // dY (or its codes) and X are ready on the main stream
     if (hipEventRecord(M->sev_fork, st) != hipSuccess || hipStreamWaitEvent(M->side, M->sev_fork, 0) != hipSuccess)
       return GPT_ERR_HIP;
     if ((rc = run_gemm(M, pw, M->side, true))) return rc;
-    if (hipEventRecord(M->sev_rd[rd], M->side) != hipSuccess) return GPT_ERR_HIP;
-    M->sev_pending[rd] = true;
+    if (hipEventRecord(M->sev_rd[rbuf], M->side) != hipSuccess) return GPT_ERR_HIP;
+    M->sev_pending[rbuf] = true;
   } else if ((rc = run_gemm(M, pw, st, true))) {
     return rc;
   }
@@ -1104,8 +1126,10 @@ static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* 
 // one forward + backward on stream st; the side stream (weight gradients) joins st before
 // this returns, on every path
 static int forward_backward(gpt_model* M, const int32_t* tok, const int32_t* tgt, float grad_scale, hipStream_t st) {
-  // fp8 steps share quantised-operand scratch between the two products of a Linear
-  M->use_side = g_side_stream && M->side && !M->fp8 && (M->side_pays || g_side_stream == 2);
+  // fp8 steps whose weight gradients quantise X themselves share that scratch (q8c) between
+  // Linears: one stream for them
+  M->use_side = g_side_stream && M->side && (!M->fp8 || keeps_xt(M->cfg)) && (M->side_pays || g_side_stream == 2);
+  M->q8b_cur = 0;
   for (bool& b : M->sev_pending) b = false;
   int rc = forward_backward_on(M, tok, tgt, grad_scale, st);
   if (M->use_side) {

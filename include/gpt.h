@@ -368,7 +368,8 @@ int gptk_fp8_fused_amax(int on);
  * the data-gradient chain, with events so that each dY buffer is rewritten only after its
  * weight-gradient product has read it and the caller's stream waits for all of them before
  * gpt_step returns (or, for gpt_step_async, before any later work on that stream); the LM
- * head's and fp8 steps' products always stay on the caller's stream.  on = 1 (the
+ * head's products, and those of e4m3 steps whose weight gradients quantise their own
+ * inputs (fp8_gemms without the forward bit), always stay on the caller's stream.  on = 1 (the
  * default): the side stream for models whose data-gradient products ([B*T][d], [B*T][F])
  * leave part of a round of 256x256 tiles on the device's CUs idle, which the weight
  * gradients then fill; 2: the side stream for every model; 0: every product on the

@@ -490,7 +490,7 @@ def test_fp8_fused_amax_is_bit_identical(name, over):
     say(f"  {name} {over}: losses {fused[0][0]:.6f}, {fused[1][0]:.6f}; fused and separate amax bit-identical")
 
 
-def _bf16_steps(cfg, params, batches):
+def _side_steps(cfg, params, batches):
     """Two steps with a Muon update between them; the second accumulates a half-scaled
     micro-batch onto the first's gradients before the update is taken again."""
     model = binding.Model(cfg, seed=0)
@@ -510,11 +510,14 @@ def _bf16_steps(cfg, params, batches):
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("laptop", {"batch": 8}),
                                        ("d12", {"batch": 2, "depth": 2}),
-                                       ("laptop", {"batch": 8, "extras": 31, "n_kv_head": 1, "attn_window": 100})],
-                         ids=["tiny", "laptop", "d12_L2", "laptop_extras_mqa_window"])
+                                       ("laptop", {"batch": 8, "extras": 31, "n_kv_head": 1, "attn_window": 100}),
+                                       ("laptop", {"batch": 8, "precision": "fp8"}),
+                                       ("d26", {"batch": 1, "depth": 2})],
+                         ids=["tiny", "laptop", "d12_L2", "laptop_extras_mqa_window", "laptop_fp8", "d26_fp8_L2"])
 def test_side_stream_is_bit_identical(name, over):
     """The backward's weight-gradient products run on a second stream beside the
-    data-gradient chain (each dY buffer rewritten only after its product has read it).
+    data-gradient chain (each dY buffer, or for e4m3 products each of the two buffers of
+    transposed dY codes, rewritten only after its product has read it).
     Every product is computed exactly as on one stream, so two steps (the second with an
     accumulated micro-batch) and the Muon updates after them must be bit-identical
     with the side stream on and off."""
@@ -524,9 +527,9 @@ def test_side_stream_is_bit_identical(name, over):
                for s in range(2)]
     prev = binding.side_stream(2)
     try:
-        two = _bf16_steps(cfg, params, batches)
+        two = _side_steps(cfg, params, batches)
         binding.side_stream(0)
-        one = _bf16_steps(cfg, params, batches)
+        one = _side_steps(cfg, params, batches)
     finally:
         binding.side_stream(prev)
     for s in range(2):
