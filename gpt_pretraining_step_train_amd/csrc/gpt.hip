@@ -136,6 +136,12 @@ size_t wgrad_ws_bytes(const gpt_cfg& c) {
   return best;
 }
 
+// elements of the Gram-sized Newton-Schulz workspace of the first (d x d) batch: Wq, Wk, Wv,
+// Wo of every layer, or Wq, Wo when grouped-query attention gives Wk, Wv their own shape
+static size_t ns_first_elems(const gpt_cfg& c) {
+  return (size_t)(kv_dim(c) == (size_t)c.d_model ? 4 : 2) * c.depth * c.d_model * c.d_model;
+}
+
 Offsets plan(const gpt_cfg& c, size_t* total) {
   Plan P;
   Offsets O;
@@ -209,11 +215,15 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   O.xa1 = P.add(nBlk * es);
   O.xl0 = P.add(nBlk * es);
   O.xl1 = P.add(nBlk * es);
-  O.Af = P.add(std::max(4 * L * d * d, 2 * L * s * s) * 4);
-  O.Aa = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
-  O.Ba = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
-  O.Al = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
-  O.Bl = P.add(std::max(4 * L * d * d, 2 * L * s * s) * es);
+  // Newton-Schulz Gram-sized workspaces: the d x d batch first, then room for the other
+  // batches (the (kv x d) and (s x lw) matrices, run one after the other), so that the
+  // first batch can run beside the others on the side stream
+  const size_t nsA = ns_first_elems(c) + 2 * L * s * s;
+  O.Af = P.add(nsA * 4);
+  O.Aa = P.add(nsA * es);
+  O.Ba = P.add(nsA * es);
+  O.Al = P.add(nsA * es);
+  O.Bl = P.add(nsA * es);
   (void)l;
   O.ss_part = P.add(6 * L * kSumsqParts * 8);
   O.ss = P.add(6 * L * 8);
@@ -1345,10 +1355,29 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   void* Alo = M->base + O.Al;
   void* Blo = M->base + O.Bl;
   int rc;
-  const NsBuffers nb{xf, {xa[0], xa[1]}, {xl[0], xl[1]}, es, Af, Aa, Ba, Alo, Blo};
-  auto run = [&](const GemmArgs& p) { return run_gemm(M, p, st, false); };
-  for (const Batch& bt : batches)
-    if ((rc = ns_iterate(nat, nsplit, c.ns_steps, c.ns_coeffs, bt.s, bt.l, bt.nb, bt.off, nb, run))) return rc;
+  // the d x d batch on the caller's stream; the others one after another in the second
+  // part of the Gram-sized workspaces, on the side stream beside it when the model's
+  // launches leave CUs idle (gptk_side_stream), joined before the update is applied
+  const size_t a1 = ns_first_elems(c);
+  const NsBuffers nb0{xf, {xa[0], xa[1]}, {xl[0], xl[1]}, es, Af, Aa, Ba, Alo, Blo};
+  const NsBuffers nb1{xf, {xa[0], xa[1]}, {xl[0], xl[1]}, es, Af + a1, (char*)Aa + a1 * es, (char*)Ba + a1 * es,
+                      (char*)Alo + a1 * es, (char*)Blo + a1 * es};
+  const bool ns_side = g_side_stream && M->side && (M->side_pays || g_side_stream == 2) && batches.size() > 1;
+  hipStream_t st1 = ns_side ? M->side : st;
+  if (ns_side &&
+      (hipEventRecord(M->sev_fork, st) != hipSuccess || hipStreamWaitEvent(st1, M->sev_fork, 0) != hipSuccess))
+    return GPT_ERR_HIP;
+  auto run0 = [&](const GemmArgs& p) { return run_gemm(M, p, st, false); };
+  auto run1 = [&](const GemmArgs& p) { return run_gemm(M, p, st1, false); };
+  rc = ns_iterate(nat, nsplit, c.ns_steps, c.ns_coeffs, batches[0].s, batches[0].l, batches[0].nb, batches[0].off, nb0,
+                  run0);
+  for (size_t i = 1; i < batches.size() && !rc; ++i)
+    rc = ns_iterate(nat, nsplit, c.ns_steps, c.ns_coeffs, batches[i].s, batches[i].l, batches[i].nb, batches[i].off,
+                    nb1, run1);
+  if (ns_side &&
+      (hipEventRecord(M->sev_join, st1) != hipSuccess || hipStreamWaitEvent(st, M->sev_join, 0) != hipSuccess))
+    rc = rc ? rc : GPT_ERR_HIP;
+  if (rc) return rc;
   // NorMuon: per output row, the running second moment of the update; rows scaled by its
   // inverse root, the update's Frobenius norm kept
   const bool nm = c.extras & GPT_EXTRA_NORMUON;
