@@ -218,7 +218,8 @@ Offsets plan(const gpt_cfg& c, size_t* total) {
   // Newton-Schulz Gram-sized workspaces: the d x d batch first, then room for the other
   // batches (the (kv x d) and (s x lw) matrices, run one after the other), so that the
   // first batch can run beside the others on the side stream
-  const size_t nsA = ns_first_elems(c) + 2 * L * s * s;
+  const size_t kvd = kv_dim(c);
+  const size_t nsA = ns_first_elems(c) + 2 * L * std::max(s * s, kvd * kvd);
   O.Af = P.add(nsA * 4);
   O.Aa = P.add(nsA * es);
   O.Ba = P.add(nsA * es);
