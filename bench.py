@@ -253,7 +253,9 @@ def main() -> int:
     cfg = configs.get(args.config, attn_window=args.window, n_kv_head=args.kv_heads, extras=args.extras)
     if args.dominant is None:
         args.dominant = "gemm_fp8_dma_kernel<256,256,NT>" if args.fp8 else "gemm_bf16_dma_kernel<256,256,NT>"
-    cfg["precision"] = "fp8" if args.fp8 else "bf16"
+    # e4m3 Linears only with --fp8; otherwise the configuration's own precision (fp32 for
+    # tiny), with d26's e4m3 default taken as bf16
+    cfg["precision"] = "fp8" if args.fp8 else ("bf16" if cfg["precision"] == "fp8" else cfg["precision"])
     torch.cuda.set_device(0)
     model = binding.Model(cfg, seed=0)
     B, T, V = cfg["batch"], cfg["seq_len"], cfg["vocab"]
@@ -300,7 +302,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8-e4m3 linears, bf16 attention/NS" if args.fp8 else "bf16", "data": "synthetic (seeded Zipf(1.1) token ids, 8 batches cycled)",
+        "vs_baseline": None, "dtype": "fp8-e4m3 linears, bf16 attention/NS" if args.fp8 else cfg["precision"], "data": "synthetic (seeded Zipf(1.1) token ids, 8 batches cycled)",
         "config": {"workload": f"{args.config} GPT training step{' (fp8 linears)' if args.fp8 else ''}: "
                                + (f"{K} accumulated fwd+bwd micro-batches of B={B} x T={T}, then Muon(5 NS)"
                                 f"{'+AdamW(E,U)' if args.adamw else ''}" if K > 1 else

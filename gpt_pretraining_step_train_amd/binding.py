@@ -85,6 +85,7 @@ _SIGS = {
     "gptk_fp8_fused_amax": (_I, [_I]),
     "gptk_side_stream": (_I, [_I]),
     "gptk_attn_fwd": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "gptk_attn_fwd_qknorm": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_attn_bwd_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gptk_rmsnorm_fwd": (_I, [_I, _P, _P, _P, _I, _I, _F, _P]),
@@ -396,6 +397,13 @@ def attn_fwd(dtype, qkv, o, lse, B, T, H, hd, window=0, n_kv=None):
     hk = H if n_kv is None else n_kv
     check(lib().gptk_attn_fwd(dtype, _ptr(qkv), _ptr(o), _ptr(lse), B, T, H, hk, hd, window, _stream()),
           "gptk_attn_fwd")
+
+
+def attn_fwd_qknorm(dtype, qkv, o, lse, B, T, H, hd, window=0, n_kv=None):
+    """gptk_attn_fwd_qknorm: q and k rows must be RMS-normalised per head."""
+    hk = H if n_kv is None else n_kv
+    check(lib().gptk_attn_fwd_qknorm(dtype, _ptr(qkv), _ptr(o), _ptr(lse), B, T, H, hk, hd, window, _stream()),
+          "gptk_attn_fwd_qknorm")
 
 
 def attn_bwd(dtype, qkv, o, dO, lse, D, dqkv, B, T, H, hd, window=0, n_kv=None):

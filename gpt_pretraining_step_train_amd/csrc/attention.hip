@@ -249,7 +249,13 @@ struct DmaTilePair {
 // forward
 
 // NW waves of 32 queries per block: every K/V tile staged in LDS serves 32 NW queries
-template <int HD, int NW>
+// QKN: q and k are RMS-normalised per head (the step's QK-norm), so |q.k| <= hd (up to
+// their bf16 rounding) and every scaled score s = q.k log2(e) / sqrt(hd) lies within
+// +-sqrt(hd) log2(e) (16.3 for hd 128).  exp2(s - m) with the fixed reference m =
+// sqrt(hd) log2(e) then lies in [2^-33, ~1]: no overflow, no underflow, and the same
+// relative precision as with the running maximum, which this form neither computes nor
+// rescales to.
+template <int HD, int NW, bool QKN>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int T, int H,
                      int Hkv, int W, float* __restrict__ amax_part) {
@@ -281,9 +287,10 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
-  // running reference maximum (log2 units) and sum; the maximum starts finite so that
-  // a lane whose keys in a tile are all masked (sliding window) gets p = 0, not NaN
-  float m = -1e30f, l = 0.f;
+  // reference (log2 units) and sum: the running maximum, which starts finite so that a
+  // lane whose keys in a tile are all masked (sliding window) gets p = 0, not NaN; or,
+  // for QK-normalised inputs, the fixed bound of the scores
+  float m = QKN ? sqrtf((float)HD) * LOG2E : -1e30f, l = 0.f;
   const float sl2 = LOG2E / sqrtf((float)HD);
   const int Wn = W > 0 ? W : T;  // keys a query sees, itself included
   const int kv_end = min(T, (qb + 1) * BQ);
@@ -348,22 +355,24 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
             if (key > myq || key >= T || key <= myq - Wn) s[kb2][r] = -INFINITY;
           }
       }
-      float bmax = -INFINITY;
+      if constexpr (!QKN) {
+        float bmax = -INFINITY;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kb2][r]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64)) * sl2;
-      const bool raise = bmax > m + RESCALE_LOG2;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float mnew = raise ? bmax : m;
-        const float alpha = fast_exp2(m - mnew);  // 0 on the first raise (m = -1e30)
-        l *= alpha;
+          for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[kb2][r]);
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64)) * sl2;
+        const bool raise = bmax > m + RESCALE_LOG2;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+          const float mnew = raise ? bmax : m;
+          const float alpha = fast_exp2(m - mnew);  // 0 on the first raise (m = -1e30)
+          l *= alpha;
 #pragma unroll
-        for (int i = 0; i < NDB; ++i)
+          for (int i = 0; i < NDB; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-        m = mnew;
+            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+          m = mnew;
+        }
       }
       float rs = 0.f;
 #pragma unroll
@@ -1755,7 +1764,7 @@ int g_attn_bwd_variant = 0;
 // returns the number of amax partials written (0: none)
 template <int HD>
 int fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int W, hipStream_t st,
-                 float* amax_part, long amax_cap) {
+                 float* amax_part, long amax_cap, bool qk_normed) {
   constexpr int NW = kFwdWaves;
   if constexpr (HD == 128) {
     if (at == ACT_BF16 && g_attn_fwd_variant == 1) {
@@ -1768,8 +1777,12 @@ int fwd_dispatch(const void* qkv, void* o, float* lse, int at, int B, int T, int
     const dim3 g((T + 32 * NW - 1) / (32 * NW), B * H);
     const long parts = (long)g.x * g.y * NW;
     if (!amax_part || parts > amax_cap) amax_part = nullptr;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD, NW>), g, dim3(NW * 64), 0, st, (const bf16_t*)qkv, (bf16_t*)o, lse,
-                       T, H, Hkv, W, amax_part);
+    if (qk_normed)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD, NW, true>), g, dim3(NW * 64), 0, st, (const bf16_t*)qkv,
+                         (bf16_t*)o, lse, T, H, Hkv, W, amax_part);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<HD, NW, false>), g, dim3(NW * 64), 0, st, (const bf16_t*)qkv,
+                         (bf16_t*)o, lse, T, H, Hkv, W, amax_part);
     return amax_part ? (int)parts : 0;
   }
   hipLaunchKernelGGL(attn_fwd_f32_kernel<HD>, dim3((T + 63) / 64, B * H), dim3(64), 0, st, (const float*)qkv,
@@ -1831,11 +1844,11 @@ void set_attn_bwd_variant(int v) { g_attn_bwd_variant = v; }
 
 // Hkv must divide H (the callers validate it)
 int launch_attn_fwd(const void* qkv, void* o, float* lse, int at, int B, int T, int H, int Hkv, int hd, int window,
-                    hipStream_t st, float* amax_part, long amax_cap) {
+                    hipStream_t st, float* amax_part, long amax_cap, bool qk_normed) {
   if (B * T * H == 0) return 0;
-  if (hd == 128) return fwd_dispatch<128>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
-  if (hd == 64) return fwd_dispatch<64>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
-  if (hd == 32) return fwd_dispatch<32>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap);
+  if (hd == 128) return fwd_dispatch<128>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap, qk_normed);
+  if (hd == 64) return fwd_dispatch<64>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap, qk_normed);
+  if (hd == 32) return fwd_dispatch<32>(qkv, o, lse, at, B, T, H, Hkv, window, st, amax_part, amax_cap, qk_normed);
   return 0;
 }
 

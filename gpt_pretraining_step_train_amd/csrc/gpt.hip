@@ -952,7 +952,8 @@ static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* 
       launch_ve_fwd(qkv, at, a, tok, ve_tab(M->params(), l), ve_gate(M->params(), l), ve_g(l), N, V, H, Hkv, hd, d,
                     st);
     launch_rope_qknorm_fwd(qkv, at, M->at_off<float>(O.rope), rq, rk, B, T, H, Hkv, hd, eps, st);
-    const int so = fold(launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st, fpart, fcap));
+    // q and k leave the QK-norm RMS-normalised per head: the forward takes its fixed reference
+    const int so = fold(launch_attn_fwd(qkv, o, lse, at, B, T, H, Hkv, hd, c.attn_window, st, fpart, fcap, true));
     cap(l, CAP_O, o);
     {
       GemmArgs p;  // h' = h + o Wo^T
@@ -1714,13 +1715,23 @@ int gptk_attn_variant(int pass, int variant) {
   return GPT_OK;
 }
 
-int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
-                  void* stream) {
+static int attn_fwd_entry(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd,
+                          int window, void* stream, bool qk_normed) {
   int rc = attn_ok(dtype, hd);
   if (rc) return rc;
   if (B < 0 || T < 0 || H < 0 || !kv_heads_ok(H, Hkv) || window < 0 || !qkv || !o || !lse) return GPT_ERR_ARG;
-  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, Hkv, hd, window, (hipStream_t)stream);
+  launch_attn_fwd(qkv, o, lse, act_type(dtype), B, T, H, Hkv, hd, window, (hipStream_t)stream, nullptr, 0, qk_normed);
   return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_HIP;
+}
+
+int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
+                  void* stream) {
+  return attn_fwd_entry(dtype, qkv, o, lse, B, T, H, Hkv, hd, window, stream, false);
+}
+
+int gptk_attn_fwd_qknorm(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd,
+                         int window, void* stream) {
+  return attn_fwd_entry(dtype, qkv, o, lse, B, T, H, Hkv, hd, window, stream, true);
 }
 
 int gptk_attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* D, void* dqkv,

@@ -195,8 +195,11 @@ void launch_quant_e4m3(const void* x, int in_type, int rows, int cols, long ld, 
 void set_attn_fwd_variant(int v);
 void set_attn_bwd_variant(int v);
 void set_ce_variant(int v);
+// qk_normed: every q and k row is RMS-normalised per head (as the step's QK-norm leaves
+// them), which bounds the scores, so the forward skips its running maximum
 int launch_attn_fwd(const void* qkv, void* o, float* lse, int act_type, int B, int T, int H, int Hkv, int hd,
-                    int window, hipStream_t st, float* amax_part = nullptr, long amax_cap = 0);  // partials of o
+                    int window, hipStream_t st, float* amax_part = nullptr, long amax_cap = 0,  // partials of o
+                    bool qk_normed = false);
 int launch_attn_bwd(const void* qkv, const void* o, const void* dO, const float* lse, float* Dbuf,
                     void* dqkv, int act_type, int B, int T, int H, int Hkv, int hd, int window, hipStream_t st,
                     float* amax_part = nullptr, long amax_cap = 0);  // partials of dv

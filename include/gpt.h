@@ -329,6 +329,15 @@ const char* gpt_gemm_kernel_name(int dtype, int a_kmaj, int b_kmaj, int M, int N
  * window); 0: all j <= i; negative: GPT_ERR_ARG. */
 int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd, int window,
                   void* stream);
+/* gptk_attn_fwd for inputs whose every q and k row is RMS-normalised per head, as the
+ * article's QK-norm ("1. GPT Modeli") leaves them and as gpt_step runs it: |q.k| is then at
+ * most hd (up to bf16 rounding), so the bf16 kernel exponentiates against a fixed
+ * reference sqrt(hd) log2(e) instead of a running row maximum (same arguments, layout and
+ * errors; same result up to rounding).  Inputs that are not normalised can overflow the
+ * exponentials: the caller guarantees the normalisation.  fp32 uses gptk_attn_fwd's
+ * kernel. */
+int gptk_attn_fwd_qknorm(int dtype, const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd,
+                         int window, void* stream);
 /* Process-wide choice among the bf16 head_dim-128 attention kernels, for A/B
  * measurements (every variant computes the same result; the default is the fastest
  * measured).  pass 0 = forward: variant 0 = 32 queries per wave (two waves per SIMD),
@@ -342,7 +351,7 @@ int gptk_attn_fwd(int dtype, const void* qkv, void* o, float* lse, int B, int T,
 int gptk_attn_variant(int pass, int variant);
 
 /* Which cross-entropy kernel later steps and gptk_ce take when V is a multiple of 16384
- * (P1, "1. GPT Modeli": the loss over the 32,768-entry vocabulary).  variant 0 (the
+ * (the article's "1. GPT Modeli": the loss over the 32,768-entry vocabulary).  variant 0 (the
  * default) = two passes over each row with few registers, two rows in flight per CU;
  * 1 = the row held in registers, one row per CU.  Both give the same argmax (lowest index
  * among equal maxima) and, up to the order of the exponential sums, the same loss and
@@ -362,7 +371,7 @@ int gptk_ce_variant(int variant);
  * previous setting.  Not thread-safe against concurrent steps. */
 int gptk_fp8_fused_amax(int on);
 
-/* Where the backward's weight-gradient products run (P1, "2. Muon Optimize Edici": the
+/* Where the backward's weight-gradient products run (the article's "2. Muon Optimize Edici": the
  * gradients of one step feed one optimizer update, so each dW = dY^T X only has to exist
  * by the end of the step).  On the side stream: a second stream the model owns, beside
  * the data-gradient chain, with events so that each dY buffer is rewritten only after its

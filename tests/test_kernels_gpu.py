@@ -302,6 +302,14 @@ def test_attention_fwd_bwd(case):
     tol = 1e-2 if dtype == "bf16" else 1e-5
     assert rel_l2(o_got, o_ref) < tol
     assert np.abs(from_dev(lse).reshape(Bn, H, T) - lse_ref).max() < (2e-3 if dtype == "bf16" else 1e-5)
+    # the forward the step runs: q and k are RMS-normalised per head (as _qkv makes them), so
+    # it exponentiates against a fixed reference instead of a running maximum
+    o2 = torch.zeros_like(o)
+    lse2 = torch.zeros_like(lse)
+    B.attn_fwd_qknorm(DT[dtype], dq, o2, lse2, Bn, T, H, hd, win, n_kv=Hkv)
+    torch.cuda.synchronize()
+    assert rel_l2(from_dev(o2).reshape(Bn, T, H, hd), o_ref) < tol
+    assert np.abs(from_dev(lse2).reshape(Bn, H, T) - lse_ref).max() < (2e-3 if dtype == "bf16" else 1e-5)
     # backward, from the kernel's own forward output (as in the step)
     rng = np.random.default_rng(12)
     dO = _round(rng.standard_normal((Bn, T, H, hd)), dtype)
