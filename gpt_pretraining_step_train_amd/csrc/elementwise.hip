@@ -44,6 +44,17 @@ __device__ inline void st4<bf16_t>(bf16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
+template <typename T>
+__device__ inline float4 ld4(const T* p) { return make_float4(ld<T>(p), ld<T>(p + 1), ld<T>(p + 2), ld<T>(p + 3)); }
+template <>
+__device__ inline float4 ld4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <>
+__device__ inline float4 ld4<bf16_t>(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
 // the magnitude m as a store of type T holds it (see bf16_round)
 template <typename T>
 __device__ inline float round_act(float m) { return m; }
@@ -110,8 +121,11 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
 }
 
 // dx = dres + r * (dy - y * mean(dy * y)),  y = x * r
-template <typename T>
-__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+// HAT: x is the forward's stored output y = x rstd (type T: the bf16 copy the step keeps
+// for its Linear), read in place of the fp32 input and its product with rstd (2 bytes per
+// element less; y then carries that store's rounding)
+template <typename T, bool HAT>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dy, const void* __restrict__ x,
                                                           const float* __restrict__ rstd, const float* __restrict__ dres,
                                                           float* __restrict__ dx, T* __restrict__ dxa, int N, int d,
                                                           float* __restrict__ amax_part) {
@@ -119,7 +133,6 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
   const long off = (long)row * d;
-  const float4* xr = reinterpret_cast<const float4*>(x + off);
   const float4* gr = reinterpret_cast<const float4*>(dy + off);
   const int n4 = d / 4;
   const float r = rstd[row];
@@ -128,9 +141,17 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
 #pragma unroll
   for (int j = 0; j < MAXV4; ++j) {
     const int i = lane + j * 64;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), g = a;
-    if (i < n4) { a = xr[i]; g = gr[i]; }
-    yv[j] = make_float4(a.x * r, a.y * r, a.z * r, a.w * r);
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f), g = y;
+    if (i < n4) {
+      g = gr[i];
+      if constexpr (HAT) {
+        y = ld4<T>(reinterpret_cast<const T*>(x) + off + 4 * i);
+      } else {
+        const float4 a = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off)[i];
+        y = make_float4(a.x * r, a.y * r, a.z * r, a.w * r);
+      }
+    }
+    yv[j] = y;
     gv[j] = g;
     dot += g.x * yv[j].x + g.y * yv[j].y + g.z * yv[j].z + g.w * yv[j].w;
   }
@@ -1701,14 +1722,26 @@ int launch_rmsnorm_fwd(const float* x, void* y, int yt, float* rstd, int N, int 
 }
 
 int launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres, float* dx,
-                       void* dxa, int at, int N, int d, float eps, hipStream_t st, float* amax_part, long amax_cap) {
+                       void* dxa, int at, int N, int d, float eps, hipStream_t st, float* amax_part, long amax_cap,
+                       const void* y) {
   (void)eps;
   dim3 g((N + 3) / 4), b(256);
   if (!amax_part || !dxa || N > amax_cap) amax_part = nullptr;
-  if (at == ACT_BF16)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, g, b, 0, st, dy, x, rstd, dres, dx, (bf16_t*)dxa, N, d, amax_part);
-  else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, b, 0, st, dy, x, rstd, dres, dx, (float*)dxa, N, d, amax_part);
+  if (at == ACT_BF16) {
+    if (y)
+      hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, true>), g, b, 0, st, dy, y, rstd, dres, dx, (bf16_t*)dxa, N, d,
+                         amax_part);
+    else
+      hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, false>), g, b, 0, st, dy, x, rstd, dres, dx, (bf16_t*)dxa, N, d,
+                         amax_part);
+  } else {
+    if (y)
+      hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, true>), g, b, 0, st, dy, y, rstd, dres, dx, (float*)dxa, N, d,
+                         amax_part);
+    else
+      hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, false>), g, b, 0, st, dy, x, rstd, dres, dx, (float*)dxa, N, d,
+                         amax_part);
+  }
   return amax_part ? N : 0;
 }
 

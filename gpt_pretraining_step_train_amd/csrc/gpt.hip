@@ -1034,7 +1034,7 @@ static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* 
   int sdh = -1;  // slot of the output gradient entering the next block's W2 (dh_act)
   if (!ex_back)
     sdh = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * L), M->at_off<float>(O.rstd_f), nullptr, dh[0], dh_act, at, N, d, eps,
-                                  st, fpart, fcap));
+                                  st, fpart, fcap, r));  // the norm's stored output r stands in for x rstd
   if (ex_resid) launch_zero(dx0, (size_t)N * d * 4, st);
   if (ex_ve) launch_embed_sort(tok, N, V, M->base + O.embws, st);  // shared by every scatter below
   int cur = 0;
@@ -1068,7 +1068,7 @@ static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* 
     cap(l, CAP_DM, dtmp);
     if ((rc = side_wait(M, RD_DH, st))) return rc;  // dh_act is rewritten here
     const int sdo = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * l + 1), M->at_off<float>(O.rstd_m) + (size_t)l * N, dh[cur],
-                                            dh[cur ^ 1], dh_act, at, N, d, eps, st, fpart, fcap));
+                                            dh[cur ^ 1], dh_act, at, N, d, eps, st, fpart, fcap, m));
     cur ^= 1;
     cap(l, CAP_DYO, dh_act);
     {
@@ -1117,7 +1117,7 @@ static int forward_backward_on(gpt_model* M, const int32_t* tok, const int32_t* 
       sdh = -1;
     } else {  // (layer 0's output feeds the embedding, no Linear: no partials)
       sdh = fold(launch_rmsnorm_bwd(dtmp, hsl(2 * l), M->at_off<float>(O.rstd_a) + (size_t)l * N, dh[cur],
-                                    dh[cur ^ 1], dh_act, at, N, d, eps, st, l > 0 ? fpart : nullptr, fcap));
+                                    dh[cur ^ 1], dh_act, at, N, d, eps, st, l > 0 ? fpart : nullptr, fcap, a));
     }
     cur ^= 1;
   }

@@ -73,9 +73,11 @@ void launch_embed_gather(const int32_t* tok, const float* E, float* h, int N, in
 // (launch_amax_fold) is the tensor's amax without a pass of its own.
 int launch_rmsnorm_fwd(const float* x, void* y, int ytype, float* rstd, int N, int d, float eps,
                        hipStream_t st, float* amax_part = nullptr, long amax_cap = 0);
+// y (or null): the forward's stored output x * rstd (act type), read instead of x
 int launch_rmsnorm_bwd(const float* dy, const float* x, const float* rstd, const float* dres,
                        float* dx, void* dx_act, int act_type, int N, int d, float eps, hipStream_t st,
-                       float* amax_part = nullptr, long amax_cap = 0);  // partials of dx_act
+                       float* amax_part = nullptr, long amax_cap = 0,  // partials of dx_act
+                       const void* y = nullptr);
 // extras (per-layer residual scaling, smear, backout).  A coefficient is mul * (*p), or mul
 // when p is null; p points into the parameter vector on the device.
 // m = a x + b z (fp32, z null: b = 0), y = m / rms(m), rstd as for launch_rmsnorm_fwd
