@@ -1213,12 +1213,23 @@ __global__ void __launch_bounds__(256) momentum_sumsq_kernel(float* __restrict__
   const long per = (n4 + parts - 1) / parts;
   const long b = part * per, e = min(n4, b + per);
   double s = 0.0;
-  for (long i = b + threadIdx.x; i < e; i += 256) {
-    float4 a = reinterpret_cast<float4*>(mp)[i];
-    const float4 q = reinterpret_cast<const float4*>(gp)[i];
-    a.x = mu * a.x + q.x; a.y = mu * a.y + q.y; a.z = mu * a.z + q.z; a.w = mu * a.w + q.w;
-    reinterpret_cast<float4*>(mp)[i] = a;
-    s += (double)a.x * a.x + (double)a.y * a.y + (double)a.z * a.z + (double)a.w * a.w;
+  // four float4 of each operand per thread in flight before any is used
+  for (long i0 = b + threadIdx.x; i0 < e; i0 += 4 * 256) {
+    float4 a[4], q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long i = i0 + k * 256;
+      if (i < e) { a[k] = reinterpret_cast<float4*>(mp)[i]; q[k] = reinterpret_cast<const float4*>(gp)[i]; }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long i = i0 + k * 256;
+      if (i >= e) break;
+      float4 v = a[k];
+      v.x = mu * v.x + q[k].x; v.y = mu * v.y + q[k].y; v.z = mu * v.z + q[k].z; v.w = mu * v.w + q[k].w;
+      reinterpret_cast<float4*>(mp)[i] = v;
+      s += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+    }
   }
   if (part == parts - 1)
     for (long i = n4 * 4 + threadIdx.x; i < n; i += 256) {
@@ -1313,15 +1324,23 @@ __global__ void __launch_bounds__(256) ns_normalize_batched_kernel(const float* 
   float4* f4 = reinterpret_cast<float4*>(xf + jb.dst);
   T* a = xa + jb.dst;
   T* lo = xlo ? xlo + jb.dst : nullptr;
-  const long n4 = jb.n / 4;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-    const float4 u = s4[i];
-    const float4 v = make_float4(u.x * scale, u.y * scale, u.z * scale, u.w * scale);
-    f4[i] = v;
-    st4<T>(a + 4 * i, v);
-    if (lo) {
-      const float4 h = make_float4(ld<T>(a + 4 * i), ld<T>(a + 4 * i + 1), ld<T>(a + 4 * i + 2), ld<T>(a + 4 * i + 3));
-      st4<T>(lo + 4 * i, make_float4(v.x - h.x, v.y - h.y, v.z - h.z, v.w - h.w));
+  const long n4 = jb.n / 4, stride = (long)gridDim.x * 256;
+  for (long i0 = blockIdx.x * 256L + threadIdx.x; i0 < n4; i0 += 4 * stride) {
+    float4 u[4];  // four loads in flight before the first store
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i0 + k * stride < n4) u[k] = s4[i0 + k * stride];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long i = i0 + k * stride;
+      if (i >= n4) break;
+      const float4 v = make_float4(u[k].x * scale, u[k].y * scale, u[k].z * scale, u[k].w * scale);
+      f4[i] = v;
+      st4<T>(a + 4 * i, v);
+      if (lo) {
+        const float4 h = make_float4(ld<T>(a + 4 * i), ld<T>(a + 4 * i + 1), ld<T>(a + 4 * i + 2), ld<T>(a + 4 * i + 3));
+        st4<T>(lo + 4 * i, make_float4(v.x - h.x, v.y - h.y, v.z - h.z, v.w - h.w));
+      }
     }
   }
 }
@@ -1336,14 +1355,22 @@ __global__ void __launch_bounds__(256) muon_apply_batched_kernel(float* __restri
   const float4* x4 = reinterpret_cast<const float4*>(x + jb.dst);
   T* a = wa ? wa + jb.wact : nullptr;
   const float* rs = row_scale ? row_scale + jb.srow : nullptr;
-  const long n4 = jb.n / 4;
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-    float4 v = w4[i];
-    const float4 q = x4[i];
-    const float f = rs ? lr * rs[4 * i / jb.cols] : lr;  // cols % 4 == 0: one row
-    v.x -= f * q.x; v.y -= f * q.y; v.z -= f * q.z; v.w -= f * q.w;
-    w4[i] = v;
-    if (a) st4<T>(a + 4 * i, v);
+  const long n4 = jb.n / 4, stride = (long)gridDim.x * 256;
+  for (long i0 = blockIdx.x * 256L + threadIdx.x; i0 < n4; i0 += 4 * stride) {
+    float4 v[4], q[4];  // four of each in flight before the first store
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i0 + k * stride < n4) { v[k] = w4[i0 + k * stride]; q[k] = x4[i0 + k * stride]; }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long i = i0 + k * stride;
+      if (i >= n4) break;
+      const float f = rs ? lr * rs[4 * i / jb.cols] : lr;  // cols % 4 == 0: one row
+      float4 o = v[k];
+      o.x -= f * q[k].x; o.y -= f * q[k].y; o.z -= f * q[k].z; o.w -= f * q[k].w;
+      w4[i] = o;
+      if (a) st4<T>(a + 4 * i, o);
+    }
   }
 }
 
