@@ -207,3 +207,24 @@ def test_capture_sizes(lib):
     assert lib.gpt_capture(None, 0, None, 0) == 1
     names = [n for n, _, _ in binding.Model.CAPTURE_BLOCK]
     assert len(names) == len(block) and len(binding.Model.CAPTURE_HEAD) == len(head)
+
+
+ERR_ARG = 1  # GPT_ERR_ARG in include/gpt.h
+
+
+def test_process_switches_validate_and_report(lib):
+    """The process-wide switches set no device state: they validate their argument and
+    return the previous setting (a negative argument only queries)."""
+    prev = lib.gptk_side_stream(-1)
+    assert prev == 1                                   # default: where CUs would idle
+    assert lib.gptk_side_stream(0) == 1
+    assert lib.gptk_side_stream(2) == 0
+    assert lib.gptk_side_stream(-1) == 2
+    assert lib.gptk_side_stream(prev) == 2
+    assert lib.gptk_side_stream(-1) == prev
+    assert lib.gptk_ce_variant(1) == 0 and lib.gptk_ce_variant(0) == 0
+    for bad in (-1, 2, 7):
+        assert lib.gptk_ce_variant(bad) == ERR_ARG
+    for p, v in ((0, 2), (1, 3), (2, 0), (-1, 0), (0, -1)):
+        assert lib.gptk_attn_variant(p, v) == ERR_ARG
+    assert lib.gptk_attn_variant(0, 0) == 0 and lib.gptk_attn_variant(1, 0) == 0
