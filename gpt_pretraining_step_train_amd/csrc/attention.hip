@@ -780,18 +780,31 @@ attn_bwd_dq_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ o,
     body(std::integral_constant<int, 0>{}, it);
     if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
-  if (myq < T) {
-    const float sc = 1.f / sqrtf((float)HD);
-    bf16_t* op = dqkv + ((long)b * T + myq) * ld + h * HD;
+  const float sc = 1.f / sqrtf((float)HD);
+  // The wave's 32 queries x HD go through LDS so that they leave as whole rows, 16 bytes
+  // per lane (a lane holds four dimensions of one query per store otherwise).  Every
+  // wave is past the last tile's barrier, so the K / V buffers are free: waves 0, 1
+  // stage in Ks, waves 2, 3 in Vs (padded rows).
+  constexpr int SR = HD + 8, LPR = HD / 8, RPI = 64 / LPR;
+  static_assert(2 * 32 * SR <= 2 * TE, "staging fits the tile buffers");
+  bf16_t* sb = (wave < 2 ? &Ks[0][0] : &Vs[0][0]) + (wave & 1) * 32 * SR;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + g * 8 + hl * 4;
-        uint2 u = make_uint2(pack_bf2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
-                             pack_bf2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc));
-        *reinterpret_cast<uint2*>(op + d) = u;
-      }
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + hl * 4;
+      *reinterpret_cast<uint2*>(sb + lq * SR + d) =
+          make_uint2(pack_bf2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                     pack_bf2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc));
+    }
+  __syncthreads();
+  const int c8 = (lane % LPR) * 8, rl = lane / LPR;
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int q = q0 + r0 + rl;
+    if (q < T)
+      *reinterpret_cast<uint4*>(dqkv + ((long)b * T + q) * ld + h * HD + c8) =
+          *reinterpret_cast<const uint4*>(sb + (r0 + rl) * SR + c8);
   }
 }
 
@@ -1394,17 +1407,31 @@ attn_bwd_dkdv_pipe_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restri
   const float scale = dk_role ? 1.f / sqrtf((float)HD) : 1.f;
   const long col = (long)(dk_role ? H + hk : H + Hkv + hk) * HD;
   float mo = 0.f;  // max |dv| of the lane as stored (amax_part)
+  // The wave's 32 x HD result goes through LDS so that it leaves as whole rows, 16 bytes
+  // per lane (a lane holds one column of the accumulator, which would make 2-byte
+  // stores).  Every wave is past the last step's barrier, so the Q / dO tile buffers are
+  // free: the dV waves stage in Qs, the dK waves in Gs (4 x 32 padded rows each).
+  constexpr int SR = HD + 8, LPR = HD / 8, RPI = 64 / LPR;
+  bf16_t* sb = (dk_role ? &Gs[0][0] : &Qs[0][0]) + kw * 32 * SR;
+  static_assert(4 * 32 * SR <= 3 * TE, "staging fits the tile buffers");
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = key0 + acc_row(lane, r);
-      if (key < T) {
-        const float v = acc[db][r] * scale;
-        dqkv[((long)b * T + key) * ld + col + db * 32 + lq] = f2bf(v);
-        if (!dk_role) mo = fmaxf(mo, fabsf(v));
-      }
+      const int kr = acc_row(lane, r);
+      const float v = acc[db][r] * scale;
+      sb[kr * SR + db * 32 + lq] = f2bf(v);
+      if (!dk_role && key0 + kr < T) mo = fmaxf(mo, fabsf(v));
     }
+  __syncthreads();
+  const int c8 = (lane % LPR) * 8, rl = lane / LPR;
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int kr = r0 + rl, key = key0 + kr;
+    if (key < T)
+      *reinterpret_cast<uint4*>(dqkv + ((long)b * T + key) * ld + col + c8) =
+          *reinterpret_cast<const uint4*>(sb + kr * SR + c8);
+  }
   if (amax_part) {
     mo = wave_max(mo);
     if (lane == 0) amax_part[((long)blockIdx.y * gridDim.x + blockIdx.x) * 8 + wave] = bf16_round(mo);
