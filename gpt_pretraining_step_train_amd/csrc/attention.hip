@@ -410,9 +410,15 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
     if (it + 1 < nkv) body(std::integral_constant<int, 1>{}, it + 1);
   }
   float mo = 0.f;  // max |o| of the lane as stored (amax_part)
-  if (myq < T) {
-    const float inv = 1.f / l;
-    bf16_t* op = out + ((long)b * T + myq) * ((long)H * HD) + h * HD;
+  // The wave's 32 queries x HD go through LDS so that they leave as whole rows, 16 bytes
+  // per lane (a lane holds four dimensions of one query per store otherwise).  Every wave
+  // is past the last tile's barrier, so the K / V buffers are free: the first half of the
+  // waves stage in Ks, the others in Vs (padded rows).
+  {
+    constexpr int SR = HD + 8, LPR = HD / 8, RPI = 64 / LPR, NH = NW / 2;
+    static_assert(NW % 2 == 0 && NH * 32 * SR <= 2 * TE, "staging fits the tile buffers");
+    bf16_t* sb = (wave < NH ? &Ks[0][0] : &Vs[0][0]) + (wave % NH) * 32 * SR;
+    const float inv = myq < T ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -424,9 +430,18 @@ attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, f
           ov[e] = oacc[db][4 * g + e] * inv;
           mo = fmaxf(mo, fabsf(ov[e]));
         }
-        *reinterpret_cast<uint2*>(op + d) = make_uint2(pack_bf2(ov[0], ov[1]), pack_bf2(ov[2], ov[3]));
+        *reinterpret_cast<uint2*>(sb + lq * SR + d) = make_uint2(pack_bf2(ov[0], ov[1]), pack_bf2(ov[2], ov[3]));
       }
-    if (hl == 0) lse[(long)bh * T + myq] = (m + log2f(l)) * LN2;
+    if (myq < T && hl == 0) lse[(long)bh * T + myq] = (m + log2f(l)) * LN2;
+    __syncthreads();
+    const int c8 = (lane % LPR) * 8, rl = lane / LPR;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int q = q0 + r0 + rl;
+      if (q < T)
+        *reinterpret_cast<uint4*>(out + ((long)b * T + q) * ((long)H * HD) + h * HD + c8) =
+            *reinterpret_cast<const uint4*>(sb + (r0 + rl) * SR + c8);
+    }
   }
   if (amax_part) {  // one entry per wave
     mo = wave_max(mo);
