@@ -1657,23 +1657,29 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
   }
   if (!qt) return;
   __syncthreads();
-  const int cl = t & 127, rs = (t >> 7) * 64, c = c0 + cl, rb = r0 + rs;
-  if (c >= cols || rb >= rows) return;
-  uint32_t w[16];
+  // qt row c (tile column cl) is the tile's 128 rows: eight lanes write it as one whole
+  // 128-byte line, 16 rows each, so that a wave's store covers eight lines (lanes writing
+  // 16 bytes into 64 different rows left every line partial)
+  const int ch = t & 7, rs = ch * 16, rb = r0 + rs;
+  const bool vec = rb + 16 <= rows && (ldqt % 16) == 0;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    uint32_t v = 0;
+  for (int it = 0; it < 4; ++it) {
+    const int cl = it * 32 + (t >> 3), c = c0 + cl;
+    if (c >= cols || rb >= rows) continue;
+    uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[(rs + 4 * k + e) * TS + cl] << (8 * e);
-    w[k] = v;
-  }
-  uint8_t* dst = qt + (long)c * ldqt + rb;
-  if (rb + 64 <= rows && (ldqt % 16) == 0 && (rb % 16) == 0) {
+    for (int k = 0; k < 4; ++k) {
+      uint32_t v = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      reinterpret_cast<uint4*>(dst)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
-  } else {
-    for (int e = 0; e < 64 && rb + e < rows; ++e) dst[e] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+      for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[(rs + 4 * k + e) * TS + cl] << (8 * e);
+      w[k] = v;
+    }
+    uint8_t* dst = qt + (long)c * ldqt + rb;
+    if (vec) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int e = 0; e < 16 && rb + e < rows; ++e) dst[e] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+    }
   }
 }
 
