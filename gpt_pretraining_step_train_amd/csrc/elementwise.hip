@@ -1627,8 +1627,12 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
                                                               const unsigned* amax_bits, uint8_t* __restrict__ q,
                                                               long ldq, uint8_t* __restrict__ qt, long ldqt,
                                                               float* inv_scale) {
-  constexpr int TS = 136;  // LDS row stride in bytes (8-byte aligned rows)
-  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * TS];
+  // LDS row stride in bytes (8-byte aligned rows); each group of 16 rows is shifted by a
+  // further 8 bytes, so the eight row groups that one column read touches start in
+  // different banks (544 dwords apart they shared two)
+  constexpr int TS = 136;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * TS + 7 * 8];
+  auto lrow = [](int rl) { return rl * TS + (rl >> 4) * 8; };
   const float amax = __uint_as_float(*amax_bits);
   const float s = amax > 0.f ? 448.f / amax : 1.f;
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
@@ -1653,7 +1657,7 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
       b = e4m3x8(f[j], s);
       if (q) *reinterpret_cast<uint2*>(q + (long)r * ldq + c) = b;
     }
-    if (qt) *reinterpret_cast<uint2*>(tile + rl * TS + c8) = b;
+    if (qt) *reinterpret_cast<uint2*>(tile + lrow(rl) + c8) = b;
   }
   if (!qt) return;
   __syncthreads();
@@ -1671,7 +1675,7 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
     for (int k = 0; k < 4; ++k) {
       uint32_t v = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[(rs + 4 * k + e) * TS + cl] << (8 * e);
+      for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[lrow(rs + 4 * k + e) + cl] << (8 * e);
       w[k] = v;
     }
     uint8_t* dst = qt + (long)c * ldqt + rb;

@@ -49,7 +49,7 @@ def test_cfg_from_depth(lib):
     assert c.d_model % 128 == 0 and c.n_head * c.head_dim == c.d_model
 
 
-def test_param_counts_match_survey_shapes():
+def test_param_counts_of_the_five_configs():
     assert configs.n_params(configs.get("tiny")) == 1441792
     assert configs.n_params(configs.get("laptop")) == 2899968
     assert configs.n_params(configs.get("d12")) == 135266304
