@@ -1486,22 +1486,40 @@ __global__ void __launch_bounds__(256) quant_e4m3_kernel(const T* __restrict__ x
 // produced by v_cvt_pk_fp8_f32 (round to nearest even) on values first clamped to
 // +-448, which is the saturating encode above.
 
+// eight consecutive elements as loaded; widened to fp32 only where they are used, so
+// that a thread can hold several chunks in flight in their stored width
 template <typename T>
-__device__ inline void load8f(const T* p, float (&f)[8]);
+struct Raw8;
 template <>
-__device__ inline void load8f<bf16_t>(const bf16_t* p, float (&f)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+struct Raw8<bf16_t> {
+  uint4 u;
+  __device__ inline void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ inline void get(float (&f)[8]) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
   }
-}
+};
 template <>
-__device__ inline void load8f<float>(const float* p, float (&f)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+struct Raw8<float> {
+  float4 a, b;
+  __device__ inline void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ inline void get(float (&f)[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+template <typename T>
+__device__ inline void load8f(const T* p, float (&f)[8]) {
+  Raw8<T> r;
+  r.load(p);
+  r.get(f);
 }
 
 __device__ inline uint2 e4m3x8(const float (&f)[8], float s) {
@@ -1621,8 +1639,9 @@ __global__ void __launch_bounds__(256) amax_fold_kernel(const float* __restrict_
 
 // a 128x128 tile per block: rows of q and of qt leave as whole 128-byte lines.  Each
 // thread converts eight 8-wide row chunks (16 threads per row); qt is read back from
-// LDS by columns, a wave per 64 columns and half of the rows, 64 bytes per thread.
-template <typename T>
+// LDS by columns, eight lanes per 128-byte line of qt.  FULL: the tile lies inside the
+// matrix and qt rows are 16-byte aligned, so no chunk or store needs a bounds check
+template <typename T, bool FULL>
 __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restrict__ x, int rows, int cols, long ldx,
                                                               const unsigned* amax_bits, uint8_t* __restrict__ q,
                                                               long ldq, uint8_t* __restrict__ qt, long ldqt,
@@ -1633,28 +1652,30 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
   constexpr int TS = 136;
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * TS + 7 * 8];
   auto lrow = [](int rl) { return rl * TS + (rl >> 4) * 8; };
-  const float amax = __uint_as_float(*amax_bits);
-  const float s = amax > 0.f ? 448.f / amax : 1.f;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
   const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
   const int t = threadIdx.x, c8 = (t & 15) * 8;
-  // the thread's eight 8-element chunks are all loaded before the first is converted (a
-  // chunk outside the matrix reads element 0 and is zeroed), so that eight loads per
-  // thread are in flight instead of one load-convert-store chain at a time
-  float f[8][8];
+  // the thread's eight chunks are all loaded, in their stored width, before the first is
+  // converted (a chunk outside the matrix reads element 0 and is zeroed), so that eight
+  // loads per thread are in flight instead of one load-convert-store chain at a time
+  Raw8<T> raw[8];
   bool ok[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = r0 + (t >> 4) + 16 * j, c = c0 + c8;
-    ok[j] = r < rows && c < cols;
-    load8f<T>(x + (ok[j] ? (long)r * ldx + c : 0L), f[j]);
+    ok[j] = FULL || (r < rows && c < cols);
+    raw[j].load(x + (ok[j] ? (long)r * ldx + c : 0L));
   }
+  const float amax = __uint_as_float(*amax_bits);
+  const float s = amax > 0.f ? 448.f / amax : 1.f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *inv_scale = 1.f / s;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int rl = (t >> 4) + 16 * j, r = r0 + rl, c = c0 + c8;
     uint2 b = make_uint2(0, 0);
     if (ok[j]) {
-      b = e4m3x8(f[j], s);
+      float f[8];
+      raw[j].get(f);
+      b = e4m3x8(f, s);
       if (q) *reinterpret_cast<uint2*>(q + (long)r * ldq + c) = b;
     }
     if (qt) *reinterpret_cast<uint2*>(tile + lrow(rl) + c8) = b;
@@ -1665,11 +1686,11 @@ __global__ void __launch_bounds__(256) quant_e4m3_t128_kernel(const T* __restric
   // 128-byte line, 16 rows each, so that a wave's store covers eight lines (lanes writing
   // 16 bytes into 64 different rows left every line partial)
   const int ch = t & 7, rs = ch * 16, rb = r0 + rs;
-  const bool vec = rb + 16 <= rows && (ldqt % 16) == 0;
+  const bool vec = FULL || (rb + 16 <= rows && (ldqt % 16) == 0);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int cl = it * 32 + (t >> 3), c = c0 + cl;
-    if (c >= cols || rb >= rows) continue;
+    if (!FULL && (c >= cols || rb >= rows)) continue;
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -2267,12 +2288,22 @@ void launch_quant_e4m3(const void* x, int it, int rows, int cols, long ld, const
   if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0 && (!q || (ldq % 8 == 0 && (uintptr_t)q % 8 == 0)) &&
       rows >= 128 && cols >= 128) {
     const dim3 g2((cols + 127) / 128, (rows + 127) / 128);
-    if (it == ACT_BF16)
-      hipLaunchKernelGGL(quant_e4m3_t128_kernel<bf16_t>, g2, b, 0, st, (const bf16_t*)x, rows, cols, ld, amax_bits, q,
-                         ldq, qt, ldqt, inv_scale);
-    else
-      hipLaunchKernelGGL(quant_e4m3_t128_kernel<float>, g2, b, 0, st, (const float*)x, rows, cols, ld, amax_bits, q,
-                         ldq, qt, ldqt, inv_scale);
+    const bool full = rows % 128 == 0 && cols % 128 == 0 && (!qt || (ldqt % 16 == 0 && (uintptr_t)qt % 16 == 0));
+    if (it == ACT_BF16) {
+      if (full)
+        hipLaunchKernelGGL((quant_e4m3_t128_kernel<bf16_t, true>), g2, b, 0, st, (const bf16_t*)x, rows, cols, ld,
+                           amax_bits, q, ldq, qt, ldqt, inv_scale);
+      else
+        hipLaunchKernelGGL((quant_e4m3_t128_kernel<bf16_t, false>), g2, b, 0, st, (const bf16_t*)x, rows, cols, ld,
+                           amax_bits, q, ldq, qt, ldqt, inv_scale);
+    } else {
+      if (full)
+        hipLaunchKernelGGL((quant_e4m3_t128_kernel<float, true>), g2, b, 0, st, (const float*)x, rows, cols, ld,
+                           amax_bits, q, ldq, qt, ldqt, inv_scale);
+      else
+        hipLaunchKernelGGL((quant_e4m3_t128_kernel<float, false>), g2, b, 0, st, (const float*)x, rows, cols, ld,
+                           amax_bits, q, ldq, qt, ldqt, inv_scale);
+    }
     return;
   }
   if (cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0 && (!q || (ldq % 8 == 0 && (uintptr_t)q % 8 == 0))) {
