@@ -185,8 +185,8 @@ __device__ inline long o_act(const GemmArgs& p, int bz, int row, int col) {
   return bz * p.strideOA + (long)row * p.ldoa + col;
 }
 
-// HALF: the fp16-operand NT instantiations (the Newton-Schulz A A product), the only ones that
-// read CinA
+// HALF: the fp16-operand instantiations (the Newton-Schulz products), the only ones that read
+// CinA
 template <bool HALF = false>
 __device__ inline bool epi_has_in(const GemmArgs& p) {
   return p.epi == EPI_DRELU2 || (p.epi == EPI_LINEAR && (p.Cin || (HALF && p.CinA)));
@@ -858,7 +858,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
   // the element-wise inputs of the vector path, one row block ahead: the loads of block
   // ib + 1 are in flight while block ib is written
   constexpr int NR = 32 / RPI;
-  const int ekind = p.splits == 1 && vec && n0 + wn * TN + lc + 3 < p.N ? epi_kind<F16 && BKM>(p) : 0;
+  const int ekind = p.splits == 1 && vec && n0 + wn * TN + lc + 3 < p.N ? epi_kind<F16>(p) : 0;
   uint4 rin[NR];
   epi_load<NR, RPI>(p, ekind, bz, m0 + wm * TM, n0 + wn * TN + lc, lrow, rin);
   float emx = 0.f;  // max |stored output| of the lane (amax_part)
@@ -878,7 +878,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
     const int col = n0 + wn * TN + lc;
     uint4 rnext[NR];
     epi_load<NR, RPI>(p, ib + 1 < FM ? ekind : 0, bz, row0 + 32, col, lrow, rnext);
-    write_block<F16 && BKM, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
+    write_block<F16, CS, RPI>(p, bz, row0, col, lrow, lc, vec, stage,
                                      p.splits > 1 ? p.ws + (long)yy * p.M * p.N : nullptr, ekind, rin, emx);
 #pragma unroll
     for (int i = 0; i < NR; ++i) rin[i] = rnext[i];
@@ -895,7 +895,7 @@ gemm_bf16_dma_kernel(GemmArgs p) {
                                      stage[(r4 + 3) * CS + cc]);
         if (vec && m + 3 < p.M) {
           float mx_ = 0.f;
-          epilogue_vec4<F16 && BKM>(p, bz, n, m, a, epi_in4<F16 && BKM>(p, bz, n, m), epi_has_in<F16 && BKM>(p),
+          epilogue_vec4<F16>(p, bz, n, m, a, epi_in4<F16>(p, bz, n, m), epi_has_in<F16>(p),
                                     mx_);
         } else {
 #pragma unroll 1
@@ -1398,9 +1398,9 @@ int launch_gemm(const GemmArgs& p0, hipStream_t st) {
     if ((size_t)p.splits * p.batch * p.M * p.N * sizeof(float) > p.ws_bytes) return 1;
   }
   if (p.split && (p.dtype != ACT_BF16 || p.splits != 1 || !p.A_lo || !p.B_lo)) return 1;
-  // CinA is read by the vectorised epilogue of the fp16 NT kernels only: every row and
-  // column in groups of four
-  if (p.CinA && (p.dtype != ACT_F16 || !p.a_kmaj || !p.b_kmaj || p.Cin || p.M % 4 || p.N % 4 || p.ldcin % 4 ||
+  // CinA is read by the vectorised epilogue of the fp16 NT and NN kernels only: every row
+  // and column in groups of four
+  if (p.CinA && (p.dtype != ACT_F16 || !p.a_kmaj || p.Cin || p.M % 4 || p.N % 4 || p.ldcin % 4 ||
                  p.strideCin % 4 ||
                  p.ldo % 4 || p.ldoa % 4 || p.strideO % 4 || p.strideOA % 4))
     return 1;

@@ -24,7 +24,7 @@ struct GemmArgs {
   int epi = EPI_LINEAR;
   float alpha = 1.f, beta = 0.f;
   const float* Cin = nullptr; long ldcin = 0, strideCin = 0;
-  const void* CinA = nullptr;     // fp16 NT kernels only: Cin as fp16 instead (Cin null; same ld/stride; M, N and
+  const void* CinA = nullptr;     // fp16 NT / NN kernels only: Cin as fp16 instead (Cin null; same ld/stride; M, N and
                                   // every leading dimension / stride multiples of 4, else launch_gemm fails)
   float* outF = nullptr; long ldo = 0, strideO = 0;
   void* outA = nullptr; long ldoa = 0, strideOA = 0;
