@@ -1223,7 +1223,8 @@ extern "C++" {
 // stored one after another from element offset off: A = X X^T, B = b A + c A A, X <- a X
 // + B X, every product on MFMA with operands of type nat (fp16 by default; bf16 with hi /
 // lo planes in the first nsplit iterations; fp32 for the all-fp32 configuration) and fp32
-// accumulation, X carried in fp32 (xf) and as operand planes (xa, xl, ping-ponged).
+// accumulation, X carried in fp32 (xf; with fp16 operands only through the first
+// kNsF32Carry iterations and for the result) and as operand planes (xa, xl, ping-ponged).
 struct NsBuffers {
   float* xf;
   char* xa[2];
@@ -1319,8 +1320,9 @@ int muon_update(gpt_model* M, float lr, void* stream) {
   char* xl[2] = {M->base + O.xl0, M->base + O.xl1};
   // 16-bit precisions: by default every product takes fp16 operands (11 significant
   // bits, the bf16 MFMA rate; X, A and B stay well inside fp16's range), with X carried
-  // in fp32 for the a X term (an fp16 carry loses the small entries of low-rank-plus-noise
-  // momenta to fp16's subnormals) and the b A term read from A's fp16 plane (as accurate
+  // in fp32 for the a X term of the first kNsF32Carry iterations (an fp16 carry from the
+  // start loses the small entries of low-rank-plus-noise momenta to fp16's subnormals),
+  // from its fp16 plane after them, and the b A term read from A's fp16 plane (as accurate
   // as an fp32 A in a numpy model of the iteration, and 4 bytes per element less).  With ns_split_steps > 0 the products run on bf16 MFMA
   // instead, and the leading iterations multiply A A and B X with operands carried as
   // bf16 hi + lo planes (three MFMA products each): rounding errors of the early
