@@ -1292,6 +1292,42 @@ __global__ void __launch_bounds__(256) ns_normalize_kernel(const float* __restri
   }
 }
 
+// The transposed form on 64 x 64 tiles (rows and cols multiples of 64): 16 lanes per
+// 256-byte row with float4 accesses on both sides of the transpose; the tile's row
+// stride of 65 floats puts the lanes of every LDS access in 64 different banks
+template <typename T>
+__global__ void __launch_bounds__(256) ns_normalize_t64_kernel(const float* __restrict__ src, const double* sumsq,
+                                                               int mat, float eps, int rows, int cols,
+                                                               float* __restrict__ xf, T* __restrict__ xa,
+                                                               T* __restrict__ xlo) {
+  __shared__ float tile[64][65];
+  const float scale = (float)(1.0 / (sqrt(sumsq[mat]) + (double)eps));
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x, q = (t & 15) * 4, i0 = t >> 4;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // rows r0 + i of src, columns c0 + q .. + 3
+    const int i = i0 + 16 * p;
+    const float4 a = *reinterpret_cast<const float4*>(src + (long)(r0 + i) * cols + c0 + q);
+    tile[i][q] = a.x * scale;
+    tile[i][q + 1] = a.y * scale;
+    tile[i][q + 2] = a.z * scale;
+    tile[i][q + 3] = a.w * scale;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // output row c0 + c ([cols][rows]), elements r0 + q .. + 3
+    const int c = i0 + 16 * p;
+    const float4 v = make_float4(tile[q][c], tile[q + 1][c], tile[q + 2][c], tile[q + 3][c]);
+    const long o = (long)(c0 + c) * rows + r0 + q;
+    *reinterpret_cast<float4*>(xf + o) = v;
+    st4<T>(xa + o, v);
+    if (xlo) {
+      const float4 h = make_float4(ld<T>(xa + o), ld<T>(xa + o + 1), ld<T>(xa + o + 2), ld<T>(xa + o + 3));
+      st4<T>(xlo + o, make_float4(v.x - h.x, v.y - h.y, v.z - h.z, v.w - h.w));
+    }
+  }
+}
+
 // the same without a transpose, four consecutive elements per thread (n % 4 == 0)
 template <typename T>
 __global__ void __launch_bounds__(256) ns_normalize_vec_kernel(const float* __restrict__ src, const double* sumsq,
@@ -1413,6 +1449,39 @@ __global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, 
       w[(long)r * cols + c] = nw;
       if (wa) st<T>(wa + (long)r * cols + c, nw);
     }
+  }
+}
+
+// The transposed apply on 64 x 64 tiles (rows and cols multiples of 64): X^T rows (the
+// columns of W) staged through LDS, then W rows updated with float4 accesses (same tile
+// layout as ns_normalize_t64_kernel)
+template <typename T>
+__global__ void __launch_bounds__(256) muon_apply_t64_kernel(float* __restrict__ w, T* __restrict__ wa,
+                                                             const float* __restrict__ x, float lr, int rows,
+                                                             int cols, const float* __restrict__ row_scale) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x, q = (t & 15) * 4, i0 = t >> 4;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // X^T row c0 + c, elements r0 + q .. + 3
+    const int c = i0 + 16 * p;
+    const float4 a = *reinterpret_cast<const float4*>(x + (long)(c0 + c) * rows + r0 + q);
+    tile[c][q] = a.x;
+    tile[c][q + 1] = a.y;
+    tile[c][q + 2] = a.z;
+    tile[c][q + 3] = a.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {  // W row r0 + r, columns c0 + q .. + 3
+    const int r = i0 + 16 * p;
+    const long o = (long)(r0 + r) * cols + c0 + q;
+    const float s = row_scale ? lr * row_scale[r0 + r] : lr;
+    const float4 wv = *reinterpret_cast<const float4*>(w + o);
+    const float4 nw = make_float4(wv.x - s * tile[q][r], wv.y - s * tile[q + 1][r], wv.z - s * tile[q + 2][r],
+                                  wv.w - s * tile[q + 3][r]);
+    *reinterpret_cast<float4*>(w + o) = nw;
+    if (wa) st4<T>(wa + o, nw);
   }
 }
 
@@ -2077,6 +2146,17 @@ void launch_ns_normalize(const float* src, const double* sumsq, int mat, float e
                          (f16_t*)xa, (f16_t*)xlo);
     return;
   }
+  const bool a16 = ((uintptr_t)src | (uintptr_t)xf) % 16 == 0 && ((uintptr_t)xa | (uintptr_t)xlo) % 8 == 0;
+  if (tr && rows % 64 == 0 && cols % 64 == 0 && a16 && at != ACT_F32) {
+    const dim3 gt(cols / 64, rows / 64);
+    if (at == ACT_BF16)
+      hipLaunchKernelGGL(ns_normalize_t64_kernel<bf16_t>, gt, dim3(256), 0, st, src, sumsq, mat, eps, rows, cols, xf,
+                         (bf16_t*)xa, (bf16_t*)xlo);
+    else
+      hipLaunchKernelGGL(ns_normalize_t64_kernel<f16_t>, gt, dim3(256), 0, st, src, sumsq, mat, eps, rows, cols, xf,
+                         (f16_t*)xa, (f16_t*)xlo);
+    return;
+  }
   dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
   if (at == ACT_BF16)
     hipLaunchKernelGGL(ns_normalize_kernel<bf16_t>, g, b, 0, st, src, sumsq, mat, eps, rows, cols, (int)tr, xf,
@@ -2126,6 +2206,17 @@ void launch_muon_apply(float* w, void* wa, int at, const float* x, float lr, int
     else
       hipLaunchKernelGGL(muon_apply_vec_kernel<float>, gv, dim3(256), 0, st, w, (float*)wa, x, lr, n4, row_scale,
                          cols);
+    return;
+  }
+  const bool a16 = ((uintptr_t)w | (uintptr_t)x) % 16 == 0 && (uintptr_t)wa % 16 == 0;
+  if (tr && rows % 64 == 0 && cols % 64 == 0 && a16) {
+    const dim3 gt(cols / 64, rows / 64);
+    if (at == ACT_BF16)
+      hipLaunchKernelGGL(muon_apply_t64_kernel<bf16_t>, gt, dim3(256), 0, st, w, (bf16_t*)wa, x, lr, rows, cols,
+                         row_scale);
+    else
+      hipLaunchKernelGGL(muon_apply_t64_kernel<float>, gt, dim3(256), 0, st, w, (float*)wa, x, lr, rows, cols,
+                         row_scale);
     return;
   }
   dim3 g((cols + 31) / 32, (rows + 31) / 32), b(256);
