@@ -1292,9 +1292,11 @@ static int ns_iterate(int nat, int nsplit, int steps, const float (*coeffs)[3], 
       // the a X term: X in fp32 through the first kNsF32Carry iterations, then (fp16
       // operands) from X's fp16 plane, which the product reads anyway
       const bool f16carry = nat == ACT_F16 && it >= kNsF32Carry;
+      const bool next_f16carry = nat == ACT_F16 && it + 1 >= kNsF32Carry;
       if (f16carry) p.CinA = xh;
       else p.Cin = nb.xf + off;
-      if (!f16carry || it + 1 == steps) { p.outF = nb.xf + off; p.ldo = l; p.strideO = sl; }
+      // the fp32 X only where it is read: by the next iteration's a X term, or as the result
+      if (it + 1 == steps || !next_f16carry) { p.outF = nb.xf + off; p.ldo = l; p.strideO = sl; }
       if (it + 1 < steps) {  // the operand planes of the next iteration (the last X is read in fp32 only)
         p.outA = nb.xa[cur ^ 1] + off * es; p.ldoa = l; p.strideOA = sl;
         if (next_sp) p.outA_lo = nb.xl[cur ^ 1] + off * es;
